@@ -1,0 +1,205 @@
+"""Oracle block allocator (pure Python).  Test infrastructure only.
+
+What it follows:
+
+* Lazy allocation: a sequence records its length and a list of logical
+  blocks; a physical block is taken from the pool only when a token position
+  first enters that logical block.  Page "Lazy Allocation 与 Copy-on-Write 在
+  LLM 推理系统中的应用", section 3.3 (Lazy Allocation 思想的迁移); page
+  "放下账簿，打开源码", section "PagedAttention：虚实分离，按需取用" (a block is
+  taken when the previous 16 tokens are full).
+* Slot of position ``pos``: the block table maps logical block ``pos // BS``
+  to a physical block; the slot is that block times BS plus ``pos % BS``
+  (same page, same section, block-table example 37/12/88; 0-based).
+* Fork: the child gets a copy of the parent's block table and every shared
+  block's refcount goes up; no KV bytes move.  Page "vLLM：把 KV 缓存当成虚拟
+  内存", section "碎片从哪里来".
+* Copy-on-write: a write into a block whose refcount is above one first takes
+  a fresh block, copies, drops the old block's count by one, points the
+  writer's table at the copy and writes there; the last holder writes in
+  place.  Page "Lazy Allocation 与 Copy-on-Write ...", section 4.4 (blocks 7,
+  1 and 3); page "放下账簿，打开源码", section "写时复制与前缀缓存" (refcount 4
+  -> 3 and 1).
+* Prefix sharing and release: a request sharing the first P tokens copies the
+  first ceil(P/BS) table entries and their counts go up; ending a request
+  drops each count by one and a block whose count reaches zero goes back to
+  the free pool.  Page "第 6 章 缓存管理", section "块表长什么样".
+
+Readings where the pages are silent (each one is a documented choice):
+
+* The free pool is a FIFO: allocation pops the front; release walks the
+  sequence's table in logical order and appends each block whose count hits
+  zero at the back.  ``initial_free_order`` seeds the FIFO.
+* One append writes positions ``len .. len+n-1``.  Only its first position
+  can land in an existing block; if that block is shared, exactly one CoW
+  copy is made.  Full shared blocks are never written.
+* An append that cannot get all the blocks it needs (new blocks plus the CoW
+  block) fails with ``OOM`` and changes nothing (reject, do not crash:
+  "第 6 章 缓存管理", section "缓存放不下的时候").
+* Sharing ``n`` tokens copies ``ceil(n / BS)`` entries even when the last one
+  holds more of the source's tokens; the sharer's length masks them and its
+  first write into that block copies it.
+"""
+from __future__ import annotations
+
+from collections import deque
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+class OracleError(Exception):
+    """Allocator error; ``code`` is one of ARG, OOM, REFCOUNT, NOT_FOUND."""
+
+    def __init__(self, code: str, msg: str = ""):
+        super().__init__(f"{code}: {msg}")
+        self.code = code
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+class OracleAllocator:
+    def __init__(self, num_blocks: int, block_size: int,
+                 initial_free_order: Optional[Sequence[int]] = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise OracleError("ARG", "num_blocks and block_size must be positive")
+        if initial_free_order is None:
+            order = list(range(num_blocks))
+        else:
+            order = [int(b) for b in initial_free_order]
+            if sorted(order) != list(range(num_blocks)):
+                raise OracleError("ARG", "initial_free_order must be a permutation of 0..NB-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free: deque = deque(order)
+        self.refcount: List[int] = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lens: Dict[int, int] = {}
+        self._next_seq = 0
+        # counters
+        self.lazy_allocs = 0
+        self.cow_copies = 0
+
+    # ------------------------------------------------------------ helpers
+    def _seq(self, seq: int) -> List[int]:
+        if seq not in self.tables:
+            raise OracleError("NOT_FOUND", f"sequence {seq}")
+        return self.tables[seq]
+
+    def _new_id(self) -> int:
+        s = self._next_seq
+        self._next_seq += 1
+        return s
+
+    # ------------------------------------------------------------ operations
+    def create(self) -> int:
+        s = self._new_id()
+        self.tables[s] = []
+        self.lens[s] = 0
+        return s
+
+    def append(self, seq: int, n_tokens: int) -> Tuple[List[int], Optional[Tuple[int, int]]]:
+        """Write positions len..len+n-1.  Returns (slots, cow_pair or None)."""
+        table = self._seq(seq)
+        if n_tokens < 0:
+            raise OracleError("ARG", "n_tokens < 0")
+        bs = self.block_size
+        start = self.lens[seq]
+        end = start + n_tokens
+        if n_tokens == 0:
+            return [], None
+        # is the first position inside an existing, shared block?
+        needs_cow = start % bs != 0 and self.refcount[table[start // bs]] > 1
+        new_blocks = _ceil_div(end, bs) - _ceil_div(start, bs)
+        if new_blocks + int(needs_cow) > len(self.free):
+            raise OracleError("OOM", f"need {new_blocks + int(needs_cow)}, free {len(self.free)}")
+        pair = None
+        if needs_cow:
+            src = table[start // bs]
+            dst = self.free.popleft()
+            self.refcount[src] -= 1
+            self.refcount[dst] = 1
+            table[start // bs] = dst
+            pair = (src, dst)
+            self.cow_copies += 1
+        slots = []
+        for pos in range(start, end):
+            if pos % bs == 0:
+                blk = self.free.popleft()
+                self.refcount[blk] = 1
+                table.append(blk)
+                self.lazy_allocs += 1
+            slots.append(table[pos // bs] * bs + pos % bs)
+        self.lens[seq] = end
+        return slots, pair
+
+    def fork(self, parent: int) -> int:
+        table = self._seq(parent)
+        child = self._new_id()
+        self.tables[child] = list(table)
+        self.lens[child] = self.lens[parent]
+        for b in table:
+            self.refcount[b] += 1
+        return child
+
+    def share_prefix(self, src: int, n_tokens: int) -> int:
+        table = self._seq(src)
+        if n_tokens < 0 or n_tokens > self.lens[src]:
+            raise OracleError("ARG", "prefix longer than the source")
+        k = _ceil_div(n_tokens, self.block_size)
+        s = self._new_id()
+        self.tables[s] = list(table[:k])
+        self.lens[s] = n_tokens
+        for b in self.tables[s]:
+            self.refcount[b] += 1
+        return s
+
+    def free_seq(self, seq: int) -> None:
+        table = self._seq(seq)
+        for b in table:
+            if self.refcount[b] <= 0:
+                raise OracleError("REFCOUNT", f"block {b} already free")
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.free.append(b)
+        del self.tables[seq]
+        del self.lens[seq]
+
+    def build_tables(self, seqs: Sequence[int], max_blocks: int):
+        """Block tables [n][max_blocks] int32 padded with -1, and lengths [n]."""
+        out = np.full((len(seqs), max_blocks), -1, dtype=np.int32)
+        lens = np.zeros(len(seqs), dtype=np.int32)
+        for r, s in enumerate(seqs):
+            t = self._seq(s)
+            if len(t) > max_blocks:
+                raise OracleError("ARG", f"sequence {s} has {len(t)} blocks > {max_blocks}")
+            out[r, :len(t)] = t
+            lens[r] = self.lens[s]
+        return out, lens
+
+    # ------------------------------------------------------------ invariants
+    def check_invariants(self) -> None:
+        """Refcount = in-degree from all tables; a block is free iff its count
+        is zero; the free pool has no duplicates; every table has exactly
+        ceil(len / BS) entries."""
+        indeg = [0] * self.num_blocks
+        for s, t in self.tables.items():
+            if len(t) != _ceil_div(self.lens[s], self.block_size):
+                raise AssertionError(f"seq {s}: {len(t)} blocks for {self.lens[s]} tokens")
+            for b in t:
+                indeg[b] += 1
+        if indeg != self.refcount:
+            raise AssertionError("refcount differs from table in-degree")
+        free_set = set(self.free)
+        if len(free_set) != len(self.free):
+            raise AssertionError("duplicate block in the free pool")
+        for b in range(self.num_blocks):
+            if (b in free_set) != (self.refcount[b] == 0):
+                raise AssertionError(f"block {b}: free={b in free_set} refcount={self.refcount[b]}")
+
+    def snapshot(self):
+        """(free FIFO as a list, refcounts, {seq: (table, len)}) for comparisons."""
+        return (list(self.free), list(self.refcount),
+                {s: (list(t), self.lens[s]) for s, t in self.tables.items()})

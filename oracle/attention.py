@@ -1,0 +1,136 @@
+"""Oracle decode attention in float64.  Test infrastructure only.
+
+Paging changes where K/V rows are stored, not the attention formula: the
+kernel follows the block table to find each logical block's physical block,
+and the result is plain scaled dot-product attention over the sequence's
+tokens (page "vLLM：把 KV 缓存当成虚拟内存", sections "破除误解" and
+"跨域连接"; page "放下账簿，打开源码", section "注意力计算的改写", whose dense
+form is softmax(Q K^T / sqrt(d_k)) V).
+
+So the oracle (1) walks a sequence's block table in logical order and
+concatenates the physical blocks, (2) keeps the first ``ctx`` token rows (the
+tokens the sequence has actually produced; slots past them in the last block
+are not part of the sequence), (3) decodes the element bits to float64 and
+(4) runs textbook softmax attention per query head.
+
+Readings where the pages are silent:
+
+* q head ``h`` reads kv head ``h // (Hq / Hkv)`` (grouped-query attention in
+  contiguous groups).
+* No mask other than the length: a decode query sees every cached token and
+  its own (already written) token.
+* The page's block-loop pseudocode leaves its running maximum undefined and
+  does not rescale; ``partitioned_decode`` states the standard online-softmax
+  merge (running max, rescaled sums) and is pinned to ``paged_decode``.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Element bit patterns -> float64 values."""
+    if dtype == "f32":
+        return np.asarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        # a bf16 value is the top half of the float32 with the same sign,
+        # exponent and leading mantissa bits
+        wide = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return wide.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def gather_sequence(pool: np.ndarray, table_row, ctx: int) -> np.ndarray:
+    """Reassemble one sequence's tokens from a pool [NB][Hkv][BS][D]:
+    logical block j is physical block table_row[j]; returns [ctx][Hkv][D]."""
+    bs = pool.shape[2]
+    n_blocks = -(-ctx // bs)
+    pieces = []
+    for j in range(n_blocks):
+        blk = int(table_row[j])
+        pieces.append(np.transpose(pool[blk], (1, 0, 2)))  # [BS][Hkv][D]
+    rows = np.concatenate(pieces, axis=0)
+    return rows[:ctx]
+
+
+def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Textbook attention for one decode query.
+
+    q [Hq][D], k and v [ctx][Hkv][D] (float64) -> out [Hq][D]:
+    out[h] = sum_t softmax_t(scale * <q[h], k[t, g]>) * v[t, g], g = h // G.
+    """
+    hq = q.shape[0]
+    hkv = k.shape[1]
+    group = hq // hkv
+    out = np.empty_like(q)
+    for h in range(hq):
+        g = h // group
+        s = scale * (k[:, g, :] @ q[h])
+        p = np.exp(s - s.max())
+        out[h] = (p @ v[:, g, :]) / p.sum()
+    return out
+
+
+def paged_decode(q_bits, k_pool_bits, v_pool_bits, block_tables, context_lens,
+                 scale: float, dtype: str, seqs=None) -> np.ndarray:
+    """Decode attention for every sequence (or the listed ``seqs``).
+
+    q_bits [B][Hq][D]; pools [NB][Hkv][BS][D]; block_tables [B][max_blocks];
+    context_lens [B].  Returns float64 [len(seqs)][Hq][D].
+    """
+    if seqs is None:
+        seqs = range(q_bits.shape[0])
+    outs = []
+    for i in seqs:
+        ctx = int(context_lens[i])
+        k = decode_bits(gather_sequence(k_pool_bits, block_tables[i], ctx), dtype)
+        v = decode_bits(gather_sequence(v_pool_bits, block_tables[i], ctx), dtype)
+        q = decode_bits(q_bits[i], dtype)
+        outs.append(dense_attention(q, k, v, scale))
+    return np.stack(outs) if outs else np.zeros((0,) + q_bits.shape[1:])
+
+
+def partition_state(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
+    """One partition's softmax state for each q head: running maximum m,
+    sum l = sum_t exp(s_t - m) and unnormalised o = sum_t exp(s_t - m) v_t."""
+    hq = q.shape[0]
+    group = hq // k.shape[1]
+    m = np.empty(hq)
+    l = np.empty(hq)
+    o = np.empty_like(q)
+    for h in range(hq):
+        g = h // group
+        s = scale * (k[:, g, :] @ q[h])
+        m[h] = s.max()
+        e = np.exp(s - m[h])
+        l[h] = e.sum()
+        o[h] = e @ v[:, g, :]
+    return m, l, o
+
+
+def merge_partitions(ms, ls, os_):
+    """Combine partition states: with M = max_p m_p and w_p = exp(m_p - M),
+    out = sum_p w_p o_p / sum_p w_p l_p."""
+    ms = np.asarray(ms)
+    big_m = ms.max(axis=0)
+    w = np.exp(ms - big_m)
+    num = np.einsum("ph,phd->hd", w, np.asarray(os_))
+    den = np.einsum("ph,ph->h", w, np.asarray(ls))
+    return num / den[:, None]
+
+
+def partitioned_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                       partition_tokens: int) -> np.ndarray:
+    """Split the sequence into runs of ``partition_tokens`` tokens, compute
+    each run's (m, l, o) and merge them (split-K with a log-sum-exp merge)."""
+    ctx = k.shape[0]
+    n_parts = max(1, math.ceil(ctx / partition_tokens))
+    states = [partition_state(q, k[p * partition_tokens:(p + 1) * partition_tokens],
+                              v[p * partition_tokens:(p + 1) * partition_tokens], scale)
+              for p in range(n_parts)]
+    return merge_partitions([s[0] for s in states], [s[1] for s in states],
+                            [s[2] for s in states])

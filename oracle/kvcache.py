@@ -1,0 +1,41 @@
+"""Oracle cache write and CoW block copy on raw element bits.  Test
+infrastructure only.
+
+Pool layout (both pools): [num_blocks][num_kv_heads][block_size][head_dim];
+element (block b, head h, offset o, dim d) holds token ``b*BS + o``'s value
+for kv head h.  Values are raw bit patterns (uint32 for f32, uint16 for
+f16/bf16), so both operations are bit-exact by construction.
+
+* ``write_slots``: decode reads every earlier token's K/V and appends the
+  new token's K/V ("Lazy Allocation 与 Copy-on-Write 在 LLM 推理系统中的应用",
+  section 2.1); the slot says where: physical block ``slot // BS``, offset
+  ``slot % BS`` ("放下账簿，打开源码", section "PagedAttention：虚实分离，按需取用").
+  A negative slot means "no write".
+* ``copy_blocks``: the copy-on-write copy of a whole shared block before the
+  writer's first write ("Lazy Allocation 与 Copy-on-Write ...", section 4.4).
+  Pairs are applied in order, all before any write of the same step.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def write_slots(pool: np.ndarray, new: np.ndarray, slots: np.ndarray) -> None:
+    """pool[slot // BS, :, slot % BS, :] = new[t] for every t with slot >= 0.
+
+    pool: [NB][Hkv][BS][D] bits (modified in place); new: [T][Hkv][D] bits;
+    slots: [T] int64.
+    """
+    bs = pool.shape[2]
+    slots = np.asarray(slots, dtype=np.int64)
+    for t in range(slots.shape[0]):
+        s = int(slots[t])
+        if s < 0:
+            continue
+        pool[s // bs, :, s % bs, :] = new[t]
+
+
+def copy_blocks(pool: np.ndarray, pairs) -> None:
+    """pool[dst] = pool[src] for each (src, dst), in order."""
+    for src, dst in pairs:
+        pool[int(dst)] = pool[int(src)]

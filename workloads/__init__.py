@@ -1,0 +1,220 @@
+"""Seeded synthetic inputs for the paged-attention decode workloads.
+
+This module is shared by the HIP path's tests/bench and by the oracle's tests.
+It holds no step of the method itself: no allocation policy, no cache write,
+no attention arithmetic. It only draws lengths, random K/V/q values and the
+initial free-block order, and rounds the float32 draws to the element type
+the workload names (inputs, not results).
+
+Workloads (shapes follow the pages' model sizes; all are one layer):
+
+* ``tiny``   4 sequences attending {10, 5, 33, 7} tokens, 4 q heads = 4 kv
+             heads, head_dim 64, fp32, block 16, 64-block pool.
+* ``7b_mha`` 7B-shaped MHA: 32 q = 32 kv heads, head_dim 128, fp16, block 16,
+             batch 64, lengths uniform in [128, 2048].  The 7B shape is the one
+             whose per-token KV size the page "放下账簿，打开源码"
+             (section "KV Cache：推理的工作记忆") works out.
+* ``8b_gqa`` 8B GQA: 32 q heads, 8 kv heads, head_dim 128, bf16, block 16,
+             batch 256, lengths log-normal (median 1500, sigma 0.8) clipped to
+             [16, 8192].  Shape of chapter 6 of the AI-infra book
+             ("第 6 章 缓存管理", section "分页：把缓存切成固定大小的块").
+* ``cow``    parallel sampling: 32 prompts x 4 branches, 8B-GQA shape, bf16;
+             a 1000-token prefix shared by fork, then per-branch tails uniform
+             in [0, 256] plus one decode token.
+* ``qwen32b_long``  64 q heads, 8 kv heads, head_dim 128, bf16, 32 sequences
+             of 2048 tokens plus 4 of 32768, block 16 (``_bs32``: block 32).
+
+Context lengths here are the number of tokens a decode query attends to,
+including the token being decoded (its K/V is written first).
+
+Random streams: the workload's own generator ``default_rng(seed)`` draws the
+lengths first and then the initial free-block permutation.  K/V of sequence
+(or prompt / branch) ``i`` come from their own child stream so that a single
+sequence can be regenerated without drawing the whole batch.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    block_size: int
+    partition_tokens: int = 512
+    # copy-on-write workload only
+    num_prompts: int = 0
+    branches: int = 0
+    prefix_len: int = 0
+    tail_max: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def elem_bytes(self) -> int:
+        return DTYPE_BYTES[self.dtype]
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", 0, 4, 4, 64, "f32", 16),
+    "7b_mha": Workload("7b_mha", 1, 32, 32, 128, "f16", 16),
+    "8b_gqa": Workload("8b_gqa", 2, 32, 8, 128, "bf16", 16),
+    "cow": Workload("cow", 3, 32, 8, 128, "bf16", 16, num_prompts=32, branches=4,
+                    prefix_len=1000, tail_max=256),
+    "qwen32b_long": Workload("qwen32b_long", 4, 64, 8, 128, "bf16", 16),
+    "qwen32b_long_bs32": Workload("qwen32b_long_bs32", 4, 64, 8, 128, "bf16", 32),
+}
+
+
+@dataclasses.dataclass
+class Draw:
+    """Everything random about one workload instance."""
+    wl: Workload
+    context_lens: np.ndarray          # [B] int64, attended tokens per sequence
+    num_blocks: int                   # physical pool size
+    free_order: np.ndarray            # [num_blocks] int64 permutation
+    tails: Optional[np.ndarray] = None  # cow only: [prompts][branches]
+
+    @property
+    def batch(self) -> int:
+        return int(self.context_lens.shape[0])
+
+
+def _blocks_for(n_tokens: np.ndarray, block_size: int) -> int:
+    return int(np.sum((n_tokens + block_size - 1) // block_size))
+
+
+def draw(name: str, batch: Optional[int] = None) -> Draw:
+    """Draw lengths, pool size and free order for a named workload.
+
+    ``batch`` truncates the batch (the first draws are kept), for small
+    parity cases of the same distribution.
+    """
+    wl = WORKLOADS[name]
+    rng = np.random.default_rng(wl.seed)
+    tails = None
+    if wl.name == "tiny":
+        lens = np.array([10, 5, 33, 7], dtype=np.int64)
+        nb = 64
+    elif wl.name == "7b_mha":
+        lens = rng.integers(128, 2048, 64, endpoint=True).astype(np.int64)
+    elif wl.name == "8b_gqa":
+        lens = np.clip(np.rint(rng.lognormal(math.log(1500.0), 0.8, 256)), 16, 8192).astype(np.int64)
+    elif wl.name == "cow":
+        tails = rng.integers(0, wl.tail_max, (wl.num_prompts, wl.branches), endpoint=True).astype(np.int64)
+        lens = (wl.prefix_len + tails + 1).reshape(-1)
+    elif wl.name.startswith("qwen32b_long"):
+        lens = np.array([2048] * 32 + [32768] * 4, dtype=np.int64)
+    else:  # pragma: no cover
+        raise KeyError(name)
+    if batch is not None:
+        if tails is not None:
+            keep = max(1, batch // wl.branches)
+            tails = tails[:keep]
+            lens = (wl.prefix_len + tails + 1).reshape(-1)
+        else:
+            lens = lens[:batch]
+    if wl.name != "tiny":
+        # pool sized to 1.25x the unshared block demand of the batch
+        nb = int(math.ceil(1.25 * _blocks_for(lens, wl.block_size)))
+    free_order = rng.permutation(nb).astype(np.int64)
+    return Draw(wl, lens, nb, free_order, tails)
+
+
+# ---------------------------------------------------------------- element bits
+
+def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to ``dtype`` (round to nearest even) and return
+    the raw bit patterns (uint32 for f32, uint16 for f16/bf16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x.view(np.uint32).copy()
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        u = x.view(np.uint32)
+        rounded = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+        return rounded.astype(np.uint16)
+    raise ValueError(dtype)
+
+
+def bits_dtype(dtype: str):
+    return np.uint32 if dtype == "f32" else np.uint16
+
+
+def _normal_bits(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    return to_bits(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
+def query_bits(d: Draw) -> np.ndarray:
+    """q for the decode step: [B][Hq][D] bits."""
+    wl = d.wl
+    rng = np.random.default_rng([wl.seed, 3])
+    return _normal_bits(rng, (d.batch, wl.num_q_heads, wl.head_dim), wl.dtype)
+
+
+def sequence_kv_bits(d: Draw, i: int):
+    """Contiguous K and V of sequence ``i`` for all of its attended tokens:
+    two [ctx_i][Hkv][D] bit arrays.  For the copy-on-write workload, the
+    first ``prefix_len`` tokens come from the prompt's stream (identical for
+    the prompt's branches) and the rest from the branch's own stream."""
+    wl = d.wl
+    ctx = int(d.context_lens[i])
+    shape_tail = (wl.num_kv_heads, wl.head_dim)
+    if wl.name == "cow":
+        p, b = divmod(i, wl.branches)
+        pk, pv = prompt_kv_bits(d, p)
+        rng = np.random.default_rng([wl.seed, 2, p, b])
+        n = ctx - wl.prefix_len
+        tk = _normal_bits(rng, (n,) + shape_tail, wl.dtype)
+        tv = _normal_bits(rng, (n,) + shape_tail, wl.dtype)
+        return np.concatenate([pk, tk]), np.concatenate([pv, tv])
+    rng = np.random.default_rng([wl.seed, 1, i])
+    k = _normal_bits(rng, (ctx,) + shape_tail, wl.dtype)
+    v = _normal_bits(rng, (ctx,) + shape_tail, wl.dtype)
+    return k, v
+
+
+def prompt_kv_bits(d: Draw, p: int):
+    """Copy-on-write workload: K and V of prompt ``p``'s shared prefix."""
+    wl = d.wl
+    rng = np.random.default_rng([wl.seed, 1, p])
+    shape = (wl.prefix_len, wl.num_kv_heads, wl.head_dim)
+    return _normal_bits(rng, shape, wl.dtype), _normal_bits(rng, shape, wl.dtype)
+
+
+def pool_fill_bits(d: Draw, nan: bool = False) -> List[np.ndarray]:
+    """Initial contents of the K and V pools before any cache write:
+    N(0,1) values, or NaN everywhere when ``nan`` (poisoned-padding runs).
+    Returns [k_pool, v_pool], each [NB][Hkv][BS][D] bits."""
+    wl = d.wl
+    shape = (d.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    if nan:
+        nan_bits = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}[wl.dtype]
+        return [np.full(shape, nan_bits, dtype=bits_dtype(wl.dtype)) for _ in range(2)]
+    rng = np.random.default_rng([wl.seed, 4])
+    return [_normal_bits(rng, shape, wl.dtype) for _ in range(2)]
+
+
+def kv_bytes(d: Draw) -> int:
+    """Algorithmic K+V bytes one decode step reads: attended tokens only."""
+    wl = d.wl
+    return int(d.context_lens.sum()) * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
