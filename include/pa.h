@@ -1,0 +1,249 @@
+/*
+ * pa.h -- C ABI of the paged KV-cache decode library (libpa.so) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method: a sequence's K/V live in fixed-size physical blocks of a shared
+ * pool, found through a per-sequence block table (logical block -> physical
+ * block).  Attention itself is unchanged; only where the rows are stored
+ * changes, and the kernel follows the table (page "vLLM：把 KV 缓存当成虚拟
+ * 内存", section "破除误解"; page "放下账簿，打开源码", sections
+ * "PagedAttention：虚实分离，按需取用" and "注意力计算的改写").  Blocks are
+ * taken lazily, shared by fork / prefix sharing with reference counts, and
+ * copied on the first write into a shared block (page "Lazy Allocation 与
+ * Copy-on-Write 在 LLM 推理系统中的应用", sections 3.3 and 4.4; page "第 6 章
+ * 缓存管理：把显存当操作系统来管", section "块表长什么样").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pool layout (K and V alike): contiguous [num_blocks][num_kv_heads]
+ *   [block_size][head_dim] elements of the pool dtype.  Token position `pos`
+ *   of a sequence lives in physical block table[pos / block_size] at offset
+ *   pos % block_size; its slot is block * block_size + offset.
+ * - Device pointers are caller-owned (e.g. torch tensors) and must be 16-byte
+ *   aligned.  The library never allocates device memory; the split-K
+ *   workspace is passed in by the caller.
+ * - Kernels run asynchronously on `hip_stream` (NULL = the null stream), in
+ *   the order the calls are made.  A step that copies blocks and writes new
+ *   tokens must call pa_copy_blocks before pa_reshape_and_cache on the same
+ *   stream (copies of a step land before its writes).
+ * - Argument, shape and dtype checks happen on the host before any launch and
+ *   return a negative status with nothing launched.  A failed launch returns
+ *   PA_ERR_HIP.  Device-side values (block ids, slots, context lengths) are not
+ *   validated on the host; the kernels never access memory outside the pools,
+ *   tables or buffers for out-of-range values, but the numbers they produce
+ *   for such inputs are unspecified (see each call).
+ * - Supported shapes: dtype f32, f16 or bf16; head_dim 64 or 128; block_size
+ *   16 or 32; num_q_heads a multiple of num_kv_heads with group
+ *   G = num_q_heads / num_kv_heads <= 16 (<= 8 for f32 or head_dim 64).
+ *
+ * Thread safety: the kernel entry points are reentrant.  An allocator handle
+ * must not be used from two threads at once.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_ARG = -1,       /* null pointer, misalignment, value out of range */
+  PA_ERR_DTYPE = -2,     /* unknown dtype */
+  PA_ERR_SHAPE = -3,     /* unsupported head_dim / block_size / group size */
+  PA_ERR_OOM = -4,       /* allocator: not enough free blocks (state unchanged) */
+  PA_ERR_REFCOUNT = -5,  /* allocator: refcount would go below zero */
+  PA_ERR_NOT_FOUND = -6, /* allocator: unknown sequence id */
+  PA_ERR_HIP = -7        /* a HIP launch or runtime call failed */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Shape of one K pool and one V pool (both have this shape). */
+typedef struct {
+  int32_t num_blocks;   /* physical blocks NB >= 1 */
+  int32_t block_size;   /* tokens per block BS: 16 or 32 */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t dtype;        /* pa_dtype of pools, q and out */
+} pa_pool_desc;
+
+/* Library version of this ABI (bumped on incompatible change). */
+int32_t pa_abi_version(void);
+
+/* Static string naming a status code. */
+const char* pa_status_string(int32_t status);
+
+/* ------------------------------------------------------------------------
+ * Decode attention (one new query token per sequence).
+ *
+ * For sequence i, q head h and its kv head g = h / G, with ctx = context_lens[i]
+ * tokens at positions 0..ctx-1 found through block_tables[i]:
+ *     out[i][h] = sum_t softmax_t(scale * <q[i][h], K[t][g]>) * V[t][g]
+ * accumulated in fp32 and rounded once (round to nearest even) to the pool
+ * dtype.  context_lens count every token the query attends to, including the
+ * token being decoded, whose K/V must already be written (pa_reshape_and_cache
+ * before pa_decode on the same stream).
+ *
+ * Work split: one workgroup per (sequence, kv head, partition of
+ * `partition_tokens` consecutive positions).  A sequence with a single
+ * partition is written to `out` directly; longer ones leave one fp32
+ * (max, sum, unnormalised output) per partition in the workspace and a second
+ * kernel merges them with a log-sum-exp rescale (split-K).
+ *
+ *   q             device, [num_seqs][num_q_heads][head_dim], pool dtype
+ *   k_pool/v_pool device, pool layout above
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(ctx / BS) are never read (any padding value is fine)
+ *   context_lens  device int32 [num_seqs]; a value <= 0 yields an all-zero
+ *                 output row; values are clamped to max_context_len and to
+ *                 max_blocks_per_seq * BS
+ *   max_context_len  host bound >= every context_lens[i]; sizes the grid
+ *                 without a device->host copy
+ *   scale         softmax scale (typically 1 / sqrt(head_dim))
+ *   out           device, [num_seqs][num_q_heads][head_dim], pool dtype
+ *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
+ *                 aligned; may be NULL when that size is 0.  Scratch only:
+ *                 its contents on entry do not matter.
+ *   partition_tokens  multiple of 16 and of block_size, in [16, 8192];
+ *                 0 selects the default (512)
+ * Block ids outside [0, num_blocks) are skipped (those tokens do not take
+ * part); the output is then unspecified but no access leaves the pool.
+ * ------------------------------------------------------------------------ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_tokens);
+
+pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const pa_pool_desc* pool, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
+                    void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                    void* hip_stream);
+
+/* The two passes of pa_decode, callable one at a time (same arguments, same
+ * stream; pa_decode == pa_decode_partition then pa_decode_reduce).  The
+ * reduce pass only touches sequences with more than one partition. */
+pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_pool,
+                              const pa_pool_desc* pool, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                              float scale, void* out, void* workspace, size_t workspace_bytes,
+                              int32_t partition_tokens, void* hip_stream);
+
+pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool,
+                           const pa_pool_desc* pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                           float scale, void* out, void* workspace, size_t workspace_bytes,
+                           int32_t partition_tokens, void* hip_stream);
+
+/* Decode kernel family: PA_PATH_AUTO picks the matrix-core kernel for 16-bit
+ * pools with head_dim 128 and G >= 2 and the vector kernel otherwise;
+ * PA_PATH_VALU / PA_PATH_MFMA force one (PA_ERR_SHAPE if it does not support
+ * the shape).  Process-wide setting; returns the previous value. */
+typedef enum { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 } pa_decode_path;
+int32_t pa_set_decode_path(int32_t path);
+
+/* ------------------------------------------------------------------------
+ * Cache write: decode appends each new token's K/V to the cache (page
+ * "Lazy Allocation 与 Copy-on-Write 在 LLM 推理系统中的应用", section 2.1), at
+ * the slot its block table gives.  For every t with slot = slot_mapping[t]
+ * >= 0 and every kv head h:
+ *     k_pool[slot / BS][h][slot % BS][:] = k[t][h][:]   (same for v)
+ * Bit-exact copy.  Slots < 0 are skipped; slots >= num_blocks * BS are
+ * skipped too (never written).  Two tokens with the same slot race.
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim], pool dtype
+ *   slot_mapping  device int64 [num_tokens]
+ * ------------------------------------------------------------------------ */
+pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
+                               int32_t num_tokens, void* k_pool, void* v_pool,
+                               const pa_pool_desc* pool, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Copy-on-write block copy: before the first write into a block that other
+ * sequences still share, the writer gets a private copy (page "Lazy
+ * Allocation 与 Copy-on-Write 在 LLM 推理系统中的应用", section 4.4; page
+ * "第 6 章 缓存管理：把显存当操作系统来管", section "块表长什么样").  For each
+ * pair p: k_pool[dst] = k_pool[src] and v_pool[dst] = v_pool[src], whole
+ * blocks (all kv heads, all slots).  Bit-exact.  No dst may be a src or a dst
+ * of another pair of the same call (the allocator guarantees this); pairs
+ * with an id outside [0, num_blocks) are skipped.
+ *   pairs  device int32 [num_pairs][2] = (src, dst)
+ * ------------------------------------------------------------------------ */
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool,
+                         const int32_t* pairs, int32_t num_pairs, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator (no device memory; host arrays only).
+ *
+ * Free pool: a FIFO seeded with `initial_free_order` (NULL = 0..NB-1).
+ * Allocation pops the front; freeing a sequence walks its table in logical
+ * order and appends every block whose refcount reaches zero at the back.
+ *
+ * pa_seq_append writes positions len..len+n-1 of a sequence.  A position that
+ * starts a logical block takes a fresh block (lazy allocation).  If the first
+ * position falls inside the last block and that block's refcount is > 1, the
+ * writer first gets a copy: a fresh block dst, the pair (src, dst) is
+ * returned for pa_copy_blocks, src's refcount drops by one and the table
+ * points at dst (the last holder writes in place; page "Lazy Allocation 与
+ * Copy-on-Write ...", section 4.4).  At most one pair per call.  If the free
+ * pool cannot supply every block the call needs it returns PA_ERR_OOM and
+ * changes nothing.
+ *
+ * pa_seq_fork: the child gets a copy of the parent's table and length; every
+ * block's refcount goes up by one (no KV moves; page "vLLM：把 KV 缓存当成虚拟
+ * 内存", section "碎片从哪里来").
+ * pa_seq_share_prefix: a new sequence whose first ceil(n / BS) table entries
+ * are src's, refcounts +1, length n (0 <= n <= src length; page "第 6 章
+ * 缓存管理：把显存当操作系统来管", section "块表长什么样").
+ * pa_seq_free: refcount -1 on each block; zero -> back to the free pool.
+ * Sequence ids are assigned 0, 1, 2, ... in creation order, never reused.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_alloc pa_alloc;
+
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
+                          const int32_t* initial_free_order, pa_alloc** out);
+void pa_alloc_destroy(pa_alloc* a);
+
+pa_status pa_seq_create(pa_alloc* a, int64_t* seq_out);
+/* slots_out: host int64 [n_tokens]; cow_pair_out: host int32 [2]; num_cow_out: 0 or 1 */
+pa_status pa_seq_append(pa_alloc* a, int64_t seq, int32_t n_tokens, int64_t* slots_out,
+                        int32_t* cow_pair_out, int32_t* num_cow_out);
+/* One decode step for many sequences: appends n_tokens to each of seqs[0..n)
+ * in order.  slots_out [n * n_tokens]; pairs_out [n][2]; *num_pairs_out =
+ * pairs written.  All or nothing: on PA_ERR_OOM nothing changes. */
+pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32_t n_tokens,
+                              int64_t* slots_out, int32_t* pairs_out, int32_t* num_pairs_out);
+pa_status pa_seq_fork(pa_alloc* a, int64_t parent, int64_t* child_out);
+pa_status pa_seq_share_prefix(pa_alloc* a, int64_t src, int32_t n_tokens, int64_t* seq_out);
+pa_status pa_seq_free(pa_alloc* a, int64_t seq);
+/* Length and table of one sequence: table_out [capacity] (may be NULL);
+ * *num_blocks_out = its number of blocks (PA_ERR_ARG if > capacity and
+ * table_out is non-NULL). */
+pa_status pa_seq_info(const pa_alloc* a, int64_t seq, int32_t* len_out, int32_t* table_out,
+                      int32_t capacity, int32_t* num_blocks_out);
+/* Block tables of seqs[0..n) padded with -1: tables_out [n][max_blocks],
+ * lens_out [n].  PA_ERR_ARG if a sequence has more than max_blocks blocks. */
+pa_status pa_build_tables(const pa_alloc* a, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                          int32_t* tables_out, int32_t* lens_out);
+/* Free-pool size, the free pool front to back (free_list_out [NB] or NULL)
+ * and every block's refcount (refcounts_out [NB] or NULL). */
+pa_status pa_alloc_query(const pa_alloc* a, int32_t* num_free, int32_t* free_list_out,
+                         int32_t* refcounts_out);
+/* Counters: lazy block allocations and CoW copies since creation, live
+ * sequences, blocks with refcount > 1. */
+pa_status pa_alloc_stats(const pa_alloc* a, int64_t* lazy_allocs, int64_t* cow_copies,
+                         int32_t* live_seqs, int32_t* shared_blocks);
+/* PA_OK if refcount == in-degree over all tables, a block is free iff its
+ * refcount is 0, the free pool has no duplicates and every table has
+ * ceil(len / BS) entries; PA_ERR_REFCOUNT otherwise. */
+pa_status pa_alloc_check_invariants(const pa_alloc* a);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

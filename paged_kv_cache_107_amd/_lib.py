@@ -1,0 +1,86 @@
+"""Loads libpa.so and declares its C signatures (ctypes).
+
+The library must have been built (``python -m paged_kv_cache_107_amd.build``
+or ``__graft_entry__.build()``); there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_OK, PA_ERR_ARG, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_OOM, PA_ERR_REFCOUNT, \
+    PA_ERR_NOT_FOUND, PA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6, -7
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA = 0, 1, 2
+
+
+class pa_pool_desc(C.Structure):
+    _fields_ = [("num_blocks", C.c_int32), ("block_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32)]
+
+
+_vp, _i32, _i64, _f32, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+_pi32, _pi64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
+_desc = C.POINTER(pa_pool_desc)
+
+_DECODE_ARGS = [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _sz,
+                _i32, _vp]
+
+SIGNATURES = {
+    "pa_abi_version": (_i32, []),
+    "pa_status_string": (C.c_char_p, [_i32]),
+    "pa_set_decode_path": (_i32, [_i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (_i32, _DECODE_ARGS),
+    "pa_decode_partition": (_i32, _DECODE_ARGS),
+    "pa_decode_reduce": (_i32, _DECODE_ARGS),
+    "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _desc, _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _desc, _vp, _i32, _vp]),
+    "pa_alloc_create": (_i32, [_i32, _i32, _pi32, C.POINTER(_vp)]),
+    "pa_alloc_destroy": (None, [_vp]),
+    "pa_seq_create": (_i32, [_vp, _pi64]),
+    "pa_seq_append": (_i32, [_vp, _i64, _i32, _pi64, _pi32, _pi32]),
+    "pa_seq_append_batch": (_i32, [_vp, _pi64, _i32, _i32, _pi64, _pi32, _pi32]),
+    "pa_seq_fork": (_i32, [_vp, _i64, _pi64]),
+    "pa_seq_share_prefix": (_i32, [_vp, _i64, _i32, _pi64]),
+    "pa_seq_free": (_i32, [_vp, _i64]),
+    "pa_seq_info": (_i32, [_vp, _i64, _pi32, _pi32, _i32, _pi32]),
+    "pa_build_tables": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
+    "pa_alloc_query": (_i32, [_vp, _pi32, _pi32, _pi32]),
+    "pa_alloc_stats": (_i32, [_vp, _pi64, _pi64, _pi32, _pi32]),
+    "pa_alloc_check_invariants": (_i32, [_vp]),
+}
+
+_lib = None
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        self.code = status
+        name = lib().pa_status_string(status).decode()
+        super().__init__(f"{fn} failed: {name} ({status})")
+
+
+def lib() -> C.CDLL:
+    """The loaded library, with argtypes/restype set.  Raises if not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_107_amd.build` "
+                "(the decode path has no non-HIP fallback)")
+        h = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != PA_OK:
+        raise PaError(fn, status)

@@ -1,0 +1,128 @@
+"""Python handle on libpa's host block allocator (pa_alloc_* / pa_seq_*).
+
+Methods call the C function of the same name; arrays come back as numpy.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from ._lib import PaError, check, lib
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _i64p(a: np.ndarray):
+    return a.ctypes.data_as(C.POINTER(C.c_int64))
+
+
+class PaAllocator:
+    def __init__(self, num_blocks: int, block_size: int,
+                 initial_free_order: Optional[Sequence[int]] = None):
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        h = C.c_void_p()
+        order = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            if order.shape != (self.num_blocks,):
+                raise ValueError("initial_free_order must have num_blocks entries")
+        check("pa_alloc_create", lib().pa_alloc_create(
+            self.num_blocks, self.block_size, None if order is None else _i32p(order),
+            C.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_alloc_destroy(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ sequences
+    def pa_seq_create(self) -> int:
+        s = C.c_int64()
+        check("pa_seq_create", lib().pa_seq_create(self._h, C.byref(s)))
+        return s.value
+
+    def pa_seq_append(self, seq: int, n_tokens: int) -> Tuple[np.ndarray, Optional[Tuple[int, int]]]:
+        slots = np.empty(max(n_tokens, 1), dtype=np.int64)
+        pair = np.zeros(2, dtype=np.int32)
+        ncow = C.c_int32()
+        check("pa_seq_append", lib().pa_seq_append(self._h, int(seq), int(n_tokens), _i64p(slots),
+                                                   _i32p(pair), C.byref(ncow)))
+        return slots[:n_tokens], ((int(pair[0]), int(pair[1])) if ncow.value else None)
+
+    def pa_seq_append_batch(self, seqs: Sequence[int], n_tokens: int):
+        """Returns (slots [len(seqs) * n_tokens] int64, pairs [P][2] int32)."""
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        slots = np.empty(max(n * n_tokens, 1), dtype=np.int64)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        npairs = C.c_int32()
+        check("pa_seq_append_batch", lib().pa_seq_append_batch(
+            self._h, _i64p(s), n, int(n_tokens), _i64p(slots), _i32p(pairs), C.byref(npairs)))
+        return slots[:n * n_tokens], pairs[:npairs.value]
+
+    def pa_seq_fork(self, parent: int) -> int:
+        c = C.c_int64()
+        check("pa_seq_fork", lib().pa_seq_fork(self._h, int(parent), C.byref(c)))
+        return c.value
+
+    def pa_seq_share_prefix(self, src: int, n_tokens: int) -> int:
+        c = C.c_int64()
+        check("pa_seq_share_prefix",
+              lib().pa_seq_share_prefix(self._h, int(src), int(n_tokens), C.byref(c)))
+        return c.value
+
+    def pa_seq_free(self, seq: int) -> None:
+        check("pa_seq_free", lib().pa_seq_free(self._h, int(seq)))
+
+    def pa_seq_info(self, seq: int) -> Tuple[int, np.ndarray]:
+        length, nblk = C.c_int32(), C.c_int32()
+        check("pa_seq_info", lib().pa_seq_info(self._h, int(seq), C.byref(length), None, 0,
+                                                C.byref(nblk)))
+        table = np.empty(max(nblk.value, 1), dtype=np.int32)
+        check("pa_seq_info", lib().pa_seq_info(self._h, int(seq), None, _i32p(table),
+                                                table.shape[0], C.byref(nblk)))
+        return length.value, table[:nblk.value]
+
+    def pa_build_tables(self, seqs: Sequence[int], max_blocks: int):
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        tables = np.empty((n, max_blocks), dtype=np.int32)
+        lens = np.empty(n, dtype=np.int32)
+        check("pa_build_tables", lib().pa_build_tables(self._h, _i64p(s), n, int(max_blocks),
+                                                       _i32p(tables), _i32p(lens)))
+        return tables, lens
+
+    # ------------------------------------------------------------ pool state
+    def pa_alloc_query(self):
+        """(free pool front to back, refcounts) as int32 arrays."""
+        nf = C.c_int32()
+        free = np.empty(self.num_blocks, dtype=np.int32)
+        rc = np.empty(self.num_blocks, dtype=np.int32)
+        check("pa_alloc_query", lib().pa_alloc_query(self._h, C.byref(nf), _i32p(free), _i32p(rc)))
+        return free[:nf.value], rc
+
+    def pa_alloc_stats(self):
+        la, cc = C.c_int64(), C.c_int64()
+        live, shared = C.c_int32(), C.c_int32()
+        check("pa_alloc_stats", lib().pa_alloc_stats(self._h, C.byref(la), C.byref(cc),
+                                                     C.byref(live), C.byref(shared)))
+        return {"lazy_allocs": la.value, "cow_copies": cc.value, "live_seqs": live.value,
+                "shared_blocks": shared.value}
+
+    def pa_alloc_check_invariants(self) -> bool:
+        st = lib().pa_alloc_check_invariants(self._h)
+        if st not in (0, -5):
+            raise PaError("pa_alloc_check_invariants", st)
+        return st == 0

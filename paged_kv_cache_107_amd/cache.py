@@ -1,0 +1,120 @@
+"""A paged KV cache for one attention layer: device pools plus the host
+allocator, and the decode step over them.
+
+A step has a host half and a device half:
+
+* ``plan``: the allocator reserves one slot per new token (taking blocks
+  lazily, copying shared blocks on write) and the block tables and lengths
+  of the sequences to decode are built; the small index arrays are copied to
+  the device once;
+* ``run``: on the device, in order on one stream, the CoW block copies, the
+  new tokens' cache write, then decode attention through the tables.
+
+Everything on the device runs in libpa's HIP kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from .allocator import PaAllocator
+from .ops import (alloc_workspace, pa_copy_blocks, pa_decode, pa_reshape_and_cache)
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass
+class StepPlan:
+    """Device-resident index arrays of one decode step."""
+    seqs: List[int]
+    slots: torch.Tensor         # int64 [T]
+    pairs: torch.Tensor         # int32 [P][2]
+    tables: torch.Tensor        # int32 [B][max_blocks]
+    lens: torch.Tensor          # int32 [B]
+    max_context_len: int
+    host_lens: np.ndarray
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                 dtype: str, initial_free_order: Optional[Sequence[int]] = None,
+                 device="cuda", pools: Optional[tuple] = None):
+        self.block_size = block_size
+        self.num_kv_heads = num_kv_heads
+        self.head_dim = head_dim
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.alloc = PaAllocator(num_blocks, block_size, initial_free_order)
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        if pools is None:
+            tdt = TORCH_DTYPES[dtype]
+            pools = (torch.zeros(shape, dtype=tdt, device=self.device),
+                     torch.zeros(shape, dtype=tdt, device=self.device))
+        self.k_pool, self.v_pool = pools
+        if tuple(self.k_pool.shape) != shape or tuple(self.v_pool.shape) != shape:
+            raise ValueError(f"pools must be {shape}")
+
+    # ------------------------------------------------------------ sequences
+    def create(self) -> int:
+        return self.alloc.pa_seq_create()
+
+    def fork(self, seq: int) -> int:
+        return self.alloc.pa_seq_fork(seq)
+
+    def share_prefix(self, seq: int, n_tokens: int) -> int:
+        return self.alloc.pa_seq_share_prefix(seq, n_tokens)
+
+    def free(self, seq: int) -> None:
+        self.alloc.pa_seq_free(seq)
+
+    def reserve(self, seq: int, n_tokens: int):
+        """Host only: slots for the next n tokens of seq (and a CoW pair)."""
+        return self.alloc.pa_seq_append(seq, n_tokens)
+
+    # ------------------------------------------------------------ device work
+    def _dev(self, a: np.ndarray, dtype) -> torch.Tensor:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(self.device, dtype)
+
+    def write(self, k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor,
+              pairs: Optional[torch.Tensor] = None, stream=None) -> None:
+        """CoW copies first, then the cache write of the new tokens."""
+        if pairs is not None and pairs.shape[0] > 0:
+            pa_copy_blocks(self.k_pool, self.v_pool, pairs, stream)
+        if slots.shape[0] > 0:
+            pa_reshape_and_cache(k, v, slots, self.k_pool, self.v_pool, stream)
+
+    def write_host(self, k: torch.Tensor, v: torch.Tensor, slots: np.ndarray, pairs) -> None:
+        pr = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+        self.write(k, v, self._dev(slots, torch.int64), self._dev(pr, torch.int32))
+
+    def plan(self, seqs: Sequence[int], n_tokens: int = 1,
+             max_blocks: Optional[int] = None) -> StepPlan:
+        """Reserve n_tokens per sequence and upload the step's index arrays."""
+        seqs = [int(s) for s in seqs]
+        slots, pairs = self.alloc.pa_seq_append_batch(seqs, n_tokens)
+        lens = np.array([self.alloc.pa_seq_info(s)[0] for s in seqs], dtype=np.int32)
+        if max_blocks is None:
+            max_blocks = int(-(-int(lens.max(initial=0)) // self.block_size))
+        tables, lens = self.alloc.pa_build_tables(seqs, max(max_blocks, 1))
+        return StepPlan(seqs, self._dev(slots, torch.int64), self._dev(pairs, torch.int32),
+                        self._dev(tables, torch.int32), self._dev(lens, torch.int32),
+                        int(lens.max(initial=0)), lens)
+
+    def workspace(self, num_seqs: int, num_q_heads: int, max_context_len: int,
+                  partition_tokens: int = 0):
+        return alloc_workspace(num_seqs, num_q_heads, self.head_dim, max_context_len,
+                               partition_tokens, self.device)
+
+    def decode(self, plan: StepPlan, q: torch.Tensor, scale: float, out: torch.Tensor,
+               workspace: Optional[torch.Tensor], partition_tokens: int = 0, stream=None):
+        return pa_decode(q, self.k_pool, self.v_pool, plan.tables, plan.lens, scale, out,
+                         workspace, plan.max_context_len, partition_tokens, stream)
+
+    def run(self, plan: StepPlan, k_new, v_new, q, scale, out, workspace,
+            partition_tokens: int = 0, stream=None):
+        """The device half of a decode step: copies, cache write, attention."""
+        self.write(k_new, v_new, plan.slots, plan.pairs, stream)
+        return self.decode(plan, q, scale, out, workspace, partition_tokens, stream)

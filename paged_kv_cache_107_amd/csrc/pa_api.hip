@@ -1,0 +1,247 @@
+// C ABI of libpa: argument validation and dispatch for the decode, cache-write
+// and block-copy kernels.  Every check runs on the host before any launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kDefaultPartition = 512;
+constexpr int32_t kMaxPartition = 8192;
+constexpr int32_t kMaxGridYZ = 65535;
+
+std::atomic<int32_t> g_decode_path{PA_PATH_AUTO};
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int32_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+inline int32_t ilog2(int32_t x) {
+  int32_t r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+pa_status check_pool(const pa_pool_desc* pool) {
+  if (!pool) return PA_ERR_ARG;
+  if (pool->dtype != PA_F32 && pool->dtype != PA_F16 && pool->dtype != PA_BF16)
+    return PA_ERR_DTYPE;
+  if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0) return PA_ERR_ARG;
+  if (pool->block_size != 16 && pool->block_size != 32) return PA_ERR_SHAPE;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+inline int32_t max_parts_of(int32_t max_ctx, int32_t part_tokens) {
+  return max_ctx > 0 ? (max_ctx + part_tokens - 1) / part_tokens : 1;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace: (max, sum) pairs first, then the unnormalised outputs.
+size_t ws_ml_bytes(int32_t b, int32_t hq, int32_t parts) {
+  return align256((size_t)b * hq * parts * sizeof(float2));
+}
+size_t ws_o_bytes(int32_t b, int32_t hq, int32_t d, int32_t parts) {
+  return (size_t)b * hq * parts * d * sizeof(float);
+}
+
+struct Prepared {
+  pa::DecodeArgs args;
+  int32_t dtype;
+  int32_t head_dim;
+  bool use_mfma;
+};
+
+pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
+                         const pa_pool_desc* pool, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
+                         void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                         Prepared* pr) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || max_blocks_per_seq < 0 ||
+      max_context_len < 0)
+    return PA_ERR_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_ARG;
+  if (pool->num_kv_heads > kMaxGridYZ || num_q_heads > kMaxGridYZ) return PA_ERR_ARG;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int32_t group = num_q_heads / pool->num_kv_heads;
+  if (partition_tokens == 0) partition_tokens = kDefaultPartition;
+  if (partition_tokens < 16 || partition_tokens > kMaxPartition || partition_tokens % 16 != 0 ||
+      partition_tokens % pool->block_size != 0)
+    return PA_ERR_ARG;
+  const int32_t path = g_decode_path.load();
+  bool use_mfma;
+  if (path == PA_PATH_MFMA) {
+    if (!pa::mfma_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
+    use_mfma = true;
+  } else if (path == PA_PATH_VALU) {
+    if (!pa::valu_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
+    use_mfma = false;
+  } else {
+    use_mfma = group >= 2 && pa::mfma_supports(pool->dtype, pool->head_dim, group);
+    if (!use_mfma && !pa::valu_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
+  }
+  if (num_seqs == 0) {
+    *pr = Prepared{};
+    pr->args.num_seqs = 0;
+    return PA_OK;
+  }
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PA_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+    return PA_ERR_ARG;
+  const int32_t max_parts = max_parts_of(max_context_len, partition_tokens);
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim,
+                                                max_context_len, partition_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PA_ERR_ARG;
+
+  pa::DecodeArgs& a = pr->args;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws_ml = need ? static_cast<float2*>(workspace) : nullptr;
+  a.ws_o = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           ws_ml_bytes(num_seqs, num_q_heads, max_parts))
+                : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.num_blocks = pool->num_blocks;
+  a.log2_bs = ilog2(pool->block_size);
+  a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.part_tokens = partition_tokens;
+  a.max_parts = max_parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  pr->dtype = pool->dtype;
+  pr->head_dim = pool->head_dim;
+  pr->use_mfma = use_mfma;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return kAbiVersion; }
+
+const char* pa_status_string(int32_t s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_ARG: return "PA_ERR_ARG";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE";
+    case PA_ERR_OOM: return "PA_ERR_OOM";
+    case PA_ERR_REFCOUNT: return "PA_ERR_REFCOUNT";
+    case PA_ERR_NOT_FOUND: return "PA_ERR_NOT_FOUND";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+int32_t pa_set_decode_path(int32_t path) {
+  if (path != PA_PATH_AUTO && path != PA_PATH_VALU && path != PA_PATH_MFMA) return -1;
+  return g_decode_path.exchange(path);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  if (partition_tokens == 0) partition_tokens = kDefaultPartition;
+  if (partition_tokens <= 0) return 0;
+  const int32_t parts = max_parts_of(max_context_len, partition_tokens);
+  if (parts <= 1) return 0;
+  return ws_ml_bytes(num_seqs, num_q_heads, parts) +
+         ws_o_bytes(num_seqs, num_q_heads, head_dim, parts);
+}
+
+pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_pool,
+                              const pa_pool_desc* pool, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                              float scale, void* out, void* workspace, size_t workspace_bytes,
+                              int32_t partition_tokens, void* hip_stream) {
+  Prepared pr;
+  pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                                context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
+                                workspace, workspace_bytes, partition_tokens, &pr);
+  if (st != PA_OK || pr.args.num_seqs == 0) return st;
+  return pa::launch_decode_partition(pr.args, pr.dtype, pr.head_dim, pr.use_mfma,
+                                     static_cast<hipStream_t>(hip_stream));
+}
+
+pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool,
+                           const pa_pool_desc* pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                           float scale, void* out, void* workspace, size_t workspace_bytes,
+                           int32_t partition_tokens, void* hip_stream) {
+  Prepared pr;
+  pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                                context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
+                                workspace, workspace_bytes, partition_tokens, &pr);
+  if (st != PA_OK || pr.args.num_seqs == 0 || pr.args.max_parts <= 1) return st;
+  return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim,
+                                  static_cast<hipStream_t>(hip_stream));
+}
+
+pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const pa_pool_desc* pool, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
+                    void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                    void* hip_stream) {
+  Prepared pr;
+  pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                                context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
+                                workspace, workspace_bytes, partition_tokens, &pr);
+  if (st != PA_OK || pr.args.num_seqs == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  st = pa::launch_decode_partition(pr.args, pr.dtype, pr.head_dim, pr.use_mfma, s);
+  if (st != PA_OK || pr.args.max_parts <= 1) return st;
+  return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim, s);
+}
+
+pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
+                               int32_t num_tokens, void* k_pool, void* v_pool,
+                               const pa_pool_desc* pool, void* hip_stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PA_ERR_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+    return PA_ERR_ARG;
+  return pa::launch_reshape_and_cache(k, v, slot_mapping, num_tokens, k_pool, v_pool, *pool,
+                                      static_cast<hipStream_t>(hip_stream));
+}
+
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool,
+                         const int32_t* pairs, int32_t num_pairs, void* hip_stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0 || num_pairs > kMaxGridYZ) return PA_ERR_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !pairs) return PA_ERR_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || (reinterpret_cast<uintptr_t>(pairs) & 3u))
+    return PA_ERR_ARG;
+  return pa::launch_copy_blocks(k_pool, v_pool, *pool, pairs, num_pairs,
+                                static_cast<hipStream_t>(hip_stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// KV-pool writes of the paged cache (gfx950): the new-token cache write and
+// the copy-on-write block copy.  Both move raw 16-byte chunks (bit-exact).
+//
+//  * reshape_and_cache: decode appends the new token's K/V ("Lazy Allocation
+//    与 Copy-on-Write 在 LLM 推理系统中的应用", section 2.1) into the slot the
+//    block table gives (physical block slot / BS, offset slot % BS: "放下账簿，
+//    打开源码", section "PagedAttention：虚实分离，按需取用").  One thread per
+//    16-byte chunk of a (token, kv head) row; consecutive threads read
+//    consecutive input bytes and write one contiguous pool row.
+//  * copy_blocks: a writer's private copy of a shared block before its first
+//    write ("Lazy Allocation 与 Copy-on-Write ...", section 4.4).  A block is
+//    Hkv x BS rows, contiguous in the pool; each workgroup streams a slice of
+//    one block of one pool.
+#include <hip/hip_runtime.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, const int64_t* __restrict__ slots,
+    int64_t total_chunks, int32_t chunks_per_token, int32_t chunks_per_row, int32_t num_kv_heads,
+    int32_t block_size, int64_t num_slots, u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total_chunks) return;
+  const int64_t t = idx / chunks_per_token;
+  const int32_t c = (int32_t)(idx - t * chunks_per_token);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int32_t h = c / chunks_per_row, cc = c - h * chunks_per_row;
+  const int64_t blk = slot / block_size, off = slot - blk * block_size;
+  const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * chunks_per_row + cc;
+  k_pool[dst] = k[idx];
+  v_pool[dst] = v[idx];
+}
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_pool,
+                                                          u32x4* __restrict__ v_pool,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int32_t num_blocks,
+                                                          int64_t chunks_per_block) {
+  const int32_t pr = blockIdx.y;
+  const int32_t src = pairs[2 * pr], dst = pairs[2 * pr + 1];
+  if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
+  u32x4* pool = blockIdx.z == 0 ? k_pool : v_pool;
+  const u32x4* s = pool + (int64_t)src * chunks_per_block;
+  u32x4* d = pool + (int64_t)dst * chunks_per_block;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks_per_block;
+       c += (int64_t)gridDim.x * blockDim.x)
+    d[c] = s[c];
+}
+
+static int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+pa_status launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
+                                   int32_t num_tokens, void* k_pool, void* v_pool,
+                                   const pa_pool_desc& pool, hipStream_t st) {
+  if (num_tokens == 0) return PA_OK;
+  const int32_t chunks_per_row = pool.head_dim * elem_bytes(pool.dtype) / 16;
+  const int32_t chunks_per_token = chunks_per_row * pool.num_kv_heads;
+  const int64_t total = (int64_t)num_tokens * chunks_per_token;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return PA_ERR_ARG;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots, total,
+                     chunks_per_token, chunks_per_row, pool.num_kv_heads, pool.block_size,
+                     (int64_t)pool.num_blocks * pool.block_size, static_cast<u32x4*>(k_pool),
+                     static_cast<u32x4*>(v_pool));
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status launch_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc& pool,
+                             const int32_t* pairs, int32_t num_pairs, hipStream_t st) {
+  if (num_pairs == 0) return PA_OK;
+  const int64_t chunks_per_block = (int64_t)pool.num_kv_heads * pool.block_size * pool.head_dim *
+                                   elem_bytes(pool.dtype) / 16;
+  const int64_t slices = (chunks_per_block + 255) / 256;
+  const unsigned gx = (unsigned)(slices < 64 ? slices : 64);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, (unsigned)num_pairs, 2), dim3(256), 0, st,
+                     static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), pairs,
+                     pool.num_blocks, chunks_per_block);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace pa

@@ -1,0 +1,568 @@
+// Paged decode attention for gfx950.
+//
+// The attention formula is plain scaled dot-product attention; paging only
+// changes where K/V rows live, so the kernel follows the block table to each
+// physical block (page "vLLM：把 KV 缓存当成虚拟内存", sections "破除误解" and
+// "KV 的体积从哪来，页表如何把它切开": loop over blocks doing the Q x K/V
+// multiply-adds, then reduce across blocks; page "放下账簿，打开源码", section
+// "注意力计算的改写", whose block-loop sketch is completed here with a running
+// maximum and rescaling, i.e. an online softmax).
+//
+// Work split: one workgroup (4 waves) per (sequence, kv head, partition of
+// part_tokens positions).  A partition is cut into 16-token tiles; wave w
+// takes tiles w, w+4, ...  Each tile is one 16-token run of one physical
+// block (a block of 32 tokens is two tiles), so the block-table entry is read
+// once per tile, as a scalar load, one tile ahead of its use.
+//
+// Two tile kernels:
+//  * MFMA (16-bit pools, head_dim 128, G = Hq/Hkv >= 2): the G query heads of
+//    a kv head share every K row, so S^T = K_tile (16 x 128) . Q^T (128 x G)
+//    is a small dense contraction: four v_mfma_f32_16x16x32 per tile with the
+//    G heads in the 16 columns.  The P.V product runs on the matrix cores too
+//    (O^T = V^T . P^T, eight v_mfma_f32_16x16x16 per tile): the S^T result
+//    layout is exactly the B operand layout, and V's A operand is assembled
+//    from the same 16-byte row loads with byte permutes.  Softmax state stays
+//    per lane: each lane's column is one query head.
+//  * VALU (every dtype, head_dim 64/128, G <= 8): lanes along head_dim, 16
+//    bytes per lane per row, dot products reduced across the row's lanes with
+//    DPP, online softmax per head in registers.
+// Both keep K/V tiles in registers: the MFMA operand layouts and the VALU row
+// layout are fed straight from coalesced 16-byte global loads.
+//
+// Split-K: a sequence with one partition is normalised and written to `out`
+// by its workgroup.  Otherwise each partition writes (m, l, o) -- running max
+// (log2 units), sum of exp2(s - m) and the unnormalised output -- and
+// decode_reduce merges them: M = max m_p, out = sum 2^(m_p-M) o_p /
+// sum 2^(m_p-M) l_p.
+#include <hip/hip_runtime.h>
+
+#include "pa.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTile = 16;  // tokens per tile
+
+__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int i) {
+  int ctx = a.context_lens[i];
+  ctx = min(ctx, a.max_ctx);
+  ctx = min(ctx, a.max_blocks << a.log2_bs);
+  return ctx;
+}
+
+__device__ __forceinline__ int num_parts(const DecodeArgs& a, int ctx) {
+  return ctx > 0 ? (ctx + a.part_tokens - 1) / a.part_tokens : 1;
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ----------------------------------------------------------------- epilogue
+// LDS layout of the per-wave partial states: m[4][16], l[4][16], then
+// o[4][G][D + 4] (row padding staggers banks).
+template <int D>
+__host__ __device__ constexpr int o_stride() { return D + 4; }
+
+template <int D>
+size_t merge_smem_bytes(int group) {
+  return (2 * kWaves * 16 + (size_t)kWaves * group * o_stride<D>()) * sizeof(float);
+}
+
+// Merge the four waves' states of head h (log2-domain max) and store either
+// the normalised output or the partition's (m, l, o) for the reduce pass.
+template <class E, int D>
+__device__ void combine_store(const DecodeArgs& a, const float* smem, int group, int i, int g,
+                              int p, int n_parts) {
+  const float* sm_m = smem;
+  const float* sm_l = smem + kWaves * 16;
+  const float* sm_o = smem + 2 * kWaves * 16;
+  for (int idx = threadIdx.x; idx < group * D; idx += kThreads) {
+    const int h = idx / D, d = idx % D;
+    float M = sm_m[h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + h]);
+    float L = 0.f, O = 0.f;
+    if (M != neg_inf()) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = fast_exp2(sm_m[w * 16 + h] - M);
+        L += wt * sm_l[w * 16 + h];
+        O += wt * sm_o[((size_t)w * group + h) * o_stride<D>() + d];
+      }
+    }
+    const size_t row = (size_t)i * a.num_q_heads + (size_t)g * group + h;
+    if (n_parts == 1) {
+      const float y = L > 0.f ? O / L : 0.f;
+      reinterpret_cast<typename E::storage*>(a.out)[row * D + d] =
+          (typename E::storage)float_to_bits(E{}, y);
+    } else {
+      a.ws_o[(row * a.max_parts + p) * D + d] = O;
+      if (d == 0) a.ws_ml[row * a.max_parts + p] = make_float2(M, L);
+    }
+  }
+}
+
+template <class E, int D>
+__device__ void store_zero_rows(const DecodeArgs& a, int group, int i, int g) {
+  for (int idx = threadIdx.x; idx < group * D; idx += kThreads) {
+    const size_t row = (size_t)i * a.num_q_heads + (size_t)g * group + idx / D;
+    reinterpret_cast<typename E::storage*>(a.out)[row * D + idx % D] = 0;
+  }
+}
+
+// ----------------------------------------------------------------- MFMA path
+template <class E>
+struct Mfma;
+
+template <>
+struct Mfma<BF16> {
+  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 v, u32x2 p, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v),
+                                                     __builtin_bit_cast(i16x4, p), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t round16(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+};
+
+template <>
+struct Mfma<F16> {
+  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                  __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 v, u32x2 p, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v),
+                                                 __builtin_bit_cast(f16x4, p), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t round16(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+};
+
+// Lane roles in a tile (c16 = lane % 16, g4 = lane / 16):
+//  QK  A = K tile:   lane holds K[row c16][32 s + 8 g4 .. +7]   for k-step s = 0..3
+//      B = Q^T:      lane holds q[head c16][32 s + 8 g4 .. +7]  (zero for c16 >= G)
+//      S^T out:      lane holds S[token 4 g4 + r][head c16], r = 0..3
+//  PV  A_e = V^T:    lane holds V[token 4 g4 + r][8 c16 + e], r = 0..3 (e = 0..7)
+//      B = P^T:      lane holds P[head c16][token 4 g4 + r]  (= S^T out layout)
+//      O^T_e out:    lane holds O[head c16][32 g4 + 8 r + e], r = 0..3
+// so a lane keeps 32 output values of its own head, and the softmax rescale
+// needs no cross-lane traffic.
+template <class E>
+__global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) {
+  constexpr int D = 128;
+  extern __shared__ float smem[];
+  const int p = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+  const int ctx = clamp_ctx(a, i);
+  const int n_parts = num_parts(a, ctx);
+  if (p >= n_parts) return;
+  const int G = a.group;
+  if (ctx <= 0) {
+    store_zero_rows<E, D>(a, G, i, g);
+    return;
+  }
+  const int lane = threadIdx.x % kWave, w = wave_id();
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int t0 = p * a.part_tokens;
+  const int ntok = min(a.part_tokens, ctx - t0);
+  const int ntiles = (ntok + kTile - 1) / kTile;
+  const int bs_mask = (1 << a.log2_bs) - 1;
+
+  using S = typename E::storage;
+  u32x4 qv[4];
+  {
+    const S* qrow = reinterpret_cast<const S*>(a.q) +
+                    ((size_t)i * a.num_q_heads + (size_t)g * G + c16) * D + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qv[s] = c16 < G ? load16(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+  }
+  const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
+  const size_t head_stride = (size_t)D << a.log2_bs;
+  const size_t block_stride = head_stride * a.num_kv_heads;
+  const S* kbase = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride + c16 * D + 8 * g4;
+  const S* vbase = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride +
+                   (4 * g4) * D + 8 * c16;
+
+  // Loads tile j's K and V rows; false (nothing loaded) for a bad block id.
+  auto load_tile = [&](int j, u32x4 (&kr)[4], u32x4 (&vr)[4]) -> bool {
+    const int tok = t0 + kTile * j;
+    const int blk = table[tok >> a.log2_bs];
+    if ((unsigned)blk >= (unsigned)a.num_blocks) return false;
+    const size_t off = (size_t)blk * block_stride + (size_t)(tok & bs_mask) * D;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kr[s] = load16(kbase + off + 32 * s);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vr[r] = load16(vbase + off + r * D);
+    return true;
+  };
+
+  float m = neg_inf(), l = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int j = w;
+  u32x4 kc[4], vc[4];
+  bool okc = j < ntiles && load_tile(j, kc, vc);
+  for (; j < ntiles; j += kWaves) {
+    u32x4 kn[4], vn[4];
+    bool okn = false;
+    if (j + kWaves < ntiles) okn = load_tile(j + kWaves, kn, vn);
+    if (okc) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s = Mfma<E>::qk(kc[t], qv[t], s);
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = s[r] * a.scale_log2;
+      const int valid = ntok - kTile * j;
+      if (valid < kTile) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (4 * g4 + r >= valid) {
+            sv[r] = neg_inf();
+            vc[r] = u32x4{0, 0, 0, 0};  // slots past the sequence may hold anything
+          }
+        }
+      }
+      float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mt = fmaxf(mt, shfl_xor(mt, 16));
+      mt = fmaxf(mt, shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mn);
+      uint32_t pb[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pb[r] = Mfma<E>::round16(fast_exp2(sv[r] - mn));
+        psum += bits_to_float(E{}, pb[r]);  // the weights the P.V product uses
+      }
+      l = l * alpha + psum;
+      m = mn;
+      const u32x2 pw = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const u32x2 vw = {__builtin_amdgcn_perm(vc[1][e >> 1], vc[0][e >> 1], sel),
+                          __builtin_amdgcn_perm(vc[3][e >> 1], vc[2][e >> 1], sel)};
+        o[e] = Mfma<E>::pv(vw, pw, o[e] * alpha);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      kc[t] = kn[t];
+      vc[t] = vn[t];
+    }
+    okc = okn;
+  }
+
+  // wave state -> LDS
+  l = across_groups_sum<16>(l);
+  float* sm_m = smem;
+  float* sm_l = smem + kWaves * 16;
+  float* sm_o = smem + 2 * kWaves * 16;
+  if (c16 < G) {
+    if (g4 == 0) {
+      sm_m[w * 16 + c16] = m;
+      sm_l[w * 16 + c16] = l;
+    }
+    float* dst = sm_o + ((size_t)w * G + c16) * o_stride<D>() + 32 * g4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<f32x4*>(dst + 8 * r) = f32x4{o[0][r], o[1][r], o[2][r], o[3][r]};
+      *reinterpret_cast<f32x4*>(dst + 8 * r + 4) = f32x4{o[4][r], o[5][r], o[6][r], o[7][r]};
+    }
+  }
+  __syncthreads();
+  combine_store<E, D>(a, smem, G, i, g, p, n_parts);
+}
+
+// ----------------------------------------------------------------- VALU path
+// Lanes along head_dim: a K/V row of D elements is LPR lanes x 16 bytes; one
+// 16-byte load per lane covers RPL rows; a 16-token tile is LPT loads.
+template <class E, int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) {
+  constexpr int EB = E::bytes;
+  constexpr int EPL = 16 / EB;
+  constexpr int LPR = D * EB / 16;
+  constexpr int RPL = kWave / LPR;
+  constexpr int LPT = kTile / RPL;
+  extern __shared__ float smem[];
+  const int p = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+  const int ctx = clamp_ctx(a, i);
+  const int n_parts = num_parts(a, ctx);
+  if (p >= n_parts) return;
+  if (ctx <= 0) {
+    store_zero_rows<E, D>(a, G, i, g);
+    return;
+  }
+  const int lane = threadIdx.x % kWave, w = wave_id();
+  const int r0 = lane / LPR, cl = lane % LPR;
+  const int t0 = p * a.part_tokens;
+  const int ntok = min(a.part_tokens, ctx - t0);
+  const int ntiles = (ntok + kTile - 1) / kTile;
+  const int bs_mask = (1 << a.log2_bs) - 1;
+
+  using S = typename E::storage;
+  float qf[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const S* qrow = reinterpret_cast<const S*>(a.q) +
+                    ((size_t)i * a.num_q_heads + (size_t)g * G + h) * D + cl * EPL;
+    const u32x4 c = load16(qrow);
+    const uint4 cu = {c[0], c[1], c[2], c[3]};
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[h][e] = chunk_elem(E{}, cu, e) * a.scale_log2;
+  }
+  const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
+  const size_t head_stride = (size_t)D << a.log2_bs;
+  const size_t block_stride = head_stride * a.num_kv_heads;
+  const S* kbase = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride + r0 * D + cl * EPL;
+  const S* vbase = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride + r0 * D + cl * EPL;
+
+  auto load_tile = [&](int j, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) -> bool {
+    const int tok = t0 + kTile * j;
+    const int blk = table[tok >> a.log2_bs];
+    if ((unsigned)blk >= (unsigned)a.num_blocks) return false;
+    const size_t off = (size_t)blk * block_stride + (size_t)(tok & bs_mask) * D;
+#pragma unroll
+    for (int k = 0; k < LPT; ++k) {
+      const u32x4 x = load16(kbase + off + (size_t)k * RPL * D);
+      const u32x4 y = load16(vbase + off + (size_t)k * RPL * D);
+      kr[k] = uint4{x[0], x[1], x[2], x[3]};
+      vr[k] = uint4{y[0], y[1], y[2], y[3]};
+    }
+    return true;
+  };
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = neg_inf();
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  int j = w;
+  uint4 kc[LPT], vc[LPT];
+  bool okc = j < ntiles && load_tile(j, kc, vc);
+  for (; j < ntiles; j += kWaves) {
+    uint4 kn[LPT], vn[LPT];
+    bool okn = false;
+    if (j + kWaves < ntiles) okn = load_tile(j + kWaves, kn, vn);
+    if (okc) {
+      const int valid = ntok - kTile * j;
+      float s[G][LPT];
+#pragma unroll
+      for (int k = 0; k < LPT; ++k) {
+        float kf[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) kf[e] = chunk_elem(E{}, kc[k], e);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) part = fmaf(qf[h][e], kf[e], part);
+          s[h][k] = group_sum<LPR>(part);
+        }
+      }
+      if (valid < kTile) {
+#pragma unroll
+        for (int k = 0; k < LPT; ++k) {
+          if (k * RPL + r0 >= valid) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) s[h][k] = neg_inf();
+            vc[k] = uint4{0, 0, 0, 0};
+          }
+        }
+      }
+      float vf[LPT][EPL];
+#pragma unroll
+      for (int k = 0; k < LPT; ++k)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[k][e] = chunk_elem(E{}, vc[k], e);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mt = s[h][0];
+#pragma unroll
+        for (int k = 1; k < LPT; ++k) mt = fmaxf(mt, s[h][k]);
+        mt = across_groups_max<LPR>(mt);
+        const float mn = fmaxf(m[h], mt);
+        const float alpha = fast_exp2(m[h] - mn);
+        m[h] = mn;
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+#pragma unroll
+        for (int k = 0; k < LPT; ++k) {
+          const float pk = fast_exp2(s[h][k] - mn);
+          l[h] += pk;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pk, vf[k][e], acc[h][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < LPT; ++k) {
+      kc[k] = kn[k];
+      vc[k] = vn[k];
+    }
+    okc = okn;
+  }
+
+  float* sm_m = smem;
+  float* sm_l = smem + kWaves * 16;
+  float* sm_o = smem + 2 * kWaves * 16;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l[h] = across_groups_sum<LPR>(l[h]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = across_groups_sum<LPR>(acc[h][e]);
+  }
+  if (r0 == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (cl == 0) {
+        sm_m[w * 16 + h] = m[h];
+        sm_l[w * 16 + h] = l[h];
+      }
+      float* dst = sm_o + ((size_t)w * G + h) * o_stride<D>() + cl * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dst[e] = acc[h][e];
+    }
+  }
+  __syncthreads();
+  combine_store<E, D>(a, smem, G, i, g, p, n_parts);
+}
+
+// ----------------------------------------------------------------- reduce
+template <class E, int D>
+__global__ __launch_bounds__(kWave) void decode_reduce(DecodeArgs a) {
+  const int h = blockIdx.x, i = blockIdx.y;
+  const int ctx = clamp_ctx(a, i);
+  const int n_parts = num_parts(a, ctx);
+  if (n_parts <= 1) return;
+  const int lane = threadIdx.x;
+  const size_t row = (size_t)i * a.num_q_heads + h;
+  const float2* ml = a.ws_ml + row * a.max_parts;
+  const float* wo = a.ws_o + row * a.max_parts * D;
+  float M = neg_inf();
+  for (int q = lane; q < n_parts; q += kWave) M = fmaxf(M, ml[q].x);
+  M = wave_max(M);
+  float L = 0.f;
+  if (M != neg_inf())
+    for (int q = lane; q < n_parts; q += kWave) L += fast_exp2(ml[q].x - M) * ml[q].y;
+  L = wave_sum(L);
+  constexpr int PER = D / kWave;
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  if (L > 0.f) {
+    for (int q = 0; q < n_parts; ++q) {
+      const float2 s = ml[q];
+      const float wt = fast_exp2(s.x - M);
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] = fmaf(wt, wo[(size_t)q * D + lane * PER + k], acc[k]);
+    }
+  }
+  auto* out = reinterpret_cast<typename E::storage*>(a.out) + row * D + lane * PER;
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    out[k] = (typename E::storage)float_to_bits(E{}, L > 0.f ? acc[k] / L : 0.f);
+}
+
+// ----------------------------------------------------------------- launchers
+namespace {
+
+template <class E, int D, int G>
+pa_status launch_valu(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_partition_valu<E, D, G>), grid, dim3(kThreads),
+                     merge_smem_bytes<D>(G), st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+template <class E, int D>
+pa_status launch_valu_g(const DecodeArgs& a, hipStream_t st) {
+  switch (a.group) {
+    case 1: return launch_valu<E, D, 1>(a, st);
+    case 2: return launch_valu<E, D, 2>(a, st);
+    case 4: return launch_valu<E, D, 4>(a, st);
+    case 8: return launch_valu<E, D, 8>(a, st);
+    default: return PA_ERR_SHAPE;
+  }
+}
+
+template <class E>
+pa_status launch_valu_d(const DecodeArgs& a, int head_dim, hipStream_t st) {
+  return head_dim == 64 ? launch_valu_g<E, 64>(a, st) : launch_valu_g<E, 128>(a, st);
+}
+
+template <class E>
+pa_status launch_mfma(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_partition_mfma<E>), grid, dim3(kThreads),
+                     merge_smem_bytes<128>(a.group), st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+template <class E, int D>
+pa_status launch_reduce(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.num_q_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_reduce<E, D>), grid, dim3(kWave), 0, st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+bool mfma_supports(int dtype, int head_dim, int group) {
+  return (dtype == PA_F16 || dtype == PA_BF16) && head_dim == 128 && group >= 1 && group <= 16;
+}
+
+bool valu_supports(int /*dtype*/, int head_dim, int group) {
+  return (head_dim == 64 || head_dim == 128) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+pa_status launch_decode_partition(const DecodeArgs& a, int dtype, int head_dim, bool use_mfma,
+                                  hipStream_t st) {
+  if (use_mfma) {
+    if (dtype == PA_BF16) return launch_mfma<BF16>(a, st);
+    if (dtype == PA_F16) return launch_mfma<F16>(a, st);
+    return PA_ERR_SHAPE;
+  }
+  switch (dtype) {
+    case PA_F32: return launch_valu_d<F32>(a, head_dim, st);
+    case PA_F16: return launch_valu_d<F16>(a, head_dim, st);
+    case PA_BF16: return launch_valu_d<BF16>(a, head_dim, st);
+    default: return PA_ERR_DTYPE;
+  }
+}
+
+pa_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t st) {
+  const bool d64 = head_dim == 64;
+  switch (dtype) {
+    case PA_F32: return d64 ? launch_reduce<F32, 64>(a, st) : launch_reduce<F32, 128>(a, st);
+    case PA_F16: return d64 ? launch_reduce<F16, 64>(a, st) : launch_reduce<F16, 128>(a, st);
+    case PA_BF16: return d64 ? launch_reduce<BF16, 64>(a, st) : launch_reduce<BF16, 128>(a, st);
+    default: return PA_ERR_DTYPE;
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,127 @@
+// Device-side helpers shared by the libpa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------- element types
+// Storage types: the kernels move raw bits and convert explicitly.
+struct F32 {
+  using storage = uint32_t;
+  static constexpr int bytes = 4;
+};
+struct F16 {
+  using storage = uint16_t;
+  static constexpr int bytes = 2;
+};
+struct BF16 {
+  using storage = uint16_t;
+  static constexpr int bytes = 2;
+};
+
+__device__ __forceinline__ float bits_to_float(F32, uint32_t b) { return __uint_as_float(b); }
+__device__ __forceinline__ float bits_to_float(F16, uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+__device__ __forceinline__ float bits_to_float(BF16, uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> element bits, round to nearest even.
+__device__ __forceinline__ uint32_t float_to_bits(F32, float x) { return __float_as_uint(x); }
+__device__ __forceinline__ uint32_t float_to_bits(F16, float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ uint32_t float_to_bits(BF16, float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two 16-bit elements of a 32-bit word as floats.
+template <class E>
+__device__ __forceinline__ float lo16(E e, uint32_t w) { return bits_to_float(e, w & 0xFFFFu); }
+template <class E>
+__device__ __forceinline__ float hi16(E e, uint32_t w) { return bits_to_float(e, w >> 16); }
+
+// Element `i` of a 16-byte chunk (4 words) as float.
+template <class E>
+__device__ __forceinline__ float chunk_elem(E e, const uint4& c, int i) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  if constexpr (E::bytes == 4) {
+    return bits_to_float(e, w[i]);
+  } else {
+    return (i & 1) ? hi16(e, w[i >> 1]) : lo16(e, w[i >> 1]);
+  }
+}
+
+// ------------------------------------------------------------- math
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+// ------------------------------------------------------------- cross-lane
+// DPP controls (gfx9): quad_perm, row_mirror, row_half_mirror.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, kWave); }
+
+// Sum over groups of N consecutive lanes (N = 8, 16, 32 or 64); every lane of
+// a group ends with the group total.  Within a row of 16 the butterfly uses
+// DPP: two quad exchanges, then the half-row and row mirrors pair each lane
+// with a lane of the other half.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (N >= 32) x += shfl_xor(x, 16);
+  if constexpr (N >= 64) x += shfl_xor(x, 32);
+  return x;
+}
+
+// Max / sum across lanes whose index differs only in bits >= log2(STRIDE)
+// (i.e. over the 64 / STRIDE groups, lane-position-wise).
+template <int STRIDE>
+__device__ __forceinline__ float across_groups_max(float x) {
+#pragma unroll
+  for (int m = STRIDE; m < kWave; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
+  return x;
+}
+template <int STRIDE>
+__device__ __forceinline__ float across_groups_sum(float x) {
+#pragma unroll
+  for (int m = STRIDE; m < kWave; m <<= 1) x += shfl_xor(x, m);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  x = fmaxf(x, shfl_xor(x, 16));
+  x = fmaxf(x, shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+
+// Wave index as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+}  // namespace pa

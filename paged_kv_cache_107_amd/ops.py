@@ -1,0 +1,144 @@
+"""Python binding of the libpa kernels: torch tensors in, C ABI calls out.
+
+Each function has the name of the C entry point it calls and only marshals
+arguments (shapes, dtypes, device pointers, the current HIP stream); every
+step runs in the HIP kernels.  PyTorch provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import torch
+
+from ._lib import (PA_BF16, PA_F16, PA_F32, check, lib, pa_pool_desc)
+
+_DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> C.c_void_p:
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need_cuda(name: str, t: torch.Tensor, dtype=None, contiguous=True) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pool_desc(k_pool: torch.Tensor) -> pa_pool_desc:
+    """Descriptor of a [num_blocks][num_kv_heads][block_size][head_dim] pool."""
+    if k_pool.dim() != 4:
+        raise ValueError("pools are [num_blocks][num_kv_heads][block_size][head_dim]")
+    if k_pool.dtype not in _DTYPES:
+        raise ValueError(f"unsupported pool dtype {k_pool.dtype}")
+    nb, hkv, bs, d = k_pool.shape
+    return pa_pool_desc(nb, bs, hkv, d, _DTYPES[k_pool.dtype])
+
+
+def _check_pools(k_pool, v_pool):
+    _need_cuda("k_pool", k_pool)
+    _need_cuda("v_pool", v_pool, k_pool.dtype)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape")
+    return pool_desc(k_pool)
+
+
+def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                              max_context_len: int, partition_tokens: int = 0) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                               max_context_len, partition_tokens))
+
+
+def alloc_workspace(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0,
+                    device="cuda"):
+    """A workspace tensor sized for pa_decode (None when none is needed)."""
+    n = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                  partition_tokens)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _decode_call(fn_name, q, k_pool, v_pool, block_tables, context_lens, scale, out,
+                 workspace, max_context_len, partition_tokens, stream):
+    desc = _check_pools(k_pool, v_pool)
+    _need_cuda("q", q, k_pool.dtype)
+    _need_cuda("out", out, k_pool.dtype)
+    _need_cuda("block_tables", block_tables, torch.int32)
+    _need_cuda("context_lens", context_lens, torch.int32)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs][num_q_heads][head_dim]")
+    b, hq, _ = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or context_lens.shape != (b,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    ws_bytes = 0
+    if workspace is not None:
+        _need_cuda("workspace", workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    fn = getattr(lib(), fn_name)
+    st = fn(_ptr(q), _ptr(k_pool), _ptr(v_pool), C.byref(desc), _ptr(block_tables),
+            int(block_tables.shape[1]), _ptr(context_lens), int(b), int(hq),
+            int(max_context_len), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+            int(partition_tokens), _stream(stream))
+    check(fn_name, st)
+    return out
+
+
+def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
+              max_context_len, partition_tokens=0, stream=None):
+    """Paged decode attention (partition + reduce).  See pa.h."""
+    return _decode_call("pa_decode", q, k_pool, v_pool, block_tables, context_lens, scale, out,
+                        workspace, max_context_len, partition_tokens, stream)
+
+
+def pa_decode_partition(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
+                        max_context_len, partition_tokens=0, stream=None):
+    return _decode_call("pa_decode_partition", q, k_pool, v_pool, block_tables, context_lens,
+                        scale, out, workspace, max_context_len, partition_tokens, stream)
+
+
+def pa_decode_reduce(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
+                     max_context_len, partition_tokens=0, stream=None):
+    return _decode_call("pa_decode_reduce", q, k_pool, v_pool, block_tables, context_lens,
+                        scale, out, workspace, max_context_len, partition_tokens, stream)
+
+
+def pa_set_decode_path(path: int) -> int:
+    prev = int(lib().pa_set_decode_path(int(path)))
+    if prev < 0:
+        raise ValueError(f"bad decode path {path}")
+    return prev
+
+
+def pa_reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None):
+    """Write new tokens' K/V ([T][Hkv][D]) into their slots.  See pa.h."""
+    desc = _check_pools(k_pool, v_pool)
+    _need_cuda("k", k, k_pool.dtype)
+    _need_cuda("v", v, k_pool.dtype)
+    _need_cuda("slot_mapping", slot_mapping, torch.int64)
+    t = slot_mapping.shape[0]
+    shape = (t, desc.num_kv_heads, desc.head_dim)
+    if tuple(k.shape) != shape or tuple(v.shape) != shape:
+        raise ValueError(f"k and v must be {shape}")
+    st = lib().pa_reshape_and_cache(_ptr(k), _ptr(v), _ptr(slot_mapping), int(t), _ptr(k_pool),
+                                    _ptr(v_pool), C.byref(desc), _stream(stream))
+    check("pa_reshape_and_cache", st)
+
+
+def pa_copy_blocks(k_pool, v_pool, pairs, stream=None):
+    """Copy whole blocks src -> dst for each (src, dst) row of pairs ([P][2] int32)."""
+    desc = _check_pools(k_pool, v_pool)
+    _need_cuda("pairs", pairs, torch.int32)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [num_pairs][2]")
+    st = lib().pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), C.byref(desc), _ptr(pairs),
+                              int(pairs.shape[0]), _stream(stream))
+    check("pa_copy_blocks", st)

@@ -1,0 +1,294 @@
+"""HIP path against the oracle on the GPU, through the C ABI.
+
+Bit-exact: pools after every cache write and CoW copy, the step's slots and
+copy pairs, block tables, lengths, allocator free pool and refcounts.
+Tolerance (max-abs error of the decode output): 1e-5 for fp32 inputs and
+2e-2 for fp16/bf16 inputs, with fp32 accumulation.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from _scenario import KV, TOL, from_device_bits, max_abs_err, run_gpu, run_oracle, to_device, to_f64
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # the CPU suite deselects these; never a fallback
+    pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="needs a GPU")]
+
+import paged_kv_cache_107_amd as pa  # noqa: E402
+
+
+def compare_state(o, g, d):
+    wl = d.wl
+    cache = g["cache"]
+    assert np.array_equal(from_device_bits(cache.k_pool, wl.dtype), o["kp"]), "k_pool differs"
+    assert np.array_equal(from_device_bits(cache.v_pool, wl.dtype), o["vp"]), "v_pool differs"
+    free, rc = cache.alloc.pa_alloc_query()
+    assert free.tolist() == list(o["alloc"].free)
+    assert rc.tolist() == o["alloc"].refcount
+    assert g["plan"].slots.cpu().tolist() == o["step_slots"]
+    assert [tuple(p) for p in g["plan"].pairs.cpu().tolist()] == o["step_pairs"]
+    t = g["plan"].tables.cpu().numpy()
+    w = o["tables"].shape[1]
+    assert np.array_equal(t[:, :w], o["tables"]) and np.all(t[:, w:] == -1)
+    assert np.array_equal(g["plan"].lens.cpu().numpy(), o["lens"])
+
+
+def check_case(d, partition_tokens=0, nan_fill=False, state=True):
+    kv = KV(d)
+    o = run_oracle(d, kv, nan_fill=nan_fill)
+    g = run_gpu(d, kv, nan_fill=nan_fill, partition_tokens=partition_tokens)
+    if state:
+        compare_state(o, g, d)
+    err = max_abs_err(g["out"], o["out"])
+    print(f"{d.wl.name} B={d.batch} ctx_max={int(d.context_lens.max())} "
+          f"pt={partition_tokens} max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL[d.wl.dtype], err
+    return o, g
+
+
+@pytest.fixture
+def decode_path():
+    prev = pa.pa_set_decode_path(pa.PA_PATH_AUTO)
+    yield lambda p: pa.pa_set_decode_path(p)
+    pa.pa_set_decode_path(prev)
+
+
+# ------------------------------------------------------------ cache write / copy
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("bs,d", [(16, 128), (32, 64)])
+def test_reshape_and_cache_bitexact(dtype, bs, d):
+    from oracle.kvcache import write_slots
+    rng = np.random.default_rng(1)
+    nb, hkv, t = 40, 3, 300
+    pool = W.to_bits(rng.standard_normal((nb, hkv, bs, d), dtype=np.float32), dtype)
+    k = W.to_bits(rng.standard_normal((t, hkv, d), dtype=np.float32), dtype)
+    v = W.to_bits(rng.standard_normal((t, hkv, d), dtype=np.float32), dtype)
+    slots = rng.permutation(nb * bs)[:t].astype(np.int64)
+    slots[::7] = -1                        # skipped
+    kp_dev, vp_dev = to_device(pool, dtype), to_device(pool.copy(), dtype)
+    pa.pa_reshape_and_cache(to_device(k, dtype), to_device(v, dtype),
+                            torch.from_numpy(slots).cuda(), kp_dev, vp_dev)
+    kp, vp = pool.copy(), pool.copy()
+    write_slots(kp, k, slots)
+    write_slots(vp, v, slots)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_device_bits(kp_dev, dtype), kp)
+    assert np.array_equal(from_device_bits(vp_dev, dtype), vp)
+    # slots past the pool are never written
+    bad = torch.tensor([nb * bs, nb * bs + 5, 1 << 40], dtype=torch.int64, device="cuda")
+    kk = to_device(k[:3], dtype)
+    pa.pa_reshape_and_cache(kk, kk, bad, kp_dev, vp_dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_device_bits(kp_dev, dtype), kp)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_copy_blocks_bitexact(dtype):
+    from oracle.kvcache import copy_blocks
+    rng = np.random.default_rng(2)
+    nb, hkv, bs, d = 64, 8, 16, 128
+    kp = W.to_bits(rng.standard_normal((nb, hkv, bs, d), dtype=np.float32), dtype)
+    vp = W.to_bits(rng.standard_normal((nb, hkv, bs, d), dtype=np.float32), dtype)
+    perm = rng.permutation(nb)
+    pairs = np.stack([perm[:20], perm[20:40]], axis=1).astype(np.int32)  # dst never a src
+    kd, vd = to_device(kp, dtype), to_device(vp, dtype)
+    pa.pa_copy_blocks(kd, vd, torch.from_numpy(pairs).cuda())
+    copy_blocks(kp, pairs)
+    copy_blocks(vp, pairs)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_device_bits(kd, dtype), kp)
+    assert np.array_equal(from_device_bits(vd, dtype), vp)
+    bad = torch.tensor([[0, nb], [-1, 3], [nb + 9, 1]], dtype=torch.int32, device="cuda")
+    pa.pa_copy_blocks(kd, vd, bad)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_device_bits(kd, dtype), kp)
+
+
+# ------------------------------------------------------------ decode, named workloads
+
+@pytest.mark.parametrize("name,batch", [("tiny", None), ("7b_mha", 8), ("8b_gqa", 32),
+                                        ("cow", 16)])
+def test_workload_parity_small(name, batch):
+    check_case(W.draw(name, batch=batch))
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("name,batch", [("8b_gqa", 16), ("7b_mha", 4), ("cow", 8)])
+def test_both_kernel_paths(name, batch, path, decode_path):
+    d = W.draw(name, batch=batch)
+    decode_path(pa.PA_PATH_VALU if path == "valu" else pa.PA_PATH_MFMA)
+    check_case(d, state=False)
+
+
+# ------------------------------------------------------------ decode, shapes and edges
+
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 33, 511, 512, 513, 1024, 1100]
+
+SHAPES = [
+    # (dtype, Hq, Hkv, D, BS)
+    ("f32", 4, 4, 64, 16),
+    ("f32", 8, 2, 128, 32),
+    ("f16", 8, 8, 128, 16),
+    ("f16", 16, 4, 128, 32),
+    ("bf16", 32, 8, 128, 16),
+    ("bf16", 16, 2, 128, 16),
+    ("bf16", 16, 1, 128, 32),
+    ("bf16", 4, 2, 64, 16),
+    ("f16", 16, 2, 64, 32),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+@pytest.mark.parametrize("pt", [0, 16, 64, 1024])
+def test_shapes_and_ragged_lengths(shape, pt):
+    dtype, hq, hkv, d, bs = shape
+    if pt and pt % bs:
+        pytest.skip("partition must be a multiple of the block size")
+    dr = W.custom(100 * SHAPES.index(shape) + pt % 97, hq, hkv, d, dtype, bs, EDGE_LENS)
+    check_case(dr, partition_tokens=pt)
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_group_sizes(g, path, decode_path):
+    if path == "valu" and g == 16:
+        pytest.skip("vector kernel covers G <= 8")
+    decode_path(pa.PA_PATH_VALU if path == "valu" else pa.PA_PATH_MFMA)
+    dr = W.custom(50 + g, 2 * g, 2, 128, "bf16", 16, [7, 300, 600, 1])
+    check_case(dr, partition_tokens=256, state=False)
+
+
+def test_block_permutation_invariance_bitexact():
+    """Relabelling physical blocks changes nothing, bit for bit."""
+    d = W.draw("8b_gqa", batch=12)
+    kv = KV(d)
+    g = run_gpu(d, kv)
+    cache, plan = g["cache"], g["plan"]
+    nb = cache.k_pool.shape[0]
+    pi = torch.from_numpy(np.random.default_rng(5).permutation(nb)).cuda()
+    kp2 = torch.empty_like(cache.k_pool)
+    vp2 = torch.empty_like(cache.v_pool)
+    kp2[pi] = cache.k_pool
+    vp2[pi] = cache.v_pool
+    t = plan.tables.long()
+    t2 = torch.where(t >= 0, pi[t.clamp(min=0)], t).int()
+    out2 = torch.empty_like(g["out"])
+    ws = cache.workspace(d.batch, d.wl.num_q_heads, plan.max_context_len)
+    pa.pa_decode(g["q"], kp2, vp2, t2, plan.lens, d.wl.scale, out2, ws, plan.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), g["out"].view(torch.int16))
+
+
+def test_block_size_invariance():
+    lens = [40, 700, 33, 1]
+    a = W.custom(7, 8, 2, 128, "bf16", 16, lens)
+    b = W.custom(7, 8, 2, 128, "bf16", 32, lens)
+    ga = run_gpu(a, KV(a))
+    gb = run_gpu(b, KV(b))
+    # same seed -> same K/V values; the 16-token tiles are the same either way
+    assert torch.equal(ga["out"].view(torch.int16), gb["out"].view(torch.int16))
+
+
+@pytest.mark.parametrize("name,batch", [("8b_gqa", 16), ("tiny", None), ("7b_mha", 4)])
+def test_poisoned_padding(name, batch):
+    """NaN in every slot no sequence owns and a huge id in table padding."""
+    d = W.draw(name, batch=batch)
+    kv = KV(d)
+    clean = run_gpu(d, kv)
+    o, g = check_case(d, nan_fill=True)
+    assert torch.equal(clean["out"], g["out"])
+    cache, plan = g["cache"], g["plan"]
+    tables = plan.tables.clone()
+    tables[tables < 0] = 1 << 30
+    wide = torch.full((tables.shape[0], tables.shape[1] + 5), 1 << 30, dtype=torch.int32,
+                      device="cuda")
+    wide[:, :tables.shape[1]] = tables
+    out2 = torch.empty_like(g["out"])
+    pa.pa_decode(g["q"], cache.k_pool, cache.v_pool, wide, plan.lens, d.wl.scale, out2, g["ws"],
+                 plan.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, g["out"])
+
+
+def test_zero_length_and_clamping():
+    """ctx <= 0 gives a zero row; lengths beyond max_context_len are clamped
+    (reads stay inside the tables)."""
+    d = W.custom(9, 8, 2, 128, "bf16", 16, [20, 40, 3])
+    kv = KV(d)
+    g = run_gpu(d, kv)
+    cache, plan = g["cache"], g["plan"]
+    lens = plan.lens.clone()
+    lens[1] = 0
+    lens[2] = -5
+    out = torch.full_like(g["out"], 7.0)
+    pa.pa_decode(g["q"], cache.k_pool, cache.v_pool, plan.tables, lens, d.wl.scale, out, None,
+                 plan.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], g["out"][0])
+    assert torch.all(out[1:] == 0)
+    # a length above max_context_len behaves as max_context_len
+    lens = plan.lens.clone()
+    lens[0] = 10 ** 6
+    out3 = torch.empty_like(out)
+    pa.pa_decode(g["q"], cache.k_pool, cache.v_pool, plan.tables, lens, d.wl.scale, out3, g["ws"],
+                 plan.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out3.float()))
+
+
+def test_single_token_is_exact():
+    """ctx = 1: the output is that token's V row exactly."""
+    d = W.custom(11, 8, 2, 128, "bf16", 16, [1, 1, 1])
+    kv = KV(d)
+    g = run_gpu(d, kv)
+    for i in range(3):
+        v0 = kv(i)[1][0]                      # [Hkv][D] bits
+        want = np.repeat(v0, 4, axis=0)       # q heads of each group
+        assert np.array_equal(from_device_bits(g["out"][i], "bf16"), want)
+
+
+def test_split_passes_equal_fused_call():
+    d = W.draw("8b_gqa", batch=24)
+    kv = KV(d)
+    g = run_gpu(d, kv)
+    cache, plan = g["cache"], g["plan"]
+    out = torch.empty_like(g["out"])
+    args = (g["q"], cache.k_pool, cache.v_pool, plan.tables, plan.lens, d.wl.scale, out, g["ws"],
+            plan.max_context_len)
+    pa.pa_decode_partition(*args)
+    pa.pa_decode_reduce(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(out, g["out"])
+
+
+def test_cow_workload_allocator_state_and_release():
+    """Parallel sampling: 96 copies for 32 prompts x 4 branches, shared
+    prefix refcounts, and freeing every branch restores the pool."""
+    d = W.draw("cow")
+    kv = KV(d)
+    o = run_oracle(d, kv, compute_out=False)
+    g = run_gpu(d, kv, decode=False)
+    compare_state(o, g, d)
+    stats = g["cache"].alloc.pa_alloc_stats()
+    assert stats["cow_copies"] == 96 == o["alloc"].cow_copies
+    # the 62 full prefix blocks of each prompt are shared by its 4 branches
+    _, rc = g["cache"].alloc.pa_alloc_query()
+    assert int((rc == 4).sum()) == 32 * 62
+    for s in range(d.batch):
+        g["cache"].free(s)
+    free, rc = g["cache"].alloc.pa_alloc_query()
+    assert sorted(free.tolist()) == list(range(d.num_blocks)) and not rc.any()
+
+
+# ------------------------------------------------------------ full sizes
+
+@pytest.mark.parametrize("name", ["8b_gqa", "7b_mha", "cow", "qwen32b_long",
+                                  "qwen32b_long_bs32"])
+def test_full_size_parity(name):
+    """Every output of the full workload, in the launch configuration the
+    benchmark times (default 512-token partitions)."""
+    check_case(W.draw(name))

@@ -218,3 +218,57 @@ def kv_bytes(d: Draw) -> int:
     """Algorithmic K+V bytes one decode step reads: attended tokens only."""
     wl = d.wl
     return int(d.context_lens.sum()) * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+
+
+# ---------------------------------------------------------------- scenario
+
+def scenario(d: Draw):
+    """The order of allocator operations that builds a workload's decode
+    step, as phases of ops (structure only):
+
+      ("create", i)              new sequence; ids come out 0, 1, 2, ...
+      ("append", i, start, n)    sequence i writes its tokens start..start+n-1
+                                 (values: ``sequence_kv_bits(d, i)[start:start+n]``)
+      ("fork", parent, child)    child shares parent's blocks
+
+    The last phase is the decode step: every sequence appends its last
+    attended token (position ctx_i - 1), then attends ctx_i tokens.
+
+    copy-on-write workload: prompt p's first branch (id 4p) writes the
+    1000-token prefix and is forked three times; then the branches write
+    their tails in branch order; then the decode step.
+    """
+    wl = d.wl
+    lens = d.context_lens
+    if wl.name == "cow":
+        setup = []
+        for p in range(lens.shape[0] // wl.branches):
+            base = p * wl.branches
+            setup.append(("create", base))
+            setup.append(("append", base, 0, wl.prefix_len))
+            for b in range(1, wl.branches):
+                setup.append(("fork", base, base + b))
+        tails = [("append", i, wl.prefix_len, int(lens[i]) - 1 - wl.prefix_len)
+                 for i in range(lens.shape[0]) if int(lens[i]) - 1 > wl.prefix_len]
+        phases = [setup, tails]
+    else:
+        setup = []
+        for i in range(lens.shape[0]):
+            setup.append(("create", i))
+            if lens[i] > 1:
+                setup.append(("append", i, 0, int(lens[i]) - 1))
+        phases = [setup]
+    step = [("append", i, int(lens[i]) - 1, 1) for i in range(lens.shape[0])]
+    return phases + [step]
+
+
+def custom(seed: int, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
+           block_size: int, lens, spare_blocks: int = 7) -> Draw:
+    """A workload of any supported shape with given attended lengths (for
+    parity cases beyond the named workloads).  The pool holds every needed
+    block plus ``spare_blocks``; the free order is a seeded permutation."""
+    wl = Workload(f"custom{seed}", seed, num_q_heads, num_kv_heads, head_dim, dtype, block_size)
+    lens = np.asarray(lens, dtype=np.int64)
+    nb = _blocks_for(np.maximum(lens, 0), block_size) + spare_blocks
+    free_order = np.random.default_rng(seed).permutation(nb).astype(np.int64)
+    return Draw(wl, lens, nb, free_order)
