@@ -1,0 +1,335 @@
+"""Benchmark of the paged decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b_gqa]
+
+A step is one pass of the whole device path over one batch: the step's CoW
+block copies, the cache write of every sequence's new token, decode attention
+through the block tables (partition kernel, then the split-K reduce).  The
+host half of the step (allocator reservations, block tables, their upload)
+is timed once and reported beside it; the inputs of the timed steps are
+already resident in HBM.
+
+Default workload: 8B-shaped GQA decode, one layer, batch 256 (32 q heads,
+8 kv heads, head_dim 128, bf16, block 16, log-normal lengths with median
+1500 and sigma 0.8 clipped to [16, 8192]), synthetic N(0,1) data.
+
+Printed (one JSON line): sequences/s of the whole step, KV GB/s and its
+fraction of the HBM peak, the partition kernel's roofline (algorithmic bytes
+over its average duration, timed with HIP events on the launch stream), and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "paged decode-attn KV GB/s (% of HBM peak) + sequences/s, 8B-GQA batch 256"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["paged_kv_cache_107_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_107_amd/csrc/pa_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pa_decode_partition.json")
+
+DESCRIPTIONS = {
+    "8b_gqa": "8B GQA decode, 1 layer: B=256, 32 q / 8 kv heads, head_dim 128, bf16, block 16, "
+              "lengths lognormal(median 1500, sigma 0.8) clipped to [16, 8192], seed 2",
+    "7b_mha": "7B MHA decode, 1 layer: B=64, 32 q = 32 kv heads, head_dim 128, fp16, block 16, "
+              "lengths uniform [128, 2048], seed 1",
+    "cow": "parallel-sampling CoW, 8B GQA shape, bf16: 32 prompts x 4 branches, 1000-token "
+           "shared prefix, tails uniform [0, 256], seed 3",
+    "qwen32b_long": "Qwen3-32B-shaped long context, 1 layer: 64 q / 8 kv heads, head_dim 128, "
+                    "bf16, block 16, 32 x 2048 + 4 x 32768 tokens",
+    "qwen32b_long_bs32": "as qwen32b_long with block 32",
+    "tiny": "tiny: 4 sequences {10, 5, 33, 7}, 4 heads, head_dim 64, fp32, block 16",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, part_tokens: int):
+    """HBM bytes per partition-kernel launch from the committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("source_sha256") != kernel_source_hash():
+        return None
+    if entry.get("partition_tokens", 512) != part_tokens:
+        return None
+    return entry.get("traffic_bytes")
+
+
+# ------------------------------------------------------------------ setup
+
+def build_state(d, part_tokens: int, log):
+    """Pool population (prefill-size cache writes) and the step's plan."""
+    import torch
+    from paged_kv_cache_107_amd.cache import TORCH_DTYPES, PagedKVCache
+    wl = d.wl
+    signed = np.int32 if wl.dtype == "f32" else np.int16
+    tdt = TORCH_DTYPES[wl.dtype]
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits.view(signed))).cuda().view(tdt)
+
+    shape = (d.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+    pools = tuple(torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(tdt)
+                  for _ in range(2))
+    cache = PagedKVCache(d.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.dtype,
+                         d.free_order, pools=pools)
+    phases = W.scenario(d)
+    kv_cache = {}
+
+    def kv(i):
+        if i not in kv_cache:
+            kv_cache[i] = W.sequence_kv_bits(d, i)
+        return kv_cache[i]
+
+    t0 = time.perf_counter()
+    for phase in phases[:-1]:
+        slots, pairs, ks, vs, n_tok = [], [], [], [], 0
+        for op in phase:
+            if op[0] == "create":
+                cache.create()
+            elif op[0] == "fork":
+                cache.fork(op[1])
+            else:
+                i, start, n = op[1:]
+                s, pair = cache.reserve(i, n)
+                # copies of earlier reservations must land before later writes
+                if pair is not None:
+                    pairs.append(pair)
+                slots.append(s)
+                k, v = kv(i)
+                ks.append(k[start:start + n])
+                vs.append(v[start:start + n])
+                n_tok += n
+            if n_tok > (1 << 18):
+                cache.write_host(dev(np.concatenate(ks)), dev(np.concatenate(vs)),
+                                 np.concatenate(slots), pairs)
+                slots, pairs, ks, vs, n_tok = [], [], [], [], 0
+        if slots or pairs:
+            cache.write_host(dev(np.concatenate(ks)), dev(np.concatenate(vs)),
+                             np.concatenate(slots), pairs)
+    step = phases[-1]
+    k_new = dev(np.stack([kv(op[1])[0][op[2]] for op in step]))
+    v_new = dev(np.stack([kv(op[1])[1][op[2]] for op in step]))
+    kv_cache.clear()
+    torch.cuda.synchronize()
+    log(f"pool populated in {time.perf_counter() - t0:.1f}s")
+    t0 = time.perf_counter()
+    plan = cache.plan([op[1] for op in step], 1)
+    torch.cuda.synchronize()
+    host_step_ms = (time.perf_counter() - t0) * 1e3
+    q = dev(W.query_bits(d))
+    out = torch.empty_like(q)
+    ws = cache.workspace(d.batch, wl.num_q_heads, plan.max_context_len, part_tokens)
+    return cache, plan, q, out, ws, k_new, v_new, host_step_ms
+
+
+# ------------------------------------------------------------------ CPU oracle
+
+def cpu_baseline(d, gpu_out, budget_s: float, log):
+    """The oracle (as it stands) on the first sequences of the same workload,
+    timed on the host; also checks those outputs against the GPU's."""
+    from oracle import OracleAllocator
+    from oracle.attention import paged_decode
+    from oracle.kvcache import write_slots
+    wl = d.wl
+    q_all = W.query_bits(d)
+    # probe one sequence, then size the sample to the time budget
+    n_target = d.batch
+    shape = (d.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    kp = np.full(shape, 0, W.bits_dtype(wl.dtype))
+    vp = np.full(shape, 0, W.bits_dtype(wl.dtype))
+    a = OracleAllocator(d.num_blocks, wl.block_size, d.free_order)
+    wall = cpu = 0.0
+    outs = []
+    done = 0
+    for i in range(n_target):
+        k, v = W.sequence_kv_bits(d, i)
+        s = a.create()
+        slots, _ = a.append(s, k.shape[0])
+        write_slots(kp, k, np.asarray(slots))
+        write_slots(vp, v, np.asarray(slots))
+        tables, lens = a.build_tables([s], -(-k.shape[0] // wl.block_size))
+        c0, t0 = time.process_time(), time.perf_counter()
+        outs.append(paged_decode(q_all[i:i + 1], kp, vp, tables, lens, wl.scale, wl.dtype)[0])
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        done += 1
+        if wall >= budget_s:
+            break
+    ref = np.stack(outs)
+    got = gpu_out[:done].float().cpu().numpy().astype(np.float64)
+    err = float(np.max(np.abs(got - ref)))
+    tokens = int(d.context_lens[:done].sum())
+    log(f"oracle: {done} sequences ({tokens} tokens) in {wall:.2f}s wall, {cpu:.2f}s cpu; "
+        f"max |gpu - oracle| = {err:.2e}")
+    return {"value": done / wall, "unit": "seq/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"first {done} of {d.batch} sequences ({tokens} attended tokens), fp64 "
+                      f"numpy oracle attention timed alone; host has {os.cpu_count()} logical "
+                      f"CPUs; max abs diff vs GPU output on the sample {err:.2e}"}
+
+
+# ------------------------------------------------------------------ main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="8b_gqa", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--partition-tokens", type=int, default=512)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for the CPU baseline (0 = skip)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        return 2
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    import torch
+    import paged_kv_cache_107_amd as pa
+    torch.cuda.set_device(0)
+    pa.lib()
+    d = W.draw(args.workload)
+    wl = d.wl
+    pt = args.partition_tokens
+    log(f"workload {args.workload}: B={d.batch} sum(ctx)={int(d.context_lens.sum())} "
+        f"pool={d.num_blocks} blocks")
+    cache, plan, q, out, ws, k_new, v_new, host_step_ms = build_state(d, pt, log)
+    stream = torch.cuda.current_stream()
+    dec_args = (q, cache.k_pool, cache.v_pool, plan.tables, plan.lens, wl.scale, out, ws,
+                plan.max_context_len, pt)
+
+    def step(ev=None):
+        if plan.pairs.shape[0]:
+            pa.pa_copy_blocks(cache.k_pool, cache.v_pool, plan.pairs)
+        pa.pa_reshape_and_cache(k_new, v_new, plan.slots, cache.k_pool, cache.v_pool)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_decode_partition(*dec_args)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.pa_decode_reduce(*dec_args)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    part_ms = [e[0].elapsed_time(e[1]) for e in events]
+    ms_per_step = elapsed * 1e3 / args.steps
+    part_us = 1e3 * float(np.mean(part_ms))
+    log(f"step {ms_per_step * 1e3:.1f} us, partition kernel mean {part_us:.1f} us "
+        f"(median {1e3 * float(np.median(part_ms)):.1f}, min {1e3 * float(np.min(part_ms)):.1f})")
+
+    # per-pass breakdown (separate loop; informational)
+    def timed(fn, n=50):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        s.record(stream)
+        for _ in range(n):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * s.elapsed_time(e) / n
+
+    write_us = timed(lambda: pa.pa_reshape_and_cache(k_new, v_new, plan.slots, cache.k_pool,
+                                                     cache.v_pool))
+    reduce_us = timed(lambda: pa.pa_decode_reduce(*dec_args))
+    copy_us = (timed(lambda: pa.pa_copy_blocks(cache.k_pool, cache.v_pool, plan.pairs))
+               if plan.pairs.shape[0] else 0.0)
+
+    ctx = d.context_lens.astype(np.int64)
+    eb = wl.elem_bytes
+    kv_bytes = int(ctx.sum()) * 2 * wl.num_kv_heads * wl.head_dim * eb
+    qo_bytes = 2 * d.batch * wl.num_q_heads * wl.head_dim * eb
+    table_bytes = int(np.sum(-(-ctx // wl.block_size))) * 4 + 4 * d.batch
+    alg_bytes = kv_bytes + qo_bytes + table_bytes
+    achieved = alg_bytes / (part_us * 1e-6) / 1e9
+    traffic = measured_traffic(args.workload, pt)
+    seq_per_s = d.batch / (ms_per_step * 1e-3)
+    kv_gbps_step = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(d, out, args.cpu_budget, log)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(seq_per_s, 1),
+        "unit": "seq/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": DESCRIPTIONS[args.workload],
+            "global_batch": d.batch,
+            "attended_tokens": int(ctx.sum()),
+            "partition_tokens": pt,
+            "parallelism": "none (1 GPU)",
+        },
+        "kv_gbps": round(kv_gbps_step, 1),
+        "kv_frac_of_hbm_peak": round(kv_gbps_step / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode_partition",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": alg_bytes,
+            "kernel_us": round(part_us, 2),
+        },
+        "passes_us": {"copy_blocks": round(copy_us, 2), "reshape_and_cache": round(write_us, 2),
+                      "decode_partition": round(part_us, 2), "decode_reduce": round(reduce_us, 2)},
+        "host_step_ms": round(host_step_ms, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
