@@ -108,7 +108,7 @@ const char* pa_status_string(int32_t status);
  *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
  *                 aligned; may be NULL when that size is 0.  Scratch only:
  *                 its contents on entry do not matter.
- *   partition_tokens  multiple of 16 and of block_size, in [16, 8192];
+ *   partition_tokens  multiple of 16 and of block_size, in [16, 4096];
  *                 0 selects the default (512)
  * Block ids outside [0, num_blocks) are skipped (those tokens do not take
  * part); the output is then unspecified but no access leaves the pool.

@@ -24,7 +24,10 @@ SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_cache.hip", "pa_alloc.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.  The host pass
 # does not know the feature and says so; that warning is harmless.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs (not AGPRs), so the
+# softmax rescale of the output accumulators needs no register copies.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 

@@ -12,7 +12,7 @@ namespace {
 
 constexpr int32_t kAbiVersion = 1;
 constexpr int32_t kDefaultPartition = 512;
-constexpr int32_t kMaxPartition = 8192;
+constexpr int32_t kMaxPartition = 4096;
 constexpr int32_t kMaxGridYZ = 65535;
 
 std::atomic<int32_t> g_decode_path{PA_PATH_AUTO};
@@ -68,6 +68,9 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0)
+    return PA_ERR_ARG;
+  if (max_parts_of(max_context_len, partition_tokens ? partition_tokens : kDefaultPartition) >
+      kMaxGridYZ)
     return PA_ERR_ARG;
   if (!std::isfinite(scale)) return PA_ERR_ARG;
   if (pool->num_kv_heads > kMaxGridYZ || num_q_heads > kMaxGridYZ) return PA_ERR_ARG;

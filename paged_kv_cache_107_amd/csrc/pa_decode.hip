@@ -9,7 +9,11 @@
 // maximum and rescaling, i.e. an online softmax).
 //
 // Work split: one workgroup (4 waves) per (sequence, kv head, partition of
-// part_tokens positions).  A partition is cut into 16-token tiles; wave w
+// part_tokens positions).  The grid is (kv head, sequence, partition) with the
+// partition slowest: workgroups go to the 8 XCDs round-robin by linear id, so
+// neighbouring ids must carry similar work -- with the partition fastest, the
+// XCD would be p % 8 and the first partitions (which every sequence has) would
+// pile onto a few XCDs.  A partition is cut into 16-token tiles; wave w
 // takes tiles w, w+4, ...  Each tile is one 16-token run of one physical
 // block (a block of 32 tokens is two tiles), so the block-table entry is read
 // once per tile, as a scalar load, one tile ahead of its use.
@@ -53,6 +57,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 16;  // tokens per tile
+#ifndef PA_MFMA_PREFETCH
+#define PA_MFMA_PREFETCH 3
+#endif
+constexpr int kPrefetch = PA_MFMA_PREFETCH;  // tiles per wave in the register ring
+constexpr float kRescaleSlack = 8.f;           // log2 units: p <= 256 between rescales
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int i) {
   int ctx = a.context_lens[i];
@@ -167,7 +176,7 @@ template <class E>
 __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) {
   constexpr int D = 128;
   extern __shared__ float smem[];
-  const int p = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+  const int g = blockIdx.x, i = blockIdx.y, p = blockIdx.z;
   const int ctx = clamp_ctx(a, i);
   const int n_parts = num_parts(a, ctx);
   if (p >= n_parts) return;
@@ -194,21 +203,38 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
   const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
   const size_t head_stride = (size_t)D << a.log2_bs;
   const size_t block_stride = head_stride * a.num_kv_heads;
-  const S* kbase = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride + c16 * D + 8 * g4;
-  const S* vbase = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride +
-                   (4 * g4) * D + 8 * c16;
+  const S* kbase0 = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride;
+  const S* vbase0 = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride;
 
-  // Loads tile j's K and V rows; false (nothing loaded) for a bad block id.
-  auto load_tile = [&](int j, u32x4 (&kr)[4], u32x4 (&vr)[4]) -> bool {
-    const int tok = t0 + kTile * j;
-    const int blk = table[tok >> a.log2_bs];
-    if ((unsigned)blk >= (unsigned)a.num_blocks) return false;
-    const size_t off = (size_t)blk * block_stride + (size_t)(tok & bs_mask) * D;
+  // This wave's tiles are w, w + 4, w + 8, ...; tile k of the wave is
+  // partition tile w + 4k.  Lane k holds the physical block of the wave's
+  // tile k, read once with one vector load (a partition has at most 4096
+  // tokens, so a wave has at most 64 tiles).
+  const int my_n = w < ntiles ? (ntiles - w + kWaves - 1) / kWaves : 0;
+  const int ids =
+      lane < my_n ? table[min((t0 + kTile * (w + kWaves * lane)) >> a.log2_bs, a.max_blocks - 1)]
+                  : -1;
+  const uint32_t k_lane_off = (uint32_t)(c16 * D + 8 * g4) * 2u;       // bytes
+  const uint32_t v_lane_off = (uint32_t)((4 * g4) * D + 8 * c16) * 2u;
+
+  // Issues the 8 loads of the wave's tile k through per-tile buffer
+  // descriptors.  A tile past the wave's last (or with a bad block id) gets
+  // an empty descriptor: its loads return zeros without touching memory, so
+  // every ring slot always has exactly 8 loads in flight and the wait counts
+  // stay static.  Returns whether the tile holds data.
+  auto issue = [&](int k, u32x4 (&kr)[4], u32x4 (&vr)[4]) -> bool {
+    const int blk = k < my_n ? __builtin_amdgcn_readlane(ids, k) : -1;
+    const bool ok = (unsigned)blk < (unsigned)a.num_blocks;
+    const int tok = t0 + kTile * (w + kWaves * k);
+    const size_t off = ok ? (size_t)blk * block_stride + (size_t)(tok & bs_mask) * D : 0;
+    const uint32_t bytes = ok ? kTile * D * 2u : 0u;
+    const rsrc_t kr_rs = make_rsrc(kbase0 + off, bytes);
+    const rsrc_t vr_rs = make_rsrc(vbase0 + off, bytes);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kr[s] = load16(kbase + off + 32 * s);
+    for (int s = 0; s < 4; ++s) kr[s] = buffer_load16(kr_rs, k_lane_off + 64u * s);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = load16(vbase + off + r * D);
-    return true;
+    for (int r = 0; r < 4; ++r) vr[r] = buffer_load16(vr_rs, v_lane_off + 256u * r);
+    return ok;
   };
 
   float m = neg_inf(), l = 0.f;
@@ -216,59 +242,74 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int j = w;
-  u32x4 kc[4], vc[4];
-  bool okc = j < ntiles && load_tile(j, kc, vc);
-  for (; j < ntiles; j += kWaves) {
-    u32x4 kn[4], vn[4];
-    bool okn = false;
-    if (j + kWaves < ntiles) okn = load_tile(j + kWaves, kn, vn);
-    if (okc) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  // One tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
+  //
+  // The softmax uses a per-head reference m (log2 units) and p = 2^(s - m).
+  // m, l and O are rescaled only when a score exceeds m + kRescaleSlack: then
+  // m becomes the running maximum.  Any reference gives the same quotient
+  // sum p v / sum p, and p <= 2^kRescaleSlack stays well inside the 16-bit
+  // range of the P operand.  The check is lane-local plus one wave vote, so
+  // the common case needs no cross-lane traffic and no accumulator rescale.
+  auto compute = [&](int k, u32x4 (&kc)[4], u32x4 (&vc)[4]) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s = Mfma<E>::qk(kc[t], qv[t], s);
-      float sv[4];
+    for (int t = 0; t < 4; ++t) s = Mfma<E>::qk(kc[t], qv[t], s);
+    float sv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = s[r] * a.scale_log2;
-      const int valid = ntok - kTile * j;
-      if (valid < kTile) {
+    for (int r = 0; r < 4; ++r) sv[r] = s[r] * a.scale_log2;
+    const int valid = ntok - kTile * (w + kWaves * k);
+    if (valid < kTile) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (4 * g4 + r >= valid) {
-            sv[r] = neg_inf();
-            vc[r] = u32x4{0, 0, 0, 0};  // slots past the sequence may hold anything
-          }
+      for (int r = 0; r < 4; ++r) {
+        if (4 * g4 + r >= valid) {
+          sv[r] = neg_inf();
+          vc[r] = u32x4{0, 0, 0, 0};  // slots past the sequence may hold anything
         }
       }
+    }
+    const float lim = m + kRescaleSlack;
+    const bool over = sv[0] > lim || sv[1] > lim || sv[2] > lim || sv[3] > lim;
+    if (__builtin_amdgcn_ballot_w64(over)) {
       float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mt = fmaxf(mt, shfl_xor(mt, 16));
       mt = fmaxf(mt, shfl_xor(mt, 32));
       const float mn = fmaxf(m, mt);
       const float alpha = fast_exp2(m - mn);
-      uint32_t pb[4];
-      float psum = 0.f;
+      l *= alpha;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pb[r] = Mfma<E>::round16(fast_exp2(sv[r] - mn));
-        psum += bits_to_float(E{}, pb[r]);  // the weights the P.V product uses
-      }
-      l = l * alpha + psum;
+      for (int e = 0; e < 8; ++e) o[e] *= alpha;
       m = mn;
-      const u32x2 pw = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const u32x2 vw = {__builtin_amdgcn_perm(vc[1][e >> 1], vc[0][e >> 1], sel),
-                          __builtin_amdgcn_perm(vc[3][e >> 1], vc[2][e >> 1], sel)};
-        o[e] = Mfma<E>::pv(vw, pw, o[e] * alpha);
-      }
     }
+    uint32_t pb[4];
+    float psum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      kc[t] = kn[t];
-      vc[t] = vn[t];
+    for (int r = 0; r < 4; ++r) {
+      pb[r] = Mfma<E>::round16(fast_exp2(sv[r] - m));
+      psum += bits_to_float(E{}, pb[r]);  // the weights the P.V product uses
     }
-    okc = okn;
+    l += psum;
+    const u32x2 pw = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const u32x2 vw = {__builtin_amdgcn_perm(vc[1][e >> 1], vc[0][e >> 1], sel),
+                        __builtin_amdgcn_perm(vc[3][e >> 1], vc[2][e >> 1], sel)};
+      o[e] = Mfma<E>::pv(vw, pw, o[e]);
+    }
+  };
+
+  // Register ring of kPrefetch tiles: while one tile is computed the loads
+  // of the next kPrefetch - 1 are in flight.
+  u32x4 kb[kPrefetch][4], vb[kPrefetch][4];
+  bool okb[kPrefetch];
+#pragma unroll
+  for (int s = 0; s < kPrefetch; ++s) okb[s] = issue(s, kb[s], vb[s]);
+  for (int base = 0; base < my_n; base += kPrefetch) {
+#pragma unroll
+    for (int s = 0; s < kPrefetch; ++s) {
+      if (okb[s]) compute(base + s, kb[s], vb[s]);
+      okb[s] = issue(base + s + kPrefetch, kb[s], vb[s]);
+    }
   }
 
   // wave state -> LDS
@@ -303,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
   constexpr int RPL = kWave / LPR;
   constexpr int LPT = kTile / RPL;
   extern __shared__ float smem[];
-  const int p = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+  const int g = blockIdx.x, i = blockIdx.y, p = blockIdx.z;
   const int ctx = clamp_ctx(a, i);
   const int n_parts = num_parts(a, ctx);
   if (p >= n_parts) return;
@@ -492,7 +533,7 @@ namespace {
 
 template <class E, int D, int G>
 pa_status launch_valu(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
   hipLaunchKernelGGL((decode_partition_valu<E, D, G>), grid, dim3(kThreads),
                      merge_smem_bytes<D>(G), st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -516,7 +557,7 @@ pa_status launch_valu_d(const DecodeArgs& a, int head_dim, hipStream_t st) {
 
 template <class E>
 pa_status launch_mfma(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
   hipLaunchKernelGGL((decode_partition_mfma<E>), grid, dim3(kThreads),
                      merge_smem_bytes<128>(a.group), st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;

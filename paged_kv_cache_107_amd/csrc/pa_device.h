@@ -58,6 +58,27 @@ __device__ __forceinline__ float chunk_elem(E e, const uint4& c, int i) {
   }
 }
 
+// ------------------------------------------------------------- buffer loads
+// A raw buffer descriptor over [base, base + bytes): loads at offsets past
+// `bytes` return zeros and make no memory access (bytes = 0: every load).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, raw addressing
+
+// `base` and `bytes` must be wave-uniform; they are moved to scalar registers
+// so the descriptor is built with scalar instructions.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 // ------------------------------------------------------------- math
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
