@@ -163,14 +163,12 @@ def build_state(d, part_tokens: int, log):
     kv_cache.clear()
     torch.cuda.synchronize()
     log(f"pool populated in {time.perf_counter() - t0:.1f}s")
-    t0 = time.perf_counter()
     plan = cache.plan([op[1] for op in step], 1)
     torch.cuda.synchronize()
-    host_step_ms = (time.perf_counter() - t0) * 1e3
     q = dev(W.query_bits(d))
     out = torch.empty_like(q)
     ws = cache.workspace(d.batch, wl.num_q_heads, plan.max_context_len, part_tokens)
-    return cache, plan, q, out, ws, k_new, v_new, host_step_ms
+    return cache, plan, q, out, ws, k_new, v_new
 
 
 # ------------------------------------------------------------------ CPU oracle
@@ -252,7 +250,7 @@ def main(argv=None):
     pt = args.partition_tokens or DEFAULT_PARTITION[args.workload]
     log(f"workload {args.workload}: B={d.batch} sum(ctx)={int(d.context_lens.sum())} "
         f"pool={d.num_blocks} blocks")
-    cache, plan, q, out, ws, k_new, v_new, host_step_ms = build_state(d, pt, log)
+    cache, plan, q, out, ws, k_new, v_new = build_state(d, pt, log)
     if args.calibration_copy:
         calibration_copy(args.calibration_copy, wl, log)
     stream = torch.cuda.current_stream()
@@ -260,49 +258,53 @@ def main(argv=None):
                 plan.max_context_len, pt)
 
     def step(ev=None):
+        """One decode step; with `ev`, each pass is bracketed by its own pair
+        of HIP events on the launch stream."""
+        def timed(name, fn):
+            if ev is None:
+                fn()
+            else:
+                ev[name][0].record(stream)
+                fn()
+                ev[name][1].record(stream)
         if plan.pairs.shape[0]:
-            pa.pa_copy_blocks(cache.k_pool, cache.v_pool, plan.pairs)
-        pa.pa_reshape_and_cache(k_new, v_new, plan.slots, cache.k_pool, cache.v_pool)
-        if ev is not None:
-            ev[0].record(stream)
-        pa.pa_decode_partition(*dec_args)
-        if ev is not None:
-            ev[1].record(stream)
-        pa.pa_decode_reduce(*dec_args)
+            timed("copy_blocks", lambda: pa.pa_copy_blocks(cache.k_pool, cache.v_pool, plan.pairs))
+        timed("reshape_and_cache", lambda: pa.pa_reshape_and_cache(
+            k_new, v_new, plan.slots, cache.k_pool, cache.v_pool))
+        timed("decode_partition", lambda: pa.pa_decode_partition(*dec_args))
+        timed("decode_reduce", lambda: pa.pa_decode_reduce(*dec_args))
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # Timed region: K whole steps back to back, bracketed by synchronisations
+    # (HIP events between the kernels would add a pipeline drain to each step).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    # The same K steps again with HIP events around every pass on the launch
+    # stream: the partition kernel's mean duration for the roofline, and the
+    # other passes' durations.
+    passes = ["copy_blocks", "reshape_and_cache", "decode_partition", "decode_reduce"]
+    events = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for n in passes} for _ in range(args.steps)]
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    part_ms = [e[0].elapsed_time(e[1]) for e in events]
-    ms_per_step = elapsed * 1e3 / args.steps
+    passes_us = {}
+    for n in passes:
+        if n == "copy_blocks" and not plan.pairs.shape[0]:
+            passes_us[n] = 0.0
+            continue
+        passes_us[n] = round(1e3 * float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in events])), 2)
+    part_ms = [e["decode_partition"][0].elapsed_time(e["decode_partition"][1]) for e in events]
     part_us = 1e3 * float(np.mean(part_ms))
     log(f"step {ms_per_step * 1e3:.1f} us, partition kernel mean {part_us:.1f} us "
-        f"(median {1e3 * float(np.median(part_ms)):.1f}, min {1e3 * float(np.min(part_ms)):.1f})")
-
-    # per-pass breakdown (separate loop; informational)
-    def timed(fn, n=50):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        s.record(stream)
-        for _ in range(n):
-            fn()
-        e.record(stream)
-        torch.cuda.synchronize()
-        return 1e3 * s.elapsed_time(e) / n
-
-    write_us = timed(lambda: pa.pa_reshape_and_cache(k_new, v_new, plan.slots, cache.k_pool,
-                                                     cache.v_pool))
-    reduce_us = timed(lambda: pa.pa_decode_reduce(*dec_args))
-    copy_us = (timed(lambda: pa.pa_copy_blocks(cache.k_pool, cache.v_pool, plan.pairs))
-               if plan.pairs.shape[0] else 0.0)
+        f"(median {1e3 * float(np.median(part_ms)):.1f}, min {1e3 * float(np.min(part_ms)):.1f}); "
+        f"passes {passes_us}")
 
     ctx = d.context_lens.astype(np.int64)
     eb = wl.elem_bytes
@@ -314,6 +316,16 @@ def main(argv=None):
     traffic = measured_traffic(args.workload, pt)
     seq_per_s = d.batch / (ms_per_step * 1e-3)
     kv_gbps_step = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # Host half of a step (allocator reservations, tables, upload), in steady
+    # state: the median of 5 more steps planned after the timed region.
+    host_ms = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        cache.plan(plan.seqs, 1)
+        torch.cuda.synchronize()
+        host_ms.append((time.perf_counter() - t0) * 1e3)
+    host_step_ms = float(np.median(host_ms))
 
     cpu = None
     if args.cpu_budget > 0:
@@ -352,8 +364,7 @@ def main(argv=None):
             "algorithmic_bytes": alg_bytes,
             "kernel_us": round(part_us, 2),
         },
-        "passes_us": {"copy_blocks": round(copy_us, 2), "reshape_and_cache": round(write_us, 2),
-                      "decode_partition": round(part_us, 2), "decode_reduce": round(reduce_us, 2)},
+        "passes_us": passes_us,
         "host_step_ms": round(host_step_ms, 3),
         "cpu_baseline": cpu,
     }

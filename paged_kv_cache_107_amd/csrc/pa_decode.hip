@@ -13,7 +13,9 @@
 // partition slowest: workgroups go to the 8 XCDs round-robin by linear id, so
 // neighbouring ids must carry similar work -- with the partition fastest, the
 // XCD would be p % 8 and the first partitions (which every sequence has) would
-// pile onto a few XCDs.  A partition is cut into 16-token tiles; wave w
+// pile onto a few XCDs.  Partitions are visited last-first: only long
+// sequences have high partitions and those are full, so the big uniform work
+// starts early and the ragged last partitions fill the tail.  A partition is cut into 16-token tiles; wave w
 // takes tiles w, w+4, ...  Each tile is one 16-token run of one physical
 // block (a block of 32 tokens is two tiles), so the block-table entry is read
 // once per tile, as a scalar load, one tile ahead of its use.
@@ -54,9 +56,18 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+#ifndef PA_WG_WAVES
+#define PA_WG_WAVES 4
+#endif
+constexpr int kWaves = PA_WG_WAVES;  // waves per workgroup
+constexpr int kThreads = kWaves * kWave;
+// Lane k of a wave holds the block id of the wave's k-th tile, so a wave
+// takes at most 64 tiles: partitions of up to 4096 tokens need 4 waves.
+static_assert(kWaves * kWave * 16 >= 4096, "partition_tokens <= 4096 needs >= 4 waves");
 constexpr int kTile = 16;  // tokens per tile
+#ifndef PA_PART_DESC
+#define PA_PART_DESC 1
+#endif
 #ifndef PA_MFMA_PREFETCH
 #define PA_MFMA_PREFETCH 3
 #endif
@@ -77,8 +88,8 @@ __device__ __forceinline__ int num_parts(const DecodeArgs& a, int ctx) {
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // ----------------------------------------------------------------- epilogue
-// LDS layout of the per-wave partial states: m[4][16], l[4][16], then
-// o[4][G][D + 4] (row padding staggers banks).
+// LDS layout of the per-wave partial states: m[waves][16], l[waves][16],
+// then o[waves][G][D + 4] (row padding staggers banks).
 template <int D>
 __host__ __device__ constexpr int o_stride() { return D + 4; }
 
@@ -176,7 +187,8 @@ template <class E>
 __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) {
   constexpr int D = 128;
   extern __shared__ float smem[];
-  const int g = blockIdx.x, i = blockIdx.y, p = blockIdx.z;
+  const int g = blockIdx.x, i = blockIdx.y;
+  const int p = PA_PART_DESC ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
   const int ctx = clamp_ctx(a, i);
   const int n_parts = num_parts(a, ctx);
   if (p >= n_parts) return;
@@ -344,7 +356,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
   constexpr int RPL = kWave / LPR;
   constexpr int LPT = kTile / RPL;
   extern __shared__ float smem[];
-  const int g = blockIdx.x, i = blockIdx.y, p = blockIdx.z;
+  const int g = blockIdx.x, i = blockIdx.y;
+  const int p = PA_PART_DESC ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
   const int ctx = clamp_ctx(a, i);
   const int n_parts = num_parts(a, ctx);
   if (p >= n_parts) return;
@@ -493,6 +506,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
 }
 
 // ----------------------------------------------------------------- reduce
+// One wave per (sequence, q head).  A lane covers 8 consecutive outputs, so
+// D / 8 lanes cover a partition's vector and the wave's 64 / (D / 8) lane
+// groups walk disjoint partitions (q = group, group + groups, ...), each
+// with 4 partitions' loads in flight; the groups' sums are added at the end.
 template <class E, int D>
 __global__ __launch_bounds__(kWave) void decode_reduce(DecodeArgs a) {
   const int h = blockIdx.x, i = blockIdx.y;
@@ -510,22 +527,44 @@ __global__ __launch_bounds__(kWave) void decode_reduce(DecodeArgs a) {
   if (M != neg_inf())
     for (int q = lane; q < n_parts; q += kWave) L += fast_exp2(ml[q].x - M) * ml[q].y;
   L = wave_sum(L);
-  constexpr int PER = D / kWave;
-  float acc[PER];
+
+  constexpr int LPR = D / 8;           // lanes per output vector
+  constexpr int GROUPS = kWave / LPR;  // partitions walked side by side
+  constexpr int U = 4;
+  const int grp = lane / LPR, col = (lane % LPR) * 8;
+  float acc[8];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
   if (L > 0.f) {
-    for (int q = 0; q < n_parts; ++q) {
-      const float2 s = ml[q];
-      const float wt = fast_exp2(s.x - M);
+    for (int q0 = grp; q0 < n_parts; q0 += GROUPS * U) {
+      float wt[U];
+      f32x4 o[U][2];
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] = fmaf(wt, wo[(size_t)q * D + lane * PER + k], acc[k]);
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * GROUPS;
+        const bool in = q < n_parts;
+        wt[u] = in ? fast_exp2(ml[q].x - M) : 0.f;
+        const f32x4* src = reinterpret_cast<const f32x4*>(wo + (size_t)q * D + col);
+        o[u][0] = in ? src[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+        o[u][1] = in ? src[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[k] = fmaf(wt[u], o[u][0][k], acc[k]);
+          acc[4 + k] = fmaf(wt[u], o[u][1][k], acc[4 + k]);
+        }
     }
   }
-  auto* out = reinterpret_cast<typename E::storage*>(a.out) + row * D + lane * PER;
 #pragma unroll
-  for (int k = 0; k < PER; ++k)
-    out[k] = (typename E::storage)float_to_bits(E{}, L > 0.f ? acc[k] / L : 0.f);
+  for (int k = 0; k < 8; ++k) acc[k] = across_groups_sum<LPR>(acc[k]);
+  if (grp == 0) {
+    auto* out = reinterpret_cast<typename E::storage*>(a.out) + row * D + col;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      out[k] = (typename E::storage)float_to_bits(E{}, L > 0.f ? acc[k] / L : 0.f);
+  }
 }
 
 // ----------------------------------------------------------------- launchers

@@ -286,9 +286,10 @@ def test_cow_workload_allocator_state_and_release():
 
 # ------------------------------------------------------------ full sizes
 
-@pytest.mark.parametrize("name", ["8b_gqa", "7b_mha", "cow", "qwen32b_long",
-                                  "qwen32b_long_bs32"])
-def test_full_size_parity(name):
-    """Every output of the full workload, in the launch configuration the
-    benchmark times (default 512-token partitions)."""
-    check_case(W.draw(name))
+@pytest.mark.parametrize("name,pt", [("8b_gqa", 2048), ("8b_gqa", 512), ("7b_mha", 512),
+                                     ("cow", 2048), ("qwen32b_long", 512),
+                                     ("qwen32b_long_bs32", 512)])
+def test_full_size_parity(name, pt):
+    """Every output of the full workload, including the launch configuration
+    the benchmark times (its partition size per workload)."""
+    check_case(W.draw(name), partition_tokens=pt)
