@@ -98,35 +98,50 @@ size_t merge_smem_bytes(int group) {
   return (2 * kWaves * 16 + (size_t)kWaves * group * o_stride<D>()) * sizeof(float);
 }
 
-// Merge the four waves' states of head h (log2-domain max) and store either
-// the normalised output or the partition's (m, l, o) for the reduce pass.
+// Merge the waves' states and store either the normalised output or the
+// partition's (m, l, o) for the reduce pass.  A thread owns 4 consecutive
+// outputs of one head: it forms that head's per-wave weights 2^(m_w - M)
+// once, then reads the 4 waves' partial vectors as float4s; everything it
+// reads is independent, so the merge is a few LDS round trips long.
 template <class E, int D>
 __device__ void combine_store(const DecodeArgs& a, const float* smem, int group, int i, int g,
                               int p, int n_parts) {
   const float* sm_m = smem;
   const float* sm_l = smem + kWaves * 16;
   const float* sm_o = smem + 2 * kWaves * 16;
-  for (int idx = threadIdx.x; idx < group * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
-    float M = sm_m[h];
+  constexpr int V = D / 4;  // float4 columns per head
+  for (int idx = threadIdx.x; idx < group * V; idx += kThreads) {
+    const int h = idx / V, d = (idx % V) * 4;
+    float mw[kWaves], M = neg_inf();
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + h]);
-    float L = 0.f, O = 0.f;
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = sm_m[w * 16 + h];
+      M = fmaxf(M, mw[w]);
+    }
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
     if (M != neg_inf()) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float wt = fast_exp2(sm_m[w * 16 + h] - M);
+        const float wt = fast_exp2(mw[w] - M);
         L += wt * sm_l[w * 16 + h];
-        O += wt * sm_o[((size_t)w * group + h) * o_stride<D>() + d];
+        O += wt * *reinterpret_cast<const f32x4*>(sm_o + ((size_t)w * group + h) * o_stride<D>() + d);
       }
     }
     const size_t row = (size_t)i * a.num_q_heads + (size_t)g * group + h;
     if (n_parts == 1) {
-      const float y = L > 0.f ? O / L : 0.f;
-      reinterpret_cast<typename E::storage*>(a.out)[row * D + d] =
-          (typename E::storage)float_to_bits(E{}, y);
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      using S = typename E::storage;
+      S* dst = reinterpret_cast<S*>(a.out) + row * D + d;
+      if constexpr (E::bytes == 4) {
+        *reinterpret_cast<f32x4*>(dst) = O * inv;
+      } else {
+        const uint32_t b0 = float_to_bits(E{}, O[0] * inv), b1 = float_to_bits(E{}, O[1] * inv);
+        const uint32_t b2 = float_to_bits(E{}, O[2] * inv), b3 = float_to_bits(E{}, O[3] * inv);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      }
     } else {
-      a.ws_o[(row * a.max_parts + p) * D + d] = O;
+      *reinterpret_cast<f32x4*>(a.ws_o + (row * a.max_parts + p) * D + d) = O;
       if (d == 0) a.ws_ml[row * a.max_parts + p] = make_float2(M, L);
     }
   }
