@@ -88,11 +88,16 @@ const char* pa_status_string(int32_t status);
  * token being decoded, whose K/V must already be written (pa_reshape_and_cache
  * before pa_decode on the same stream).
  *
- * Work split: one workgroup per (sequence, kv head, partition of
- * `partition_tokens` consecutive positions).  A sequence with a single
- * partition is written to `out` directly; longer ones leave one fp32
- * (max, sum, unnormalised output) per partition in the workspace and a second
- * kernel merges them with a log-sum-exp rescale (split-K).
+ * Work split (split-K).  Each kernel splits every sequence's positions into
+ * pieces and merges the pieces' fp32 (max, sum, unnormalised output) with a
+ * log-sum-exp rescale in a second kernel:
+ *  - grid split: one workgroup per (sequence, kv head, partition of
+ *    `partition_tokens` consecutive positions); a sequence with a single
+ *    partition is written to `out` directly;
+ *  - stream split (matrix-core kernel, up to 4096 sequences): all 16-token
+ *    tiles of the batch, in (kv head, sequence, position) order, are divided
+ *    evenly among a fixed set of waves (one 4-wave workgroup per CU); a
+ *    (sequence, kv head) inside one wave's share is written directly.
  *
  *   q             device, [num_seqs][num_q_heads][head_dim], pool dtype
  *   k_pool/v_pool device, pool layout above
@@ -107,14 +112,20 @@ const char* pa_status_string(int32_t status);
  *   out           device, [num_seqs][num_q_heads][head_dim], pool dtype
  *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
  *                 aligned; may be NULL when that size is 0.  Scratch only:
- *                 its contents on entry do not matter.
+ *                 its contents on entry do not matter.  Layout is private.
  *   partition_tokens  multiple of 16 and of block_size, in [16, 4096];
- *                 0 selects the default (512)
+ *                 0 selects the default (512).  Sizes the grid split's
+ *                 partitions; validated but unused by the stream split.
  * Block ids outside [0, num_blocks) are skipped (those tokens do not take
  * part); the output is then unspecified but no access leaves the pool.
  * ------------------------------------------------------------------------ */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_tokens);
+/* Workspace bytes pa_decode may need for these arguments: the largest need
+ * of the kernels that can run this shape under any path setting (so the
+ * setting may change without a new workspace).  0 when none is needed or the
+ * arguments are invalid (pa_decode then reports the error). */
+size_t pa_decode_workspace_bytes(const pa_pool_desc* pool, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len,
+                                 int32_t partition_tokens);
 
 pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     const pa_pool_desc* pool, const int32_t* block_tables,
@@ -124,8 +135,10 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     void* hip_stream);
 
 /* The two passes of pa_decode, callable one at a time (same arguments, same
- * stream; pa_decode == pa_decode_partition then pa_decode_reduce).  The
- * reduce pass only touches sequences with more than one partition. */
+ * path setting, same stream; pa_decode == pa_decode_partition then
+ * pa_decode_reduce).  The reduce pass finishes the rows the partition pass
+ * left in the workspace and, for the stream split, zeroes the rows of empty
+ * sequences; it does nothing when the grid split has one partition. */
 pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_pool,
                               const pa_pool_desc* pool, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -140,11 +153,20 @@ pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool
                            float scale, void* out, void* workspace, size_t workspace_bytes,
                            int32_t partition_tokens, void* hip_stream);
 
-/* Decode kernel family: PA_PATH_AUTO picks the matrix-core kernel for 16-bit
- * pools with head_dim 128 and G >= 2 and the vector kernel otherwise;
- * PA_PATH_VALU / PA_PATH_MFMA force one (PA_ERR_SHAPE if it does not support
- * the shape).  Process-wide setting; returns the previous value. */
-typedef enum { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 } pa_decode_path;
+/* Decode kernel family.  PA_PATH_AUTO: the matrix-core kernel for 16-bit
+ * pools with head_dim 128 and G = num_q_heads / num_kv_heads in [2, 16], the
+ * vector kernel otherwise.  PA_PATH_MFMA / PA_PATH_VALU force one family
+ * (PA_ERR_SHAPE if it does not support the shape).  The matrix-core kernel
+ * uses the stream split when the batch has at most 4096 sequences, else the
+ * grid split; PA_PATH_MFMA_GRID forces the grid split.  Results agree up to
+ * the order of the fp32 merges.  Process-wide setting; returns the previous
+ * value (-1 for an unknown path, which leaves the setting unchanged). */
+typedef enum {
+  PA_PATH_AUTO = 0,
+  PA_PATH_VALU = 1,
+  PA_PATH_MFMA = 2,
+  PA_PATH_MFMA_GRID = 3
+} pa_decode_path;
 int32_t pa_set_decode_path(int32_t path);
 
 /* ------------------------------------------------------------------------

@@ -6,8 +6,8 @@ write and the copy-on-write block copy, plus a host block allocator with a
 FIFO free pool, refcounts, fork and prefix sharing.  This package is the thin
 Python binding: ``ops`` (kernels on torch device tensors) and ``allocator``.
 """
-from ._lib import (PA_BF16, PA_F16, PA_F32, PA_PATH_AUTO, PA_PATH_MFMA, PA_PATH_VALU,  # noqa: F401
-                   LIB_PATH, PaError, SIGNATURES, lib)
+from ._lib import (LIB_PATH, PA_BF16, PA_F16, PA_F32, PA_PATH_AUTO, PA_PATH_MFMA,  # noqa: F401
+                   PA_PATH_MFMA_GRID, PA_PATH_VALU, SIGNATURES, PaError, lib)
 from .allocator import PaAllocator  # noqa: F401
 from .ops import (alloc_workspace, pa_copy_blocks, pa_decode, pa_decode_partition,  # noqa: F401
                   pa_decode_reduce, pa_decode_workspace_bytes, pa_reshape_and_cache,

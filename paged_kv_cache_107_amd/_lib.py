@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_OK, PA_ERR_ARG, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_OOM, PA_ERR_REFCOUNT, \
     PA_ERR_NOT_FOUND, PA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6, -7
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
-PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA = 0, 1, 2
+PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA, PA_PATH_MFMA_GRID = 0, 1, 2, 3
 
 
 class pa_pool_desc(C.Structure):
@@ -32,7 +32,7 @@ SIGNATURES = {
     "pa_abi_version": (_i32, []),
     "pa_status_string": (C.c_char_p, [_i32]),
     "pa_set_decode_path": (_i32, [_i32]),
-    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_desc, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_partition": (_i32, _DECODE_ARGS),
     "pa_decode_reduce": (_i32, _DECODE_ARGS),

@@ -105,8 +105,8 @@ class PagedKVCache:
 
     def workspace(self, num_seqs: int, num_q_heads: int, max_context_len: int,
                   partition_tokens: int = 0):
-        return alloc_workspace(num_seqs, num_q_heads, self.head_dim, max_context_len,
-                               partition_tokens, self.device)
+        return alloc_workspace(self.k_pool, num_seqs, num_q_heads, max_context_len,
+                               partition_tokens)
 
     def decode(self, plan: StepPlan, q: torch.Tensor, scale: float, out: torch.Tensor,
                workspace: Optional[torch.Tensor], partition_tokens: int = 0, stream=None):

@@ -2,6 +2,7 @@
 // and block-copy kernels.  Every check runs on the host before any launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 
@@ -10,7 +11,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr int32_t kDefaultPartition = 512;
 constexpr int32_t kMaxPartition = 4096;
 constexpr int32_t kMaxGridYZ = 65535;
@@ -43,20 +44,59 @@ inline int32_t max_parts_of(int32_t max_ctx, int32_t part_tokens) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: (max, sum) pairs first, then the unnormalised outputs.
+// Grid split workspace: (max, sum) pairs first, then the unnormalised
+// outputs, one per (sequence, q head, partition); none with one partition.
 size_t ws_ml_bytes(int32_t b, int32_t hq, int32_t parts) {
   return align256((size_t)b * hq * parts * sizeof(float2));
 }
-size_t ws_o_bytes(int32_t b, int32_t hq, int32_t d, int32_t parts) {
-  return (size_t)b * hq * parts * d * sizeof(float);
+size_t grid_ws_bytes(int32_t b, int32_t hq, int32_t d, int32_t max_ctx, int32_t part_tokens) {
+  const int32_t parts = max_parts_of(max_ctx, part_tokens);
+  if (parts <= 1) return 0;
+  return ws_ml_bytes(b, hq, parts) + (size_t)b * hq * parts * d * sizeof(float);
+}
+
+// Stream split workspace: the merge record of each wave rank
+// [kStreamMaxWaves][4], then (max, sum) and the unnormalised outputs for
+// slot-heads (b * hkv + kStreamMaxWaves) * g.
+size_t stream_heads(int32_t b, int32_t hkv, int32_t g) {
+  return ((size_t)b * hkv + pa::kStreamMaxWaves) * g;
+}
+constexpr size_t kStreamOwnerBytes = pa::kStreamMaxWaves * 4 * sizeof(int32_t);
+size_t stream_ml_bytes(int32_t b, int32_t hkv, int32_t g) {
+  return align256(stream_heads(b, hkv, g) * sizeof(float2));
+}
+size_t stream_ws_bytes(int32_t b, int32_t hkv, int32_t g, int32_t d) {
+  return kStreamOwnerBytes + stream_ml_bytes(b, hkv, g) + stream_heads(b, hkv, g) * d * sizeof(float);
 }
 
 struct Prepared {
   pa::DecodeArgs args;
   int32_t dtype;
   int32_t head_dim;
-  bool use_mfma;
+  pa::DecodeKernel kernel;
 };
+
+// The kernel pa_decode runs for this shape under the current path setting.
+pa_status choose_kernel(const pa_pool_desc* pool, int32_t group, int32_t num_seqs,
+                        int32_t max_context_len, pa::DecodeKernel* k) {
+  const bool mfma = pa::mfma_supports(pool->dtype, pool->head_dim, group);
+  const bool stream = mfma && pa::stream_supports(num_seqs, pool->num_kv_heads, max_context_len);
+  const int32_t path = g_decode_path.load();
+  if (path == PA_PATH_VALU) {
+    if (!pa::valu_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
+    *k = pa::DecodeKernel::kValu;
+  } else if (path == PA_PATH_MFMA_GRID) {
+    if (!mfma) return PA_ERR_SHAPE;
+    *k = pa::DecodeKernel::kMfmaGrid;
+  } else if (path == PA_PATH_MFMA || (mfma && group >= 2)) {
+    if (!mfma) return PA_ERR_SHAPE;
+    *k = stream ? pa::DecodeKernel::kMfmaStream : pa::DecodeKernel::kMfmaGrid;
+  } else {
+    if (!pa::valu_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
+    *k = pa::DecodeKernel::kValu;
+  }
+  return PA_OK;
+}
 
 pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
                          const pa_pool_desc* pool, const int32_t* block_tables,
@@ -80,18 +120,9 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
   if (partition_tokens < 16 || partition_tokens > kMaxPartition || partition_tokens % 16 != 0 ||
       partition_tokens % pool->block_size != 0)
     return PA_ERR_ARG;
-  const int32_t path = g_decode_path.load();
-  bool use_mfma;
-  if (path == PA_PATH_MFMA) {
-    if (!pa::mfma_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
-    use_mfma = true;
-  } else if (path == PA_PATH_VALU) {
-    if (!pa::valu_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
-    use_mfma = false;
-  } else {
-    use_mfma = group >= 2 && pa::mfma_supports(pool->dtype, pool->head_dim, group);
-    if (!use_mfma && !pa::valu_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
-  }
+  pa::DecodeKernel kernel;
+  st = choose_kernel(pool, group, num_seqs, max_context_len, &kernel);
+  if (st != PA_OK) return st;
   if (num_seqs == 0) {
     *pr = Prepared{};
     pr->args.num_seqs = 0;
@@ -102,23 +133,34 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
     return PA_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
     return PA_ERR_ARG;
+  const bool stream = kernel == pa::DecodeKernel::kMfmaStream;
   const int32_t max_parts = max_parts_of(max_context_len, partition_tokens);
-  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim,
-                                                max_context_len, partition_tokens);
+  const size_t need = stream ? stream_ws_bytes(num_seqs, pool->num_kv_heads, group, pool->head_dim)
+                             : grid_ws_bytes(num_seqs, num_q_heads, pool->head_dim,
+                                             max_context_len, partition_tokens);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_ARG;
 
   pa::DecodeArgs& a = pr->args;
+  a = pa::DecodeArgs{};
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  a.ws_ml = need ? static_cast<float2*>(workspace) : nullptr;
-  a.ws_o = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           ws_ml_bytes(num_seqs, num_q_heads, max_parts))
-                : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  if (stream) {
+    a.ws_owner = reinterpret_cast<int32_t*>(ws);
+    a.ws_ml = reinterpret_cast<float2*>(ws + kStreamOwnerBytes);
+    a.ws_o = reinterpret_cast<float*>(ws + kStreamOwnerBytes +
+                                      stream_ml_bytes(num_seqs, pool->num_kv_heads, group));
+    a.stream_waves = pa::stream_waves();
+    if (a.stream_waves <= 0 || a.stream_waves > pa::kStreamMaxWaves) return PA_ERR_HIP;
+  } else if (need > 0) {
+    a.ws_ml = reinterpret_cast<float2*>(ws);
+    a.ws_o = reinterpret_cast<float*>(ws + ws_ml_bytes(num_seqs, num_q_heads, max_parts));
+  }
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
@@ -132,8 +174,13 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
   a.scale_log2 = scale * 1.4426950408889634f;
   pr->dtype = pool->dtype;
   pr->head_dim = pool->head_dim;
-  pr->use_mfma = use_mfma;
+  pr->kernel = kernel;
   return PA_OK;
+}
+
+// Whether the partition pass leaves work for the reduce pass.
+bool needs_reduce(const Prepared& pr) {
+  return pr.kernel == pa::DecodeKernel::kMfmaStream || pr.args.max_parts > 1;
 }
 
 }  // namespace
@@ -157,19 +204,27 @@ const char* pa_status_string(int32_t s) {
 }
 
 int32_t pa_set_decode_path(int32_t path) {
-  if (path != PA_PATH_AUTO && path != PA_PATH_VALU && path != PA_PATH_MFMA) return -1;
+  if (path != PA_PATH_AUTO && path != PA_PATH_VALU && path != PA_PATH_MFMA &&
+      path != PA_PATH_MFMA_GRID)
+    return -1;
   return g_decode_path.exchange(path);
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_tokens) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+size_t pa_decode_workspace_bytes(const pa_pool_desc* pool, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len,
+                                 int32_t partition_tokens) {
+  if (check_pool(pool) != PA_OK || num_seqs <= 0 || num_q_heads <= 0 || max_context_len < 0)
+    return 0;
+  if (num_q_heads % pool->num_kv_heads != 0) return 0;
   if (partition_tokens == 0) partition_tokens = kDefaultPartition;
   if (partition_tokens <= 0) return 0;
-  const int32_t parts = max_parts_of(max_context_len, partition_tokens);
-  if (parts <= 1) return 0;
-  return ws_ml_bytes(num_seqs, num_q_heads, parts) +
-         ws_o_bytes(num_seqs, num_q_heads, head_dim, parts);
+  const int32_t group = num_q_heads / pool->num_kv_heads;
+  size_t need = grid_ws_bytes(num_seqs, num_q_heads, pool->head_dim, max_context_len,
+                              partition_tokens);
+  if (pa::mfma_supports(pool->dtype, pool->head_dim, group) &&
+      pa::stream_supports(num_seqs, pool->num_kv_heads, max_context_len))
+    need = std::max(need, stream_ws_bytes(num_seqs, pool->num_kv_heads, group, pool->head_dim));
+  return need;
 }
 
 pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_pool,
@@ -183,7 +238,7 @@ pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_p
                                 context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
                                 workspace, workspace_bytes, partition_tokens, &pr);
   if (st != PA_OK || pr.args.num_seqs == 0) return st;
-  return pa::launch_decode_partition(pr.args, pr.dtype, pr.head_dim, pr.use_mfma,
+  return pa::launch_decode_partition(pr.args, pr.dtype, pr.head_dim, pr.kernel,
                                      static_cast<hipStream_t>(hip_stream));
 }
 
@@ -197,8 +252,8 @@ pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool
   pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                                 context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
                                 workspace, workspace_bytes, partition_tokens, &pr);
-  if (st != PA_OK || pr.args.num_seqs == 0 || pr.args.max_parts <= 1) return st;
-  return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim,
+  if (st != PA_OK || pr.args.num_seqs == 0 || !needs_reduce(pr)) return st;
+  return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim, pr.kernel,
                                   static_cast<hipStream_t>(hip_stream));
 }
 
@@ -214,9 +269,9 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                                 workspace, workspace_bytes, partition_tokens, &pr);
   if (st != PA_OK || pr.args.num_seqs == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  st = pa::launch_decode_partition(pr.args, pr.dtype, pr.head_dim, pr.use_mfma, s);
-  if (st != PA_OK || pr.args.max_parts <= 1) return st;
-  return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim, s);
+  st = pa::launch_decode_partition(pr.args, pr.dtype, pr.head_dim, pr.kernel, s);
+  if (st != PA_OK || !needs_reduce(pr)) return st;
+  return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim, pr.kernel, s);
 }
 
 pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,

@@ -42,6 +42,9 @@
 // sum 2^(m_p-M) l_p.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "pa.h"
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -68,10 +71,13 @@ constexpr int kTile = 16;  // tokens per tile
 #ifndef PA_PART_DESC
 #define PA_PART_DESC 1
 #endif
-#ifndef PA_MFMA_PREFETCH
-#define PA_MFMA_PREFETCH 3
-#endif
-constexpr int kPrefetch = PA_MFMA_PREFETCH;  // tiles per wave in the register ring
+// Tiles per wave in the register ring.  The grid kernel runs two workgroups
+// per CU (two waves per SIMD) with a 3-deep ring; the stream kernel runs one
+// workgroup per CU with a 4-deep ring, which keeps as many bytes in flight
+// per CU without two co-resident workgroups competing (measured: with two,
+// one of them takes most of the bandwidth and the other finishes late).
+constexpr int kPrefetch = 3;
+constexpr int kStreamPrefetch = 4;
 constexpr float kRescaleSlack = 8.f;           // log2 units: p <= 256 between rescales
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int i) {
@@ -360,6 +366,393 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
   combine_store<E, D>(a, smem, G, i, g, p, n_parts);
 }
 
+// ----------------------------------------------------------------- stream MFMA path
+// The tile math of decode_partition_mfma with another work split.  Every tile
+// of the batch is put in one flat order -- kv head, then sequence, then
+// token -- and the grid (kStreamWgPerCu workgroups per CU) is treated as a
+// set of independent waves, each taking one contiguous run of that order
+// (StreamSplit).  All waves get the same number of tiles to within one, none
+// waits on a sibling (there is no barrier after the prologue), and one
+// register ring runs through the wave's whole run, across the (kv head,
+// sequence) pairs it touches, so the next pair's loads are in flight while
+// the current one is stored.  The run of a kv head stays on one or two XCDs,
+// so sequences that share prefix blocks read them through the same L2.
+//
+// A pair that lies inside one wave's run is normalised and written to `out`
+// by that wave.  The waves that share a pair each leave (m, l, o) for its G
+// heads in workspace slot (pair + wave rank), and decode_reduce_stream merges
+// them.  Slots never collide: pairs are numbered in the flat order and the
+// first wave of the next pair is never below the last wave of this one.
+// The wave in whose run a split pair starts owns its merge and records it:
+// ws_owner[rank] = (pair, number of segments, tiles per kv head, whether
+// every run is non-empty), or pair -1.  Rows of empty sequences are zeroed
+// here.
+constexpr int kStreamWgPerCu = 1;  // resident workgroups per CU: one wave per SIMD
+constexpr int kXcds = 8;           // accelerator dies, each with its own L2
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
+constexpr int kVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Wave-uniform loads through the constant address space become scalar loads:
+// they are counted apart from the vector loads of the K/V ring, so the ring's
+// waits stay exact.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int scalar_load(const int32_t* p) {
+  return *reinterpret_cast<const_i32_ptr>(reinterpret_cast<uintptr_t>(p));
+}
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef const __attribute__((address_space(4))) i32x16* const_i32x16_ptr;
+__device__ __forceinline__ i32x16 scalar_load16(const int32_t* p) {
+  return *reinterpret_cast<const_i32x16_ptr>(reinterpret_cast<uintptr_t>(p));
+}
+
+// tb[i] = sum over j < i of ceil(ctx[j] / 16) (tile offset of sequence i
+// within a kv head's run), tb[n] = total.  Block-wide; ends with a barrier.
+__device__ void scan_tiles(const int* ctx, int* tb, int n, int* tmp) {
+  const int t = threadIdx.x;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int k = lo; k < hi; ++k) sum += ceil_div(ctx[k], kTile);
+  tmp[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int x = t >= off ? tmp[t - off] : 0;
+    __syncthreads();
+    tmp[t] += x;
+    __syncthreads();
+  }
+  int run = t > 0 ? tmp[t - 1] : 0;
+  for (int k = lo; k < hi; ++k) {
+    tb[k] = run;
+    run += ceil_div(ctx[k], kTile);
+  }
+  if (t == kThreads - 1) tb[n] = tmp[t];
+  __syncthreads();
+}
+
+// Even split of T flat tiles over the kWaves * nwg waves of nwg workgroups.
+// The hardware deals workgroups to the XCDs round-robin, so workgroup b runs
+// on XCD b % X (X = min(8, nwg)).  The tiles are cut into X contiguous
+// chunks, chunk x going to the workgroups b = x, x + X, ...; each chunk is
+// split evenly over its waves.  Ranks number the waves in flat order: rank
+// r's run is [lo(r), lo(r + 1)).
+struct StreamSplit {
+  long long T;
+  int nwg;
+  __device__ int chunks() const { return min(kXcds, nwg); }
+  __device__ int wgs_of(int x) const { return nwg / chunks() + (x < nwg % chunks() ? 1 : 0); }
+  __device__ int base(int x) const {  // first rank of chunk x
+    return kWaves * (x * (nwg / chunks()) + min(x, nwg % chunks()));
+  }
+  __device__ long long chunk_lo(int x) const { return T * x / chunks(); }
+  __device__ long long lo(int r) const {
+    if (r >= kWaves * nwg) return T;
+    int x = 0;
+    while (x + 1 < chunks() && base(x + 1) <= r) ++x;
+    const long long c0 = chunk_lo(x);
+    return c0 + (chunk_lo(x + 1) - c0) * (r - base(x)) / (kWaves * wgs_of(x));
+  }
+  // rank of workgroup b's wave w
+  __device__ int rank(int b, int w) const {
+    return base(b % chunks()) + (b / chunks()) * kWaves + w;
+  }
+  // every run non-empty: at least as many tiles in each chunk as waves
+  __device__ int dense() const {
+    return T / chunks() >= (long long)kWaves * ((nwg + chunks() - 1) / chunks()) ? 1 : 0;
+  }
+  // rank whose run holds tile t, 0 <= t < T
+  __device__ int rank_of(long long t) const {
+    const int x = (int)(((t + 1) * chunks() - 1) / T);
+    const long long c0 = chunk_lo(x), tx = chunk_lo(x + 1) - c0;
+    return base(x) + (int)(((t - c0 + 1) * (kWaves * wgs_of(x)) - 1) / tx);
+  }
+};
+
+size_t stream_smem_bytes(int num_seqs) { return (2 * (size_t)num_seqs + 1 + kThreads) * 4; }
+
+template <class E>
+__global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeArgs a) {
+  constexpr int D = 128;
+  using S = typename E::storage;
+  extern __shared__ int s_int[];
+  const int B = a.num_seqs, Hkv = a.num_kv_heads, G = a.group;
+  int* s_ctx = s_int;         // [B] clamped lengths, >= 0
+  int* s_tb = s_ctx + B;      // [B + 1] tile offset of each sequence in a head's run
+  int* s_tmp = s_tb + B + 1;  // [kThreads]
+  for (int i = threadIdx.x; i < B; i += kThreads) s_ctx[i] = max(clamp_ctx(a, i), 0);
+  __syncthreads();
+  scan_tiles(s_ctx, s_tb, B, s_tmp);
+
+  const int lane = threadIdx.x % kWave, w = wave_id();
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int Th = uni(s_tb[B]);  // tiles of one kv head's run
+  const StreamSplit split{(long long)Th * Hkv, (int)gridDim.x};
+  const int rank = split.rank(blockIdx.x, w);
+  const int lo = (int)split.lo(rank), hi = (int)split.lo(rank + 1);
+  // rows of empty sequences are zero; spread over the workgroups
+  for (int i = blockIdx.x; i < B; i += gridDim.x) {
+    if (s_ctx[i] > 0) continue;
+    for (int k = threadIdx.x; k < a.num_q_heads * D; k += kThreads)
+      reinterpret_cast<S*>(a.out)[(size_t)i * a.num_q_heads * D + k] = 0;
+  }
+  if (lo >= hi) {  // no barrier follows
+    if (lane == 0) reinterpret_cast<int4*>(a.ws_owner)[rank] = int4{-1, 0, 0, 0};
+    return;
+  }
+
+  const int bs_mask = (1 << a.log2_bs) - 1;
+  const size_t head_stride = (size_t)D << a.log2_bs;
+  const size_t block_stride = head_stride * Hkv;
+
+  // Position in the flat order: kv head g, sequence i, tile t of its n.
+  struct Cur {
+    int i, g, t, n;
+  };
+  auto tiles_of = [&](int i) { return ceil_div(uni(s_ctx[i]), kTile); };
+  auto next_seq = [&](int i) {  // next sequence with tiles, B if none
+    do {
+      ++i;
+    } while (i < B && uni(s_ctx[i]) == 0);
+    return i;
+  };
+  auto advance = [&](Cur& c) {
+    if (++c.t < c.n) return;
+    c.t = 0;
+    c.i = next_seq(c.i);
+    if (c.i == B) {
+      c.i = next_seq(-1);
+      ++c.g;
+    }
+    c.n = c.g < Hkv ? tiles_of(c.i) : 0;
+  };
+  Cur start;
+  {
+    const int g = lo / Th, off = lo - g * Th;
+    int l = 0, r = B;  // last sequence whose first tile is <= off; it has tiles
+    while (r - l > 1) {
+      const int mid = (l + r) >> 1;
+      if (uni(s_tb[mid]) <= off) l = mid; else r = mid;
+    }
+    start = Cur{l, g, off - uni(s_tb[l]), tiles_of(l)};
+  }
+
+  // q rows of one pair through a buffer descriptor bounded to its G heads:
+  // lanes with c16 >= G read zeros.  Lane (c16, g4) gets q[head c16][32 s +
+  // 8 g4 .. +7], the B operand layout of the QK product.
+  const uint32_t q_lane_off = (uint32_t)(c16 * D + 8 * g4) * 2u;
+  auto load_q = [&](const Cur& c, u32x4 (&dst)[4]) {
+    const rsrc_t rs = make_rsrc(reinterpret_cast<const S*>(a.q) +
+                                    ((size_t)c.i * a.num_q_heads + (size_t)c.g * G) * D,
+                                (uint32_t)(G * D * 2));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dst[s] = buffer_load16(rs, q_lane_off + 64u * s);
+  };
+
+  // ---- issue side: the ring's loads, one tile at a time ----
+  // The block id of the next tile is read (scalar load) one issue ahead of
+  // its use.  Tiles past the range, or with a block id outside the pool, get
+  // an empty buffer descriptor: the loads return zeros without touching
+  // memory, and every issue has exactly 8 loads, so the waits stay static.
+  // The first tile of a pair also fetches the pair's q into qn, ahead of its
+  // K/V, unless qn still holds a q the compute side has not taken (pairs of
+  // at most two tiles); that pair then loads q when it starts.
+  Cur ic = start;
+  int irem = hi - lo;
+  auto table_entry = [&](const Cur& c) {
+    return scalar_load(a.block_tables + (size_t)c.i * a.max_blocks + ((c.t * kTile) >> a.log2_bs));
+  };
+  int iblk = table_entry(ic);
+  u32x4 qn[4];
+  bool qn_full = false;
+  int qn_i = 0, qn_g = 0;
+  const uint32_t k_lane_off = (uint32_t)(c16 * D + 8 * g4) * 2u;  // bytes
+  const uint32_t v_lane_off = (uint32_t)((4 * g4) * D + 8 * c16) * 2u;
+  auto issue = [&](u32x4 (&kr)[4], u32x4 (&vr)[4]) -> bool {
+    bool ok = false;
+    size_t off = 0;
+    if (irem > 0) {
+      if (ic.t == 0 && !qn_full && irem < hi - lo) {
+        load_q(ic, qn);
+        qn_full = true;
+        qn_i = ic.i;
+        qn_g = ic.g;
+      }
+      ok = (unsigned)iblk < (unsigned)a.num_blocks;
+      if (ok)
+        off = (size_t)iblk * block_stride + (size_t)ic.g * head_stride +
+              (size_t)((ic.t * kTile) & bs_mask) * D;
+      if (--irem > 0) {
+        advance(ic);
+        iblk = table_entry(ic);
+      }
+    }
+    const uint32_t bytes = ok ? kTile * D * 2u : 0u;
+    const rsrc_t kr_rs = make_rsrc(reinterpret_cast<const S*>(a.k_pool) + off, bytes);
+    const rsrc_t vr_rs = make_rsrc(reinterpret_cast<const S*>(a.v_pool) + off, bytes);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kr[s] = buffer_load16(kr_rs, k_lane_off + 64u * s);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vr[r] = buffer_load16(vr_rs, v_lane_off + 256u * r);
+    return ok;
+  };
+
+  // ---- compute side ----
+  Cur cc = start;
+  int crem = hi - lo;
+  int seg_t0 = 0, ctx_c = 0;
+  u32x4 qv[4];
+  float m = neg_inf(), l = 0.f;
+  f32x4 o[8];
+
+  // A segment is the run of the current pair's tiles inside this range.
+  auto begin_segment = [&]() {
+    seg_t0 = cc.t;
+    ctx_c = uni(s_ctx[cc.i]);
+    if (qn_full && qn_i == cc.i && qn_g == cc.g) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qv[s] = qn[s];
+      qn_full = false;
+    } else {
+      // Rare (start of the range, or a pair of at most two tiles): wait for
+      // the load here, so the join does not leave qv pending in every path.
+      load_q(cc, qv);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    }
+    m = neg_inf();
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // One tile, as in decode_partition_mfma (lazy rescale, P rounded to the
+  // 16-bit operand type and summed as rounded).
+  auto compute = [&](u32x4 (&kc)[4], u32x4 (&vc)[4]) {
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sacc = Mfma<E>::qk(kc[t], qv[t], sacc);
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = sacc[r] * a.scale_log2;
+    const int valid = ctx_c - kTile * cc.t;
+    if (valid < kTile) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * g4 + r >= valid) {
+          sv[r] = neg_inf();
+          vc[r] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+    const float lim = m + kRescaleSlack;
+    const bool over = sv[0] > lim || sv[1] > lim || sv[2] > lim || sv[3] > lim;
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mt = fmaxf(mt, shfl_xor(mt, 16));
+      mt = fmaxf(mt, shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] *= alpha;
+      m = mn;
+    }
+    uint32_t pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pb[r] = Mfma<E>::round16(fast_exp2(sv[r] - m));
+      psum += bits_to_float(E{}, pb[r]);
+    }
+    l += psum;
+    const u32x2 pw = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const u32x2 vw = {__builtin_amdgcn_perm(vc[1][e >> 1], vc[0][e >> 1], sel),
+                        __builtin_amdgcn_perm(vc[3][e >> 1], vc[2][e >> 1], sel)};
+      o[e] = Mfma<E>::pv(vw, pw, o[e]);
+    }
+  };
+
+  // Store the segment: the normalised rows when it is the whole pair, else
+  // its (m, l, o) in slot (pair + rank).  Lane (c16, g4) holds
+  // O[head c16][32 g4 + 8 r + e] = o[e][r].
+  auto end_segment = [&]() {
+    const float lsum = across_groups_sum<16>(l);
+    const bool whole = seg_t0 == 0 && cc.t + 1 == cc.n;
+    if (c16 >= G) return;
+    if (whole) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      S* dst = reinterpret_cast<S*>(a.out) +
+               ((size_t)cc.i * a.num_q_heads + (size_t)cc.g * G + c16) * D + 32 * g4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = float_to_bits(E{}, o[e][r] * inv);
+        *reinterpret_cast<u32x4*>(dst + 8 * r) =
+            u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+      }
+    } else {
+      const size_t slot = (size_t)cc.g * B + cc.i + rank;
+      float* dst = a.ws_o + (slot * G + c16) * D + 32 * g4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<f32x4*>(dst + 8 * r) = f32x4{o[0][r], o[1][r], o[2][r], o[3][r]};
+        *reinterpret_cast<f32x4*>(dst + 8 * r + 4) = f32x4{o[4][r], o[5][r], o[6][r], o[7][r]};
+      }
+      if (g4 == 0) a.ws_ml[slot * G + c16] = make_float2(m, lsum);
+    }
+  };
+
+  begin_segment();
+  u32x4 kb[kStreamPrefetch][4], vb[kStreamPrefetch][4];
+  bool okb[kStreamPrefetch];
+#pragma unroll
+  for (int s = 0; s < kStreamPrefetch; ++s) okb[s] = issue(kb[s], vb[s]);
+  // Every slot issues on every path (past the range the descriptors are
+  // empty) and the loop only exits at the bottom of the unrolled body: all
+  // paths then carry the same load sequence, so no path in which some slot
+  // was issued last can reach the loop header and make the waits
+  // conservative.
+  do {
+#pragma unroll
+    for (int s = 0; s < kStreamPrefetch; ++s) {
+      const bool live = crem > 0;
+      if (live && okb[s]) compute(kb[s], vb[s]);
+      okb[s] = issue(kb[s], vb[s]);
+      if (live) {
+        --crem;
+        if (cc.t + 1 == cc.n || crem == 0) {
+          end_segment();
+          if (crem > 0) {
+            advance(cc);
+            begin_segment();
+          }
+        } else {
+          ++cc.t;
+        }
+      }
+    }
+  } while (crem > 0);
+
+  // The run's last segment (still in cc): if it starts its pair and the pair
+  // goes on, this rank owns the pair's merge.  Only a last segment can.
+  if (lane == 0) {
+    int4 rec = {-1, 0, 0, 0};
+    if (seg_t0 == 0 && cc.t + 1 < cc.n) {
+      const long long last = (long long)cc.g * Th + uni(s_tb[cc.i]) + cc.n - 1;
+      rec = int4{(int)((size_t)cc.g * B + cc.i), split.rank_of(last) - rank + 1, Th,
+                 split.dense()};
+    }
+    reinterpret_cast<int4*>(a.ws_owner)[rank] = rec;
+  }
+}
+
 // ----------------------------------------------------------------- VALU path
 // Lanes along head_dim: a K/V row of D elements is LPR lanes x 16 bytes; one
 // 16-byte load per lane covers RPL rows; a 16-token tile is LPT loads.
@@ -521,64 +914,108 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
 }
 
 // ----------------------------------------------------------------- reduce
-// One wave per (sequence, q head).  A lane covers 8 consecutive outputs, so
-// D / 8 lanes cover a partition's vector and the wave's 64 / (D / 8) lane
-// groups walk disjoint partitions (q = group, group + groups, ...), each
-// with 4 partitions' loads in flight; the groups' sums are added at the end.
-template <class E, int D>
-__global__ __launch_bounds__(kWave) void decode_reduce(DecodeArgs a) {
-  const int h = blockIdx.x, i = blockIdx.y;
-  const int ctx = clamp_ctx(a, i);
-  const int n_parts = num_parts(a, ctx);
-  if (n_parts <= 1) return;
-  const int lane = threadIdx.x;
-  const size_t row = (size_t)i * a.num_q_heads + h;
-  const float2* ml = a.ws_ml + row * a.max_parts;
-  const float* wo = a.ws_o + row * a.max_parts * D;
-  float M = neg_inf();
-  for (int q = lane; q < n_parts; q += kWave) M = fmaxf(M, ml[q].x);
-  M = wave_max(M);
-  float L = 0.f;
-  if (M != neg_inf())
-    for (int q = lane; q < n_parts; q += kWave) L += fast_exp2(ml[q].x - M) * ml[q].y;
-  L = wave_sum(L);
-
+// Merges the n partial states (m_k, l_k, o_k) of one output row in one pass
+// and writes the normalised row (zeros when the total weight is 0).  A lane
+// covers 8 consecutive outputs, so D / 8 lanes cover a vector and the wave's
+// 64 / (D / 8) lane groups walk disjoint states k = group, group + groups,
+// ..., U at a time, each group with its own running maximum; the groups are
+// merged at the end.  The (m, l) and o loads of a step are independent of
+// each other and of the maximum, so a row costs one round of loads.
+// ok(k): state k exists; ml(k): its (m, l); ov(k): its D outputs.
+template <class E, int D, class Ok, class Ml, class Ov>
+__device__ void merge_row(int n, Ok ok, Ml ml, Ov ov, typename E::storage* out) {
   constexpr int LPR = D / 8;           // lanes per output vector
-  constexpr int GROUPS = kWave / LPR;  // partitions walked side by side
+  constexpr int GROUPS = kWave / LPR;  // states walked side by side
   constexpr int U = 4;
-  const int grp = lane / LPR, col = (lane % LPR) * 8;
+  const int lane = threadIdx.x % kWave, grp = lane / LPR, col = (lane % LPR) * 8;
+  float Mg = neg_inf(), Lg = 0.f;
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  if (L > 0.f) {
-    for (int q0 = grp; q0 < n_parts; q0 += GROUPS * U) {
-      float wt[U];
-      f32x4 o[U][2];
+  for (int k0 = grp; k0 < n; k0 += GROUPS * U) {
+    float2 st[U];
+    f32x4 o[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + u * GROUPS;
+      const bool in = k < n && ok(k);
+      st[u] = in ? ml(k) : make_float2(neg_inf(), 0.f);
+      const f32x4* src = reinterpret_cast<const f32x4*>(ov(k) + col);
+      o[u][0] = in ? src[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+      o[u][1] = in ? src[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float Mn = Mg;
+#pragma unroll
+    for (int u = 0; u < U; ++u) Mn = fmaxf(Mn, st[u].x);
+    if (Mn != neg_inf()) {
+      const float sc = fast_exp2(Mg - Mn);  // 0 while the group is empty
+      Lg *= sc;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] *= sc;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int q = q0 + u * GROUPS;
-        const bool in = q < n_parts;
-        wt[u] = in ? fast_exp2(ml[q].x - M) : 0.f;
-        const f32x4* src = reinterpret_cast<const f32x4*>(wo + (size_t)q * D + col);
-        o[u][0] = in ? src[0] : f32x4{0.f, 0.f, 0.f, 0.f};
-        o[u][1] = in ? src[1] : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
+        const float wt = fast_exp2(st[u].x - Mn);
+        Lg = fmaf(wt, st[u].y, Lg);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          acc[k] = fmaf(wt[u], o[u][0][k], acc[k]);
-          acc[4 + k] = fmaf(wt[u], o[u][1][k], acc[4 + k]);
+          acc[k] = fmaf(wt, o[u][0][k], acc[k]);
+          acc[4 + k] = fmaf(wt, o[u][1][k], acc[4 + k]);
         }
+      }
+      Mg = Mn;
     }
   }
+  const float M = across_groups_max<LPR>(Mg);
+  const float sc = Mg == neg_inf() ? 0.f : fast_exp2(Mg - M);
+  const float L = across_groups_sum<LPR>(Lg * sc);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = across_groups_sum<LPR>(acc[k]);
+  for (int k = 0; k < 8; ++k) acc[k] = across_groups_sum<LPR>(acc[k] * sc);
   if (grp == 0) {
-    auto* out = reinterpret_cast<typename E::storage*>(a.out) + row * D + col;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      out[k] = (typename E::storage)float_to_bits(E{}, L > 0.f ? acc[k] / L : 0.f);
+      out[col + k] = (typename E::storage)float_to_bits(E{}, L > 0.f ? acc[k] / L : 0.f);
+  }
+}
+
+// Grid split: one wave per (sequence, q head) with more than one partition.
+template <class E, int D>
+__global__ __launch_bounds__(kWave) void decode_reduce(DecodeArgs a) {
+  const int h = blockIdx.x, i = blockIdx.y;
+  const int n_parts = num_parts(a, clamp_ctx(a, i));
+  if (n_parts <= 1) return;
+  const size_t row = (size_t)i * a.num_q_heads + h;
+  const float2* ml = a.ws_ml + row * a.max_parts;
+  const float* wo = a.ws_o + row * a.max_parts * D;
+  merge_row<E, D>(
+      n_parts, [](int) { return true; }, [&](int k) { return ml[k]; },
+      [&](int k) { return wo + (size_t)k * D; },
+      reinterpret_cast<typename E::storage*>(a.out) + row * D);
+}
+
+// Stream split: one workgroup per wave rank r of the partition pass.  If r
+// owns a pair, its n segments are slots (pair + r), ..., (pair + r + n - 1);
+// a rank with an empty run (possible only with fewer tiles than waves, when
+// the record says so) left nothing and is skipped.  Wave w merges q heads
+// w, w + 4, ... of the pair's G.
+template <class E>
+__global__ __launch_bounds__(kThreads) void decode_reduce_stream(DecodeArgs a) {
+  constexpr int D = 128;
+  const int r = blockIdx.x;
+  const int4 rec = reinterpret_cast<const int4*>(a.ws_owner)[r];
+  const int pq = rec.x;
+  if (pq < 0) return;
+  const int B = a.num_seqs, G = a.group;
+  const int g = pq / B, i = pq - g * B;
+  const StreamSplit split{(long long)rec.z * a.num_kv_heads, a.stream_waves / kWaves};
+  const bool dense = rec.w != 0;
+  const size_t base = (size_t)pq + r;
+  for (int hh = wave_id(); hh < G; hh += kWaves) {
+    merge_row<E, D>(
+        rec.y, [&](int k) { return dense || split.lo(r + k) < split.lo(r + k + 1); },
+        [&](int k) { return a.ws_ml[(base + k) * G + hh]; },
+        [&](int k) { return a.ws_o + ((base + k) * G + hh) * D; },
+        reinterpret_cast<typename E::storage*>(a.out) +
+            ((size_t)i * a.num_q_heads + (size_t)g * G + hh) * D);
   }
 }
 
@@ -617,6 +1054,33 @@ pa_status launch_mfma(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load();
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cache[dev].store(n);
+  }
+  return n;
+}
+
+template <class E>
+pa_status launch_mfma_stream(const DecodeArgs& a, hipStream_t st) {
+  if (a.stream_waves <= 0 || a.stream_waves % kWaves != 0) return PA_ERR_ARG;
+  hipLaunchKernelGGL((decode_partition_mfma_stream<E>), dim3(a.stream_waves / kWaves),
+                     dim3(kThreads), stream_smem_bytes(a.num_seqs), st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+template <class E>
+pa_status launch_reduce_stream(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_reduce_stream<E>), dim3(a.stream_waves), dim3(kThreads), 0, st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 template <class E, int D>
 pa_status launch_reduce(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_q_heads, a.num_seqs);
@@ -625,6 +1089,18 @@ pa_status launch_reduce(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int stream_waves() {
+  const int cus = device_cus();
+  if (cus <= 0) return 0;
+  return std::min(kStreamWgPerCu * cus, kStreamMaxWaves / kWaves) * kWaves;
+}
+
+bool stream_supports(int num_seqs, int num_kv_heads, int max_ctx) {
+  if (num_seqs > kStreamMaxSeqs) return false;  // sequence table in LDS
+  const long long tiles_per_seq = ((long long)max_ctx + kTile - 1) / kTile;
+  return tiles_per_seq * num_kv_heads * num_seqs < (1ll << 31);  // 32-bit flat tile ids
+}
 
 bool mfma_supports(int dtype, int head_dim, int group) {
   return (dtype == PA_F16 || dtype == PA_BF16) && head_dim == 128 && group >= 1 && group <= 16;
@@ -635,9 +1111,14 @@ bool valu_supports(int /*dtype*/, int head_dim, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-pa_status launch_decode_partition(const DecodeArgs& a, int dtype, int head_dim, bool use_mfma,
+pa_status launch_decode_partition(const DecodeArgs& a, int dtype, int head_dim, DecodeKernel k,
                                   hipStream_t st) {
-  if (use_mfma) {
+  if (k == DecodeKernel::kMfmaStream) {
+    if (dtype == PA_BF16) return launch_mfma_stream<BF16>(a, st);
+    if (dtype == PA_F16) return launch_mfma_stream<F16>(a, st);
+    return PA_ERR_SHAPE;
+  }
+  if (k == DecodeKernel::kMfmaGrid) {
     if (dtype == PA_BF16) return launch_mfma<BF16>(a, st);
     if (dtype == PA_F16) return launch_mfma<F16>(a, st);
     return PA_ERR_SHAPE;
@@ -650,7 +1131,13 @@ pa_status launch_decode_partition(const DecodeArgs& a, int dtype, int head_dim, 
   }
 }
 
-pa_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t st) {
+pa_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, DecodeKernel k,
+                               hipStream_t st) {
+  if (k == DecodeKernel::kMfmaStream) {
+    if (dtype == PA_BF16) return launch_reduce_stream<BF16>(a, st);
+    if (dtype == PA_F16) return launch_reduce_stream<F16>(a, st);
+    return PA_ERR_SHAPE;
+  }
   const bool d64 = head_dim == 64;
   switch (dtype) {
     case PA_F32: return d64 ? launch_reduce<F32, 64>(a, st) : launch_reduce<F32, 128>(a, st);

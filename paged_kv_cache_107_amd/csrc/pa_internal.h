@@ -17,8 +17,13 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float2* ws_ml;  // [B][Hq][max_parts] (max, sum), log2 units
-  float* ws_o;    // [B][Hq][max_parts][D] unnormalised outputs
+  // Split-K state, (max, sum) in log2 units and unnormalised outputs.  Grid
+  // split: [B][Hq][max_parts] entries.  Stream split: [slot][G] entries for
+  // slot < B * Hkv + stream_waves, plus ws_owner [stream_waves][4], the merge
+  // record of each wave rank.
+  float2* ws_ml;
+  float* ws_o;
+  int32_t* ws_owner;
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -29,14 +34,30 @@ struct DecodeArgs {
   int32_t max_ctx;
   int32_t part_tokens;
   int32_t max_parts;
-  float scale_log2;  // softmax scale times log2(e)
+  float scale_log2;      // softmax scale times log2(e)
+  int32_t stream_waves;  // waves of the stream split's grid
 };
+
+// Decode kernel families.
+enum class DecodeKernel {
+  kValu,        // vector ALU, one workgroup per (sequence, kv head, partition)
+  kMfmaGrid,    // matrix cores, same grid
+  kMfmaStream,  // matrix cores, flat tile order split evenly over the waves
+};
+
+// Stream split limits: the sequence table lives in LDS, and the wave count
+// (one 4-wave workgroup per CU of a 256-CU part) bounds the workspace.
+constexpr int kStreamMaxSeqs = 4096;
+constexpr int kStreamMaxWaves = 1024;
 
 bool mfma_supports(int dtype, int head_dim, int group);
 bool valu_supports(int dtype, int head_dim, int group);
-pa_status launch_decode_partition(const DecodeArgs& a, int dtype, int head_dim, bool use_mfma,
+bool stream_supports(int num_seqs, int num_kv_heads, int max_ctx);
+int stream_waves();  // on the current device; 0 if it cannot be queried
+pa_status launch_decode_partition(const DecodeArgs& a, int dtype, int head_dim, DecodeKernel k,
                                   hipStream_t st);
-pa_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t st);
+pa_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, DecodeKernel k,
+                               hipStream_t st);
 
 pa_status launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
                                    int32_t num_tokens, void* k_pool, void* v_pool,

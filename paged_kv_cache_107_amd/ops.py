@@ -53,18 +53,20 @@ def _check_pools(k_pool, v_pool):
     return pool_desc(k_pool)
 
 
-def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
-                              max_context_len: int, partition_tokens: int = 0) -> int:
-    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+def pa_decode_workspace_bytes(pool, num_seqs: int, num_q_heads: int, max_context_len: int,
+                              partition_tokens: int = 0) -> int:
+    """Workspace bytes for pa_decode; `pool` is a pa_pool_desc or the K pool tensor."""
+    desc = pool if isinstance(pool, pa_pool_desc) else pool_desc(pool)
+    return int(lib().pa_decode_workspace_bytes(C.byref(desc), num_seqs, num_q_heads,
                                                max_context_len, partition_tokens))
 
 
-def alloc_workspace(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens=0,
-                    device="cuda"):
-    """A workspace tensor sized for pa_decode (None when none is needed)."""
-    n = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+def alloc_workspace(k_pool: torch.Tensor, num_seqs: int, num_q_heads: int, max_context_len: int,
+                    partition_tokens: int = 0):
+    """A workspace tensor sized for pa_decode on this pool (None when none is needed)."""
+    n = pa_decode_workspace_bytes(k_pool, num_seqs, num_q_heads, max_context_len,
                                   partition_tokens)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return torch.empty(n, dtype=torch.uint8, device=k_pool.device) if n else None
 
 
 def _decode_call(fn_name, q, k_pool, v_pool, block_tables, context_lens, scale, out,

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = pa.lib()
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
     assert lib.pa_status_string(0) == b"PA_OK"
     assert lib.pa_status_string(-4) == b"PA_ERR_OOM"
     assert lib.pa_status_string(-99) == b"PA_ERR_UNKNOWN"
@@ -44,12 +44,29 @@ def test_version_and_status_strings():
 
 def test_workspace_bytes():
     f = pa.pa_decode_workspace_bytes
-    assert f(4, 4, 64, 33, 512) == 0          # one partition: written directly
-    assert f(0, 32, 128, 9000, 512) == 0
+    bf16 = pa_pool_desc(64, 16, 8, 128, pa.PA_BF16)
+    # vector kernel only (f32, or head_dim 64), one partition: written directly
+    assert f(pa_pool_desc(64, 16, 4, 64, pa.PA_BF16), 4, 4, 33, 512) == 0
+    assert f(pa_pool_desc(64, 16, 4, 128, pa.PA_F32), 4, 4, 33, 512) == 0
+    assert f(bf16, 0, 32, 9000, 512) == 0
+    assert f(bf16, 4, 7, 100, 512) == 0                       # Hq % Hkv: invalid
+    # grid split: (max, sum) and outputs per (sequence, q head, partition)
     b, hq, d, parts = 256, 32, 128, 16
-    ml = (b * hq * parts * 8 + 255) // 256 * 256
-    assert f(b, hq, d, 8192, 512) == ml + b * hq * parts * d * 4
-    assert f(b, hq, d, 8192, 0) == f(b, hq, d, 8192, 512)
+    grid = (b * hq * parts * 8 + 255) // 256 * 256 + b * hq * parts * d * 4
+    f32 = pa_pool_desc(64, 16, 8, 128, pa.PA_F32)
+    assert f(f32, b, hq, 8192, 512) == grid
+    assert f(f32, b, hq, 8192, 0) == f(f32, b, hq, 8192, 512)
+
+    # stream split: 16-byte merge records of the 1024 wave ranks, then
+    # (max, sum) and outputs for (B * Hkv + 1024) slots of G heads each
+    def stream(b, hkv, g):
+        heads = (b * hkv + 1024) * g
+        return 16 * 1024 + (heads * 8 + 255) // 256 * 256 + heads * d * 4
+    assert f(bf16, b, hq, 8192, 512) == max(grid, stream(b, 8, 4))
+    assert f(bf16, b, hq, 100, 512) == stream(b, 8, 4)
+    assert f(bf16, 4096, hq, 100, 512) == stream(4096, 8, 4)
+    assert f(bf16, 4097, hq, 100, 512) == 0                   # beyond the stream split
+    assert f(pa_pool_desc(64, 16, 32, 128, pa.PA_F16), 3, 32, 100, 0) == stream(3, 32, 1)
 
 
 FAKE = C.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first

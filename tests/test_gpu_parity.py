@@ -49,10 +49,15 @@ def check_case(d, partition_tokens=0, nan_fill=False, state=True):
     return o, g
 
 
+# kernel paths: vector ALU, matrix cores with the (sequence, kv head,
+# partition) grid, matrix cores with the even split of the flat tile order
+PATHS = {"valu": pa.PA_PATH_VALU, "grid": pa.PA_PATH_MFMA_GRID, "stream": pa.PA_PATH_MFMA}
+
+
 @pytest.fixture
 def decode_path():
     prev = pa.pa_set_decode_path(pa.PA_PATH_AUTO)
-    yield lambda p: pa.pa_set_decode_path(p)
+    yield lambda p: pa.pa_set_decode_path(PATHS[p] if isinstance(p, str) else p)
     pa.pa_set_decode_path(prev)
 
 
@@ -116,11 +121,11 @@ def test_workload_parity_small(name, batch):
     check_case(W.draw(name, batch=batch))
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", ["valu", "grid", "stream"])
 @pytest.mark.parametrize("name,batch", [("8b_gqa", 16), ("7b_mha", 4), ("cow", 8)])
-def test_both_kernel_paths(name, batch, path, decode_path):
+def test_every_kernel_path(name, batch, path, decode_path):
     d = W.draw(name, batch=batch)
-    decode_path(pa.PA_PATH_VALU if path == "valu" else pa.PA_PATH_MFMA)
+    decode_path(path)
     check_case(d, state=False)
 
 
@@ -144,20 +149,25 @@ SHAPES = [
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
 @pytest.mark.parametrize("pt", [0, 16, 64, 1024])
-def test_shapes_and_ragged_lengths(shape, pt):
+@pytest.mark.parametrize("path", ["auto", "grid"])
+def test_shapes_and_ragged_lengths(shape, pt, path, decode_path):
     dtype, hq, hkv, d, bs = shape
     if pt and pt % bs:
         pytest.skip("partition must be a multiple of the block size")
+    if path == "grid":
+        if dtype == "f32" or d != 128:
+            pytest.skip("matrix-core kernels take 16-bit pools with head_dim 128")
+        decode_path(path)
     dr = W.custom(100 * SHAPES.index(shape) + pt % 97, hq, hkv, d, dtype, bs, EDGE_LENS)
     check_case(dr, partition_tokens=pt)
 
 
 @pytest.mark.parametrize("g", [1, 2, 4, 8, 16])
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", ["valu", "grid", "stream"])
 def test_group_sizes(g, path, decode_path):
     if path == "valu" and g == 16:
         pytest.skip("vector kernel covers G <= 8")
-    decode_path(pa.PA_PATH_VALU if path == "valu" else pa.PA_PATH_MFMA)
+    decode_path(path)
     dr = W.custom(50 + g, 2 * g, 2, 128, "bf16", 16, [7, 300, 600, 1])
     check_case(dr, partition_tokens=256, state=False)
 
@@ -225,7 +235,7 @@ def test_zero_length_and_clamping():
     lens[1] = 0
     lens[2] = -5
     out = torch.full_like(g["out"], 7.0)
-    pa.pa_decode(g["q"], cache.k_pool, cache.v_pool, plan.tables, lens, d.wl.scale, out, None,
+    pa.pa_decode(g["q"], cache.k_pool, cache.v_pool, plan.tables, lens, d.wl.scale, out, g["ws"],
                  plan.max_context_len)
     torch.cuda.synchronize()
     assert torch.equal(out[0], g["out"][0])
@@ -238,6 +248,37 @@ def test_zero_length_and_clamping():
                  plan.max_context_len)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out3.float()))
+
+
+@pytest.mark.parametrize("path", ["valu", "grid", "stream"])
+def test_empty_sequences_between_others(path, decode_path):
+    """Sequences of length 0 amid others: zero rows, and the flat tile order
+    of the even split steps over them."""
+    from oracle.attention import paged_decode
+    decode_path(path)
+    d = W.custom(13, 8, 2, 128, "bf16", 16, [5, 37, 9, 3, 300, 16, 2, 1, 7])
+    kv = KV(d)
+    o = run_oracle(d, kv, compute_out=False)
+    g = run_gpu(d, kv)
+    cache, plan = g["cache"], g["plan"]
+    zero, kept = [0, 2, 3, 6, 8], [1, 4, 5, 7]
+    lens = o["lens"].copy()
+    lens[zero] = 0
+    want = paged_decode(W.query_bits(d), o["kp"], o["vp"], o["tables"], lens, d.wl.scale, "bf16",
+                        seqs=kept)
+    out = torch.full_like(g["out"], 7.0)
+    pa.pa_decode(g["q"], cache.k_pool, cache.v_pool, plan.tables,
+                 torch.from_numpy(lens).cuda(), d.wl.scale, out, g["ws"], plan.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.all(out[zero] == 0)       # the library's convention for ctx <= 0
+    assert max_abs_err(out[kept], want) <= TOL["bf16"]
+
+
+def test_batch_beyond_stream_split_limit():
+    """4100 sequences: the matrix-core kernel falls back to the grid split."""
+    lens = [1 + (i * 7) % 40 for i in range(4100)]
+    d = W.custom(17, 8, 2, 128, "bf16", 16, lens)
+    check_case(d, state=False)
 
 
 def test_single_token_is_exact():
