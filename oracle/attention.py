@@ -134,3 +134,40 @@ def partitioned_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float
               for p in range(n_parts)]
     return merge_partitions([s[0] for s in states], [s[1] for s in states],
                             [s[2] for s in states])
+
+
+def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_tables, query_start, context_lens,
+                  scale: float, dtype: str) -> np.ndarray:
+    """Chunked-prefill attention for a batch of sequences.
+
+    Prefill runs a prompt's tokens through attention and writes their K/V
+    into the cache; a long prompt can be cut into chunks that run between
+    decode steps (page "附录：Lazy Allocation 与 Copy-on-Write 在 LLM 推理系统中的
+    应用" §2.1; page "vLLM：把 KV 缓存当成虚拟内存", section "KV 的体积从哪来，页表
+    如何把它切开").  Sequence ``i``'s chunk is the ``n_i = query_start[i+1] -
+    query_start[i]`` query rows ``q_bits[query_start[i]:query_start[i+1]]``,
+    its tokens at positions ``ctx_i - n_i .. ctx_i - 1`` (``ctx_i`` =
+    ``context_lens[i]`` counts the chunk, whose K/V are already written).
+    Each token attends to itself and every earlier position of its sequence
+    (the autoregressive rule of the same §2.1): chunk token ``j`` sees
+    positions ``0 .. ctx_i - n_i + j``.  A token whose position would be
+    negative (``ctx_i < n_i``) has an all-zero row.
+
+    q_bits [T][Hq][D]; pools [NB][Hkv][BS][D]; block_tables [B][max_blocks];
+    query_start [B+1]; context_lens [B].  Returns float64 [T][Hq][D].
+    """
+    out = np.zeros(q_bits.shape, dtype=np.float64)
+    for i in range(len(context_lens)):
+        a, b = int(query_start[i]), int(query_start[i + 1])
+        n, ctx = b - a, int(context_lens[i])
+        if n <= 0 or ctx <= 0:
+            continue
+        k = decode_bits(gather_sequence(k_pool_bits, block_tables[i], ctx), dtype)
+        v = decode_bits(gather_sequence(v_pool_bits, block_tables[i], ctx), dtype)
+        for j in range(n):
+            pos = ctx - n + j
+            if pos < 0:
+                continue
+            q = decode_bits(q_bits[a + j], dtype)
+            out[a + j] = dense_attention(q, k[:pos + 1], v[:pos + 1], scale)
+    return out

@@ -59,6 +59,9 @@ class Workload:
     branches: int = 0
     prefix_len: int = 0
     tail_max: int = 0
+    # chunked-prefill workload only: sequences and new tokens per sequence
+    batch: int = 0
+    chunk: int = 0
 
     @property
     def group(self) -> int:
@@ -81,6 +84,7 @@ WORKLOADS: Dict[str, Workload] = {
                     prefix_len=1000, tail_max=256),
     "qwen32b_long": Workload("qwen32b_long", 4, 64, 8, 128, "bf16", 16),
     "qwen32b_long_bs32": Workload("qwen32b_long_bs32", 4, 64, 8, 128, "bf16", 32),
+    "prefill_8b": Workload("prefill_8b", 5, 32, 8, 128, "bf16", 16, batch=16, chunk=512),
 }
 
 
@@ -92,10 +96,25 @@ class Draw:
     num_blocks: int                   # physical pool size
     free_order: np.ndarray            # [num_blocks] int64 permutation
     tails: Optional[np.ndarray] = None  # cow only: [prompts][branches]
+    # new tokens of the step per sequence: None = 1 (decode); else a chunked
+    # prefill step whose chunk is the last chunk_lens[i] of ctx_i tokens
+    chunk_lens: Optional[np.ndarray] = None
 
     @property
     def batch(self) -> int:
         return int(self.context_lens.shape[0])
+
+    @property
+    def step_lens(self) -> np.ndarray:
+        """New tokens per sequence in the step (1 for decode)."""
+        if self.chunk_lens is None:
+            return np.ones(self.batch, dtype=np.int64)
+        return self.chunk_lens
+
+    @property
+    def query_start(self) -> np.ndarray:
+        """[B+1] offsets of each sequence's query rows in the step."""
+        return np.concatenate([[0], np.cumsum(self.step_lens)]).astype(np.int64)
 
 
 def _blocks_for(n_tokens: np.ndarray, block_size: int) -> int:
@@ -123,6 +142,12 @@ def draw(name: str, batch: Optional[int] = None) -> Draw:
         lens = (wl.prefix_len + tails + 1).reshape(-1)
     elif wl.name.startswith("qwen32b_long"):
         lens = np.array([2048] * 32 + [32768] * 4, dtype=np.int64)
+    elif wl.name == "prefill_8b":
+        # chunked prefill: a 512-token chunk on top of a cached prefix drawn
+        # like the decode workload's lengths
+        prefix = np.clip(np.rint(rng.lognormal(math.log(1500.0), 0.8, wl.batch)), 0,
+                         8192 - wl.chunk).astype(np.int64)
+        lens = prefix + wl.chunk
     else:  # pragma: no cover
         raise KeyError(name)
     if batch is not None:
@@ -136,7 +161,8 @@ def draw(name: str, batch: Optional[int] = None) -> Draw:
         # pool sized to 1.25x the unshared block demand of the batch
         nb = int(math.ceil(1.25 * _blocks_for(lens, wl.block_size)))
     free_order = rng.permutation(nb).astype(np.int64)
-    return Draw(wl, lens, nb, free_order, tails)
+    chunks = np.full(lens.shape[0], wl.chunk, dtype=np.int64) if wl.chunk else None
+    return Draw(wl, lens, nb, free_order, tails, chunks)
 
 
 # ---------------------------------------------------------------- element bits
@@ -169,6 +195,14 @@ def query_bits(d: Draw) -> np.ndarray:
     wl = d.wl
     rng = np.random.default_rng([wl.seed, 3])
     return _normal_bits(rng, (d.batch, wl.num_q_heads, wl.head_dim), wl.dtype)
+
+
+def prefill_query_bits(d: Draw) -> np.ndarray:
+    """q for a chunked-prefill step: [sum of chunk lengths][Hq][D] bits,
+    sequence i's rows at query_start[i] .. query_start[i+1]."""
+    wl = d.wl
+    rng = np.random.default_rng([wl.seed, 5])
+    return _normal_bits(rng, (int(d.step_lens.sum()), wl.num_q_heads, wl.head_dim), wl.dtype)
 
 
 def sequence_kv_bits(d: Draw, i: int):
@@ -231,8 +265,9 @@ def scenario(d: Draw):
                                  (values: ``sequence_kv_bits(d, i)[start:start+n]``)
       ("fork", parent, child)    child shares parent's blocks
 
-    The last phase is the decode step: every sequence appends its last
-    attended token (position ctx_i - 1), then attends ctx_i tokens.
+    The last phase is the step: every sequence appends its last attended
+    token (position ctx_i - 1), then attends ctx_i tokens; for a chunked
+    prefill step it appends its last chunk_lens[i] tokens instead.
 
     copy-on-write workload: prompt p's first branch (id 4p) writes the
     1000-token prefix and is forked three times; then the branches write
@@ -253,22 +288,26 @@ def scenario(d: Draw):
         phases = [setup, tails]
     else:
         setup = []
+        new = d.step_lens
         for i in range(lens.shape[0]):
             setup.append(("create", i))
-            if lens[i] > 1:
-                setup.append(("append", i, 0, int(lens[i]) - 1))
+            if lens[i] > new[i]:
+                setup.append(("append", i, 0, int(lens[i] - new[i])))
         phases = [setup]
-    step = [("append", i, int(lens[i]) - 1, 1) for i in range(lens.shape[0])]
+    step = [("append", i, int(lens[i] - d.step_lens[i]), int(d.step_lens[i]))
+            for i in range(lens.shape[0])]
     return phases + [step]
 
 
 def custom(seed: int, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
-           block_size: int, lens, spare_blocks: int = 7) -> Draw:
+           block_size: int, lens, spare_blocks: int = 7, chunk_lens=None) -> Draw:
     """A workload of any supported shape with given attended lengths (for
     parity cases beyond the named workloads).  The pool holds every needed
-    block plus ``spare_blocks``; the free order is a seeded permutation."""
+    block plus ``spare_blocks``; the free order is a seeded permutation.
+    ``chunk_lens`` makes the step a chunked prefill of that many tokens."""
     wl = Workload(f"custom{seed}", seed, num_q_heads, num_kv_heads, head_dim, dtype, block_size)
     lens = np.asarray(lens, dtype=np.int64)
     nb = _blocks_for(np.maximum(lens, 0), block_size) + spare_blocks
     free_order = np.random.default_rng(seed).permutation(nb).astype(np.int64)
-    return Draw(wl, lens, nb, free_order)
+    chunks = None if chunk_lens is None else np.asarray(chunk_lens, dtype=np.int64)
+    return Draw(wl, lens, nb, free_order, None, chunks)
