@@ -15,8 +15,10 @@ Default workload: 8B-shaped GQA decode, one layer, batch 256 (32 q heads,
 
 Printed (one JSON line): sequences/s of the whole step, KV GB/s and its
 fraction of the HBM peak, the partition kernel's roofline (algorithmic bytes
-over its average duration, timed with HIP events on the launch stream), and
-the CPU oracle timed on a bounded sample of the same workload.
+over its average duration, timed with HIP events on the launch stream), the
+CPU oracle timed on a bounded sample of the same workload, and, apart from the
+timed step, the chunked-prefill kernel on its own workload with its
+matrix-core roofline.
 """
 from __future__ import annotations
 
@@ -38,6 +40,7 @@ import workloads as W  # noqa: E402
 
 METRIC = "paged decode-attn KV GB/s (% of HBM peak) + sequences/s, 8B-GQA batch 256"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 matrix-core peak
 KERNEL_SOURCES = ["paged_kv_cache_107_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_107_amd/csrc/pa_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pa_decode_partition.json")
@@ -54,6 +57,9 @@ DESCRIPTIONS = {
     "qwen32b_long_bs32": "as qwen32b_long with block 32",
     "tiny": "tiny: 4 sequences {10, 5, 33, 7}, 4 heads, head_dim 64, fp32, block 16",
 }
+PREFILL_DESCRIPTION = ("8B GQA chunked prefill, 1 layer: 16 sequences x 512-token chunks on "
+                       "cached prefixes lognormal(median 1500, sigma 0.8) clipped to [0, 7680], "
+                       "32 q / 8 kv heads, head_dim 128, bf16, block 16, seed 5")
 
 
 # Split-K partition size per workload: the long-context workload is stated
@@ -171,6 +177,79 @@ def build_state(d, part_tokens: int, log):
     return cache, plan, q, out, ws, k_new, v_new
 
 
+def measure_prefill(reps: int, log):
+    """pa_prefill on the chunked-prefill workload: every sequence's prefix and
+    chunk K/V written through the allocator and the cache kernels, then `reps`
+    timed calls (HIP events on the launch stream)."""
+    import torch
+    import paged_kv_cache_107_amd as pa
+    from paged_kv_cache_107_amd.cache import TORCH_DTYPES, PagedKVCache
+    d = W.draw("prefill_8b")
+    wl = d.wl
+    tdt = TORCH_DTYPES[wl.dtype]
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits.view(np.int16))).cuda().view(tdt)
+
+    shape = (d.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+    pools = tuple(torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(tdt)
+                  for _ in range(2))
+    cache = PagedKVCache(d.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.dtype,
+                         d.free_order, pools=pools)
+    for phase in W.scenario(d):
+        slots, ks, vs = [], [], []
+        for op in phase:
+            if op[0] == "create":
+                cache.create()
+            else:
+                i, start, n = op[1:]
+                s, pair = cache.reserve(i, n)
+                assert pair is None
+                k, v = W.sequence_kv_bits(d, i)
+                slots.append(s)
+                ks.append(k[start:start + n])
+                vs.append(v[start:start + n])
+        cache.write_host(dev(np.concatenate(ks)), dev(np.concatenate(vs)),
+                         np.concatenate(slots), [])
+    seqs = list(range(d.batch))
+    lens = d.context_lens
+    tables, lens_i = cache.alloc.pa_build_tables(seqs, int(-(-lens.max() // wl.block_size)))
+    q = dev(W.prefill_query_bits(d))
+    out = torch.empty_like(q)
+    qs = torch.from_numpy(d.query_start.astype(np.int32)).cuda()
+    args = (q, cache.k_pool, cache.v_pool, torch.from_numpy(tables).cuda(), qs,
+            torch.from_numpy(lens_i).cuda(), wl.scale, out, int(d.step_lens.max()),
+            int(lens.max()))
+    for _ in range(3):
+        pa.pa_prefill(*args)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        pa.pa_prefill(*args)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # causal work: row at position p attends p + 1 keys; 2 flops per
+    # multiply-add in each of Q K^T and P V
+    seen = sum(int(((L - c) + np.arange(c) + 1).sum()) for L, c in zip(lens, d.step_lens))
+    flops = 4 * wl.head_dim * wl.num_q_heads * seen
+    tflops = flops / (us * 1e-6) / 1e12
+    tokens = int(d.step_lens.sum())
+    log(f"prefill: {us:.1f} us, {tflops:.1f} TFLOP/s, {tokens / (us * 1e-6):.0f} tokens/s")
+    return {
+        "workload": PREFILL_DESCRIPTION,
+        "kernel_us": round(us, 2),
+        "tokens_per_s": round(tokens / (us * 1e-6), 1),
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill", "achieved": round(tflops, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops": flops},
+    }
+
+
 # ------------------------------------------------------------------ CPU oracle
 
 def cpu_baseline(d, gpu_out, budget_s: float, log):
@@ -232,6 +311,8 @@ def main(argv=None):
                          "scratch pool (a plain copy of known size for counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
+    ap.add_argument("--prefill-reps", type=int, default=20,
+                    help="timed pa_prefill calls on the chunked-prefill workload (0 = skip)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
@@ -330,6 +411,9 @@ def main(argv=None):
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(d, out, args.cpu_budget, log)
+    prefill = None
+    if args.prefill_reps > 0:
+        prefill = measure_prefill(args.prefill_reps, log)
 
     rec = {
         "metric": METRIC,
@@ -367,6 +451,7 @@ def main(argv=None):
         "passes_us": passes_us,
         "host_step_ms": round(host_step_ms, 3),
         "cpu_baseline": cpu,
+        "prefill": prefill,
     }
     print(json.dumps(rec), flush=True)
     return 0

@@ -170,6 +170,39 @@ typedef enum {
 int32_t pa_set_decode_path(int32_t path);
 
 /* ------------------------------------------------------------------------
+ * Chunked prefill attention: a step that runs a chunk of each sequence's
+ * prompt tokens, after their K/V have been written to the cache
+ * (pa_reshape_and_cache before pa_prefill on the same stream).  Prefill
+ * writes every prompt token's K/V; a long prompt may be cut into chunks run
+ * between decode steps (page "附录：Lazy Allocation 与 Copy-on-Write 在 LLM 推理
+ * 系统中的应用" §2.1; page "vLLM：把 KV 缓存当成虚拟内存", section "KV 的体积从哪
+ * 来，页表如何把它切开").
+ *
+ * Sequence i's chunk is query rows a = query_start[i] .. b - 1 (b =
+ * query_start[i+1], n = b - a), its tokens at positions ctx - n .. ctx - 1
+ * with ctx = context_lens[i] (the length after the chunk).  Row a + j, q
+ * head h, kv head g = h / G attends to positions 0 .. ctx - n + j:
+ *     out[a+j][h] = sum_{p <= ctx-n+j} softmax_p(scale * <q[a+j][h], K[p][g]>) * V[p][g]
+ * in fp32, rounded once (RNE) to the pool dtype.  A row whose position is
+ * negative (ctx < n) is all zeros.
+ *
+ *   q, out        device [num_tokens][num_q_heads][head_dim], pool dtype
+ *   query_start   device int32 [num_seqs + 1], non-decreasing; a sequence
+ *                 whose rows fall outside [0, num_tokens) is skipped
+ *   context_lens  device int32 [num_seqs], clamped like pa_decode's
+ *   max_query_len host bound >= every n; rows past it are not computed
+ *   max_context_len, block_tables, max_blocks_per_seq, scale: as pa_decode
+ * Supported: f16/bf16 pools, head_dim 128, G in {1, 2, 4, 8, 16}
+ * (PA_ERR_SHAPE otherwise).  No workspace; one kernel launch.
+ * ------------------------------------------------------------------------ */
+pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const pa_pool_desc* pool, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* query_start,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
+                     int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
+                     float scale, void* out, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Cache write: decode appends each new token's K/V to the cache (page
  * "Lazy Allocation 与 Copy-on-Write 在 LLM 推理系统中的应用", section 2.1), at
  * the slot its block table gives.  For every t with slot = slot_mapping[t]

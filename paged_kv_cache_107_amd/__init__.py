@@ -1,8 +1,8 @@
 """Paged KV-cache decode for AMD MI355X (gfx950).
 
 The product is ``libpa.so`` (C ABI declared in ``include/pa.h``): HIP kernels
-for paged decode attention (partition + split-K reduce), the new-token cache
-write and the copy-on-write block copy, plus a host block allocator with a
+for paged decode attention (partition + split-K reduce), chunked prefill
+attention, the new-token cache write and the copy-on-write block copy, plus a host block allocator with a
 FIFO free pool, refcounts, fork and prefix sharing.  This package is the thin
 Python binding: ``ops`` (kernels on torch device tensors) and ``allocator``.
 """
@@ -10,5 +10,5 @@ from ._lib import (LIB_PATH, PA_BF16, PA_F16, PA_F32, PA_PATH_AUTO, PA_PATH_MFMA
                    PA_PATH_MFMA_GRID, PA_PATH_VALU, SIGNATURES, PaError, lib)
 from .allocator import PaAllocator  # noqa: F401
 from .ops import (alloc_workspace, pa_copy_blocks, pa_decode, pa_decode_partition,  # noqa: F401
-                  pa_decode_reduce, pa_decode_workspace_bytes, pa_reshape_and_cache,
+                  pa_decode_reduce, pa_decode_workspace_bytes, pa_prefill, pa_reshape_and_cache,
                   pa_set_decode_path, pool_desc)

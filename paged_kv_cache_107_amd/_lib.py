@@ -36,6 +36,8 @@ SIGNATURES = {
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_partition": (_i32, _DECODE_ARGS),
     "pa_decode_reduce": (_i32, _DECODE_ARGS),
+    "pa_prefill": (_i32, [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                          _f32, _vp, _vp]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _desc, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _desc, _vp, _i32, _vp]),
     "pa_alloc_create": (_i32, [_i32, _i32, _pi32, C.POINTER(_vp)]),

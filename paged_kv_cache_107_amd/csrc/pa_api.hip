@@ -274,6 +274,53 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim, pr.kernel, s);
 }
 
+pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const pa_pool_desc* pool, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* query_start,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
+                     int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
+                     float scale, void* out, void* hip_stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_tokens < 0 || num_q_heads <= 0 ||
+      max_blocks_per_seq < 0 || max_query_len < 0 || max_context_len < 0)
+    return PA_ERR_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_ARG;
+  if (pool->num_kv_heads > kMaxGridYZ || num_q_heads > kMaxGridYZ) return PA_ERR_ARG;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int32_t group = num_q_heads / pool->num_kv_heads;
+  if (!pa::prefill_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
+  if (pa::prefill_query_blocks(max_query_len, group) > kMaxGridYZ * 4) return PA_ERR_ARG;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !query_start || !context_lens || !out)
+    return PA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+      (reinterpret_cast<uintptr_t>(query_start) & 3u) ||
+      (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+    return PA_ERR_ARG;
+  pa::PrefillArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.query_start = query_start;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.num_blocks = pool->num_blocks;
+  a.log2_bs = ilog2(pool->block_size);
+  a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.max_query = max_query_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return pa::launch_prefill(a, pool->dtype, static_cast<hipStream_t>(hip_stream));
+}
+
 pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
                                int32_t num_tokens, void* k_pool, void* v_pool,
                                const pa_pool_desc* pool, void* hip_stream) {

@@ -51,14 +51,6 @@
 
 namespace pa {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 #ifndef PA_WG_WAVES
 #define PA_WG_WAVES 4
 #endif
@@ -162,39 +154,6 @@ __device__ void store_zero_rows(const DecodeArgs& a, int group, int i, int g) {
 }
 
 // ----------------------------------------------------------------- MFMA path
-template <class E>
-struct Mfma;
-
-template <>
-struct Mfma<BF16> {
-  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
-                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 pv(u32x2 v, u32x2 p, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v),
-                                                     __builtin_bit_cast(i16x4, p), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t round16(float x) {
-    return __builtin_bit_cast(uint16_t, (__bf16)x);
-  }
-};
-
-template <>
-struct Mfma<F16> {
-  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
-                                                  __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 pv(u32x2 v, u32x2 p, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v),
-                                                 __builtin_bit_cast(f16x4, p), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t round16(float x) {
-    return __builtin_bit_cast(uint16_t, (_Float16)x);
-  }
-};
-
 // Lane roles in a tile (c16 = lane % 16, g4 = lane / 16):
 //  QK  A = K tile:   lane holds K[row c16][32 s + 8 g4 .. +7]   for k-step s = 0..3
 //      B = Q^T:      lane holds q[head c16][32 s + 8 g4 .. +7]  (zero for c16 >= G)
@@ -392,22 +351,6 @@ constexpr int kXcds = 8;           // accelerator dies, each with its own L2
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
 // maxima (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 constexpr int kVmcnt0 = 0x0F70;
-
-__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Wave-uniform loads through the constant address space become scalar loads:
-// they are counted apart from the vector loads of the K/V ring, so the ring's
-// waits stay exact.
-typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-__device__ __forceinline__ int scalar_load(const int32_t* p) {
-  return *reinterpret_cast<const_i32_ptr>(reinterpret_cast<uintptr_t>(p));
-}
-typedef int i32x16 __attribute__((ext_vector_type(16)));
-typedef const __attribute__((address_space(4))) i32x16* const_i32x16_ptr;
-__device__ __forceinline__ i32x16 scalar_load16(const int32_t* p) {
-  return *reinterpret_cast<const_i32x16_ptr>(reinterpret_cast<uintptr_t>(p));
-}
 
 // tb[i] = sum over j < i of ceil(ctx[j] / 16) (tile offset of sequence i
 // within a kv head's run), tb[n] = total.  Block-wide; ends with a barrier.

@@ -58,6 +58,15 @@ __device__ __forceinline__ float chunk_elem(E e, const uint4& c, int i) {
   }
 }
 
+// ------------------------------------------------------------- vector types
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
 // ------------------------------------------------------------- buffer loads
 // A raw buffer descriptor over [base, base + bytes): loads at offsets past
 // `bytes` return zeros and make no memory access (bytes = 0: every load).
@@ -144,5 +153,54 @@ __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Wave-uniform loads through the constant address space become scalar loads:
+// they are counted apart from the vector loads of a register ring, so the
+// ring's waits stay exact.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int scalar_load(const int32_t* p) {
+  return *reinterpret_cast<const_i32_ptr>(reinterpret_cast<uintptr_t>(p));
+}
+
+// ------------------------------------------------------------- matrix cores
+// The two products of a 16-token tile: qk = v_mfma_f32_16x16x32 (A and B 8
+// elements per lane), pv = v_mfma_f32_16x16x16 (4 elements per lane);
+// round16 rounds a probability to the 16-bit operand type.
+template <class E>
+struct Mfma;
+
+template <>
+struct Mfma<BF16> {
+  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 v, u32x2 p, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v),
+                                                     __builtin_bit_cast(i16x4, p), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t round16(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+};
+
+template <>
+struct Mfma<F16> {
+  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                  __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 v, u32x2 p, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v),
+                                                 __builtin_bit_cast(f16x4, p), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t round16(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+};
+
 
 }  // namespace pa

@@ -59,6 +59,33 @@ pa_status launch_decode_partition(const DecodeArgs& a, int dtype, int head_dim, 
 pa_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, DecodeKernel k,
                                hipStream_t st);
 
+// Chunked prefill: sequence i's query rows are query_start[i] ..
+// query_start[i+1] - 1, its chunk tokens at positions ctx_i - n_i .. ctx_i - 1.
+struct PrefillArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* query_start;
+  const int32_t* context_lens;
+  void* out;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t num_blocks;
+  int32_t log2_bs;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t max_query;
+  float scale_log2;
+};
+
+bool prefill_supports(int dtype, int head_dim, int group);
+int prefill_query_blocks(int max_query_len, int group);  // per sequence, grid bound
+pa_status launch_prefill(const PrefillArgs& a, int dtype, hipStream_t st);
+
 pa_status launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
                                    int32_t num_tokens, void* k_pool, void* v_pool,
                                    const pa_pool_desc& pool, hipStream_t st);

@@ -1,0 +1,273 @@
+// Paged chunked-prefill attention for gfx950.
+//
+// A prefill step runs a chunk of a prompt's tokens through attention after
+// writing their K/V into the cache; a long prompt is cut into chunks that run
+// between decode steps (page "附录：Lazy Allocation 与 Copy-on-Write 在 LLM 推理
+// 系统中的应用" §2.1; page "vLLM：把 KV 缓存当成虚拟内存", section "KV 的体积从哪来，
+// 页表如何把它切开", which also notes that prefill is bound by compute and decode
+// by KV bandwidth).  Sequence i's chunk holds its tokens at positions
+// ctx_i - n_i .. ctx_i - 1; each attends to every earlier position of its
+// sequence and to itself (the autoregressive rule of the same §2.1).  K/V
+// rows are found through the block table as in decode.
+//
+// Work split: one wave per (sequence, kv head, block of query tokens).  The
+// G query heads of the kv head and 64 / G consecutive chunk tokens make 64
+// query rows, taken as four groups of 16: each group is the 16 columns of the
+// decode kernel's tile products (S^T = K . Q^T with v_mfma_f32_16x16x32, then
+// O^T += V^T . P^T with v_mfma_f32_16x16x16), so one K/V tile load feeds four
+// groups' products.  A wave walks the 16-key tiles from position 0 to its
+// last token through a register ring; the tiles at and past the block's first
+// position are masked per element.  Each lane keeps the softmax state of its
+// column in each group, with the decode kernel's lazy rescale.
+//
+// Grid (kv head, sequence, query-block group) with the last dimension
+// slowest: workgroup z takes query blocks nqb-1-4z .. nqb-4-4z of every
+// (kv head, sequence), so the heaviest blocks (latest positions, most keys)
+// start first; neighbouring ids share a kv head's sequence, so its K/V tiles
+// are read from L2 by the workgroups of the same sequence.
+#include <hip/hip_runtime.h>
+
+#include "pa.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kPfWaves = 4;                 // waves per workgroup
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kGroups = 4;                  // 16-column groups per wave
+constexpr int kRows = 16 * kGroups;         // query rows (token, head) per wave
+constexpr int kTile = 16;                   // keys per tile
+constexpr int kPfPrefetch = 2;              // tiles in the register ring
+constexpr float kRescaleSlack = 8.f;        // log2 units
+
+__device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
+  int ctx = a.context_lens[i];
+  ctx = min(ctx, a.max_ctx);
+  ctx = min(ctx, a.max_blocks << a.log2_bs);
+  return ctx;
+}
+
+template <class E>
+__global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
+  constexpr int D = 128;
+  using S = typename E::storage;
+  const int g = blockIdx.x, i = blockIdx.y;
+  const int G = a.group, QT = kRows / G;  // chunk tokens per wave
+  const int qa = a.query_start[i], qb = a.query_start[i + 1];
+  if (qa < 0 || qb > a.num_tokens || qb <= qa) return;
+  const int n = qb - qa;                   // chunk tokens: positions ctx - n ..
+  const int nqb = ceil_div(min(n, a.max_query), QT);  // rows past max_query are not run
+  const int blk = nqb - 1 - ((int)blockIdx.z * kPfWaves + wave_id());
+  if (blk < 0) return;
+  const int lane = threadIdx.x % kWave;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int ctx = clamp_ctx(a, i);
+  const int tok0 = blk * QT, ntok = min(QT, min(n, a.max_query) - tok0);
+  const int pos0 = ctx - n + tok0;  // position of the block's first token
+  const int kend = pos0 + ntok;     // keys [0, kend) are seen by some row
+
+  // This lane's column in each group: chunk token tl, head h of the group.
+  // lim = last position the column sees; rows without a query (past the
+  // chunk, or at a negative position) see every key like the last row, which
+  // keeps their state finite; they are never stored as attention outputs.
+  int lim[kGroups], row[kGroups];
+  bool live[kGroups];
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const int col = q * 16 + c16, tl = col / G, h = col - tl * G;
+    live[q] = tl < ntok && pos0 + tl >= 0;
+    lim[q] = live[q] ? pos0 + tl : kend - 1;
+    row[q] = tl < ntok ? (qa + tok0 + tl) * a.num_q_heads + g * G + h : -1;
+  }
+  S* out = reinterpret_cast<S*>(a.out);
+  if (kend <= 0) {  // every position negative: zero rows
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q)
+      if (row[q] >= 0)
+        for (int d = 8 * g4; d < D; d += 32) *reinterpret_cast<u32x4*>(out + (size_t)row[q] * D + d) = u32x4{0, 0, 0, 0};
+    return;
+  }
+
+  // q operand of each group: lane (c16, g4) holds q[column c16][32 s + 8 g4 .. +7]
+  u32x4 qv[kGroups][4];
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const S* qrow = reinterpret_cast<const S*>(a.q) + (size_t)max(row[q], 0) * D + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qv[q][s] = row[q] >= 0 ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+  }
+
+  const int bs_mask = (1 << a.log2_bs) - 1;
+  const size_t head_stride = (size_t)D << a.log2_bs;
+  const size_t block_stride = head_stride * a.num_kv_heads;
+  const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
+  const S* kbase0 = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride;
+  const S* vbase0 = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride;
+  const uint32_t k_lane_off = (uint32_t)(c16 * D + 8 * g4) * 2u;
+  const uint32_t v_lane_off = (uint32_t)((4 * g4) * D + 8 * c16) * 2u;
+  const int ntiles = ceil_div(kend, kTile);
+  const int unmasked = max(pos0, 0);  // every row sees keys <= this position
+
+  // Issue side: the block id of the next tile is read one issue ahead; tiles
+  // past the last (or with a bad block id) get an empty descriptor, so every
+  // issue has exactly 8 loads and the waits stay static.
+  int it = 0;
+  int iblk = scalar_load(table + 0);
+  auto issue = [&](u32x4 (&kr)[4], u32x4 (&vr)[4]) -> bool {
+    bool ok = false;
+    size_t off = 0;
+    if (it < ntiles) {
+      ok = (unsigned)iblk < (unsigned)a.num_blocks;
+      if (ok) off = (size_t)iblk * block_stride + (size_t)((it * kTile) & bs_mask) * D;
+      if (++it < ntiles) iblk = scalar_load(table + ((it * kTile) >> a.log2_bs));
+    }
+    const uint32_t bytes = ok ? kTile * D * 2u : 0u;
+    const rsrc_t kr_rs = make_rsrc(kbase0 + off, bytes);
+    const rsrc_t vr_rs = make_rsrc(vbase0 + off, bytes);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kr[s] = buffer_load16(kr_rs, k_lane_off + 64u * s);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vr[r] = buffer_load16(vr_rs, v_lane_off + 256u * r);
+    return ok;
+  };
+
+  float m[kGroups], l[kGroups];
+  f32x4 o[kGroups][8];
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    m[q] = neg_inf();
+    l[q] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One key tile for the four groups.
+  auto compute = [&](int t, u32x4 (&kc)[4], u32x4 (&vc)[4]) {
+    const int k0 = t * kTile;
+    if (k0 + kTile > ctx) {  // slots past the sequence may hold anything
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (k0 + 4 * g4 + r >= ctx) vc[r] = u32x4{0, 0, 0, 0};
+    }
+    u32x2 vw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      vw[e] = u32x2{__builtin_amdgcn_perm(vc[1][e >> 1], vc[0][e >> 1], sel),
+                    __builtin_amdgcn_perm(vc[3][e >> 1], vc[2][e >> 1], sel)};
+    }
+    const bool masked = k0 + kTile - 1 > unmasked;
+    // The tile in three phases over the groups -- every QK product, then
+    // every softmax update, then every PV product -- so the matrix cores work
+    // on one group's products while the vector ALU handles another's scores.
+    f32x4 sacc[kGroups];
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      sacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sacc[q] = Mfma<E>::qk(kc[s], qv[q][s], sacc[q]);
+    }
+    u32x2 pw[kGroups];
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = sacc[q][r] * a.scale_log2;
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (k0 + 4 * g4 + r > lim[q]) sv[r] = neg_inf();
+      }
+      const float lim_s = m[q] + kRescaleSlack;
+      const bool over = sv[0] > lim_s || sv[1] > lim_s || sv[2] > lim_s || sv[3] > lim_s;
+      if (__builtin_amdgcn_ballot_w64(over)) {
+        float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mt = fmaxf(mt, shfl_xor(mt, 16));
+        mt = fmaxf(mt, shfl_xor(mt, 32));
+        const float mn = fmaxf(m[q], mt);
+        const float alpha = fast_exp2(m[q] - mn);
+        l[q] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[q][e] *= alpha;
+        m[q] = mn;
+      }
+      uint32_t pb[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pb[r] = Mfma<E>::round16(fast_exp2(sv[r] - m[q]));
+        psum += bits_to_float(E{}, pb[r]);
+      }
+      l[q] += psum;
+      pw[q] = u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+    }
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[q][e] = Mfma<E>::pv(vw[e], pw[q], o[q][e]);
+  };
+
+  u32x4 kb[kPfPrefetch][4], vb[kPfPrefetch][4];
+  bool okb[kPfPrefetch];
+#pragma unroll
+  for (int s = 0; s < kPfPrefetch; ++s) okb[s] = issue(kb[s], vb[s]);
+  // Every slot issues on every path and the loop exits at the bottom of the
+  // unrolled body, so the compiler's wait counts stay static.
+  int t = 0;
+  do {
+#pragma unroll
+    for (int s = 0; s < kPfPrefetch; ++s) {
+      if (t < ntiles && okb[s]) compute(t, kb[s], vb[s]);
+      okb[s] = issue(kb[s], vb[s]);
+      ++t;
+    }
+  } while (t < ntiles);
+
+  // Lane (c16, g4) holds O[column c16][32 g4 + 8 r + e] = o[q][e][r].
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const float lsum = across_groups_sum<16>(l[q]);
+    if (row[q] < 0) continue;
+    const float inv = live[q] && lsum > 0.f ? 1.f / lsum : 0.f;
+    S* dst = out + (size_t)row[q] * D + 32 * g4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = float_to_bits(E{}, o[q][e][r] * inv);
+      *reinterpret_cast<u32x4*>(dst + 8 * r) =
+          u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+    }
+  }
+}
+
+template <class E>
+pa_status launch(const PrefillArgs& a, int max_query_blocks, hipStream_t st) {
+  const dim3 grid(a.num_kv_heads, a.num_seqs, ceil_div(max_query_blocks, kPfWaves));
+  hipLaunchKernelGGL((prefill_mfma<E>), grid, dim3(kPfThreads), 0, st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+bool prefill_supports(int dtype, int head_dim, int group) {
+  return (dtype == PA_F16 || dtype == PA_BF16) && head_dim == 128 &&
+         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+}
+
+int prefill_query_blocks(int max_query_len, int group) {
+  return max_query_len > 0 ? (max_query_len + kRows / group - 1) / (kRows / group) : 0;
+}
+
+pa_status launch_prefill(const PrefillArgs& a, int dtype, hipStream_t st) {
+  const int blocks = prefill_query_blocks(a.max_query, a.group);
+  if (blocks <= 0) return PA_OK;
+  if (dtype == PA_BF16) return launch<BF16>(a, blocks, st);
+  if (dtype == PA_F16) return launch<F16>(a, blocks, st);
+  return PA_ERR_SHAPE;
+}
+
+}  // namespace pa

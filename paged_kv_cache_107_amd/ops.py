@@ -113,6 +113,33 @@ def pa_decode_reduce(q, k_pool, v_pool, block_tables, context_lens, scale, out, 
                         scale, out, workspace, max_context_len, partition_tokens, stream)
 
 
+def pa_prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale, out,
+               max_query_len, max_context_len, stream=None):
+    """Chunked prefill attention over the paged cache.  See pa.h.
+
+    q, out [num_tokens][num_q_heads][head_dim]; query_start int32 [B+1];
+    block_tables int32 [B][max_blocks]; context_lens int32 [B]."""
+    desc = _check_pools(k_pool, v_pool)
+    _need_cuda("q", q, k_pool.dtype)
+    _need_cuda("out", out, k_pool.dtype)
+    _need_cuda("block_tables", block_tables, torch.int32)
+    _need_cuda("query_start", query_start, torch.int32)
+    _need_cuda("context_lens", context_lens, torch.int32)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim or out.shape != q.shape:
+        raise ValueError("q and out must be [num_tokens][num_q_heads][head_dim]")
+    t, hq, _ = q.shape
+    b = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or query_start.shape != (b + 1,):
+        raise ValueError("block_tables must be [B][max_blocks], query_start [B+1], "
+                         "context_lens [B]")
+    st = lib().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), C.byref(desc), _ptr(block_tables),
+                          int(block_tables.shape[1]), _ptr(query_start), _ptr(context_lens),
+                          int(b), int(t), int(hq), int(max_query_len), int(max_context_len),
+                          float(scale), _ptr(out), _stream(stream))
+    check("pa_prefill", st)
+    return out
+
+
 def pa_set_decode_path(path: int) -> int:
     prev = int(lib().pa_set_decode_path(int(path)))
     if prev < 0:
