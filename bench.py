@@ -18,7 +18,9 @@ fraction of the HBM peak, the partition kernel's roofline (algorithmic bytes
 over its average duration, timed with HIP events on the launch stream), the
 CPU oracle timed on a bounded sample of the same workload, and, apart from the
 timed step, the chunked-prefill kernel on its own workload with its
-matrix-core roofline.
+matrix-core roofline, and the prefill of requests sharing a system prompt
+with and without the prefix cache (hit rate, pinned blocks, blocks held,
+device time of the prefill pass, host time per request).
 """
 from __future__ import annotations
 
@@ -250,6 +252,103 @@ def measure_prefill(reps: int, log):
     }
 
 
+PREFIX_DESCRIPTION = ("8B GQA prompts sharing a system prompt, 1 layer: 100 requests, one "
+                      "1024-token system prompt + per-request suffix uniform [16, 256] tokens, "
+                      "32 q / 8 kv heads, head_dim 128, bf16, block 16, seed 6")
+
+
+def measure_prefix_cache(reps: int, log):
+    """The prefill of 100 requests that share a system prompt, with the
+    prefix cache and without it.  Host: the allocator's lookups and appends
+    (with token ids) for every request.  Device: one pass of the prefill path
+    over the positions left to compute -- the cache write of their K/V and
+    pa_prefill through the block tables -- timed with HIP events on the
+    launch stream, `reps` passes per variant."""
+    import torch
+    import paged_kv_cache_107_amd as pa
+    from paged_kv_cache_107_amd.cache import TORCH_DTYPES, PagedKVCache
+    ps = W.prompt_set("prefix_1k")
+    wl = ps.wl
+    tdt = TORCH_DTYPES[wl.dtype]
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits.view(np.int16))).cuda().view(tdt)
+
+    prompts = [W.prompt_token_ids(ps, r) for r in range(ps.requests)]
+    res = {}
+    for variant in ("cached", "uncached"):
+        cache = PagedKVCache(ps.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
+                             wl.dtype, ps.free_order)
+        if variant == "cached":
+            cache.enable_prefix_cache()
+        t0 = time.perf_counter()
+        slots, hits = [], []
+        for r, ids in enumerate(prompts):
+            s, hit = cache.create_prefix(ids) if variant == "cached" else (cache.create(), 0)
+            sl, _ = cache.reserve_tokens(s, ids[hit:])
+            slots.append(sl)
+            hits.append(hit)
+        host_s = time.perf_counter() - t0
+        hits = np.array(hits, dtype=np.int64)
+        kv = [W.prompt_kv_bits_of(ps, r) for r in range(ps.requests)]
+        k_new = dev(np.concatenate([k[h:] for (k, _), h in zip(kv, hits)]))
+        v_new = dev(np.concatenate([v[h:] for (_, v), h in zip(kv, hits)]))
+        del kv
+        q = dev(np.concatenate([W.prompt_query_bits_of(ps, r)[h:] for r, h in enumerate(hits)]))
+        out = torch.empty_like(q)
+        slot_t = torch.from_numpy(np.concatenate(slots)).cuda()
+        lens = ps.prompt_lens
+        tables, lens32 = cache.alloc.pa_build_tables(list(range(ps.requests)),
+                                                     int(-(-int(lens.max()) // wl.block_size)))
+        qs = torch.from_numpy(np.concatenate([[0], np.cumsum(lens - hits)]).astype(np.int32)).cuda()
+        args = (q, cache.k_pool, cache.v_pool, torch.from_numpy(tables).cuda(), qs,
+                torch.from_numpy(lens32).cuda(), wl.scale, out, int((lens - hits).max()),
+                int(lens.max()))
+
+        def one_pass():
+            pa.pa_reshape_and_cache(k_new, v_new, slot_t, cache.k_pool, cache.v_pool)
+            pa.pa_prefill(*args)
+
+        for _ in range(3):
+            one_pass()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            one_pass()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        held = int(np.unique(tables[tables >= 0]).size)
+        res[variant] = dict(us=us, held=held, host_s=host_s, computed=int((lens - hits).sum()),
+                            stats=cache.prefix_stats() if variant == "cached" else None)
+        del cache, k_new, v_new, q, out
+        torch.cuda.empty_cache()
+    c, u = res["cached"], res["uncached"]
+    st = c["stats"]
+    block_bytes = 2 * wl.num_kv_heads * wl.block_size * wl.head_dim * wl.elem_bytes
+    lookups_per_s = ps.requests / c["host_s"]
+    log(f"prefix cache: hit rate {st['hit_tokens'] / st['lookup_tokens']:.3f}, "
+        f"prefill pass {c['us']:.1f} us cached vs {u['us']:.1f} us uncached "
+        f"({u['us'] / c['us']:.2f}x), blocks held {c['held']} vs {u['held']}, "
+        f"host {1e6 * c['host_s'] / ps.requests:.1f} us per request")
+    return {
+        "workload": PREFIX_DESCRIPTION,
+        "hit_rate": round(st["hit_tokens"] / st["lookup_tokens"], 4),
+        "pinned_blocks": st["pinned_blocks"],
+        "cached_blocks": st["cached_blocks"],
+        "tokens_computed": {"cached": c["computed"], "uncached": u["computed"]},
+        "prefill_pass_us": {"cached": round(c["us"], 2), "uncached": round(u["us"], 2)},
+        "prefill_speedup": round(u["us"] / c["us"], 3),
+        "blocks_held": {"cached": c["held"], "uncached": u["held"]},
+        "kv_bytes_saved_per_layer": (u["held"] - c["held"]) * block_bytes,
+        "host_us_per_request": {"cached": round(1e6 * c["host_s"] / ps.requests, 2),
+                                "uncached": round(1e6 * u["host_s"] / ps.requests, 2)},
+        "host_lookups_per_s": round(lookups_per_s, 1),
+    }
+
+
 # ------------------------------------------------------------------ CPU oracle
 
 def cpu_baseline(d, gpu_out, budget_s: float, log):
@@ -313,6 +412,9 @@ def main(argv=None):
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--prefill-reps", type=int, default=20,
                     help="timed pa_prefill calls on the chunked-prefill workload (0 = skip)")
+    ap.add_argument("--prefix-reps", type=int, default=10,
+                    help="timed prefill passes per variant on the shared-system-prompt "
+                         "workload, with and without the prefix cache (0 = skip)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
@@ -414,6 +516,9 @@ def main(argv=None):
     prefill = None
     if args.prefill_reps > 0:
         prefill = measure_prefill(args.prefill_reps, log)
+    prefix = None
+    if args.prefix_reps > 0:
+        prefix = measure_prefix_cache(args.prefix_reps, log)
 
     rec = {
         "metric": METRIC,
@@ -452,6 +557,7 @@ def main(argv=None):
         "host_step_ms": round(host_step_ms, 3),
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "prefix_cache": prefix,
     }
     print(json.dumps(rec), flush=True)
     return 0

@@ -254,7 +254,8 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool,
  * pa_seq_share_prefix: a new sequence whose first ceil(n / BS) table entries
  * are src's, refcounts +1, length n (0 <= n <= src length; page "第 6 章
  * 缓存管理：把显存当操作系统来管", section "块表长什么样").
- * pa_seq_free: refcount -1 on each block; zero -> back to the free pool.
+ * pa_seq_free: refcount -1 on each block; zero -> back to the free pool
+ * (or, for a cached block, to the evictable list; see the prefix cache).
  * Sequence ids are assigned 0, 1, 2, ... in creation order, never reused.
  * ------------------------------------------------------------------------ */
 typedef struct pa_alloc pa_alloc;
@@ -292,10 +293,63 @@ pa_status pa_alloc_query(const pa_alloc* a, int32_t* num_free, int32_t* free_lis
  * sequences, blocks with refcount > 1. */
 pa_status pa_alloc_stats(const pa_alloc* a, int64_t* lazy_allocs, int64_t* cow_copies,
                          int32_t* live_seqs, int32_t* shared_blocks);
-/* PA_OK if refcount == in-degree over all tables, a block is free iff its
- * refcount is 0, the free pool has no duplicates and every table has
- * ceil(len / BS) entries; PA_ERR_REFCOUNT otherwise. */
+/* PA_OK if refcount == in-degree over all tables, a block is in the free
+ * pool iff its refcount is 0 and it is not cached, in the evictable list iff
+ * its refcount is 0 and it is cached, neither list has duplicates, the cache
+ * index and the cached blocks agree, and every table has ceil(len / BS)
+ * entries; PA_ERR_REFCOUNT otherwise. */
 pa_status pa_alloc_check_invariants(const pa_alloc* a);
+
+/* ------------------------------------------------------------------------
+ * Prefix cache.  A prefix many requests share (a system prompt) stays in
+ * memory as cached blocks kept out of the free pool, and a later request with
+ * the same prefix takes them instead of computing that prefill (page "vLLM：
+ * 把 KV 缓存当成虚拟内存", sections "碎片从哪里来" and "KV 的体积从哪来，页表如何
+ * 把它切开"; page "放下账簿，打开源码", section "写时复制与前缀缓存").  When
+ * memory runs out, cached blocks are dropped least recently used first and
+ * recomputed when needed (page "第 6 章 缓存管理", section "缓存放不下的时候").
+ *
+ * Rules:
+ *  - only full blocks whose token ids are known are cached, under the whole
+ *    token prefix up to the block's end (a chained 64-bit hash; the block's
+ *    own tokens and its parent's hash are compared on a hit);
+ *  - pa_seq_append_tokens caches each block it fills, unless that prefix is
+ *    already cached under another block (the first registration stays);
+ *    pa_seq_append and pa_seq_append_batch carry no ids and cache nothing
+ *    from the first position they write onwards;
+ *  - pa_seq_create_prefix walks the prompt's full blocks from the start and
+ *    takes each cached one (refcount + 1) up to the first miss, at most
+ *    n_tokens - 1 tokens (one prompt token is always left to compute); the
+ *    sequence's length is the hit length; the caller appends the rest;
+ *  - a cached block whose count drops to zero is evictable: released
+ *    sequences' cached blocks enter a least-recently-used list from the
+ *    sequence's last block to its first; a hit takes a block back out;
+ *  - new blocks come from the free pool, else by evicting the least recently
+ *    used evictable block (PA_ERR_OOM only when both are short);
+ *  - a cached block is never written: an append whose first position falls
+ *    in one copies it first (a CoW pair, as for a shared block).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t lookup_tokens;     /* prompt tokens looked up */
+  int64_t hit_tokens;        /* of which found cached */
+  int64_t evictions;         /* cached blocks dropped for new data */
+  int32_t cached_blocks;     /* blocks currently cached */
+  int32_t evictable_blocks;  /* cached with refcount 0 */
+  int32_t pinned_blocks;     /* cached with refcount > 0 */
+} pa_prefix_stats;
+
+/* Turns the cache on; PA_ERR_ARG once any sequence exists. */
+pa_status pa_alloc_enable_prefix_cache(pa_alloc* a);
+/* A new sequence for a prompt of n_tokens ids (host int32); *hit_tokens_out
+ * = tokens found cached.  PA_ERR_ARG if the cache is off. */
+pa_status pa_seq_create_prefix(pa_alloc* a, const int32_t* tokens, int32_t n_tokens,
+                               int64_t* seq_out, int32_t* hit_tokens_out);
+/* pa_seq_append with the new positions' token ids (host int32 [n_tokens]). */
+pa_status pa_seq_append_tokens(pa_alloc* a, int64_t seq, const int32_t* tokens, int32_t n_tokens,
+                               int64_t* slots_out, int32_t* cow_pair_out, int32_t* num_cow_out);
+pa_status pa_prefix_cache_stats(const pa_alloc* a, pa_prefix_stats* out);
+/* Evictable blocks, least recently used first (evictable_out [NB] or NULL). */
+pa_status pa_prefix_cache_query(const pa_alloc* a, int32_t* evictable_out, int32_t* num_out);
 
 #ifdef __cplusplus
 }

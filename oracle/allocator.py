@@ -39,10 +39,41 @@ Readings where the pages are silent (each one is a documented choice):
 * Sharing ``n`` tokens copies ``ceil(n / BS)`` entries even when the last one
   holds more of the source's tokens; the sharer's length masks them and its
   first write into that block copies it.
+
+Prefix cache (``enable_prefix_cache``): a prompt prefix that many requests
+share stays in memory as cached blocks, marked as cached and kept out of the
+free pool, so a later request with the same prefix finds them and skips that
+prefill ("vLLM：把 KV 缓存当成虚拟内存", sections "碎片从哪里来" and "KV 的体积
+从哪来，页表如何把它切开"; "放下账簿，打开源码", section "写时复制与前缀缓存");
+when memory runs out, cached blocks are dropped least recently used first and
+recomputed when needed ("第 6 章 缓存管理", section "缓存放不下的时候").
+Readings (the pages give no mechanism):
+
+* Only full blocks are cached; a block's identity is the whole token prefix
+  up to its end (here the exact tuple of token ids; two requests with the same
+  tokens up to there have the same K/V there).  A block is registered when an
+  append with known token ids fills it, unless that prefix is already cached
+  under another block (the first registration stays).
+* A lookup for a new request walks its full blocks from the start and takes
+  every cached block (refcount + 1) until the first miss, leaving at least
+  one prompt token to compute (the last token's query produces the next
+  token).
+* A released block whose count reaches zero goes to the back of the free pool
+  if it is not cached; a cached one becomes evictable and enters a
+  least-recently-used list: the released sequence's cached blocks enter it
+  from its last block to its first, so a shared prompt's first blocks are
+  the most recently used and are evicted last.  A lookup hit on an evictable
+  block takes it out of the list.
+* A new block comes from the front of the free pool, or, when that is empty,
+  by evicting the least recently used evictable block (its registration is
+  dropped).  An append fails with OOM only if both are short.
+* A cached block is never written: an append whose first position falls in a
+  cached block (possible after sharing a prefix that ends mid-block) copies
+  it first, as for a shared block.
 """
 from __future__ import annotations
 
-from collections import deque
+from collections import OrderedDict, deque
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -81,6 +112,15 @@ class OracleAllocator:
         # counters
         self.lazy_allocs = 0
         self.cow_copies = 0
+        # prefix cache (off until enable_prefix_cache)
+        self.caching = False
+        self.tokens: Dict[int, List[int]] = {}    # known token ids of each sequence
+        self.index: Dict[tuple, int] = {}          # token prefix -> cached block
+        self.block_key: Dict[int, tuple] = {}      # cached block -> its prefix
+        self.lru: "OrderedDict[int, None]" = OrderedDict()  # evictable, least recent first
+        self.lookup_tokens = 0
+        self.hit_tokens = 0
+        self.evictions = 0
 
     # ------------------------------------------------------------ helpers
     def _seq(self, seq: int) -> List[int]:
@@ -93,12 +133,80 @@ class OracleAllocator:
         self._next_seq += 1
         return s
 
+    def _available(self) -> int:
+        return len(self.free) + len(self.lru)
+
+    def _take(self) -> int:
+        """A block for new data: free pool front, else evict the least
+        recently used cached block."""
+        if self.free:
+            return self.free.popleft()
+        blk, _ = self.lru.popitem(last=False)
+        del self.index[self.block_key.pop(blk)]
+        self.evictions += 1
+        return blk
+
+    def _register(self, seq: int) -> None:
+        """Cache every full block of ``seq`` whose token ids are all known."""
+        if not self.caching:
+            return
+        bs = self.block_size
+        known = self.tokens[seq]
+        table = self.tables[seq]
+        full = min(self.lens[seq], len(known)) // bs
+        for j in range(full):
+            key = tuple(known[:(j + 1) * bs])
+            blk = table[j]
+            if key not in self.index and blk not in self.block_key:
+                self.index[key] = blk
+                self.block_key[blk] = key
+
     # ------------------------------------------------------------ operations
     def create(self) -> int:
         s = self._new_id()
         self.tables[s] = []
         self.lens[s] = 0
+        self.tokens[s] = []
         return s
+
+    def enable_prefix_cache(self) -> None:
+        if self.tables:
+            raise OracleError("ARG", "enable the prefix cache before creating sequences")
+        self.caching = True
+
+    def create_prefix(self, prompt: Sequence[int]) -> Tuple[int, int]:
+        """A new sequence for ``prompt``: its longest cached prefix of whole
+        blocks (at most len(prompt) - 1 tokens) is shared; returns (seq,
+        hit_tokens).  The caller appends prompt[hit_tokens:] next."""
+        if not self.caching:
+            raise OracleError("ARG", "prefix cache is off")
+        prompt = [int(t) for t in prompt]
+        bs = self.block_size
+        s = self.create()
+        hits = 0
+        for j in range(max(len(prompt) - 1, 0) // bs):
+            blk = self.index.get(tuple(prompt[:(j + 1) * bs]))
+            if blk is None:
+                break
+            if self.refcount[blk] == 0:
+                del self.lru[blk]
+            self.refcount[blk] += 1
+            self.tables[s].append(blk)
+            hits += 1
+        self.lens[s] = hits * bs
+        self.tokens[s] = prompt[:hits * bs]
+        self.lookup_tokens += len(prompt)
+        self.hit_tokens += hits * bs
+        return s, hits * bs
+
+    def append_tokens(self, seq: int, ids: Sequence[int]):
+        """``append`` with the token ids of the new positions: full blocks
+        whose ids are all known are cached."""
+        slots, pair = self.append(seq, len(ids))
+        if len(self.tokens[seq]) == self.lens[seq] - len(ids):
+            self.tokens[seq].extend(int(t) for t in ids)
+        self._register(seq)
+        return slots, pair
 
     def append(self, seq: int, n_tokens: int) -> Tuple[List[int], Optional[Tuple[int, int]]]:
         """Write positions len..len+n-1.  Returns (slots, cow_pair or None)."""
@@ -110,16 +218,20 @@ class OracleAllocator:
         end = start + n_tokens
         if n_tokens == 0:
             return [], None
-        # is the first position inside an existing, shared block?
-        needs_cow = start % bs != 0 and self.refcount[table[start // bs]] > 1
+        # is the first position inside an existing block that is shared, or
+        # cached (a cached block's contents must not change)?
+        needs_cow = start % bs != 0 and (self.refcount[table[start // bs]] > 1
+                                         or table[start // bs] in self.block_key)
         new_blocks = _ceil_div(end, bs) - _ceil_div(start, bs)
-        if new_blocks + int(needs_cow) > len(self.free):
-            raise OracleError("OOM", f"need {new_blocks + int(needs_cow)}, free {len(self.free)}")
+        if new_blocks + int(needs_cow) > self._available():
+            raise OracleError("OOM", f"need {new_blocks + int(needs_cow)}, free {self._available()}")
         pair = None
         if needs_cow:
             src = table[start // bs]
-            dst = self.free.popleft()
+            dst = self._take()
             self.refcount[src] -= 1
+            if self.refcount[src] == 0:           # a cached block's last holder copied
+                self.lru[src] = None
             self.refcount[dst] = 1
             table[start // bs] = dst
             pair = (src, dst)
@@ -127,7 +239,7 @@ class OracleAllocator:
         slots = []
         for pos in range(start, end):
             if pos % bs == 0:
-                blk = self.free.popleft()
+                blk = self._take()
                 self.refcount[blk] = 1
                 table.append(blk)
                 self.lazy_allocs += 1
@@ -140,6 +252,7 @@ class OracleAllocator:
         child = self._new_id()
         self.tables[child] = list(table)
         self.lens[child] = self.lens[parent]
+        self.tokens[child] = list(self.tokens[parent])
         for b in table:
             self.refcount[b] += 1
         return child
@@ -152,6 +265,7 @@ class OracleAllocator:
         s = self._new_id()
         self.tables[s] = list(table[:k])
         self.lens[s] = n_tokens
+        self.tokens[s] = list(self.tokens[src][:n_tokens])
         for b in self.tables[s]:
             self.refcount[b] += 1
         return s
@@ -161,11 +275,20 @@ class OracleAllocator:
         for b in table:
             if self.refcount[b] <= 0:
                 raise OracleError("REFCOUNT", f"block {b} already free")
+        released = []
+        for b in table:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
+                released.append(b)
+        for b in released:                      # uncached: free pool, logical order
+            if b not in self.block_key:
                 self.free.append(b)
+        for b in reversed(released):            # cached: LRU, last block first
+            if b in self.block_key:
+                self.lru[b] = None
         del self.tables[seq]
         del self.lens[seq]
+        del self.tokens[seq]
 
     def build_tables(self, seqs: Sequence[int], max_blocks: int):
         """Block tables [n][max_blocks] int32 padded with -1, and lengths [n]."""
@@ -196,10 +319,26 @@ class OracleAllocator:
         if len(free_set) != len(self.free):
             raise AssertionError("duplicate block in the free pool")
         for b in range(self.num_blocks):
-            if (b in free_set) != (self.refcount[b] == 0):
+            idle = self.refcount[b] == 0
+            cached = b in self.block_key
+            if (b in free_set) != (idle and not cached):
                 raise AssertionError(f"block {b}: free={b in free_set} refcount={self.refcount[b]}")
+            if (b in self.lru) != (idle and cached):
+                raise AssertionError(f"block {b}: evictable={b in self.lru} cached={cached}")
+        if len(self.index) != len(self.block_key) or any(
+                self.block_key.get(b) != k for k, b in self.index.items()):
+            raise AssertionError("cache index and block keys differ")
+        for k in self.index:
+            if len(k) % self.block_size:
+                raise AssertionError("a cached key is not a whole number of blocks")
 
     def snapshot(self):
         """(free FIFO as a list, refcounts, {seq: (table, len)}) for comparisons."""
         return (list(self.free), list(self.refcount),
                 {s: (list(t), self.lens[s]) for s, t in self.tables.items()})
+
+    def prefix_stats(self) -> Dict[str, int]:
+        return dict(lookup_tokens=self.lookup_tokens, hit_tokens=self.hit_tokens,
+                    evictions=self.evictions, cached_blocks=len(self.block_key),
+                    evictable_blocks=len(self.lru),
+                    pinned_blocks=sum(1 for b in self.block_key if self.refcount[b] > 0))

@@ -25,6 +25,12 @@ _vp, _i32, _i64, _f32, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_si
 _pi32, _pi64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
 _desc = C.POINTER(pa_pool_desc)
 
+class pa_prefix_stats(C.Structure):
+    _fields_ = [("lookup_tokens", C.c_int64), ("hit_tokens", C.c_int64), ("evictions", C.c_int64),
+                ("cached_blocks", C.c_int32), ("evictable_blocks", C.c_int32),
+                ("pinned_blocks", C.c_int32)]
+
+
 _DECODE_ARGS = [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _sz,
                 _i32, _vp]
 
@@ -53,6 +59,11 @@ SIGNATURES = {
     "pa_alloc_query": (_i32, [_vp, _pi32, _pi32, _pi32]),
     "pa_alloc_stats": (_i32, [_vp, _pi64, _pi64, _pi32, _pi32]),
     "pa_alloc_check_invariants": (_i32, [_vp]),
+    "pa_alloc_enable_prefix_cache": (_i32, [_vp]),
+    "pa_seq_create_prefix": (_i32, [_vp, _pi32, _i32, _pi64, _pi32]),
+    "pa_seq_append_tokens": (_i32, [_vp, _i64, _pi32, _i32, _pi64, _pi32, _pi32]),
+    "pa_prefix_cache_stats": (_i32, [_vp, C.POINTER(pa_prefix_stats)]),
+    "pa_prefix_cache_query": (_i32, [_vp, _pi32, _pi32]),
 }
 
 _lib = None

@@ -9,7 +9,7 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-from ._lib import PaError, check, lib
+from ._lib import PaError, check, lib, pa_prefix_stats
 
 
 def _i32p(a: np.ndarray):
@@ -126,3 +126,38 @@ class PaAllocator:
         if st not in (0, -5):
             raise PaError("pa_alloc_check_invariants", st)
         return st == 0
+
+    # ------------------------------------------------------------ prefix cache
+    def pa_alloc_enable_prefix_cache(self) -> None:
+        check("pa_alloc_enable_prefix_cache", lib().pa_alloc_enable_prefix_cache(self._h))
+
+    def pa_seq_create_prefix(self, tokens: Sequence[int]) -> Tuple[int, int]:
+        """(sequence, hit_tokens) for a prompt of token ids."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        s, hit = C.c_int64(), C.c_int32()
+        check("pa_seq_create_prefix", lib().pa_seq_create_prefix(
+            self._h, _i32p(t) if t.size else None, int(t.size), C.byref(s), C.byref(hit)))
+        return s.value, hit.value
+
+    def pa_seq_append_tokens(self, seq: int, tokens: Sequence[int]):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = int(t.size)
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        pair = np.zeros(2, dtype=np.int32)
+        ncow = C.c_int32()
+        check("pa_seq_append_tokens", lib().pa_seq_append_tokens(
+            self._h, int(seq), _i32p(t) if n else None, n, _i64p(slots), _i32p(pair),
+            C.byref(ncow)))
+        return slots[:n], ((int(pair[0]), int(pair[1])) if ncow.value else None)
+
+    def pa_prefix_cache_stats(self) -> dict:
+        st = pa_prefix_stats()
+        check("pa_prefix_cache_stats", lib().pa_prefix_cache_stats(self._h, C.byref(st)))
+        return {f: getattr(st, f) for f, _ in pa_prefix_stats._fields_}
+
+    def pa_prefix_cache_query(self) -> np.ndarray:
+        """Evictable blocks, least recently used first."""
+        n = C.c_int32()
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        check("pa_prefix_cache_query", lib().pa_prefix_cache_query(self._h, _i32p(out), C.byref(n)))
+        return out[:n.value]

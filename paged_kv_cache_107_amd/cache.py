@@ -74,6 +74,23 @@ class PagedKVCache:
         """Host only: slots for the next n tokens of seq (and a CoW pair)."""
         return self.alloc.pa_seq_append(seq, n_tokens)
 
+    # ------------------------------------------------------------ prefix cache
+    def enable_prefix_cache(self) -> None:
+        self.alloc.pa_alloc_enable_prefix_cache()
+
+    def create_prefix(self, token_ids: Sequence[int]):
+        """A sequence for a prompt: (seq, hit_tokens); the prompt's first
+        hit_tokens positions are cached blocks already holding their K/V."""
+        return self.alloc.pa_seq_create_prefix(token_ids)
+
+    def reserve_tokens(self, seq: int, token_ids: Sequence[int]):
+        """``reserve`` with the new positions' token ids, so that full blocks
+        can be cached for later prompts."""
+        return self.alloc.pa_seq_append_tokens(seq, token_ids)
+
+    def prefix_stats(self) -> dict:
+        return self.alloc.pa_prefix_cache_stats()
+
     # ------------------------------------------------------------ device work
     def _dev(self, a: np.ndarray, dtype) -> torch.Tensor:
         return torch.from_numpy(np.ascontiguousarray(a)).to(self.device, dtype)

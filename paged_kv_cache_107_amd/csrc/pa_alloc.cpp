@@ -14,9 +14,25 @@
 //  * prefix sharing and release to the free pool at refcount zero ("第 6 章
 //    缓存管理：把显存当操作系统来管", section "块表长什么样").
 //
+//  * the prefix cache: full blocks of a common prompt prefix stay cached, kept
+//    out of the free pool, and later requests with that prefix take them
+//    instead of computing it ("vLLM：把 KV 缓存当成虚拟内存", sections
+//    "碎片从哪里来" and "KV 的体积从哪来，页表如何把它切开"; "放下账簿，打开源码",
+//    section "写时复制与前缀缓存"); when memory runs out cached blocks are dropped
+//    least recently used first ("第 6 章 缓存管理", section "缓存放不下的时候").
+//
 // Policy choices the pages leave open: FIFO free pool (pop front, push back in
 // logical order on release); all-or-nothing appends; at most one CoW copy per
 // append (only the first written position can fall in an existing block).
+// Prefix cache: only full blocks whose token ids are known are cached, keyed
+// by the whole token prefix up to the block's end (a chained 64-bit hash, with
+// the block's own tokens and its parent's hash kept and compared on a hit);
+// the first registration of a prefix stays; a lookup takes cached blocks from
+// the start of the prompt up to the first miss and leaves at least one token;
+// released cached blocks enter a least-recently-used list from the sequence's
+// last block to its first; new blocks come from the free pool, else by
+// evicting the least recently used cached block; a cached block is never
+// written (an append into one copies it first).
 #include <algorithm>
 #include <cstring>
 #include <deque>
@@ -34,16 +50,119 @@ struct pa_alloc {
   struct Seq {
     std::vector<int32_t> table;
     int32_t len = 0;
+    std::vector<int32_t> tokens;  // known token ids of positions 0 .. tokens.size()-1
+    std::vector<uint64_t> hashes;  // chain hash of each leading full known block
   };
   std::unordered_map<int64_t, Seq> seqs;
   int64_t next_id = 0;
   int64_t lazy_allocs = 0;
   int64_t cow_copies = 0;
+
+  // prefix cache
+  bool caching = false;
+  std::unordered_map<uint64_t, int32_t> index;  // prefix hash -> cached block
+  std::vector<char> cached;                     // per block
+  std::vector<uint64_t> key_of, parent_of;      // per cached block
+  std::vector<std::vector<int32_t>> tokens_of;  // per cached block
+  std::vector<int32_t> lru_prev, lru_next;      // evictable blocks, head = least recent
+  std::vector<char> in_lru;
+  int32_t lru_head = -1, lru_tail = -1, lru_size = 0;
+  int64_t lookup_tokens = 0, hit_tokens = 0, evictions = 0;
 };
 
 namespace {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- prefix cache
+constexpr uint64_t kRootHash = 0x9E3779B97F4A7C15ull;
+
+inline uint64_t mix64(uint64_t x) {  // splitmix64 finaliser
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+// Hash of a block's prefix: its parent's hash and the block's token ids.
+uint64_t chain_hash(uint64_t parent, const int32_t* tok, int32_t bs) {
+  uint64_t h = mix64(parent);
+  for (int32_t i = 0; i < bs; ++i) h = mix64(h ^ (uint64_t)(uint32_t)tok[i]);
+  return h;
+}
+
+void lru_push_back(pa_alloc* a, int32_t b) {
+  a->lru_prev[b] = a->lru_tail;
+  a->lru_next[b] = -1;
+  if (a->lru_tail >= 0) a->lru_next[a->lru_tail] = b; else a->lru_head = b;
+  a->lru_tail = b;
+  a->in_lru[b] = 1;
+  a->lru_size += 1;
+}
+
+void lru_remove(pa_alloc* a, int32_t b) {
+  const int32_t p = a->lru_prev[b], n = a->lru_next[b];
+  if (p >= 0) a->lru_next[p] = n; else a->lru_head = n;
+  if (n >= 0) a->lru_prev[n] = p; else a->lru_tail = p;
+  a->in_lru[b] = 0;
+  a->lru_size -= 1;
+}
+
+inline int64_t available(const pa_alloc* a) {
+  return (int64_t)a->free_pool.size() + a->lru_size;
+}
+
+// A block for new data: free pool front, else evict the least recently used
+// cached block (its registration goes).  The caller checked available().
+int32_t take_block(pa_alloc* a) {
+  if (!a->free_pool.empty()) {
+    const int32_t b = a->free_pool.front();
+    a->free_pool.pop_front();
+    return b;
+  }
+  const int32_t b = a->lru_head;
+  lru_remove(a, b);
+  a->index.erase(a->key_of[b]);
+  a->cached[b] = 0;
+  a->tokens_of[b].clear();
+  a->tokens_of[b].shrink_to_fit();
+  a->evictions += 1;
+  return b;
+}
+
+// Cache every full block of `s` whose token ids are all known.
+void register_blocks(pa_alloc* a, pa_alloc::Seq& s) {
+  if (!a->caching) return;
+  const int32_t bs = a->block_size;
+  const int64_t full = std::min<int64_t>(s.len, (int64_t)s.tokens.size()) / bs;
+  for (int64_t j = (int64_t)s.hashes.size(); j < full; ++j) {
+    const uint64_t parent = j ? s.hashes[j - 1] : kRootHash;
+    const int32_t* tok = s.tokens.data() + j * bs;
+    const uint64_t h = chain_hash(parent, tok, bs);
+    s.hashes.push_back(h);
+    const int32_t b = s.table[j];
+    if (a->cached[b] || a->index.count(h)) continue;
+    a->index.emplace(h, b);
+    a->cached[b] = 1;
+    a->key_of[b] = h;
+    a->parent_of[b] = parent;
+    a->tokens_of[b].assign(tok, tok + bs);
+  }
+}
+
+// Drops one reference from each block of a released table.  Blocks that
+// reach zero go to the back of the free pool in logical order if uncached;
+// cached ones enter the LRU list from the table's last block to its first, so
+// a sequence's first blocks are its most recently used.
+void release_table(pa_alloc* a, const std::vector<int32_t>& table) {
+  std::vector<int32_t> released;
+  for (int32_t b : table)
+    if (--a->refcount[b] == 0) released.push_back(b);
+  for (int32_t b : released)
+    if (!a->cached[b]) a->free_pool.push_back(b);
+  for (auto it = released.rbegin(); it != released.rend(); ++it)
+    if (a->cached[*it]) lru_push_back(a, *it);
+}
 
 // Blocks an append of n tokens to `s` needs: fresh blocks for the positions
 // that start a logical block, plus one if the first position lands in a
@@ -53,12 +172,21 @@ struct AppendPlan {
   bool cow;
 };
 
+// The first written position falls in an existing block that must not be
+// written in place: shared (refcount > 1) or cached.
+inline bool must_copy(const pa_alloc* a, int32_t b, int32_t refcount) {
+  return refcount > 1 || a->cached[b];
+}
+
 AppendPlan plan_append(const pa_alloc* a, const pa_alloc::Seq& s, int32_t n) {
   AppendPlan p{0, false};
   if (n <= 0) return p;
   const int64_t bs = a->block_size;
   const int64_t start = s.len, end = start + n;
-  p.cow = (start % bs != 0) && a->refcount[s.table[start / bs]] > 1;
+  if (start % bs != 0) {
+    const int32_t last = s.table[start / bs];
+    p.cow = must_copy(a, last, a->refcount[last]);
+  }
   p.new_blocks = ceil_div(end, bs) - ceil_div(start, bs);
   return p;
 }
@@ -72,13 +200,13 @@ void do_append(pa_alloc* a, pa_alloc::Seq& s, int32_t n, int64_t* slots, int32_t
   if (n <= 0) return;
   if (start % bs != 0) {
     int32_t& last = s.table[start / bs];
-    if (a->refcount[last] > 1) {
-      const int32_t dst = a->free_pool.front();
-      a->free_pool.pop_front();
-      pair[0] = last;
+    if (must_copy(a, last, a->refcount[last])) {
+      const int32_t src = last;
+      const int32_t dst = take_block(a);
+      pair[0] = src;
       pair[1] = dst;
       *num_pair = 1;
-      a->refcount[last] -= 1;
+      if (--a->refcount[src] == 0) lru_push_back(a, src);  // a cached block's last holder
       a->refcount[dst] = 1;
       last = dst;
       a->cow_copies += 1;
@@ -86,8 +214,7 @@ void do_append(pa_alloc* a, pa_alloc::Seq& s, int32_t n, int64_t* slots, int32_t
   }
   for (int64_t pos = start; pos < end; ++pos) {
     if (pos % bs == 0) {
-      const int32_t b = a->free_pool.front();
-      a->free_pool.pop_front();
+      const int32_t b = take_block(a);
       a->refcount[b] = 1;
       s.table.push_back(b);
       a->lazy_allocs += 1;
@@ -110,6 +237,13 @@ pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
   a->num_blocks = num_blocks;
   a->block_size = block_size;
   a->refcount.assign(num_blocks, 0);
+  a->cached.assign(num_blocks, 0);
+  a->key_of.assign(num_blocks, 0);
+  a->parent_of.assign(num_blocks, 0);
+  a->tokens_of.resize(num_blocks);
+  a->lru_prev.assign(num_blocks, -1);
+  a->lru_next.assign(num_blocks, -1);
+  a->in_lru.assign(num_blocks, 0);
   if (initial_free_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -146,8 +280,85 @@ pa_status pa_seq_append(pa_alloc* a, int64_t seq, int32_t n_tokens, int64_t* slo
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
   if ((int64_t)it->second.len + n_tokens > INT32_MAX) return PA_ERR_ARG;
   const AppendPlan p = plan_append(a, it->second, n_tokens);
-  if (p.new_blocks + (p.cow ? 1 : 0) > (int64_t)a->free_pool.size()) return PA_ERR_OOM;
+  if (p.new_blocks + (p.cow ? 1 : 0) > available(a)) return PA_ERR_OOM;
   do_append(a, it->second, n_tokens, slots_out, cow_pair_out, num_cow_out);
+  return PA_OK;
+}
+
+pa_status pa_seq_append_tokens(pa_alloc* a, int64_t seq, const int32_t* tokens, int32_t n_tokens,
+                               int64_t* slots_out, int32_t* cow_pair_out, int32_t* num_cow_out) {
+  if (!a || n_tokens < 0 || (n_tokens > 0 && !tokens)) return PA_ERR_ARG;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
+  const int32_t before = it->second.len;
+  const pa_status st = pa_seq_append(a, seq, n_tokens, slots_out, cow_pair_out, num_cow_out);
+  if (st != PA_OK) return st;
+  pa_alloc::Seq& s = a->seqs.find(seq)->second;
+  if ((int64_t)s.tokens.size() == before) s.tokens.insert(s.tokens.end(), tokens, tokens + n_tokens);
+  register_blocks(a, s);
+  return PA_OK;
+}
+
+pa_status pa_alloc_enable_prefix_cache(pa_alloc* a) {
+  if (!a || !a->seqs.empty()) return PA_ERR_ARG;
+  a->caching = true;
+  return PA_OK;
+}
+
+pa_status pa_seq_create_prefix(pa_alloc* a, const int32_t* tokens, int32_t n_tokens,
+                               int64_t* seq_out, int32_t* hit_tokens_out) {
+  if (!a || !seq_out || !hit_tokens_out || n_tokens < 0 || (n_tokens > 0 && !tokens) ||
+      !a->caching)
+    return PA_ERR_ARG;
+  const int32_t bs = a->block_size;
+  pa_alloc::Seq s;
+  uint64_t parent = kRootHash;
+  const int64_t max_blocks = n_tokens > 0 ? (int64_t)(n_tokens - 1) / bs : 0;
+  for (int64_t j = 0; j < max_blocks; ++j) {
+    const int32_t* tok = tokens + j * bs;
+    const uint64_t h = chain_hash(parent, tok, bs);
+    auto hit = a->index.find(h);
+    if (hit == a->index.end()) break;
+    const int32_t b = hit->second;
+    if (a->parent_of[b] != parent || !std::equal(tok, tok + bs, a->tokens_of[b].begin())) break;
+    if (a->refcount[b] == 0) lru_remove(a, b);
+    a->refcount[b] += 1;
+    s.table.push_back(b);
+    s.hashes.push_back(h);
+    parent = h;
+  }
+  s.len = (int32_t)(s.table.size() * bs);
+  s.tokens.assign(tokens, tokens + s.len);
+  a->lookup_tokens += n_tokens;
+  a->hit_tokens += s.len;
+  const int64_t id = a->next_id++;
+  *hit_tokens_out = s.len;
+  a->seqs.emplace(id, std::move(s));
+  *seq_out = id;
+  return PA_OK;
+}
+
+pa_status pa_prefix_cache_stats(const pa_alloc* a, pa_prefix_stats* out) {
+  if (!a || !out) return PA_ERR_ARG;
+  out->lookup_tokens = a->lookup_tokens;
+  out->hit_tokens = a->hit_tokens;
+  out->evictions = a->evictions;
+  int32_t cached = 0, pinned = 0;
+  for (int32_t b = 0; b < a->num_blocks; ++b) {
+    cached += a->cached[b];
+    pinned += a->cached[b] && a->refcount[b] > 0;
+  }
+  out->cached_blocks = cached;
+  out->evictable_blocks = a->lru_size;
+  out->pinned_blocks = pinned;
+  return PA_OK;
+}
+
+pa_status pa_prefix_cache_query(const pa_alloc* a, int32_t* evictable_out, int32_t* num_out) {
+  if (!a) return PA_ERR_ARG;
+  if (num_out) *num_out = a->lru_size;
+  if (evictable_out)
+    for (int32_t b = a->lru_head, k = 0; b >= 0; b = a->lru_next[b]) evictable_out[k++] = b;
   return PA_OK;
 }
 
@@ -170,23 +381,29 @@ pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32
     if ((int64_t)it->second.len + n_tokens > INT32_MAX) return PA_ERR_ARG;
     ptrs[i] = &it->second;
   }
-  int64_t need = 0;
+  // Each append must fit what is available when it runs, as if the appends
+  // were made one by one: a copied cached block whose last holder wrote
+  // becomes evictable for the appends after it.
+  int64_t avail = available(a);
   std::unordered_map<int32_t, int32_t> drops;  // block -> refcount drops so far
   const int64_t bs = a->block_size;
   for (int32_t i = 0; i < n && n_tokens > 0; ++i) {
     const pa_alloc::Seq& s = *ptrs[i];
     const int64_t start = s.len, end = start + n_tokens;
-    need += ceil_div(end, bs) - ceil_div(start, bs);
+    int64_t need = ceil_div(end, bs) - ceil_div(start, bs);
+    bool released = false;
     if (start % bs != 0) {
       const int32_t last = s.table[start / bs];
       const int32_t rc = a->refcount[last] - drops[last];
-      if (rc > 1) {
+      if (must_copy(a, last, rc)) {
         need += 1;
         drops[last] += 1;
+        released = rc == 1;
       }
     }
+    if (need > avail) return PA_ERR_OOM;
+    avail -= need - (released ? 1 : 0);
   }
-  if (need > (int64_t)a->free_pool.size()) return PA_ERR_OOM;
   int32_t np = 0;
   for (int32_t i = 0; i < n; ++i) {
     int32_t one = 0;
@@ -215,9 +432,15 @@ pa_status pa_seq_share_prefix(pa_alloc* a, int64_t src, int32_t n_tokens, int64_
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
   if (n_tokens < 0 || n_tokens > it->second.len) return PA_ERR_ARG;
   pa_alloc::Seq s;
+  const pa_alloc::Seq& src_seq = it->second;
   const int64_t k = ceil_div(n_tokens, a->block_size);
-  s.table.assign(it->second.table.begin(), it->second.table.begin() + k);
+  s.table.assign(src_seq.table.begin(), src_seq.table.begin() + k);
   s.len = n_tokens;
+  s.tokens.assign(src_seq.tokens.begin(),
+                  src_seq.tokens.begin() + std::min<int64_t>(n_tokens, src_seq.tokens.size()));
+  s.hashes.assign(src_seq.hashes.begin(),
+                  src_seq.hashes.begin() +
+                      std::min<int64_t>(n_tokens / a->block_size, src_seq.hashes.size()));
   for (int32_t b : s.table) a->refcount[b] += 1;
   const int64_t id = a->next_id++;
   a->seqs.emplace(id, std::move(s));
@@ -231,9 +454,7 @@ pa_status pa_seq_free(pa_alloc* a, int64_t seq) {
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
   for (int32_t b : it->second.table)
     if (a->refcount[b] <= 0) return PA_ERR_REFCOUNT;
-  for (int32_t b : it->second.table) {
-    if (--a->refcount[b] == 0) a->free_pool.push_back(b);
-  }
+  release_table(a, it->second.table);
   a->seqs.erase(it);
   return PA_OK;
 }
@@ -313,8 +534,23 @@ pa_status pa_alloc_check_invariants(const pa_alloc* a) {
     if (b < 0 || b >= a->num_blocks || in_free[b]) return PA_ERR_REFCOUNT;
     in_free[b] = 1;
   }
-  for (int32_t b = 0; b < a->num_blocks; ++b)
-    if ((bool)in_free[b] != (a->refcount[b] == 0)) return PA_ERR_REFCOUNT;
+  int32_t lru = 0;
+  for (int32_t b = a->lru_head, prev = -1; b >= 0; prev = b, b = a->lru_next[b]) {
+    if (!a->in_lru[b] || a->lru_prev[b] != prev || ++lru > a->num_blocks) return PA_ERR_REFCOUNT;
+  }
+  if (lru != a->lru_size) return PA_ERR_REFCOUNT;
+  int32_t cached = 0;
+  for (int32_t b = 0; b < a->num_blocks; ++b) {
+    const bool idle = a->refcount[b] == 0;
+    if ((bool)in_free[b] != (idle && !a->cached[b])) return PA_ERR_REFCOUNT;
+    if ((bool)a->in_lru[b] != (idle && a->cached[b])) return PA_ERR_REFCOUNT;
+    if (a->cached[b]) {
+      auto hit = a->index.find(a->key_of[b]);
+      if (hit == a->index.end() || hit->second != b) return PA_ERR_REFCOUNT;
+      cached += 1;
+    }
+  }
+  if (cached != (int32_t)a->index.size()) return PA_ERR_REFCOUNT;
   return PA_OK;
 }
 

@@ -1,0 +1,224 @@
+"""The native allocator's prefix cache against the oracle's, CPU only.
+
+Bit-exact parity of every observable with the cache on: sequence ids and hit
+counts of lookups, slots and CoW pairs of appends, tables and lengths, the
+free pool front to back, the least-recently-used list front to back, all
+refcounts and the cache counters -- after every operation of the pages'
+worked numbers (a 1K-token system prompt shared by 100 requests, a
+4096-token prompt computed once) and of random operation sequences that mix
+cached and uncached appends, forks, prefix shares, frees and evictions.
+"""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import OracleAllocator, OracleError
+from paged_kv_cache_107_amd import PaAllocator, PaError
+
+from test_native_allocator import Twin
+
+
+class CacheTwin(Twin):
+    def __init__(self, nb, bs, order=None):
+        super().__init__(nb, bs, order if order is not None else list(range(nb)))
+        self.o.enable_prefix_cache()
+        self.n.pa_alloc_enable_prefix_cache()
+
+    def _state_equal(self):
+        super()._state_equal()
+        assert self.n.pa_prefix_cache_query().tolist() == list(self.o.lru)
+        assert self.n.pa_prefix_cache_stats() == self.o.prefix_stats()
+
+    def create_prefix(self, prompt):
+        (so, ho), (sn, hn) = self._both(lambda: self.o.create_prefix(prompt),
+                                        lambda: self.n.pa_seq_create_prefix(prompt))
+        assert (so, ho) == (sn, hn)
+        return so, ho
+
+    def append_tokens(self, s, ids):
+        (so, po), (sn, pn) = self._both(lambda: self.o.append_tokens(s, ids),
+                                        lambda: self.n.pa_seq_append_tokens(s, ids))
+        assert list(so) == sn.tolist() and po == pn
+        return so, po
+
+    def serve(self, prompt):
+        s, hit = self.create_prefix(prompt)
+        self.append_tokens(s, prompt[hit:])
+        return s, hit
+
+
+def test_system_prompt_shared_by_a_hundred_requests():
+    t = CacheTwin(8000, 16)
+    rng = np.random.default_rng(0)
+    system = [int(x) for x in rng.integers(0, 50000, 1024)]
+    seqs = []
+    for r in range(100):
+        s, hit = t.serve(system + [int(x) for x in rng.integers(0, 50000, 40 + r)])
+        assert hit == (0 if r == 0 else 1024)
+        seqs.append(s)
+    assert t.n.pa_prefix_cache_stats()["hit_tokens"] == 99 * 1024
+    for s in seqs[::3]:
+        t.free(s)
+    t.serve(system + [1, 2, 3])
+
+
+def test_long_prompt_computed_once_and_lru_reuse():
+    t = CacheTwin(600, 16)
+    system = list(range(4096))
+    first, _ = t.serve(system + [7])
+    for r in range(50):
+        s, hit = t.serve(system + [10 ** 6 + r])
+        assert hit == 4096
+        t.free(s)
+    t.free(first)                                  # 256 cached blocks, all evictable
+    # fill the pool with unrelated prompts: cached blocks are evicted LRU-first
+    live = []
+    for r in range(40):
+        try:
+            s, _ = t.serve([2 * 10 ** 6 + 100 * r + i for i in range(200)])
+        except OracleError as e:
+            assert e.code == "OOM"
+            break
+        live.append(s)
+    assert t.n.pa_prefix_cache_stats()["evictions"] > 0
+
+
+def test_least_recently_used_order_and_eviction():
+    t = CacheTwin(12, 4)
+    seqs = {}
+    for j, k in enumerate("ABC"):
+        seqs[k], _ = t.serve([100 * (j + 1) + i for i in range(8)] + [0])
+    for k in "ABC":
+        t.free(seqs[k])
+    t.serve([9] * 31)
+    assert t.n.pa_prefix_cache_stats()["evictions"] == 2
+    assert t.create_prefix([300 + i for i in range(8)] + [1])[1] == 8
+    assert t.create_prefix([100 + i for i in range(8)] + [1])[1] == 0
+
+
+def test_cached_block_copied_before_a_write():
+    t = CacheTwin(16, 4)
+    src, _ = t.serve([1, 2, 3, 4, 5, 6, 7, 8, 9])
+    blk = t.table(src)[1]
+    child = t.share(src, 6)
+    t.free(src)
+    _, pair = t.append_tokens(child, [60, 61])
+    assert pair is not None and pair[0] == blk
+
+
+def test_errors_and_enable_order():
+    a = PaAllocator(8, 4)
+    a.pa_seq_create()
+    with pytest.raises(PaError) as e:
+        a.pa_alloc_enable_prefix_cache()
+    assert e.value.status == -1
+    b = PaAllocator(8, 4)
+    with pytest.raises(PaError):
+        b.pa_seq_create_prefix([1, 2, 3])         # cache off
+    t = CacheTwin(4, 4)
+    with pytest.raises(OracleError):
+        t.append_tokens(77, [1])                   # unknown sequence
+    s, _ = t.serve([1] * 12)                       # 3 blocks
+    with pytest.raises(OracleError):
+        t.append_tokens(s, [2] * 9)                # OOM: needs 3, 1 free -- nothing changes
+    s2, hit = t.create_prefix([])                  # an empty prompt: nothing to look up
+    assert hit == 0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_append_batch_with_evictions(seed):
+    """A decode step of plain appends for many sequences, with cached blocks
+    evicted and cached partial blocks copied on the way, equals the oracle's
+    appends in order; an OOM step changes nothing."""
+    rng = np.random.default_rng(seed)
+    nb, bs = 40, 4
+    order = rng.permutation(nb).tolist()
+    o = OracleAllocator(nb, bs, order)
+    n = PaAllocator(nb, bs, order)
+    o.enable_prefix_cache()
+    n.pa_alloc_enable_prefix_cache()
+    seqs = []
+    for r in range(6):
+        prompt = [int(x) for x in rng.integers(0, 3, int(rng.integers(2, 14)))]
+        so, ho = o.create_prefix(prompt)
+        sn, hn = n.pa_seq_create_prefix(prompt)
+        assert (so, ho) == (sn, hn)
+        o.append_tokens(so, prompt[ho:])
+        n.pa_seq_append_tokens(sn, prompt[ho:])
+        if r % 2:
+            o.free_seq(so)
+            n.pa_seq_free(sn)
+        else:
+            seqs.append(so)
+            c = o.share_prefix(so, int(rng.integers(0, len(prompt) + 1)))
+            assert n.pa_seq_share_prefix(so, o.lens[c]) == c
+            seqs.append(c)
+    for step in range(4):
+        k = int(rng.integers(1, 4))
+        need = sum(-(-(o.lens[s] + k) // bs) - -(-o.lens[s] // bs) for s in seqs)
+        if need + len(seqs) > len(o.free) + len(o.lru):   # may not fit: check all-or-nothing
+            before = (n.pa_alloc_query(), n.pa_prefix_cache_query().tolist())
+            try:
+                n.pa_seq_append_batch(seqs, 10 ** 4)
+            except PaError as e:
+                assert e.status == -4
+            after = (n.pa_alloc_query(), n.pa_prefix_cache_query().tolist())
+            assert all(np.array_equal(x, y) for x, y in zip(before[0], after[0]))
+            assert before[1] == after[1]
+            break
+        slots_n, pairs_n = n.pa_seq_append_batch(seqs, k)
+        slots_o, pairs_o = [], []
+        for s in seqs:
+            sl, pr = o.append(s, k)
+            slots_o += sl
+            if pr is not None:
+                pairs_o.append(pr)
+        assert slots_n.tolist() == slots_o
+        assert [tuple(p) for p in pairs_n.tolist()] == pairs_o
+        free, rc = n.pa_alloc_query()
+        assert free.tolist() == list(o.free) and rc.tolist() == o.refcount
+        assert n.pa_prefix_cache_query().tolist() == list(o.lru)
+        assert n.pa_prefix_cache_stats() == o.prefix_stats()
+        assert n.pa_alloc_check_invariants()
+
+
+# ------------------------------------------------------------------ random operations
+
+OPS = st.lists(st.tuples(st.sampled_from(["serve", "serve", "append", "append_plain", "fork",
+                                          "share", "free", "free"]),
+                         st.integers(0, 1 << 30)), min_size=1, max_size=40)
+
+
+@settings(max_examples=150, deadline=None)
+@given(ops=OPS, bs=st.sampled_from([1, 2, 4]), nb=st.integers(6, 40))
+def test_random_ops_native_equals_oracle(ops, bs, nb):
+    t = CacheTwin(nb, bs, list(np.random.default_rng(nb).permutation(nb)))
+    live = []
+    for op, r in ops:
+        rng = np.random.default_rng(r)
+        try:
+            if op == "serve":
+                prompt = [1, 2, 3, 4, 5, 6][:rng.integers(0, 7)] + \
+                         [int(x) for x in rng.integers(0, 3, rng.integers(1, 12))]
+                s, _ = t.create_prefix(prompt)
+                live.append(s)
+                t.append_tokens(s, prompt[t.o.lens[s]:])
+            elif op in ("append", "append_plain") and live:
+                s = live[r % len(live)]
+                ids = [int(x) for x in rng.integers(0, 3, rng.integers(1, 6))]
+                if op == "append":
+                    t.append_tokens(s, ids)
+                else:
+                    t.append(s, len(ids))
+            elif op == "fork" and live:
+                live.append(t.fork(live[r % len(live)]))
+            elif op == "share" and live:
+                s = live[r % len(live)]
+                live.append(t.share(s, int(rng.integers(0, t.o.lens[s] + 1))))
+            elif op == "free" and live:
+                t.free(live.pop(r % len(live)))
+        except OracleError as e:
+            assert e.code == "OOM"
+    for s in live:
+        t.free(s)
+    assert sorted(t.free_list() + list(t.o.lru)) == list(range(nb))

@@ -23,6 +23,12 @@ Workloads (shapes follow the pages' model sizes; all are one layer):
              in [0, 256] plus one decode token.
 * ``qwen32b_long``  64 q heads, 8 kv heads, head_dim 128, bf16, 32 sequences
              of 2048 tokens plus 4 of 32768, block 16 (``_bs32``: block 32).
+* ``prefill_8b``  chunked prefill: 16 sequences, a 512-token chunk each on a
+             cached prefix drawn like ``8b_gqa``'s lengths (clipped to [0, 7680]).
+* ``prefix_1k``  requests sharing a system prompt (``prompt_set``): 100
+             requests, one 1024-token system prompt (64 blocks of 16, the
+             size "第 6 章 缓存管理" works through), each followed by its own
+             user suffix of uniform [16, 256] tokens; 8B-GQA shape, bf16.
 
 Context lengths here are the number of tokens a decode query attends to,
 including the token being decoded (its K/V is written first).
@@ -35,6 +41,7 @@ sequence can be regenerated without drawing the whole batch.
 from __future__ import annotations
 
 import dataclasses
+import functools
 import math
 from typing import Dict, List, Optional
 
@@ -85,6 +92,12 @@ WORKLOADS: Dict[str, Workload] = {
     "qwen32b_long": Workload("qwen32b_long", 4, 64, 8, 128, "bf16", 16),
     "qwen32b_long_bs32": Workload("qwen32b_long_bs32", 4, 64, 8, 128, "bf16", 32),
     "prefill_8b": Workload("prefill_8b", 5, 32, 8, 128, "bf16", 16, batch=16, chunk=512),
+}
+
+# Prompt sets (``prompt_set``): requests sharing a system prompt.
+PROMPT_WORKLOADS: Dict[str, Workload] = {
+    "prefix_1k": Workload("prefix_1k", 6, 32, 8, 128, "bf16", 16, batch=100, prefix_len=1024,
+                          tail_max=256),
 }
 
 
@@ -311,3 +324,82 @@ def custom(seed: int, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype:
     free_order = np.random.default_rng(seed).permutation(nb).astype(np.int64)
     chunks = None if chunk_lens is None else np.asarray(chunk_lens, dtype=np.int64)
     return Draw(wl, lens, nb, free_order, None, chunks)
+
+
+# ---------------------------------------------------------------- shared prompts
+
+@dataclasses.dataclass
+class PromptSet:
+    """Requests that open with one shared system prompt, each followed by its
+    own suffix.  Token ids, K/V and q of the system prompt's positions are the
+    same for every request (they depend only on the tokens before them); the
+    suffix's come from the request's own stream."""
+    wl: Workload
+    system_len: int
+    suffix_lens: np.ndarray           # [R] int64
+    num_blocks: int                   # pool for every request unshared, x1.25
+    free_order: np.ndarray
+
+    @property
+    def requests(self) -> int:
+        return int(self.suffix_lens.shape[0])
+
+    @property
+    def prompt_lens(self) -> np.ndarray:
+        return self.system_len + self.suffix_lens
+
+
+def prompt_set(name: str = "prefix_1k", requests: Optional[int] = None) -> PromptSet:
+    wl = PROMPT_WORKLOADS[name]
+    rng = np.random.default_rng(wl.seed)
+    suffix = rng.integers(16, wl.tail_max, wl.batch, endpoint=True).astype(np.int64)
+    if requests is not None:
+        suffix = suffix[:requests]
+    return _prompt_set(wl, wl.prefix_len, suffix, rng)
+
+
+def custom_prompt_set(seed: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      dtype: str, block_size: int, system_len: int, suffix_lens) -> PromptSet:
+    wl = Workload(f"custom{seed}", seed, num_q_heads, num_kv_heads, head_dim, dtype, block_size,
+                  prefix_len=system_len)
+    return _prompt_set(wl, system_len, np.asarray(suffix_lens, dtype=np.int64),
+                       np.random.default_rng(seed))
+
+
+def _prompt_set(wl: Workload, system_len: int, suffix: np.ndarray, rng) -> PromptSet:
+    nb = int(math.ceil(1.25 * _blocks_for(system_len + suffix, wl.block_size))) + 4
+    return PromptSet(wl, system_len, suffix, nb, rng.permutation(nb).astype(np.int64))
+
+
+def prompt_token_ids(ps: PromptSet, r: int) -> List[int]:
+    """Token ids of request r's prompt (int32 range)."""
+    wl = ps.wl
+    system = np.random.default_rng([wl.seed, 6]).integers(0, 50000, ps.system_len)
+    own = np.random.default_rng([wl.seed, 7, r]).integers(0, 50000, int(ps.suffix_lens[r]))
+    return [int(t) for t in np.concatenate([system, own])]
+
+
+@functools.lru_cache(maxsize=6)
+def _shared_bits(seed: int, stream: int, shape, dtype: str) -> np.ndarray:
+    out = _normal_bits(np.random.default_rng([seed, stream, 0]), shape, dtype)
+    out.flags.writeable = False
+    return out
+
+
+def _shared_then_own(ps: PromptSet, r: int, stream: int, width: int):
+    wl = ps.wl
+    shared = _shared_bits(wl.seed, stream, (ps.system_len, width, wl.head_dim), wl.dtype)
+    own = _normal_bits(np.random.default_rng([wl.seed, stream, 1, r]),
+                       (int(ps.suffix_lens[r]), width, wl.head_dim), wl.dtype)
+    return np.concatenate([shared, own])
+
+
+def prompt_kv_bits_of(ps: PromptSet, r: int):
+    """K and V of request r's prompt: two [len][Hkv][D] bit arrays."""
+    h = ps.wl.num_kv_heads
+    return _shared_then_own(ps, r, 8, h), _shared_then_own(ps, r, 9, h)
+
+
+def prompt_query_bits_of(ps: PromptSet, r: int) -> np.ndarray:
+    """q of request r's prompt positions: [len][Hq][D] bits."""
+    return _shared_then_own(ps, r, 10, ps.wl.num_q_heads)
