@@ -115,6 +115,7 @@ class OracleAllocator:
         # prefix cache (off until enable_prefix_cache)
         self.caching = False
         self.tokens: Dict[int, List[int]] = {}    # known token ids of each sequence
+        self.considered: Dict[int, int] = {}       # leading full blocks already offered to the cache
         self.index: Dict[tuple, int] = {}          # token prefix -> cached block
         self.block_key: Dict[int, tuple] = {}      # cached block -> its prefix
         self.lru: "OrderedDict[int, None]" = OrderedDict()  # evictable, least recent first
@@ -147,19 +148,22 @@ class OracleAllocator:
         return blk
 
     def _register(self, seq: int) -> None:
-        """Cache every full block of ``seq`` whose token ids are all known."""
+        """Offer the cache each block of ``seq`` that has become full with
+        all of its token ids known: it is cached unless its prefix (or the
+        block) already is.  A block is offered once, when it fills."""
         if not self.caching:
             return
         bs = self.block_size
         known = self.tokens[seq]
         table = self.tables[seq]
         full = min(self.lens[seq], len(known)) // bs
-        for j in range(full):
+        for j in range(self.considered[seq], full):
             key = tuple(known[:(j + 1) * bs])
             blk = table[j]
             if key not in self.index and blk not in self.block_key:
                 self.index[key] = blk
                 self.block_key[blk] = key
+        self.considered[seq] = max(self.considered[seq], full)
 
     # ------------------------------------------------------------ operations
     def create(self) -> int:
@@ -167,6 +171,7 @@ class OracleAllocator:
         self.tables[s] = []
         self.lens[s] = 0
         self.tokens[s] = []
+        self.considered[s] = 0
         return s
 
     def enable_prefix_cache(self) -> None:
@@ -195,6 +200,7 @@ class OracleAllocator:
             hits += 1
         self.lens[s] = hits * bs
         self.tokens[s] = prompt[:hits * bs]
+        self.considered[s] = hits
         self.lookup_tokens += len(prompt)
         self.hit_tokens += hits * bs
         return s, hits * bs
@@ -253,6 +259,7 @@ class OracleAllocator:
         self.tables[child] = list(table)
         self.lens[child] = self.lens[parent]
         self.tokens[child] = list(self.tokens[parent])
+        self.considered[child] = self.considered[parent]
         for b in table:
             self.refcount[b] += 1
         return child
@@ -266,6 +273,7 @@ class OracleAllocator:
         self.tables[s] = list(table[:k])
         self.lens[s] = n_tokens
         self.tokens[s] = list(self.tokens[src][:n_tokens])
+        self.considered[s] = min(self.considered[src], n_tokens // self.block_size)
         for b in self.tables[s]:
             self.refcount[b] += 1
         return s
@@ -289,6 +297,7 @@ class OracleAllocator:
         del self.tables[seq]
         del self.lens[seq]
         del self.tokens[seq]
+        del self.considered[seq]
 
     def build_tables(self, seqs: Sequence[int], max_blocks: int):
         """Block tables [n][max_blocks] int32 padded with -1, and lengths [n]."""

@@ -222,3 +222,23 @@ def test_random_ops_native_equals_oracle(ops, bs, nb):
     for s in live:
         t.free(s)
     assert sorted(t.free_list() + list(t.o.lru)) == list(range(nb))
+
+
+def test_a_block_is_offered_to_the_cache_once():
+    """Two requests compute the same prompt at once (the second finds nothing
+    cached yet): the first registration stays, the second's blocks are not
+    cached.  After the first is freed and its blocks evicted, the second's
+    older blocks are not offered again by later appends."""
+    t = CacheTwin(6, 4)
+    p = [5, 6, 7, 8, 9, 10, 11, 12]
+    a, _ = t.create_prefix(p)
+    b, _ = t.create_prefix(p)
+    t.append_tokens(a, p)
+    t.append_tokens(b, p)
+    assert t.n.pa_prefix_cache_stats()["cached_blocks"] == 2
+    t.free(a)                              # a's 2 blocks: evictable
+    c, _ = t.serve([1] * 13)               # 4 blocks: 2 free + 2 evictions
+    assert t.n.pa_prefix_cache_stats()["evictions"] == 2
+    t.free(c)                              # 3 full blocks cached, the partial one free
+    t.append_tokens(b, [13, 14, 15, 16])   # fills b's block 2: cached; blocks 0-1 are not
+    assert t.n.pa_prefix_cache_stats()["cached_blocks"] == 3 + 1
