@@ -70,6 +70,31 @@ Readings (the pages give no mechanism):
 * A cached block is never written: an append whose first position falls in a
   cached block (possible after sharing a prefix that ends mid-block) copies
   it first, as for a shared block.
+
+Swapping (``enable_swap``): a preempted sequence's KV moves to host memory
+and comes back later, block by block rather than as one contiguous buffer
+("vLLM：把 KV 缓存当成虚拟内存", section "碎片从哪里来", on preemption; "第 6 章
+缓存管理", section "缓存放不下的时候", on moving cold cache to CPU memory).
+Readings (the pages name the move, not its bookkeeping):
+
+* The host side is a second pool of ``num_host_blocks`` blocks of the same
+  shape, with its own FIFO free list (ids 0.. in order at start).
+* Swap-out moves the blocks only this sequence holds (refcount 1) to host
+  blocks taken from the front of the host list, in logical order, and
+  releases those device blocks as ``free_seq`` does (free pool, or the
+  evictable list if cached).  Blocks it shares with other sequences stay on
+  the device and it keeps its reference: moving them frees nothing.
+  Returns the (device block, host block) copies, which must run before the
+  released device blocks are written again.
+* A swapped-out sequence can only be swapped in or freed; any other use is
+  an error (``SWAPPED``).  Freeing it returns its host blocks to the back of
+  the host list in logical order and drops its device references.
+* Swap-in takes a device block for each host-resident entry, in logical
+  order, the same way an append does (free pool, else eviction), and returns
+  the (host block, device block) copies; the host blocks go back to the host
+  list in logical order.  The new blocks are private (refcount 1) and not
+  cached.
+* Both moves are all or nothing: ``OOM`` when the destination is short.
 """
 from __future__ import annotations
 
@@ -80,7 +105,8 @@ import numpy as np
 
 
 class OracleError(Exception):
-    """Allocator error; ``code`` is one of ARG, OOM, REFCOUNT, NOT_FOUND."""
+    """Allocator error; ``code`` is one of ARG, OOM, REFCOUNT, NOT_FOUND,
+    SWAPPED."""
 
     def __init__(self, code: str, msg: str = ""):
         super().__init__(f"{code}: {msg}")
@@ -122,12 +148,33 @@ class OracleAllocator:
         self.lookup_tokens = 0
         self.hit_tokens = 0
         self.evictions = 0
+        # swapping to a host pool (off until enable_swap)
+        self.host_free: Optional[deque] = None
+        self.num_host_blocks = 0
+        self.swapped: Dict[int, List[Tuple[bool, int]]] = {}  # seq -> (on host, id) per block
+        self.swap_outs = 0
+        self.swap_ins = 0
+        self.blocks_out = 0
+        self.blocks_in = 0
 
     # ------------------------------------------------------------ helpers
     def _seq(self, seq: int) -> List[int]:
+        if seq in self.swapped:
+            raise OracleError("SWAPPED", f"sequence {seq} is on the host")
         if seq not in self.tables:
             raise OracleError("NOT_FOUND", f"sequence {seq}")
         return self.tables[seq]
+
+    def _release(self, released: List[int]) -> None:
+        """Blocks whose count reached zero, in logical order: uncached ones to
+        the back of the free pool in that order; cached ones to the back of
+        the evictable list, last block first."""
+        for b in released:
+            if b not in self.block_key:
+                self.free.append(b)
+        for b in reversed(released):
+            if b in self.block_key:
+                self.lru[b] = None
 
     def _new_id(self) -> int:
         s = self._next_seq
@@ -279,6 +326,21 @@ class OracleAllocator:
         return s
 
     def free_seq(self, seq: int) -> None:
+        if seq in self.swapped:
+            entries = self.swapped.pop(seq)
+            released = []
+            for on_host, i in entries:
+                if on_host:
+                    self.host_free.append(i)
+                else:
+                    self.refcount[i] -= 1
+                    if self.refcount[i] == 0:
+                        released.append(i)
+            self._release(released)
+            del self.lens[seq]
+            del self.tokens[seq]
+            del self.considered[seq]
+            return
         table = self._seq(seq)
         for b in table:
             if self.refcount[b] <= 0:
@@ -288,16 +350,73 @@ class OracleAllocator:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
                 released.append(b)
-        for b in released:                      # uncached: free pool, logical order
-            if b not in self.block_key:
-                self.free.append(b)
-        for b in reversed(released):            # cached: LRU, last block first
-            if b in self.block_key:
-                self.lru[b] = None
+        self._release(released)
         del self.tables[seq]
         del self.lens[seq]
         del self.tokens[seq]
         del self.considered[seq]
+
+    # ------------------------------------------------------------ swapping
+    def enable_swap(self, num_host_blocks: int) -> None:
+        if self.host_free is not None or num_host_blocks <= 0:
+            raise OracleError("ARG", "swap already on, or no host blocks")
+        self.num_host_blocks = num_host_blocks
+        self.host_free = deque(range(num_host_blocks))
+
+    def swap_out(self, seq: int) -> List[Tuple[int, int]]:
+        """Move the blocks only ``seq`` holds to host blocks; returns the
+        (device, host) copies in logical order."""
+        if self.host_free is None:
+            raise OracleError("ARG", "swap is off")
+        table = self._seq(seq)
+        own = [j for j, b in enumerate(table) if self.refcount[b] == 1]
+        if len(own) > len(self.host_free):
+            raise OracleError("OOM", f"need {len(own)} host blocks, free {len(self.host_free)}")
+        entries = [(False, b) for b in table]
+        pairs, released = [], []
+        for j in own:
+            h = self.host_free.popleft()
+            pairs.append((table[j], h))
+            entries[j] = (True, h)
+            self.refcount[table[j]] = 0
+            released.append(table[j])
+        self._release(released)
+        del self.tables[seq]
+        self.swapped[seq] = entries
+        self.swap_outs += 1
+        self.blocks_out += len(pairs)
+        return pairs
+
+    def swap_in(self, seq: int) -> List[Tuple[int, int]]:
+        """Bring a swapped-out sequence back; returns the (host, device)
+        copies in logical order."""
+        if seq in self.tables:
+            raise OracleError("ARG", f"sequence {seq} is not swapped out")
+        if seq not in self.swapped:
+            raise OracleError("NOT_FOUND", f"sequence {seq}")
+        entries = self.swapped[seq]
+        on_host = [j for j, (h, _) in enumerate(entries) if h]
+        if len(on_host) > self._available():
+            raise OracleError("OOM", f"need {len(on_host)}, free {self._available()}")
+        table = [i for _, i in entries]
+        pairs = []
+        for j in on_host:
+            d = self._take()
+            self.refcount[d] = 1
+            pairs.append((entries[j][1], d))
+            table[j] = d
+        for j in on_host:
+            self.host_free.append(entries[j][1])
+        del self.swapped[seq]
+        self.tables[seq] = table
+        self.swap_ins += 1
+        self.blocks_in += len(pairs)
+        return pairs
+
+    def swap_stats(self) -> Dict[str, int]:
+        return dict(swap_outs=self.swap_outs, swap_ins=self.swap_ins, blocks_out=self.blocks_out,
+                    blocks_in=self.blocks_in, swapped_seqs=len(self.swapped),
+                    host_free=len(self.host_free) if self.host_free is not None else 0)
 
     def build_tables(self, seqs: Sequence[int], max_blocks: int):
         """Block tables [n][max_blocks] int32 padded with -1, and lengths [n]."""
@@ -322,6 +441,18 @@ class OracleAllocator:
                 raise AssertionError(f"seq {s}: {len(t)} blocks for {self.lens[s]} tokens")
             for b in t:
                 indeg[b] += 1
+        host_used = []
+        for s, entries in self.swapped.items():
+            if len(entries) != _ceil_div(self.lens[s], self.block_size):
+                raise AssertionError(f"swapped seq {s}: wrong entry count")
+            for on_host, i in entries:
+                if on_host:
+                    host_used.append(i)
+                else:
+                    indeg[i] += 1
+        if self.host_free is not None and sorted(list(self.host_free) + host_used) != \
+                list(range(self.num_host_blocks)):
+            raise AssertionError("host blocks lost or duplicated")
         if indeg != self.refcount:
             raise AssertionError("refcount differs from table in-degree")
         free_set = set(self.free)

@@ -14,6 +14,9 @@ f16/bf16), so both operations are bit-exact by construction.
 * ``copy_blocks``: the copy-on-write copy of a whole shared block before the
   writer's first write ("Lazy Allocation 与 Copy-on-Write ...", section 4.4).
   Pairs are applied in order, all before any write of the same step.
+* ``swap_blocks``: a preempted sequence's blocks moved one by one between the
+  device pool and a host pool of the same block shape ("vLLM：把 KV 缓存当成
+  虚拟内存", section "碎片从哪里来").
 """
 from __future__ import annotations
 
@@ -39,3 +42,10 @@ def copy_blocks(pool: np.ndarray, pairs) -> None:
     """pool[dst] = pool[src] for each (src, dst), in order."""
     for src, dst in pairs:
         pool[int(dst)] = pool[int(src)]
+
+
+def swap_blocks(src_pool: np.ndarray, dst_pool: np.ndarray, pairs) -> None:
+    """dst_pool[d] = src_pool[s] for each (s, d): whole blocks between two
+    pools of the same block shape (device -> host or host -> device)."""
+    for src, dst in pairs:
+        dst_pool[int(dst)] = src_pool[int(src)]
