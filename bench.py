@@ -20,7 +20,9 @@ CPU oracle timed on a bounded sample of the same workload, and, apart from the
 timed step, the chunked-prefill kernel on its own workload with its
 matrix-core roofline, and the prefill of requests sharing a system prompt
 with and without the prefix cache (hit rate, pinned blocks, blocks held,
-device time of the prefill pass, host time per request).
+device time of the prefill pass, host time per request), and swapping every
+8th decode sequence out to pinned host memory and back (host-link rate of
+the swap kernel beside a plain copy of the same size).
 """
 from __future__ import annotations
 
@@ -252,6 +254,91 @@ def measure_prefill(reps: int, log):
     }
 
 
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, per direction
+SWAP_DESCRIPTION = ("preemption on the 8B GQA decode batch: every 8th of the 256 sequences "
+                    "swapped out to pinned host pools and back, 32 q / 8 kv heads, head_dim 128, "
+                    "bf16, block 16")
+
+
+def measure_swap(cache, d, reps: int, log):
+    """Swap-out and swap-in of every 8th sequence of the decode batch on its
+    populated cache: the allocator's host work, then pa_swap_blocks (device
+    pools <-> pinned host pools), timed with HIP events on the launch stream.
+    Beside it, a plain copy of the same byte count between a contiguous
+    device buffer and pinned host memory (the DMA engines' rate)."""
+    import torch
+    import paged_kv_cache_107_amd as pa
+    wl = d.wl
+    victims = list(range(0, d.batch, 8))
+    blocks = sum(int(cache.alloc.pa_seq_info(s)[1].size) for s in victims)
+    cache.enable_swap(blocks + 64)
+    block_bytes = wl.num_kv_heads * wl.block_size * wl.head_dim * wl.elem_bytes
+    stream = torch.cuda.current_stream()
+    out_us, in_us, host_out, host_in, moved = [], [], [], [], []
+    for _ in range(reps + 1):
+        t0 = time.perf_counter()
+        pairs_out = [cache.alloc.pa_seq_swap_out(s) for s in victims]
+        host_out.append(time.perf_counter() - t0)
+        p_out = torch.from_numpy(np.concatenate(pairs_out)).cuda()
+        t0 = time.perf_counter()
+        pairs_in = [cache.alloc.pa_seq_swap_in(s) for s in victims]
+        host_in.append(time.perf_counter() - t0)
+        p_in = torch.from_numpy(np.concatenate(pairs_in)).cuda()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        pa.pa_swap_blocks(cache.k_pool, cache.v_pool, cache.k_host, cache.v_host, p_out,
+                          pa.PA_SWAP_OUT)
+        ev[1].record(stream)
+        pa.pa_swap_blocks(cache.k_pool, cache.v_pool, cache.k_host, cache.v_host, p_in,
+                          pa.PA_SWAP_IN)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        out_us.append(1e3 * ev[0].elapsed_time(ev[1]))
+        in_us.append(1e3 * ev[1].elapsed_time(ev[2]))
+        moved.append(int(p_out.shape[0]))
+    out_us, in_us, host_out, host_in = out_us[1:], in_us[1:], host_out[1:], host_in[1:]
+    nbytes = 2 * moved[-1] * block_bytes
+    dev_buf = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    host_buf = torch.empty(nbytes // 2, dtype=torch.int16, pin_memory=True)
+    dma = {"out": [], "in": []}
+    for _ in range(reps + 1):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        host_buf.copy_(dev_buf, non_blocking=True)
+        ev[1].record(stream)
+        dev_buf.copy_(host_buf, non_blocking=True)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        dma["out"].append(1e3 * ev[0].elapsed_time(ev[1]))
+        dma["in"].append(1e3 * ev[1].elapsed_time(ev[2]))
+    del dev_buf, host_buf
+    o_us, i_us = float(np.mean(out_us)), float(np.mean(in_us))
+    d_out, d_in = float(np.mean(dma["out"][1:])), float(np.mean(dma["in"][1:]))
+    gbps = {k: nbytes / (u * 1e-6) / 1e9 for k, u in
+            (("out", o_us), ("in", i_us), ("dma_out", d_out), ("dma_in", d_in))}
+    log(f"swap: {moved[-1]} blocks ({nbytes / 1e6:.1f} MB) out {o_us:.0f} us "
+        f"({gbps['out']:.1f} GB/s), in {i_us:.0f} us ({gbps['in']:.1f} GB/s); plain copy "
+        f"{gbps['dma_out']:.1f} / {gbps['dma_in']:.1f} GB/s; host "
+        f"{1e6 * np.mean(host_out) / len(victims):.1f} / {1e6 * np.mean(host_in) / len(victims):.1f}"
+        f" us per sequence")
+    return {
+        "workload": SWAP_DESCRIPTION,
+        "sequences": len(victims),
+        "blocks": moved[-1],
+        "bytes_per_direction": nbytes,
+        "swap_out_us": round(o_us, 1),
+        "swap_in_us": round(i_us, 1),
+        "roofline": {"bound": "host link", "kernel": "pa_swap_blocks", "unit": "GB/s",
+                     "peak": HOST_LINK_PEAK_GBPS,
+                     "achieved_out": round(gbps["out"], 2), "achieved_in": round(gbps["in"], 2),
+                     "frac_out": round(gbps["out"] / HOST_LINK_PEAK_GBPS, 4),
+                     "frac_in": round(gbps["in"] / HOST_LINK_PEAK_GBPS, 4), "traffic": None},
+        "plain_copy_gbps": {"out": round(gbps["dma_out"], 2), "in": round(gbps["dma_in"], 2)},
+        "host_us_per_sequence": {"out": round(1e6 * float(np.mean(host_out)) / len(victims), 2),
+                                 "in": round(1e6 * float(np.mean(host_in)) / len(victims), 2)},
+    }
+
+
 PREFIX_DESCRIPTION = ("8B GQA prompts sharing a system prompt, 1 layer: 100 requests, one "
                       "1024-token system prompt + per-request suffix uniform [16, 256] tokens, "
                       "32 q / 8 kv heads, head_dim 128, bf16, block 16, seed 6")
@@ -412,6 +499,9 @@ def main(argv=None):
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--prefill-reps", type=int, default=20,
                     help="timed pa_prefill calls on the chunked-prefill workload (0 = skip)")
+    ap.add_argument("--swap-reps", type=int, default=10,
+                    help="timed swap-out + swap-in cycles of every 8th decode sequence "
+                         "(0 = skip)")
     ap.add_argument("--prefix-reps", type=int, default=10,
                     help="timed prefill passes per variant on the shared-system-prompt "
                          "workload, with and without the prefix cache (0 = skip)")
@@ -519,6 +609,9 @@ def main(argv=None):
     prefix = None
     if args.prefix_reps > 0:
         prefix = measure_prefix_cache(args.prefix_reps, log)
+    swap = None
+    if args.swap_reps > 0 and args.workload == "8b_gqa":
+        swap = measure_swap(cache, d, args.swap_reps, log)
 
     rec = {
         "metric": METRIC,
@@ -558,6 +651,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "prefill": prefill,
         "prefix_cache": prefix,
+        "swap": swap,
     }
     print(json.dumps(rec), flush=True)
     return 0

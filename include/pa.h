@@ -57,7 +57,8 @@ typedef enum {
   PA_ERR_OOM = -4,       /* allocator: not enough free blocks (state unchanged) */
   PA_ERR_REFCOUNT = -5,  /* allocator: refcount would go below zero */
   PA_ERR_NOT_FOUND = -6, /* allocator: unknown sequence id */
-  PA_ERR_HIP = -7        /* a HIP launch or runtime call failed */
+  PA_ERR_HIP = -7,       /* a HIP launch or runtime call failed */
+  PA_ERR_SWAPPED = -8    /* allocator: the sequence is swapped out to the host */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -350,6 +351,72 @@ pa_status pa_seq_append_tokens(pa_alloc* a, int64_t seq, const int32_t* tokens, 
 pa_status pa_prefix_cache_stats(const pa_alloc* a, pa_prefix_stats* out);
 /* Evictable blocks, least recently used first (evictable_out [NB] or NULL). */
 pa_status pa_prefix_cache_query(const pa_alloc* a, int32_t* evictable_out, int32_t* num_out);
+
+/* ------------------------------------------------------------------------
+ * Swapping (preemption).  A preempted sequence's KV moves to host memory and
+ * comes back later, block by block, not as one contiguous buffer (page
+ * "vLLM：把 KV 缓存当成虚拟内存", section "碎片从哪里来"; page "第 6 章 缓存管理",
+ * section "缓存放不下的时候", on moving cold cache to CPU memory).
+ *
+ * The host side is a second pool pair (K and V) of num_host_blocks blocks of
+ * the device pool's block shape, [NHB][Hkv][BS][D] each, in pinned host
+ * memory; the allocator keeps its free list (FIFO, ids 0.. in order at
+ * start).
+ *  - pa_seq_swap_out: the blocks only this sequence holds (refcount 1) get
+ *    host blocks from the front of the host list, in logical order, and are
+ *    released like pa_seq_free releases them (free pool, or evictable if
+ *    cached).  Blocks it shares stay on the device with its reference kept.
+ *    pairs_out [capacity][2] = (device block, host block); these copies must
+ *    run (pa_swap_blocks, PA_SWAP_OUT) before the released blocks are
+ *    written again.  PA_ERR_OOM if the host list is short (nothing changes).
+ *  - A swapped-out sequence can only be swapped in, freed or inspected:
+ *    other calls on it return PA_ERR_SWAPPED.  pa_seq_info reports a host
+ *    entry h as -(h + 1).  Freeing it returns its host blocks to the back of
+ *    the host list in logical order.
+ *  - pa_seq_swap_in: each host entry gets a device block the way an append
+ *    takes one (free pool front, else eviction of a cached block), in
+ *    logical order; pairs_out = (host block, device block), to be copied
+ *    (PA_SWAP_IN) before the sequence is read; the host blocks go back to
+ *    the host list in logical order.  The new blocks are private and not
+ *    cached.  PA_ERR_OOM if the device is short (nothing changes);
+ *    PA_ERR_ARG if the sequence is not swapped out.
+ * capacity must cover the sequence's block count (pa_seq_info), else
+ * PA_ERR_ARG before any change.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t swap_outs;     /* sequences swapped out (preemptions) */
+  int64_t swap_ins;
+  int64_t blocks_out;    /* blocks moved device -> host */
+  int64_t blocks_in;
+  int32_t swapped_seqs;  /* sequences on the host now */
+  int32_t host_free;     /* free host blocks */
+} pa_swap_stats;
+
+/* Turns swapping on with a host pool of num_host_blocks blocks (once). */
+pa_status pa_alloc_enable_swap(pa_alloc* a, int32_t num_host_blocks);
+pa_status pa_seq_swap_out(pa_alloc* a, int64_t seq, int32_t* pairs_out, int32_t capacity,
+                          int32_t* num_pairs_out);
+pa_status pa_seq_swap_in(pa_alloc* a, int64_t seq, int32_t* pairs_out, int32_t capacity,
+                         int32_t* num_pairs_out);
+/* Counters, and the host free list front to back (host_free_out [NHB] or NULL). */
+pa_status pa_swap_query(const pa_alloc* a, pa_swap_stats* stats, int32_t* host_free_out);
+
+typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_direction;
+
+/* Copies whole blocks between the device pools and the host pools (both K and
+ * V): PA_SWAP_OUT copies device block p[0] to host block p[1] for each pair p
+ * of pairs (device int32 [num_pairs][2]); PA_SWAP_IN copies host block p[0]
+ * to device block p[1].  The host pools must be pinned host allocations
+ * (hipHostMalloc, or torch's pin_memory) of num_host_blocks blocks of the
+ * device pools' block shape; the kernel reads or writes them directly over
+ * the host link.  Pairs with an id out of range are skipped; every
+ * destination block must be distinct.  PA_ERR_ARG for null or misaligned
+ * pointers, host pointers that are not pinned host memory, or num_pairs
+ * beyond 65535.  Asynchronous on the stream: the host pool is complete (out)
+ * or may be reused (in) once the stream has passed the call. */
+pa_status pa_swap_blocks(void* k_pool, void* v_pool, void* k_host, void* v_host,
+                         int32_t num_host_blocks, const pa_pool_desc* pool, const int32_t* pairs,
+                         int32_t num_pairs, int32_t direction, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -2,13 +2,16 @@
 
 The product is ``libpa.so`` (C ABI declared in ``include/pa.h``): HIP kernels
 for paged decode attention (partition + split-K reduce), chunked prefill
-attention, the new-token cache write and the copy-on-write block copy, plus a host block allocator with a
-FIFO free pool, refcounts, fork and prefix sharing.  This package is the thin
-Python binding: ``ops`` (kernels on torch device tensors) and ``allocator``.
+attention, the new-token cache write, the copy-on-write block copy and block
+swapping to pinned host pools, plus a host block allocator with a FIFO free
+pool, refcounts, fork, prefix sharing, a prefix cache and swap bookkeeping.
+This package is the thin Python binding: ``ops`` (kernels on torch device
+tensors), ``allocator`` and ``cache`` (a per-layer driver of both).
 """
 from ._lib import (LIB_PATH, PA_BF16, PA_F16, PA_F32, PA_PATH_AUTO, PA_PATH_MFMA,  # noqa: F401
-                   PA_PATH_MFMA_GRID, PA_PATH_VALU, SIGNATURES, PaError, lib)
+                   PA_PATH_MFMA_GRID, PA_PATH_VALU, PA_SWAP_IN, PA_SWAP_OUT, SIGNATURES, PaError,
+                   lib)
 from .allocator import PaAllocator  # noqa: F401
 from .ops import (alloc_workspace, pa_copy_blocks, pa_decode, pa_decode_partition,  # noqa: F401
                   pa_decode_reduce, pa_decode_workspace_bytes, pa_prefill, pa_reshape_and_cache,
-                  pa_set_decode_path, pool_desc)
+                  pa_set_decode_path, pa_swap_blocks, pool_desc)

@@ -11,7 +11,8 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_OK, PA_ERR_ARG, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_OOM, PA_ERR_REFCOUNT, \
-    PA_ERR_NOT_FOUND, PA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6, -7
+    PA_ERR_NOT_FOUND, PA_ERR_HIP, PA_ERR_SWAPPED = 0, -1, -2, -3, -4, -5, -6, -7, -8
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA, PA_PATH_MFMA_GRID = 0, 1, 2, 3
 
@@ -29,6 +30,11 @@ class pa_prefix_stats(C.Structure):
     _fields_ = [("lookup_tokens", C.c_int64), ("hit_tokens", C.c_int64), ("evictions", C.c_int64),
                 ("cached_blocks", C.c_int32), ("evictable_blocks", C.c_int32),
                 ("pinned_blocks", C.c_int32)]
+
+
+class pa_swap_stats(C.Structure):
+    _fields_ = [("swap_outs", C.c_int64), ("swap_ins", C.c_int64), ("blocks_out", C.c_int64),
+                ("blocks_in", C.c_int64), ("swapped_seqs", C.c_int32), ("host_free", C.c_int32)]
 
 
 _DECODE_ARGS = [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _sz,
@@ -64,6 +70,11 @@ SIGNATURES = {
     "pa_seq_append_tokens": (_i32, [_vp, _i64, _pi32, _i32, _pi64, _pi32, _pi32]),
     "pa_prefix_cache_stats": (_i32, [_vp, C.POINTER(pa_prefix_stats)]),
     "pa_prefix_cache_query": (_i32, [_vp, _pi32, _pi32]),
+    "pa_alloc_enable_swap": (_i32, [_vp, _i32]),
+    "pa_seq_swap_out": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pa_seq_swap_in": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pa_swap_query": (_i32, [_vp, C.POINTER(pa_swap_stats), _pi32]),
+    "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _desc, _vp, _i32, _i32, _vp]),
 }
 
 _lib = None

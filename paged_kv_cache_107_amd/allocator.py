@@ -9,7 +9,7 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-from ._lib import PaError, check, lib, pa_prefix_stats
+from ._lib import PaError, check, lib, pa_prefix_stats, pa_swap_stats
 
 
 def _i32p(a: np.ndarray):
@@ -25,6 +25,7 @@ class PaAllocator:
                  initial_free_order: Optional[Sequence[int]] = None):
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
+        self.num_host_blocks = 0
         h = C.c_void_p()
         order = None
         if initial_free_order is not None:
@@ -161,3 +162,31 @@ class PaAllocator:
         out = np.empty(self.num_blocks, dtype=np.int32)
         check("pa_prefix_cache_query", lib().pa_prefix_cache_query(self._h, _i32p(out), C.byref(n)))
         return out[:n.value]
+
+    # ------------------------------------------------------------ swapping
+    def pa_alloc_enable_swap(self, num_host_blocks: int) -> None:
+        check("pa_alloc_enable_swap", lib().pa_alloc_enable_swap(self._h, int(num_host_blocks)))
+        self.num_host_blocks = int(num_host_blocks)
+
+    def _swap(self, fn: str, seq: int) -> np.ndarray:
+        n = self.pa_seq_info(seq)[1].size
+        pairs = np.zeros((max(n, 1), 2), dtype=np.int32)
+        num = C.c_int32()
+        check(fn, getattr(lib(), fn)(self._h, int(seq), _i32p(pairs), int(n), C.byref(num)))
+        return pairs[:num.value]
+
+    def pa_seq_swap_out(self, seq: int) -> np.ndarray:
+        """(device block, host block) pairs [P][2] to copy out."""
+        return self._swap("pa_seq_swap_out", seq)
+
+    def pa_seq_swap_in(self, seq: int) -> np.ndarray:
+        """(host block, device block) pairs [P][2] to copy in."""
+        return self._swap("pa_seq_swap_in", seq)
+
+    def pa_swap_query(self):
+        """(counters dict, host free list front to back)."""
+        st = pa_swap_stats()
+        out = np.empty(max(self.num_host_blocks, 1), dtype=np.int32)
+        check("pa_swap_query", lib().pa_swap_query(self._h, C.byref(st), _i32p(out)))
+        return {f: getattr(st, f) for f, _ in pa_swap_stats._fields_}, out[:st.host_free]
+

@@ -21,7 +21,9 @@ import numpy as np
 import torch
 
 from .allocator import PaAllocator
-from .ops import (alloc_workspace, pa_copy_blocks, pa_decode, pa_reshape_and_cache)
+from ._lib import PA_SWAP_IN, PA_SWAP_OUT
+from .ops import (alloc_workspace, pa_copy_blocks, pa_decode, pa_reshape_and_cache,
+                  pa_swap_blocks)
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -90,6 +92,32 @@ class PagedKVCache:
 
     def prefix_stats(self) -> dict:
         return self.alloc.pa_prefix_cache_stats()
+
+    # ------------------------------------------------------------ swapping
+    def enable_swap(self, num_host_blocks: int) -> None:
+        """A pinned host pool pair of num_host_blocks blocks for preempted
+        sequences."""
+        self.alloc.pa_alloc_enable_swap(num_host_blocks)
+        shape = (num_host_blocks,) + tuple(self.k_pool.shape[1:])
+        self.k_host = torch.empty(shape, dtype=self.k_pool.dtype, pin_memory=True)
+        self.v_host = torch.empty(shape, dtype=self.k_pool.dtype, pin_memory=True)
+
+    def swap_out(self, seq: int, stream=None) -> np.ndarray:
+        """Move seq's private blocks to the host pool (copies queued on the
+        stream before anything else can write the released blocks)."""
+        pairs = self.alloc.pa_seq_swap_out(seq)
+        if pairs.shape[0]:
+            pa_swap_blocks(self.k_pool, self.v_pool, self.k_host, self.v_host,
+                           self._dev(pairs, torch.int32), PA_SWAP_OUT, stream)
+        return pairs
+
+    def swap_in(self, seq: int, stream=None) -> np.ndarray:
+        """Bring seq back into device blocks (copies queued on the stream)."""
+        pairs = self.alloc.pa_seq_swap_in(seq)
+        if pairs.shape[0]:
+            pa_swap_blocks(self.k_pool, self.v_pool, self.k_host, self.v_host,
+                           self._dev(pairs, torch.int32), PA_SWAP_IN, stream)
+        return pairs
 
     # ------------------------------------------------------------ device work
     def _dev(self, a: np.ndarray, dtype) -> torch.Tensor:

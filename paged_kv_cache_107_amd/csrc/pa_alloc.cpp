@@ -33,6 +33,15 @@
 // last block to its first; new blocks come from the free pool, else by
 // evicting the least recently used cached block; a cached block is never
 // written (an append into one copies it first).
+//
+//  * swapping: a preempted sequence's KV moves to host memory and back block
+//    by block, not as one contiguous buffer ("vLLM：把 KV 缓存当成虚拟内存",
+//    section "碎片从哪里来"; "第 6 章 缓存管理", section "缓存放不下的时候").
+//    Choices: a host pool of its own with a FIFO free list; swap-out moves the
+//    blocks only this sequence holds (refcount 1) and releases them, keeping
+//    its references to shared blocks on the device; swap-in takes device
+//    blocks the way an append does; both are all or nothing; a swapped-out
+//    sequence can only be swapped in or freed.
 #include <algorithm>
 #include <cstring>
 #include <deque>
@@ -52,6 +61,7 @@ struct pa_alloc {
     int32_t len = 0;
     std::vector<int32_t> tokens;  // known token ids of positions 0 .. tokens.size()-1
     std::vector<uint64_t> hashes;  // chain hash of each leading full known block
+    bool swapped = false;          // table entries < 0 are host blocks -(h + 1)
   };
   std::unordered_map<int64_t, Seq> seqs;
   int64_t next_id = 0;
@@ -68,6 +78,11 @@ struct pa_alloc {
   std::vector<char> in_lru;
   int32_t lru_head = -1, lru_tail = -1, lru_size = 0;
   int64_t lookup_tokens = 0, hit_tokens = 0, evictions = 0;
+  // swapping
+  int32_t num_host_blocks = 0;  // 0: swap off
+  std::deque<int32_t> host_free;
+  int64_t swap_outs = 0, swap_ins = 0, blocks_out = 0, blocks_in = 0;
+  int32_t swapped_seqs = 0;
 };
 
 namespace {
@@ -154,14 +169,27 @@ void register_blocks(pa_alloc* a, pa_alloc::Seq& s) {
 // reach zero go to the back of the free pool in logical order if uncached;
 // cached ones enter the LRU list from the table's last block to its first, so
 // a sequence's first blocks are its most recently used.
-void release_table(pa_alloc* a, const std::vector<int32_t>& table) {
-  std::vector<int32_t> released;
-  for (int32_t b : table)
-    if (--a->refcount[b] == 0) released.push_back(b);
+void release_blocks(pa_alloc* a, const std::vector<int32_t>& released) {
   for (int32_t b : released)
     if (!a->cached[b]) a->free_pool.push_back(b);
   for (auto it = released.rbegin(); it != released.rend(); ++it)
     if (a->cached[*it]) lru_push_back(a, *it);
+}
+
+void release_table(pa_alloc* a, const std::vector<int32_t>& table) {
+  std::vector<int32_t> released;
+  for (int32_t b : table)
+    if (--a->refcount[b] == 0) released.push_back(b);
+  release_blocks(a, released);
+}
+
+// A resident sequence, or the status that says why not.
+pa_status find_resident(pa_alloc* a, int64_t seq, pa_alloc::Seq** out) {
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
+  if (it->second.swapped) return PA_ERR_SWAPPED;
+  *out = &it->second;
+  return PA_OK;
 }
 
 // Blocks an append of n tokens to `s` needs: fresh blocks for the positions
@@ -278,6 +306,7 @@ pa_status pa_seq_append(pa_alloc* a, int64_t seq, int32_t n_tokens, int64_t* slo
     return PA_ERR_ARG;
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
+  if (it->second.swapped) return PA_ERR_SWAPPED;
   if ((int64_t)it->second.len + n_tokens > INT32_MAX) return PA_ERR_ARG;
   const AppendPlan p = plan_append(a, it->second, n_tokens);
   if (p.new_blocks + (p.cow ? 1 : 0) > available(a)) return PA_ERR_OOM;
@@ -290,6 +319,7 @@ pa_status pa_seq_append_tokens(pa_alloc* a, int64_t seq, const int32_t* tokens, 
   if (!a || n_tokens < 0 || (n_tokens > 0 && !tokens)) return PA_ERR_ARG;
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
+  if (it->second.swapped) return PA_ERR_SWAPPED;
   const int32_t before = it->second.len;
   const pa_status st = pa_seq_append(a, seq, n_tokens, slots_out, cow_pair_out, num_cow_out);
   if (st != PA_OK) return st;
@@ -362,6 +392,94 @@ pa_status pa_prefix_cache_query(const pa_alloc* a, int32_t* evictable_out, int32
   return PA_OK;
 }
 
+pa_status pa_alloc_enable_swap(pa_alloc* a, int32_t num_host_blocks) {
+  if (!a || num_host_blocks <= 0 || a->num_host_blocks > 0) return PA_ERR_ARG;
+  a->num_host_blocks = num_host_blocks;
+  for (int32_t h = 0; h < num_host_blocks; ++h) a->host_free.push_back(h);
+  return PA_OK;
+}
+
+pa_status pa_seq_swap_out(pa_alloc* a, int64_t seq, int32_t* pairs_out, int32_t capacity,
+                          int32_t* num_pairs_out) {
+  if (!a || !num_pairs_out || capacity < 0 || (capacity > 0 && !pairs_out) ||
+      a->num_host_blocks == 0)
+    return PA_ERR_ARG;
+  pa_alloc::Seq* s = nullptr;
+  const pa_status st = find_resident(a, seq, &s);
+  if (st != PA_OK) return st;
+  int64_t own = 0;
+  for (int32_t b : s->table) own += a->refcount[b] == 1;
+  if (own > capacity) return PA_ERR_ARG;
+  if (own > (int64_t)a->host_free.size()) return PA_ERR_OOM;
+  std::vector<int32_t> released;
+  int32_t np = 0;
+  for (int32_t& b : s->table) {
+    if (a->refcount[b] != 1) continue;  // shared: stays on the device
+    const int32_t h = a->host_free.front();
+    a->host_free.pop_front();
+    pairs_out[2 * np] = b;
+    pairs_out[2 * np + 1] = h;
+    ++np;
+    a->refcount[b] = 0;
+    released.push_back(b);
+    b = -h - 1;
+  }
+  release_blocks(a, released);
+  s->swapped = true;
+  a->swapped_seqs += 1;
+  a->swap_outs += 1;
+  a->blocks_out += np;
+  *num_pairs_out = np;
+  return PA_OK;
+}
+
+pa_status pa_seq_swap_in(pa_alloc* a, int64_t seq, int32_t* pairs_out, int32_t capacity,
+                         int32_t* num_pairs_out) {
+  if (!a || !num_pairs_out || capacity < 0 || (capacity > 0 && !pairs_out)) return PA_ERR_ARG;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
+  pa_alloc::Seq& s = it->second;
+  if (!s.swapped) return PA_ERR_ARG;
+  int64_t on_host = 0;
+  for (int32_t b : s.table) on_host += b < 0;
+  if (on_host > capacity) return PA_ERR_ARG;
+  if (on_host > available(a)) return PA_ERR_OOM;
+  std::vector<int32_t> hosts;
+  int32_t np = 0;
+  for (int32_t& b : s.table) {
+    if (b >= 0) continue;
+    const int32_t h = -b - 1;
+    const int32_t d = take_block(a);
+    a->refcount[d] = 1;
+    pairs_out[2 * np] = h;
+    pairs_out[2 * np + 1] = d;
+    ++np;
+    hosts.push_back(h);
+    b = d;
+  }
+  for (int32_t h : hosts) a->host_free.push_back(h);
+  s.swapped = false;
+  a->swapped_seqs -= 1;
+  a->swap_ins += 1;
+  a->blocks_in += np;
+  *num_pairs_out = np;
+  return PA_OK;
+}
+
+pa_status pa_swap_query(const pa_alloc* a, pa_swap_stats* stats, int32_t* host_free_out) {
+  if (!a) return PA_ERR_ARG;
+  if (stats) {
+    stats->swap_outs = a->swap_outs;
+    stats->swap_ins = a->swap_ins;
+    stats->blocks_out = a->blocks_out;
+    stats->blocks_in = a->blocks_in;
+    stats->swapped_seqs = a->swapped_seqs;
+    stats->host_free = (int32_t)a->host_free.size();
+  }
+  if (host_free_out) std::copy(a->host_free.begin(), a->host_free.end(), host_free_out);
+  return PA_OK;
+}
+
 pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32_t n_tokens,
                               int64_t* slots_out, int32_t* pairs_out, int32_t* num_pairs_out) {
   if (!a || n < 0 || n_tokens < 0 || (n > 0 && (!seqs || !pairs_out)) || !num_pairs_out ||
@@ -376,6 +494,7 @@ pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32
   for (int32_t i = 0; i < n; ++i) {
     auto it = a->seqs.find(seqs[i]);
     if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
+    if (it->second.swapped) return PA_ERR_SWAPPED;
     for (int32_t j = 0; j < i; ++j)
       if (seqs[j] == seqs[i]) return PA_ERR_ARG;  // one append per sequence per step
     if ((int64_t)it->second.len + n_tokens > INT32_MAX) return PA_ERR_ARG;
@@ -418,6 +537,7 @@ pa_status pa_seq_fork(pa_alloc* a, int64_t parent, int64_t* child_out) {
   if (!a || !child_out) return PA_ERR_ARG;
   auto it = a->seqs.find(parent);
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
+  if (it->second.swapped) return PA_ERR_SWAPPED;
   pa_alloc::Seq child = it->second;  // copy before emplace (rehash)
   for (int32_t b : child.table) a->refcount[b] += 1;
   const int64_t id = a->next_id++;
@@ -430,6 +550,7 @@ pa_status pa_seq_share_prefix(pa_alloc* a, int64_t src, int32_t n_tokens, int64_
   if (!a || !seq_out) return PA_ERR_ARG;
   auto it = a->seqs.find(src);
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
+  if (it->second.swapped) return PA_ERR_SWAPPED;
   if (n_tokens < 0 || n_tokens > it->second.len) return PA_ERR_ARG;
   pa_alloc::Seq s;
   const pa_alloc::Seq& src_seq = it->second;
@@ -453,8 +574,21 @@ pa_status pa_seq_free(pa_alloc* a, int64_t seq) {
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
   for (int32_t b : it->second.table)
-    if (a->refcount[b] <= 0) return PA_ERR_REFCOUNT;
-  release_table(a, it->second.table);
+    if (b >= 0 && a->refcount[b] <= 0) return PA_ERR_REFCOUNT;
+  if (it->second.swapped) {
+    // host blocks back to the host list, device references dropped
+    std::vector<int32_t> released;
+    for (int32_t b : it->second.table) {
+      if (b < 0)
+        a->host_free.push_back(-b - 1);
+      else if (--a->refcount[b] == 0)
+        released.push_back(b);
+    }
+    release_blocks(a, released);
+    a->swapped_seqs -= 1;
+  } else {
+    release_table(a, it->second.table);
+  }
   a->seqs.erase(it);
   return PA_OK;
 }
@@ -482,6 +616,7 @@ pa_status pa_build_tables(const pa_alloc* a, const int64_t* seqs, int32_t n, int
   for (int32_t i = 0; i < n; ++i) {
     auto it = a->seqs.find(seqs[i]);
     if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
+    if (it->second.swapped) return PA_ERR_SWAPPED;
     if ((int64_t)it->second.table.size() > max_blocks) return PA_ERR_ARG;
   }
   for (int32_t i = 0; i < n; ++i) {
@@ -520,15 +655,28 @@ pa_status pa_alloc_stats(const pa_alloc* a, int64_t* lazy_allocs, int64_t* cow_c
 pa_status pa_alloc_check_invariants(const pa_alloc* a) {
   if (!a) return PA_ERR_ARG;
   std::vector<int32_t> indeg(a->num_blocks, 0);
+  std::vector<char> host_seen(a->num_host_blocks, 0);
   for (const auto& kv : a->seqs) {
     const auto& s = kv.second;
     if ((int64_t)s.table.size() != ceil_div(s.len, a->block_size)) return PA_ERR_REFCOUNT;
     for (int32_t b : s.table) {
+      if (b < 0 && s.swapped) {
+        const int32_t h = -b - 1;
+        if (h >= a->num_host_blocks || host_seen[h]) return PA_ERR_REFCOUNT;
+        host_seen[h] = 1;
+        continue;
+      }
       if (b < 0 || b >= a->num_blocks) return PA_ERR_REFCOUNT;
       indeg[b] += 1;
     }
   }
   if (indeg != a->refcount) return PA_ERR_REFCOUNT;
+  for (int32_t h : a->host_free) {
+    if (h < 0 || h >= a->num_host_blocks || host_seen[h]) return PA_ERR_REFCOUNT;
+    host_seen[h] = 1;
+  }
+  for (char c : host_seen)
+    if (!c) return PA_ERR_REFCOUNT;
   std::vector<char> in_free(a->num_blocks, 0);
   for (int32_t b : a->free_pool) {
     if (b < 0 || b >= a->num_blocks || in_free[b]) return PA_ERR_REFCOUNT;

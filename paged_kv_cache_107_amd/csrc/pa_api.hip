@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr int32_t kDefaultPartition = 512;
 constexpr int32_t kMaxPartition = 4096;
 constexpr int32_t kMaxGridYZ = 65535;
@@ -185,6 +185,31 @@ bool needs_reduce(const Prepared& pr) {
 
 }  // namespace
 
+// The device address of a pinned host range [host, host + bytes): both ends
+// must lie in pinned host memory mapped for the device, at device addresses
+// bytes - 1 apart.  PA_ERR_ARG otherwise (pageable memory would fault).
+static pa_status mapped_host_range(void* host, int64_t bytes, void** dev_out) {
+  char* first = static_cast<char*>(host);
+  char* last = first + bytes - 1;
+  void* dev[2] = {nullptr, nullptr};
+  char* ends[2] = {first, last};
+  for (int e = 0; e < 2; ++e) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, ends[e]) != hipSuccess) {
+      (void)hipGetLastError();
+      return PA_ERR_ARG;
+    }
+    if (attr.type != hipMemoryTypeHost) return PA_ERR_ARG;
+    if (hipHostGetDevicePointer(&dev[e], ends[e], 0) != hipSuccess || !dev[e]) {
+      (void)hipGetLastError();
+      return PA_ERR_ARG;
+    }
+  }
+  if (static_cast<char*>(dev[1]) - static_cast<char*>(dev[0]) != bytes - 1) return PA_ERR_ARG;
+  *dev_out = dev[0];
+  return PA_OK;
+}
+
 extern "C" {
 
 int32_t pa_abi_version(void) { return kAbiVersion; }
@@ -199,6 +224,7 @@ const char* pa_status_string(int32_t s) {
     case PA_ERR_REFCOUNT: return "PA_ERR_REFCOUNT";
     case PA_ERR_NOT_FOUND: return "PA_ERR_NOT_FOUND";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_SWAPPED: return "PA_ERR_SWAPPED";
     default: return "PA_ERR_UNKNOWN";
   }
 }
@@ -347,6 +373,34 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool,
     return PA_ERR_ARG;
   return pa::launch_copy_blocks(k_pool, v_pool, *pool, pairs, num_pairs,
                                 static_cast<hipStream_t>(hip_stream));
+}
+
+pa_status pa_swap_blocks(void* k_pool, void* v_pool, void* k_host, void* v_host,
+                         int32_t num_host_blocks, const pa_pool_desc* pool, const int32_t* pairs,
+                         int32_t num_pairs, int32_t direction, void* hip_stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0 || num_pairs > kMaxGridYZ || num_host_blocks <= 0) return PA_ERR_ARG;
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN) return PA_ERR_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_host || !v_host || !pairs) return PA_ERR_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_host) || !aligned16(v_host) ||
+      (reinterpret_cast<uintptr_t>(pairs) & 3u))
+    return PA_ERR_ARG;
+  const int64_t block_bytes = (int64_t)pool->num_kv_heads * pool->block_size * pool->head_dim *
+                              (pool->dtype == PA_F32 ? 4 : 2);
+  void* k_dev = nullptr;
+  void* v_dev = nullptr;
+  st = mapped_host_range(k_host, (int64_t)num_host_blocks * block_bytes, &k_dev);
+  if (st != PA_OK) return st;
+  st = mapped_host_range(v_host, (int64_t)num_host_blocks * block_bytes, &v_dev);
+  if (st != PA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (direction == PA_SWAP_OUT)
+    return pa::launch_swap_blocks(k_pool, v_pool, k_dev, v_dev, pool->num_blocks,
+                                  num_host_blocks, *pool, pairs, num_pairs, s);
+  return pa::launch_swap_blocks(k_dev, v_dev, k_pool, v_pool, num_host_blocks, pool->num_blocks,
+                                *pool, pairs, num_pairs, s);
 }
 
 }  // extern "C"

@@ -11,6 +11,11 @@
 //    write ("Lazy Allocation 与 Copy-on-Write ...", section 4.4).  A block is
 //    Hkv x BS rows, contiguous in the pool; each workgroup streams a slice of
 //    one block of one pool.
+//  * swap_blocks: a preempted sequence's blocks moved one by one between the
+//    device pools and pinned host pools of the same block shape ("vLLM：把 KV
+//    缓存当成虚拟内存", section "碎片从哪里来").  The same slicing as
+//    copy_blocks, with the host side read or written directly over the host
+//    link: many 16-byte accesses in flight per CU cover its latency.
 #include <hip/hip_runtime.h>
 
 #include "pa.h"
@@ -53,6 +58,20 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_
     d[c] = s[c];
 }
 
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const u32x4* __restrict__ src_k, const u32x4* __restrict__ src_v, u32x4* __restrict__ dst_k,
+    u32x4* __restrict__ dst_v, const int32_t* __restrict__ pairs, int32_t src_blocks,
+    int32_t dst_blocks, int64_t chunks_per_block) {
+  const int32_t pr = blockIdx.y;
+  const int32_t src = pairs[2 * pr], dst = pairs[2 * pr + 1];
+  if ((unsigned)src >= (unsigned)src_blocks || (unsigned)dst >= (unsigned)dst_blocks) return;
+  const u32x4* s = (blockIdx.z == 0 ? src_k : src_v) + (int64_t)src * chunks_per_block;
+  u32x4* d = (blockIdx.z == 0 ? dst_k : dst_v) + (int64_t)dst * chunks_per_block;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks_per_block;
+       c += (int64_t)gridDim.x * blockDim.x)
+    d[c] = s[c];
+}
+
 static int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
 
 pa_status launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
@@ -82,6 +101,21 @@ pa_status launch_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc& poo
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, (unsigned)num_pairs, 2), dim3(256), 0, st,
                      static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), pairs,
                      pool.num_blocks, chunks_per_block);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                             int32_t src_blocks, int32_t dst_blocks, const pa_pool_desc& pool,
+                             const int32_t* pairs, int32_t num_pairs, hipStream_t st) {
+  if (num_pairs == 0) return PA_OK;
+  const int64_t chunks_per_block = (int64_t)pool.num_kv_heads * pool.block_size * pool.head_dim *
+                                   elem_bytes(pool.dtype) / 16;
+  const int64_t slices = (chunks_per_block + 255) / 256;
+  const unsigned gx = (unsigned)(slices < 64 ? slices : 64);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(gx, (unsigned)num_pairs, 2), dim3(256), 0, st,
+                     static_cast<const u32x4*>(src_k), static_cast<const u32x4*>(src_v),
+                     static_cast<u32x4*>(dst_k), static_cast<u32x4*>(dst_v), pairs, src_blocks,
+                     dst_blocks, chunks_per_block);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -91,5 +91,8 @@ pa_status launch_reshape_and_cache(const void* k, const void* v, const int64_t* 
                                    const pa_pool_desc& pool, hipStream_t st);
 pa_status launch_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc& pool,
                              const int32_t* pairs, int32_t num_pairs, hipStream_t st);
+pa_status launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                             int32_t src_blocks, int32_t dst_blocks, const pa_pool_desc& pool,
+                             const int32_t* pairs, int32_t num_pairs, hipStream_t st);
 
 }  // namespace pa

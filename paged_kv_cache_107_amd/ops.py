@@ -171,3 +171,26 @@ def pa_copy_blocks(k_pool, v_pool, pairs, stream=None):
     st = lib().pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), C.byref(desc), _ptr(pairs),
                               int(pairs.shape[0]), _stream(stream))
     check("pa_copy_blocks", st)
+
+
+def pa_swap_blocks(k_pool, v_pool, k_host, v_host, pairs, direction: int, stream=None):
+    """Copy whole blocks between the device pools and pinned host pools of the
+    same block shape: PA_SWAP_OUT copies device p[0] -> host p[1], PA_SWAP_IN
+    host p[0] -> device p[1] for each row p of pairs ([P][2] int32, device).
+    See pa.h."""
+    desc = _check_pools(k_pool, v_pool)
+    for name, h in (("k_host", k_host), ("v_host", v_host)):
+        if h.device.type != "cpu" or not h.is_pinned() or not h.is_contiguous() \
+                or h.dtype != k_pool.dtype or tuple(h.shape[1:]) != tuple(k_pool.shape[1:]):
+            raise ValueError(f"{name} must be a contiguous pinned host tensor "
+                             f"[NHB]{list(k_pool.shape[1:])} of {k_pool.dtype}")
+    if k_host.shape != v_host.shape:
+        raise ValueError("k_host and v_host must have the same shape")
+    _need_cuda("pairs", pairs, torch.int32)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [num_pairs][2]")
+    st = lib().pa_swap_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(k_host), _ptr(v_host),
+                              int(k_host.shape[0]), C.byref(desc), _ptr(pairs),
+                              int(pairs.shape[0]), int(direction), _stream(stream))
+    check("pa_swap_blocks", st)
+

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = pa.lib()
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
     assert lib.pa_status_string(0) == b"PA_OK"
     assert lib.pa_status_string(-4) == b"PA_ERR_OOM"
     assert lib.pa_status_string(-99) == b"PA_ERR_UNKNOWN"

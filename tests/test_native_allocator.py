@@ -71,7 +71,7 @@ class Twin:
         stats = self.n.pa_alloc_stats()
         assert stats["cow_copies"] == self.o.cow_copies
         assert stats["lazy_allocs"] == self.o.lazy_allocs
-        assert stats["live_seqs"] == len(self.o.tables)
+        assert stats["live_seqs"] == len(self.o.tables) + len(self.o.swapped)
 
     def _both(self, fo, fn):
         eo = en = None
@@ -85,7 +85,8 @@ class Twin:
             en = e
         assert (eo is None) == (en is None), (eo, en)
         if eo is not None:
-            code = {"ARG": -1, "OOM": -4, "REFCOUNT": -5, "NOT_FOUND": -6}[eo.code]
+            code = {"ARG": -1, "OOM": -4, "REFCOUNT": -5, "NOT_FOUND": -6,
+                    "SWAPPED": -8}[eo.code]
             assert en.status == code, (eo, en)
             self._state_equal()
             raise eo

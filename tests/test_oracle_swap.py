@@ -211,9 +211,11 @@ def test_random_operations_keep_contents_and_invariants(ops, bs, nb, nh, cache):
                 a.free_seq(pick)
                 del toks[pick]
             elif op == "out" and pick is not None:
-                pools.out(a.swap_out(pick))
+                resident = [x for x in live if x in a.tables] or [pick]
+                pools.out(a.swap_out(resident[r % len(resident)]))
             elif op == "in" and pick is not None:
-                pools.back(a.swap_in(pick))
+                away = [x for x in live if x in a.swapped] or [pick]
+                pools.back(a.swap_in(away[r % len(away)]))
         except OracleError as e:
             assert e.code in ("OOM", "SWAPPED", "ARG"), e
             if e.code == "ARG":
