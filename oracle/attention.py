@@ -22,6 +22,16 @@ Readings where the pages are silent:
 * The page's block-loop pseudocode leaves its running maximum undefined and
   does not rescale; ``partitioned_decode`` states the standard online-softmax
   merge (running max, rescaled sums) and is pinned to ``paged_decode``.
+
+Variants (the pages list sliding windows and the cache's element type among
+the things the paged kernel must follow: "vLLM：把 KV 缓存当成虚拟内存", the
+paragraph on variants; no formula is given):
+
+* ``window`` W > 0: a token at position p attends positions max(0, p - W + 1)
+  .. p, i.e. its own and the W - 1 before it.  A decode query sits at
+  position ctx - 1.
+* An 8-bit pool (``kv_dtype="fp8_e4m3"``) holds E4M3 codes; element value =
+  code value * k_scale (K) or * v_scale (V); q and outputs keep ``dtype``.
 """
 from __future__ import annotations
 
@@ -29,9 +39,14 @@ import math
 
 import numpy as np
 
+from . import fp8
 
-def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Element bit patterns -> float64 values."""
+
+def decode_bits(bits: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Element bit patterns -> float64 values (an 8-bit pool's codes times
+    its scale)."""
+    if dtype == "fp8_e4m3":
+        return fp8.dequantize(bits, scale)
     if dtype == "f32":
         return np.asarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
     if dtype == "f16":
@@ -44,17 +59,24 @@ def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def gather_sequence(pool: np.ndarray, table_row, ctx: int) -> np.ndarray:
-    """Reassemble one sequence's tokens from a pool [NB][Hkv][BS][D]:
-    logical block j is physical block table_row[j]; returns [ctx][Hkv][D]."""
+def gather_sequence(pool: np.ndarray, table_row, ctx: int, first: int = 0) -> np.ndarray:
+    """Reassemble tokens first .. ctx - 1 of one sequence from a pool
+    [NB][Hkv][BS][D]: logical block j is physical block table_row[j] (only
+    the blocks holding those positions are read); returns [ctx - first][Hkv][D]."""
     bs = pool.shape[2]
+    j0 = first // bs
     n_blocks = -(-ctx // bs)
     pieces = []
-    for j in range(n_blocks):
+    for j in range(j0, n_blocks):
         blk = int(table_row[j])
         pieces.append(np.transpose(pool[blk], (1, 0, 2)))  # [BS][Hkv][D]
     rows = np.concatenate(pieces, axis=0)
-    return rows[:ctx]
+    return rows[first - j0 * bs:ctx - j0 * bs]
+
+
+def window_start(pos: int, window: int) -> int:
+    """First position a token at ``pos`` attends (0 without a window)."""
+    return max(0, pos - window + 1) if window > 0 else 0
 
 
 def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
@@ -76,19 +98,25 @@ def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -
 
 
 def paged_decode(q_bits, k_pool_bits, v_pool_bits, block_tables, context_lens,
-                 scale: float, dtype: str, seqs=None) -> np.ndarray:
+                 scale: float, dtype: str, seqs=None, window: int = 0, kv_dtype=None,
+                 k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Decode attention for every sequence (or the listed ``seqs``).
 
     q_bits [B][Hq][D]; pools [NB][Hkv][BS][D]; block_tables [B][max_blocks];
-    context_lens [B].  Returns float64 [len(seqs)][Hq][D].
+    context_lens [B].  With ``window`` the query (position ctx - 1) attends
+    only positions window_start(ctx - 1, window) .. ctx - 1.  ``kv_dtype``
+    (default ``dtype``) is the pools' element type.  Returns float64
+    [len(seqs)][Hq][D].
     """
     if seqs is None:
         seqs = range(q_bits.shape[0])
+    kvt = kv_dtype or dtype
     outs = []
     for i in seqs:
         ctx = int(context_lens[i])
-        k = decode_bits(gather_sequence(k_pool_bits, block_tables[i], ctx), dtype)
-        v = decode_bits(gather_sequence(v_pool_bits, block_tables[i], ctx), dtype)
+        first = window_start(ctx - 1, window)
+        k = decode_bits(gather_sequence(k_pool_bits, block_tables[i], ctx, first), kvt, k_scale)
+        v = decode_bits(gather_sequence(v_pool_bits, block_tables[i], ctx, first), kvt, v_scale)
         q = decode_bits(q_bits[i], dtype)
         outs.append(dense_attention(q, k, v, scale))
     return np.stack(outs) if outs else np.zeros((0,) + q_bits.shape[1:])
@@ -137,7 +165,8 @@ def partitioned_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float
 
 
 def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_tables, query_start, context_lens,
-                  scale: float, dtype: str) -> np.ndarray:
+                  scale: float, dtype: str, window: int = 0, kv_dtype=None, k_scale: float = 1.0,
+                  v_scale: float = 1.0) -> np.ndarray:
     """Chunked-prefill attention for a batch of sequences.
 
     Prefill runs a prompt's tokens through attention and writes their K/V
@@ -153,21 +182,27 @@ def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_tables, query_start, c
     positions ``0 .. ctx_i - n_i + j``.  A token whose position would be
     negative (``ctx_i < n_i``) has an all-zero row.
 
+    With ``window`` token j sees only positions window_start(pos, window) ..
+    pos; ``kv_dtype``, ``k_scale``, ``v_scale`` as in ``paged_decode``.
+
     q_bits [T][Hq][D]; pools [NB][Hkv][BS][D]; block_tables [B][max_blocks];
     query_start [B+1]; context_lens [B].  Returns float64 [T][Hq][D].
     """
     out = np.zeros(q_bits.shape, dtype=np.float64)
+    kvt = kv_dtype or dtype
     for i in range(len(context_lens)):
         a, b = int(query_start[i]), int(query_start[i + 1])
         n, ctx = b - a, int(context_lens[i])
         if n <= 0 or ctx <= 0:
             continue
-        k = decode_bits(gather_sequence(k_pool_bits, block_tables[i], ctx), dtype)
-        v = decode_bits(gather_sequence(v_pool_bits, block_tables[i], ctx), dtype)
+        first = window_start(max(ctx - n, 0), window)   # the first row's window
+        k = decode_bits(gather_sequence(k_pool_bits, block_tables[i], ctx, first), kvt, k_scale)
+        v = decode_bits(gather_sequence(v_pool_bits, block_tables[i], ctx, first), kvt, v_scale)
         for j in range(n):
             pos = ctx - n + j
             if pos < 0:
                 continue
+            lo = window_start(pos, window) - first
             q = decode_bits(q_bits[a + j], dtype)
-            out[a + j] = dense_attention(q, k[:pos + 1], v[:pos + 1], scale)
+            out[a + j] = dense_attention(q, k[lo:pos + 1 - first], v[lo:pos + 1 - first], scale)
     return out

@@ -14,6 +14,8 @@ f16/bf16), so both operations are bit-exact by construction.
 * ``copy_blocks``: the copy-on-write copy of a whole shared block before the
   writer's first write ("Lazy Allocation 与 Copy-on-Write ...", section 4.4).
   Pairs are applied in order, all before any write of the same step.
+* ``write_slots_fp8``: the cache write into an 8-bit pool: each element is
+  quantised (``oracle.fp8.quantize``) with the pool's scale as it is stored.
 * ``swap_blocks``: a preempted sequence's blocks moved one by one between the
   device pool and a host pool of the same block shape ("vLLM：把 KV 缓存当成
   虚拟内存", section "碎片从哪里来").
@@ -49,3 +51,12 @@ def swap_blocks(src_pool: np.ndarray, dst_pool: np.ndarray, pairs) -> None:
     pools of the same block shape (device -> host or host -> device)."""
     for src, dst in pairs:
         dst_pool[int(dst)] = src_pool[int(src)]
+
+
+def write_slots_fp8(pool: np.ndarray, new_values: np.ndarray, slots: np.ndarray,
+                    scale: float) -> None:
+    """``write_slots`` into an E4M3 pool of uint8 codes: new_values [T][Hkv][D]
+    are float32 K or V values, quantised with the pool's scale."""
+    from .fp8 import quantize
+    write_slots(pool, quantize(new_values, scale), slots)
+
