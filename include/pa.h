@@ -261,6 +261,9 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool,
  * ------------------------------------------------------------------------ */
 typedef struct pa_alloc pa_alloc;
 
+/* Table entry of a block a sliding window released (pa_seq_trim_window). */
+#define PA_NO_BLOCK (-2147483647 - 1)
+
 pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
                           const int32_t* initial_free_order, pa_alloc** out);
 void pa_alloc_destroy(pa_alloc* a);
@@ -351,6 +354,22 @@ pa_status pa_seq_append_tokens(pa_alloc* a, int64_t seq, const int32_t* tokens, 
 pa_status pa_prefix_cache_stats(const pa_alloc* a, pa_prefix_stats* out);
 /* Evictable blocks, least recently used first (evictable_out [NB] or NULL). */
 pa_status pa_prefix_cache_query(const pa_alloc* a, int32_t* evictable_out, int32_t* num_out);
+
+/* ------------------------------------------------------------------------
+ * Sliding window.  With a window of W positions, the newest token (position
+ * len - 1) and every later one attend only positions >= len - W, so a block
+ * whose positions all lie below len - W is never read again (page "vLLM：把
+ * KV 缓存当成虚拟内存": sliding windows change how long K/V live).
+ * pa_seq_trim_window drops the sequence's reference to each such block
+ * (released as pa_seq_free releases: free pool, or evictable if cached) and
+ * leaves PA_NO_BLOCK in its table entry; the table keeps its length, so
+ * entry j still maps positions j * BS ...  Attention with the same window
+ * never reads those entries.  Holes are skipped by every other call; a fork
+ * copies them; pa_seq_share_prefix of a prefix that includes one returns
+ * PA_ERR_ARG.  *released_out (may be NULL) = entries that became holes.
+ * PA_ERR_ARG for window <= 0; PA_ERR_SWAPPED for a swapped-out sequence.
+ * ------------------------------------------------------------------------ */
+pa_status pa_seq_trim_window(pa_alloc* a, int64_t seq, int32_t window, int32_t* released_out);
 
 /* ------------------------------------------------------------------------
  * Swapping (preemption).  A preempted sequence's KV moves to host memory and

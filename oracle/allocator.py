@@ -95,6 +95,17 @@ Readings (the pages name the move, not its bookkeeping):
   list in logical order.  The new blocks are private (refcount 1) and not
   cached.
 * Both moves are all or nothing: ``OOM`` when the destination is short.
+
+Sliding window (``trim_window``): with a window of W positions, the newest
+token (position len - 1) and every later one attend only positions >= len -
+W, so a block whose positions all lie below len - W is never read again
+("vLLM：把 KV 缓存当成虚拟内存": sliding windows change how long K/V live).
+Trimming drops the sequence's reference to each such block (released as
+``free_seq`` releases) and leaves a hole (``NO_BLOCK``) in its table, which
+keeps its length, so logical block j still maps position j * BS.  Holes are
+skipped by every other operation; a fork copies them; sharing a prefix that
+includes a hole is refused (ARG): the allocator does not know the sharer's
+window, and a prefix without its early blocks is not the whole prefix.
 """
 from __future__ import annotations
 
@@ -102,6 +113,9 @@ from collections import OrderedDict, deque
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
+
+
+NO_BLOCK = -(2 ** 31)  # table entry of a block released by a sliding window
 
 
 class OracleError(Exception):
@@ -207,7 +221,7 @@ class OracleAllocator:
         for j in range(self.considered[seq], full):
             key = tuple(known[:(j + 1) * bs])
             blk = table[j]
-            if key not in self.index and blk not in self.block_key:
+            if blk != NO_BLOCK and key not in self.index and blk not in self.block_key:
                 self.index[key] = blk
                 self.block_key[blk] = key
         self.considered[seq] = max(self.considered[seq], full)
@@ -308,7 +322,8 @@ class OracleAllocator:
         self.tokens[child] = list(self.tokens[parent])
         self.considered[child] = self.considered[parent]
         for b in table:
-            self.refcount[b] += 1
+            if b != NO_BLOCK:
+                self.refcount[b] += 1
         return child
 
     def share_prefix(self, src: int, n_tokens: int) -> int:
@@ -316,13 +331,16 @@ class OracleAllocator:
         if n_tokens < 0 or n_tokens > self.lens[src]:
             raise OracleError("ARG", "prefix longer than the source")
         k = _ceil_div(n_tokens, self.block_size)
+        if NO_BLOCK in table[:k]:
+            raise OracleError("ARG", "part of the prefix was released by a sliding window")
         s = self._new_id()
         self.tables[s] = list(table[:k])
         self.lens[s] = n_tokens
         self.tokens[s] = list(self.tokens[src][:n_tokens])
         self.considered[s] = min(self.considered[src], n_tokens // self.block_size)
         for b in self.tables[s]:
-            self.refcount[b] += 1
+            if b != NO_BLOCK:
+                self.refcount[b] += 1
         return s
 
     def free_seq(self, seq: int) -> None:
@@ -332,7 +350,7 @@ class OracleAllocator:
             for on_host, i in entries:
                 if on_host:
                     self.host_free.append(i)
-                else:
+                elif i != NO_BLOCK:
                     self.refcount[i] -= 1
                     if self.refcount[i] == 0:
                         released.append(i)
@@ -341,7 +359,7 @@ class OracleAllocator:
             del self.tokens[seq]
             del self.considered[seq]
             return
-        table = self._seq(seq)
+        table = [b for b in self._seq(seq) if b != NO_BLOCK]
         for b in table:
             if self.refcount[b] <= 0:
                 raise OracleError("REFCOUNT", f"block {b} already free")
@@ -356,6 +374,28 @@ class OracleAllocator:
         del self.tokens[seq]
         del self.considered[seq]
 
+    # ------------------------------------------------------------ sliding window
+    def trim_window(self, seq: int, window: int) -> int:
+        """Release the blocks of ``seq`` that lie wholly below position
+        len - window; returns how many table entries became holes."""
+        table = self._seq(seq)
+        if window <= 0:
+            raise OracleError("ARG", "window must be positive")
+        bs = self.block_size
+        dead = max(self.lens[seq] - window, 0) // bs     # blocks j with (j + 1) * BS <= len - W
+        released, n = [], 0
+        for j in range(dead):
+            b = table[j]
+            if b == NO_BLOCK:
+                continue
+            table[j] = NO_BLOCK
+            n += 1
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                released.append(b)
+        self._release(released)
+        return n
+
     # ------------------------------------------------------------ swapping
     def enable_swap(self, num_host_blocks: int) -> None:
         if self.host_free is not None or num_host_blocks <= 0:
@@ -369,7 +409,7 @@ class OracleAllocator:
         if self.host_free is None:
             raise OracleError("ARG", "swap is off")
         table = self._seq(seq)
-        own = [j for j, b in enumerate(table) if self.refcount[b] == 1]
+        own = [j for j, b in enumerate(table) if b != NO_BLOCK and self.refcount[b] == 1]
         if len(own) > len(self.host_free):
             raise OracleError("OOM", f"need {len(own)} host blocks, free {len(self.host_free)}")
         entries = [(False, b) for b in table]
@@ -440,7 +480,8 @@ class OracleAllocator:
             if len(t) != _ceil_div(self.lens[s], self.block_size):
                 raise AssertionError(f"seq {s}: {len(t)} blocks for {self.lens[s]} tokens")
             for b in t:
-                indeg[b] += 1
+                if b != NO_BLOCK:
+                    indeg[b] += 1
         host_used = []
         for s, entries in self.swapped.items():
             if len(entries) != _ceil_div(self.lens[s], self.block_size):
@@ -448,7 +489,7 @@ class OracleAllocator:
             for on_host, i in entries:
                 if on_host:
                     host_used.append(i)
-                else:
+                elif i != NO_BLOCK:
                     indeg[i] += 1
         if self.host_free is not None and sorted(list(self.host_free) + host_used) != \
                 list(range(self.num_host_blocks)):

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_OK, PA_ERR_ARG, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_OOM, PA_ERR_REFCOUNT, \
     PA_ERR_NOT_FOUND, PA_ERR_HIP, PA_ERR_SWAPPED = 0, -1, -2, -3, -4, -5, -6, -7, -8
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
+PA_NO_BLOCK = -(2 ** 31)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA, PA_PATH_MFMA_GRID = 0, 1, 2, 3
 
@@ -70,6 +71,7 @@ SIGNATURES = {
     "pa_seq_append_tokens": (_i32, [_vp, _i64, _pi32, _i32, _pi64, _pi32, _pi32]),
     "pa_prefix_cache_stats": (_i32, [_vp, C.POINTER(pa_prefix_stats)]),
     "pa_prefix_cache_query": (_i32, [_vp, _pi32, _pi32]),
+    "pa_seq_trim_window": (_i32, [_vp, _i64, _i32, _pi32]),
     "pa_alloc_enable_swap": (_i32, [_vp, _i32]),
     "pa_seq_swap_out": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
     "pa_seq_swap_in": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),

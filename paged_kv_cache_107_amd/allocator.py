@@ -163,6 +163,15 @@ class PaAllocator:
         check("pa_prefix_cache_query", lib().pa_prefix_cache_query(self._h, _i32p(out), C.byref(n)))
         return out[:n.value]
 
+    # ------------------------------------------------------------ sliding window
+    def pa_seq_trim_window(self, seq: int, window: int) -> int:
+        """Release the blocks wholly below position len - window; returns the
+        number of table entries that became PA_NO_BLOCK."""
+        n = C.c_int32()
+        check("pa_seq_trim_window", lib().pa_seq_trim_window(self._h, int(seq), int(window),
+                                                              C.byref(n)))
+        return n.value
+
     # ------------------------------------------------------------ swapping
     def pa_alloc_enable_swap(self, num_host_blocks: int) -> None:
         check("pa_alloc_enable_swap", lib().pa_alloc_enable_swap(self._h, int(num_host_blocks)))

@@ -93,6 +93,11 @@ class PagedKVCache:
     def prefix_stats(self) -> dict:
         return self.alloc.pa_prefix_cache_stats()
 
+    def trim_window(self, seq: int, window: int) -> int:
+        """Host only: release seq's blocks that a sliding window of `window`
+        positions will never read again."""
+        return self.alloc.pa_seq_trim_window(seq, window)
+
     # ------------------------------------------------------------ swapping
     def enable_swap(self, num_host_blocks: int) -> None:
         """A pinned host pool pair of num_host_blocks blocks for preempted

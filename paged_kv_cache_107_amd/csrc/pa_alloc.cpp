@@ -42,6 +42,13 @@
 //    its references to shared blocks on the device; swap-in takes device
 //    blocks the way an append does; both are all or nothing; a swapped-out
 //    sequence can only be swapped in or freed.
+//
+//  * sliding window: with a window of W positions the newest token and every
+//    later one attend only positions >= len - W, so blocks wholly below that
+//    are released and leave a hole (PA_NO_BLOCK) in the table, which keeps
+//    its length ("vLLM：把 KV 缓存当成虚拟内存": sliding windows change how long
+//    K/V live).  Holes are skipped everywhere; a fork copies them; a prefix
+//    that includes one cannot be shared.
 #include <algorithm>
 #include <cstring>
 #include <deque>
@@ -156,7 +163,7 @@ void register_blocks(pa_alloc* a, pa_alloc::Seq& s) {
     const uint64_t h = chain_hash(parent, tok, bs);
     s.hashes.push_back(h);
     const int32_t b = s.table[j];
-    if (a->cached[b] || a->index.count(h)) continue;
+    if (b == PA_NO_BLOCK || a->cached[b] || a->index.count(h)) continue;
     a->index.emplace(h, b);
     a->cached[b] = 1;
     a->key_of[b] = h;
@@ -179,7 +186,7 @@ void release_blocks(pa_alloc* a, const std::vector<int32_t>& released) {
 void release_table(pa_alloc* a, const std::vector<int32_t>& table) {
   std::vector<int32_t> released;
   for (int32_t b : table)
-    if (--a->refcount[b] == 0) released.push_back(b);
+    if (b != PA_NO_BLOCK && --a->refcount[b] == 0) released.push_back(b);
   release_blocks(a, released);
 }
 
@@ -408,13 +415,13 @@ pa_status pa_seq_swap_out(pa_alloc* a, int64_t seq, int32_t* pairs_out, int32_t 
   const pa_status st = find_resident(a, seq, &s);
   if (st != PA_OK) return st;
   int64_t own = 0;
-  for (int32_t b : s->table) own += a->refcount[b] == 1;
+  for (int32_t b : s->table) own += b != PA_NO_BLOCK && a->refcount[b] == 1;
   if (own > capacity) return PA_ERR_ARG;
   if (own > (int64_t)a->host_free.size()) return PA_ERR_OOM;
   std::vector<int32_t> released;
   int32_t np = 0;
   for (int32_t& b : s->table) {
-    if (a->refcount[b] != 1) continue;  // shared: stays on the device
+    if (b == PA_NO_BLOCK || a->refcount[b] != 1) continue;  // shared: stays on the device
     const int32_t h = a->host_free.front();
     a->host_free.pop_front();
     pairs_out[2 * np] = b;
@@ -441,13 +448,13 @@ pa_status pa_seq_swap_in(pa_alloc* a, int64_t seq, int32_t* pairs_out, int32_t c
   pa_alloc::Seq& s = it->second;
   if (!s.swapped) return PA_ERR_ARG;
   int64_t on_host = 0;
-  for (int32_t b : s.table) on_host += b < 0;
+  for (int32_t b : s.table) on_host += b < 0 && b != PA_NO_BLOCK;
   if (on_host > capacity) return PA_ERR_ARG;
   if (on_host > available(a)) return PA_ERR_OOM;
   std::vector<int32_t> hosts;
   int32_t np = 0;
   for (int32_t& b : s.table) {
-    if (b >= 0) continue;
+    if (b >= 0 || b == PA_NO_BLOCK) continue;
     const int32_t h = -b - 1;
     const int32_t d = take_block(a);
     a->refcount[d] = 1;
@@ -539,7 +546,8 @@ pa_status pa_seq_fork(pa_alloc* a, int64_t parent, int64_t* child_out) {
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
   if (it->second.swapped) return PA_ERR_SWAPPED;
   pa_alloc::Seq child = it->second;  // copy before emplace (rehash)
-  for (int32_t b : child.table) a->refcount[b] += 1;
+  for (int32_t b : child.table)
+    if (b != PA_NO_BLOCK) a->refcount[b] += 1;
   const int64_t id = a->next_id++;
   a->seqs.emplace(id, std::move(child));
   *child_out = id;
@@ -555,6 +563,9 @@ pa_status pa_seq_share_prefix(pa_alloc* a, int64_t src, int32_t n_tokens, int64_
   pa_alloc::Seq s;
   const pa_alloc::Seq& src_seq = it->second;
   const int64_t k = ceil_div(n_tokens, a->block_size);
+  if (std::find(src_seq.table.begin(), src_seq.table.begin() + k, PA_NO_BLOCK) !=
+      src_seq.table.begin() + k)
+    return PA_ERR_ARG;  // part of the prefix was released by a sliding window
   s.table.assign(src_seq.table.begin(), src_seq.table.begin() + k);
   s.len = n_tokens;
   s.tokens.assign(src_seq.tokens.begin(),
@@ -569,16 +580,37 @@ pa_status pa_seq_share_prefix(pa_alloc* a, int64_t src, int32_t n_tokens, int64_
   return PA_OK;
 }
 
+pa_status pa_seq_trim_window(pa_alloc* a, int64_t seq, int32_t window, int32_t* released_out) {
+  if (!a || window <= 0) return PA_ERR_ARG;
+  pa_alloc::Seq* s = nullptr;
+  const pa_status st = find_resident(a, seq, &s);
+  if (st != PA_OK) return st;
+  const int64_t dead = std::max<int64_t>((int64_t)s->len - window, 0) / a->block_size;
+  std::vector<int32_t> released;
+  int32_t n = 0;
+  for (int64_t j = 0; j < dead; ++j) {
+    int32_t& b = s->table[j];
+    if (b == PA_NO_BLOCK) continue;
+    if (--a->refcount[b] == 0) released.push_back(b);
+    b = PA_NO_BLOCK;
+    ++n;
+  }
+  release_blocks(a, released);
+  if (released_out) *released_out = n;
+  return PA_OK;
+}
+
 pa_status pa_seq_free(pa_alloc* a, int64_t seq) {
   if (!a) return PA_ERR_ARG;
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return PA_ERR_NOT_FOUND;
   for (int32_t b : it->second.table)
-    if (b >= 0 && a->refcount[b] <= 0) return PA_ERR_REFCOUNT;
+    if (b >= 0 && a->refcount[b] <= 0) return PA_ERR_REFCOUNT;  // holes and host entries are < 0
   if (it->second.swapped) {
     // host blocks back to the host list, device references dropped
     std::vector<int32_t> released;
     for (int32_t b : it->second.table) {
+      if (b == PA_NO_BLOCK) continue;
       if (b < 0)
         a->host_free.push_back(-b - 1);
       else if (--a->refcount[b] == 0)
@@ -660,6 +692,7 @@ pa_status pa_alloc_check_invariants(const pa_alloc* a) {
     const auto& s = kv.second;
     if ((int64_t)s.table.size() != ceil_div(s.len, a->block_size)) return PA_ERR_REFCOUNT;
     for (int32_t b : s.table) {
+      if (b == PA_NO_BLOCK) continue;
       if (b < 0 && s.swapped) {
         const int32_t h = -b - 1;
         if (h >= a->num_host_blocks || host_seen[h]) return PA_ERR_REFCOUNT;

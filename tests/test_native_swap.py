@@ -199,3 +199,70 @@ def test_long_random_run(seed, cache):
     ops = [(names[int(rng.integers(0, len(names)))], int(rng.integers(0, 1 << 30)))
            for _ in range(600)]
     test_random_ops_native_equals_oracle.hypothesis.inner_test(ops, 2, 40, 24, cache)
+
+
+# ------------------------------------------------------------------ sliding-window trims
+
+TRIM_OPS = st.lists(st.tuples(st.sampled_from(["new", "append", "append", "fork", "share", "free",
+                                               "trim", "trim", "out", "in", "serve"]),
+                              st.integers(0, 1 << 30)), min_size=1, max_size=60)
+
+
+def _trim_twin_run(ops, bs, nb, nh, cache, window):
+    t = SwapTwin(nb, bs, nh, cache, list(np.random.default_rng(nb + 1).permutation(nb)))
+    live = []
+    for op, r in ops:
+        rng = np.random.default_rng(r)
+        pick = live[r % len(live)] if live else None
+        try:
+            if op == "new":
+                live.append(t.create())
+            elif op == "serve" and cache:
+                prompt = [int(x) for x in rng.integers(0, 2, rng.integers(1, 10))]
+                s, hit = t.create_prefix(prompt)
+                live.append(s)
+                t.append_tokens(s, prompt[hit:])
+            elif op == "append" and pick is not None:
+                ids = [int(x) for x in rng.integers(0, 2, rng.integers(1, 6))]
+                if cache and r % 2:
+                    t.append_tokens(pick, ids)
+                else:
+                    t.append(pick, len(ids))
+            elif op == "fork" and pick is not None:
+                live.append(t.fork(pick))
+            elif op == "share" and pick is not None:
+                live.append(t.share(pick, int(rng.integers(0, t.o.lens[pick] + 1))))
+            elif op == "free" and pick is not None:
+                t.free(pick)
+                live.remove(pick)
+            elif op == "trim" and pick is not None:
+                a, b = t._both(lambda: t.o.trim_window(pick, window),
+                               lambda: t.n.pa_seq_trim_window(pick, window))
+                assert a == b
+            elif op == "out" and pick is not None:
+                t.swap_out(pick)
+            elif op == "in" and pick is not None:
+                t.swap_in(pick)
+        except OracleError as e:
+            assert e.code in ("OOM", "SWAPPED", "ARG"), e
+    for s in live:
+        t.free(s)
+    stats, host_free = t.n.pa_swap_query()
+    assert sorted(host_free.tolist()) == list(range(nh))
+
+
+@settings(max_examples=200, deadline=None)
+@given(ops=TRIM_OPS, bs=st.sampled_from([1, 2, 4]), nb=st.integers(4, 40),
+       nh=st.integers(1, 16), cache=st.booleans(), window=st.integers(1, 10))
+def test_trims_native_equals_oracle(ops, bs, nb, nh, cache, window):
+    _trim_twin_run(ops, bs, nb, nh, cache, window)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_trims_long_run(seed):
+    rng = np.random.default_rng(100 + seed)
+    names = ["new", "append", "append", "append", "fork", "share", "free", "trim", "out", "in",
+             "serve"]
+    ops = [(names[int(rng.integers(0, len(names)))], int(rng.integers(0, 1 << 30)))
+           for _ in range(600)]
+    _trim_twin_run(ops, 2, 48, 20, seed % 2 == 1, 5)
