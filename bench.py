@@ -22,7 +22,8 @@ matrix-core roofline, and the prefill of requests sharing a system prompt
 with and without the prefix cache (hit rate, pinned blocks, blocks held,
 device time of the prefill pass, host time per request), and swapping every
 8th decode sequence out to pinned host memory and back (host-link rate of
-the swap kernel beside a plain copy of the same size).
+the swap kernel beside a plain copy of the same size), and the decode of the
+same batch with a 1024-position sliding window and on 8-bit E4M3 pools.
 """
 from __future__ import annotations
 
@@ -255,6 +256,74 @@ def measure_prefill(reps: int, log):
 
 
 HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, per direction
+VARIANT_WINDOW = 1024
+FP8_SCALES = (0.05, 0.05)
+
+
+def measure_variants(cache, plan, q, d, reps: int, log):
+    """Decode of the same 8B batch (same block tables, same q) in the
+    attention variants: a sliding window of 1024 positions on the 16-bit
+    pools, and 8-bit E4M3 pools holding the quantised contents of the 16-bit
+    pools (written by the quantising pa_reshape_and_cache), with and without
+    the window.  Each: partition and reduce kernels timed with HIP events on
+    the launch stream; the partition kernel's algorithmic bytes are the
+    attended K/V (at the pool's element size), q, out and the table entries
+    of the attended blocks."""
+    import torch
+    import paged_kv_cache_107_amd as pa
+    wl = d.wl
+    ctx = d.context_lens.astype(np.int64)
+    n_blocks, hkv, bs, dh = cache.k_pool.shape
+    # the 8-bit copy of the pools: every slot written once by the quantising write
+    flat = lambda p: p.permute(0, 2, 1, 3).reshape(n_blocks * bs, hkv, dh).contiguous()
+    k8 = torch.zeros_like(cache.k_pool, dtype=torch.uint8).view(pa.FP8)
+    v8 = torch.zeros_like(k8)
+    slots = torch.arange(n_blocks * bs, dtype=torch.int64, device="cuda")
+    pa.pa_reshape_and_cache(flat(cache.k_pool), flat(cache.v_pool), slots, k8, v8,
+                            kv_scales=FP8_SCALES)
+    torch.cuda.synchronize()
+    del slots
+    out = torch.empty_like(q)
+    ws = cache.workspace(d.batch, wl.num_q_heads, plan.max_context_len)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, kp, vp, window, scales, eb in (
+            ("window_1024", cache.k_pool, cache.v_pool, VARIANT_WINDOW, (1.0, 1.0), wl.elem_bytes),
+            ("fp8_e4m3", k8, v8, 0, FP8_SCALES, 1),
+            ("fp8_e4m3_window_1024", k8, v8, VARIANT_WINDOW, FP8_SCALES, 1)):
+        args = (q, kp, vp, plan.tables, plan.lens, wl.scale, out, ws, plan.max_context_len, 0,
+                None, window, scales)
+        for _ in range(3):
+            pa.pa_decode(*args)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for e in ev:
+            e[0].record(stream)
+            pa.pa_decode_partition(*args)
+            e[1].record(stream)
+            pa.pa_decode_reduce(*args)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        part = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        whole = 1e3 * float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
+        att = np.minimum(ctx, window) if window else ctx
+        first = ctx - att
+        tiles = -(-ctx // 16) - first // 16
+        kv = int(att.sum()) * 2 * hkv * dh * eb
+        alg = kv + 2 * d.batch * wl.num_q_heads * dh * wl.elem_bytes + int(tiles.sum()) * 4 // (
+            bs // 16) + 4 * d.batch
+        gbps = alg / (part * 1e-6) / 1e9
+        res[name] = {"window": window, "kv_dtype": "fp8_e4m3" if eb == 1 else wl.dtype,
+                     "attended_tokens": int(att.sum()), "kv_bytes": kv, "algorithmic_bytes": alg,
+                     "partition_us": round(part, 2), "decode_us": round(whole, 2),
+                     "seq_per_s": round(d.batch / (whole * 1e-6), 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbps, 1),
+                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                  "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
+        log(f"{name}: partition {part:.1f} us ({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS:.1%}), "
+            f"decode {whole:.1f} us, {d.batch / (whole * 1e-6):.0f} seq/s")
+    del k8, v8
+    torch.cuda.empty_cache()
+    return res
 SWAP_DESCRIPTION = ("preemption on the 8B GQA decode batch: every 8th of the 256 sequences "
                     "swapped out to pinned host pools and back, 32 q / 8 kv heads, head_dim 128, "
                     "bf16, block 16")
@@ -499,6 +568,9 @@ def main(argv=None):
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--prefill-reps", type=int, default=20,
                     help="timed pa_prefill calls on the chunked-prefill workload (0 = skip)")
+    ap.add_argument("--variant-reps", type=int, default=50,
+                    help="timed decode calls per attention variant (window, 8-bit pools; 0 = "
+                         "skip)")
     ap.add_argument("--swap-reps", type=int, default=10,
                     help="timed swap-out + swap-in cycles of every 8th decode sequence "
                          "(0 = skip)")
@@ -609,6 +681,9 @@ def main(argv=None):
     prefix = None
     if args.prefix_reps > 0:
         prefix = measure_prefix_cache(args.prefix_reps, log)
+    variants = None
+    if args.variant_reps > 0 and args.workload == "8b_gqa":
+        variants = measure_variants(cache, plan, q, d, args.variant_reps, log)
     swap = None
     if args.swap_reps > 0 and args.workload == "8b_gqa":
         swap = measure_swap(cache, d, args.swap_reps, log)
@@ -651,6 +726,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "prefill": prefill,
         "prefix_cache": prefix,
+        "variants": variants,
         "swap": swap,
     }
     print(json.dumps(rec), flush=True)

@@ -16,7 +16,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pool layout (K and V alike): contiguous [num_blocks][num_kv_heads]
- *   [block_size][head_dim] elements of the pool dtype.  Token position `pos`
+ *   [block_size][head_dim] elements of the pool element type (the dtype, or
+ *   8-bit E4M3 codes for a quantised pool).  Token position `pos`
  *   of a sequence lives in physical block table[pos / block_size] at offset
  *   pos % block_size; its slot is block * block_size + offset.
  * - Device pointers are caller-owned (e.g. torch tensors) and must be 16-byte
@@ -35,6 +36,7 @@
  * - Supported shapes: dtype f32, f16 or bf16; head_dim 64 or 128; block_size
  *   16 or 32; num_q_heads a multiple of num_kv_heads with group
  *   G = num_q_heads / num_kv_heads <= 16 (<= 8 for f32 or head_dim 64).
+ *   8-bit pools: f16 or bf16 dtype, head_dim 128.
  *
  * Thread safety: the kernel entry points are reentrant.  An allocator handle
  * must not be used from two threads at once.
@@ -63,13 +65,24 @@ typedef enum {
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 
+/* Element type of the pools: the dtype itself, or E4M3 8-bit floats (OCP
+ * "fn" variant: bias 7, no infinity, 0x7F/0xFF NaN, largest 448) scaled per
+ * pool.  A quantised cache trades accuracy for capacity and bandwidth (page
+ * "第 6 章 缓存管理", section "缓存的边界"). */
+typedef enum { PA_KV_SAME = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
+
 /* Shape of one K pool and one V pool (both have this shape). */
 typedef struct {
   int32_t num_blocks;   /* physical blocks NB >= 1 */
   int32_t block_size;   /* tokens per block BS: 16 or 32 */
   int32_t num_kv_heads; /* Hkv >= 1 */
   int32_t head_dim;     /* D: 64 or 128 */
-  int32_t dtype;        /* pa_dtype of pools, q and out */
+  int32_t dtype;        /* pa_dtype of q, out and new K/V rows (and of the pools
+                           when kv_dtype is PA_KV_SAME) */
+  int32_t kv_dtype;     /* pa_kv_dtype of the pools */
+  float k_scale;        /* PA_KV_FP8_E4M3: a K element's value is its code's
+                           value times k_scale (finite, > 0); ignored otherwise */
+  float v_scale;        /* the same for V */
 } pa_pool_desc;
 
 /* Library version of this ABI (bumped on incompatible change). */
@@ -84,7 +97,7 @@ const char* pa_status_string(int32_t status);
  * For sequence i, q head h and its kv head g = h / G, with ctx = context_lens[i]
  * tokens at positions 0..ctx-1 found through block_tables[i]:
  *     out[i][h] = sum_t softmax_t(scale * <q[i][h], K[t][g]>) * V[t][g]
- * accumulated in fp32 and rounded once (round to nearest even) to the pool
+ * accumulated in fp32 and rounded once (round to nearest even) to the
  * dtype.  context_lens count every token the query attends to, including the
  * token being decoded, whose K/V must already be written (pa_reshape_and_cache
  * before pa_decode on the same stream).
@@ -100,7 +113,7 @@ const char* pa_status_string(int32_t status);
  *    evenly among a fixed set of waves (one 4-wave workgroup per CU); a
  *    (sequence, kv head) inside one wave's share is written directly.
  *
- *   q             device, [num_seqs][num_q_heads][head_dim], pool dtype
+ *   q             device, [num_seqs][num_q_heads][head_dim], dtype
  *   k_pool/v_pool device, pool layout above
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past
  *                 ceil(ctx / BS) are never read (any padding value is fine)
@@ -110,13 +123,19 @@ const char* pa_status_string(int32_t status);
  *   max_context_len  host bound >= every context_lens[i]; sizes the grid
  *                 without a device->host copy
  *   scale         softmax scale (typically 1 / sqrt(head_dim))
- *   out           device, [num_seqs][num_q_heads][head_dim], pool dtype
+ *   out           device, [num_seqs][num_q_heads][head_dim], dtype
  *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
  *                 aligned; may be NULL when that size is 0.  Scratch only:
  *                 its contents on entry do not matter.  Layout is private.
  *   partition_tokens  multiple of 16 and of block_size, in [16, 4096];
  *                 0 selects the default (512).  Sizes the grid split's
  *                 partitions; validated but unused by the stream split.
+ *   sliding_window  0: none.  W > 0: the query (position ctx - 1) attends only
+ *                 positions max(0, ctx - W) .. ctx - 1 (its own and the W - 1
+ *                 before it); table entries of blocks wholly below that are
+ *                 never read (they may be PA_NO_BLOCK).  < 0: PA_ERR_ARG.
+ * 8-bit pools: K and V elements are dequantised as code value * k_scale /
+ * v_scale (k_scale folded into the score scale, v_scale into the output).
  * Block ids outside [0, num_blocks) are skipped (those tokens do not take
  * part); the output is then unspecified but no access leaves the pool.
  * ------------------------------------------------------------------------ */
@@ -131,9 +150,9 @@ size_t pa_decode_workspace_bytes(const pa_pool_desc* pool, int32_t num_seqs,
 pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     const pa_pool_desc* pool, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                    int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
-                    void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                    void* hip_stream);
+                    int32_t num_q_heads, int32_t max_context_len, float scale,
+                    int32_t sliding_window, void* out, void* workspace,
+                    size_t workspace_bytes, int32_t partition_tokens, void* hip_stream);
 
 /* The two passes of pa_decode, callable one at a time (same arguments, same
  * path setting, same stream; pa_decode == pa_decode_partition then
@@ -144,15 +163,16 @@ pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_p
                               const pa_pool_desc* pool, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
                               int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                              float scale, void* out, void* workspace, size_t workspace_bytes,
-                              int32_t partition_tokens, void* hip_stream);
+                              float scale, int32_t sliding_window, void* out, void* workspace,
+                              size_t workspace_bytes, int32_t partition_tokens,
+                              void* hip_stream);
 
 pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool,
                            const pa_pool_desc* pool, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                           float scale, void* out, void* workspace, size_t workspace_bytes,
-                           int32_t partition_tokens, void* hip_stream);
+                           float scale, int32_t sliding_window, void* out, void* workspace,
+                           size_t workspace_bytes, int32_t partition_tokens, void* hip_stream);
 
 /* Decode kernel family.  PA_PATH_AUTO: the matrix-core kernel for 16-bit
  * pools with head_dim 128 and G = num_q_heads / num_kv_heads in [2, 16], the
@@ -184,24 +204,26 @@ int32_t pa_set_decode_path(int32_t path);
  * with ctx = context_lens[i] (the length after the chunk).  Row a + j, q
  * head h, kv head g = h / G attends to positions 0 .. ctx - n + j:
  *     out[a+j][h] = sum_{p <= ctx-n+j} softmax_p(scale * <q[a+j][h], K[p][g]>) * V[p][g]
- * in fp32, rounded once (RNE) to the pool dtype.  A row whose position is
- * negative (ctx < n) is all zeros.
+ * in fp32, rounded once (RNE) to the dtype.  A row whose position is
+ * negative (ctx < n) is all zeros.  With sliding_window W > 0 a row at
+ * position p attends only positions max(0, p - W + 1) .. p.
  *
- *   q, out        device [num_tokens][num_q_heads][head_dim], pool dtype
+ *   q, out        device [num_tokens][num_q_heads][head_dim], dtype
  *   query_start   device int32 [num_seqs + 1], non-decreasing; a sequence
  *                 whose rows fall outside [0, num_tokens) is skipped
  *   context_lens  device int32 [num_seqs], clamped like pa_decode's
  *   max_query_len host bound >= every n; rows past it are not computed
  *   max_context_len, block_tables, max_blocks_per_seq, scale: as pa_decode
- * Supported: f16/bf16 pools, head_dim 128, G in {1, 2, 4, 8, 16}
- * (PA_ERR_SHAPE otherwise).  No workspace; one kernel launch.
+ * Supported: f16/bf16 dtype (16-bit or 8-bit pools), head_dim 128, G in
+ * {1, 2, 4, 8, 16} (PA_ERR_SHAPE otherwise).  No workspace; one kernel
+ * launch.
  * ------------------------------------------------------------------------ */
 pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                      const pa_pool_desc* pool, const int32_t* block_tables,
                      int32_t max_blocks_per_seq, const int32_t* query_start,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
                      int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
-                     float scale, void* out, void* hip_stream);
+                     float scale, int32_t sliding_window, void* out, void* hip_stream);
 
 /* ------------------------------------------------------------------------
  * Cache write: decode appends each new token's K/V to the cache (page
@@ -209,9 +231,12 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
  * the slot its block table gives.  For every t with slot = slot_mapping[t]
  * >= 0 and every kv head h:
  *     k_pool[slot / BS][h][slot % BS][:] = k[t][h][:]   (same for v)
- * Bit-exact copy.  Slots < 0 are skipped; slots >= num_blocks * BS are
- * skipped too (never written).  Two tokens with the same slot race.
- *   k, v          device, [num_tokens][num_kv_heads][head_dim], pool dtype
+ * Bit-exact copy into a pool of the dtype.  Into an 8-bit pool each element
+ * x is stored as the E4M3 code nearest to clamp(x * (1 / k_scale), -448,
+ * 448) (products and the reciprocal in fp32, ties to the even code; NaN
+ * stays NaN); v with v_scale.  Slots < 0 are skipped; slots >= num_blocks *
+ * BS are skipped too (never written).  Two tokens with the same slot race.
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim], dtype
  *   slot_mapping  device int64 [num_tokens]
  * ------------------------------------------------------------------------ */
 pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,

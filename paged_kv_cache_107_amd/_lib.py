@@ -18,9 +18,13 @@ PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA, PA_PATH_MFMA_GRID = 0, 1, 2, 3
 
 
+PA_KV_SAME, PA_KV_FP8_E4M3 = 0, 1
+
+
 class pa_pool_desc(C.Structure):
     _fields_ = [("num_blocks", C.c_int32), ("block_size", C.c_int32),
-                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32)]
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32),
+                ("kv_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float)]
 
 
 _vp, _i32, _i64, _f32, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
@@ -38,8 +42,8 @@ class pa_swap_stats(C.Structure):
                 ("blocks_in", C.c_int64), ("swapped_seqs", C.c_int32), ("host_free", C.c_int32)]
 
 
-_DECODE_ARGS = [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _sz,
-                _i32, _vp]
+_DECODE_ARGS = [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp,
+                _sz, _i32, _vp]
 
 SIGNATURES = {
     "pa_abi_version": (_i32, []),
@@ -50,7 +54,7 @@ SIGNATURES = {
     "pa_decode_partition": (_i32, _DECODE_ARGS),
     "pa_decode_reduce": (_i32, _DECODE_ARGS),
     "pa_prefill": (_i32, [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                          _f32, _vp, _vp]),
+                          _f32, _i32, _vp, _vp]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _desc, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _desc, _vp, _i32, _vp]),
     "pa_alloc_create": (_i32, [_i32, _i32, _pi32, C.POINTER(_vp)]),

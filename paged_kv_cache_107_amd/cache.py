@@ -22,7 +22,7 @@ import torch
 
 from .allocator import PaAllocator
 from ._lib import PA_SWAP_IN, PA_SWAP_OUT
-from .ops import (alloc_workspace, pa_copy_blocks, pa_decode, pa_reshape_and_cache,
+from .ops import (FP8, alloc_workspace, pa_copy_blocks, pa_decode, pa_reshape_and_cache,
                   pa_swap_blocks)
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -43,18 +43,29 @@ class StepPlan:
 class PagedKVCache:
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  dtype: str, initial_free_order: Optional[Sequence[int]] = None,
-                 device="cuda", pools: Optional[tuple] = None):
+                 device="cuda", pools: Optional[tuple] = None, kv_dtype: Optional[str] = None,
+                 kv_scales=(1.0, 1.0), sliding_window: int = 0):
+        """dtype: activations (q, out, new K/V); kv_dtype "fp8_e4m3" stores
+        the pools as E4M3 codes with per-pool kv_scales = (k_scale, v_scale);
+        sliding_window: positions each query attends (0 = all)."""
         self.block_size = block_size
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
         self.dtype = dtype
+        self.kv_dtype = kv_dtype or dtype
+        self.kv_scales = tuple(float(x) for x in kv_scales)
+        self.sliding_window = int(sliding_window)
         self.device = torch.device(device)
         self.alloc = PaAllocator(num_blocks, block_size, initial_free_order)
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         if pools is None:
-            tdt = TORCH_DTYPES[dtype]
-            pools = (torch.zeros(shape, dtype=tdt, device=self.device),
-                     torch.zeros(shape, dtype=tdt, device=self.device))
+            if self.kv_dtype == "fp8_e4m3":  # zero codes, allocated as bytes
+                pools = tuple(torch.zeros(shape, dtype=torch.uint8, device=self.device).view(FP8)
+                              for _ in range(2))
+            else:
+                tdt = TORCH_DTYPES[dtype]
+                pools = (torch.zeros(shape, dtype=tdt, device=self.device),
+                         torch.zeros(shape, dtype=tdt, device=self.device))
         self.k_pool, self.v_pool = pools
         if tuple(self.k_pool.shape) != shape or tuple(self.v_pool.shape) != shape:
             raise ValueError(f"pools must be {shape}")
@@ -134,7 +145,7 @@ class PagedKVCache:
         if pairs is not None and pairs.shape[0] > 0:
             pa_copy_blocks(self.k_pool, self.v_pool, pairs, stream)
         if slots.shape[0] > 0:
-            pa_reshape_and_cache(k, v, slots, self.k_pool, self.v_pool, stream)
+            pa_reshape_and_cache(k, v, slots, self.k_pool, self.v_pool, stream, self.kv_scales)
 
     def write_host(self, k: torch.Tensor, v: torch.Tensor, slots: np.ndarray, pairs) -> None:
         pr = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
@@ -161,7 +172,8 @@ class PagedKVCache:
     def decode(self, plan: StepPlan, q: torch.Tensor, scale: float, out: torch.Tensor,
                workspace: Optional[torch.Tensor], partition_tokens: int = 0, stream=None):
         return pa_decode(q, self.k_pool, self.v_pool, plan.tables, plan.lens, scale, out,
-                         workspace, plan.max_context_len, partition_tokens, stream)
+                         workspace, plan.max_context_len, partition_tokens, stream,
+                         self.sliding_window, self.kv_scales)
 
     def run(self, plan: StepPlan, k_new, v_new, q, scale, out, workspace,
             partition_tokens: int = 0, stream=None):

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 constexpr int32_t kDefaultPartition = 512;
 constexpr int32_t kMaxPartition = 4096;
 constexpr int32_t kMaxGridYZ = 65535;
@@ -32,6 +32,14 @@ pa_status check_pool(const pa_pool_desc* pool) {
   if (!pool) return PA_ERR_ARG;
   if (pool->dtype != PA_F32 && pool->dtype != PA_F16 && pool->dtype != PA_BF16)
     return PA_ERR_DTYPE;
+  if (pool->kv_dtype != PA_KV_SAME && pool->kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_DTYPE;
+  if (pool->kv_dtype == PA_KV_FP8_E4M3) {
+    if (pool->dtype == PA_F32) return PA_ERR_DTYPE;
+    if (pool->head_dim != 128) return PA_ERR_SHAPE;
+    if (!std::isfinite(pool->k_scale) || !std::isfinite(pool->v_scale) || !(pool->k_scale > 0.f) ||
+        !(pool->v_scale > 0.f))
+      return PA_ERR_ARG;
+  }
   if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0) return PA_ERR_ARG;
   if (pool->block_size != 16 && pool->block_size != 32) return PA_ERR_SHAPE;
   if (pool->head_dim != 64 && pool->head_dim != 128) return PA_ERR_SHAPE;
@@ -72,16 +80,28 @@ size_t stream_ws_bytes(int32_t b, int32_t hkv, int32_t g, int32_t d) {
 struct Prepared {
   pa::DecodeArgs args;
   int32_t dtype;
+  pa::KvType kv;
   int32_t head_dim;
   pa::DecodeKernel kernel;
 };
 
+inline pa::KvType kv_type(const pa_pool_desc* pool) {
+  return pool->kv_dtype == PA_KV_FP8_E4M3 ? pa::KvType::kFp8 : pa::KvType::kSame;
+}
+
 // The kernel pa_decode runs for this shape under the current path setting.
+// 8-bit pools run on the matrix-core kernels only (any G up to 16).
 pa_status choose_kernel(const pa_pool_desc* pool, int32_t group, int32_t num_seqs,
                         int32_t max_context_len, pa::DecodeKernel* k) {
   const bool mfma = pa::mfma_supports(pool->dtype, pool->head_dim, group);
   const bool stream = mfma && pa::stream_supports(num_seqs, pool->num_kv_heads, max_context_len);
   const int32_t path = g_decode_path.load();
+  if (kv_type(pool) == pa::KvType::kFp8) {
+    if (!mfma || path == PA_PATH_VALU) return PA_ERR_SHAPE;
+    *k = stream && path != PA_PATH_MFMA_GRID ? pa::DecodeKernel::kMfmaStream
+                                             : pa::DecodeKernel::kMfmaGrid;
+    return PA_OK;
+  }
   if (path == PA_PATH_VALU) {
     if (!pa::valu_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
     *k = pa::DecodeKernel::kValu;
@@ -101,9 +121,9 @@ pa_status choose_kernel(const pa_pool_desc* pool, int32_t group, int32_t num_seq
 pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
                          const pa_pool_desc* pool, const int32_t* block_tables,
                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                         int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
-                         void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                         Prepared* pr) {
+                         int32_t num_q_heads, int32_t max_context_len, float scale,
+                         int32_t sliding_window, void* out, void* workspace,
+                         size_t workspace_bytes, int32_t partition_tokens, Prepared* pr) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || max_blocks_per_seq < 0 ||
@@ -112,7 +132,7 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
   if (max_parts_of(max_context_len, partition_tokens ? partition_tokens : kDefaultPartition) >
       kMaxGridYZ)
     return PA_ERR_ARG;
-  if (!std::isfinite(scale)) return PA_ERR_ARG;
+  if (!std::isfinite(scale) || sliding_window < 0) return PA_ERR_ARG;
   if (pool->num_kv_heads > kMaxGridYZ || num_q_heads > kMaxGridYZ) return PA_ERR_ARG;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
   const int32_t group = num_q_heads / pool->num_kv_heads;
@@ -171,8 +191,12 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
   a.max_ctx = max_context_len;
   a.part_tokens = partition_tokens;
   a.max_parts = max_parts;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  const bool fp8 = kv_type(pool) == pa::KvType::kFp8;
+  a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? pool->k_scale : 1.f);
+  a.window = sliding_window;
+  a.v_scale = fp8 ? pool->v_scale : 1.f;
   pr->dtype = pool->dtype;
+  pr->kv = kv_type(pool);
   pr->head_dim = pool->head_dim;
   pr->kernel = kernel;
   return PA_OK;
@@ -257,14 +281,16 @@ pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_p
                               const pa_pool_desc* pool, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
                               int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                              float scale, void* out, void* workspace, size_t workspace_bytes,
-                              int32_t partition_tokens, void* hip_stream) {
+                              float scale, int32_t sliding_window, void* out, void* workspace,
+                              size_t workspace_bytes, int32_t partition_tokens,
+                              void* hip_stream) {
   Prepared pr;
   pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
-                                context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
-                                workspace, workspace_bytes, partition_tokens, &pr);
+                                context_lens, num_seqs, num_q_heads, max_context_len, scale,
+                                sliding_window, out, workspace, workspace_bytes, partition_tokens,
+                                &pr);
   if (st != PA_OK || pr.args.num_seqs == 0) return st;
-  return pa::launch_decode_partition(pr.args, pr.dtype, pr.head_dim, pr.kernel,
+  return pa::launch_decode_partition(pr.args, pr.dtype, pr.kv, pr.head_dim, pr.kernel,
                                      static_cast<hipStream_t>(hip_stream));
 }
 
@@ -272,12 +298,13 @@ pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool
                            const pa_pool_desc* pool, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                           float scale, void* out, void* workspace, size_t workspace_bytes,
-                           int32_t partition_tokens, void* hip_stream) {
+                           float scale, int32_t sliding_window, void* out, void* workspace,
+                           size_t workspace_bytes, int32_t partition_tokens, void* hip_stream) {
   Prepared pr;
   pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
-                                context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
-                                workspace, workspace_bytes, partition_tokens, &pr);
+                                context_lens, num_seqs, num_q_heads, max_context_len, scale,
+                                sliding_window, out, workspace, workspace_bytes, partition_tokens,
+                                &pr);
   if (st != PA_OK || pr.args.num_seqs == 0 || !needs_reduce(pr)) return st;
   return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim, pr.kernel,
                                   static_cast<hipStream_t>(hip_stream));
@@ -286,16 +313,17 @@ pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool
 pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     const pa_pool_desc* pool, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                    int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
-                    void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                    void* hip_stream) {
+                    int32_t num_q_heads, int32_t max_context_len, float scale,
+                    int32_t sliding_window, void* out, void* workspace,
+                    size_t workspace_bytes, int32_t partition_tokens, void* hip_stream) {
   Prepared pr;
   pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
-                                context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
-                                workspace, workspace_bytes, partition_tokens, &pr);
+                                context_lens, num_seqs, num_q_heads, max_context_len, scale,
+                                sliding_window, out, workspace, workspace_bytes, partition_tokens,
+                                &pr);
   if (st != PA_OK || pr.args.num_seqs == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  st = pa::launch_decode_partition(pr.args, pr.dtype, pr.head_dim, pr.kernel, s);
+  st = pa::launch_decode_partition(pr.args, pr.dtype, pr.kv, pr.head_dim, pr.kernel, s);
   if (st != PA_OK || !needs_reduce(pr)) return st;
   return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim, pr.kernel, s);
 }
@@ -305,13 +333,13 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                      int32_t max_blocks_per_seq, const int32_t* query_start,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
                      int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
-                     float scale, void* out, void* hip_stream) {
+                     float scale, int32_t sliding_window, void* out, void* hip_stream) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_tokens < 0 || num_q_heads <= 0 ||
       max_blocks_per_seq < 0 || max_query_len < 0 || max_context_len < 0)
     return PA_ERR_ARG;
-  if (!std::isfinite(scale)) return PA_ERR_ARG;
+  if (!std::isfinite(scale) || sliding_window < 0) return PA_ERR_ARG;
   if (pool->num_kv_heads > kMaxGridYZ || num_q_heads > kMaxGridYZ) return PA_ERR_ARG;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
   const int32_t group = num_q_heads / pool->num_kv_heads;
@@ -343,8 +371,11 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.max_blocks = max_blocks_per_seq;
   a.max_ctx = max_context_len;
   a.max_query = max_query_len;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  return pa::launch_prefill(a, pool->dtype, static_cast<hipStream_t>(hip_stream));
+  const bool fp8 = kv_type(pool) == pa::KvType::kFp8;
+  a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? pool->k_scale : 1.f);
+  a.window = sliding_window;
+  a.v_scale = fp8 ? pool->v_scale : 1.f;
+  return pa::launch_prefill(a, pool->dtype, kv_type(pool), static_cast<hipStream_t>(hip_stream));
 }
 
 pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
@@ -388,7 +419,7 @@ pa_status pa_swap_blocks(void* k_pool, void* v_pool, void* k_host, void* v_host,
       (reinterpret_cast<uintptr_t>(pairs) & 3u))
     return PA_ERR_ARG;
   const int64_t block_bytes = (int64_t)pool->num_kv_heads * pool->block_size * pool->head_dim *
-                              (pool->dtype == PA_F32 ? 4 : 2);
+                              pa::pool_elem_bytes(*pool);
   void* k_dev = nullptr;
   void* v_dev = nullptr;
   st = mapped_host_range(k_host, (int64_t)num_host_blocks * block_bytes, &k_dev);

@@ -6,7 +6,9 @@
 //    block table gives (physical block slot / BS, offset slot % BS: "放下账簿，
 //    打开源码", section "PagedAttention：虚实分离，按需取用").  One thread per
 //    16-byte chunk of a (token, kv head) row; consecutive threads read
-//    consecutive input bytes and write one contiguous pool row.
+//    consecutive input bytes and write one contiguous pool row.  Into an
+//    8-bit pool each 16-byte input chunk (8 values) becomes 8 E4M3 codes:
+//    x * (1 / scale) in fp32, clamped to +-448, rounded to nearest even.
 //  * copy_blocks: a writer's private copy of a shared block before its first
 //    write ("Lazy Allocation 与 Copy-on-Write ...", section 4.4).  A block is
 //    Hkv x BS rows, contiguous in the pool; each workgroup streams a slice of
@@ -19,11 +21,10 @@
 #include <hip/hip_runtime.h>
 
 #include "pa.h"
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const u32x4* __restrict__ k, const u32x4* __restrict__ v, const int64_t* __restrict__ slots,
@@ -40,6 +41,37 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * chunks_per_row + cc;
   k_pool[dst] = k[idx];
   v_pool[dst] = v[idx];
+}
+
+// 8 values of type E (one 16-byte chunk) -> 8 E4M3 codes of x * inv.
+template <class E>
+__device__ __forceinline__ uint2 quantize8(const u32x4& x, float inv) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = lo16(E{}, x[j]) * inv, b = hi16(E{}, x[j]) * inv;
+    w[j >> 1] = to_e4m3_pair(a, b, w[j >> 1], (j & 1) != 0);
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+template <class E>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, const int64_t* __restrict__ slots,
+    int64_t total_chunks, int32_t chunks_per_token, int32_t chunks_per_row, int32_t num_kv_heads,
+    int32_t block_size, int64_t num_slots, uint2* __restrict__ k_pool, uint2* __restrict__ v_pool,
+    float k_inv, float v_inv) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total_chunks) return;
+  const int64_t t = idx / chunks_per_token;
+  const int32_t c = (int32_t)(idx - t * chunks_per_token);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int32_t h = c / chunks_per_row, cc = c - h * chunks_per_row;
+  const int64_t blk = slot / block_size, off = slot - blk * block_size;
+  const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * chunks_per_row + cc;
+  k_pool[dst] = quantize8<E>(k[idx], k_inv);
+  v_pool[dst] = quantize8<E>(v[idx], v_inv);
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_pool,
@@ -74,6 +106,20 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(
 
 static int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
 
+template <class E>
+pa_status launch_fp8_write(const void* k, const void* v, const int64_t* slots, int64_t total,
+                           int32_t chunks_per_token, int32_t chunks_per_row, void* k_pool,
+                           void* v_pool, const pa_pool_desc& pool, hipStream_t st) {
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return PA_ERR_ARG;
+  hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<E>), dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots, total,
+                     chunks_per_token, chunks_per_row, pool.num_kv_heads, pool.block_size,
+                     (int64_t)pool.num_blocks * pool.block_size, static_cast<uint2*>(k_pool),
+                     static_cast<uint2*>(v_pool), 1.0f / pool.k_scale, 1.0f / pool.v_scale);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
                                    int32_t num_tokens, void* k_pool, void* v_pool,
                                    const pa_pool_desc& pool, hipStream_t st) {
@@ -81,6 +127,15 @@ pa_status launch_reshape_and_cache(const void* k, const void* v, const int64_t* 
   const int32_t chunks_per_row = pool.head_dim * elem_bytes(pool.dtype) / 16;
   const int32_t chunks_per_token = chunks_per_row * pool.num_kv_heads;
   const int64_t total = (int64_t)num_tokens * chunks_per_token;
+  if (pool.kv_dtype == PA_KV_FP8_E4M3) {
+    if (pool.dtype == PA_BF16)
+      return launch_fp8_write<BF16>(k, v, slots, total, chunks_per_token, chunks_per_row, k_pool,
+                                    v_pool, pool, st);
+    if (pool.dtype == PA_F16)
+      return launch_fp8_write<F16>(k, v, slots, total, chunks_per_token, chunks_per_row, k_pool,
+                                   v_pool, pool, st);
+    return PA_ERR_DTYPE;
+  }
   const int64_t blocks = (total + 255) / 256;
   if (blocks > 0x7FFFFFFF) return PA_ERR_ARG;
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
@@ -95,7 +150,7 @@ pa_status launch_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc& poo
                              const int32_t* pairs, int32_t num_pairs, hipStream_t st) {
   if (num_pairs == 0) return PA_OK;
   const int64_t chunks_per_block = (int64_t)pool.num_kv_heads * pool.block_size * pool.head_dim *
-                                   elem_bytes(pool.dtype) / 16;
+                                   pool_elem_bytes(pool) / 16;
   const int64_t slices = (chunks_per_block + 255) / 256;
   const unsigned gx = (unsigned)(slices < 64 ? slices : 64);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, (unsigned)num_pairs, 2), dim3(256), 0, st,
@@ -109,7 +164,7 @@ pa_status launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k, 
                              const int32_t* pairs, int32_t num_pairs, hipStream_t st) {
   if (num_pairs == 0) return PA_OK;
   const int64_t chunks_per_block = (int64_t)pool.num_kv_heads * pool.block_size * pool.head_dim *
-                                   elem_bytes(pool.dtype) / 16;
+                                   pool_elem_bytes(pool) / 16;
   const int64_t slices = (chunks_per_block + 255) / 256;
   const unsigned gx = (unsigned)(slices < 64 ? slices : 64);
   hipLaunchKernelGGL(swap_blocks_kernel, dim3(gx, (unsigned)num_pairs, 2), dim3(256), 0, st,

@@ -79,8 +79,16 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int i) {
   return ctx;
 }
 
+// First position the query (at ctx - 1) attends: the sliding window's
+// start, 0 without one.  Tile walks start at first & ~15 and mask below it.
+__device__ __forceinline__ int first_pos(const DecodeArgs& a, int ctx) {
+  return a.window > 0 ? max(ctx - a.window, 0) : 0;
+}
+
+// Partitions of the attended range [first & ~15, ctx).
 __device__ __forceinline__ int num_parts(const DecodeArgs& a, int ctx) {
-  return ctx > 0 ? (ctx + a.part_tokens - 1) / a.part_tokens : 1;
+  return ctx > 0 ? (ctx - (first_pos(a, ctx) & ~(kTile - 1)) + a.part_tokens - 1) / a.part_tokens
+                 : 1;
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -128,7 +136,7 @@ __device__ void combine_store(const DecodeArgs& a, const float* smem, int group,
     }
     const size_t row = (size_t)i * a.num_q_heads + (size_t)g * group + h;
     if (n_parts == 1) {
-      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const float inv = L > 0.f ? a.v_scale / L : 0.f;
       using S = typename E::storage;
       S* dst = reinterpret_cast<S*>(a.out) + row * D + d;
       if constexpr (E::bytes == 4) {
@@ -163,9 +171,11 @@ __device__ void store_zero_rows(const DecodeArgs& a, int group, int i, int g) {
 //      O^T_e out:    lane holds O[head c16][32 g4 + 8 r + e], r = 0..3
 // so a lane keeps 32 output values of its own head, and the softmax rescale
 // needs no cross-lane traffic.
-template <class E>
+template <class E, KvType KV>
 __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) {
   constexpr int D = 128;
+  using Tile = KvTile<E, KV>;
+  using P = typename Tile::P;
   extern __shared__ float smem[];
   const int g = blockIdx.x, i = blockIdx.y;
   const int p = PA_PART_DESC ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
@@ -179,7 +189,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
   }
   const int lane = threadIdx.x % kWave, w = wave_id();
   const int c16 = lane & 15, g4 = lane >> 4;
-  const int t0 = p * a.part_tokens;
+  const int first = first_pos(a, ctx);
+  const int t0 = (first & ~(kTile - 1)) + p * a.part_tokens;
   const int ntok = min(a.part_tokens, ctx - t0);
   const int ntiles = (ntok + kTile - 1) / kTile;
   const int bs_mask = (1 << a.log2_bs) - 1;
@@ -188,15 +199,16 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
   u32x4 qv[4];
   {
     const S* qrow = reinterpret_cast<const S*>(a.q) +
-                    ((size_t)i * a.num_q_heads + (size_t)g * G + c16) * D + 8 * g4;
+                    ((size_t)i * a.num_q_heads + (size_t)g * G + c16) * D;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qv[s] = c16 < G ? load16(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < 4; ++s)
+      qv[s] = c16 < G ? load16(qrow + Tile::q_elem(s, g4)) : u32x4{0, 0, 0, 0};
   }
   const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
   const size_t head_stride = (size_t)D << a.log2_bs;
   const size_t block_stride = head_stride * a.num_kv_heads;
-  const S* kbase0 = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride;
-  const S* vbase0 = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride;
+  const P* kbase0 = reinterpret_cast<const P*>(a.k_pool) + (size_t)g * head_stride;
+  const P* vbase0 = reinterpret_cast<const P*>(a.v_pool) + (size_t)g * head_stride;
 
   // This wave's tiles are w, w + 4, w + 8, ...; tile k of the wave is
   // partition tile w + 4k.  Lane k holds the physical block of the wave's
@@ -206,26 +218,19 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
   const int ids =
       lane < my_n ? table[min((t0 + kTile * (w + kWaves * lane)) >> a.log2_bs, a.max_blocks - 1)]
                   : -1;
-  const uint32_t k_lane_off = (uint32_t)(c16 * D + 8 * g4) * 2u;       // bytes
-  const uint32_t v_lane_off = (uint32_t)((4 * g4) * D + 8 * c16) * 2u;
 
-  // Issues the 8 loads of the wave's tile k through per-tile buffer
+  // Issues the loads of the wave's tile k through per-tile buffer
   // descriptors.  A tile past the wave's last (or with a bad block id) gets
   // an empty descriptor: its loads return zeros without touching memory, so
-  // every ring slot always has exactly 8 loads in flight and the wait counts
+  // every ring slot always has the same loads in flight and the wait counts
   // stay static.  Returns whether the tile holds data.
-  auto issue = [&](int k, u32x4 (&kr)[4], u32x4 (&vr)[4]) -> bool {
+  auto issue = [&](int k, Tile& t) -> bool {
     const int blk = k < my_n ? __builtin_amdgcn_readlane(ids, k) : -1;
     const bool ok = (unsigned)blk < (unsigned)a.num_blocks;
     const int tok = t0 + kTile * (w + kWaves * k);
     const size_t off = ok ? (size_t)blk * block_stride + (size_t)(tok & bs_mask) * D : 0;
-    const uint32_t bytes = ok ? kTile * D * 2u : 0u;
-    const rsrc_t kr_rs = make_rsrc(kbase0 + off, bytes);
-    const rsrc_t vr_rs = make_rsrc(vbase0 + off, bytes);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kr[s] = buffer_load16(kr_rs, k_lane_off + 64u * s);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = buffer_load16(vr_rs, v_lane_off + 256u * r);
+    const uint32_t bytes = ok ? Tile::kBytes : 0u;
+    t.load(make_rsrc(kbase0 + off, bytes), make_rsrc(vbase0 + off, bytes), c16, g4);
     return ok;
   };
 
@@ -242,20 +247,27 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
   // sum p v / sum p, and p <= 2^kRescaleSlack stays well inside the 16-bit
   // range of the P operand.  The check is lane-local plus one wave vote, so
   // the common case needs no cross-lane traffic and no accumulator rescale.
-  auto compute = [&](int k, u32x4 (&kc)[4], u32x4 (&vc)[4]) {
+  // Rows before the window's first position or past the sequence are masked
+  // (every tile keeps at least one attended row).
+  auto compute = [&](int k, const Tile& t) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) s = Mfma<E>::qk(kc[t], qv[t], s);
+    for (int st = 0; st < 4; ++st) s = Mfma<E>::qk(t.k_op(st), qv[st], s);
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[r] = s[r] * a.scale_log2;
-    const int valid = ntok - kTile * (w + kWaves * k);
-    if (valid < kTile) {
+    u32x4 vc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vc[r] = t.v_row(r);
+    const int tok = t0 + kTile * (w + kWaves * k);
+    const int valid = ntok - kTile * (w + kWaves * k), low = first - tok;
+    if (valid < kTile || low > 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (4 * g4 + r >= valid) {
+        const int e = 4 * g4 + r;
+        if (e >= valid || e < low) {
           sv[r] = neg_inf();
-          vc[r] = u32x4{0, 0, 0, 0};  // slots past the sequence may hold anything
+          vc[r] = u32x4{0, 0, 0, 0};  // slots outside the range may hold anything
         }
       }
     }
@@ -292,15 +304,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
 
   // Register ring of kPrefetch tiles: while one tile is computed the loads
   // of the next kPrefetch - 1 are in flight.
-  u32x4 kb[kPrefetch][4], vb[kPrefetch][4];
+  Tile tb[kPrefetch];
   bool okb[kPrefetch];
 #pragma unroll
-  for (int s = 0; s < kPrefetch; ++s) okb[s] = issue(s, kb[s], vb[s]);
+  for (int s = 0; s < kPrefetch; ++s) okb[s] = issue(s, tb[s]);
   for (int base = 0; base < my_n; base += kPrefetch) {
 #pragma unroll
     for (int s = 0; s < kPrefetch; ++s) {
-      if (okb[s]) compute(base + s, kb[s], vb[s]);
-      okb[s] = issue(base + s + kPrefetch, kb[s], vb[s]);
+      if (okb[s]) compute(base + s, tb[s]);
+      okb[s] = issue(base + s + kPrefetch, tb[s]);
     }
   }
 
@@ -352,14 +364,21 @@ constexpr int kXcds = 8;           // accelerator dies, each with its own L2
 // maxima (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 constexpr int kVmcnt0 = 0x0F70;
 
-// tb[i] = sum over j < i of ceil(ctx[j] / 16) (tile offset of sequence i
-// within a kv head's run), tb[n] = total.  Block-wide; ends with a barrier.
-__device__ void scan_tiles(const int* ctx, int* tb, int n, int* tmp) {
+// Tiles of a sequence of ctx tokens whose first attended position is
+// `first`: the 16-token tiles from first & ~15 to ctx (none when ctx = 0).
+__device__ __forceinline__ int seq_tiles(int ctx, int first) {
+  return ctx > 0 ? ceil_div(ctx, kTile) - (first >> 4) : 0;
+}
+
+// tb[i] = sum over j < i of seq_tiles(ctx[j], first[j]) (tile offset of
+// sequence i within a kv head's run), tb[n] = total.  Block-wide; ends with a
+// barrier.
+__device__ void scan_tiles(const int* ctx, const int* first, int* tb, int n, int* tmp) {
   const int t = threadIdx.x;
   const int per = (n + kThreads - 1) / kThreads;
   const int lo = min(n, t * per), hi = min(n, lo + per);
   int sum = 0;
-  for (int k = lo; k < hi; ++k) sum += ceil_div(ctx[k], kTile);
+  for (int k = lo; k < hi; ++k) sum += seq_tiles(ctx[k], first[k]);
   tmp[t] = sum;
   __syncthreads();
   for (int off = 1; off < kThreads; off <<= 1) {
@@ -371,7 +390,7 @@ __device__ void scan_tiles(const int* ctx, int* tb, int n, int* tmp) {
   int run = t > 0 ? tmp[t - 1] : 0;
   for (int k = lo; k < hi; ++k) {
     tb[k] = run;
-    run += ceil_div(ctx[k], kTile);
+    run += seq_tiles(ctx[k], first[k]);
   }
   if (t == kThreads - 1) tb[n] = tmp[t];
   __syncthreads();
@@ -415,20 +434,27 @@ struct StreamSplit {
   }
 };
 
-size_t stream_smem_bytes(int num_seqs) { return (2 * (size_t)num_seqs + 1 + kThreads) * 4; }
+size_t stream_smem_bytes(int num_seqs) { return (3 * (size_t)num_seqs + 1 + kThreads) * 4; }
 
-template <class E>
+template <class E, KvType KV>
 __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeArgs a) {
   constexpr int D = 128;
   using S = typename E::storage;
+  using Tile = KvTile<E, KV>;
+  using P = typename Tile::P;
   extern __shared__ int s_int[];
   const int B = a.num_seqs, Hkv = a.num_kv_heads, G = a.group;
   int* s_ctx = s_int;         // [B] clamped lengths, >= 0
-  int* s_tb = s_ctx + B;      // [B + 1] tile offset of each sequence in a head's run
+  int* s_first = s_ctx + B;   // [B] first attended position (sliding window)
+  int* s_tb = s_first + B;    // [B + 1] tile offset of each sequence in a head's run
   int* s_tmp = s_tb + B + 1;  // [kThreads]
-  for (int i = threadIdx.x; i < B; i += kThreads) s_ctx[i] = max(clamp_ctx(a, i), 0);
+  for (int i = threadIdx.x; i < B; i += kThreads) {
+    const int ctx = max(clamp_ctx(a, i), 0);
+    s_ctx[i] = ctx;
+    s_first[i] = first_pos(a, ctx);
+  }
   __syncthreads();
-  scan_tiles(s_ctx, s_tb, B, s_tmp);
+  scan_tiles(s_ctx, s_first, s_tb, B, s_tmp);
 
   const int lane = threadIdx.x % kWave, w = wave_id();
   const int c16 = lane & 15, g4 = lane >> 4;
@@ -451,11 +477,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   const size_t head_stride = (size_t)D << a.log2_bs;
   const size_t block_stride = head_stride * Hkv;
 
-  // Position in the flat order: kv head g, sequence i, tile t of its n.
+  // Position in the flat order: kv head g, sequence i, tile t of its n; the
+  // sequence's tiles start at tile ts of its positions (sliding window).
   struct Cur {
-    int i, g, t, n;
+    int i, g, t, n, ts;
   };
-  auto tiles_of = [&](int i) { return ceil_div(uni(s_ctx[i]), kTile); };
+  auto tiles_of = [&](int i) { return seq_tiles(uni(s_ctx[i]), uni(s_first[i])); };
+  auto first_tile = [&](int i) { return uni(s_first[i]) >> 4; };
   auto next_seq = [&](int i) {  // next sequence with tiles, B if none
     do {
       ++i;
@@ -471,6 +499,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
       ++c.g;
     }
     c.n = c.g < Hkv ? tiles_of(c.i) : 0;
+    c.ts = c.g < Hkv ? first_tile(c.i) : 0;
   };
   Cur start;
   {
@@ -480,19 +509,20 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
       const int mid = (l + r) >> 1;
       if (uni(s_tb[mid]) <= off) l = mid; else r = mid;
     }
-    start = Cur{l, g, off - uni(s_tb[l]), tiles_of(l)};
+    start = Cur{l, g, off - uni(s_tb[l]), tiles_of(l), first_tile(l)};
   }
 
   // q rows of one pair through a buffer descriptor bounded to its G heads:
-  // lanes with c16 >= G read zeros.  Lane (c16, g4) gets q[head c16][32 s +
-  // 8 g4 .. +7], the B operand layout of the QK product.
-  const uint32_t q_lane_off = (uint32_t)(c16 * D + 8 * g4) * 2u;
+  // lanes with c16 >= G read zeros.  Lane (c16, g4) gets the 8 elements of
+  // q[head c16] that k-step s contracts (Tile::q_elem), the B operand layout
+  // of the QK product.
   auto load_q = [&](const Cur& c, u32x4 (&dst)[4]) {
     const rsrc_t rs = make_rsrc(reinterpret_cast<const S*>(a.q) +
                                     ((size_t)c.i * a.num_q_heads + (size_t)c.g * G) * D,
                                 (uint32_t)(G * D * 2));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dst[s] = buffer_load16(rs, q_lane_off + 64u * s);
+    for (int s = 0; s < 4; ++s)
+      dst[s] = buffer_load16(rs, (uint32_t)(c16 * D + Tile::q_elem(s, g4)) * 2u);
   };
 
   // ---- issue side: the ring's loads, one tile at a time ----
@@ -506,15 +536,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   Cur ic = start;
   int irem = hi - lo;
   auto table_entry = [&](const Cur& c) {
-    return scalar_load(a.block_tables + (size_t)c.i * a.max_blocks + ((c.t * kTile) >> a.log2_bs));
+    return scalar_load(a.block_tables + (size_t)c.i * a.max_blocks +
+                       (((c.t + c.ts) * kTile) >> a.log2_bs));
   };
   int iblk = table_entry(ic);
   u32x4 qn[4];
   bool qn_full = false;
   int qn_i = 0, qn_g = 0;
-  const uint32_t k_lane_off = (uint32_t)(c16 * D + 8 * g4) * 2u;  // bytes
-  const uint32_t v_lane_off = (uint32_t)((4 * g4) * D + 8 * c16) * 2u;
-  auto issue = [&](u32x4 (&kr)[4], u32x4 (&vr)[4]) -> bool {
+  auto issue = [&](Tile& tile) -> bool {
     bool ok = false;
     size_t off = 0;
     if (irem > 0) {
@@ -527,26 +556,22 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
       ok = (unsigned)iblk < (unsigned)a.num_blocks;
       if (ok)
         off = (size_t)iblk * block_stride + (size_t)ic.g * head_stride +
-              (size_t)((ic.t * kTile) & bs_mask) * D;
+              (size_t)(((ic.t + ic.ts) * kTile) & bs_mask) * D;
       if (--irem > 0) {
         advance(ic);
         iblk = table_entry(ic);
       }
     }
-    const uint32_t bytes = ok ? kTile * D * 2u : 0u;
-    const rsrc_t kr_rs = make_rsrc(reinterpret_cast<const S*>(a.k_pool) + off, bytes);
-    const rsrc_t vr_rs = make_rsrc(reinterpret_cast<const S*>(a.v_pool) + off, bytes);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kr[s] = buffer_load16(kr_rs, k_lane_off + 64u * s);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = buffer_load16(vr_rs, v_lane_off + 256u * r);
+    const uint32_t bytes = ok ? Tile::kBytes : 0u;
+    tile.load(make_rsrc(reinterpret_cast<const P*>(a.k_pool) + off, bytes),
+              make_rsrc(reinterpret_cast<const P*>(a.v_pool) + off, bytes), c16, g4);
     return ok;
   };
 
   // ---- compute side ----
   Cur cc = start;
   int crem = hi - lo;
-  int seg_t0 = 0, ctx_c = 0;
+  int seg_t0 = 0, ctx_c = 0, first_c = 0;
   u32x4 qv[4];
   float m = neg_inf(), l = 0.f;
   f32x4 o[8];
@@ -555,6 +580,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   auto begin_segment = [&]() {
     seg_t0 = cc.t;
     ctx_c = uni(s_ctx[cc.i]);
+    first_c = uni(s_first[cc.i]);
     if (qn_full && qn_i == cc.i && qn_g == cc.g) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) qv[s] = qn[s];
@@ -572,19 +598,25 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   };
 
   // One tile, as in decode_partition_mfma (lazy rescale, P rounded to the
-  // 16-bit operand type and summed as rounded).
-  auto compute = [&](u32x4 (&kc)[4], u32x4 (&vc)[4]) {
+  // 16-bit operand type and summed as rounded, rows outside [first, ctx)
+  // masked).
+  auto compute = [&](const Tile& tile) {
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sacc = Mfma<E>::qk(kc[t], qv[t], sacc);
+    for (int t = 0; t < 4; ++t) sacc = Mfma<E>::qk(tile.k_op(t), qv[t], sacc);
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[r] = sacc[r] * a.scale_log2;
-    const int valid = ctx_c - kTile * cc.t;
-    if (valid < kTile) {
+    u32x4 vc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vc[r] = tile.v_row(r);
+    const int tok = kTile * (cc.t + cc.ts);
+    const int valid = ctx_c - tok, low = first_c - tok;
+    if (valid < kTile || low > 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (4 * g4 + r >= valid) {
+        const int e = 4 * g4 + r;
+        if (e >= valid || e < low) {
           sv[r] = neg_inf();
           vc[r] = u32x4{0, 0, 0, 0};
         }
@@ -629,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
     const bool whole = seg_t0 == 0 && cc.t + 1 == cc.n;
     if (c16 >= G) return;
     if (whole) {
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
       S* dst = reinterpret_cast<S*>(a.out) +
                ((size_t)cc.i * a.num_q_heads + (size_t)cc.g * G + c16) * D + 32 * g4;
 #pragma unroll
@@ -653,10 +685,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   };
 
   begin_segment();
-  u32x4 kb[kStreamPrefetch][4], vb[kStreamPrefetch][4];
+  Tile tb[kStreamPrefetch];
   bool okb[kStreamPrefetch];
 #pragma unroll
-  for (int s = 0; s < kStreamPrefetch; ++s) okb[s] = issue(kb[s], vb[s]);
+  for (int s = 0; s < kStreamPrefetch; ++s) okb[s] = issue(tb[s]);
   // Every slot issues on every path (past the range the descriptors are
   // empty) and the loop only exits at the bottom of the unrolled body: all
   // paths then carry the same load sequence, so no path in which some slot
@@ -666,8 +698,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
 #pragma unroll
     for (int s = 0; s < kStreamPrefetch; ++s) {
       const bool live = crem > 0;
-      if (live && okb[s]) compute(kb[s], vb[s]);
-      okb[s] = issue(kb[s], vb[s]);
+      if (live && okb[s]) compute(tb[s]);
+      okb[s] = issue(tb[s]);
       if (live) {
         --crem;
         if (cc.t + 1 == cc.n || crem == 0) {
@@ -718,7 +750,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
   }
   const int lane = threadIdx.x % kWave, w = wave_id();
   const int r0 = lane / LPR, cl = lane % LPR;
-  const int t0 = p * a.part_tokens;
+  const int first = first_pos(a, ctx);
+  const int t0 = (first & ~(kTile - 1)) + p * a.part_tokens;
   const int ntok = min(a.part_tokens, ctx - t0);
   const int ntiles = (ntok + kTile - 1) / kTile;
   const int bs_mask = (1 << a.log2_bs) - 1;
@@ -772,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
     bool okn = false;
     if (j + kWaves < ntiles) okn = load_tile(j + kWaves, kn, vn);
     if (okc) {
-      const int valid = ntok - kTile * j;
+      const int valid = ntok - kTile * j, low = first - (t0 + kTile * j);
       float s[G][LPT];
 #pragma unroll
       for (int k = 0; k < LPT; ++k) {
@@ -787,10 +820,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
           s[h][k] = group_sum<LPR>(part);
         }
       }
-      if (valid < kTile) {
+      if (valid < kTile || low > 0) {
 #pragma unroll
         for (int k = 0; k < LPT; ++k) {
-          if (k * RPL + r0 >= valid) {
+          if (k * RPL + r0 >= valid || k * RPL + r0 < low) {
 #pragma unroll
             for (int h = 0; h < G; ++h) s[h][k] = neg_inf();
             vc[k] = uint4{0, 0, 0, 0};
@@ -864,9 +897,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
 // ..., U at a time, each group with its own running maximum; the groups are
 // merged at the end.  The (m, l) and o loads of a step are independent of
 // each other and of the maximum, so a row costs one round of loads.
-// ok(k): state k exists; ml(k): its (m, l); ov(k): its D outputs.
+// ok(k): state k exists; ml(k): its (m, l); ov(k): its D outputs.  The
+// outputs are scaled by `factor` (an 8-bit pool's v_scale, else 1).
 template <class E, int D, class Ok, class Ml, class Ov>
-__device__ void merge_row(int n, Ok ok, Ml ml, Ov ov, typename E::storage* out) {
+__device__ void merge_row(int n, Ok ok, Ml ml, Ov ov, typename E::storage* out, float factor) {
   constexpr int LPR = D / 8;           // lanes per output vector
   constexpr int GROUPS = kWave / LPR;  // states walked side by side
   constexpr int U = 4;
@@ -916,7 +950,8 @@ __device__ void merge_row(int n, Ok ok, Ml ml, Ov ov, typename E::storage* out) 
   if (grp == 0) {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      out[col + k] = (typename E::storage)float_to_bits(E{}, L > 0.f ? acc[k] / L : 0.f);
+      out[col + k] =
+          (typename E::storage)float_to_bits(E{}, L > 0.f ? acc[k] / L * factor : 0.f);
   }
 }
 
@@ -932,7 +967,7 @@ __global__ __launch_bounds__(kWave) void decode_reduce(DecodeArgs a) {
   merge_row<E, D>(
       n_parts, [](int) { return true; }, [&](int k) { return ml[k]; },
       [&](int k) { return wo + (size_t)k * D; },
-      reinterpret_cast<typename E::storage*>(a.out) + row * D);
+      reinterpret_cast<typename E::storage*>(a.out) + row * D, a.v_scale);
 }
 
 // Stream split: one workgroup per wave rank r of the partition pass.  If r
@@ -958,7 +993,8 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_stream(DecodeArgs a) {
         [&](int k) { return a.ws_ml[(base + k) * G + hh]; },
         [&](int k) { return a.ws_o + ((base + k) * G + hh) * D; },
         reinterpret_cast<typename E::storage*>(a.out) +
-            ((size_t)i * a.num_q_heads + (size_t)g * G + hh) * D);
+            ((size_t)i * a.num_q_heads + (size_t)g * G + hh) * D,
+        a.v_scale);
   }
 }
 
@@ -989,10 +1025,10 @@ pa_status launch_valu_d(const DecodeArgs& a, int head_dim, hipStream_t st) {
   return head_dim == 64 ? launch_valu_g<E, 64>(a, st) : launch_valu_g<E, 128>(a, st);
 }
 
-template <class E>
+template <class E, KvType KV>
 pa_status launch_mfma(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
-  hipLaunchKernelGGL((decode_partition_mfma<E>), grid, dim3(kThreads),
+  hipLaunchKernelGGL((decode_partition_mfma<E, KV>), grid, dim3(kThreads),
                      merge_smem_bytes<128>(a.group), st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -1010,10 +1046,10 @@ int device_cus() {
   return n;
 }
 
-template <class E>
+template <class E, KvType KV>
 pa_status launch_mfma_stream(const DecodeArgs& a, hipStream_t st) {
   if (a.stream_waves <= 0 || a.stream_waves % kWaves != 0) return PA_ERR_ARG;
-  hipLaunchKernelGGL((decode_partition_mfma_stream<E>), dim3(a.stream_waves / kWaves),
+  hipLaunchKernelGGL((decode_partition_mfma_stream<E, KV>), dim3(a.stream_waves / kWaves),
                      dim3(kThreads), stream_smem_bytes(a.num_seqs), st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -1054,18 +1090,26 @@ bool valu_supports(int /*dtype*/, int head_dim, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-pa_status launch_decode_partition(const DecodeArgs& a, int dtype, int head_dim, DecodeKernel k,
-                                  hipStream_t st) {
+pa_status launch_decode_partition(const DecodeArgs& a, int dtype, KvType kv, int head_dim,
+                                  DecodeKernel k, hipStream_t st) {
+  const bool fp8 = kv == KvType::kFp8;
   if (k == DecodeKernel::kMfmaStream) {
-    if (dtype == PA_BF16) return launch_mfma_stream<BF16>(a, st);
-    if (dtype == PA_F16) return launch_mfma_stream<F16>(a, st);
+    if (dtype == PA_BF16)
+      return fp8 ? launch_mfma_stream<BF16, KvType::kFp8>(a, st)
+                 : launch_mfma_stream<BF16, KvType::kSame>(a, st);
+    if (dtype == PA_F16)
+      return fp8 ? launch_mfma_stream<F16, KvType::kFp8>(a, st)
+                 : launch_mfma_stream<F16, KvType::kSame>(a, st);
     return PA_ERR_SHAPE;
   }
   if (k == DecodeKernel::kMfmaGrid) {
-    if (dtype == PA_BF16) return launch_mfma<BF16>(a, st);
-    if (dtype == PA_F16) return launch_mfma<F16>(a, st);
+    if (dtype == PA_BF16)
+      return fp8 ? launch_mfma<BF16, KvType::kFp8>(a, st) : launch_mfma<BF16, KvType::kSame>(a, st);
+    if (dtype == PA_F16)
+      return fp8 ? launch_mfma<F16, KvType::kFp8>(a, st) : launch_mfma<F16, KvType::kSame>(a, st);
     return PA_ERR_SHAPE;
   }
+  if (fp8) return PA_ERR_SHAPE;
   switch (dtype) {
     case PA_F32: return launch_valu_d<F32>(a, head_dim, st);
     case PA_F16: return launch_valu_d<F16>(a, head_dim, st);

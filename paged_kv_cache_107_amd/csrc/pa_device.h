@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_internal.h"
+
 namespace pa {
 
 constexpr int kWave = 64;
@@ -86,6 +88,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ u32x4_t buffer_load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buffer_load8(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
 // ------------------------------------------------------------- math
@@ -203,4 +208,104 @@ struct Mfma<F16> {
 };
 
 
+// ------------------------------------------------------------- 8-bit pools
+// Two E4M3 codes (the low or high 16 bits of w) -> two 16-bit operand values,
+// packed low first.  Every E4M3 value is exactly a bf16 and an f16 value, so
+// the widening is exact (scale operand 1).
+template <class E>
+__device__ __forceinline__ uint32_t widen2(uint32_t w, bool hi);
+template <>
+__device__ __forceinline__ uint32_t widen2<BF16>(uint32_t w, bool hi) {
+  return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+            : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen2<F16>(uint32_t w, bool hi) {
+  return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+            : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+// Eight codes in two words -> eight 16-bit values in the operand layout.
+template <class E>
+__device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
+  return u32x4{widen2<E>(w0, false), widen2<E>(w0, true), widen2<E>(w1, false),
+               widen2<E>(w1, true)};
+}
+
+// ------------------------------------------------------------- K/V tiles
+// One 16-token tile of one kv head (head_dim 128) in the registers of lane
+// (c16 = lane % 16, g4 = lane / 16), and the matrix-core operands built from
+// it: k_op(s) is the A operand of k-step s of S^T = K . Q^T (K row c16, 8
+// elements), v_row(r) holds V row 4 g4 + r, elements 8 c16 .. +7 (the
+// source of the P.V product's A operands).  q_elem(s, g4) is where the q
+// operand of k-step s starts, so that q and K agree on the order of the
+// contraction.
+//  * pools of the 16-bit operand type: k-step s takes elements 32 s + 8 g4
+//    .. +7 (four 16-byte loads; a load instruction covers 64 contiguous bytes
+//    of each row); V: four 16-byte loads.
+//  * 8-bit pools: the lane loads bytes 16 g4 .. +15 and 64 + 16 g4 .. +15 of
+//    its K row (two 16-byte loads), so k-step s takes elements 64 (s / 2) +
+//    16 g4 + 8 (s % 2) .. +7; V: four 8-byte loads.  The codes are widened
+//    when the operand is built.
+template <class E, KvType KV>
+struct KvTile;
+
+template <class E>
+struct KvTile<E, KvType::kSame> {
+  using P = typename E::storage;                     // pool element
+  static constexpr uint32_t kBytes = 16u * 128u * 2u;  // one tile of one kv head
+  u32x4 k[4], v[4];
+  static __device__ __forceinline__ int q_elem(int s, int g4) { return 32 * s + 8 * g4; }
+  __device__ __forceinline__ void load(rsrc_t kr, rsrc_t vr, int c16, int g4) {
+    const uint32_t ko = (uint32_t)(c16 * 128 + 8 * g4) * 2u;
+    const uint32_t vo = (uint32_t)((4 * g4) * 128 + 8 * c16) * 2u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) k[s] = buffer_load16(kr, ko + 64u * s);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = buffer_load16(vr, vo + 256u * r);
+  }
+  __device__ __forceinline__ u32x4 k_op(int s) const { return k[s]; }
+  __device__ __forceinline__ u32x4 v_row(int r) const { return v[r]; }
+};
+
+template <class E>
+struct KvTile<E, KvType::kFp8> {
+  using P = uint8_t;
+  static constexpr uint32_t kBytes = 16u * 128u;
+  u32x4 k[2];
+  u32x2 v[4];
+  static __device__ __forceinline__ int q_elem(int s, int g4) {
+    return 64 * (s >> 1) + 16 * g4 + 8 * (s & 1);
+  }
+  __device__ __forceinline__ void load(rsrc_t kr, rsrc_t vr, int c16, int g4) {
+    const uint32_t ko = (uint32_t)(c16 * 128 + 16 * g4);
+    const uint32_t vo = (uint32_t)((4 * g4) * 128 + 8 * c16);
+    k[0] = buffer_load16(kr, ko);
+    k[1] = buffer_load16(kr, ko + 64u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = buffer_load8(vr, vo + 128u * r);
+  }
+  __device__ __forceinline__ u32x4 k_op(int s) const {
+    const u32x4& c = k[s >> 1];
+    return (s & 1) ? widen8<E>(c[2], c[3]) : widen8<E>(c[0], c[1]);
+  }
+  __device__ __forceinline__ u32x4 v_row(int r) const { return widen8<E>(v[r][0], v[r][1]); }
+};
+
+// fp32 -> E4M3 code for a quantised cache write: the caller has already
+// multiplied by 1 / scale; clamps to +-448, rounds to nearest even; NaN ->
+// 0x7F.  Two values at a time into the low or high 16 bits of `old`.
+__device__ __forceinline__ uint32_t to_e4m3_pair(float a, float b, uint32_t old, bool hi) {
+  const float lim = 448.f;
+  const bool na = a != a, nb = b != b;
+  a = fminf(fmaxf(a, -lim), lim);
+  b = fminf(fmaxf(b, -lim), lim);
+  uint32_t r = hi ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true)
+                  : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+  const int sh = hi ? 16 : 0;
+  if (na) r = (r & ~(0xFFu << sh)) | (0x7Fu << sh);
+  if (nb) r = (r & ~(0xFFu << (sh + 8))) | (0x7Fu << (sh + 8));
+  return r;
+}
+
 }  // namespace pa
+

@@ -34,8 +34,10 @@ struct DecodeArgs {
   int32_t max_ctx;
   int32_t part_tokens;
   int32_t max_parts;
-  float scale_log2;      // softmax scale times log2(e)
+  float scale_log2;      // softmax scale times log2(e) (times k_scale for 8-bit pools)
   int32_t stream_waves;  // waves of the stream split's grid
+  int32_t window;        // sliding window in positions, 0 = none
+  float v_scale;         // output factor: v_scale for 8-bit pools, else 1
 };
 
 // Decode kernel families.
@@ -50,12 +52,16 @@ enum class DecodeKernel {
 constexpr int kStreamMaxSeqs = 4096;
 constexpr int kStreamMaxWaves = 1024;
 
+// Pool element types the kernels are built for: the activation dtype itself,
+// or 8-bit E4M3 codes (matrix-core kernels only).
+enum class KvType { kSame, kFp8 };
+
 bool mfma_supports(int dtype, int head_dim, int group);
 bool valu_supports(int dtype, int head_dim, int group);
 bool stream_supports(int num_seqs, int num_kv_heads, int max_ctx);
 int stream_waves();  // on the current device; 0 if it cannot be queried
-pa_status launch_decode_partition(const DecodeArgs& a, int dtype, int head_dim, DecodeKernel k,
-                                  hipStream_t st);
+pa_status launch_decode_partition(const DecodeArgs& a, int dtype, KvType kv, int head_dim,
+                                  DecodeKernel k, hipStream_t st);
 pa_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, DecodeKernel k,
                                hipStream_t st);
 
@@ -79,12 +85,19 @@ struct PrefillArgs {
   int32_t max_blocks;
   int32_t max_ctx;
   int32_t max_query;
-  float scale_log2;
+  float scale_log2;  // softmax scale times log2(e) (times k_scale for 8-bit pools)
+  int32_t window;    // sliding window in positions, 0 = none
+  float v_scale;     // output factor: v_scale for 8-bit pools, else 1
 };
 
 bool prefill_supports(int dtype, int head_dim, int group);
 int prefill_query_blocks(int max_query_len, int group);  // per sequence, grid bound
-pa_status launch_prefill(const PrefillArgs& a, int dtype, hipStream_t st);
+pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, hipStream_t st);
+
+// Pool element bytes for a valid descriptor.
+inline int pool_elem_bytes(const pa_pool_desc& pool) {
+  return pool.kv_dtype == PA_KV_FP8_E4M3 ? 1 : pool.dtype == PA_F32 ? 4 : 2;
+}
 
 pa_status launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
                                    int32_t num_tokens, void* k_pool, void* v_pool,

@@ -20,6 +20,11 @@
 // position are masked per element.  Each lane keeps the softmax state of its
 // column in each group, with the decode kernel's lazy rescale.
 //
+// With a sliding window of W positions a row at position p attends only
+// positions p - W + 1 .. p: the wave starts at the tile of its first row's
+// window and masks per element below each row's window as well.  8-bit pools
+// are widened to the 16-bit operand type as the tiles are used (KvTile).
+//
 // Grid (kv head, sequence, query-block group) with the last dimension
 // slowest: workgroup z takes query blocks nqb-1-4z .. nqb-4-4z of every
 // (kv head, sequence), so the heaviest blocks (latest positions, most keys)
@@ -49,10 +54,15 @@ __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
   return ctx;
 }
 
-template <class E>
+// WIN: a sliding window is set (a.window > 0); without one every column's
+// first tile holds its key 0, so no column meets a fully masked tile before
+// its first key and the guards below are compiled out.
+template <class E, KvType KV, bool WIN>
 __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
   constexpr int D = 128;
   using S = typename E::storage;
+  using Tile = KvTile<E, KV>;
+  using P = typename Tile::P;
   const int g = blockIdx.x, i = blockIdx.y;
   const int G = a.group, QT = kRows / G;  // chunk tokens per wave
   const int qa = a.query_start[i], qb = a.query_start[i + 1];
@@ -90,33 +100,37 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
     return;
   }
 
-  // q operand of each group: lane (c16, g4) holds q[column c16][32 s + 8 g4 .. +7]
+  // q operand of each group: lane (c16, g4) holds the 8 elements of
+  // q[column c16] that k-step s contracts (Tile::q_elem)
   u32x4 qv[kGroups][4];
 #pragma unroll
   for (int q = 0; q < kGroups; ++q) {
-    const S* qrow = reinterpret_cast<const S*>(a.q) + (size_t)max(row[q], 0) * D + 8 * g4;
+    const S* qrow = reinterpret_cast<const S*>(a.q) + (size_t)max(row[q], 0) * D;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      qv[q][s] = row[q] >= 0 ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+      qv[q][s] = row[q] >= 0 ? *reinterpret_cast<const u32x4*>(qrow + Tile::q_elem(s, g4))
+                             : u32x4{0, 0, 0, 0};
   }
 
   const int bs_mask = (1 << a.log2_bs) - 1;
   const size_t head_stride = (size_t)D << a.log2_bs;
   const size_t block_stride = head_stride * a.num_kv_heads;
   const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
-  const S* kbase0 = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride;
-  const S* vbase0 = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride;
-  const uint32_t k_lane_off = (uint32_t)(c16 * D + 8 * g4) * 2u;
-  const uint32_t v_lane_off = (uint32_t)((4 * g4) * D + 8 * c16) * 2u;
+  const P* kbase0 = reinterpret_cast<const P*>(a.k_pool) + (size_t)g * head_stride;
+  const P* vbase0 = reinterpret_cast<const P*>(a.v_pool) + (size_t)g * head_stride;
   const int ntiles = ceil_div(kend, kTile);
   const int unmasked = max(pos0, 0);  // every row sees keys <= this position
+  // Sliding window: the first row's window starts the walk; rows' windows
+  // start at lim - W + 1, the latest at kend - W.
+  const int W = WIN ? a.window : 0;
+  const int t_begin = WIN ? max(unmasked - W + 1, 0) / kTile : 0;
 
   // Issue side: the block id of the next tile is read one issue ahead; tiles
   // past the last (or with a bad block id) get an empty descriptor, so every
-  // issue has exactly 8 loads and the waits stay static.
-  int it = 0;
-  int iblk = scalar_load(table + 0);
-  auto issue = [&](u32x4 (&kr)[4], u32x4 (&vr)[4]) -> bool {
+  // issue has the same loads and the waits stay static.
+  int it = t_begin;
+  int iblk = scalar_load(table + ((it * kTile) >> a.log2_bs));
+  auto issue = [&](Tile& tile) -> bool {
     bool ok = false;
     size_t off = 0;
     if (it < ntiles) {
@@ -124,13 +138,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
       if (ok) off = (size_t)iblk * block_stride + (size_t)((it * kTile) & bs_mask) * D;
       if (++it < ntiles) iblk = scalar_load(table + ((it * kTile) >> a.log2_bs));
     }
-    const uint32_t bytes = ok ? kTile * D * 2u : 0u;
-    const rsrc_t kr_rs = make_rsrc(kbase0 + off, bytes);
-    const rsrc_t vr_rs = make_rsrc(vbase0 + off, bytes);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kr[s] = buffer_load16(kr_rs, k_lane_off + 64u * s);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = buffer_load16(vr_rs, v_lane_off + 256u * r);
+    const uint32_t bytes = ok ? Tile::kBytes : 0u;
+    tile.load(make_rsrc(kbase0 + off, bytes), make_rsrc(vbase0 + off, bytes), c16, g4);
     return ok;
   };
 
@@ -144,9 +153,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
     for (int e = 0; e < 8; ++e) o[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One key tile for the four groups.
-  auto compute = [&](int t, u32x4 (&kc)[4], u32x4 (&vc)[4]) {
+  // One key tile for the four groups.  A column whose keys in this tile
+  // are all masked (before its window) may not have seen a key yet (m =
+  // -inf): its weights and rescale factor are then taken as 0 and 1.
+  auto compute = [&](int t, const Tile& tile) {
     const int k0 = t * kTile;
+    u32x4 vc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vc[r] = tile.v_row(r);
     if (k0 + kTile > ctx) {  // slots past the sequence may hold anything
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -159,7 +173,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
       vw[e] = u32x2{__builtin_amdgcn_perm(vc[1][e >> 1], vc[0][e >> 1], sel),
                     __builtin_amdgcn_perm(vc[3][e >> 1], vc[2][e >> 1], sel)};
     }
-    const bool masked = k0 + kTile - 1 > unmasked;
+    const bool masked = k0 + kTile - 1 > unmasked || (WIN && k0 < kend - W);
     // The tile in three phases over the groups -- every QK product, then
     // every softmax update, then every PV product -- so the matrix cores work
     // on one group's products while the vector ALU handles another's scores.
@@ -168,7 +182,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
     for (int q = 0; q < kGroups; ++q) {
       sacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) sacc[q] = Mfma<E>::qk(kc[s], qv[q][s], sacc[q]);
+      for (int s = 0; s < 4; ++s) sacc[q] = Mfma<E>::qk(tile.k_op(s), qv[q][s], sacc[q]);
     }
     u32x2 pw[kGroups];
 #pragma unroll
@@ -178,8 +192,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
       for (int r = 0; r < 4; ++r) sv[r] = sacc[q][r] * a.scale_log2;
       if (masked) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (k0 + 4 * g4 + r > lim[q]) sv[r] = neg_inf();
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 4 * g4 + r;
+          if (key > lim[q] || (WIN && key <= lim[q] - W)) sv[r] = neg_inf();
+        }
       }
       const float lim_s = m[q] + kRescaleSlack;
       const bool over = sv[0] > lim_s || sv[1] > lim_s || sv[2] > lim_s || sv[3] > lim_s;
@@ -188,7 +204,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
         mt = fmaxf(mt, shfl_xor(mt, 16));
         mt = fmaxf(mt, shfl_xor(mt, 32));
         const float mn = fmaxf(m[q], mt);
-        const float alpha = fast_exp2(m[q] - mn);
+        const float alpha = WIN && mn == neg_inf() ? 1.f : fast_exp2(m[q] - mn);
         l[q] *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[q][e] *= alpha;
@@ -196,11 +212,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
       }
       uint32_t pb[4];
       float psum = 0.f;
+      if (WIN && masked) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pb[r] = Mfma<E>::round16(fast_exp2(sv[r] - m[q]));
-        psum += bits_to_float(E{}, pb[r]);
+        for (int r = 0; r < 4; ++r)
+          pb[r] = Mfma<E>::round16(sv[r] == neg_inf() ? 0.f : fast_exp2(sv[r] - m[q]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pb[r] = Mfma<E>::round16(fast_exp2(sv[r] - m[q]));
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) psum += bits_to_float(E{}, pb[r]);
       l[q] += psum;
       pw[q] = u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
     }
@@ -210,18 +231,18 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
       for (int e = 0; e < 8; ++e) o[q][e] = Mfma<E>::pv(vw[e], pw[q], o[q][e]);
   };
 
-  u32x4 kb[kPfPrefetch][4], vb[kPfPrefetch][4];
+  Tile tb[kPfPrefetch];
   bool okb[kPfPrefetch];
 #pragma unroll
-  for (int s = 0; s < kPfPrefetch; ++s) okb[s] = issue(kb[s], vb[s]);
+  for (int s = 0; s < kPfPrefetch; ++s) okb[s] = issue(tb[s]);
   // Every slot issues on every path and the loop exits at the bottom of the
   // unrolled body, so the compiler's wait counts stay static.
-  int t = 0;
+  int t = t_begin;
   do {
 #pragma unroll
     for (int s = 0; s < kPfPrefetch; ++s) {
-      if (t < ntiles && okb[s]) compute(t, kb[s], vb[s]);
-      okb[s] = issue(kb[s], vb[s]);
+      if (t < ntiles && okb[s]) compute(t, tb[s]);
+      okb[s] = issue(tb[s]);
       ++t;
     }
   } while (t < ntiles);
@@ -231,7 +252,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
   for (int q = 0; q < kGroups; ++q) {
     const float lsum = across_groups_sum<16>(l[q]);
     if (row[q] < 0) continue;
-    const float inv = live[q] && lsum > 0.f ? 1.f / lsum : 0.f;
+    const float inv = live[q] && lsum > 0.f ? a.v_scale / lsum : 0.f;
     S* dst = out + (size_t)row[q] * D + 32 * g4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -244,10 +265,13 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
   }
 }
 
-template <class E>
+template <class E, KvType KV>
 pa_status launch(const PrefillArgs& a, int max_query_blocks, hipStream_t st) {
   const dim3 grid(a.num_kv_heads, a.num_seqs, ceil_div(max_query_blocks, kPfWaves));
-  hipLaunchKernelGGL((prefill_mfma<E>), grid, dim3(kPfThreads), 0, st, a);
+  if (a.window > 0)
+    hipLaunchKernelGGL((prefill_mfma<E, KV, true>), grid, dim3(kPfThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_mfma<E, KV, false>), grid, dim3(kPfThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -262,11 +286,14 @@ int prefill_query_blocks(int max_query_len, int group) {
   return max_query_len > 0 ? (max_query_len + kRows / group - 1) / (kRows / group) : 0;
 }
 
-pa_status launch_prefill(const PrefillArgs& a, int dtype, hipStream_t st) {
+pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, hipStream_t st) {
   const int blocks = prefill_query_blocks(a.max_query, a.group);
   if (blocks <= 0) return PA_OK;
-  if (dtype == PA_BF16) return launch<BF16>(a, blocks, st);
-  if (dtype == PA_F16) return launch<F16>(a, blocks, st);
+  const bool fp8 = kv == KvType::kFp8;
+  if (dtype == PA_BF16)
+    return fp8 ? launch<BF16, KvType::kFp8>(a, blocks, st) : launch<BF16, KvType::kSame>(a, blocks, st);
+  if (dtype == PA_F16)
+    return fp8 ? launch<F16, KvType::kFp8>(a, blocks, st) : launch<F16, KvType::kSame>(a, blocks, st);
   return PA_ERR_SHAPE;
 }
 

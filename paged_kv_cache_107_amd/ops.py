@@ -11,9 +11,11 @@ from typing import Optional
 
 import torch
 
-from ._lib import (PA_BF16, PA_F16, PA_F32, check, lib, pa_pool_desc)
+from ._lib import (PA_BF16, PA_F16, PA_F32, PA_KV_FP8_E4M3, PA_KV_SAME, check, lib,
+                   pa_pool_desc)
 
 _DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+FP8 = torch.float8_e4m3fn  # 8-bit pool element (E4M3, the OCP "fn" variant)
 
 
 def _stream(stream) -> C.c_void_p:
@@ -35,22 +37,37 @@ def _need_cuda(name: str, t: torch.Tensor, dtype=None, contiguous=True) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def pool_desc(k_pool: torch.Tensor) -> pa_pool_desc:
-    """Descriptor of a [num_blocks][num_kv_heads][block_size][head_dim] pool."""
+def pool_desc(k_pool: torch.Tensor, act_dtype=None, kv_scales=(1.0, 1.0)) -> pa_pool_desc:
+    """Descriptor of a [num_blocks][num_kv_heads][block_size][head_dim] pool.
+    An 8-bit (float8_e4m3fn) pool needs the activation dtype (q, out, new
+    K/V rows; bf16 when only the block size matters) and its (k, v) scales."""
     if k_pool.dim() != 4:
         raise ValueError("pools are [num_blocks][num_kv_heads][block_size][head_dim]")
+    nb, hkv, bs, d = k_pool.shape
+    if k_pool.dtype == FP8:
+        act = act_dtype or torch.bfloat16
+        if act not in _DTYPES:
+            raise ValueError(f"unsupported activation dtype {act}")
+        return pa_pool_desc(nb, bs, hkv, d, _DTYPES[act], PA_KV_FP8_E4M3, float(kv_scales[0]),
+                            float(kv_scales[1]))
     if k_pool.dtype not in _DTYPES:
         raise ValueError(f"unsupported pool dtype {k_pool.dtype}")
-    nb, hkv, bs, d = k_pool.shape
-    return pa_pool_desc(nb, bs, hkv, d, _DTYPES[k_pool.dtype])
+    if act_dtype is not None and act_dtype != k_pool.dtype:
+        raise ValueError(f"activations must be {k_pool.dtype}, got {act_dtype}")
+    return pa_pool_desc(nb, bs, hkv, d, _DTYPES[k_pool.dtype], PA_KV_SAME, 1.0, 1.0)
 
 
-def _check_pools(k_pool, v_pool):
+def _check_pools(k_pool, v_pool, act_dtype=None, kv_scales=(1.0, 1.0)):
     _need_cuda("k_pool", k_pool)
     _need_cuda("v_pool", v_pool, k_pool.dtype)
     if v_pool.shape != k_pool.shape:
         raise ValueError("k_pool and v_pool must have the same shape")
-    return pool_desc(k_pool)
+    return pool_desc(k_pool, act_dtype, kv_scales)
+
+
+def _act_dtype(k_pool, t):
+    """Activation dtype: the pool's, or t's for an 8-bit pool."""
+    return t.dtype if k_pool.dtype == FP8 else k_pool.dtype
 
 
 def pa_decode_workspace_bytes(pool, num_seqs: int, num_q_heads: int, max_context_len: int,
@@ -70,10 +87,11 @@ def alloc_workspace(k_pool: torch.Tensor, num_seqs: int, num_q_heads: int, max_c
 
 
 def _decode_call(fn_name, q, k_pool, v_pool, block_tables, context_lens, scale, out,
-                 workspace, max_context_len, partition_tokens, stream):
-    desc = _check_pools(k_pool, v_pool)
-    _need_cuda("q", q, k_pool.dtype)
-    _need_cuda("out", out, k_pool.dtype)
+                 workspace, max_context_len, partition_tokens, stream, sliding_window, kv_scales):
+    act = _act_dtype(k_pool, q)
+    desc = _check_pools(k_pool, v_pool, act, kv_scales)
+    _need_cuda("q", q, act)
+    _need_cuda("out", out, act)
     _need_cuda("block_tables", block_tables, torch.int32)
     _need_cuda("context_lens", context_lens, torch.int32)
     if q.dim() != 3 or q.shape[2] != desc.head_dim or out.shape != q.shape:
@@ -88,40 +106,49 @@ def _decode_call(fn_name, q, k_pool, v_pool, block_tables, context_lens, scale, 
     fn = getattr(lib(), fn_name)
     st = fn(_ptr(q), _ptr(k_pool), _ptr(v_pool), C.byref(desc), _ptr(block_tables),
             int(block_tables.shape[1]), _ptr(context_lens), int(b), int(hq),
-            int(max_context_len), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
-            int(partition_tokens), _stream(stream))
+            int(max_context_len), float(scale), int(sliding_window), _ptr(out), _ptr(workspace),
+            ws_bytes, int(partition_tokens), _stream(stream))
     check(fn_name, st)
     return out
 
 
 def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
-              max_context_len, partition_tokens=0, stream=None):
-    """Paged decode attention (partition + reduce).  See pa.h."""
+              max_context_len, partition_tokens=0, stream=None, sliding_window=0,
+              kv_scales=(1.0, 1.0)):
+    """Paged decode attention (partition + reduce).  See pa.h.  kv_scales:
+    (k_scale, v_scale) of an 8-bit pool."""
     return _decode_call("pa_decode", q, k_pool, v_pool, block_tables, context_lens, scale, out,
-                        workspace, max_context_len, partition_tokens, stream)
+                        workspace, max_context_len, partition_tokens, stream, sliding_window,
+                        kv_scales)
 
 
 def pa_decode_partition(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
-                        max_context_len, partition_tokens=0, stream=None):
+                        max_context_len, partition_tokens=0, stream=None, sliding_window=0,
+                        kv_scales=(1.0, 1.0)):
     return _decode_call("pa_decode_partition", q, k_pool, v_pool, block_tables, context_lens,
-                        scale, out, workspace, max_context_len, partition_tokens, stream)
+                        scale, out, workspace, max_context_len, partition_tokens, stream,
+                        sliding_window, kv_scales)
 
 
 def pa_decode_reduce(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
-                     max_context_len, partition_tokens=0, stream=None):
+                     max_context_len, partition_tokens=0, stream=None, sliding_window=0,
+                     kv_scales=(1.0, 1.0)):
     return _decode_call("pa_decode_reduce", q, k_pool, v_pool, block_tables, context_lens,
-                        scale, out, workspace, max_context_len, partition_tokens, stream)
+                        scale, out, workspace, max_context_len, partition_tokens, stream,
+                        sliding_window, kv_scales)
 
 
 def pa_prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale, out,
-               max_query_len, max_context_len, stream=None):
+               max_query_len, max_context_len, stream=None, sliding_window=0,
+               kv_scales=(1.0, 1.0)):
     """Chunked prefill attention over the paged cache.  See pa.h.
 
     q, out [num_tokens][num_q_heads][head_dim]; query_start int32 [B+1];
     block_tables int32 [B][max_blocks]; context_lens int32 [B]."""
-    desc = _check_pools(k_pool, v_pool)
-    _need_cuda("q", q, k_pool.dtype)
-    _need_cuda("out", out, k_pool.dtype)
+    act = _act_dtype(k_pool, q)
+    desc = _check_pools(k_pool, v_pool, act, kv_scales)
+    _need_cuda("q", q, act)
+    _need_cuda("out", out, act)
     _need_cuda("block_tables", block_tables, torch.int32)
     _need_cuda("query_start", query_start, torch.int32)
     _need_cuda("context_lens", context_lens, torch.int32)
@@ -135,7 +162,7 @@ def pa_prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale
     st = lib().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), C.byref(desc), _ptr(block_tables),
                           int(block_tables.shape[1]), _ptr(query_start), _ptr(context_lens),
                           int(b), int(t), int(hq), int(max_query_len), int(max_context_len),
-                          float(scale), _ptr(out), _stream(stream))
+                          float(scale), int(sliding_window), _ptr(out), _stream(stream))
     check("pa_prefill", st)
     return out
 
@@ -147,11 +174,13 @@ def pa_set_decode_path(path: int) -> int:
     return prev
 
 
-def pa_reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None):
-    """Write new tokens' K/V ([T][Hkv][D]) into their slots.  See pa.h."""
-    desc = _check_pools(k_pool, v_pool)
-    _need_cuda("k", k, k_pool.dtype)
-    _need_cuda("v", v, k_pool.dtype)
+def pa_reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None, kv_scales=(1.0, 1.0)):
+    """Write new tokens' K/V ([T][Hkv][D]) into their slots (quantised for an
+    8-bit pool with kv_scales).  See pa.h."""
+    act = _act_dtype(k_pool, k)
+    desc = _check_pools(k_pool, v_pool, act, kv_scales)
+    _need_cuda("k", k, act)
+    _need_cuda("v", v, act)
     _need_cuda("slot_mapping", slot_mapping, torch.int64)
     t = slot_mapping.shape[0]
     shape = (t, desc.num_kv_heads, desc.head_dim)
