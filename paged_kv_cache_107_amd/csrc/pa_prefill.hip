@@ -25,11 +25,16 @@
 // window and masks per element below each row's window as well.  8-bit pools
 // are widened to the 16-bit operand type as the tiles are used (KvTile).
 //
-// Grid (kv head, sequence, query-block group) with the last dimension
-// slowest: workgroup z takes query blocks nqb-1-4z .. nqb-4-4z of every
-// (kv head, sequence), so the heaviest blocks (latest positions, most keys)
-// start first; neighbouring ids share a kv head's sequence, so its K/V tiles
-// are read from L2 by the workgroups of the same sequence.
+// Grid: kv head x, then a flat item index k over (sequence, query-block
+// group z); group z takes query blocks nqb-1-4z .. nqb-4-4z of its
+// sequence, the heaviest first.  A wave's work grows with its sequence's
+// length, so the items run longest sequence first: each workgroup ranks the
+// batch by length class (512 positions) in LDS (up to kLptSeqs sequences),
+// and the sequences of one class run group-major (every sequence's group 0,
+// then group 1, ...).  Short sequences then fill the tail instead of long
+// sequences' last groups starting late.  Larger batches run group-major in
+// batch order.  The kv heads of an item are neighbouring ids, so each XCD
+// serves one kv head of every sequence and re-reads its K/V from its own L2.
 #include <hip/hip_runtime.h>
 
 #include "pa.h"
@@ -46,6 +51,8 @@ constexpr int kRows = 16 * kGroups;         // query rows (token, head) per wave
 constexpr int kTile = 16;                   // keys per tile
 constexpr int kPfPrefetch = 2;              // tiles in the register ring
 constexpr float kRescaleSlack = 8.f;        // log2 units
+constexpr int kLptSeqs = 256;               // batches up to this size run longest first
+constexpr int kLenClassShift = 9;           // length classes of 512 positions
 
 __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
   int ctx = a.context_lens[i];
@@ -63,13 +70,46 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
   using S = typename E::storage;
   using Tile = KvTile<E, KV>;
   using P = typename Tile::P;
-  const int g = blockIdx.x, i = blockIdx.y;
+  const int g = blockIdx.x;
+  const int Z = gridDim.y, B = a.num_seqs;
+  const int k = (int)blockIdx.y + Z * (int)blockIdx.z;  // item index, 0 .. Z * B - 1
+  int i, zq;
+  if (B <= kLptSeqs) {
+    // rank[u] = sequences in longer classes + earlier ones in u's class; the
+    // class of rank r starts at rank first[r] and has cnt[r] sequences, and
+    // its items are [first * Z, (first + cnt) * Z), group-major.
+    __shared__ int s_cls[kLptSeqs], s_seq[kLptSeqs], s_first[kLptSeqs], s_cnt[kLptSeqs];
+    const int t = threadIdx.x;
+    for (int u = t; u < B; u += kPfThreads) s_cls[u] = max(clamp_ctx(a, u), 0) >> kLenClassShift;
+    __syncthreads();
+    for (int u = t; u < B; u += kPfThreads) {
+      const int cu = s_cls[u];
+      int longer = 0, before = 0, same = 0;
+      for (int v = 0; v < B; ++v) {
+        const int cv = s_cls[v];
+        longer += cv > cu;
+        before += cv == cu && v < u;
+        same += cv == cu;
+      }
+      s_seq[longer + before] = u;
+      s_first[longer + before] = longer;
+      s_cnt[longer + before] = same;
+    }
+    __syncthreads();
+    const int rr = k / Z, first = s_first[rr], cnt = s_cnt[rr];
+    const int off = k - first * Z;
+    zq = off / cnt;
+    i = s_seq[first + (off - zq * cnt)];
+  } else {
+    zq = k / B;
+    i = k - zq * B;
+  }
   const int G = a.group, QT = kRows / G;  // chunk tokens per wave
   const int qa = a.query_start[i], qb = a.query_start[i + 1];
   if (qa < 0 || qb > a.num_tokens || qb <= qa) return;
   const int n = qb - qa;                   // chunk tokens: positions ctx - n ..
   const int nqb = ceil_div(min(n, a.max_query), QT);  // rows past max_query are not run
-  const int blk = nqb - 1 - ((int)blockIdx.z * kPfWaves + wave_id());
+  const int blk = nqb - 1 - (zq * kPfWaves + wave_id());
   if (blk < 0) return;
   const int lane = threadIdx.x % kWave;
   const int c16 = lane & 15, g4 = lane >> 4;
@@ -267,7 +307,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
 
 template <class E, KvType KV>
 pa_status launch(const PrefillArgs& a, int max_query_blocks, hipStream_t st) {
-  const dim3 grid(a.num_kv_heads, a.num_seqs, ceil_div(max_query_blocks, kPfWaves));
+  const dim3 grid(a.num_kv_heads, ceil_div(max_query_blocks, kPfWaves), a.num_seqs);
   if (a.window > 0)
     hipLaunchKernelGGL((prefill_mfma<E, KV, true>), grid, dim3(kPfThreads), 0, st, a);
   else
