@@ -190,6 +190,12 @@ struct Mfma<BF16> {
   static __device__ __forceinline__ uint32_t round16(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
   }
+  // two probabilities rounded (RNE) and packed, the first in the low half
+  static __device__ __forceinline__ uint32_t round16x2(float x, float y) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x, y}, b2));
+  }
 };
 
 template <>
@@ -204,6 +210,11 @@ struct Mfma<F16> {
   }
   static __device__ __forceinline__ uint32_t round16(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  static __device__ __forceinline__ uint32_t round16x2(float x, float y) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x, y}, h2));
   }
 };
 
@@ -253,6 +264,7 @@ template <class E>
 struct KvTile<E, KvType::kSame> {
   using P = typename E::storage;                     // pool element
   static constexpr uint32_t kBytes = 16u * 128u * 2u;  // one tile of one kv head
+  static constexpr uint32_t kRowBytes = kBytes / 16u;
   u32x4 k[4], v[4];
   static __device__ __forceinline__ int q_elem(int s, int g4) { return 32 * s + 8 * g4; }
   __device__ __forceinline__ void load(rsrc_t kr, rsrc_t vr, int c16, int g4) {
@@ -271,6 +283,7 @@ template <class E>
 struct KvTile<E, KvType::kFp8> {
   using P = uint8_t;
   static constexpr uint32_t kBytes = 16u * 128u;
+  static constexpr uint32_t kRowBytes = kBytes / 16u;
   u32x4 k[2];
   u32x2 v[4];
   static __device__ __forceinline__ int q_elem(int s, int g4) {

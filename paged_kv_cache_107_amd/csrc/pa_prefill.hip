@@ -173,16 +173,27 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
   auto issue = [&](Tile& tile) -> bool {
     bool ok = false;
     size_t off = 0;
+    int rows = 0;  // V rows of the tile inside the sequence; the rest read as zeros
     if (it < ntiles) {
       ok = (unsigned)iblk < (unsigned)a.num_blocks;
       if (ok) off = (size_t)iblk * block_stride + (size_t)((it * kTile) & bs_mask) * D;
+      rows = min(kTile, ctx - it * kTile);
       if (++it < ntiles) iblk = scalar_load(table + ((it * kTile) >> a.log2_bs));
     }
-    const uint32_t bytes = ok ? Tile::kBytes : 0u;
-    tile.load(make_rsrc(kbase0 + off, bytes), make_rsrc(vbase0 + off, bytes), c16, g4);
+    const uint32_t kbytes = ok ? Tile::kBytes : 0u;
+    const uint32_t vbytes = ok ? (uint32_t)rows * Tile::kRowBytes : 0u;
+    tile.load(make_rsrc(kbase0 + off, kbytes), make_rsrc(vbase0 + off, vbytes), c16, g4);
     return ok;
   };
 
+  // score scale c > 0 in log2 units: a negative scale flips q's sign (exact)
+  const float c = fabsf(a.scale_log2), inv_c = 1.f / c;
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qv[q][s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
   float m[kGroups], l[kGroups];
   f32x4 o[kGroups][8];
 #pragma unroll
@@ -195,17 +206,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
 
   // One key tile for the four groups.  A column whose keys in this tile
   // are all masked (before its window) may not have seen a key yet (m =
-  // -inf): its weights and rescale factor are then taken as 0 and 1.
+  // -inf): its weights and rescale factor are then taken as 0 and 1.  V rows
+  // past the sequence arrive as zeros (the descriptor ends at the last row).
+  // Scores stay unscaled: the rescale test compares them with (m + slack) /
+  // c and the weights are exp2(s * c - m) in one fused multiply-add, c > 0
+  // (q's sign carries a negative scale).
   auto compute = [&](int t, const Tile& tile) {
     const int k0 = t * kTile;
     u32x4 vc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) vc[r] = tile.v_row(r);
-    if (k0 + kTile > ctx) {  // slots past the sequence may hold anything
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (k0 + 4 * g4 + r >= ctx) vc[r] = u32x4{0, 0, 0, 0};
-    }
     u32x2 vw[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -229,7 +239,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
     for (int q = 0; q < kGroups; ++q) {
       float sv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = sacc[q][r] * a.scale_log2;
+      for (int r = 0; r < 4; ++r) sv[r] = sacc[q][r];
       if (masked) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -237,33 +247,31 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
           if (key > lim[q] || (WIN && key <= lim[q] - W)) sv[r] = neg_inf();
         }
       }
-      const float lim_s = m[q] + kRescaleSlack;
-      const bool over = sv[0] > lim_s || sv[1] > lim_s || sv[2] > lim_s || sv[3] > lim_s;
+      const float thr = (m[q] + kRescaleSlack) * inv_c;
+      const bool over = sv[0] > thr || sv[1] > thr || sv[2] > thr || sv[3] > thr;
       if (__builtin_amdgcn_ballot_w64(over)) {
         float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
         mt = fmaxf(mt, shfl_xor(mt, 16));
         mt = fmaxf(mt, shfl_xor(mt, 32));
-        const float mn = fmaxf(m[q], mt);
+        const float mn = fmaxf(m[q], mt * c);
         const float alpha = WIN && mn == neg_inf() ? 1.f : fast_exp2(m[q] - mn);
         l[q] *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[q][e] *= alpha;
         m[q] = mn;
       }
-      uint32_t pb[4];
-      float psum = 0.f;
+      float pf[4];
       if (WIN && masked) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          pb[r] = Mfma<E>::round16(sv[r] == neg_inf() ? 0.f : fast_exp2(sv[r] - m[q]));
+          pf[r] = sv[r] == neg_inf() ? 0.f : fast_exp2(__builtin_fmaf(sv[r], c, -m[q]));
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pb[r] = Mfma<E>::round16(fast_exp2(sv[r] - m[q]));
+        for (int r = 0; r < 4; ++r) pf[r] = fast_exp2(__builtin_fmaf(sv[r], c, -m[q]));
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) psum += bits_to_float(E{}, pb[r]);
-      l[q] += psum;
-      pw[q] = u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+      pw[q] = u32x2{Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3])};
+      // l sums the weights as rounded for the P.V product
+      l[q] += (lo16(E{}, pw[q][0]) + hi16(E{}, pw[q][0])) + (lo16(E{}, pw[q][1]) + hi16(E{}, pw[q][1]));
     }
 #pragma unroll
     for (int q = 0; q < kGroups; ++q)
