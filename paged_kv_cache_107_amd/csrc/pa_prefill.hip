@@ -29,9 +29,9 @@
 // group z); group z takes query blocks nqb-1-4z .. nqb-4-4z of its
 // sequence, the heaviest first.  A wave's work grows with its sequence's
 // length, so the items run longest sequence first: each workgroup ranks the
-// batch by length class (512 positions) in LDS (up to kLptSeqs sequences),
-// and the sequences of one class run group-major (every sequence's group 0,
-// then group 1, ...).  Short sequences then fill the tail instead of long
+// batch by length class (512 positions) with counts in LDS (up to kLptSeqs
+// sequences), and the sequences of one class run group-major (every
+// sequence's group 0, then group 1, ...).  Short sequences then fill the tail instead of long
 // sequences' last groups starting late.  Larger batches run group-major in
 // batch order.  The kv heads of an item are neighbouring ids, so each XCD
 // serves one kv head of every sequence and re-reads its K/V from its own L2.
@@ -51,8 +51,9 @@ constexpr int kRows = 16 * kGroups;         // query rows (token, head) per wave
 constexpr int kTile = 16;                   // keys per tile
 constexpr int kPfPrefetch = 2;              // tiles in the register ring
 constexpr float kRescaleSlack = 8.f;        // log2 units
-constexpr int kLptSeqs = 256;               // batches up to this size run longest first
+constexpr int kLptSeqs = 4096;              // batches up to this size run longest first
 constexpr int kLenClassShift = 9;           // length classes of 512 positions
+constexpr int kClasses = 4 * 64;            // classes counted (longer ones share the top class)
 
 __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
   int ctx = a.context_lens[i];
@@ -75,31 +76,71 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
   const int k = (int)blockIdx.y + Z * (int)blockIdx.z;  // item index, 0 .. Z * B - 1
   int i, zq;
   if (B <= kLptSeqs) {
-    // rank[u] = sequences in longer classes + earlier ones in u's class; the
-    // class of rank r starts at rank first[r] and has cnt[r] sequences, and
-    // its items are [first * Z, (first + cnt) * Z), group-major.
-    __shared__ int s_cls[kLptSeqs], s_seq[kLptSeqs], s_first[kLptSeqs], s_cnt[kLptSeqs];
+    // Classes are counted in LDS; class C holds ranks [start(C), start(C) +
+    // cnt(C)) with start(C) = sequences in longer classes, and items
+    // [start * Z, (start + cnt) * Z), group-major.  The item's class is found
+    // from the counts, then its sequence -- the j-th of the class in batch
+    // order -- by one wave with ballots over 64 sequences at a time.
+    __shared__ int s_cls[kLptSeqs], s_cnt[kClasses], s_pick[3];
     const int t = threadIdx.x;
-    for (int u = t; u < B; u += kPfThreads) s_cls[u] = max(clamp_ctx(a, u), 0) >> kLenClassShift;
+    for (int c = t; c < kClasses; c += kPfThreads) s_cnt[c] = 0;
     __syncthreads();
     for (int u = t; u < B; u += kPfThreads) {
-      const int cu = s_cls[u];
-      int longer = 0, before = 0, same = 0;
-      for (int v = 0; v < B; ++v) {
-        const int cv = s_cls[v];
-        longer += cv > cu;
-        before += cv == cu && v < u;
-        same += cv == cu;
-      }
-      s_seq[longer + before] = u;
-      s_first[longer + before] = longer;
-      s_cnt[longer + before] = same;
+      const int c = min(max(clamp_ctx(a, u), 0) >> kLenClassShift, kClasses - 1);
+      s_cls[u] = c;
+      atomicAdd(&s_cnt[c], 1);
     }
     __syncthreads();
-    const int rr = k / Z, first = s_first[rr], cnt = s_cnt[rr];
+    // Wave 0: lane l holds the counts of classes 255 - 4l .. 252 - 4l (the
+    // descending order), a wave-wide scan gives each class's first rank, and
+    // the lane holding the item's rank finds its class; then the class's j-th
+    // sequence is found with ballots.
+    const int rr = k / Z;  // the item's rank
+    if (wave_id() == 0) {
+      const int lane = threadIdx.x % kWave;
+      int cnt4[4], own = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cnt4[e] = s_cnt[kClasses - 1 - (4 * lane + e)];
+        own += cnt4[e];
+      }
+      int incl = own;  // inclusive scan over lanes
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int x = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += x;
+      }
+      int first = incl - own;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (cnt4[e] > 0 && rr >= first && rr < first + cnt4[e]) {
+          s_pick[0] = kClasses - 1 - (4 * lane + e);
+          s_pick[1] = first;
+        }
+        first += cnt4[e];
+      }
+    }
+    __syncthreads();
+    const int cls = s_pick[0], first = s_pick[1], cnt = s_cnt[cls];
     const int off = k - first * Z;
     zq = off / cnt;
-    i = s_seq[first + (off - zq * cnt)];
+    int j = off - zq * cnt;  // the j-th sequence of the class, in batch order
+    if (wave_id() == 0) {
+      const int lane = threadIdx.x % kWave;
+      for (int base = 0; base < B; base += kWave) {
+        const int u = base + lane;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(u < B && s_cls[u] == cls);
+        const int n = __builtin_popcountll(hit);
+        if (j < n) {
+          const uint64_t below = lane ? hit & (~0ull >> (64 - lane)) : 0ull;
+          if (((hit >> lane) & 1ull) && __builtin_popcountll(below) == j) s_pick[2] = u;
+          break;
+        }
+        j -= n;
+      }
+    }
+    __syncthreads();
+    i = s_pick[2];
   } else {
     zq = k / B;
     i = k - zq * B;
