@@ -13,12 +13,15 @@
 // Work split: one wave per (sequence, kv head, block of query tokens).  The
 // G query heads of the kv head and 64 / G consecutive chunk tokens make 64
 // query rows, taken as four groups of 16: each group is the 16 columns of the
-// decode kernel's tile products (S^T = K . Q^T with v_mfma_f32_16x16x32, then
-// O^T += V^T . P^T with v_mfma_f32_16x16x16), so one K/V tile load feeds four
-// groups' products.  A wave walks the 16-key tiles from position 0 to its
-// last token through a register ring; the tiles at and past the block's first
-// position are masked per element.  Each lane keeps the softmax state of its
-// column in each group, with the decode kernel's lazy rescale.
+// decode kernel's tile products (S^T = K . Q^T with v_mfma_f32_16x16x32), so
+// one K/V tile load feeds four groups' products.  A wave walks the 16-key
+// tiles from position 0 to its last token two at a time through a register
+// ring of two pairs; with 32 keys per step the P.V product also runs on the
+// double-rate v_mfma_f32_16x16x32 (O^T += V^T . P^T).  The steps at and past
+// the block's first position are masked per element.  Each lane keeps the
+// softmax state of its column in each group, with the decode kernel's lazy
+// rescale; the running maximum starts at a finite floor, so a step has no
+// branch between the rescale test and the P.V product.
 //
 // With a sliding window of W positions a row at position p attends only
 // positions p - W + 1 .. p: the wave starts at the tile of its first row's
@@ -41,6 +44,7 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+
 namespace pa {
 namespace {
 
@@ -49,11 +53,34 @@ constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kGroups = 4;                  // 16-column groups per wave
 constexpr int kRows = 16 * kGroups;         // query rows (token, head) per wave
 constexpr int kTile = 16;                   // keys per tile
-constexpr int kPfPrefetch = 2;              // tiles in the register ring
+constexpr int kPfPairs = 2;                 // tile pairs in the register ring
 constexpr float kRescaleSlack = 8.f;        // log2 units
+constexpr float kMFloor = -1.0e30f;         // initial running maximum
 constexpr int kLptSeqs = 4096;              // batches up to this size run longest first
 constexpr int kLenClassShift = 9;           // length classes of 512 positions
 constexpr int kClasses = 4 * 64;            // classes counted (longer ones share the top class)
+
+// The P.V product over 32 keys (v_mfma_f32_16x16x32, both operands 8
+// elements per lane), and acc + both 16-bit values of a word (a dot product
+// with (1, 1)).
+__device__ __forceinline__ f32x4 pv32(BF16, u32x4 v, u32x4 p, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v),
+                                                 __builtin_bit_cast(bf16x8, p), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 pv32(F16, u32x4 v, u32x4 p, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, v),
+                                                __builtin_bit_cast(f16x8, p), c, 0, 0, 0);
+}
+__device__ __forceinline__ float sum2(BF16, uint32_t w, float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w),
+                                         __builtin_bit_cast(b2, 0x3F803F80u), acc, false);
+}
+__device__ __forceinline__ float sum2(F16, uint32_t w, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), __builtin_bit_cast(h2, 0x3C003C00u),
+                                acc, false);
+}
 
 __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
   int ctx = a.context_lens[i];
@@ -239,100 +266,119 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
   f32x4 o[kGroups][8];
 #pragma unroll
   for (int q = 0; q < kGroups; ++q) {
-    m[q] = neg_inf();
+    m[q] = kMFloor;
     l[q] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One key tile for the four groups.  A column whose keys in this tile
-  // are all masked (before its window) may not have seen a key yet (m =
-  // -inf): its weights and rescale factor are then taken as 0 and 1.  V rows
-  // past the sequence arrive as zeros (the descriptor ends at the last row).
-  // Scores stay unscaled: the rescale test compares them with (m + slack) /
-  // c and the weights are exp2(s * c - m) in one fused multiply-add, c > 0
-  // (q's sign carries a negative scale).
-  auto compute = [&](int t, const Tile& tile) {
+  // Two 16-key tiles per step, so the P.V product runs on the double-rate
+  // v_mfma_f32_16x16x32: its k-slot (g4, j) is key 4 g4 + j of the first
+  // tile for j < 4 and key 4 g4 + j - 4 of the second for j >= 4, which is
+  // where the lane's own S^T results of the two QK products sit.  A tile with
+  // a bad block id (or past the last) is masked out; so are keys past a
+  // column's position and, with a window, before its window.
+  auto compute2 = [&](int t, const Tile& ta, const Tile& tb, bool oka, bool okb) {
     const int k0 = t * kTile;
-    u32x4 vc[4];
+    u32x4 vw[8];
+    {
+      u32x4 va[4], vb[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vc[r] = tile.v_row(r);
-    u32x2 vw[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      vw[e] = u32x2{__builtin_amdgcn_perm(vc[1][e >> 1], vc[0][e >> 1], sel),
-                    __builtin_amdgcn_perm(vc[3][e >> 1], vc[2][e >> 1], sel)};
-    }
-    const bool masked = k0 + kTile - 1 > unmasked || (WIN && k0 < kend - W);
-    // The tile in three phases over the groups -- every QK product, then
-    // every softmax update, then every PV product -- so the matrix cores work
-    // on one group's products while the vector ALU handles another's scores.
-    f32x4 sacc[kGroups];
-#pragma unroll
-    for (int q = 0; q < kGroups; ++q) {
-      sacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) sacc[q] = Mfma<E>::qk(tile.k_op(s), qv[q][s], sacc[q]);
-    }
-    u32x2 pw[kGroups];
-#pragma unroll
-    for (int q = 0; q < kGroups; ++q) {
-      float sv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = sacc[q][r];
-      if (masked) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + 4 * g4 + r;
-          if (key > lim[q] || (WIN && key <= lim[q] - W)) sv[r] = neg_inf();
-        }
+      for (int r = 0; r < 4; ++r) {
+        va[r] = ta.v_row(r);
+        vb[r] = tb.v_row(r);
       }
-      const float thr = (m[q] + kRescaleSlack) * inv_c;
-      const bool over = sv[0] > thr || sv[1] > thr || sv[2] > thr || sv[3] > thr;
-      if (__builtin_amdgcn_ballot_w64(over)) {
-        float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        mt = fmaxf(mt, shfl_xor(mt, 16));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
-        const float mn = fmaxf(m[q], mt * c);
-        const float alpha = WIN && mn == neg_inf() ? 1.f : fast_exp2(m[q] - mn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        vw[e] = u32x4{__builtin_amdgcn_perm(va[1][e >> 1], va[0][e >> 1], sel),
+                      __builtin_amdgcn_perm(va[3][e >> 1], va[2][e >> 1], sel),
+                      __builtin_amdgcn_perm(vb[1][e >> 1], vb[0][e >> 1], sel),
+                      __builtin_amdgcn_perm(vb[3][e >> 1], vb[2][e >> 1], sel)};
+      }
+    }
+    const bool masked =
+        k0 + 2 * kTile - 1 > unmasked || (WIN && k0 < kend - W) || !oka || !okb;
+    float sv[kGroups][8];
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sa = Mfma<E>::qk(ta.k_op(s), qv[q][s], sa);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sb = Mfma<E>::qk(tb.k_op(s), qv[q][s], sb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[q][r] = sa[r];
+        sv[q][4 + r] = sb[r];
+      }
+    }
+    if (masked) {
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = k0 + (j < 4 ? 0 : kTile) + 4 * g4 + (j & 3);
+          if (key > lim[q] || (WIN && key <= lim[q] - W) || !(j < 4 ? oka : okb))
+            sv[q][j] = neg_inf();
+        }
+    }
+    // m starts at a finite floor, so a column that has seen no key yet
+    // (all -inf so far) gets weights exp2(-inf) = 0 and a rescale factor of
+    // 0 or 1, never NaN: the weights need no guard and the step has no
+    // branch between the rescale test and the P.V product.
+    float mt[kGroups];
+    bool over = false;
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      mt[q] = fmaxf(fmaxf(fmaxf(sv[q][0], sv[q][1]), fmaxf(sv[q][2], sv[q][3])),
+                    fmaxf(fmaxf(sv[q][4], sv[q][5]), fmaxf(sv[q][6], sv[q][7])));
+      over |= mt[q] > (m[q] + kRescaleSlack) * inv_c;
+    }
+    if (__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q) {
+        float x = fmaxf(mt[q], shfl_xor(mt[q], 16));
+        x = fmaxf(x, shfl_xor(x, 32));
+        const float mn = fmaxf(m[q], x * c);
+        const float alpha = fast_exp2(m[q] - mn);
         l[q] *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[q][e] *= alpha;
         m[q] = mn;
       }
-      float pf[4];
-      if (WIN && masked) {
+    }
+    u32x4 pw[kGroups];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          pf[r] = sv[r] == neg_inf() ? 0.f : fast_exp2(__builtin_fmaf(sv[r], c, -m[q]));
-      } else {
+    for (int q = 0; q < kGroups; ++q) {
+      float pf[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pf[r] = fast_exp2(__builtin_fmaf(sv[r], c, -m[q]));
-      }
-      pw[q] = u32x2{Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3])};
+      for (int j = 0; j < 8; ++j) pf[j] = fast_exp2(__builtin_fmaf(sv[q][j], c, -m[q]));
+      pw[q] = u32x4{Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3]),
+                    Mfma<E>::round16x2(pf[4], pf[5]), Mfma<E>::round16x2(pf[6], pf[7])};
       // l sums the weights as rounded for the P.V product
-      l[q] += (lo16(E{}, pw[q][0]) + hi16(E{}, pw[q][0])) + (lo16(E{}, pw[q][1]) + hi16(E{}, pw[q][1]));
+      l[q] = sum2(E{}, pw[q][3], sum2(E{}, pw[q][2], sum2(E{}, pw[q][1], sum2(E{}, pw[q][0], l[q]))));
     }
 #pragma unroll
     for (int q = 0; q < kGroups; ++q)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[q][e] = Mfma<E>::pv(vw[e], pw[q], o[q][e]);
+      for (int e = 0; e < 8; ++e) o[q][e] = pv32(E{}, vw[e], pw[q], o[q][e]);
   };
 
-  Tile tb[kPfPrefetch];
-  bool okb[kPfPrefetch];
+  Tile tb[2 * kPfPairs];
+  bool okb[2 * kPfPairs];
 #pragma unroll
-  for (int s = 0; s < kPfPrefetch; ++s) okb[s] = issue(tb[s]);
+  for (int s = 0; s < 2 * kPfPairs; ++s) okb[s] = issue(tb[s]);
   // Every slot issues on every path and the loop exits at the bottom of the
   // unrolled body, so the compiler's wait counts stay static.
   int t = t_begin;
   do {
 #pragma unroll
-    for (int s = 0; s < kPfPrefetch; ++s) {
-      if (t < ntiles && okb[s]) compute(t, tb[s]);
+    for (int s = 0; s < 2 * kPfPairs; s += 2) {
+      if (t < ntiles && (okb[s] || okb[s + 1])) compute2(t, tb[s], tb[s + 1], okb[s], okb[s + 1]);
       okb[s] = issue(tb[s]);
-      ++t;
+      okb[s + 1] = issue(tb[s + 1]);
+      t += 2;
     }
   } while (t < ntiles);
 
