@@ -31,6 +31,12 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # moved its 128 accumulators between the register files every tile.)
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 AGPR_FORM_SOURCES = set()
+# Per-source scheduler choice.  The prefill kernel holds more live values than
+# fit in 256 VGPRs (128 output accumulators, a 4-tile K/V ring, q operands);
+# the register-pressure-first scheduler keeps fewer of them in AGPRs and
+# copies fewer between register files, which measured 10% faster than the
+# default on the 8B chunked-prefill workload (474 vs 528 us).
+SOURCE_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 
@@ -45,6 +51,7 @@ def hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     extra = [] if src in AGPR_FORM_SOURCES else VGPR_FORM
+    extra = extra + SOURCE_FLAGS.get(src, [])
     cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc(), *[f for f in COMMON if not f.startswith("--offload-arch")], "-c",
