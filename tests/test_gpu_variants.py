@@ -131,6 +131,44 @@ def test_windowed_prefill(window, g):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("window", [7, 40])
+@pytest.mark.parametrize("g", [1, 4])
+def test_windowed_prefill_after_trims(window, g):
+    """Blocks no chunk row's window reaches are released (each sequence is
+    trimmed to window + its chunk length, so the chunk's first row keeps its
+    whole window), the released blocks are poisoned with NaN and the tables
+    rebuilt with their holes: the windowed prefill output is unchanged."""
+    chunks = [1, 17, 64, 65, 100, 33]
+    prefixes = [0, 400, 160, 300, 90, 1000]
+    lens = [c + p for c, p in zip(chunks, prefixes)]
+    d = W.custom(1300 + g + window, 2 * g, 2, 128, "bf16", 16, lens, chunk_lens=chunks)
+    from test_gpu_prefill import run_gpu_prefill
+    kv = KV(d)
+    o = run_oracle(d, kv, compute_out=False)
+    gp = run_gpu_prefill(d, kv)
+    cache = gp["cache"]
+    free_before = set(cache.alloc.pa_alloc_query()[0].tolist())
+    released = sum(cache.trim_window(s, window + c) for s, c in enumerate(chunks))
+    freed = sorted(set(cache.alloc.pa_alloc_query()[0].tolist()) - free_before)
+    assert released == len(freed) > 0
+    idx = torch.tensor(freed, dtype=torch.long, device="cuda")
+    cache.k_pool[idx] = float("nan")
+    cache.v_pool[idx] = float("nan")
+    tables, _ = cache.alloc.pa_build_tables(list(range(d.batch)), gp["host_tables"].shape[1])
+    assert (tables == pa.PA_NO_BLOCK).any()
+    out = torch.full_like(gp["q"], float("nan"))
+    pa.pa_prefill(gp["q"], cache.k_pool, cache.v_pool, torch.from_numpy(tables).cuda(),
+                  gp["qs"], gp["lens"], d.wl.scale, out, gp["max_q"], gp["max_ctx"],
+                  sliding_window=window)
+    torch.cuda.synchronize()
+    want = paged_prefill(W.prefill_query_bits(d), o["kp"], o["vp"], o["tables"], d.query_start,
+                         o["lens"], d.wl.scale, "bf16", window=window)
+    err = max_abs_err(out, want)
+    print(f"trimmed prefill window={window} G={g} released={released} max_abs_err={err:.3e}",
+          flush=True)
+    assert err <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------ 8-bit pools
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
