@@ -224,6 +224,32 @@ def test_poisoned_padding(name, batch):
     assert torch.equal(out2, g["out"])
 
 
+@pytest.mark.parametrize("path", ["valu", "grid", "stream"])
+def test_bad_block_ids_inside_a_sequence(path, decode_path):
+    """Table entries outside the pool inside one sequence's attended range:
+    the kernels read nothing for them (the header leaves that sequence's
+    numbers unspecified; here its row stays finite), every other sequence's
+    output is unchanged bit for bit, and the pools are untouched."""
+    decode_path(path)
+    d = W.custom(17, 8, 2, 128, "bf16", 16, [40, 300, 77, 129])
+    g = run_gpu(d, KV(d))
+    cache, plan = g["cache"], g["plan"]
+    nb = cache.k_pool.shape[0]
+    kp0, vp0 = cache.k_pool.clone(), cache.v_pool.clone()
+    tables = plan.tables.clone()
+    tables[1, 3] = nb + 3
+    tables[1, 7] = -7
+    tables[1, 12] = 1 << 30
+    out = torch.full_like(g["out"], float("nan"))
+    pa.pa_decode(g["q"], cache.k_pool, cache.v_pool, tables, plan.lens, d.wl.scale, out, g["ws"],
+                 plan.max_context_len)
+    torch.cuda.synchronize()
+    for i in (0, 2, 3):
+        assert torch.equal(out[i], g["out"][i])
+    assert torch.all(torch.isfinite(out[1].float()))
+    assert torch.equal(cache.k_pool, kp0) and torch.equal(cache.v_pool, vp0)
+
+
 def test_zero_length_and_clamping():
     """ctx <= 0 gives a zero row; lengths beyond max_context_len are clamped
     (reads stay inside the tables)."""

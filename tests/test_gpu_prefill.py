@@ -173,3 +173,29 @@ def test_prefill_workload_full_size_sampled():
     print(f"prefill_8b sampled max_abs_err={worst:.3e}", flush=True)
     assert worst <= TOL["bf16"]
     assert torch.all(torch.isfinite(g["out"].float()))
+
+
+def test_bad_block_ids_inside_a_sequence():
+    """Table entries outside the pool inside one sequence's keys: the kernel
+    reads nothing for them (numbers unspecified for that sequence; here its
+    rows stay finite), every other sequence's rows are unchanged bit for bit
+    and the pools are untouched."""
+    chunks, prefixes = [17, 64, 33], [100, 300, 40]
+    d = W.custom(23, 16, 4, 128, "bf16", 16, [c + p for c, p in zip(chunks, prefixes)],
+                 chunk_lens=chunks)
+    g = run_gpu_prefill(d, KV(d))
+    cache = g["cache"]
+    nb = cache.k_pool.shape[0]
+    kp0, vp0 = cache.k_pool.clone(), cache.v_pool.clone()
+    tables = g["tables"].clone()
+    tables[1, 2] = nb + 1
+    tables[1, 9] = -3
+    out = torch.full_like(g["q"], float("nan"))
+    pa.pa_prefill(g["q"], cache.k_pool, cache.v_pool, tables, g["qs"], g["lens"], d.wl.scale, out,
+                  g["max_q"], g["max_ctx"])
+    torch.cuda.synchronize()
+    qs = d.query_start
+    for i in (0, 2):
+        assert torch.equal(out[qs[i]:qs[i + 1]], g["out"][qs[i]:qs[i + 1]])
+    assert torch.all(torch.isfinite(out[qs[1]:qs[2]].float()))
+    assert torch.equal(cache.k_pool, kp0) and torch.equal(cache.v_pool, vp0)
