@@ -51,18 +51,12 @@
 
 namespace pa {
 
-#ifndef PA_WG_WAVES
-#define PA_WG_WAVES 4
-#endif
-constexpr int kWaves = PA_WG_WAVES;  // waves per workgroup
+constexpr int kWaves = 4;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 // Lane k of a wave holds the block id of the wave's k-th tile, so a wave
 // takes at most 64 tiles: partitions of up to 4096 tokens need 4 waves.
 static_assert(kWaves * kWave * 16 >= 4096, "partition_tokens <= 4096 needs >= 4 waves");
 constexpr int kTile = 16;  // tokens per tile
-#ifndef PA_PART_DESC
-#define PA_PART_DESC 1
-#endif
 // Tiles per wave in the register ring.  The grid kernel runs two workgroups
 // per CU (two waves per SIMD) with a 3-deep ring; the stream kernel runs one
 // workgroup per CU with a 4-deep ring, which keeps as many bytes in flight
@@ -178,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
   using P = typename Tile::P;
   extern __shared__ float smem[];
   const int g = blockIdx.x, i = blockIdx.y;
-  const int p = PA_PART_DESC ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
+  const int p = (int)(gridDim.z - 1 - blockIdx.z);  // last partitions first
   const int ctx = clamp_ctx(a, i);
   const int n_parts = num_parts(a, ctx);
   if (p >= n_parts) return;
@@ -740,7 +734,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
   constexpr int LPT = kTile / RPL;
   extern __shared__ float smem[];
   const int g = blockIdx.x, i = blockIdx.y;
-  const int p = PA_PART_DESC ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
+  const int p = (int)(gridDim.z - 1 - blockIdx.z);  // last partitions first
   const int ctx = clamp_ctx(a, i);
   const int n_parts = num_parts(a, ctx);
   if (p >= n_parts) return;
