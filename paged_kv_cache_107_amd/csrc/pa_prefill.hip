@@ -23,6 +23,11 @@
 // rescale; the running maximum starts at a finite floor, so a step has no
 // branch between the rescale test and the P.V product.
 //
+// Two kernels share this step.  prefill_mfma_lds (16-bit pools, no window)
+// runs eight waves of 32 rows per item, two per SIMD, and shares each step's
+// K/V tiles through LDS; prefill_mfma (windows, 8-bit pools) gives each of
+// four waves 64 rows and its own register ring of tiles.
+//
 // With a sliding window of W positions a row at position p attends only
 // positions p - W + 1 .. p: the wave starts at the tile of its first row's
 // window and masks per element below each row's window as well.  8-bit pools
@@ -43,6 +48,7 @@
 #include "pa.h"
 #include "pa_device.h"
 #include "pa_internal.h"
+
 
 
 namespace pa {
@@ -89,19 +95,13 @@ __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
   return ctx;
 }
 
-// WIN: a sliding window is set (a.window > 0); without one every column's
-// first tile holds its key 0, so no column meets a fully masked tile before
-// its first key and the guards below are compiled out.
-template <class E, KvType KV, bool WIN>
-__global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
-  constexpr int D = 128;
-  using S = typename E::storage;
-  using Tile = KvTile<E, KV>;
-  using P = typename Tile::P;
-  const int g = blockIdx.x;
-  const int Z = gridDim.y, B = a.num_seqs;
-  const int k = (int)blockIdx.y + Z * (int)blockIdx.z;  // item index, 0 .. Z * B - 1
-  int i, zq;
+// The item (sequence i, query-block group zq) of workgroup item index k (Z
+// groups per sequence): longest sequences first (length classes counted in
+// LDS), group-major within a class; batches above kLptSeqs in batch order.
+// Every thread of the workgroup calls it (it has barriers).
+template <int THREADS>
+__device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
+  const int B = a.num_seqs;
   if (B <= kLptSeqs) {
     // Classes are counted in LDS; class C holds ranks [start(C), start(C) +
     // cnt(C)) with start(C) = sequences in longer classes, and items
@@ -110,9 +110,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
     // order -- by one wave with ballots over 64 sequences at a time.
     __shared__ int s_cls[kLptSeqs], s_cnt[kClasses], s_pick[3];
     const int t = threadIdx.x;
-    for (int c = t; c < kClasses; c += kPfThreads) s_cnt[c] = 0;
+    for (int c = t; c < kClasses; c += THREADS) s_cnt[c] = 0;
     __syncthreads();
-    for (int u = t; u < B; u += kPfThreads) {
+    for (int u = t; u < B; u += THREADS) {
       const int c = min(max(clamp_ctx(a, u), 0) >> kLenClassShift, kClasses - 1);
       s_cls[u] = c;
       atomicAdd(&s_cnt[c], 1);
@@ -172,6 +172,22 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
     zq = k / B;
     i = k - zq * B;
   }
+}
+
+// WIN: a sliding window is set (a.window > 0); without one every column's
+// first tile holds its key 0, so no column meets a fully masked tile before
+// its first key and the guards below are compiled out.
+template <class E, KvType KV, bool WIN>
+__global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
+  constexpr int D = 128;
+  using S = typename E::storage;
+  using Tile = KvTile<E, KV>;
+  using P = typename Tile::P;
+  const int g = blockIdx.x;
+  const int Z = gridDim.y;
+  const int k = (int)blockIdx.y + Z * (int)blockIdx.z;  // item index, 0 .. Z * B - 1
+  int i, zq;
+  pick_item<kPfThreads>(a, k, Z, i, zq);
   const int G = a.group, QT = kRows / G;  // chunk tokens per wave
   const int qa = a.query_start[i], qb = a.query_start[i + 1];
   if (qa < 0 || qb > a.num_tokens || qb <= qa) return;
@@ -400,9 +416,303 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
   }
 }
 
+// ----------------------------------------------------------------- shared K/V tiles
+// The same products with the K/V tiles of a step shared through LDS: eight
+// waves (two per SIMD) of 32 query rows each (two 16-column groups) take the
+// 256 / G chunk tokens of one item, and each 32-key step's two K/V tiles are
+// read from memory once per workgroup into a ring of three LDS buffers, one
+// barrier per step, three steps ahead: waves 0-3 load the K operands (two
+// 1 KiB pieces each, in KvTile's layout), waves 4 and 5 the V rows of one
+// tile each and store them already permuted into the P.V product's A
+// operands, so the byte permutes run once per workgroup, not once per wave.
+// Every wave runs every step of the workgroup's walk (keys 0 .. the item's
+// last position), computing only the steps its own rows reach.  16-bit
+// pools, no window.
+constexpr int kLdsWaves = 8;
+constexpr int kLdsThreads = kLdsWaves * kWave;
+constexpr int kLdsGroups = 2;
+constexpr int kLdsRows = 16 * kLdsGroups;  // query rows per wave
+constexpr int kLdsBufs = 3;
+constexpr int kLdsKPieces = 8;             // 1 KiB K pieces per step: tile-major, then k-step
+
+template <class E>
+__global__ __launch_bounds__(kLdsThreads) void prefill_mfma_lds(PrefillArgs a) {
+  constexpr int D = 128;
+  using S = typename E::storage;
+  using Tile = KvTile<E, KvType::kSame>;
+  __shared__ u32x4 s_k[kLdsBufs][kLdsKPieces][kWave];
+  __shared__ u32x4 s_vw[kLdsBufs][8][kWave];  // A operands of the 8 P.V products
+  __shared__ int s_ok[kLdsBufs][2];             // the step's tiles had blocks in the pool
+  const int g = blockIdx.x;
+  const int Z = gridDim.y;
+  const int k = (int)blockIdx.y + Z * (int)blockIdx.z;
+  int i, zq;
+  pick_item<kLdsThreads>(a, k, Z, i, zq);
+  const int G = a.group, QT = kLdsRows / G;  // chunk tokens per wave
+  const int qa = a.query_start[i], qb = a.query_start[i + 1];
+  if (qa < 0 || qb > a.num_tokens || qb <= qa) return;  // the whole workgroup
+  const int n = qb - qa, nq = min(n, a.max_query);
+  const int nqb = ceil_div(nq, QT);
+  const int top = nqb - 1 - kLdsWaves * zq;  // the item's latest query block
+  if (top < 0) return;                       // the whole workgroup
+  const int w = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int ctx = clamp_ctx(a, i);
+  // the workgroup's walk: keys [0, kend_wg), in 32-key steps
+  const int kend_wg = ctx - n + min(top * QT + QT, nq);
+  // this wave's block (none when blk < 0)
+  const int blk = top - w;
+  const int tok0 = blk * QT, ntok = blk >= 0 ? min(QT, nq - tok0) : 0;
+  const int pos0 = ctx - n + tok0;
+  const int kend = blk >= 0 ? pos0 + ntok : 0;
+  S* out = reinterpret_cast<S*>(a.out);
+
+  int lim[kLdsGroups], row[kLdsGroups];
+  bool live[kLdsGroups];
+#pragma unroll
+  for (int q = 0; q < kLdsGroups; ++q) {
+    const int col = q * 16 + c16, tl = col / G, h = col - tl * G;
+    live[q] = tl < ntok && pos0 + tl >= 0;
+    lim[q] = live[q] ? pos0 + tl : kend - 1;
+    row[q] = tl < ntok ? (qa + tok0 + tl) * a.num_q_heads + g * G + h : -1;
+  }
+  if (kend_wg <= 0) {  // every position of the item negative: zero rows
+#pragma unroll
+    for (int q = 0; q < kLdsGroups; ++q)
+      if (row[q] >= 0)
+        for (int d = 8 * g4; d < D; d += 32) *reinterpret_cast<u32x4*>(out + (size_t)row[q] * D + d) = u32x4{0, 0, 0, 0};
+    return;  // the whole workgroup
+  }
+  const bool mine = kend > 0;  // this wave has keys to attend
+
+  u32x4 qv[kLdsGroups][4];
+#pragma unroll
+  for (int q = 0; q < kLdsGroups; ++q) {
+    const S* qrow = reinterpret_cast<const S*>(a.q) + (size_t)max(row[q], 0) * D;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qv[q][s] = row[q] >= 0 ? *reinterpret_cast<const u32x4*>(qrow + Tile::q_elem(s, g4))
+                             : u32x4{0, 0, 0, 0};
+  }
+  const float c = fabsf(a.scale_log2), inv_c = 1.f / c;
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int q = 0; q < kLdsGroups; ++q)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qv[q][s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+
+  const int bs_mask = (1 << a.log2_bs) - 1;
+  const size_t head_stride = (size_t)D << a.log2_bs;
+  const size_t block_stride = head_stride * a.num_kv_heads;
+  const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
+  const S* kbase0 = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride;
+  const S* vbase0 = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride;
+  const int ntiles = ceil_div(kend_wg, kTile);
+  const int nsteps = ceil_div(ntiles, 2);
+  const int unmasked = max(pos0, 0);
+
+  // tile t of the walk: its block id when inside the pool, else -1
+  auto block_of = [&](int t) __attribute__((always_inline)) -> int {
+    if (t >= ntiles) return -1;
+    const int b = scalar_load(table + ((t * kTile) >> a.log2_bs));
+    return (unsigned)b < (unsigned)a.num_blocks ? b : -1;
+  };
+  // Loads of step st: waves 0-3 take K pieces 2 w, 2 w + 1 (tile j / 4,
+  // k-step j % 4); waves 4 and 5 take the four row groups of V tile w - 4
+  // (rows past the sequence read as zeros); waves 6 and 7 load nothing.
+  struct Stage {
+    u32x4 x0, x1, x2, x3;
+  };
+  // The block id each loading wave needs for its next step, read one step
+  // ahead (tile 2 st + tw of step st).
+  const int tw = w < 4 ? (w >> 1) : w - 4;
+  int next_b = w < 6 ? block_of(tw) : -1;
+  // ok: the wave's tile of the step had a block inside the pool
+  auto gload = [&](int st, int& ok) __attribute__((always_inline)) -> Stage {
+    Stage r = {};
+    const int b = next_b;
+    if (w < 6) next_b = block_of(2 * (st + 1) + tw);
+    ok = b >= 0;
+    if (w < 4) {
+      // pieces 2 w and 2 w + 1: tile w / 2, k-steps 2 (w % 2) and 2 (w % 2) + 1
+      const int t = 2 * st + (w >> 1);
+      const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
+      const rsrc_t rs = make_rsrc(kbase0 + off, b >= 0 ? Tile::kBytes : 0u);
+      const uint32_t lo = (uint32_t)(c16 * 128 + 8 * g4) * 2u + 128u * (w & 1);
+      r.x0 = buffer_load16(rs, lo);
+      r.x1 = buffer_load16(rs, lo + 64u);
+    } else if (w < 6) {
+      const int t = 2 * st + (w - 4);
+      const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
+      const uint32_t bytes = b >= 0 ? (uint32_t)min(kTile, ctx - t * kTile) * Tile::kRowBytes : 0u;
+      const rsrc_t rs = make_rsrc(vbase0 + off, bytes);
+      const uint32_t lo = (uint32_t)(4 * g4 * 128 + 8 * c16) * 2u;
+      r.x0 = buffer_load16(rs, lo);
+      r.x1 = buffer_load16(rs, lo + 256u);
+      r.x2 = buffer_load16(rs, lo + 512u);
+      r.x3 = buffer_load16(rs, lo + 768u);
+    }
+    return r;
+  };
+  auto lwrite = [&](int st, const Stage& r, int ok) __attribute__((always_inline)) {
+    const int bf = st % kLdsBufs;
+    if (w < 4) {
+      s_k[bf][2 * w][lane] = r.x0;
+      s_k[bf][2 * w + 1][lane] = r.x1;
+      if ((w & 1) == 0 && lane == 0) s_ok[bf][w >> 1] = ok;
+    } else if (w < 6) {
+      // A operand e of P.V: rows (0, 1) and (2, 3) of this tile, element e
+      // of the lane's 8 (components 2 (w - 4) and 2 (w - 4) + 1 of the
+      // operand: the first tile's keys, then the second's)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const u32x2 half = {__builtin_amdgcn_perm(r.x1[e >> 1], r.x0[e >> 1], sel),
+                            __builtin_amdgcn_perm(r.x3[e >> 1], r.x2[e >> 1], sel)};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(&s_vw[bf][e][lane]) + 2 * (w - 4)) = half;
+      }
+    }
+  };
+
+  float m[kLdsGroups], l[kLdsGroups];
+  f32x4 o[kLdsGroups][8];
+#pragma unroll
+  for (int q = 0; q < kLdsGroups; ++q) {
+    m[q] = kMFloor;
+    l[q] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One 32-key step from LDS buffer st % 3, as in prefill_mfma.
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const int k0 = 2 * st * kTile;
+    const int bf = st % kLdsBufs;
+    const bool oka = uni(s_ok[bf][0]) != 0, okb = uni(s_ok[bf][1]) != 0;
+    if (!oka && !okb) return;
+    u32x4 vw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vw[e] = s_vw[bf][e][lane];
+    const bool masked = k0 + 2 * kTile - 1 > unmasked || !oka || !okb;
+    float sv[kLdsGroups][8];
+    {
+      u32x4 ka[4], kb[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        ka[s] = s_k[bf][s][lane];
+        kb[s] = s_k[bf][4 + s][lane];
+      }
+#pragma unroll
+      for (int q = 0; q < kLdsGroups; ++q) {
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sa = Mfma<E>::qk(ka[s], qv[q][s], sa);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sb = Mfma<E>::qk(kb[s], qv[q][s], sb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sv[q][r] = sa[r];
+          sv[q][4 + r] = sb[r];
+        }
+      }
+    }
+    if (masked) {
+#pragma unroll
+      for (int q = 0; q < kLdsGroups; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = k0 + (j < 4 ? 0 : kTile) + 4 * g4 + (j & 3);
+          if (key > lim[q] || !(j < 4 ? oka : okb)) sv[q][j] = neg_inf();
+        }
+    }
+    float mt[kLdsGroups];
+    bool over = false;
+#pragma unroll
+    for (int q = 0; q < kLdsGroups; ++q) {
+      mt[q] = fmaxf(fmaxf(fmaxf(sv[q][0], sv[q][1]), fmaxf(sv[q][2], sv[q][3])),
+                    fmaxf(fmaxf(sv[q][4], sv[q][5]), fmaxf(sv[q][6], sv[q][7])));
+      over |= mt[q] > (m[q] + kRescaleSlack) * inv_c;
+    }
+    if (__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+      for (int q = 0; q < kLdsGroups; ++q) {
+        float x = fmaxf(mt[q], shfl_xor(mt[q], 16));
+        x = fmaxf(x, shfl_xor(x, 32));
+        const float mn = fmaxf(m[q], x * c);
+        const float alpha = fast_exp2(m[q] - mn);
+        l[q] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[q][e] *= alpha;
+        m[q] = mn;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kLdsGroups; ++q) {
+      float pf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[j] = fast_exp2(__builtin_fmaf(sv[q][j], c, -m[q]));
+      const u32x4 pw = {Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3]),
+                        Mfma<E>::round16x2(pf[4], pf[5]), Mfma<E>::round16x2(pf[6], pf[7])};
+      l[q] = sum2(E{}, pw[3], sum2(E{}, pw[2], sum2(E{}, pw[1], sum2(E{}, pw[0], l[q]))));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[q][e] = pv32(E{}, vw[e], pw, o[q][e]);
+    }
+  };
+
+  // The ring: step st's pieces go global -> registers two steps ahead and
+  // registers -> LDS one step ahead; the barrier after each write makes the
+  // step visible to every wave and frees the buffer written next.  All waves
+  // run the same steps, so every barrier is reached by the whole workgroup.
+  // Loads run three steps ahead in three register stages (step k in stage
+  // k % 3); the write to LDS waits only for its own stage's loads.
+  int ok0 = 0, ok1 = 0, ok2 = 0;
+  Stage r0 = gload(0, ok0), r1 = gload(1, ok1), r2 = gload(2, ok2);
+  lwrite(0, r0, ok0);
+  __syncthreads();
+  r0 = gload(3, ok0);
+  for (int st = 0; st < nsteps; st += 3) {
+    lwrite(st + 1, r1, ok1);
+    __syncthreads();
+    r1 = gload(st + 4, ok1);
+    if (mine && st * 2 * kTile < kend) compute(st);
+    if (st + 1 >= nsteps) break;
+    lwrite(st + 2, r2, ok2);
+    __syncthreads();
+    r2 = gload(st + 5, ok2);
+    if (mine && (st + 1) * 2 * kTile < kend) compute(st + 1);
+    if (st + 2 >= nsteps) break;
+    lwrite(st + 3, r0, ok0);
+    __syncthreads();
+    r0 = gload(st + 6, ok0);
+    if (mine && (st + 2) * 2 * kTile < kend) compute(st + 2);
+  }
+
+#pragma unroll
+  for (int q = 0; q < kLdsGroups; ++q) {
+    const float lsum = across_groups_sum<16>(l[q]);
+    if (row[q] < 0) continue;
+    const float inv = live[q] && lsum > 0.f ? a.v_scale / lsum : 0.f;
+    S* dst = out + (size_t)row[q] * D + 32 * g4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = float_to_bits(E{}, o[q][e][r] * inv);
+      *reinterpret_cast<u32x4*>(dst + 8 * r) =
+          u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+    }
+  }
+}
+
 template <class E, KvType KV>
 pa_status launch(const PrefillArgs& a, int max_query_blocks, hipStream_t st) {
   const dim3 grid(a.num_kv_heads, ceil_div(max_query_blocks, kPfWaves), a.num_seqs);
+  if (KV == KvType::kSame && a.window <= 0) {  // 16-bit pools, no window: shared tiles
+    hipLaunchKernelGGL((prefill_mfma_lds<E>), grid, dim3(kLdsThreads), 0, st, a);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  }
   if (a.window > 0)
     hipLaunchKernelGGL((prefill_mfma<E, KV, true>), grid, dim3(kPfThreads), 0, st, a);
   else
