@@ -38,10 +38,10 @@
 // sequence, the heaviest first.  A wave's work grows with its sequence's
 // length, so the items run longest sequence first: each workgroup ranks the
 // batch by length class (512 positions) with counts in LDS (up to kLptSeqs
-// sequences), and the sequences of one class run group-major (every
-// sequence's group 0, then group 1, ...).  Short sequences then fill the tail instead of long
-// sequences' last groups starting late.  Larger batches run group-major in
-// batch order.  The kv heads of an item are neighbouring ids, so each XCD
+// sequences); short sequences then fill the tail instead of long sequences'
+// last groups starting late.  Within a class a sequence's groups run back to
+// back, so the workgroups running together on an XCD share few sequences and
+// re-read their K/V from that XCD's L2.  Larger batches run in batch order.  The kv heads of an item are neighbouring ids, so each XCD
 // serves one kv head of every sequence and re-reads its K/V from its own L2.
 #include <hip/hip_runtime.h>
 
@@ -65,6 +65,12 @@ constexpr float kMFloor = -1.0e30f;         // initial running maximum
 constexpr int kLptSeqs = 4096;              // batches up to this size run longest first
 constexpr int kLenClassShift = 9;           // length classes of 512 positions
 constexpr int kClasses = 4 * 64;            // classes counted (longer ones share the top class)
+
+// Score maxima: the IEEE maximum, which gfx950 does as v_maximum3_f32 on the
+// MFMA results directly (fmaxf first quiets each operand with an extra
+// instruction).  A NaN operand would propagate, but scores here are finite or
+// already replaced by -inf where masked.
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // The P.V product over 32 keys (v_mfma_f32_16x16x32, both operands 8
 // elements per lane), and acc + both 16-bit values of a word (a dot product
@@ -97,7 +103,8 @@ __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
 
 // The item (sequence i, query-block group zq) of workgroup item index k (Z
 // groups per sequence): longest sequences first (length classes counted in
-// LDS), group-major within a class; batches above kLptSeqs in batch order.
+// LDS), a sequence's groups back to back within a class; batches above
+// kLptSeqs in batch order.
 // Every thread of the workgroup calls it (it has barriers).
 template <int THREADS>
 __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
@@ -105,7 +112,7 @@ __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
   if (B <= kLptSeqs) {
     // Classes are counted in LDS; class C holds ranks [start(C), start(C) +
     // cnt(C)) with start(C) = sequences in longer classes, and items
-    // [start * Z, (start + cnt) * Z), group-major.  The item's class is found
+    // [start * Z, (start + cnt) * Z), sequence by sequence.  The item's class is found
     // from the counts, then its sequence -- the j-th of the class in batch
     // order -- by one wave with ballots over 64 sequences at a time.
     __shared__ int s_cls[kLptSeqs], s_cnt[kClasses], s_pick[3];
@@ -150,8 +157,8 @@ __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
     __syncthreads();
     const int cls = s_pick[0], first = s_pick[1], cnt = s_cnt[cls];
     const int off = k - first * Z;
-    zq = off / cnt;
-    int j = off - zq * cnt;  // the j-th sequence of the class, in batch order
+    int j = off / Z;  // the j-th sequence of the class, in batch order
+    zq = off - j * Z;
     if (wave_id() == 0) {
       const int lane = threadIdx.x % kWave;
       for (int base = 0; base < B; base += kWave) {
@@ -169,8 +176,8 @@ __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
     __syncthreads();
     i = s_pick[2];
   } else {
-    zq = k / B;
-    i = k - zq * B;
+    i = k / Z;
+    zq = k - i * Z;
   }
 }
 
@@ -347,16 +354,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
     bool over = false;
 #pragma unroll
     for (int q = 0; q < kGroups; ++q) {
-      mt[q] = fmaxf(fmaxf(fmaxf(sv[q][0], sv[q][1]), fmaxf(sv[q][2], sv[q][3])),
-                    fmaxf(fmaxf(sv[q][4], sv[q][5]), fmaxf(sv[q][6], sv[q][7])));
+      mt[q] = smax(smax(smax(sv[q][0], sv[q][1]), smax(sv[q][2], sv[q][3])),
+                   smax(smax(sv[q][4], sv[q][5]), smax(sv[q][6], sv[q][7])));
       over |= mt[q] > (m[q] + kRescaleSlack) * inv_c;
     }
     if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
       for (int q = 0; q < kGroups; ++q) {
-        float x = fmaxf(mt[q], shfl_xor(mt[q], 16));
-        x = fmaxf(x, shfl_xor(x, 32));
-        const float mn = fmaxf(m[q], x * c);
+        float x = smax(mt[q], shfl_xor(mt[q], 16));
+        x = smax(x, shfl_xor(x, 32));
+        const float mn = smax(m[q], x * c);
         const float alpha = fast_exp2(m[q] - mn);
         l[q] *= alpha;
 #pragma unroll
@@ -417,18 +424,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
 }
 
 // ----------------------------------------------------------------- shared K/V tiles
-// The same products with the K/V tiles of a step shared through LDS: eight
-// waves (two per SIMD) of 32 query rows each (two 16-column groups) take the
-// 256 / G chunk tokens of one item, and each 32-key step's two K/V tiles are
-// read from memory once per workgroup into a ring of three LDS buffers, one
-// barrier per step, three steps ahead: waves 0-3 load the K operands (two
-// 1 KiB pieces each, in KvTile's layout), waves 4 and 5 the V rows of one
-// tile each and store them already permuted into the P.V product's A
-// operands, so the byte permutes run once per workgroup, not once per wave.
-// Every wave runs every step of the workgroup's walk (keys 0 .. the item's
-// last position), computing only the steps its own rows reach.  16-bit
-// pools, no window.
-constexpr int kLdsWaves = 8;
+// The same products with the K/V tiles of a step shared through LDS: four
+// waves of 32 query rows each (two 16-column groups) take the 128 / G chunk
+// tokens of one item, and each 32-key step's two K/V tiles are read from
+// memory once per workgroup into a ring of three LDS buffers, one barrier per
+// step, three steps ahead.  Wave w loads K pieces 2 w and 2 w + 1 (1 KiB
+// each, in KvTile's layout) and rows 2 (w % 2), 2 (w % 2) + 1 of every
+// four-row group of V tile w / 2, which it stores already permuted into the
+// P.V product's A operands, so the byte permutes run once per workgroup, not
+// once per wave.  Every wave runs every step of the workgroup's walk (keys
+// 0 .. the item's last position), computing only the steps its own rows
+// reach.  Two workgroups share a CU (two waves per SIMD) and, with a barrier
+// each, run out of step: one's softmax overlaps the other's products.
+// 16-bit pools, no window.
+constexpr int kLdsWaves = 4;
 constexpr int kLdsThreads = kLdsWaves * kWave;
 constexpr int kLdsGroups = 2;
 constexpr int kLdsRows = 16 * kLdsGroups;  // query rows per wave
@@ -436,7 +445,7 @@ constexpr int kLdsBufs = 3;
 constexpr int kLdsKPieces = 8;             // 1 KiB K pieces per step: tile-major, then k-step
 
 template <class E>
-__global__ __launch_bounds__(kLdsThreads) void prefill_mfma_lds(PrefillArgs a) {
+__global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_lds(PrefillArgs a) {
   constexpr int D = 128;
   using S = typename E::storage;
   using Tile = KvTile<E, KvType::kSame>;
@@ -519,60 +528,49 @@ __global__ __launch_bounds__(kLdsThreads) void prefill_mfma_lds(PrefillArgs a) {
     const int b = scalar_load(table + ((t * kTile) >> a.log2_bs));
     return (unsigned)b < (unsigned)a.num_blocks ? b : -1;
   };
-  // Loads of step st: waves 0-3 take K pieces 2 w, 2 w + 1 (tile j / 4,
-  // k-step j % 4); waves 4 and 5 take the four row groups of V tile w - 4
-  // (rows past the sequence read as zeros); waves 6 and 7 load nothing.
+  // Loads of step st: wave w takes K pieces 2 w, 2 w + 1 (piece j: tile
+  // j / 4, k-step j % 4) and its two V rows of each four-row group of tile
+  // w / 2 (rows past the sequence read as zeros).
   struct Stage {
     u32x4 x0, x1, x2, x3;
   };
-  // The block id each loading wave needs for its next step, read one step
+  // The block id each wave needs for its next step, read one step
   // ahead (tile 2 st + tw of step st).
-  const int tw = w < 4 ? (w >> 1) : w - 4;
-  int next_b = w < 6 ? block_of(tw) : -1;
+  const int tw = w >> 1;
+  int next_b = block_of(tw);
   // ok: the wave's tile of the step had a block inside the pool
   auto gload = [&](int st, int& ok) __attribute__((always_inline)) -> Stage {
     Stage r = {};
     const int b = next_b;
-    if (w < 6) next_b = block_of(2 * (st + 1) + tw);
+    next_b = block_of(2 * (st + 1) + tw);
     ok = b >= 0;
-    if (w < 4) {
-      // pieces 2 w and 2 w + 1: tile w / 2, k-steps 2 (w % 2) and 2 (w % 2) + 1
-      const int t = 2 * st + (w >> 1);
-      const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
-      const rsrc_t rs = make_rsrc(kbase0 + off, b >= 0 ? Tile::kBytes : 0u);
-      const uint32_t lo = (uint32_t)(c16 * 128 + 8 * g4) * 2u + 128u * (w & 1);
-      r.x0 = buffer_load16(rs, lo);
-      r.x1 = buffer_load16(rs, lo + 64u);
-    } else if (w < 6) {
-      const int t = 2 * st + (w - 4);
-      const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
-      const uint32_t bytes = b >= 0 ? (uint32_t)min(kTile, ctx - t * kTile) * Tile::kRowBytes : 0u;
-      const rsrc_t rs = make_rsrc(vbase0 + off, bytes);
-      const uint32_t lo = (uint32_t)(4 * g4 * 128 + 8 * c16) * 2u;
-      r.x0 = buffer_load16(rs, lo);
-      r.x1 = buffer_load16(rs, lo + 256u);
-      r.x2 = buffer_load16(rs, lo + 512u);
-      r.x3 = buffer_load16(rs, lo + 768u);
-    }
+    const int t = 2 * st + tw;
+    const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
+    // K pieces 2 w and 2 w + 1: tile w / 2, k-steps 2 (w % 2) and 2 (w % 2) + 1
+    const rsrc_t ks = make_rsrc(kbase0 + off, b >= 0 ? Tile::kBytes : 0u);
+    const uint32_t klo = (uint32_t)(c16 * 128 + 8 * g4) * 2u + 128u * (w & 1);
+    r.x0 = buffer_load16(ks, klo);
+    r.x1 = buffer_load16(ks, klo + 64u);
+    // V rows 4 g4 + 2 (w % 2) and the next, dims 8 c16 .. 8 c16 + 7
+    const uint32_t bytes = b >= 0 ? (uint32_t)min(kTile, ctx - t * kTile) * Tile::kRowBytes : 0u;
+    const rsrc_t vs = make_rsrc(vbase0 + off, bytes);
+    const uint32_t vlo = (uint32_t)(4 * g4 * 128 + 8 * c16) * 2u + 512u * (w & 1);
+    r.x2 = buffer_load16(vs, vlo);
+    r.x3 = buffer_load16(vs, vlo + 256u);
     return r;
   };
   auto lwrite = [&](int st, const Stage& r, int ok) __attribute__((always_inline)) {
     const int bf = st % kLdsBufs;
-    if (w < 4) {
-      s_k[bf][2 * w][lane] = r.x0;
-      s_k[bf][2 * w + 1][lane] = r.x1;
-      if ((w & 1) == 0 && lane == 0) s_ok[bf][w >> 1] = ok;
-    } else if (w < 6) {
-      // A operand e of P.V: rows (0, 1) and (2, 3) of this tile, element e
-      // of the lane's 8 (components 2 (w - 4) and 2 (w - 4) + 1 of the
-      // operand: the first tile's keys, then the second's)
+    s_k[bf][2 * w][lane] = r.x0;
+    s_k[bf][2 * w + 1][lane] = r.x1;
+    if ((w & 1) == 0 && lane == 0) s_ok[bf][w >> 1] = ok;
+    // Word 2 (w / 2) + w % 2 of P.V operand e (words 0, 1: the first tile's
+    // keys, 2, 3: the second's) pairs element e of the lane's 8 in the two rows.
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const u32x2 half = {__builtin_amdgcn_perm(r.x1[e >> 1], r.x0[e >> 1], sel),
-                            __builtin_amdgcn_perm(r.x3[e >> 1], r.x2[e >> 1], sel)};
-        *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(&s_vw[bf][e][lane]) + 2 * (w - 4)) = half;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      reinterpret_cast<uint32_t*>(&s_vw[bf][e][lane])[2 * (w >> 1) + (w & 1)] =
+          __builtin_amdgcn_perm(r.x3[e >> 1], r.x2[e >> 1], sel);
     }
   };
 
@@ -631,16 +629,16 @@ __global__ __launch_bounds__(kLdsThreads) void prefill_mfma_lds(PrefillArgs a) {
     bool over = false;
 #pragma unroll
     for (int q = 0; q < kLdsGroups; ++q) {
-      mt[q] = fmaxf(fmaxf(fmaxf(sv[q][0], sv[q][1]), fmaxf(sv[q][2], sv[q][3])),
-                    fmaxf(fmaxf(sv[q][4], sv[q][5]), fmaxf(sv[q][6], sv[q][7])));
+      mt[q] = smax(smax(smax(sv[q][0], sv[q][1]), smax(sv[q][2], sv[q][3])),
+                   smax(smax(sv[q][4], sv[q][5]), smax(sv[q][6], sv[q][7])));
       over |= mt[q] > (m[q] + kRescaleSlack) * inv_c;
     }
     if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
       for (int q = 0; q < kLdsGroups; ++q) {
-        float x = fmaxf(mt[q], shfl_xor(mt[q], 16));
-        x = fmaxf(x, shfl_xor(x, 32));
-        const float mn = fmaxf(m[q], x * c);
+        float x = smax(mt[q], shfl_xor(mt[q], 16));
+        x = smax(x, shfl_xor(x, 32));
+        const float mn = smax(m[q], x * c);
         const float alpha = fast_exp2(m[q] - mn);
         l[q] *= alpha;
 #pragma unroll
@@ -661,12 +659,12 @@ __global__ __launch_bounds__(kLdsThreads) void prefill_mfma_lds(PrefillArgs a) {
     }
   };
 
-  // The ring: step st's pieces go global -> registers two steps ahead and
-  // registers -> LDS one step ahead; the barrier after each write makes the
-  // step visible to every wave and frees the buffer written next.  All waves
-  // run the same steps, so every barrier is reached by the whole workgroup.
-  // Loads run three steps ahead in three register stages (step k in stage
-  // k % 3); the write to LDS waits only for its own stage's loads.
+  // The ring: step st's pieces go global -> registers three steps ahead, in
+  // three register stages (step k in stage k % 3), and registers -> LDS one
+  // step ahead; the write to LDS waits only for its own stage's loads, and
+  // the barrier after it makes the step visible to every wave and frees the
+  // buffer written next.  All waves run the same steps, so every barrier is
+  // reached by the whole workgroup.
   int ok0 = 0, ok1 = 0, ok2 = 0;
   Stage r0 = gload(0, ok0), r1 = gload(1, ok1), r2 = gload(2, ok2);
   lwrite(0, r0, ok0);
@@ -710,7 +708,9 @@ template <class E, KvType KV>
 pa_status launch(const PrefillArgs& a, int max_query_blocks, hipStream_t st) {
   const dim3 grid(a.num_kv_heads, ceil_div(max_query_blocks, kPfWaves), a.num_seqs);
   if (KV == KvType::kSame && a.window <= 0) {  // 16-bit pools, no window: shared tiles
-    hipLaunchKernelGGL((prefill_mfma_lds<E>), grid, dim3(kLdsThreads), 0, st, a);
+    const int lds_blocks = ceil_div(a.max_query, kLdsRows / a.group);
+    const dim3 lgrid(a.num_kv_heads, ceil_div(lds_blocks, kLdsWaves), a.num_seqs);
+    hipLaunchKernelGGL((prefill_mfma_lds<E>), lgrid, dim3(kLdsThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   if (a.window > 0)
