@@ -60,6 +60,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
   const int w = wave_id();
   const int lane = threadIdx.x % kWave;
   const int c16 = lane & 15, g4 = lane >> 4;
+  const int kswap = (g4 & 1) << 1;
   const int ctx = clamp_ctx(a, i);
   // the workgroup's walk: keys [0, kend_wg), in 32-key steps
   const int kend_wg = ctx - n + min(top * QT + QT, nq);
@@ -131,6 +132,12 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
   // ahead (tile 2 st + tw of step st).
   const int tw = w >> 1;
   int next_b = block_of(tw);
+  // Key order within a tile: K operand row i holds key krow(i), which swaps
+  // the row pairs (4a, 4a + 1) and (4a + 2, 4a + 3) for odd a.  S^T row
+  // 4 g4 + r is then key 4 g4 + (r ^ kswap), and the V words of odd lane
+  // groups are stored pair-swapped to match, so the two halves of a wave's
+  // 4-byte V-operand stores fall on different LDS banks.
+  const int krow = c16 ^ ((c16 >> 1) & 2);
   // ok: the wave's tile of the step had a block inside the pool
   auto gload = [&](int st, int& ok) __attribute__((always_inline)) -> Stage {
     Stage r = {};
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
     const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
     // K pieces 2 w and 2 w + 1: tile w / 2, k-steps 2 (w % 2) and 2 (w % 2) + 1
     const rsrc_t ks = make_rsrc(kbase0 + off, b >= 0 ? Tile::kBytes : 0u);
-    const uint32_t klo = (uint32_t)(c16 * 128 + 8 * g4) * 2u + 128u * (w & 1);
+    const uint32_t klo = (uint32_t)(krow * 128 + 8 * g4) * 2u + 128u * (w & 1);
     r.x0 = buffer_load16(ks, klo);
     r.x1 = buffer_load16(ks, klo + 64u);
     // V rows 4 g4 + 2 (w % 2) and the next, dims 8 c16 .. 8 c16 + 7
@@ -157,12 +164,13 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
     s_k[bf][2 * w][lane] = r.x0;
     s_k[bf][2 * w + 1][lane] = r.x1;
     if ((w & 1) == 0 && lane == 0) s_ok[bf][w >> 1] = ok;
-    // Word 2 (w / 2) + w % 2 of P.V operand e (words 0, 1: the first tile's
-    // keys, 2, 3: the second's) pairs element e of the lane's 8 in the two rows.
+    // Word 2 (w / 2) + (w % 2 ^ g4 % 2) of P.V operand e (words 0, 1: the
+    // first tile's keys, 2, 3: the second's) pairs element e of the lane's 8
+    // in the two rows (the key order of krow).
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      reinterpret_cast<uint32_t*>(&s_vw[bf][e][lane])[2 * (w >> 1) + (w & 1)] =
+      reinterpret_cast<uint32_t*>(&s_vw[bf][e][lane])[2 * (w >> 1) + ((w ^ g4) & 1)] =
           __builtin_amdgcn_perm(r.x3[e >> 1], r.x2[e >> 1], sel);
     }
   };
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
       for (int q = 0; q < kLdsGroups; ++q)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int key = k0 + (j < 4 ? 0 : kTile) + 4 * g4 + (j & 3);
+          const int key = k0 + (j < 4 ? 0 : kTile) + 4 * g4 + ((j & 3) ^ kswap);
           if (key > lim[q] || !(j < 4 ? oka : okb)) sv[q][j] = neg_inf();
         }
     }
