@@ -203,6 +203,10 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
         ka[s] = s_k[bf][s][lane];
         kb[s] = s_k[bf][4 + s][lane];
       }
+      // A wave issuing matrix products takes issue priority over the other
+      // workgroup's wave on its SIMD, whose vector instructions then fill
+      // the cycles the products leave free.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int q = 0; q < kLdsGroups; ++q) {
         f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -216,6 +220,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
           sv[q][4 + r] = sb[r];
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (masked) {
 #pragma unroll
@@ -247,6 +252,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
         m[q] = mn;
       }
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int q = 0; q < kLdsGroups; ++q) {
       float pf[8];
@@ -258,6 +264,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[q][e] = pv32(E{}, vw[e], pw, o[q][e]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // The ring: step st's pieces go global -> registers three steps ahead, in
