@@ -226,24 +226,35 @@ def measure_prefill(reps: int, log):
     args = (q, cache.k_pool, cache.v_pool, torch.from_numpy(tables).cuda(), qs,
             torch.from_numpy(lens_i).cuda(), wl.scale, out, int(d.step_lens.max()),
             int(lens.max()))
-    for _ in range(3):
-        pa.pa_prefill(*args)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for a, b in ev:
-        a.record(stream)
-        pa.pa_prefill(*args)
-        b.record(stream)
-    torch.cuda.synchronize()
-    us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    # causal work: row at position p attends p + 1 keys; 2 flops per
-    # multiply-add in each of Q K^T and P V
-    seen = sum(int(((L - c) + np.arange(c) + 1).sum()) for L, c in zip(lens, d.step_lens))
-    flops = 4 * wl.head_dim * wl.num_q_heads * seen
+
+    def timed(window: int) -> float:
+        for _ in range(3):
+            pa.pa_prefill(*args, sliding_window=window)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            pa.pa_prefill(*args, sliding_window=window)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    def attended(window: int) -> int:
+        # row at position p attends p + 1 keys, at most `window` with a window
+        pos1 = [(L - c) + np.arange(c) + 1 for L, c in zip(lens, d.step_lens)]
+        return sum(int((np.minimum(p, window) if window > 0 else p).sum()) for p in pos1)
+
+    us = timed(0)
+    # 2 flops per multiply-add in each of Q K^T and P V
+    flops = 4 * wl.head_dim * wl.num_q_heads * attended(0)
     tflops = flops / (us * 1e-6) / 1e12
     tokens = int(d.step_lens.sum())
     log(f"prefill: {us:.1f} us, {tflops:.1f} TFLOP/s, {tokens / (us * 1e-6):.0f} tokens/s")
+    us_w = timed(VARIANT_WINDOW)
+    flops_w = 4 * wl.head_dim * wl.num_q_heads * attended(VARIANT_WINDOW)
+    tflops_w = flops_w / (us_w * 1e-6) / 1e12
+    log(f"prefill window_{VARIANT_WINDOW}: {us_w:.1f} us, {tflops_w:.1f} TFLOP/s")
     return {
         "workload": PREFILL_DESCRIPTION,
         "kernel_us": round(us, 2),
@@ -252,6 +263,9 @@ def measure_prefill(reps: int, log):
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "algorithmic_flops": flops},
+        f"window_{VARIANT_WINDOW}": {
+            "kernel_us": round(us_w, 2), "achieved": round(tflops_w, 1), "unit": "TFLOP/s",
+            "frac": round(tflops_w / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops_w},
     }
 
 

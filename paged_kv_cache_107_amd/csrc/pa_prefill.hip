@@ -24,10 +24,10 @@
 // branch between the rescale test and the P.V product.
 //
 // Two kernels compute this step.  prefill_mfma_lds (pa_prefill_lds.hip;
-// 16-bit pools, no window) runs four waves of 32 rows per item, two
-// workgroups per CU, and shares each step's K/V tiles through LDS;
-// prefill_mfma (this file; windows, 8-bit pools) gives each of four waves 64
-// rows and its own register ring of tiles.
+// 16-bit pools) runs four waves of 32 rows per item, two workgroups per CU,
+// and shares each step's K/V tiles through LDS; prefill_mfma (this file;
+// 8-bit pools) gives each of four waves 64 rows and its own register ring of
+// tiles.
 //
 // With a sliding window of W positions a row at position p attends only
 // positions p - W + 1 .. p: the wave starts at the tile of its first row's
@@ -330,11 +330,9 @@ pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, hipStream_t
   const int blocks = prefill_query_blocks(a.max_query, a.group);
   if (blocks <= 0) return PA_OK;
   const bool fp8 = kv == KvType::kFp8;
-  if (!fp8 && a.window <= 0) return launch_prefill_lds(a, dtype, st);
-  if (dtype == PA_BF16)
-    return fp8 ? launch<BF16, KvType::kFp8>(a, blocks, st) : launch<BF16, KvType::kSame>(a, blocks, st);
-  if (dtype == PA_F16)
-    return fp8 ? launch<F16, KvType::kFp8>(a, blocks, st) : launch<F16, KvType::kSame>(a, blocks, st);
+  if (!fp8) return launch_prefill_lds(a, dtype, st);  // 16-bit pools: shared tiles
+  if (dtype == PA_BF16) return launch<BF16, KvType::kFp8>(a, blocks, st);
+  if (dtype == PA_F16) return launch<F16, KvType::kFp8>(a, blocks, st);
   return PA_ERR_SHAPE;
 }
 

@@ -1,5 +1,5 @@
 // Chunked-prefill attention with the K/V tiles of each step shared through
-// LDS (16-bit pools, no sliding window).  The step (S^T = K . Q^T and
+// LDS (16-bit pools, with or without a sliding window).  The step (S^T = K . Q^T and
 // O^T += V^T . P^T on v_mfma_f32_16x16x32 over 32 keys, the lazy softmax
 // rescale), the item order and the grid are those described at the top of
 // pa_prefill.hip; pages as cited there.  This file is compiled with LLVM's
@@ -29,7 +29,10 @@ using namespace prefill;
 // 0 .. the item's last position), computing only the steps its own rows
 // reach.  Two workgroups share a CU (two waves per SIMD) and, with a barrier
 // each, run out of step: one's softmax overlaps the other's products.
-// 16-bit pools, no window.
+// 16-bit pools.  With a sliding window of W positions (WIN) the walk starts
+// at the window of the item's earliest row, each wave computes only the
+// steps its rows' windows reach, and keys below a row's window are masked
+// per element.
 constexpr int kLdsWaves = 4;
 constexpr int kLdsThreads = kLdsWaves * kWave;
 constexpr int kLdsGroups = 2;
@@ -37,7 +40,7 @@ constexpr int kLdsRows = 16 * kLdsGroups;  // query rows per wave
 constexpr int kLdsBufs = 3;
 constexpr int kLdsKPieces = 8;             // 1 KiB K pieces per step: tile-major, then k-step
 
-template <class E>
+template <class E, bool WIN>
 __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_lds(PrefillArgs a) {
   constexpr int D = 128;
   using S = typename E::storage;
@@ -115,6 +118,12 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
   const int ntiles = ceil_div(kend_wg, kTile);
   const int nsteps = ceil_div(ntiles, 2);
   const int unmasked = max(pos0, 0);
+  // With a window: the walk starts at the step holding the first key of the
+  // item's earliest row's window; this wave's rows reach back to kbeg.
+  const int W = WIN ? a.window : 0;
+  const int st_begin =
+      WIN ? max(max(ctx - n + max(top - (kLdsWaves - 1), 0) * QT, 0) - W + 1, 0) / (2 * kTile) : 0;
+  const int kbeg = WIN ? max(unmasked - W + 1, 0) : 0;
 
   // tile t of the walk: its block id when inside the pool, else -1
   auto block_of = [&](int t) __attribute__((always_inline)) -> int {
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
   // The block id each wave needs for its next step, read one step
   // ahead (tile 2 st + tw of step st).
   const int tw = w >> 1;
-  int next_b = block_of(tw);
+  int next_b = block_of(2 * st_begin + tw);
   // Key order within a tile: K operand row i holds key krow(i), which swaps
   // the row pairs (4a, 4a + 1) and (4a + 2, 4a + 3) for odd a.  S^T row
   // 4 g4 + r is then key 4 g4 + (r ^ kswap), and the V words of odd lane
@@ -194,7 +203,8 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
     u32x4 vw[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) vw[e] = s_vw[bf][e][lane];
-    const bool masked = k0 + 2 * kTile - 1 > unmasked || !oka || !okb;
+    const bool masked =
+        k0 + 2 * kTile - 1 > unmasked || (WIN && k0 < kend - W) || !oka || !okb;
     float sv[kLdsGroups][8];
     {
       u32x4 ka[4], kb[4];
@@ -228,7 +238,8 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int key = k0 + (j < 4 ? 0 : kTile) + 4 * g4 + ((j & 3) ^ kswap);
-          if (key > lim[q] || !(j < 4 ? oka : okb)) sv[q][j] = neg_inf();
+          if (key > lim[q] || (WIN && key <= lim[q] - W) || !(j < 4 ? oka : okb))
+            sv[q][j] = neg_inf();
         }
     }
     float mt[kLdsGroups];
@@ -273,26 +284,31 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
   // the barrier after it makes the step visible to every wave and frees the
   // buffer written next.  All waves run the same steps, so every barrier is
   // reached by the whole workgroup.
+  // this wave computes step st: its rows reach keys [kbeg, kend)
+  auto runs = [&](int st) __attribute__((always_inline)) {
+    return mine && st * 2 * kTile < kend && (!WIN || (st + 1) * 2 * kTile > kbeg);
+  };
+  const int s0 = st_begin;
   int ok0 = 0, ok1 = 0, ok2 = 0;
-  Stage r0 = gload(0, ok0), r1 = gload(1, ok1), r2 = gload(2, ok2);
-  lwrite(0, r0, ok0);
+  Stage r0 = gload(s0, ok0), r1 = gload(s0 + 1, ok1), r2 = gload(s0 + 2, ok2);
+  lwrite(s0, r0, ok0);
   __syncthreads();
-  r0 = gload(3, ok0);
-  for (int st = 0; st < nsteps; st += 3) {
+  r0 = gload(s0 + 3, ok0);
+  for (int st = s0; st < nsteps; st += 3) {
     lwrite(st + 1, r1, ok1);
     __syncthreads();
     r1 = gload(st + 4, ok1);
-    if (mine && st * 2 * kTile < kend) compute(st);
+    if (runs(st)) compute(st);
     if (st + 1 >= nsteps) break;
     lwrite(st + 2, r2, ok2);
     __syncthreads();
     r2 = gload(st + 5, ok2);
-    if (mine && (st + 1) * 2 * kTile < kend) compute(st + 1);
+    if (runs(st + 1)) compute(st + 1);
     if (st + 2 >= nsteps) break;
     lwrite(st + 3, r0, ok0);
     __syncthreads();
     r0 = gload(st + 6, ok0);
-    if (mine && (st + 2) * 2 * kTile < kend) compute(st + 2);
+    if (runs(st + 2)) compute(st + 2);
   }
 
 #pragma unroll
@@ -317,7 +333,10 @@ pa_status launch_lds(const PrefillArgs& a, hipStream_t st) {
   const int blocks = ceil_div(a.max_query, kLdsRows / a.group);
   if (blocks <= 0) return PA_OK;
   const dim3 grid(a.num_kv_heads, ceil_div(blocks, kLdsWaves), a.num_seqs);
-  hipLaunchKernelGGL((prefill_mfma_lds<E>), grid, dim3(kLdsThreads), 0, st, a);
+  if (a.window > 0)
+    hipLaunchKernelGGL((prefill_mfma_lds<E, true>), grid, dim3(kLdsThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_mfma_lds<E, false>), grid, dim3(kLdsThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

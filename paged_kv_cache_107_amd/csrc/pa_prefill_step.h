@@ -138,7 +138,7 @@ __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
 
 }  // namespace prefill
 
-// Launches prefill_mfma_lds (16-bit pools, no sliding window).
+// Launches prefill_mfma_lds (16-bit pools).
 pa_status launch_prefill_lds(const PrefillArgs& a, int dtype, hipStream_t st);
 
 }  // namespace pa
