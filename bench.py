@@ -228,14 +228,14 @@ def measure_prefill(reps: int, log):
             int(lens.max()))
     stream = torch.cuda.current_stream()
 
-    def timed(window: int) -> float:
+    def timed(window: int, call_args=args, **kw) -> float:
         for _ in range(3):
-            pa.pa_prefill(*args, sliding_window=window)
+            pa.pa_prefill(*call_args, sliding_window=window, **kw)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
         for a, b in ev:
             a.record(stream)
-            pa.pa_prefill(*args, sliding_window=window)
+            pa.pa_prefill(*call_args, sliding_window=window, **kw)
             b.record(stream)
         torch.cuda.synchronize()
         return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
@@ -255,6 +255,14 @@ def measure_prefill(reps: int, log):
     flops_w = 4 * wl.head_dim * wl.num_q_heads * attended(VARIANT_WINDOW)
     tflops_w = flops_w / (us_w * 1e-6) / 1e12
     log(f"prefill window_{VARIANT_WINDOW}: {us_w:.1f} us, {tflops_w:.1f} TFLOP/s")
+    # 8-bit E4M3 pools of the same shape (random finite codes: the time does
+    # not depend on the values), same attended keys
+    codes = tuple(torch.randint(0, 0x78, shape, generator=gen, device="cuda", dtype=torch.uint8)
+                  .view(torch.float8_e4m3fn) for _ in range(2))
+    us_8 = timed(0, (q, *codes) + args[3:], kv_scales=FP8_SCALES)
+    tflops_8 = flops / (us_8 * 1e-6) / 1e12
+    log(f"prefill fp8_e4m3: {us_8:.1f} us, {tflops_8:.1f} TFLOP/s")
+    del codes
     return {
         "workload": PREFILL_DESCRIPTION,
         "kernel_us": round(us, 2),
@@ -266,6 +274,9 @@ def measure_prefill(reps: int, log):
         f"window_{VARIANT_WINDOW}": {
             "kernel_us": round(us_w, 2), "achieved": round(tflops_w, 1), "unit": "TFLOP/s",
             "frac": round(tflops_w / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops_w},
+        "fp8_e4m3": {
+            "kernel_us": round(us_8, 2), "achieved": round(tflops_8, 1), "unit": "TFLOP/s",
+            "frac": round(tflops_8 / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops},
     }
 
 

@@ -20,26 +20,21 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
 ARCH = "gfx950"
-SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_prefill_lds.hip", "pa_cache.hip",
-           "pa_alloc.cpp"]
+SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cache.hip", "pa_alloc.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.  The host pass
 # does not know the feature and says so; that warning is harmless.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs (not AGPRs), so the
 # softmax rescale of the output accumulators needs no register copies.  (For
-# the prefill kernel the default AGPR form measured 17% slower: the compiler
-# moved its 128 accumulators between the register files every tile.)
+# an earlier prefill kernel with 128 accumulators per wave the default AGPR
+# form measured 17% slower: the compiler moved them between the register
+# files every tile.)
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 AGPR_FORM_SOURCES = set()
-# Per-source scheduler choice.  The per-wave prefill kernel (pa_prefill.hip)
-# holds more live values than fit in 256 VGPRs (128 output accumulators, a
-# 4-tile K/V ring, q operands); the register-pressure-first scheduler keeps
-# fewer of them in AGPRs and copies fewer between register files, which
-# measured 10% faster than the default on the 8B chunked-prefill workload
-# (474 vs 528 us).  The LDS-shared prefill kernel (pa_prefill_lds.hip) fits
-# in 256 VGPRs either way and is 2-6% faster with the default scheduler.
-SOURCE_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]}
+# Per-source extra flags (none at present: the prefill kernel fits in 256
+# VGPRs and is fastest with LLVM's default machine scheduler).
+SOURCE_FLAGS: dict = {}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 

@@ -10,119 +10,256 @@
 // sequence and to itself (the autoregressive rule of the same §2.1).  K/V
 // rows are found through the block table as in decode.
 //
-// Work split: one wave per (sequence, kv head, block of query tokens).  The
-// G query heads of the kv head and 64 / G consecutive chunk tokens make 64
-// query rows, taken as four groups of 16: each group is the 16 columns of the
-// decode kernel's tile products (S^T = K . Q^T with v_mfma_f32_16x16x32), so
-// one K/V tile load feeds four groups' products.  A wave walks the 16-key
-// tiles from position 0 to its last token two at a time through a register
-// ring of two pairs; with 32 keys per step the P.V product also runs on the
-// double-rate v_mfma_f32_16x16x32 (O^T += V^T . P^T).  The steps at and past
-// the block's first position are masked per element.  Each lane keeps the
-// softmax state of its column in each group, with the decode kernel's lazy
-// rescale; the running maximum starts at a finite floor, so a step has no
-// branch between the rescale test and the P.V product.
-//
-// Two kernels compute this step.  prefill_mfma_lds (pa_prefill_lds.hip;
-// 16-bit pools) runs four waves of 32 rows per item, two workgroups per CU,
-// and shares each step's K/V tiles through LDS; prefill_mfma (this file;
-// 8-bit pools) gives each of four waves 64 rows and its own register ring of
-// tiles.
+// The step: the G query heads of a kv head and 32 / G consecutive chunk
+// tokens make a wave's 32 query rows, taken as two groups of 16; each group
+// is the 16 columns of the decode kernel's tile products (S^T = K . Q^T with
+// v_mfma_f32_16x16x32), so one K/V tile feeds both groups' products.  Keys
+// are walked 32 at a time (two 16-key tiles); with 32 keys per step the P.V
+// product also runs on the double-rate v_mfma_f32_16x16x32 (O^T += V^T .
+// P^T).  Steps at and past the rows' first position are masked per element.
+// Each lane keeps the softmax state of its column in each group, with the
+// decode kernel's lazy rescale; the running maximum starts at a finite
+// floor, so a step has no branch between the rescale test and the P.V
+// product.
 //
 // With a sliding window of W positions a row at position p attends only
-// positions p - W + 1 .. p: the wave starts at the tile of its first row's
-// window and masks per element below each row's window as well.  8-bit pools
-// are widened to the 16-bit operand type as the tiles are used (KvTile).
+// positions p - W + 1 .. p.  8-bit pools are widened to the 16-bit operand
+// type as their tiles are stored into LDS (the codes as KvTile<E, kFp8>
+// orders them).
 //
 // Grid: kv head x, then a flat item index k over (sequence, query-block
-// group z); with four waves per workgroup group z takes query blocks
-// nqb-1-4z .. nqb-4-4z of its sequence, the heaviest first.  A wave's work grows with its sequence's
-// length, so the items run longest sequence first: each workgroup ranks the
-// batch by length class (512 positions) with counts in LDS (up to kLptSeqs
-// sequences); short sequences then fill the tail instead of long sequences'
-// last groups starting late.  Within a class a sequence's groups run back to
-// back, so the workgroups running together on an XCD share few sequences and
-// re-read their K/V from that XCD's L2.  Larger batches run in batch order.
-// The kv heads of an item are neighbouring ids, so each XCD serves one kv
-// head of every sequence.
+// group z); group z takes query blocks nqb-1-4z .. nqb-4-4z of its sequence
+// (one per wave), the heaviest first.  A workgroup's work grows with its
+// sequence's length, so the items run longest sequence first: each
+// workgroup ranks the batch by length class (512 positions) with counts in
+// LDS (up to kLptSeqs sequences); short sequences then fill the tail instead
+// of long sequences' last groups starting late.  Within a class a
+// sequence's groups run back to back, so the workgroups running together on
+// an XCD share few sequences and re-read their K/V from that XCD's L2.
+// Larger batches run in batch order.  The kv heads of an item are
+// neighbouring ids, so each XCD serves one kv head of every sequence.
 #include <hip/hip_runtime.h>
 
 #include "pa.h"
 #include "pa_device.h"
 #include "pa_internal.h"
-#include "pa_prefill_step.h"
 
 namespace pa {
 namespace {
 
-using namespace prefill;
+constexpr int kTile = 16;                   // keys per tile
+constexpr float kRescaleSlack = 8.f;        // log2 units
+constexpr float kMFloor = -1.0e30f;         // initial running maximum
+constexpr int kLptSeqs = 4096;              // batches up to this size run longest first
+constexpr int kLenClassShift = 9;           // length classes of 512 positions
+constexpr int kClasses = 4 * 64;            // classes counted (longer ones share the top class)
 
-constexpr int kPfWaves = 4;                 // waves per workgroup
-constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kGroups = 4;                  // 16-column groups per wave
-constexpr int kRows = 16 * kGroups;         // query rows (token, head) per wave
-constexpr int kPfPairs = 2;                 // tile pairs in the register ring
+// Score maxima: the IEEE maximum, which gfx950 does as v_maximum3_f32 on the
+// MFMA results directly (fmaxf first quiets each operand with an extra
+// instruction).  A NaN operand would propagate, but scores here are finite or
+// already replaced by -inf where masked.
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-// WIN: a sliding window is set (a.window > 0); without one every column's
-// first tile holds its key 0, so no column meets a fully masked tile before
-// its first key and the guards below are compiled out.
+// The P.V product over 32 keys (v_mfma_f32_16x16x32, both operands 8
+// elements per lane), and acc + both 16-bit values of a word (a dot product
+// with (1, 1)).
+__device__ __forceinline__ f32x4 pv32(BF16, u32x4 v, u32x4 p, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v),
+                                                 __builtin_bit_cast(bf16x8, p), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 pv32(F16, u32x4 v, u32x4 p, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, v),
+                                                __builtin_bit_cast(f16x8, p), c, 0, 0, 0);
+}
+__device__ __forceinline__ float sum2(BF16, uint32_t w, float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w),
+                                         __builtin_bit_cast(b2, 0x3F803F80u), acc, false);
+}
+__device__ __forceinline__ float sum2(F16, uint32_t w, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), __builtin_bit_cast(h2, 0x3C003C00u),
+                                acc, false);
+}
+
+__device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
+  int ctx = a.context_lens[i];
+  ctx = min(ctx, a.max_ctx);
+  ctx = min(ctx, a.max_blocks << a.log2_bs);
+  return ctx;
+}
+
+// The item (sequence i, query-block group zq) of workgroup item index k (Z
+// groups per sequence): longest sequences first (length classes counted in
+// LDS), a sequence's groups back to back within a class; batches above
+// kLptSeqs in batch order.
+// Every thread of the workgroup calls it (it has barriers).
+template <int THREADS>
+__device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
+  const int B = a.num_seqs;
+  if (B <= kLptSeqs) {
+    // Classes are counted in LDS; class C holds ranks [start(C), start(C) +
+    // cnt(C)) with start(C) = sequences in longer classes, and items
+    // [start * Z, (start + cnt) * Z), sequence by sequence.  The item's class is found
+    // from the counts, then its sequence -- the j-th of the class in batch
+    // order -- by one wave with ballots over 64 sequences at a time.
+    __shared__ int s_cls[kLptSeqs], s_cnt[kClasses], s_pick[3];
+    const int t = threadIdx.x;
+    for (int c = t; c < kClasses; c += THREADS) s_cnt[c] = 0;
+    __syncthreads();
+    for (int u = t; u < B; u += THREADS) {
+      const int c = min(max(clamp_ctx(a, u), 0) >> kLenClassShift, kClasses - 1);
+      s_cls[u] = c;
+      atomicAdd(&s_cnt[c], 1);
+    }
+    __syncthreads();
+    // Wave 0: lane l holds the counts of classes 255 - 4l .. 252 - 4l (the
+    // descending order), a wave-wide scan gives each class's first rank, and
+    // the lane holding the item's rank finds its class; then the class's j-th
+    // sequence is found with ballots.
+    const int rr = k / Z;  // the item's rank
+    if (wave_id() == 0) {
+      const int lane = threadIdx.x % kWave;
+      int cnt4[4], own = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cnt4[e] = s_cnt[kClasses - 1 - (4 * lane + e)];
+        own += cnt4[e];
+      }
+      int incl = own;  // inclusive scan over lanes
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int x = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += x;
+      }
+      int first = incl - own;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (cnt4[e] > 0 && rr >= first && rr < first + cnt4[e]) {
+          s_pick[0] = kClasses - 1 - (4 * lane + e);
+          s_pick[1] = first;
+        }
+        first += cnt4[e];
+      }
+    }
+    __syncthreads();
+    const int cls = s_pick[0], first = s_pick[1], cnt = s_cnt[cls];
+    const int off = k - first * Z;
+    int j = off / Z;  // the j-th sequence of the class, in batch order
+    zq = off - j * Z;
+    if (wave_id() == 0) {
+      const int lane = threadIdx.x % kWave;
+      for (int base = 0; base < B; base += kWave) {
+        const int u = base + lane;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(u < B && s_cls[u] == cls);
+        const int n = __builtin_popcountll(hit);
+        if (j < n) {
+          const uint64_t below = lane ? hit & (~0ull >> (64 - lane)) : 0ull;
+          if (((hit >> lane) & 1ull) && __builtin_popcountll(below) == j) s_pick[2] = u;
+          break;
+        }
+        j -= n;
+      }
+    }
+    __syncthreads();
+    i = s_pick[2];
+  } else {
+    i = k / Z;
+    zq = k - i * Z;
+  }
+}
+
+// Kernel: the K/V tiles of a step are shared through LDS.  Four
+// waves of 32 query rows each (two 16-column groups) take the 128 / G chunk
+// tokens of one item, and each 32-key step's two K/V tiles are read from
+// memory once per workgroup into a ring of three LDS buffers, one barrier per
+// step, three steps ahead.  Wave w loads K pieces 2 w and 2 w + 1 (1 KiB
+// each, in KvTile's layout) and rows 2 (w % 2), 2 (w % 2) + 1 of every
+// four-row group of V tile w / 2, which it stores already permuted into the
+// P.V product's A operands, so the byte permutes run once per workgroup, not
+// once per wave.  Every wave runs every step of the workgroup's walk (keys
+// 0 .. the item's last position), computing only the steps its own rows
+// reach.  Two workgroups share a CU (two waves per SIMD) and, with a barrier
+// each, run out of step: one's softmax overlaps the other's products.
+// 16-bit pools.  With a sliding window of W positions (WIN) the walk starts
+// at the window of the item's earliest row, each wave computes only the
+// steps its rows' windows reach, and keys below a row's window are masked
+// per element.
+constexpr int kLdsWaves = 4;
+constexpr int kLdsThreads = kLdsWaves * kWave;
+constexpr int kLdsGroups = 2;
+constexpr int kLdsRows = 16 * kLdsGroups;  // query rows per wave
+constexpr int kLdsBufs = 3;
+constexpr int kLdsKPieces = 8;             // 1 KiB K pieces per step: tile-major, then k-step
+
 template <class E, KvType KV, bool WIN>
-__global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
+__global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_lds(PrefillArgs a) {
   constexpr int D = 128;
   using S = typename E::storage;
   using Tile = KvTile<E, KV>;
-  using P = typename Tile::P;
+  using P = typename Tile::P;  // pool element: 16-bit value or E4M3 code
+  __shared__ u32x4 s_k[kLdsBufs][kLdsKPieces][kWave];
+  __shared__ u32x4 s_vw[kLdsBufs][8][kWave];  // A operands of the 8 P.V products
+  __shared__ int s_ok[kLdsBufs][2];             // the step's tiles had blocks in the pool
   const int g = blockIdx.x;
   const int Z = gridDim.y;
-  const int k = (int)blockIdx.y + Z * (int)blockIdx.z;  // item index, 0 .. Z * B - 1
+  const int k = (int)blockIdx.y + Z * (int)blockIdx.z;
   int i, zq;
-  pick_item<kPfThreads>(a, k, Z, i, zq);
-  const int G = a.group, QT = kRows / G;  // chunk tokens per wave
+  pick_item<kLdsThreads>(a, k, Z, i, zq);
+  const int G = a.group, QT = kLdsRows / G;  // chunk tokens per wave
   const int qa = a.query_start[i], qb = a.query_start[i + 1];
-  if (qa < 0 || qb > a.num_tokens || qb <= qa) return;
-  const int n = qb - qa;                   // chunk tokens: positions ctx - n ..
-  const int nqb = ceil_div(min(n, a.max_query), QT);  // rows past max_query are not run
-  const int blk = nqb - 1 - (zq * kPfWaves + wave_id());
-  if (blk < 0) return;
+  if (qa < 0 || qb > a.num_tokens || qb <= qa) return;  // the whole workgroup
+  const int n = qb - qa, nq = min(n, a.max_query);
+  const int nqb = ceil_div(nq, QT);
+  const int top = nqb - 1 - kLdsWaves * zq;  // the item's latest query block
+  if (top < 0) return;                       // the whole workgroup
+  const int w = wave_id();
   const int lane = threadIdx.x % kWave;
   const int c16 = lane & 15, g4 = lane >> 4;
+  const int kswap = (g4 & 1) << 1;
   const int ctx = clamp_ctx(a, i);
-  const int tok0 = blk * QT, ntok = min(QT, min(n, a.max_query) - tok0);
-  const int pos0 = ctx - n + tok0;  // position of the block's first token
-  const int kend = pos0 + ntok;     // keys [0, kend) are seen by some row
+  // the workgroup's walk: keys [0, kend_wg), in 32-key steps
+  const int kend_wg = ctx - n + min(top * QT + QT, nq);
+  // this wave's block (none when blk < 0)
+  const int blk = top - w;
+  const int tok0 = blk * QT, ntok = blk >= 0 ? min(QT, nq - tok0) : 0;
+  const int pos0 = ctx - n + tok0;
+  const int kend = blk >= 0 ? pos0 + ntok : 0;
+  S* out = reinterpret_cast<S*>(a.out);
 
-  // This lane's column in each group: chunk token tl, head h of the group.
-  // lim = last position the column sees; rows without a query (past the
-  // chunk, or at a negative position) see every key like the last row, which
-  // keeps their state finite; they are never stored as attention outputs.
-  int lim[kGroups], row[kGroups];
-  bool live[kGroups];
+  int lim[kLdsGroups], row[kLdsGroups];
+  bool live[kLdsGroups];
 #pragma unroll
-  for (int q = 0; q < kGroups; ++q) {
+  for (int q = 0; q < kLdsGroups; ++q) {
     const int col = q * 16 + c16, tl = col / G, h = col - tl * G;
     live[q] = tl < ntok && pos0 + tl >= 0;
     lim[q] = live[q] ? pos0 + tl : kend - 1;
     row[q] = tl < ntok ? (qa + tok0 + tl) * a.num_q_heads + g * G + h : -1;
   }
-  S* out = reinterpret_cast<S*>(a.out);
-  if (kend <= 0) {  // every position negative: zero rows
+  if (kend_wg <= 0) {  // every position of the item negative: zero rows
 #pragma unroll
-    for (int q = 0; q < kGroups; ++q)
+    for (int q = 0; q < kLdsGroups; ++q)
       if (row[q] >= 0)
         for (int d = 8 * g4; d < D; d += 32) *reinterpret_cast<u32x4*>(out + (size_t)row[q] * D + d) = u32x4{0, 0, 0, 0};
-    return;
+    return;  // the whole workgroup
   }
+  const bool mine = kend > 0;  // this wave has keys to attend
 
-  // q operand of each group: lane (c16, g4) holds the 8 elements of
-  // q[column c16] that k-step s contracts (Tile::q_elem)
-  u32x4 qv[kGroups][4];
+  u32x4 qv[kLdsGroups][4];
 #pragma unroll
-  for (int q = 0; q < kGroups; ++q) {
+  for (int q = 0; q < kLdsGroups; ++q) {
     const S* qrow = reinterpret_cast<const S*>(a.q) + (size_t)max(row[q], 0) * D;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       qv[q][s] = row[q] >= 0 ? *reinterpret_cast<const u32x4*>(qrow + Tile::q_elem(s, g4))
                              : u32x4{0, 0, 0, 0};
+  }
+  const float c = fabsf(a.scale_log2), inv_c = 1.f / c;
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int q = 0; q < kLdsGroups; ++q)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qv[q][s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
   }
 
   const int bs_mask = (1 << a.log2_bs) - 1;
@@ -131,118 +268,159 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
   const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
   const P* kbase0 = reinterpret_cast<const P*>(a.k_pool) + (size_t)g * head_stride;
   const P* vbase0 = reinterpret_cast<const P*>(a.v_pool) + (size_t)g * head_stride;
-  const int ntiles = ceil_div(kend, kTile);
-  const int unmasked = max(pos0, 0);  // every row sees keys <= this position
-  // Sliding window: the first row's window starts the walk; rows' windows
-  // start at lim - W + 1, the latest at kend - W.
+  const int ntiles = ceil_div(kend_wg, kTile);
+  const int nsteps = ceil_div(ntiles, 2);
+  const int unmasked = max(pos0, 0);
+  // With a window: the walk starts at the step holding the first key of the
+  // item's earliest row's window; this wave's rows reach back to kbeg.
   const int W = WIN ? a.window : 0;
-  const int t_begin = WIN ? max(unmasked - W + 1, 0) / kTile : 0;
+  const int st_begin =
+      WIN ? max(max(ctx - n + max(top - (kLdsWaves - 1), 0) * QT, 0) - W + 1, 0) / (2 * kTile) : 0;
+  const int kbeg = WIN ? max(unmasked - W + 1, 0) : 0;
 
-  // Issue side: the block id of the next tile is read one issue ahead; tiles
-  // past the last (or with a bad block id) get an empty descriptor, so every
-  // issue has the same loads and the waits stay static.
-  int it = t_begin;
-  int iblk = scalar_load(table + ((it * kTile) >> a.log2_bs));
-  auto issue = [&](Tile& tile) -> bool {
-    bool ok = false;
-    size_t off = 0;
-    int rows = 0;  // V rows of the tile inside the sequence; the rest read as zeros
-    if (it < ntiles) {
-      ok = (unsigned)iblk < (unsigned)a.num_blocks;
-      if (ok) off = (size_t)iblk * block_stride + (size_t)((it * kTile) & bs_mask) * D;
-      rows = min(kTile, ctx - it * kTile);
-      if (++it < ntiles) iblk = scalar_load(table + ((it * kTile) >> a.log2_bs));
+  // tile t of the walk: its block id when inside the pool, else -1
+  auto block_of = [&](int t) __attribute__((always_inline)) -> int {
+    if (t >= ntiles) return -1;
+    const int b = scalar_load(table + ((t * kTile) >> a.log2_bs));
+    return (unsigned)b < (unsigned)a.num_blocks ? b : -1;
+  };
+  // Loads of step st: wave w takes K pieces 2 w, 2 w + 1 (piece j: tile
+  // j / 4, k-step j % 4) and its two V rows of each four-row group of tile
+  // w / 2 (rows past the sequence read as zeros).
+  struct Stage {
+    u32x4 x0, x1, x2, x3;
+  };
+  // The block id each wave needs for its next step, read one step
+  // ahead (tile 2 st + tw of step st).
+  const int tw = w >> 1;
+  int next_b = block_of(2 * st_begin + tw);
+  // Key order within a tile: K operand row i holds key krow(i), which swaps
+  // the row pairs (4a, 4a + 1) and (4a + 2, 4a + 3) for odd a.  S^T row
+  // 4 g4 + r is then key 4 g4 + (r ^ kswap), and the V words of odd lane
+  // groups are stored pair-swapped to match, so the two halves of a wave's
+  // 4-byte V-operand stores fall on different LDS banks.
+  const int krow = c16 ^ ((c16 >> 1) & 2);
+  // ok: the wave's tile of the step had a block inside the pool
+  auto gload = [&](int st, int& ok) __attribute__((always_inline)) -> Stage {
+    Stage r = {};
+    const int b = next_b;
+    next_b = block_of(2 * (st + 1) + tw);
+    ok = b >= 0;
+    const int t = 2 * st + tw;
+    const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
+    // K pieces 2 w and 2 w + 1: tile w / 2, k-steps 2 (w % 2) and 2 (w % 2) + 1
+    const rsrc_t ks = make_rsrc(kbase0 + off, b >= 0 ? Tile::kBytes : 0u);
+    // V rows 4 g4 + 2 (w % 2) and the next, dims 8 c16 .. 8 c16 + 7
+    const uint32_t bytes = b >= 0 ? (uint32_t)min(kTile, ctx - t * kTile) * Tile::kRowBytes : 0u;
+    const rsrc_t vs = make_rsrc(vbase0 + off, bytes);
+    if constexpr (KV == KvType::kFp8) {
+      // codes as loaded (KvTile<E, kFp8>'s k-slot order), widened when stored
+      r.x0 = buffer_load16(ks, (uint32_t)(krow * 128 + 16 * g4) + 64u * (w & 1));
+      const uint32_t vlo = (uint32_t)(4 * g4 * 128 + 8 * c16) + 256u * (w & 1);
+      const u32x2 v0 = buffer_load8(vs, vlo), v1 = buffer_load8(vs, vlo + 128u);
+      r.x2 = u32x4{v0[0], v0[1], v1[0], v1[1]};
+    } else {
+      const uint32_t klo = (uint32_t)(krow * 128 + 8 * g4) * 2u + 128u * (w & 1);
+      r.x0 = buffer_load16(ks, klo);
+      r.x1 = buffer_load16(ks, klo + 64u);
+      const uint32_t vlo = (uint32_t)(4 * g4 * 128 + 8 * c16) * 2u + 512u * (w & 1);
+      r.x2 = buffer_load16(vs, vlo);
+      r.x3 = buffer_load16(vs, vlo + 256u);
     }
-    const uint32_t kbytes = ok ? Tile::kBytes : 0u;
-    const uint32_t vbytes = ok ? (uint32_t)rows * Tile::kRowBytes : 0u;
-    tile.load(make_rsrc(kbase0 + off, kbytes), make_rsrc(vbase0 + off, vbytes), c16, g4);
-    return ok;
+    return r;
+  };
+  auto lwrite = [&](int st, const Stage& r, int ok) __attribute__((always_inline)) {
+    const int bf = st % kLdsBufs;
+    u32x4 k0 = r.x0, k1 = r.x1, v0 = r.x2, v1 = r.x3;
+    if constexpr (KV == KvType::kFp8) {
+      k0 = widen8<E>(r.x0[0], r.x0[1]);
+      k1 = widen8<E>(r.x0[2], r.x0[3]);
+      v0 = widen8<E>(r.x2[0], r.x2[1]);
+      v1 = widen8<E>(r.x2[2], r.x2[3]);
+    }
+    s_k[bf][2 * w][lane] = k0;
+    s_k[bf][2 * w + 1][lane] = k1;
+    if ((w & 1) == 0 && lane == 0) s_ok[bf][w >> 1] = ok;
+    // Word 2 (w / 2) + (w % 2 ^ g4 % 2) of P.V operand e (words 0, 1: the
+    // first tile's keys, 2, 3: the second's) pairs element e of the lane's 8
+    // in the two rows (the key order of krow).
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      reinterpret_cast<uint32_t*>(&s_vw[bf][e][lane])[2 * (w >> 1) + ((w ^ g4) & 1)] =
+          __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
+    }
   };
 
-  // score scale c > 0 in log2 units: a negative scale flips q's sign (exact)
-  const float c = fabsf(a.scale_log2), inv_c = 1.f / c;
-  if (a.scale_log2 < 0.f) {
+  float m[kLdsGroups], l[kLdsGroups];
+  f32x4 o[kLdsGroups][8];
 #pragma unroll
-    for (int q = 0; q < kGroups; ++q)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qv[q][s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-  }
-  float m[kGroups], l[kGroups];
-  f32x4 o[kGroups][8];
-#pragma unroll
-  for (int q = 0; q < kGroups; ++q) {
+  for (int q = 0; q < kLdsGroups; ++q) {
     m[q] = kMFloor;
     l[q] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Two 16-key tiles per step, so the P.V product runs on the double-rate
-  // v_mfma_f32_16x16x32: its k-slot (g4, j) is key 4 g4 + j of the first
-  // tile for j < 4 and key 4 g4 + j - 4 of the second for j >= 4, which is
-  // where the lane's own S^T results of the two QK products sit.  A tile with
-  // a bad block id (or past the last) is masked out; so are keys past a
-  // column's position and, with a window, before its window.
-  auto compute2 = [&](int t, const Tile& ta, const Tile& tb, bool oka, bool okb) {
-    const int k0 = t * kTile;
+  // One 32-key step from LDS buffer st % 3.
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const int k0 = 2 * st * kTile;
+    const int bf = st % kLdsBufs;
+    const bool oka = uni(s_ok[bf][0]) != 0, okb = uni(s_ok[bf][1]) != 0;
+    if (!oka && !okb) return;
     u32x4 vw[8];
-    {
-      u32x4 va[4], vb[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        va[r] = ta.v_row(r);
-        vb[r] = tb.v_row(r);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        vw[e] = u32x4{__builtin_amdgcn_perm(va[1][e >> 1], va[0][e >> 1], sel),
-                      __builtin_amdgcn_perm(va[3][e >> 1], va[2][e >> 1], sel),
-                      __builtin_amdgcn_perm(vb[1][e >> 1], vb[0][e >> 1], sel),
-                      __builtin_amdgcn_perm(vb[3][e >> 1], vb[2][e >> 1], sel)};
-      }
-    }
+    for (int e = 0; e < 8; ++e) vw[e] = s_vw[bf][e][lane];
     const bool masked =
         k0 + 2 * kTile - 1 > unmasked || (WIN && k0 < kend - W) || !oka || !okb;
-    float sv[kGroups][8];
+    float sv[kLdsGroups][8];
+    {
+      u32x4 ka[4], kb[4];
 #pragma unroll
-    for (int q = 0; q < kGroups; ++q) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) sa = Mfma<E>::qk(ta.k_op(s), qv[q][s], sa);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) sb = Mfma<E>::qk(tb.k_op(s), qv[q][s], sb);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[q][r] = sa[r];
-        sv[q][4 + r] = sb[r];
+      for (int s = 0; s < 4; ++s) {
+        ka[s] = s_k[bf][s][lane];
+        kb[s] = s_k[bf][4 + s][lane];
       }
+      // A wave issuing matrix products takes issue priority over the other
+      // workgroup's wave on its SIMD, whose vector instructions then fill
+      // the cycles the products leave free.
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int q = 0; q < kLdsGroups; ++q) {
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sa = Mfma<E>::qk(ka[s], qv[q][s], sa);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sb = Mfma<E>::qk(kb[s], qv[q][s], sb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sv[q][r] = sa[r];
+          sv[q][4 + r] = sb[r];
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (masked) {
 #pragma unroll
-      for (int q = 0; q < kGroups; ++q)
+      for (int q = 0; q < kLdsGroups; ++q)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int key = k0 + (j < 4 ? 0 : kTile) + 4 * g4 + (j & 3);
+          const int key = k0 + (j < 4 ? 0 : kTile) + 4 * g4 + ((j & 3) ^ kswap);
           if (key > lim[q] || (WIN && key <= lim[q] - W) || !(j < 4 ? oka : okb))
             sv[q][j] = neg_inf();
         }
     }
-    // m starts at a finite floor, so a column that has seen no key yet
-    // (all -inf so far) gets weights exp2(-inf) = 0 and a rescale factor of
-    // 0 or 1, never NaN: the weights need no guard and the step has no
-    // branch between the rescale test and the P.V product.
-    float mt[kGroups];
+    float mt[kLdsGroups];
     bool over = false;
 #pragma unroll
-    for (int q = 0; q < kGroups; ++q) {
+    for (int q = 0; q < kLdsGroups; ++q) {
       mt[q] = smax(smax(smax(sv[q][0], sv[q][1]), smax(sv[q][2], sv[q][3])),
                    smax(smax(sv[q][4], sv[q][5]), smax(sv[q][6], sv[q][7])));
       over |= mt[q] > (m[q] + kRescaleSlack) * inv_c;
     }
     if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
-      for (int q = 0; q < kGroups; ++q) {
+      for (int q = 0; q < kLdsGroups; ++q) {
         float x = smax(mt[q], shfl_xor(mt[q], 16));
         x = smax(x, shfl_xor(x, 32));
         const float mn = smax(m[q], x * c);
@@ -253,43 +431,56 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
         m[q] = mn;
       }
     }
-    u32x4 pw[kGroups];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int q = 0; q < kGroups; ++q) {
+    for (int q = 0; q < kLdsGroups; ++q) {
       float pf[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pf[j] = fast_exp2(__builtin_fmaf(sv[q][j], c, -m[q]));
-      pw[q] = u32x4{Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3]),
-                    Mfma<E>::round16x2(pf[4], pf[5]), Mfma<E>::round16x2(pf[6], pf[7])};
-      // l sums the weights as rounded for the P.V product
-      l[q] = sum2(E{}, pw[q][3], sum2(E{}, pw[q][2], sum2(E{}, pw[q][1], sum2(E{}, pw[q][0], l[q]))));
+      const u32x4 pw = {Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3]),
+                        Mfma<E>::round16x2(pf[4], pf[5]), Mfma<E>::round16x2(pf[6], pf[7])};
+      l[q] = sum2(E{}, pw[3], sum2(E{}, pw[2], sum2(E{}, pw[1], sum2(E{}, pw[0], l[q]))));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[q][e] = pv32(E{}, vw[e], pw, o[q][e]);
     }
-#pragma unroll
-    for (int q = 0; q < kGroups; ++q)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[q][e] = pv32(E{}, vw[e], pw[q], o[q][e]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  Tile tb[2 * kPfPairs];
-  bool okb[2 * kPfPairs];
-#pragma unroll
-  for (int s = 0; s < 2 * kPfPairs; ++s) okb[s] = issue(tb[s]);
-  // Every slot issues on every path and the loop exits at the bottom of the
-  // unrolled body, so the compiler's wait counts stay static.
-  int t = t_begin;
-  do {
-#pragma unroll
-    for (int s = 0; s < 2 * kPfPairs; s += 2) {
-      if (t < ntiles && (okb[s] || okb[s + 1])) compute2(t, tb[s], tb[s + 1], okb[s], okb[s + 1]);
-      okb[s] = issue(tb[s]);
-      okb[s + 1] = issue(tb[s + 1]);
-      t += 2;
-    }
-  } while (t < ntiles);
+  // The ring: step st's pieces go global -> registers three steps ahead, in
+  // three register stages (step k in stage k % 3), and registers -> LDS one
+  // step ahead; the write to LDS waits only for its own stage's loads, and
+  // the barrier after it makes the step visible to every wave and frees the
+  // buffer written next.  All waves run the same steps, so every barrier is
+  // reached by the whole workgroup.
+  // this wave computes step st: its rows reach keys [kbeg, kend)
+  auto runs = [&](int st) __attribute__((always_inline)) {
+    return mine && st * 2 * kTile < kend && (!WIN || (st + 1) * 2 * kTile > kbeg);
+  };
+  const int s0 = st_begin;
+  int ok0 = 0, ok1 = 0, ok2 = 0;
+  Stage r0 = gload(s0, ok0), r1 = gload(s0 + 1, ok1), r2 = gload(s0 + 2, ok2);
+  lwrite(s0, r0, ok0);
+  __syncthreads();
+  r0 = gload(s0 + 3, ok0);
+  for (int st = s0; st < nsteps; st += 3) {
+    lwrite(st + 1, r1, ok1);
+    __syncthreads();
+    r1 = gload(st + 4, ok1);
+    if (runs(st)) compute(st);
+    if (st + 1 >= nsteps) break;
+    lwrite(st + 2, r2, ok2);
+    __syncthreads();
+    r2 = gload(st + 5, ok2);
+    if (runs(st + 1)) compute(st + 1);
+    if (st + 2 >= nsteps) break;
+    lwrite(st + 3, r0, ok0);
+    __syncthreads();
+    r0 = gload(st + 6, ok0);
+    if (runs(st + 2)) compute(st + 2);
+  }
 
-  // Lane (c16, g4) holds O[column c16][32 g4 + 8 r + e] = o[q][e][r].
 #pragma unroll
-  for (int q = 0; q < kGroups; ++q) {
+  for (int q = 0; q < kLdsGroups; ++q) {
     const float lsum = across_groups_sum<16>(l[q]);
     if (row[q] < 0) continue;
     const float inv = live[q] && lsum > 0.f ? a.v_scale / lsum : 0.f;
@@ -306,12 +497,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma(PrefillArgs a) {
 }
 
 template <class E, KvType KV>
-pa_status launch(const PrefillArgs& a, int max_query_blocks, hipStream_t st) {
-  const dim3 grid(a.num_kv_heads, ceil_div(max_query_blocks, kPfWaves), a.num_seqs);
+pa_status launch_lds(const PrefillArgs& a, hipStream_t st) {
+  const int blocks = ceil_div(a.max_query, kLdsRows / a.group);
+  if (blocks <= 0) return PA_OK;
+  const dim3 grid(a.num_kv_heads, ceil_div(blocks, kLdsWaves), a.num_seqs);
   if (a.window > 0)
-    hipLaunchKernelGGL((prefill_mfma<E, KV, true>), grid, dim3(kPfThreads), 0, st, a);
+    hipLaunchKernelGGL((prefill_mfma_lds<E, KV, true>), grid, dim3(kLdsThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_mfma<E, KV, false>), grid, dim3(kPfThreads), 0, st, a);
+    hipLaunchKernelGGL((prefill_mfma_lds<E, KV, false>), grid, dim3(kLdsThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -323,16 +516,15 @@ bool prefill_supports(int dtype, int head_dim, int group) {
 }
 
 int prefill_query_blocks(int max_query_len, int group) {
-  return max_query_len > 0 ? (max_query_len + kRows / group - 1) / (kRows / group) : 0;
+  return max_query_len > 0 ? ceil_div(max_query_len, kLdsRows / group) : 0;
 }
 
 pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, hipStream_t st) {
-  const int blocks = prefill_query_blocks(a.max_query, a.group);
-  if (blocks <= 0) return PA_OK;
   const bool fp8 = kv == KvType::kFp8;
-  if (!fp8) return launch_prefill_lds(a, dtype, st);  // 16-bit pools: shared tiles
-  if (dtype == PA_BF16) return launch<BF16, KvType::kFp8>(a, blocks, st);
-  if (dtype == PA_F16) return launch<F16, KvType::kFp8>(a, blocks, st);
+  if (dtype == PA_BF16)
+    return fp8 ? launch_lds<BF16, KvType::kFp8>(a, st) : launch_lds<BF16, KvType::kSame>(a, st);
+  if (dtype == PA_F16)
+    return fp8 ? launch_lds<F16, KvType::kFp8>(a, st) : launch_lds<F16, KvType::kSame>(a, st);
   return PA_ERR_SHAPE;
 }
 
