@@ -289,17 +289,18 @@ def test_fp8_cow_workload_and_copies(dtype):
     assert max_abs_err(out, want) <= TOL[d.wl.dtype]
 
 
-@pytest.mark.parametrize("window", [0, 50])
-@pytest.mark.parametrize("g", [1, 4, 8])
-def test_fp8_prefill(window, g):
+@pytest.mark.parametrize("window,g,dtype", [(0, 1, "bf16"), (0, 4, "bf16"), (0, 8, "bf16"),
+                                            (50, 1, "bf16"), (50, 4, "bf16"), (50, 8, "bf16"),
+                                            (0, 4, "f16"), (50, 16, "f16")])
+def test_fp8_prefill(window, g, dtype):
     chunks = [1, 17, 64, 65, 100]
     prefixes = [0, 40, 16, 300, 3]
     lens = [c + p for c, p in zip(chunks, prefixes)]
-    d = W.custom(1500 + g, 2 * g, 2, 128, "bf16", 16, lens, chunk_lens=chunks)
+    d = W.custom(1500 + g, 2 * g, 2, 128, dtype, 16, lens, chunk_lens=chunks)
     kv = KV(d)
     o, cache = run_fp8_scenario(d, kv, SCALES)
     tables, lens32 = cache.alloc.pa_build_tables(list(range(d.batch)), o["tables"].shape[1])
-    q = to_device(W.prefill_query_bits(d), "bf16")
+    q = to_device(W.prefill_query_bits(d), dtype)
     out = torch.full_like(q, float("nan"))
     pa.pa_prefill(q, cache.k_pool, cache.v_pool, torch.from_numpy(tables).cuda(),
                   torch.from_numpy(d.query_start.astype(np.int32)).cuda(),
@@ -307,11 +308,11 @@ def test_fp8_prefill(window, g):
                   int(lens32.max()), sliding_window=window, kv_scales=SCALES)
     torch.cuda.synchronize()
     want = paged_prefill(W.prefill_query_bits(d), o["kp"], o["vp"], o["tables"], d.query_start,
-                         o["lens"], d.wl.scale, "bf16", window=window, kv_dtype="fp8_e4m3",
+                         o["lens"], d.wl.scale, dtype, window=window, kv_dtype="fp8_e4m3",
                          k_scale=SCALES[0], v_scale=SCALES[1])
     err = max_abs_err(out, want)
-    print(f"fp8 prefill G={g} window={window} max_abs_err={err:.3e}", flush=True)
-    assert err <= TOL["bf16"]
+    print(f"fp8 prefill {dtype} G={g} window={window} max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL[dtype]
 
 
 def test_fp8_full_size_sampled():
