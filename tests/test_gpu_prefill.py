@@ -199,3 +199,15 @@ def test_bad_block_ids_inside_a_sequence():
         assert torch.equal(out[qs[i]:qs[i + 1]], g["out"][qs[i]:qs[i + 1]])
     assert torch.all(torch.isfinite(out[qs[1]:qs[2]].float()))
     assert torch.equal(cache.k_pool, kp0) and torch.equal(cache.v_pool, vp0)
+
+
+def test_batches_above_the_longest_first_limit():
+    """More sequences than the longest-first order counts (4096): the items
+    run in batch order, each sequence's query-block groups back to back."""
+    rng = np.random.default_rng(7)
+    n = 4100
+    # up to 5 query blocks of 8 tokens: some sequences take two groups
+    chunks = [int(x) for x in rng.integers(1, 41, n)]
+    prefixes = [int(x) for x in rng.integers(0, 17, n)]
+    lens = [c + p for c, p in zip(chunks, prefixes)]
+    check(W.custom(340, 8, 2, 128, "bf16", 16, lens, chunk_lens=chunks))
