@@ -181,10 +181,10 @@ __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
 // 0 .. the item's last position), computing only the steps its own rows
 // reach.  Two workgroups share a CU (two waves per SIMD) and, with a barrier
 // each, run out of step: one's softmax overlaps the other's products.
-// 16-bit pools.  With a sliding window of W positions (WIN) the walk starts
-// at the window of the item's earliest row, each wave computes only the
-// steps its rows' windows reach, and keys below a row's window are masked
-// per element.
+// On 8-bit pools the loads carry the E4M3 codes, widened as they are stored.
+// With a sliding window of W positions (WIN) the walk starts at the window
+// of the item's earliest row, each wave computes only the steps its rows'
+// windows reach, and keys below a row's window are masked per element.
 constexpr int kLdsWaves = 4;
 constexpr int kLdsThreads = kLdsWaves * kWave;
 constexpr int kLdsGroups = 2;
