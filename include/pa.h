@@ -156,9 +156,10 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
 
 /* The two passes of pa_decode, callable one at a time (same arguments, same
  * path setting, same stream; pa_decode == pa_decode_partition then
- * pa_decode_reduce).  The reduce pass finishes the rows the partition pass
- * left in the workspace and, for the stream split, zeroes the rows of empty
- * sequences; it does nothing when the grid split has one partition. */
+ * pa_decode_reduce).  The partition pass writes every row it can finish
+ * alone, including the all-zero rows of empty sequences (context_lens <= 0),
+ * on every kernel; the reduce pass finishes the rows the partition pass left
+ * in the workspace, and does nothing when the grid split has one partition. */
 pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_pool,
                               const pa_pool_desc* pool, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -249,9 +250,16 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot
  * Allocation 与 Copy-on-Write 在 LLM 推理系统中的应用", section 4.4; page
  * "第 6 章 缓存管理：把显存当操作系统来管", section "块表长什么样").  For each
  * pair p: k_pool[dst] = k_pool[src] and v_pool[dst] = v_pool[src], whole
- * blocks (all kv heads, all slots).  Bit-exact.  No dst may be a src or a dst
- * of another pair of the same call (the allocator guarantees this); pairs
- * with an id outside [0, num_blocks) are skipped.
+ * blocks (all kv heads, all slots).  Bit-exact.  The pairs of one call run
+ * concurrently, so no dst may be a src or a dst of another pair of the same
+ * call.  The pairs of one pa_seq_append_batch call always satisfy this, and
+ * so do pairs gathered from several appends of an allocator without the
+ * prefix cache (a copied block keeps a holder).  With the prefix cache on,
+ * pairs from separate pa_seq_append / pa_seq_append_tokens calls may chain
+ * (a cached block copied by its last holder is evictable at once, and a
+ * later append may take it as its copy's destination): give each such append
+ * its own call, in order.  Pairs with an id outside [0, num_blocks) are
+ * skipped.
  *   pairs  device int32 [num_pairs][2] = (src, dst)
  * ------------------------------------------------------------------------ */
 pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool,
@@ -299,7 +307,13 @@ pa_status pa_seq_append(pa_alloc* a, int64_t seq, int32_t n_tokens, int64_t* slo
                         int32_t* cow_pair_out, int32_t* num_cow_out);
 /* One decode step for many sequences: appends n_tokens to each of seqs[0..n)
  * in order.  slots_out [n * n_tokens]; pairs_out [n][2]; *num_pairs_out =
- * pairs written.  All or nothing: on PA_ERR_OOM nothing changes. */
+ * pairs written.  The pairs are independent (no dst is another pair's src or
+ * dst), so one pa_copy_blocks call can run them all: a cached block whose
+ * last holder copies it is held back from the evictable list until the
+ * step's last append, and joins it then, in the order of release.  Each
+ * append must fit what is available when it runs (held blocks excluded).
+ * All or nothing: on PA_ERR_OOM nothing changes.  A sequence named twice is
+ * PA_ERR_ARG. */
 pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32_t n_tokens,
                               int64_t* slots_out, int32_t* pairs_out, int32_t* num_pairs_out);
 pa_status pa_seq_fork(pa_alloc* a, int64_t parent, int64_t* child_out);

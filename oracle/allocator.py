@@ -109,6 +109,7 @@ window, and a prefix without its early blocks is not the whole prefix.
 """
 from __future__ import annotations
 
+import copy
 from collections import OrderedDict, deque
 from typing import Dict, List, Optional, Sequence, Tuple
 
@@ -275,8 +276,10 @@ class OracleAllocator:
         self._register(seq)
         return slots, pair
 
-    def append(self, seq: int, n_tokens: int) -> Tuple[List[int], Optional[Tuple[int, int]]]:
-        """Write positions len..len+n-1.  Returns (slots, cow_pair or None)."""
+    def append(self, seq: int, n_tokens: int,
+               held: Optional[List[int]] = None) -> Tuple[List[int], Optional[Tuple[int, int]]]:
+        """Write positions len..len+n-1.  Returns (slots, cow_pair or None).
+        ``held``: see ``append_batch``."""
         table = self._seq(seq)
         if n_tokens < 0:
             raise OracleError("ARG", "n_tokens < 0")
@@ -298,7 +301,10 @@ class OracleAllocator:
             dst = self._take()
             self.refcount[src] -= 1
             if self.refcount[src] == 0:           # a cached block's last holder copied
-                self.lru[src] = None
+                if held is None:
+                    self.lru[src] = None
+                else:
+                    held.append(src)
             self.refcount[dst] = 1
             table[start // bs] = dst
             pair = (src, dst)
@@ -313,6 +319,43 @@ class OracleAllocator:
             slots.append(table[pos // bs] * bs + pos % bs)
         self.lens[seq] = end
         return slots, pair
+
+    def append_batch(self, seqs: Sequence[int], n_tokens: int):
+        """One decode step: ``append(s, n_tokens)`` for each of ``seqs`` in
+        order; returns (all slots, the CoW pairs in order).
+
+        The step's copies are meant to run together, before the step's
+        writes (copy, then write: page "Lazy Allocation 与 Copy-on-Write ...",
+        section 4.4), so no block may be both read and written by two copies
+        of one step.  A cached block whose last holder copies it would
+        otherwise become evictable at once, and a later append of the same
+        step could take it as its own copy's destination while the first
+        copy still reads it.  Such blocks are therefore held back and join
+        the evictable list (in the order they were released) only after the
+        step's last append.  All or nothing: on OOM (each append must fit
+        what is available when it runs, the held blocks excluded) nothing
+        changes; a sequence named twice is ARG."""
+        seqs = [int(s) for s in seqs]
+        if len(set(seqs)) != len(seqs):
+            raise OracleError("ARG", "one append per sequence per step")
+        for s in seqs:
+            self._seq(s)
+        saved = copy.deepcopy(self.__dict__)
+        held: List[int] = []
+        slots, pairs = [], []
+        try:
+            for s in seqs:
+                sl, pr = self.append(s, n_tokens, held)
+                slots += sl
+                if pr is not None:
+                    pairs.append(pr)
+        except OracleError:
+            self.__dict__.clear()
+            self.__dict__.update(saved)
+            raise
+        for b in held:
+            self.lru[b] = None
+        return slots, pairs
 
     def fork(self, parent: int) -> int:
         table = self._seq(parent)

@@ -55,7 +55,8 @@ def decode_bits(bits: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
         # a bf16 value is the top half of the float32 with the same sign,
         # exponent and leading mantissa bits
         wide = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-        return wide.view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):   # signalling-NaN patterns widen to NaN
+            return wide.view(np.float32).astype(np.float64)
     raise ValueError(dtype)
 
 

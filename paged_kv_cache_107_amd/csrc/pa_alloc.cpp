@@ -226,9 +226,11 @@ AppendPlan plan_append(const pa_alloc* a, const pa_alloc::Seq& s, int32_t n) {
   return p;
 }
 
-// Carries out a planned append (the caller checked the free pool).
+// Carries out a planned append (the caller checked the free pool).  A copied
+// cached block whose last holder this was becomes evictable, or, with `held`,
+// is put aside for the caller to make evictable later.
 void do_append(pa_alloc* a, pa_alloc::Seq& s, int32_t n, int64_t* slots, int32_t* pair,
-               int32_t* num_pair) {
+               int32_t* num_pair, std::vector<int32_t>* held = nullptr) {
   const int32_t bs = a->block_size;
   const int64_t start = s.len, end = start + n;
   *num_pair = 0;
@@ -241,7 +243,9 @@ void do_append(pa_alloc* a, pa_alloc::Seq& s, int32_t n, int64_t* slots, int32_t
       pair[0] = src;
       pair[1] = dst;
       *num_pair = 1;
-      if (--a->refcount[src] == 0) lru_push_back(a, src);  // a cached block's last holder
+      if (--a->refcount[src] == 0) {  // a cached block's last holder
+        if (held) held->push_back(src); else lru_push_back(a, src);
+      }
       a->refcount[dst] = 1;
       last = dst;
       a->cow_copies += 1;
@@ -508,8 +512,10 @@ pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32
     ptrs[i] = &it->second;
   }
   // Each append must fit what is available when it runs, as if the appends
-  // were made one by one: a copied cached block whose last holder wrote
-  // becomes evictable for the appends after it.
+  // were made one by one.  The step's copies run together in one launch, so
+  // a copied cached block whose last holder wrote is held back until the
+  // step's last append (it must not become a later copy's destination while
+  // its own copy reads it) and does not count as available meanwhile.
   int64_t avail = available(a);
   std::unordered_map<int32_t, int32_t> drops;  // block -> refcount drops so far
   const int64_t bs = a->block_size;
@@ -517,25 +523,26 @@ pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32
     const pa_alloc::Seq& s = *ptrs[i];
     const int64_t start = s.len, end = start + n_tokens;
     int64_t need = ceil_div(end, bs) - ceil_div(start, bs);
-    bool released = false;
     if (start % bs != 0) {
       const int32_t last = s.table[start / bs];
       const int32_t rc = a->refcount[last] - drops[last];
       if (must_copy(a, last, rc)) {
         need += 1;
         drops[last] += 1;
-        released = rc == 1;
       }
     }
     if (need > avail) return PA_ERR_OOM;
-    avail -= need - (released ? 1 : 0);
+    avail -= need;
   }
   int32_t np = 0;
+  std::vector<int32_t> held;
   for (int32_t i = 0; i < n; ++i) {
     int32_t one = 0;
-    do_append(a, *ptrs[i], n_tokens, slots_out + (int64_t)i * n_tokens, pairs_out + 2 * np, &one);
+    do_append(a, *ptrs[i], n_tokens, slots_out + (int64_t)i * n_tokens, pairs_out + 2 * np, &one,
+              &held);
     np += one;
   }
+  for (int32_t b : held) lru_push_back(a, b);
   *num_pairs_out = np;
   return PA_OK;
 }

@@ -167,19 +167,73 @@ def test_append_batch_with_evictions(seed):
             assert before[1] == after[1]
             break
         slots_n, pairs_n = n.pa_seq_append_batch(seqs, k)
-        slots_o, pairs_o = [], []
-        for s in seqs:
-            sl, pr = o.append(s, k)
-            slots_o += sl
-            if pr is not None:
-                pairs_o.append(pr)
+        slots_o, pairs_o = o.append_batch(seqs, k)
         assert slots_n.tolist() == slots_o
         assert [tuple(p) for p in pairs_n.tolist()] == pairs_o
+        assert_pairs_independent(pairs_o)
         free, rc = n.pa_alloc_query()
         assert free.tolist() == list(o.free) and rc.tolist() == o.refcount
         assert n.pa_prefix_cache_query().tolist() == list(o.lru)
         assert n.pa_prefix_cache_stats() == o.prefix_stats()
         assert n.pa_alloc_check_invariants()
+        o.check_invariants()
+
+
+def assert_pairs_independent(pairs):
+    """The copies of one step run together: no destination may be another
+    pair's source or destination."""
+    for i, (_, dst) in enumerate(pairs):
+        for j, (s2, d2) in enumerate(pairs):
+            if i != j:
+                assert dst != s2 and dst != d2, (pairs, i, j)
+
+
+@pytest.mark.parametrize("nb", [5, 6])
+def test_batch_copies_of_cached_blocks_stay_independent(nb):
+    """Two sequences share 20 tokens of two different cached 32-token
+    prompts; both prompts are freed, so each sharer is the last holder of a
+    cached partial block and must copy it.  The first copy's source must not
+    become the second copy's destination within the step: with 5 blocks the
+    step does not fit (OOM, nothing changes), with 6 its copies are
+    independent."""
+    bs = 16
+    o = OracleAllocator(nb, bs)
+    n = PaAllocator(nb, bs)
+    o.enable_prefix_cache()
+    n.pa_alloc_enable_prefix_cache()
+    c = []
+    for base in (100, 200):
+        prompt = list(range(base, base + 2 * bs))
+        so, _ = o.create_prefix(prompt)
+        sn, _ = n.pa_seq_create_prefix(prompt)
+        o.append_tokens(so, prompt)
+        n.pa_seq_append_tokens(sn, prompt)
+        c.append(o.share_prefix(so, 20))
+        assert n.pa_seq_share_prefix(sn, 20) == c[-1]
+        o.free_seq(so)
+        n.pa_seq_free(sn)
+    if nb == 5:
+        before = (n.pa_alloc_query(), n.pa_prefix_cache_query().tolist())
+        with pytest.raises(OracleError):
+            o.append_batch(c, 1)
+        with pytest.raises(PaError) as e:
+            n.pa_seq_append_batch(c, 1)
+        assert e.value.status == -4
+        after = (n.pa_alloc_query(), n.pa_prefix_cache_query().tolist())
+        assert all(np.array_equal(x, y) for x, y in zip(before[0], after[0]))
+        assert before[1] == after[1]
+        return
+    slots_o, pairs_o = o.append_batch(c, 1)
+    slots_n, pairs_n = n.pa_seq_append_batch(c, 1)
+    assert slots_n.tolist() == slots_o
+    assert [tuple(p) for p in pairs_n.tolist()] == pairs_o
+    assert len(pairs_o) == 2
+    assert_pairs_independent(pairs_o)
+    # the held sources join the evictable list after the step, in order
+    assert list(o.lru)[-2:] == [pairs_o[0][0], pairs_o[1][0]]
+    assert n.pa_prefix_cache_query().tolist() == list(o.lru)
+    assert n.pa_alloc_check_invariants()
+    o.check_invariants()
 
 
 # ------------------------------------------------------------------ random operations

@@ -259,3 +259,92 @@ def test_cached_prefill_equals_full_prompt_prefill(bs, system_len, suffix):
     held_c = len({int(b) for row in c["tables"] for b in row if b >= 0})
     held_u = len({int(b) for row in u["tables"] for b in row if b >= 0})
     assert held_u - held_c == int(c["hits"].sum()) // bs
+
+
+# ------------------------------------------------------------------ batched decode steps
+
+def _independent(pairs):
+    """No pair's destination is another pair's source or destination."""
+    return all(d != s2 and d != d2 for i, (_, d) in enumerate(pairs)
+               for j, (s2, d2) in enumerate(pairs) if i != j)
+
+
+def test_a_step_cannot_reuse_a_copied_cached_block():
+    """A decode step's copies run together, before its writes (copy, then
+    write: "Lazy Allocation 与 Copy-on-Write 在 LLM 推理系统中的应用", section
+    4.4).  Two sequences each hold the last reference to a cached partial
+    block and must copy it.  With one free block the step does not fit: the
+    first copy's source may not serve as the second copy's destination while
+    the first still reads it (OOM, nothing changes).  With two free blocks
+    the copies are independent, and the copied blocks become evictable
+    after the step, in order."""
+    for nb in (5, 6):
+        a = OracleAllocator(nb, 16)
+        a.enable_prefix_cache()
+        sharers = []
+        for base in (100, 200):
+            prompt = list(range(base, base + 32))
+            s, _ = a.create_prefix(prompt)
+            a.append_tokens(s, prompt)
+            sharers.append(a.share_prefix(s, 20))
+            a.free_seq(s)
+        before = (list(a.free), list(a.lru), list(a.refcount))
+        if nb == 5:
+            with pytest.raises(OracleError) as e:
+                a.append_batch(sharers, 1)
+            assert e.value.code == "OOM"
+            assert (list(a.free), list(a.lru), list(a.refcount)) == before
+            continue
+        slots, pairs = a.append_batch(sharers, 1)
+        assert len(pairs) == 2 and _independent(pairs)
+        assert list(a.lru)[-2:] == [pairs[0][0], pairs[1][0]]
+        a.check_invariants()
+
+
+@settings(max_examples=60, deadline=None)
+@given(seed=st.integers(0, 1 << 30), bs=st.sampled_from([2, 4]), nb=st.integers(8, 30))
+def test_batched_steps_keep_contents_with_copies_in_any_order(seed, bs, nb):
+    """Requests served through the cache, some released (their cached
+    blocks evictable), then decode steps of batched appends.  Each step's
+    copies are applied in reverse order before its writes: since they are
+    independent the order cannot matter, and every live sequence still
+    reads its own tokens back."""
+    rng = np.random.default_rng(seed)
+    a = OracleAllocator(nb, bs, rng.permutation(nb).tolist())
+    a.enable_prefix_cache()
+    pool = Pool(a)
+    live = {}
+    for r in range(int(rng.integers(2, 8))):
+        prompt = [int(x) for x in rng.integers(0, 2, int(rng.integers(1, 3 * bs + 2)))]
+        try:
+            s, hit = a.create_prefix(prompt)
+            slots, pair = a.append_tokens(s, prompt[hit:])
+        except OracleError as e:
+            assert e.code == "OOM"
+            break
+        pool.write(slots, pair, prompt[hit:])
+        live[s] = list(prompt)
+        if rng.random() < 0.4:
+            c = a.share_prefix(s, int(rng.integers(0, len(prompt) + 1)))
+            live[c] = live[s][:a.lens[c]]
+        if rng.random() < 0.4:
+            a.free_seq(s)
+            del live[s]
+    next_id = 1000
+    for _ in range(3):
+        seqs = list(live)
+        if not seqs:
+            break
+        try:
+            slots, pairs = a.append_batch(seqs, 1)
+        except OracleError as e:
+            assert e.code == "OOM"
+            break
+        assert _independent(pairs)
+        for src, dst in reversed(pairs):
+            pool.content[dst] = pool.content[src]
+        for s, slot in zip(seqs, slots):
+            pool.content[slot // bs, slot % bs] = next_id
+            live[s].append(next_id)
+            next_id += 1
+        pool.check(live)
