@@ -60,7 +60,9 @@ typedef enum {
   PA_ERR_REFCOUNT = -5,  /* allocator: refcount would go below zero */
   PA_ERR_NOT_FOUND = -6, /* allocator: unknown sequence id */
   PA_ERR_HIP = -7,       /* a HIP launch or runtime call failed */
-  PA_ERR_SWAPPED = -8    /* allocator: the sequence is swapped out to the host */
+  PA_ERR_SWAPPED = -8,   /* allocator: the sequence is swapped out to the host */
+  PA_ERR_SCRATCH = -9    /* pa_decode_noalloc: the call needs more scratch than
+                            PA_NOALLOC_SCRATCH_BYTES (nothing launched) */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -174,6 +176,29 @@ pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool
                            int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                            float scale, int32_t sliding_window, void* out, void* workspace,
                            size_t workspace_bytes, int32_t partition_tokens, void* hip_stream);
+
+/* pa_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and kernels as
+ * pa_decode (bit-identical output), minus workspace and workspace_bytes: the
+ * split-K workspace is a static device array of PA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each device it runs on until the process ends.  The
+ * call allocates nothing.  It runs on the current device (hip_stream must
+ * belong to it); its first call on a device looks up that device's copy of
+ * the array (PA_ERR_HIP if that fails).  Returns PA_ERR_SCRATCH, with nothing
+ * launched, when the shape needs more workspace than the array holds
+ * (pa_decode_workspace_bytes bounds the need).  Every call on one device
+ * uses the same array: calls that can overlap on one device (different
+ * streams without ordering between them) race and must not be made; calls
+ * on one stream are ordered and safe.  Nothing in the array needs to start
+ * at zero, so stale contents from an earlier call do not matter. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const pa_pool_desc* pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                            float scale, int32_t sliding_window, void* out,
+                            int32_t partition_tokens, void* hip_stream);
 
 /* Decode kernel family.  PA_PATH_AUTO: the matrix-core kernel for 16-bit
  * pools with head_dim 128 and G = num_q_heads / num_kv_heads in [2, 16], the

@@ -11,7 +11,9 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_OK, PA_ERR_ARG, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_OOM, PA_ERR_REFCOUNT, \
-    PA_ERR_NOT_FOUND, PA_ERR_HIP, PA_ERR_SWAPPED = 0, -1, -2, -3, -4, -5, -6, -7, -8
+    PA_ERR_NOT_FOUND, PA_ERR_HIP, PA_ERR_SWAPPED, PA_ERR_SCRATCH = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 PA_NO_BLOCK = -(2 ** 31)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
@@ -53,6 +55,8 @@ SIGNATURES = {
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_partition": (_i32, _DECODE_ARGS),
     "pa_decode_reduce": (_i32, _DECODE_ARGS),
+    "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                                 _i32, _vp, _i32, _vp]),
     "pa_prefill": (_i32, [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                           _f32, _i32, _vp, _vp]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _desc, _vp]),

@@ -5,13 +5,21 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_internal.h"
 
+// Scratch memory of pa_decode_noalloc, for callers that cannot allocate: the
+// split-K workspace of one call lives here instead of in a caller buffer.
+// Each device the library runs on holds its own copy until the process ends.
+// In host code `scratch` only names the symbol; its device address on the
+// current device comes from hipGetSymbolAddress (scratch_on_current_device).
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 constexpr int32_t kDefaultPartition = 512;
 constexpr int32_t kMaxPartition = 4096;
 constexpr int32_t kMaxGridYZ = 65535;
@@ -77,6 +85,33 @@ size_t stream_ws_bytes(int32_t b, int32_t hkv, int32_t g, int32_t d) {
   return kStreamOwnerBytes + stream_ml_bytes(b, hkv, g) + stream_heads(b, hkv, g) * d * sizeof(float);
 }
 
+constexpr size_t kStaticScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current.
+pa_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return PA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return PA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 struct Prepared {
   pa::DecodeArgs args;
   int32_t dtype;
@@ -123,7 +158,8 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                          int32_t num_q_heads, int32_t max_context_len, float scale,
                          int32_t sliding_window, void* out, void* workspace,
-                         size_t workspace_bytes, int32_t partition_tokens, Prepared* pr) {
+                         size_t workspace_bytes, int32_t partition_tokens, Prepared* pr,
+                         bool use_scratch = false) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || max_blocks_per_seq < 0 ||
@@ -158,6 +194,16 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
   const size_t need = stream ? stream_ws_bytes(num_seqs, pool->num_kv_heads, group, pool->head_dim)
                              : grid_ws_bytes(num_seqs, num_q_heads, pool->head_dim,
                                              max_context_len, partition_tokens);
+  if (use_scratch) {  // the static scratch replaces the caller's workspace
+    if (need > kStaticScratchBytes) return PA_ERR_SCRATCH;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      st = scratch_on_current_device(&workspace);
+      if (st != PA_OK) return st;
+      workspace_bytes = kStaticScratchBytes;
+    }
+  }
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_ARG;
 
@@ -249,6 +295,7 @@ const char* pa_status_string(int32_t s) {
     case PA_ERR_NOT_FOUND: return "PA_ERR_NOT_FOUND";
     case PA_ERR_HIP: return "PA_ERR_HIP";
     case PA_ERR_SWAPPED: return "PA_ERR_SWAPPED";
+    case PA_ERR_SCRATCH: return "PA_ERR_SCRATCH";
     default: return "PA_ERR_UNKNOWN";
   }
 }
@@ -321,6 +368,24 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                                 context_lens, num_seqs, num_q_heads, max_context_len, scale,
                                 sliding_window, out, workspace, workspace_bytes, partition_tokens,
                                 &pr);
+  if (st != PA_OK || pr.args.num_seqs == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  st = pa::launch_decode_partition(pr.args, pr.dtype, pr.kv, pr.head_dim, pr.kernel, s);
+  if (st != PA_OK || !needs_reduce(pr)) return st;
+  return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim, pr.kernel, s);
+}
+
+pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const pa_pool_desc* pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                            float scale, int32_t sliding_window, void* out,
+                            int32_t partition_tokens, void* hip_stream) {
+  Prepared pr;
+  pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                                context_lens, num_seqs, num_q_heads, max_context_len, scale,
+                                sliding_window, out, nullptr, 0, partition_tokens, &pr,
+                                /*use_scratch=*/true);
   if (st != PA_OK || pr.args.num_seqs == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   st = pa::launch_decode_partition(pr.args, pr.dtype, pr.kv, pr.head_dim, pr.kernel, s);

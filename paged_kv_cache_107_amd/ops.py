@@ -122,6 +122,31 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspa
                         kv_scales)
 
 
+def pa_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out,
+                      max_context_len, partition_tokens=0, stream=None, sliding_window=0,
+                      kv_scales=(1.0, 1.0)):
+    """pa_decode with the library's static device scratch as its workspace:
+    the call allocates nothing (for callers that cannot).  See pa.h."""
+    act = _act_dtype(k_pool, q)
+    desc = _check_pools(k_pool, v_pool, act, kv_scales)
+    _need_cuda("q", q, act)
+    _need_cuda("out", out, act)
+    _need_cuda("block_tables", block_tables, torch.int32)
+    _need_cuda("context_lens", context_lens, torch.int32)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs][num_q_heads][head_dim]")
+    b, hq, _ = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or context_lens.shape != (b,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    st = lib().pa_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), C.byref(desc),
+                                 _ptr(block_tables), int(block_tables.shape[1]),
+                                 _ptr(context_lens), int(b), int(hq), int(max_context_len),
+                                 float(scale), int(sliding_window), _ptr(out),
+                                 int(partition_tokens), _stream(stream))
+    check("pa_decode_noalloc", st)
+    return out
+
+
 def pa_decode_partition(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
                         max_context_len, partition_tokens=0, stream=None, sliding_window=0,
                         kv_scales=(1.0, 1.0)):

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = pa.lib()
-    assert lib.pa_abi_version() == 4
+    assert lib.pa_abi_version() == 5
     assert lib.pa_status_string(0) == b"PA_OK"
     assert lib.pa_status_string(-4) == b"PA_ERR_OOM"
     assert lib.pa_status_string(-99) == b"PA_ERR_UNKNOWN"
@@ -156,3 +156,23 @@ def test_python_binding_rejects_host_tensors():
     pool = torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pa.pa_reshape_and_cache(x, x, torch.zeros(2, dtype=torch.int64), pool, pool)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """pa_decode_noalloc refuses, before any launch, a shape whose workspace
+    exceeds the static scratch (here 4096 sequences of 8 kv heads x 16 q
+    heads on the stream split: about 280 MB), and validates like pa_decode."""
+    lib = pa.lib()
+    assert lib.pa_status_string(-9) == b"PA_ERR_SCRATCH"
+    big = pa_pool_desc(64, 16, 8, 128, pa.PA_BF16)
+    need = pa.pa_decode_workspace_bytes(big, 4096, 128, 100, 0)
+    assert need > pa_lib.PA_NOALLOC_SCRATCH_BYTES
+
+    def call(desc, b, hq, maxctx, q=FAKE):
+        return lib.pa_decode_noalloc(q, FAKE, FAKE, C.byref(desc), FAKE, 8, FAKE, b, hq, maxctx,
+                                     0.1, 0, FAKE, 0, None)
+    assert call(big, 4096, 128, 100) == -9
+    assert call(pa_pool_desc(64, 16, 2, 96, pa.PA_BF16), 2, 8, 100) == -3   # head_dim
+    assert call(big, 2, 7, 100) == -3                                         # Hq % Hkv
+    assert call(big, 2, 32, 100, q=None) == -1
+    assert call(big, 0, 32, 100) == 0                                         # nothing to do

@@ -1,0 +1,109 @@
+"""pa_decode_noalloc (decode with the library's static device scratch as its
+workspace, for callers that cannot allocate) against pa_decode with a
+caller workspace, through the C ABI on the GPU.
+
+Both run the same kernels, so the outputs must be bit-identical; each is
+also checked against the oracle (max-abs error <= 1e-5 for fp32 inputs,
+<= 2e-2 for 16-bit inputs).  Two calls in a row on one device, the second
+with a smaller batch, so the second reads a scratch array that still holds
+the first call's state.  Covered: the stream split (one array shared by the
+flat tile order's split pairs), the grid split with several partitions, the
+vector kernel with several partitions, and a shape needing no workspace.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from _scenario import KV, TOL, max_abs_err, run_gpu, run_oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # the CPU suite deselects these; never a fallback
+    pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="needs a GPU")]
+
+import paged_kv_cache_107_amd as pa  # noqa: E402
+
+PATHS = {"stream": pa.PA_PATH_MFMA, "grid": pa.PA_PATH_MFMA_GRID, "valu": pa.PA_PATH_VALU,
+         "auto": pa.PA_PATH_AUTO}
+
+CASES = [
+    # (path, seed, Hq, Hkv, D, dtype, BS, lengths, partition tokens)
+    ("stream", 71, 32, 8, 128, "bf16", 16, None, 0),
+    ("grid", 72, 32, 8, 128, "f16", 32, None, 512),
+    ("valu", 73, 8, 8, 64, "f32", 16, None, 256),
+    ("auto", 74, 8, 8, 128, "f32", 16, [5, 17, 100, 33], 512),   # one partition: no workspace
+]
+
+
+def _lens(seed, given):
+    if given is not None:
+        return given
+    rng = np.random.default_rng(seed)
+    return np.concatenate([[1, 16, 17, 512, 513, 2100],
+                           rng.integers(1, 3000, 34)]).tolist()
+
+
+@pytest.mark.parametrize("path,seed,hq,hkv,d,dtype,bs,lens,pt", CASES)
+def test_noalloc_equals_workspace_decode(path, seed, hq, hkv, d, dtype, bs, lens, pt):
+    dr = W.custom(seed, hq, hkv, d, dtype, bs, _lens(seed, lens))
+    print(f"noalloc case {path} seed={seed} B={dr.batch} {dtype} D={d} BS={bs} pt={pt}",
+          flush=True)
+    prev = pa.pa_set_decode_path(PATHS[path])
+    try:
+        kv = KV(dr)
+        o = run_oracle(dr, kv)
+        g = run_gpu(dr, kv, partition_tokens=pt)
+        plan, cache, q, ref_out = g["plan"], g["cache"], g["q"], g["out"]
+        scale = dr.wl.scale
+        # the first call: the whole batch
+        out = torch.full_like(q, float("nan"))
+        pa.pa_decode_noalloc(q, cache.k_pool, cache.v_pool, plan.tables, plan.lens, scale, out,
+                             plan.max_context_len, pt)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16 if dtype != "f32" else torch.int32),
+                           ref_out.view(torch.int16 if dtype != "f32" else torch.int32))
+        err = max_abs_err(out, o["out"])
+        assert err <= TOL[dtype], err
+        # the second call: a smaller batch (the last sequences, the longest
+        # kept), new q, through the same scratch
+        keep = slice(dr.batch // 2, dr.batch)
+        q2 = torch.flip(q[keep], dims=[1]).contiguous()
+        tables2 = plan.tables[keep].contiguous()
+        lens2 = plan.lens[keep].contiguous()
+        max2 = int(plan.host_lens[keep].max())
+        out2 = torch.full_like(q2, float("nan"))
+        ref2 = torch.empty_like(q2)
+        ws = cache.workspace(q2.shape[0], hq, max2, pt)
+        pa.pa_decode(q2, cache.k_pool, cache.v_pool, tables2, lens2, scale, ref2, ws, max2, pt)
+        pa.pa_decode_noalloc(q2, cache.k_pool, cache.v_pool, tables2, lens2, scale, out2, max2,
+                             pt)
+        torch.cuda.synchronize()
+        assert torch.equal(out2.view(torch.int16 if dtype != "f32" else torch.int32),
+                           ref2.view(torch.int16 if dtype != "f32" else torch.int32))
+        from oracle.attention import paged_decode
+        q2_bits = np.flip(W.query_bits(dr)[keep], axis=1)
+        want2 = paged_decode(np.ascontiguousarray(q2_bits), o["kp"], o["vp"], o["tables"][keep],
+                             o["lens"][keep], scale, dtype)
+        err2 = max_abs_err(out2, want2)
+        assert err2 <= TOL[dtype], err2
+        print(f"noalloc {path}: max_abs_err {err:.2e} then {err2:.2e}, bit-identical to "
+              f"pa_decode", flush=True)
+    finally:
+        pa.pa_set_decode_path(prev)
+
+
+def test_noalloc_refuses_oversize_without_launch():
+    """A shape whose workspace exceeds the static scratch: PA_ERR_SCRATCH,
+    and the output is untouched."""
+    hkv, g, b = 8, 16, 4096
+    pool = torch.zeros((64, hkv, 16, 128), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((b, hkv * g, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, 7.0)
+    tables = torch.zeros((b, 1), dtype=torch.int32, device="cuda")
+    lens = torch.ones(b, dtype=torch.int32, device="cuda")
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_noalloc(q, pool, pool, tables, lens, 0.1, out, 16)
+    assert e.value.status == -9
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
