@@ -72,6 +72,8 @@ PREFILL_DESCRIPTION = ("8B GQA chunked prefill, 1 layer: 16 sequences x 512-toke
 # measured partition + reduce time on MI355X.
 DEFAULT_PARTITION = {"8b_gqa": 2048, "7b_mha": 512, "cow": 2048, "qwen32b_long": 512,
                      "qwen32b_long_bs32": 512, "tiny": 512}
+# every decode workload the task names, in its order
+CONFIG_WORKLOADS = ["tiny", "7b_mha", "8b_gqa", "cow", "qwen32b_long", "qwen32b_long_bs32"]
 
 
 def calibration_copy(pairs: int, wl, log):
@@ -180,6 +182,180 @@ def build_state(d, part_tokens: int, log):
     out = torch.empty_like(q)
     ws = cache.workspace(d.batch, wl.num_q_heads, plan.max_context_len, part_tokens)
     return cache, plan, q, out, ws, k_new, v_new
+
+
+def populate_device(d, part_tokens: int, seed_stream: int = 11):
+    """Pool population for a timing-only record: the workload's allocator
+    scenario, with every written token's K/V drawn on the device (torch's
+    seeded generator, N(0,1) rounded to the dtype) and written by
+    pa_reshape_and_cache; CoW copies first within each batch of writes.
+    Returns the step's state like build_state."""
+    import torch
+    from paged_kv_cache_107_amd.cache import TORCH_DTYPES, PagedKVCache
+    wl = d.wl
+    tdt = TORCH_DTYPES[wl.dtype]
+    gen = torch.Generator(device="cuda").manual_seed(1000 * wl.seed + seed_stream)
+    shape = (d.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    pools = tuple(torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(tdt)
+                  for _ in range(2))
+    cache = PagedKVCache(d.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.dtype,
+                         d.free_order, pools=pools)
+
+    def rows(n):
+        return torch.randn((n, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda",
+                           dtype=torch.float32).to(tdt)
+
+    phases = W.scenario(d)
+    for phase in phases[:-1]:
+        slots, pairs, n_tok = [], [], 0
+
+        def flush():
+            if slots:
+                cache.write_host(rows(n_tok), rows(n_tok), np.concatenate(slots), pairs)
+
+        for op in phase:
+            if op[0] == "create":
+                cache.create()
+            elif op[0] == "fork":
+                cache.fork(op[1])
+            else:
+                sl, pair = cache.reserve(op[1], op[3])
+                if pair is not None:
+                    pairs.append(pair)
+                slots.append(sl)
+                n_tok += op[3]
+                if n_tok > (1 << 18):
+                    flush()
+                    slots, pairs, n_tok = [], [], 0
+        flush()
+    step = phases[-1]
+    plan = cache.plan([op[1] for op in step], 1)
+    n = len(step)
+    k_new, v_new = rows(n), rows(n)
+    q = torch.randn((n, wl.num_q_heads, wl.head_dim), generator=gen, device="cuda",
+                    dtype=torch.float32).to(tdt)
+    out = torch.empty_like(q)
+    ws = cache.workspace(n, wl.num_q_heads, plan.max_context_len, part_tokens)
+    torch.cuda.synchronize()
+    return cache, plan, q, out, ws, k_new, v_new
+
+
+def time_step(cache, plan, q, out, ws, k_new, v_new, wl, part_tokens: int, reps: int):
+    """`reps` decode steps on the launch stream, each pass between its own
+    HIP events: mean microseconds per pass and of the whole step (first
+    event to last)."""
+    import torch
+    import paged_kv_cache_107_amd as pa
+    stream = torch.cuda.current_stream()
+    args = (q, cache.k_pool, cache.v_pool, plan.tables, plan.lens, wl.scale, out, ws,
+            plan.max_context_len, part_tokens)
+    fns = []
+    if plan.pairs.shape[0]:
+        fns.append(("copy_blocks", lambda: pa.pa_copy_blocks(cache.k_pool, cache.v_pool,
+                                                               plan.pairs)))
+    fns += [("reshape_and_cache", lambda: pa.pa_reshape_and_cache(
+                k_new, v_new, plan.slots, cache.k_pool, cache.v_pool)),
+            ("decode_partition", lambda: pa.pa_decode_partition(*args)),
+            ("decode_reduce", lambda: pa.pa_decode_reduce(*args))]
+    for _ in range(5):
+        for _, f in fns:
+            f()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+          for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        for j, (_, f) in enumerate(fns):
+            f()
+            e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    res = {name: 1e3 * float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
+           for j, (name, _) in enumerate(fns)}
+    res["step"] = 1e3 * float(np.mean([e[0].elapsed_time(e[-1]) for e in ev]))
+    return res
+
+
+def measure_configs(names, reps: int, log):
+    """Every other decode workload the task names, each on its own freshly
+    populated cache (device-drawn contents): the decode step's passes timed
+    with HIP events on the launch stream, sequences/s of the step, KV GB/s
+    and the partition kernel's HBM roofline."""
+    import torch
+    res = {}
+    for name in names:
+        d = W.draw(name)
+        wl = d.wl
+        pt = DEFAULT_PARTITION[name]
+        t0 = time.perf_counter()
+        state = populate_device(d, pt)
+        cache, plan = state[0], state[1]
+        t = time_step(*state, wl, pt, reps)
+        ctx = d.context_lens.astype(np.int64)
+        eb = wl.elem_bytes
+        kv = int(ctx.sum()) * 2 * wl.num_kv_heads * wl.head_dim * eb
+        alg = (kv + 2 * d.batch * wl.num_q_heads * wl.head_dim * eb +
+               int(np.sum(-(-ctx // wl.block_size))) * 4 + 4 * d.batch)
+        part = t["decode_partition"]
+        gbps = alg / (part * 1e-6) / 1e9
+        rec = {"workload": DESCRIPTIONS[name], "dtype": wl.dtype, "batch": d.batch,
+               "attended_tokens": int(ctx.sum()), "partition_tokens": pt,
+               "cow_pairs": int(plan.pairs.shape[0]), "kv_bytes": kv, "algorithmic_bytes": alg,
+               "step_us": round(t["step"], 2),
+               "passes_us": {k: round(v, 2) for k, v in t.items() if k != "step"},
+               "seq_per_s": round(d.batch / (t["step"] * 1e-6), 1),
+               "kv_gbps_step": round(kv / (t["step"] * 1e-6) / 1e9, 1),
+               "roofline": {"bound": "hbm", "kernel": "pa_decode_partition",
+                            "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
+        if name == "cow":
+            rec["note"] = ("branches share their 1000-token prefix blocks, so the attended "
+                           "bytes exceed what HBM supplies (shared blocks hit in cache)")
+        if name == "tiny":
+            rec["note"] = "latency-bound (110 KiB of K/V): no bandwidth claim"
+        res[name] = rec
+        log(f"config {name}: step {t['step']:.1f} us, partition {part:.1f} us "
+            f"({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS:.1%}), {rec['seq_per_s']:.0f} seq/s, "
+            f"{rec['cow_pairs']} CoW pairs, populated in {time.perf_counter() - t0:.1f}s")
+        del state, cache, plan
+        torch.cuda.empty_cache()
+    return res
+
+
+def measure_e2e(cache, plan, q, out, ws, k_new, v_new, d, part_tokens: int, steps: int, log):
+    """Real decode steps back to back: each step plans (one batched
+    allocator call, one upload, the resident tables patched on the device)
+    and runs (copies, cache write, attention), so every sequence grows by
+    one token per step.  The host's planning of step k+1 overlaps the
+    device's work of step k.  Reports the host time of a plan (median) and
+    the wall time per step."""
+    import torch
+    wl = d.wl
+    seqs = plan.seqs
+    # the host half alone: each plan timed with the device idle (nothing to
+    # wait for), then its step run
+    host = []
+    for _ in range(steps):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        p = cache.plan(seqs, 1)
+        host.append(time.perf_counter() - h0)
+        cache.run(p, k_new, v_new, q, wl.scale, out, ws, part_tokens)
+    # pipelined: the host plans step k + 1 while the device runs step k
+    rebuilt = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        p = cache.plan(seqs, 1)
+        rebuilt += p.rebuilt
+        cache.run(p, k_new, v_new, q, wl.scale, out, ws, part_tokens)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    host_ms = 1e3 * float(np.median(host))
+    log(f"e2e: {steps} steps, {1e3 * wall:.3f} ms per step ({d.batch / wall:.0f} seq/s), host "
+        f"plan {host_ms:.3f} ms median (device idle), {rebuilt} table rebuilds")
+    return {"steps": steps, "ms_per_step": round(1e3 * wall, 4),
+            "seq_per_s": round(d.batch / wall, 1), "host_plan_ms_median": round(host_ms, 4),
+            "host_plan_ms_p90": round(1e3 * float(np.percentile(host, 90)), 4),
+            "table_rebuilds": rebuilt}
 
 
 def measure_prefill(reps: int, log):
@@ -602,6 +778,13 @@ def main(argv=None):
     ap.add_argument("--prefix-reps", type=int, default=10,
                     help="timed prefill passes per variant on the shared-system-prompt "
                          "workload, with and without the prefix cache (0 = skip)")
+    ap.add_argument("--config-reps", type=int, default=30,
+                    help="timed decode steps on each other named workload (0 = skip)")
+    ap.add_argument("--e2e-steps", type=int, default=50,
+                    help="real decode steps (plan + run) at the end, timing the host "
+                         "planner (0 = skip)")
+    ap.add_argument("--only-configs", action="store_true",
+                    help="time the other named workloads only (for a profiler run)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
@@ -615,6 +798,11 @@ def main(argv=None):
     import paged_kv_cache_107_amd as pa
     torch.cuda.set_device(0)
     pa.lib()
+    others = [n for n in CONFIG_WORKLOADS if n != args.workload]
+    if args.only_configs:
+        print(json.dumps({"configs": measure_configs(others, max(args.config_reps, 1), log)}),
+              flush=True)
+        return 0
     d = W.draw(args.workload)
     wl = d.wl
     pt = args.partition_tokens or DEFAULT_PARTITION[args.workload]
@@ -687,16 +875,6 @@ def main(argv=None):
     seq_per_s = d.batch / (ms_per_step * 1e-3)
     kv_gbps_step = kv_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # Host half of a step (allocator reservations, tables, upload), in steady
-    # state: the median of 5 more steps planned after the timed region.
-    host_ms = []
-    for _ in range(5):
-        t0 = time.perf_counter()
-        cache.plan(plan.seqs, 1)
-        torch.cuda.synchronize()
-        host_ms.append((time.perf_counter() - t0) * 1e3)
-    host_step_ms = float(np.median(host_ms))
-
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(d, out, args.cpu_budget, log)
@@ -709,9 +887,17 @@ def main(argv=None):
     variants = None
     if args.variant_reps > 0 and args.workload == "8b_gqa":
         variants = measure_variants(cache, plan, q, d, args.variant_reps, log)
+    configs = None
+    if args.config_reps > 0:
+        configs = measure_configs(others, args.config_reps, log)
     swap = None
     if args.swap_reps > 0 and args.workload == "8b_gqa":
         swap = measure_swap(cache, d, args.swap_reps, log)
+    # Last (it grows the sequences and patches the step's tables): real
+    # steps, planned and run back to back.
+    e2e = None
+    if args.e2e_steps > 0:
+        e2e = measure_e2e(cache, plan, q, out, ws, k_new, v_new, d, pt, args.e2e_steps, log)
 
     rec = {
         "metric": METRIC,
@@ -747,11 +933,13 @@ def main(argv=None):
             "kernel_us": round(part_us, 2),
         },
         "passes_us": passes_us,
-        "host_step_ms": round(host_step_ms, 3),
+        "host_step_ms": None if e2e is None else e2e["host_plan_ms_median"],
+        "e2e": e2e,
         "cpu_baseline": cpu,
         "prefill": prefill,
         "prefix_cache": prefix,
         "variants": variants,
+        "configs": configs,
         "swap": swap,
     }
     print(json.dumps(rec), flush=True)

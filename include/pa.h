@@ -136,11 +136,23 @@ const char* pa_status_string(int32_t status);
  *                 positions max(0, ctx - W) .. ctx - 1 (its own and the W - 1
  *                 before it); table entries of blocks wholly below that are
  *                 never read (they may be PA_NO_BLOCK).  < 0: PA_ERR_ARG.
+ *   status        device int32, or NULL.  When a table entry inside a
+ *                 sequence's attended range names a block outside [0,
+ *                 num_blocks), the call ORs PA_STATUS_BAD_BLOCK into it; it
+ *                 never clears it (the caller zeroes it before the call and
+ *                 reads it after).  A wrong table otherwise gives plausible
+ *                 wrong numbers with no signal at all (page "vLLM：把 KV 缓存当成
+ *                 虚拟内存", section "KV 的体积从哪来，页表如何把它切开").
  * 8-bit pools: K and V elements are dequantised as code value * k_scale /
  * v_scale (k_scale folded into the score scale, v_scale into the output).
  * Block ids outside [0, num_blocks) are skipped (those tokens do not take
- * part); the output is then unspecified but no access leaves the pool.
+ * part; `status` reports them); the output is then unspecified but no access
+ * leaves the pool.
  * ------------------------------------------------------------------------ */
+/* Bit of the status word: a block id outside the pool inside an attended
+ * range (pa_decode*, pa_prefill). */
+#define PA_STATUS_BAD_BLOCK 1
+
 /* Workspace bytes pa_decode may need for these arguments: the largest need
  * of the kernels that can run this shape under any path setting (so the
  * setting may change without a new workspace).  0 when none is needed or the
@@ -154,7 +166,8 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t max_context_len, float scale,
                     int32_t sliding_window, void* out, void* workspace,
-                    size_t workspace_bytes, int32_t partition_tokens, void* hip_stream);
+                    size_t workspace_bytes, int32_t partition_tokens, int32_t* status,
+                    void* hip_stream);
 
 /* The two passes of pa_decode, callable one at a time (same arguments, same
  * path setting, same stream; pa_decode == pa_decode_partition then
@@ -167,7 +180,7 @@ pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_p
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
                               int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                               float scale, int32_t sliding_window, void* out, void* workspace,
-                              size_t workspace_bytes, int32_t partition_tokens,
+                              size_t workspace_bytes, int32_t partition_tokens, int32_t* status,
                               void* hip_stream);
 
 pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool,
@@ -175,7 +188,8 @@ pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                            float scale, int32_t sliding_window, void* out, void* workspace,
-                           size_t workspace_bytes, int32_t partition_tokens, void* hip_stream);
+                           size_t workspace_bytes, int32_t partition_tokens, int32_t* status,
+                           void* hip_stream);
 
 /* pa_decode without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
@@ -198,7 +212,7 @@ pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_poo
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                             float scale, int32_t sliding_window, void* out,
-                            int32_t partition_tokens, void* hip_stream);
+                            int32_t partition_tokens, int32_t* status, void* hip_stream);
 
 /* Decode kernel family.  PA_PATH_AUTO: the matrix-core kernel for 16-bit
  * pools with head_dim 128 and G = num_q_heads / num_kv_heads in [2, 16], the
@@ -242,14 +256,16 @@ int32_t pa_set_decode_path(int32_t path);
  *   max_context_len, block_tables, max_blocks_per_seq, scale: as pa_decode
  * Supported: f16/bf16 dtype (16-bit or 8-bit pools), head_dim 128, G in
  * {1, 2, 4, 8, 16} (PA_ERR_SHAPE otherwise).  No workspace; one kernel
- * launch.
+ * launch.  status: as pa_decode's (a block outside the pool inside the keys
+ * some row of the chunk attends).
  * ------------------------------------------------------------------------ */
 pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                      const pa_pool_desc* pool, const int32_t* block_tables,
                      int32_t max_blocks_per_seq, const int32_t* query_start,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
                      int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
-                     float scale, int32_t sliding_window, void* out, void* hip_stream);
+                     float scale, int32_t sliding_window, void* out, int32_t* status,
+                     void* hip_stream);
 
 /* ------------------------------------------------------------------------
  * Cache write: decode appends each new token's K/V to the cache (page
@@ -268,6 +284,38 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
 pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
                                int32_t num_tokens, void* k_pool, void* v_pool,
                                const pa_pool_desc* pool, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Block-table upkeep on the device.  A decode step changes each sequence's
+ * table in at most the entries its new positions fall in: a fresh block when
+ * a position starts a logical block (lazy allocation), and the repointed last
+ * block when the first position copies a shared block (copy-on-write); both
+ * are the block of the position's slot (page "放下账簿，打开源码", section
+ * "PagedAttention：虚实分离，按需取用": the table maps a position's logical
+ * block to the physical block its slot lies in).  So device-resident tables
+ * can follow a step from the step's slots alone, without uploading them.
+ * For each row i < num_seqs and each t < tokens_per_seq, with pos =
+ * new_lens[i] - tokens_per_seq + t and slot = slot_mapping[i *
+ * tokens_per_seq + t]:
+ *     block_tables[i][pos / block_size] = slot / block_size   (slot >= 0,
+ *         pos >= 0 and pos / block_size < max_blocks_per_seq; else skipped)
+ *     context_lens[i] = new_lens[i]
+ * The arguments are exactly what pa_seq_append_batch(seqs, num_seqs,
+ * tokens_per_seq) returns for the sequences of those rows (slots_out,
+ * lens_out), copied to the device.  Entries the step does not touch keep
+ * their values, so the rows must hold the sequences' tables from before the
+ * step (any other change, e.g. a fork, a free, a swap-in or a window trim,
+ * needs the rows rebuilt, e.g. from pa_build_tables).  Writes are plain
+ * stores: rows shared by two entries of one call race.
+ *   slot_mapping  device int64 [num_seqs * tokens_per_seq]
+ *   new_lens      device int32 [num_seqs]
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq] (updated)
+ *   context_lens  device int32 [num_seqs] (written)
+ *   block_size    power of two in [1, 65536] (the allocator's)
+ * ------------------------------------------------------------------------ */
+pa_status pa_update_tables(const int64_t* slot_mapping, const int32_t* new_lens, int32_t num_seqs,
+                           int32_t tokens_per_seq, int32_t block_size, int32_t* block_tables,
+                           int32_t max_blocks_per_seq, int32_t* context_lens, void* hip_stream);
 
 /* ------------------------------------------------------------------------
  * Copy-on-write block copy: before the first write into a block that other
@@ -332,7 +380,7 @@ pa_status pa_seq_append(pa_alloc* a, int64_t seq, int32_t n_tokens, int64_t* slo
                         int32_t* cow_pair_out, int32_t* num_cow_out);
 /* One decode step for many sequences: appends n_tokens to each of seqs[0..n)
  * in order.  slots_out [n * n_tokens]; pairs_out [n][2]; *num_pairs_out =
- * pairs written.  The pairs are independent (no dst is another pair's src or
+ * pairs written; lens_out [n] (may be NULL) = each sequence's new length.  The pairs are independent (no dst is another pair's src or
  * dst), so one pa_copy_blocks call can run them all: a cached block whose
  * last holder copies it is held back from the evictable list until the
  * step's last append, and joins it then, in the order of release.  Each
@@ -340,7 +388,8 @@ pa_status pa_seq_append(pa_alloc* a, int64_t seq, int32_t n_tokens, int64_t* slo
  * All or nothing: on PA_ERR_OOM nothing changes.  A sequence named twice is
  * PA_ERR_ARG. */
 pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32_t n_tokens,
-                              int64_t* slots_out, int32_t* pairs_out, int32_t* num_pairs_out);
+                              int64_t* slots_out, int32_t* pairs_out, int32_t* num_pairs_out,
+                              int32_t* lens_out);
 pa_status pa_seq_fork(pa_alloc* a, int64_t parent, int64_t* child_out);
 pa_status pa_seq_share_prefix(pa_alloc* a, int64_t src, int32_t n_tokens, int64_t* seq_out);
 pa_status pa_seq_free(pa_alloc* a, int64_t seq);

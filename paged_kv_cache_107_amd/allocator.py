@@ -36,6 +36,9 @@ class PaAllocator:
             self.num_blocks, self.block_size, None if order is None else _i32p(order),
             C.byref(h)))
         self._h = h
+        # bumped by every call that can change a block table or a length, so
+        # a holder of device copies of tables can tell when they went stale
+        self.epoch = 0
 
     def close(self) -> None:
         if self._h:
@@ -55,6 +58,7 @@ class PaAllocator:
         return s.value
 
     def pa_seq_append(self, seq: int, n_tokens: int) -> Tuple[np.ndarray, Optional[Tuple[int, int]]]:
+        self.epoch += 1
         slots = np.empty(max(n_tokens, 1), dtype=np.int64)
         pair = np.zeros(2, dtype=np.int32)
         ncow = C.c_int32()
@@ -62,29 +66,51 @@ class PaAllocator:
                                                    _i32p(pair), C.byref(ncow)))
         return slots[:n_tokens], ((int(pair[0]), int(pair[1])) if ncow.value else None)
 
-    def pa_seq_append_batch(self, seqs: Sequence[int], n_tokens: int):
-        """Returns (slots [len(seqs) * n_tokens] int64, pairs [P][2] int32)."""
+    def pa_seq_append_batch(self, seqs: Sequence[int], n_tokens: int, with_lens: bool = False):
+        """Returns (slots [len(seqs) * n_tokens] int64, pairs [P][2] int32),
+        plus the new lengths [len(seqs)] int32 with ``with_lens``."""
+        self.epoch += 1
         s = np.ascontiguousarray(seqs, dtype=np.int64)
         n = s.shape[0]
         slots = np.empty(max(n * n_tokens, 1), dtype=np.int64)
         pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        lens = np.empty(max(n, 1), dtype=np.int32)
         npairs = C.c_int32()
         check("pa_seq_append_batch", lib().pa_seq_append_batch(
-            self._h, _i64p(s), n, int(n_tokens), _i64p(slots), _i32p(pairs), C.byref(npairs)))
+            self._h, _i64p(s), n, int(n_tokens), _i64p(slots), _i32p(pairs), C.byref(npairs),
+            _i32p(lens)))
+        if with_lens:
+            return slots[:n * n_tokens], pairs[:npairs.value], lens[:n]
         return slots[:n * n_tokens], pairs[:npairs.value]
 
+    def append_batch_into(self, seqs_ptr, n: int, n_tokens: int, slots_ptr, pairs_ptr,
+                          lens_ptr) -> int:
+        """pa_seq_append_batch into caller buffers (raw addresses of int64
+        seqs [n], int64 slots [n * n_tokens], int32 pairs [n][2], int32 lens
+        [n]); returns the number of pairs."""
+        self.epoch += 1
+        npairs = C.c_int32()
+        check("pa_seq_append_batch", lib().pa_seq_append_batch(
+            self._h, C.cast(seqs_ptr, C.POINTER(C.c_int64)), n, n_tokens,
+            C.cast(slots_ptr, C.POINTER(C.c_int64)), C.cast(pairs_ptr, C.POINTER(C.c_int32)),
+            C.byref(npairs), C.cast(lens_ptr, C.POINTER(C.c_int32))))
+        return npairs.value
+
     def pa_seq_fork(self, parent: int) -> int:
+        self.epoch += 1
         c = C.c_int64()
         check("pa_seq_fork", lib().pa_seq_fork(self._h, int(parent), C.byref(c)))
         return c.value
 
     def pa_seq_share_prefix(self, src: int, n_tokens: int) -> int:
+        self.epoch += 1
         c = C.c_int64()
         check("pa_seq_share_prefix",
               lib().pa_seq_share_prefix(self._h, int(src), int(n_tokens), C.byref(c)))
         return c.value
 
     def pa_seq_free(self, seq: int) -> None:
+        self.epoch += 1
         check("pa_seq_free", lib().pa_seq_free(self._h, int(seq)))
 
     def pa_seq_info(self, seq: int) -> Tuple[int, np.ndarray]:
@@ -134,6 +160,7 @@ class PaAllocator:
 
     def pa_seq_create_prefix(self, tokens: Sequence[int]) -> Tuple[int, int]:
         """(sequence, hit_tokens) for a prompt of token ids."""
+        self.epoch += 1
         t = np.ascontiguousarray(tokens, dtype=np.int32)
         s, hit = C.c_int64(), C.c_int32()
         check("pa_seq_create_prefix", lib().pa_seq_create_prefix(
@@ -141,6 +168,7 @@ class PaAllocator:
         return s.value, hit.value
 
     def pa_seq_append_tokens(self, seq: int, tokens: Sequence[int]):
+        self.epoch += 1
         t = np.ascontiguousarray(tokens, dtype=np.int32)
         n = int(t.size)
         slots = np.empty(max(n, 1), dtype=np.int64)
@@ -167,6 +195,7 @@ class PaAllocator:
     def pa_seq_trim_window(self, seq: int, window: int) -> int:
         """Release the blocks wholly below position len - window; returns the
         number of table entries that became PA_NO_BLOCK."""
+        self.epoch += 1
         n = C.c_int32()
         check("pa_seq_trim_window", lib().pa_seq_trim_window(self._h, int(seq), int(window),
                                                               C.byref(n)))
@@ -178,6 +207,7 @@ class PaAllocator:
         self.num_host_blocks = int(num_host_blocks)
 
     def _swap(self, fn: str, seq: int) -> np.ndarray:
+        self.epoch += 1
         n = self.pa_seq_info(seq)[1].size
         pairs = np.zeros((max(n, 1), 2), dtype=np.int32)
         num = C.c_int32()

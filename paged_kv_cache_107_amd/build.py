@@ -81,5 +81,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_alloc_only(out: str, sanitize: bool = True, verbose: bool = False) -> str:
+    """The host allocator alone (pa_alloc.cpp, plain C++) as a shared library,
+    built with the host compiler, with AddressSanitizer and
+    UndefinedBehaviorSanitizer unless ``sanitize`` is false.  Loaded through
+    PA_ALLOC_LIB (see _lib.py) with the sanitizer runtime preloaded."""
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-I", INCLUDE,
+           "-fno-omit-frame-pointer", os.path.join(CSRC, "pa_alloc.cpp"), "-o", out]
+    if sanitize:
+        cmd[1:1] = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building {out} failed:\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -4,16 +4,25 @@ allocator, and the decode step over them.
 A step has a host half and a device half:
 
 * ``plan``: the allocator reserves one slot per new token (taking blocks
-  lazily, copying shared blocks on write) and the block tables and lengths
-  of the sequences to decode are built; the small index arrays are copied to
-  the device once;
+  lazily, copying shared blocks on write) in one batched call, which writes
+  the slots, the copy pairs and the new lengths straight into a pinned
+  staging buffer; one asynchronous copy moves them to the device.  The
+  block tables stay resident on the device: a step changes a sequence's
+  table only in the blocks its new positions fall in (a fresh block, or the
+  copied last block), which are the blocks of the new slots, so
+  ``pa_update_tables`` patches them from the uploaded slots.  Any other
+  change to the batch's tables (a new batch, a fork, a free, a swap, a
+  window trim, an append outside ``plan``) rebuilds them once, uploaded
+  through the same buffer;
 * ``run``: on the device, in order on one stream, the CoW block copies, the
   new tokens' cache write, then decode attention through the tables.
 
-Everything on the device runs in libpa's HIP kernels.
+A ``StepPlan`` points into buffers the next ``plan`` reuses: it is valid
+until then.  Everything on the device runs in libpa's HIP kernels.
 """
 from __future__ import annotations
 
+import ctypes as C
 import dataclasses
 from typing import List, Optional, Sequence
 
@@ -21,23 +30,59 @@ import numpy as np
 import torch
 
 from .allocator import PaAllocator
-from ._lib import PA_SWAP_IN, PA_SWAP_OUT
-from .ops import (FP8, alloc_workspace, pa_copy_blocks, pa_decode, pa_reshape_and_cache,
-                  pa_swap_blocks)
+from ._lib import PA_SWAP_IN, PA_SWAP_OUT, check, lib
+from .ops import (FP8, _stream, alloc_workspace, pa_copy_blocks, pa_decode,
+                  pa_reshape_and_cache, pa_swap_blocks)
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
 @dataclasses.dataclass
 class StepPlan:
-    """Device-resident index arrays of one decode step."""
+    """Device-resident index arrays of one decode step (valid until the
+    next ``plan``)."""
     seqs: List[int]
     slots: torch.Tensor         # int64 [T]
     pairs: torch.Tensor         # int32 [P][2]
-    tables: torch.Tensor        # int32 [B][max_blocks]
+    tables: torch.Tensor        # int32 [B][max_blocks], -1 past each sequence's blocks
     lens: torch.Tensor          # int32 [B]
     max_context_len: int
     host_lens: np.ndarray
+    rebuilt: bool = True        # tables uploaded whole (else patched from the slots)
+
+
+def _align(x: int, a: int = 256) -> int:
+    return (x + a - 1) // a * a
+
+
+class _Staging:
+    """One step's index arrays: a pinned host buffer and its device copy.
+    Layout: slots int64 [B*n] | lens int32 [B] | pairs int32 [B][2] |
+    tables int32 [B][max_blocks] (rebuilds only)."""
+
+    def __init__(self, n_seqs: int, n_tokens: int, max_blocks: int, device):
+        self.n_seqs, self.n_tokens, self.max_blocks = n_seqs, n_tokens, max_blocks
+        self.o_lens = _align(8 * max(n_seqs * n_tokens, 1))
+        self.o_pairs = self.o_lens + _align(4 * max(n_seqs, 1))
+        self.o_tables = self.o_pairs + _align(8 * max(n_seqs, 1))
+        self.nbytes = self.o_tables + 4 * max(n_seqs * max_blocks, 1)
+        self.host = torch.empty(self.nbytes, dtype=torch.uint8, pin_memory=True)
+        self.dev = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.seqs = torch.empty(max(n_seqs, 1), dtype=torch.int64, pin_memory=True)
+        h = self.host.numpy()
+        self.h_slots = h[:self.o_lens].view(np.int64)
+        self.h_lens = h[self.o_lens:self.o_pairs].view(np.int32)
+        self.h_pairs = h[self.o_pairs:self.o_tables].view(np.int32).reshape(-1, 2)
+        self.h_tables = h[self.o_tables:].view(np.int32)
+        base = self.host.data_ptr()
+        self.p_seqs = self.seqs.data_ptr()
+        self.p_slots, self.p_lens, self.p_pairs = base, base + self.o_lens, base + self.o_pairs
+        self.d_slots = self.dev[:self.o_lens].view(torch.int64)
+        self.d_lens = self.dev[self.o_lens:self.o_pairs].view(torch.int32)
+        self.d_pairs = self.dev[self.o_pairs:self.o_tables].view(torch.int32).view(-1, 2)
+        self.d_tables = self.dev[self.o_tables:].view(torch.int32)
+        self.done = None            # event after the upload that last read `host`
+        self.key = None             # the sequence list `seqs` holds
 
 
 class PagedKVCache:
@@ -69,6 +114,12 @@ class PagedKVCache:
         self.k_pool, self.v_pool = pools
         if tuple(self.k_pool.shape) != shape or tuple(self.v_pool.shape) != shape:
             raise ValueError(f"pools must be {shape}")
+        # device-resident tables of the last planned batch: (seqs tuple,
+        # allocator epoch right after that plan's append, tables [B][cap],
+        # lens [B]); any other allocator change since moves the epoch on
+        self._resident = None
+        self._stages: List[Optional[_Staging]] = [None, None]
+        self._turn = 0
 
     # ------------------------------------------------------------ sequences
     def create(self) -> int:
@@ -151,18 +202,84 @@ class PagedKVCache:
         pr = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
         self.write(k, v, self._dev(slots, torch.int64), self._dev(pr, torch.int32))
 
+    def _stage(self, n: int, n_tokens: int, max_blocks: int) -> _Staging:
+        """The staging buffer of this turn (two alternate, so the host fills
+        one while the other's upload may still be in flight), grown to fit."""
+        st = self._stages[self._turn]
+        if st is None or st.n_seqs < n or st.n_tokens < n_tokens or st.max_blocks < max_blocks:
+            if st is not None and st.done is not None:
+                st.done.synchronize()
+            grow = max(max_blocks, 8 if st is None else st.max_blocks)
+            st = _Staging(n, n_tokens, grow, self.device)
+            self._stages[self._turn] = st
+        elif st.done is not None:
+            st.done.synchronize()          # its last upload has read the host buffer
+        return st
+
     def plan(self, seqs: Sequence[int], n_tokens: int = 1,
-             max_blocks: Optional[int] = None) -> StepPlan:
-        """Reserve n_tokens per sequence and upload the step's index arrays."""
+             max_blocks: Optional[int] = None, stream=None) -> StepPlan:
+        """Reserve n_tokens per sequence (one batched allocator call) and put
+        the step's index arrays on the device: one upload of the staging
+        buffer, then either the resident tables patched from the new slots
+        (``pa_update_tables``) or, after any other change, rebuilt whole."""
         seqs = [int(s) for s in seqs]
-        slots, pairs = self.alloc.pa_seq_append_batch(seqs, n_tokens)
-        lens = np.array([self.alloc.pa_seq_info(s)[0] for s in seqs], dtype=np.int32)
-        if max_blocks is None:
-            max_blocks = int(-(-int(lens.max(initial=0)) // self.block_size))
-        tables, lens = self.alloc.pa_build_tables(seqs, max(max_blocks, 1))
-        return StepPlan(seqs, self._dev(slots, torch.int64), self._dev(pairs, torch.int32),
-                        self._dev(tables, torch.int32), self._dev(lens, torch.int32),
-                        int(lens.max(initial=0)), lens)
+        n = len(seqs)
+        key = tuple(seqs)
+        res = self._resident
+        cap_guess = res[2].shape[1] if res is not None and res[0] == key else 0
+        st = self._stage(n, n_tokens, max(cap_guess, max_blocks or 0))
+        if st.key != key:
+            st.seqs.numpy()[:n] = seqs
+            st.key = key
+        npairs = self.alloc.append_batch_into(st.p_seqs, n, n_tokens, st.p_slots, st.p_pairs,
+                                              st.p_lens) if n else 0
+        lens = st.h_lens[:n].copy()
+        max_len = int(lens.max(initial=0))
+        need = -(-max_len // self.block_size)
+        s = torch.cuda.current_stream() if stream is None else stream
+        incremental = (res is not None and res[0] == key and res[1] == self.alloc.epoch - 1 and
+                       need <= res[2].shape[1] and (max_blocks is None or
+                                                    max_blocks == res[2].shape[1]))
+        if incremental:
+            tables, dlens = res[2], res[3]
+            self._resident = (key, self.alloc.epoch, tables, dlens)
+            nbytes = st.o_pairs + 8 * npairs
+        else:
+            cap = max(max_blocks if max_blocks is not None else -(-need // 8) * 8, need, 1)
+            if cap > st.max_blocks:       # the rebuilt tables must fit the buffer
+                old = st
+                st = _Staging(max(n, old.n_seqs), max(n_tokens, old.n_tokens), cap, self.device)
+                st.h_slots[:n * n_tokens] = old.h_slots[:n * n_tokens]
+                st.h_lens[:n] = old.h_lens[:n]
+                st.h_pairs[:npairs] = old.h_pairs[:npairs]
+                st.seqs.numpy()[:n] = seqs
+                st.key = key
+                self._stages[self._turn] = st
+            ht = st.h_tables[:n * cap]
+            check("pa_build_tables", lib().pa_build_tables(
+                self.alloc._h, C.cast(st.p_seqs, C.POINTER(C.c_int64)), n, cap,
+                C.cast(ht.ctypes.data, C.POINTER(C.c_int32)),
+                C.cast(st.p_lens, C.POINTER(C.c_int32))))
+            nbytes = st.o_pairs + 8 * npairs
+        with torch.cuda.stream(s):
+            st.dev[:nbytes].copy_(st.host[:nbytes], non_blocking=True)
+            if incremental:
+                check("pa_update_tables", lib().pa_update_tables(
+                    st.d_slots.data_ptr(), st.d_lens.data_ptr(), n, n_tokens, self.block_size,
+                    tables.data_ptr(), tables.shape[1], dlens.data_ptr(), _stream(s)))
+            else:   # new resident tables and lengths, straight from the pinned buffer
+                tables = torch.empty((max(n, 1), cap), dtype=torch.int32, device=self.device)[:n]
+                dlens = torch.empty(max(n, 1), dtype=torch.int32, device=self.device)[:n]
+                host_i32 = st.host[st.o_tables:].view(torch.int32)
+                tables.copy_(host_i32[:n * cap].view(n, cap), non_blocking=True)
+                dlens.copy_(st.host[st.o_lens:st.o_pairs].view(torch.int32)[:n],
+                            non_blocking=True)
+                self._resident = (key, self.alloc.epoch, tables, dlens)
+            st.done = torch.cuda.Event()
+            st.done.record(s)
+        self._turn ^= 1
+        return StepPlan(seqs, st.d_slots[:n * n_tokens], st.d_pairs[:npairs], tables, dlens,
+                        max_len, lens, rebuilt=not incremental)
 
     def workspace(self, num_seqs: int, num_q_heads: int, max_context_len: int,
                   partition_tokens: int = 0):

@@ -492,7 +492,8 @@ pa_status pa_swap_query(const pa_alloc* a, pa_swap_stats* stats, int32_t* host_f
 }
 
 pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32_t n_tokens,
-                              int64_t* slots_out, int32_t* pairs_out, int32_t* num_pairs_out) {
+                              int64_t* slots_out, int32_t* pairs_out, int32_t* num_pairs_out,
+                              int32_t* lens_out) {
   if (!a || n < 0 || n_tokens < 0 || (n > 0 && (!seqs || !pairs_out)) || !num_pairs_out ||
       (n > 0 && n_tokens > 0 && !slots_out))
     return PA_ERR_ARG;
@@ -544,6 +545,8 @@ pa_status pa_seq_append_batch(pa_alloc* a, const int64_t* seqs, int32_t n, int32
   }
   for (int32_t b : held) lru_push_back(a, b);
   *num_pairs_out = np;
+  if (lens_out)
+    for (int32_t i = 0; i < n; ++i) lens_out[i] = ptrs[i]->len;
   return PA_OK;
 }
 

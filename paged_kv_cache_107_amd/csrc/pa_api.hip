@@ -158,8 +158,8 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                          int32_t num_q_heads, int32_t max_context_len, float scale,
                          int32_t sliding_window, void* out, void* workspace,
-                         size_t workspace_bytes, int32_t partition_tokens, Prepared* pr,
-                         bool use_scratch = false) {
+                         size_t workspace_bytes, int32_t partition_tokens, int32_t* status,
+                         Prepared* pr, bool use_scratch = false) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || max_blocks_per_seq < 0 ||
@@ -187,7 +187,8 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return PA_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+  if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(status) & 3u))
     return PA_ERR_ARG;
   const bool stream = kernel == pa::DecodeKernel::kMfmaStream;
   const int32_t max_parts = max_parts_of(max_context_len, partition_tokens);
@@ -241,6 +242,7 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
   a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? pool->k_scale : 1.f);
   a.window = sliding_window;
   a.v_scale = fp8 ? pool->v_scale : 1.f;
+  a.status = status;
   pr->dtype = pool->dtype;
   pr->kv = kv_type(pool);
   pr->head_dim = pool->head_dim;
@@ -329,13 +331,13 @@ pa_status pa_decode_partition(const void* q, const void* k_pool, const void* v_p
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
                               int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                               float scale, int32_t sliding_window, void* out, void* workspace,
-                              size_t workspace_bytes, int32_t partition_tokens,
+                              size_t workspace_bytes, int32_t partition_tokens, int32_t* status,
                               void* hip_stream) {
   Prepared pr;
   pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                                 context_lens, num_seqs, num_q_heads, max_context_len, scale,
                                 sliding_window, out, workspace, workspace_bytes, partition_tokens,
-                                &pr);
+                                status, &pr);
   if (st != PA_OK || pr.args.num_seqs == 0) return st;
   return pa::launch_decode_partition(pr.args, pr.dtype, pr.kv, pr.head_dim, pr.kernel,
                                      static_cast<hipStream_t>(hip_stream));
@@ -346,12 +348,13 @@ pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                            float scale, int32_t sliding_window, void* out, void* workspace,
-                           size_t workspace_bytes, int32_t partition_tokens, void* hip_stream) {
+                           size_t workspace_bytes, int32_t partition_tokens, int32_t* status,
+                           void* hip_stream) {
   Prepared pr;
   pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                                 context_lens, num_seqs, num_q_heads, max_context_len, scale,
                                 sliding_window, out, workspace, workspace_bytes, partition_tokens,
-                                &pr);
+                                status, &pr);
   if (st != PA_OK || pr.args.num_seqs == 0 || !needs_reduce(pr)) return st;
   return pa::launch_decode_reduce(pr.args, pr.dtype, pr.head_dim, pr.kernel,
                                   static_cast<hipStream_t>(hip_stream));
@@ -362,12 +365,13 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t max_context_len, float scale,
                     int32_t sliding_window, void* out, void* workspace,
-                    size_t workspace_bytes, int32_t partition_tokens, void* hip_stream) {
+                    size_t workspace_bytes, int32_t partition_tokens, int32_t* status,
+                    void* hip_stream) {
   Prepared pr;
   pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                                 context_lens, num_seqs, num_q_heads, max_context_len, scale,
                                 sliding_window, out, workspace, workspace_bytes, partition_tokens,
-                                &pr);
+                                status, &pr);
   if (st != PA_OK || pr.args.num_seqs == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   st = pa::launch_decode_partition(pr.args, pr.dtype, pr.kv, pr.head_dim, pr.kernel, s);
@@ -380,11 +384,11 @@ pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_poo
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                             float scale, int32_t sliding_window, void* out,
-                            int32_t partition_tokens, void* hip_stream) {
+                            int32_t partition_tokens, int32_t* status, void* hip_stream) {
   Prepared pr;
   pa_status st = prepare_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                                 context_lens, num_seqs, num_q_heads, max_context_len, scale,
-                                sliding_window, out, nullptr, 0, partition_tokens, &pr,
+                                sliding_window, out, nullptr, 0, partition_tokens, status, &pr,
                                 /*use_scratch=*/true);
   if (st != PA_OK || pr.args.num_seqs == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -398,7 +402,8 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                      int32_t max_blocks_per_seq, const int32_t* query_start,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
                      int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
-                     float scale, int32_t sliding_window, void* out, void* hip_stream) {
+                     float scale, int32_t sliding_window, void* out, int32_t* status,
+                     void* hip_stream) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_tokens < 0 || num_q_heads <= 0 ||
@@ -416,7 +421,8 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
       (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
       (reinterpret_cast<uintptr_t>(query_start) & 3u) ||
-      (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+      (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(status) & 3u))
     return PA_ERR_ARG;
   pa::PrefillArgs a{};
   a.q = q;
@@ -440,6 +446,7 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? pool->k_scale : 1.f);
   a.window = sliding_window;
   a.v_scale = fp8 ? pool->v_scale : 1.f;
+  a.status = status;
   return pa::launch_prefill(a, pool->dtype, kv_type(pool), static_cast<hipStream_t>(hip_stream));
 }
 
@@ -456,6 +463,26 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot
     return PA_ERR_ARG;
   return pa::launch_reshape_and_cache(k, v, slot_mapping, num_tokens, k_pool, v_pool, *pool,
                                       static_cast<hipStream_t>(hip_stream));
+}
+
+pa_status pa_update_tables(const int64_t* slot_mapping, const int32_t* new_lens, int32_t num_seqs,
+                           int32_t tokens_per_seq, int32_t block_size, int32_t* block_tables,
+                           int32_t max_blocks_per_seq, int32_t* context_lens, void* hip_stream) {
+  if (num_seqs < 0 || tokens_per_seq < 0 || max_blocks_per_seq < 0 || block_size <= 0 ||
+      block_size > 65536 || (block_size & (block_size - 1)) != 0)
+    return PA_ERR_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!new_lens || !context_lens || (tokens_per_seq > 0 && !slot_mapping) ||
+      (tokens_per_seq > 0 && max_blocks_per_seq > 0 && !block_tables))
+    return PA_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) ||
+      (reinterpret_cast<uintptr_t>(new_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+      (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+    return PA_ERR_ARG;
+  return pa::launch_update_tables(slot_mapping, new_lens, num_seqs, tokens_per_seq,
+                                  ilog2(block_size), block_tables, max_blocks_per_seq,
+                                  context_lens, static_cast<hipStream_t>(hip_stream));
 }
 
 pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool,

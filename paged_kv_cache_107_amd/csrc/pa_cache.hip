@@ -104,6 +104,39 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(
     d[c] = s[c];
 }
 
+// Block-table upkeep of a decode step: one thread per new token; the token
+// at position pos points its logical block at the block its slot lies in.
+__global__ __launch_bounds__(256) void update_tables_kernel(
+    const int64_t* __restrict__ slots, const int32_t* __restrict__ new_lens, int32_t num_seqs,
+    int32_t n_tokens, int32_t log2_bs, int32_t* __restrict__ tables, int32_t max_blocks,
+    int32_t* __restrict__ lens) {
+  const int32_t per_seq = n_tokens > 0 ? n_tokens : 1;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)num_seqs * per_seq) return;
+  const int32_t i = (int32_t)(idx / per_seq), t = (int32_t)(idx - (int64_t)i * per_seq);
+  const int32_t len = new_lens[i];
+  if (t == 0) lens[i] = len;
+  if (n_tokens <= 0) return;
+  const int64_t slot = slots[idx];
+  const int64_t pos = (int64_t)len - n_tokens + t;
+  if (slot < 0 || pos < 0) return;
+  const int64_t j = pos >> log2_bs;
+  if (j >= max_blocks) return;
+  tables[(int64_t)i * max_blocks + j] = (int32_t)(slot >> log2_bs);
+}
+
+pa_status launch_update_tables(const int64_t* slots, const int32_t* new_lens, int32_t num_seqs,
+                               int32_t n_tokens, int32_t log2_bs, int32_t* tables,
+                               int32_t max_blocks, int32_t* lens, hipStream_t st) {
+  const int64_t total = (int64_t)num_seqs * (n_tokens > 0 ? n_tokens : 1);
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks == 0) return PA_OK;
+  if (blocks > 0x7FFFFFFF) return PA_ERR_ARG;
+  hipLaunchKernelGGL(update_tables_kernel, dim3((unsigned)blocks), dim3(256), 0, st, slots,
+                     new_lens, num_seqs, n_tokens, log2_bs, tables, max_blocks, lens);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 static int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
 
 template <class E>

@@ -218,9 +218,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
   // an empty descriptor: its loads return zeros without touching memory, so
   // every ring slot always has the same loads in flight and the wait counts
   // stay static.  Returns whether the tile holds data.
+  bool bad = false;  // a tile of the partition named a block outside the pool
   auto issue = [&](int k, Tile& t) -> bool {
     const int blk = k < my_n ? __builtin_amdgcn_readlane(ids, k) : -1;
     const bool ok = (unsigned)blk < (unsigned)a.num_blocks;
+    bad |= k < my_n && !ok;
     const int tok = t0 + kTile * (w + kWaves * k);
     const size_t off = ok ? (size_t)blk * block_stride + (size_t)(tok & bs_mask) * D : 0;
     const uint32_t bytes = ok ? Tile::kBytes : 0u;
@@ -310,6 +312,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
     }
   }
 
+  report_bad_block(a.status, bad);
   // wave state -> LDS
   l = across_groups_sum<16>(l);
   float* sm_m = smem;
@@ -537,6 +540,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   u32x4 qn[4];
   bool qn_full = false;
   int qn_i = 0, qn_g = 0;
+  bool bad = false;  // a tile of the run named a block outside the pool
   auto issue = [&](Tile& tile) -> bool {
     bool ok = false;
     size_t off = 0;
@@ -548,6 +552,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
         qn_g = ic.g;
       }
       ok = (unsigned)iblk < (unsigned)a.num_blocks;
+      bad |= !ok;
       if (ok)
         off = (size_t)iblk * block_stride + (size_t)ic.g * head_stride +
               (size_t)(((ic.t + ic.ts) * kTile) & bs_mask) * D;
@@ -709,6 +714,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
     }
   } while (crem > 0);
 
+  report_bad_block(a.status, bad);
   // The run's last segment (still in cc): if it starts its pair and the pair
   // goes on, this rank owns the pair's merge.  Only a last segment can.
   if (lane == 0) {
@@ -767,10 +773,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
   const S* kbase = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride + r0 * D + cl * EPL;
   const S* vbase = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride + r0 * D + cl * EPL;
 
+  bool bad = false;  // a tile of the partition named a block outside the pool
   auto load_tile = [&](int j, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) -> bool {
     const int tok = t0 + kTile * j;
     const int blk = table[tok >> a.log2_bs];
-    if ((unsigned)blk >= (unsigned)a.num_blocks) return false;
+    if ((unsigned)blk >= (unsigned)a.num_blocks) {
+      bad = true;
+      return false;
+    }
     const size_t off = (size_t)blk * block_stride + (size_t)(tok & bs_mask) * D;
 #pragma unroll
     for (int k = 0; k < LPT; ++k) {
@@ -858,6 +868,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu(DecodeArgs a) 
     okc = okn;
   }
 
+  report_bad_block(a.status, bad);
   float* sm_m = smem;
   float* sm_l = smem + kWaves * 16;
   float* sm_o = smem + 2 * kWaves * 16;

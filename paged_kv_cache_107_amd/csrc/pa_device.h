@@ -93,6 +93,15 @@ __device__ __forceinline__ u32x2 buffer_load8(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
+// ------------------------------------------------------------- status
+// ORs kStatusBadBlock into the caller's status word when this wave met a
+// table entry outside the pool inside an attended range (`bad`, uniform
+// across the wave).  One lane does it, with a vector global atomic.
+__device__ __forceinline__ void report_bad_block(int32_t* status, bool bad) {
+  if (status != nullptr && bad && (threadIdx.x % kWave) == 0)
+    __hip_atomic_fetch_or(status, kStatusBadBlock, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------- math
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }

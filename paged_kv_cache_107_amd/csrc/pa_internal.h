@@ -38,7 +38,12 @@ struct DecodeArgs {
   int32_t stream_waves;  // waves of the stream split's grid
   int32_t window;        // sliding window in positions, 0 = none
   float v_scale;         // output factor: v_scale for 8-bit pools, else 1
+  int32_t* status;       // caller's status word (kStatusBadBlock is ORed in), or null
 };
+
+// Bit of the caller's status word: a table entry inside an attended range
+// named a block outside [0, num_blocks).
+constexpr int32_t kStatusBadBlock = 1;
 
 // Decode kernel families.
 enum class DecodeKernel {
@@ -88,6 +93,7 @@ struct PrefillArgs {
   float scale_log2;  // softmax scale times log2(e) (times k_scale for 8-bit pools)
   int32_t window;    // sliding window in positions, 0 = none
   float v_scale;     // output factor: v_scale for 8-bit pools, else 1
+  int32_t* status;   // caller's status word, or null
 };
 
 bool prefill_supports(int dtype, int head_dim, int group);
@@ -102,6 +108,9 @@ inline int pool_elem_bytes(const pa_pool_desc& pool) {
 pa_status launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
                                    int32_t num_tokens, void* k_pool, void* v_pool,
                                    const pa_pool_desc& pool, hipStream_t st);
+pa_status launch_update_tables(const int64_t* slots, const int32_t* new_lens, int32_t num_seqs,
+                               int32_t n_tokens, int32_t log2_bs, int32_t* tables,
+                               int32_t max_blocks, int32_t* lens, hipStream_t st);
 pa_status launch_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc& pool,
                              const int32_t* pairs, int32_t num_pairs, hipStream_t st);
 pa_status launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,

@@ -494,6 +494,18 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
           u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
     }
   }
+  // Table entries outside the pool among the blocks some row of the item
+  // attends (keys [kfirst, kend_wg)): reported to the caller's status word.
+  // Checked after the walk, from the table alone, so the walk is unchanged.
+  if (a.status != nullptr) {
+    const int kfirst =
+        WIN ? max(max(ctx - n + max(top - (kLdsWaves - 1), 0) * QT, 0) - W + 1, 0) : 0;
+    bool bad = false;
+    for (int j = (kfirst >> a.log2_bs) + (int)threadIdx.x; j <= ((kend_wg - 1) >> a.log2_bs);
+         j += kLdsThreads)
+      bad |= (unsigned)table[j] >= (unsigned)a.num_blocks;
+    report_bad_block(a.status, __builtin_amdgcn_ballot_w64(bad) != 0);
+  }
 }
 
 template <class E, KvType KV>

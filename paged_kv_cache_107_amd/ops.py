@@ -86,8 +86,20 @@ def alloc_workspace(k_pool: torch.Tensor, num_seqs: int, num_q_heads: int, max_c
     return torch.empty(n, dtype=torch.uint8, device=k_pool.device) if n else None
 
 
+def _status_ptr(status: Optional[torch.Tensor]) -> C.c_void_p:
+    """A device int32 tensor (at least one element) the kernels OR status
+    bits into (PA_STATUS_BAD_BLOCK), or None."""
+    if status is None:
+        return C.c_void_p(0)
+    _need_cuda("status", status, torch.int32)
+    if status.numel() < 1:
+        raise ValueError("status needs at least one element")
+    return _ptr(status)
+
+
 def _decode_call(fn_name, q, k_pool, v_pool, block_tables, context_lens, scale, out,
-                 workspace, max_context_len, partition_tokens, stream, sliding_window, kv_scales):
+                 workspace, max_context_len, partition_tokens, stream, sliding_window, kv_scales,
+                 status=None):
     act = _act_dtype(k_pool, q)
     desc = _check_pools(k_pool, v_pool, act, kv_scales)
     _need_cuda("q", q, act)
@@ -107,24 +119,24 @@ def _decode_call(fn_name, q, k_pool, v_pool, block_tables, context_lens, scale, 
     st = fn(_ptr(q), _ptr(k_pool), _ptr(v_pool), C.byref(desc), _ptr(block_tables),
             int(block_tables.shape[1]), _ptr(context_lens), int(b), int(hq),
             int(max_context_len), float(scale), int(sliding_window), _ptr(out), _ptr(workspace),
-            ws_bytes, int(partition_tokens), _stream(stream))
+            ws_bytes, int(partition_tokens), _status_ptr(status), _stream(stream))
     check(fn_name, st)
     return out
 
 
 def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
               max_context_len, partition_tokens=0, stream=None, sliding_window=0,
-              kv_scales=(1.0, 1.0)):
+              kv_scales=(1.0, 1.0), status=None):
     """Paged decode attention (partition + reduce).  See pa.h.  kv_scales:
     (k_scale, v_scale) of an 8-bit pool."""
     return _decode_call("pa_decode", q, k_pool, v_pool, block_tables, context_lens, scale, out,
                         workspace, max_context_len, partition_tokens, stream, sliding_window,
-                        kv_scales)
+                        kv_scales, status)
 
 
 def pa_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out,
                       max_context_len, partition_tokens=0, stream=None, sliding_window=0,
-                      kv_scales=(1.0, 1.0)):
+                      kv_scales=(1.0, 1.0), status=None):
     """pa_decode with the library's static device scratch as its workspace:
     the call allocates nothing (for callers that cannot).  See pa.h."""
     act = _act_dtype(k_pool, q)
@@ -142,30 +154,30 @@ def pa_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out,
                                  _ptr(block_tables), int(block_tables.shape[1]),
                                  _ptr(context_lens), int(b), int(hq), int(max_context_len),
                                  float(scale), int(sliding_window), _ptr(out),
-                                 int(partition_tokens), _stream(stream))
+                                 int(partition_tokens), _status_ptr(status), _stream(stream))
     check("pa_decode_noalloc", st)
     return out
 
 
 def pa_decode_partition(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
                         max_context_len, partition_tokens=0, stream=None, sliding_window=0,
-                        kv_scales=(1.0, 1.0)):
+                        kv_scales=(1.0, 1.0), status=None):
     return _decode_call("pa_decode_partition", q, k_pool, v_pool, block_tables, context_lens,
                         scale, out, workspace, max_context_len, partition_tokens, stream,
-                        sliding_window, kv_scales)
+                        sliding_window, kv_scales, status)
 
 
 def pa_decode_reduce(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
                      max_context_len, partition_tokens=0, stream=None, sliding_window=0,
-                     kv_scales=(1.0, 1.0)):
+                     kv_scales=(1.0, 1.0), status=None):
     return _decode_call("pa_decode_reduce", q, k_pool, v_pool, block_tables, context_lens,
                         scale, out, workspace, max_context_len, partition_tokens, stream,
-                        sliding_window, kv_scales)
+                        sliding_window, kv_scales, status)
 
 
 def pa_prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale, out,
                max_query_len, max_context_len, stream=None, sliding_window=0,
-               kv_scales=(1.0, 1.0)):
+               kv_scales=(1.0, 1.0), status=None):
     """Chunked prefill attention over the paged cache.  See pa.h.
 
     q, out [num_tokens][num_q_heads][head_dim]; query_start int32 [B+1];
@@ -187,7 +199,8 @@ def pa_prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale
     st = lib().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), C.byref(desc), _ptr(block_tables),
                           int(block_tables.shape[1]), _ptr(query_start), _ptr(context_lens),
                           int(b), int(t), int(hq), int(max_query_len), int(max_context_len),
-                          float(scale), int(sliding_window), _ptr(out), _stream(stream))
+                          float(scale), int(sliding_window), _ptr(out), _status_ptr(status),
+                          _stream(stream))
     check("pa_prefill", st)
     return out
 

@@ -80,7 +80,7 @@ def decode_status(desc, **kw):
     return pa.lib().pa_decode(args["q"], args["k"], args["v"], C.byref(desc), args["tables"],
                               args["maxb"], args["lens"], args["b"], args["hq"], args["maxctx"],
                               args["scale"], args["window"], args["out"], args["ws"], args["wsb"],
-                              args["part"], None)
+                              args["part"], args.get("status"), None)
 
 
 def test_decode_validation():
@@ -102,6 +102,7 @@ def test_decode_validation():
     assert decode_status(ok, b=0) == 0                                         # nothing to do
     assert decode_status(pa_pool_desc(64, 16, 2, 128, pa.PA_F32), hq=2 * 16) == -3  # f32 G=16
     assert decode_status(ok, window=-1) == -1                                  # negative window
+    assert decode_status(ok, status=C.c_void_p((1 << 20) + 2)) == -1           # misaligned status
 
 
 def test_fp8_pool_validation():
@@ -170,7 +171,7 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
 
     def call(desc, b, hq, maxctx, q=FAKE):
         return lib.pa_decode_noalloc(q, FAKE, FAKE, C.byref(desc), FAKE, 8, FAKE, b, hq, maxctx,
-                                     0.1, 0, FAKE, 0, None)
+                                     0.1, 0, FAKE, 0, None, None)
     assert call(big, 4096, 128, 100) == -9
     assert call(pa_pool_desc(64, 16, 2, 96, pa.PA_BF16), 2, 8, 100) == -3   # head_dim
     assert call(big, 2, 7, 100) == -3                                         # Hq % Hkv

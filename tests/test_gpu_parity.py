@@ -241,13 +241,24 @@ def test_bad_block_ids_inside_a_sequence(path, decode_path):
     tables[1, 7] = -7
     tables[1, 12] = 1 << 30
     out = torch.full_like(g["out"], float("nan"))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
     pa.pa_decode(g["q"], cache.k_pool, cache.v_pool, tables, plan.lens, d.wl.scale, out, g["ws"],
-                 plan.max_context_len)
+                 plan.max_context_len, status=status)
     torch.cuda.synchronize()
     for i in (0, 2, 3):
         assert torch.equal(out[i], g["out"][i])
     assert torch.all(torch.isfinite(out[1].float()))
     assert torch.equal(cache.k_pool, kp0) and torch.equal(cache.v_pool, vp0)
+    assert int(status.item()) == pa.PA_STATUS_BAD_BLOCK      # the caller is told
+    # the clean tables: no report; a bad id only past a sequence's length
+    # (never read): no report either
+    status.zero_()
+    clean = plan.tables.clone()
+    clean[2, 5:] = nb + 5                                    # sequence 2 has 5 blocks
+    pa.pa_decode(g["q"], cache.k_pool, cache.v_pool, clean, plan.lens, d.wl.scale, out, g["ws"],
+                 plan.max_context_len, status=status)
+    torch.cuda.synchronize()
+    assert torch.equal(out, g["out"]) and int(status.item()) == 0
 
 
 def test_zero_length_and_clamping():

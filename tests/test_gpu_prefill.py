@@ -191,14 +191,21 @@ def test_bad_block_ids_inside_a_sequence():
     tables[1, 2] = nb + 1
     tables[1, 9] = -3
     out = torch.full_like(g["q"], float("nan"))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
     pa.pa_prefill(g["q"], cache.k_pool, cache.v_pool, tables, g["qs"], g["lens"], d.wl.scale, out,
-                  g["max_q"], g["max_ctx"])
+                  g["max_q"], g["max_ctx"], status=status)
     torch.cuda.synchronize()
     qs = d.query_start
     for i in (0, 2):
         assert torch.equal(out[qs[i]:qs[i + 1]], g["out"][qs[i]:qs[i + 1]])
     assert torch.all(torch.isfinite(out[qs[1]:qs[2]].float()))
     assert torch.equal(cache.k_pool, kp0) and torch.equal(cache.v_pool, vp0)
+    assert int(status.item()) == pa.PA_STATUS_BAD_BLOCK
+    status.zero_()
+    pa.pa_prefill(g["q"], cache.k_pool, cache.v_pool, g["tables"], g["qs"], g["lens"],
+                  d.wl.scale, out, g["max_q"], g["max_ctx"], status=status)
+    torch.cuda.synchronize()
+    assert torch.equal(out, g["out"]) and int(status.item()) == 0
 
 
 def test_batches_above_the_longest_first_limit():

@@ -48,10 +48,13 @@ def decode_gpu(cache, seqs, q, scale, window=0, kv_scales=(1.0, 1.0), max_blocks
     tables, lens32 = cache.alloc.pa_build_tables(seqs, mb)
     out = torch.full_like(q, float("nan"))
     ws = cache.workspace(len(seqs), q.shape[1], int(lens.max()))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
     pa.pa_decode(q, cache.k_pool, cache.v_pool, torch.from_numpy(tables).cuda(),
                  torch.from_numpy(lens32).cuda(), scale, out, ws, int(lens.max()),
-                 sliding_window=window, kv_scales=kv_scales)
+                 sliding_window=window, kv_scales=kv_scales, status=status)
     torch.cuda.synchronize()
+    # holes a window trim left below the window are never read: no report
+    assert int(status.item()) == 0
     return out, tables, lens32
 
 
@@ -157,10 +160,12 @@ def test_windowed_prefill_after_trims(window, g):
     tables, _ = cache.alloc.pa_build_tables(list(range(d.batch)), gp["host_tables"].shape[1])
     assert (tables == pa.PA_NO_BLOCK).any()
     out = torch.full_like(gp["q"], float("nan"))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
     pa.pa_prefill(gp["q"], cache.k_pool, cache.v_pool, torch.from_numpy(tables).cuda(),
                   gp["qs"], gp["lens"], d.wl.scale, out, gp["max_q"], gp["max_ctx"],
-                  sliding_window=window)
+                  sliding_window=window, status=status)
     torch.cuda.synchronize()
+    assert int(status.item()) == 0          # the released blocks are below every window
     want = paged_prefill(W.prefill_query_bits(d), o["kp"], o["vp"], o["tables"], d.query_start,
                          o["lens"], d.wl.scale, "bf16", window=window)
     err = max_abs_err(out, want)
