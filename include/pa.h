@@ -267,6 +267,17 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                      float scale, int32_t sliding_window, void* out, int32_t* status,
                      void* hip_stream);
 
+/* Prefill kernel.  PA_PREFILL_LDS: the K/V tiles of a 32-key step are loaded
+ * through registers into LDS (16-bit and 8-bit pools).  PA_PREFILL_DMA: the
+ * tiles go from memory straight into LDS and the P.V operands are read from
+ * it transposed (16-bit pools only; PA_ERR_SHAPE for 8-bit pools).
+ * PA_PREFILL_AUTO: the faster of the two on the measured workloads (today
+ * the LDS kernel).  Results agree up to the order of fp32 sums.
+ * Process-wide; returns the previous value (-1 for an unknown path, which
+ * leaves the setting unchanged). */
+typedef enum { PA_PREFILL_AUTO = 0, PA_PREFILL_LDS = 1, PA_PREFILL_DMA = 2 } pa_prefill_path;
+int32_t pa_set_prefill_path(int32_t path);
+
 /* ------------------------------------------------------------------------
  * Cache write: decode appends each new token's K/V to the cache (page
  * "Lazy Allocation 与 Copy-on-Write 在 LLM 推理系统中的应用", section 2.1), at

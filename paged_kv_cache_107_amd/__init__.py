@@ -10,8 +10,9 @@ tensors), ``allocator`` and ``cache`` (a per-layer driver of both).
 """
 from ._lib import (LIB_PATH, PA_BF16, PA_F16, PA_F32, PA_KV_FP8_E4M3, PA_KV_SAME,  # noqa: F401
                    PA_NO_BLOCK, PA_PATH_AUTO, PA_PATH_MFMA, PA_PATH_MFMA_GRID, PA_PATH_VALU,
+                   PA_PREFILL_AUTO, PA_PREFILL_DMA, PA_PREFILL_LDS,
                    PA_STATUS_BAD_BLOCK, PA_SWAP_IN, PA_SWAP_OUT, SIGNATURES, PaError, lib)
 from .allocator import PaAllocator  # noqa: F401
 from .ops import (FP8, alloc_workspace, pa_copy_blocks, pa_decode, pa_decode_noalloc,  # noqa: F401
                   pa_decode_partition, pa_decode_reduce, pa_decode_workspace_bytes, pa_prefill, pa_reshape_and_cache,
-                  pa_set_decode_path, pa_swap_blocks, pool_desc)
+                  pa_set_decode_path, pa_set_prefill_path, pa_swap_blocks, pool_desc)

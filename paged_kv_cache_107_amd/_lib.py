@@ -18,6 +18,7 @@ PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 PA_NO_BLOCK = -(2 ** 31)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_PATH_AUTO, PA_PATH_VALU, PA_PATH_MFMA, PA_PATH_MFMA_GRID = 0, 1, 2, 3
+PA_PREFILL_AUTO, PA_PREFILL_LDS, PA_PREFILL_DMA = 0, 1, 2
 
 
 PA_KV_SAME, PA_KV_FP8_E4M3 = 0, 1
@@ -52,6 +53,7 @@ SIGNATURES = {
     "pa_abi_version": (_i32, []),
     "pa_status_string": (C.c_char_p, [_i32]),
     "pa_set_decode_path": (_i32, [_i32]),
+    "pa_set_prefill_path": (_i32, [_i32]),
     "pa_decode_workspace_bytes": (_sz, [_desc, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_partition": (_i32, _DECODE_ARGS),

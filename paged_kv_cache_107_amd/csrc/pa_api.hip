@@ -25,6 +25,7 @@ constexpr int32_t kMaxPartition = 4096;
 constexpr int32_t kMaxGridYZ = 65535;
 
 std::atomic<int32_t> g_decode_path{PA_PATH_AUTO};
+std::atomic<int32_t> g_prefill_path{PA_PREFILL_AUTO};
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -309,6 +310,11 @@ int32_t pa_set_decode_path(int32_t path) {
   return g_decode_path.exchange(path);
 }
 
+int32_t pa_set_prefill_path(int32_t path) {
+  if (path != PA_PREFILL_AUTO && path != PA_PREFILL_LDS && path != PA_PREFILL_DMA) return -1;
+  return g_prefill_path.exchange(path);
+}
+
 size_t pa_decode_workspace_bytes(const pa_pool_desc* pool, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_context_len,
                                  int32_t partition_tokens) {
@@ -447,7 +453,8 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.window = sliding_window;
   a.v_scale = fp8 ? pool->v_scale : 1.f;
   a.status = status;
-  return pa::launch_prefill(a, pool->dtype, kv_type(pool), static_cast<hipStream_t>(hip_stream));
+  return pa::launch_prefill(a, pool->dtype, kv_type(pool), g_prefill_path.load(),
+                            static_cast<hipStream_t>(hip_stream));
 }
 
 pa_status pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,

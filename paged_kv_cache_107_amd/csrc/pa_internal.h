@@ -98,7 +98,7 @@ struct PrefillArgs {
 
 bool prefill_supports(int dtype, int head_dim, int group);
 int prefill_query_blocks(int max_query_len, int group);  // per sequence, grid bound
-pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, hipStream_t st);
+pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, int path, hipStream_t st);
 
 // Pool element bytes for a valid descriptor.
 inline int pool_elem_bytes(const pa_pool_desc& pool) {

@@ -103,13 +103,14 @@ __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
     // [start * Z, (start + cnt) * Z), sequence by sequence.  The item's class is found
     // from the counts, then its sequence -- the j-th of the class in batch
     // order -- by one wave with ballots over 64 sequences at a time.
-    __shared__ int s_cls[kLptSeqs], s_cnt[kClasses], s_pick[3];
+    __shared__ uint8_t s_cls[kLptSeqs];  // length class of each sequence (< kClasses)
+    __shared__ int s_cnt[kClasses], s_pick[3];
     const int t = threadIdx.x;
     for (int c = t; c < kClasses; c += THREADS) s_cnt[c] = 0;
     __syncthreads();
     for (int u = t; u < B; u += THREADS) {
       const int c = min(max(clamp_ctx(a, u), 0) >> kLenClassShift, kClasses - 1);
-      s_cls[u] = c;
+      s_cls[u] = (uint8_t)c;
       atomicAdd(&s_cnt[c], 1);
     }
     __syncthreads();
@@ -508,6 +509,429 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
 }
 
+// ----------------------------------------------------------------------------
+// Kernel for 16-bit pools: the step's K/V tiles go from memory straight into
+// LDS (direct-to-LDS buffer loads: no register staging, no LDS stores), the
+// products run on v_mfma_f32_32x32x16, and the P.V product's V^T operands
+// come out of LDS transposed (ds_read_b64_tr_b16), so no byte permutes run.
+//
+// A wave owns 32 query rows, the 32 columns of S^T = K . Q^T; a step is 32
+// keys (two 16-key tiles), so S^T is one 32 x 32 product (8 MFMAs over
+// head_dim) and O^T += V^T . P^T is four 32-row d-tiles x two 16-key k-steps
+// (8 MFMAs).  The rows of the K operand are permuted (key pi(m) in row m:
+// bits 2 and 3 of m swapped) so that the S^T result a lane holds -- 16 keys
+// of its own query column -- is in the order the P^T operand takes: value
+// v = key 16 (v / 8) + 8 (lane / 32) + v % 8.  Each lane keeps the softmax
+// state of its column (shared with its partner lane ^ 32) with the lazy
+// rescale of the decode kernel.
+//
+// LDS: three stages of [K 32 x 128 | V 32 x 128] 16-bit rows; a row's 16
+// chunks of 16 bytes are stored in the order chunk ^ swz(row), so the K
+// operand reads (16 rows, one chunk) and the transposed V reads (4 rows, two
+// chunks) spread over the banks.  A workgroup's four waves load one step
+// (16 KiB, four 1 KiB loads per wave) two steps ahead, with one barrier per
+// step.
+#ifndef PF_PRIO
+#define PF_PRIO 0    // raise wave priority around the products
+#endif
+#ifndef PF_WAVES
+#define PF_WAVES 4   // waves per workgroup (4 or 8)
+#endif
+constexpr int kDmaWaves = PF_WAVES;
+constexpr int kDmaPieces = 8 / kDmaWaves;  // 1 KiB pieces of K (and of V) a wave loads per step
+constexpr int kDmaThreads = kDmaWaves * kWave;
+constexpr int kDmaRows = 32;                      // query rows per wave
+constexpr int kDmaKeys = 32;                      // keys per step
+constexpr int kRowBytes128 = 128 * 2;             // one 16-bit K or V row
+constexpr int kDmaRegion = kDmaKeys * kRowBytes128;  // K or V of one step: 8 KiB
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4v lds_i16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// A linear (XOR) map of the row's low four bits, chosen so that both read
+// patterns touch distinct banks whether the LDS serves 128 or 256 bytes per
+// cycle: the K operand reads (16 rows, one chunk) and the transposed V reads
+// (4 consecutive rows, 2 or 4 consecutive chunks).
+__device__ __forceinline__ int dma_swz(int r) {
+  return ((r & 1) * 10) ^ ((r & 2) << 1) ^ ((r & 4) >> 1) ^ ((r & 8) >> 3);
+}
+// byte offset of (row r, 16-byte chunk c) in a 32-row region
+__device__ __forceinline__ int dma_pos(int r, int c) { return (r * 16 + (c ^ dma_swz(r))) * 16; }
+
+// LDS operand reads for the DMA kernel, written as inline asm with their wait
+// inside the block.  The stages are filled by direct-to-LDS loads; the
+// compiler cannot tell which stage a pending load writes, and before a read
+// of a stage it would otherwise wait for every load in flight -- including
+// those of the steps ahead, just issued.  The kernel's own counter waits and
+// barriers order the loads and the reads.  Every output is used.
+__device__ __forceinline__ void lds_read8_b128(u32x4 (&r)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+// Eight transposed 64-bit reads (ds_read_b64_tr_b16), paired into four
+// 128-bit operands: r[j] = {read 2 j, read 2 j + 1}.
+__device__ __forceinline__ void lds_read8_tr16(u32x4 (&r)[4], const uint32_t (&a)[8]) {
+  u32x2 x[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+        "=&v"(x[6]), "=&v"(x[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = u32x4{x[2 * j][0], x[2 * j][1], x[2 * j + 1][0], x[2 * j + 1][1]};
+}
+
+template <class E>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma32<BF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <class E, bool WIN>
+__global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_dma(PrefillArgs a) {
+  constexpr int D = 128;
+  using S = typename E::storage;
+  __shared__ __attribute__((aligned(1024))) char s_st0[2 * kDmaRegion];
+  __shared__ __attribute__((aligned(1024))) char s_st1[2 * kDmaRegion];
+  __shared__ __attribute__((aligned(1024))) char s_st2[2 * kDmaRegion];
+  __shared__ __attribute__((aligned(1024))) char s_st3[2 * kDmaRegion];
+  const int g = blockIdx.x;
+  const int Z = gridDim.y;
+  const int k = (int)blockIdx.y + Z * (int)blockIdx.z;
+  int i, zq;
+  pick_item<kDmaThreads>(a, k, Z, i, zq);
+  const int G = a.group, QT = kDmaRows / G;  // chunk tokens per wave
+  const int qa = a.query_start[i], qb = a.query_start[i + 1];
+  if (qa < 0 || qb > a.num_tokens || qb <= qa) return;  // the whole workgroup
+  const int n = qb - qa, nq = min(n, a.max_query);
+  const int nqb = ceil_div(nq, QT);
+  const int top = nqb - 1 - kDmaWaves * zq;  // the item's latest query block
+  if (top < 0) return;                       // the whole workgroup
+  const int w = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int c32 = lane & 31, h = lane >> 5;
+  const int ctx = clamp_ctx(a, i);
+  const int kend_wg = ctx - n + min(top * QT + QT, nq);  // the walk: keys [0, kend_wg)
+  const int blk = top - w;                               // this wave's query block
+  const int tok0 = blk * QT, ntok = blk >= 0 ? min(QT, nq - tok0) : 0;
+  const int pos0 = ctx - n + tok0;
+  const int kend = blk >= 0 ? pos0 + ntok : 0;
+  S* out = reinterpret_cast<S*>(a.out);
+
+  // this lane's query column: token tl, head hh
+  const int tl = c32 / G, hh = c32 - tl * G;
+  const bool live = tl < ntok && pos0 + tl >= 0;
+  const int lim = live ? pos0 + tl : kend - 1;
+  const int row = tl < ntok ? (qa + tok0 + tl) * a.num_q_heads + g * G + hh : -1;
+  if (kend_wg <= 0) {  // every position of the item negative: zero rows
+    if (row >= 0)
+      for (int d = 4 * h; d < D; d += 8)
+        *reinterpret_cast<uint2*>(out + (size_t)row * D + d) = uint2{0u, 0u};
+    return;  // the whole workgroup
+  }
+  const bool mine = kend > 0;
+
+  // Q^T operand of k-step s (head_dim 16 s .. 16 s + 15): elements
+  // 16 s + 8 h .. +7 of the lane's query row.
+  u32x4 qv[8];
+  {
+    const S* qrow = reinterpret_cast<const S*>(a.q) + (size_t)max(row, 0) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qv[s] = row >= 0 ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
+  }
+  const float c = fabsf(a.scale_log2), inv_c = 1.f / c;
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+
+  const int bs_mask = (1 << a.log2_bs) - 1;
+  const size_t head_stride = (size_t)D << a.log2_bs;
+  const size_t block_stride = head_stride * a.num_kv_heads;
+  const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
+  const S* kbase0 = reinterpret_cast<const S*>(a.k_pool) + (size_t)g * head_stride;
+  const S* vbase0 = reinterpret_cast<const S*>(a.v_pool) + (size_t)g * head_stride;
+  const int ntiles = ceil_div(kend_wg, kTile);
+  const int nsteps = ceil_div(ntiles, 2);
+  const int unmasked = max(pos0, 0);
+  const int W = WIN ? a.window : 0;
+  const int st_begin =
+      WIN ? max(max(ctx - n + max(top - (kDmaWaves - 1), 0) * QT, 0) - W + 1, 0) / kDmaKeys : 0;
+  const int kbeg = WIN ? max(unmasked - W + 1, 0) : 0;
+
+  // tile t of the walk: its block id when inside the pool, else -1
+  auto block_of = [&](int t) __attribute__((always_inline)) -> int {
+    if (t >= ntiles) return -1;
+    const int b = scalar_load(table + ((t * kTile) >> a.log2_bs));
+    return (unsigned)b < (unsigned)a.num_blocks ? b : -1;
+  };
+
+  // DMA lane offsets: wave w loads 1 KiB pieces 2 w and 2 w + 1 of the K
+  // and the V region, rows 8 w .. 8 w + 7 of the step, i.e. rows 8 (w % 2) ..
+  // of tile w / 2; lane l of piece j fills unit 64 j + l = (row r, slot
+  // l % 16) with chunk (l % 16) ^ swz(r) of that row.
+  const int tw = (kDmaPieces * w) >> 2;
+  uint32_t dma_off[kDmaPieces];
+#pragma unroll
+  for (int x = 0; x < kDmaPieces; ++x) {
+    const int r = 4 * (kDmaPieces * w + x) + (lane >> 4);
+    dma_off[x] = (uint32_t)((r & 15) * kRowBytes128 + (((lane & 15) ^ dma_swz(r)) * 16));
+  }
+  // LDS read offsets within a stage.  K operand of k-step s: row pi(c32),
+  // chunk 2 s + h.  V^T operand of d-tile dt, k-step ks, half hr: the
+  // transposed 64-bit read whose source lane (l % 16) addresses row 16 ks +
+  // 8 (l / 32) + 4 hr + (l % 16) / 4, elements 32 dt + 16 ((l / 16) % 2) +
+  // 4 (l % 4) .. +3.
+  const int kr = 16 * (c32 >> 4) + 8 * ((c32 >> 2) & 1) + 4 * ((c32 >> 3) & 1) + (c32 & 3);
+  uint32_t koff[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = (uint32_t)dma_pos(kr, 2 * s + h);
+  uint32_t voff[4][4];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int hr = 0; hr < 2; ++hr) {
+      const int R = 16 * ks + 8 * h + 4 * hr + ((lane & 15) >> 2);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int el = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        voff[dt][2 * ks + hr] = (uint32_t)(kDmaRegion + dma_pos(R, el >> 3) + 2 * (el & 7));
+      }
+    }
+
+  // Loads of step st into stage buffer `buf`: this wave's two K and two V
+  // pieces of tile 2 st + w / 2 (V rows past the sequence read as zeros).
+  auto issue = [&](int st, char* buf, int b) __attribute__((always_inline)) {
+    const int t = 2 * st + tw;
+    const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
+    const rsrc_t ks = make_rsrc(kbase0 + off, b >= 0 ? 16u * kRowBytes128 : 0u);
+    const uint32_t vbytes = b >= 0 ? (uint32_t)max(min(kTile, ctx - t * kTile), 0) * kRowBytes128 : 0u;
+    const rsrc_t vs = make_rsrc(vbase0 + off, vbytes);
+#pragma unroll
+    for (int x = 0; x < kDmaPieces; ++x) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ks, (lds_void*)(buf + (kDmaPieces * w + x) * 1024), 16, dma_off[x], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vs, (lds_void*)(buf + kDmaRegion + (kDmaPieces * w + x) * 1024), 16, dma_off[x], 0, 0, 0);
+    }
+  };
+
+  float m = kMFloor, lsum = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
+
+  // S^T of one step from stage buffer `buf`: the eight K operands, then the
+  // eight products (the matrix cores accumulate back to back).
+  auto lds_addr = [](const char* buf) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)buf;
+  };
+  auto qk = [&](const char* buf) __attribute__((always_inline)) -> f32x16 {
+    const uint32_t b = lds_addr(buf);
+    uint32_t ka[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) ka[s] = b + koff[s];
+    u32x4 kop[8];
+    lds_read8_b128(kop, ka);
+    f32x16 sacc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sacc = mfma32<E>(kop[s], qv[s], sacc);
+    return sacc;
+  };
+  // The rest of step st from its scores: masks, the lazy rescale, the
+  // weights, and O^T += V^T . P^T with the V^T operands read transposed from
+  // `buf`; oka / okb: the step's two tiles had blocks in the pool.
+  auto softmax_pv = [&](int st, const f32x16& sacc, const char* buf, bool oka, bool okb)
+      __attribute__((always_inline)) {
+    const int k0 = st * kDmaKeys;
+    const uint32_t b = lds_addr(buf);
+    u32x4 vop[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t va[8];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        va[2 * dt] = b + voff[dt][2 * ks];
+        va[2 * dt + 1] = b + voff[dt][2 * ks + 1];
+      }
+      lds_read8_tr16(vop[ks], va);
+    }
+    float sv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sv[v] = sacc[v];
+    const bool masked =
+        k0 + kDmaKeys - 1 > unmasked || (WIN && k0 < kend - W) || !oka || !okb;
+    if (masked) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + 16 * (v >> 3) + 8 * h + (v & 7);
+        if (key > lim || (WIN && key <= lim - W) || !((v >> 3) ? okb : oka)) sv[v] = neg_inf();
+      }
+    }
+    float mt = smax(smax(smax(sv[0], sv[1]), smax(sv[2], sv[3])), smax(smax(sv[4], sv[5]), smax(sv[6], sv[7])));
+    mt = smax(mt, smax(smax(smax(sv[8], sv[9]), smax(sv[10], sv[11])),
+                       smax(smax(sv[12], sv[13]), smax(sv[14], sv[15]))));
+    if (__builtin_amdgcn_ballot_w64(mt > (m + kRescaleSlack) * inv_c)) {
+      const float x = smax(mt, shfl_xor(mt, 32));
+      const float mn = smax(m, x * c);
+      const float alpha = fast_exp2(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      m = mn;
+    }
+    u32x4 pw[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float pf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(__builtin_fmaf(sv[8 * ks + e], c, -m));
+      pw[ks] = u32x4{Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3]),
+                     Mfma<E>::round16x2(pf[4], pf[5]), Mfma<E>::round16x2(pf[6], pf[7])};
+      lsum = sum2(E{}, pw[ks][3], sum2(E{}, pw[ks][2], sum2(E{}, pw[ks][1], sum2(E{}, pw[ks][0], lsum))));
+    }
+    if (PF_PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32<E>(vop[ks][dt], pw[ks], o[dt]);
+    if (PF_PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+
+  // this wave computes step st: its rows reach keys [kbeg, kend)
+  auto runs = [&](int st) __attribute__((always_inline)) {
+    return mine && st * kDmaKeys < kend && (!WIN || (st + 1) * kDmaKeys > kbeg);
+  };
+  auto tile_ok = [&](int st, int half) __attribute__((always_inline)) {
+    return block_of(2 * st + half) >= 0;
+  };
+  // The ring: step st lives in stage (st - s0) % 4, loaded three steps
+  // ahead.  The step is software-pipelined across the iterations: iteration
+  // st forms the scores of st + 1 (its products run on the matrix cores
+  // while this wave computes the weights of st) and finishes st.  So before
+  // iteration st a wave waits for its own loads of st + 1 (those of st + 2
+  // may still be in flight); the barrier then makes every wave's loads of
+  // st + 1 visible and frees the stage of st - 1, which the loads of st + 3
+  // fill.
+  const int s0 = st_begin;
+  issue(s0, s_st0, block_of(2 * s0 + tw));
+  if (s0 + 1 < nsteps) issue(s0 + 1, s_st1, block_of(2 * s0 + 2 + tw));
+  if (s0 + 2 < nsteps) issue(s0 + 2, s_st2, block_of(2 * s0 + 4 + tw));
+  // wait for this wave's loads of s0 (those of s0 + 1 and s0 + 2 may be
+  // outstanding), a plain s_barrier: __syncthreads would wait for them all
+  if (s0 + 2 < nsteps)
+    __builtin_amdgcn_s_waitcnt(0x0070 | (4 * kDmaPieces));  // vmcnt(two steps' loads), lgkmcnt(0)
+  else if (s0 + 1 < nsteps)
+    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));  // vmcnt(one step's loads), lgkmcnt(0)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  f32x16 scur = {};
+  if (runs(s0) && (tile_ok(s0, 0) || tile_ok(s0, 1))) scur = qk(s_st0);
+  auto step = [&](int st, const char* cur, const char* next, char* fill)
+      __attribute__((always_inline)) {
+    if (st + 2 < nsteps)
+      __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));  // own loads of st + 1 landed
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (st + 3 < nsteps) issue(st + 3, fill, block_of(2 * (st + 3) + tw));
+    f32x16 snext = {};
+    if (st + 1 < nsteps && runs(st + 1) && (tile_ok(st + 1, 0) || tile_ok(st + 1, 1))) {
+      if (PF_PRIO) __builtin_amdgcn_s_setprio(1);
+      snext = qk(next);
+      if (PF_PRIO) __builtin_amdgcn_s_setprio(0);
+    }
+    const bool oka = tile_ok(st, 0), okb = tile_ok(st, 1);
+    if (runs(st) && (oka || okb)) softmax_pv(st, scur, cur, oka, okb);
+    scur = snext;
+  };
+  for (int st = s0; st < nsteps; st += 4) {
+    step(st, s_st0, s_st1, s_st3);
+    if (st + 1 >= nsteps) break;
+    step(st + 1, s_st1, s_st2, s_st0);
+    if (st + 2 >= nsteps) break;
+    step(st + 2, s_st2, s_st3, s_st1);
+    if (st + 3 >= nsteps) break;
+    step(st + 3, s_st3, s_st0, s_st2);
+  }
+
+  // Normalise and store: lane (c32, h) holds O[column c32][32 dt + 8 j + 4 h + r]
+  // = o[dt][4 j + r].
+  const float total = lsum + shfl_xor(lsum, 32);
+  if (row >= 0) {
+    const float inv = live && total > 0.f ? a.v_scale / total : 0.f;
+    S* dst = out + (size_t)row * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t b0 = float_to_bits(E{}, o[dt][4 * j] * inv);
+        const uint32_t b1 = float_to_bits(E{}, o[dt][4 * j + 1] * inv);
+        const uint32_t b2 = float_to_bits(E{}, o[dt][4 * j + 2] * inv);
+        const uint32_t b3 = float_to_bits(E{}, o[dt][4 * j + 3] * inv);
+        *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * j) = uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
+      }
+  }
+  if (a.status != nullptr) {
+    const int kfirst =
+        WIN ? max(max(ctx - n + max(top - (kDmaWaves - 1), 0) * QT, 0) - W + 1, 0) : 0;
+    bool bad = false;
+    for (int j = (kfirst >> a.log2_bs) + (int)threadIdx.x; j <= ((kend_wg - 1) >> a.log2_bs);
+         j += kDmaThreads)
+      bad |= (unsigned)table[j] >= (unsigned)a.num_blocks;
+    report_bad_block(a.status, __builtin_amdgcn_ballot_w64(bad) != 0);
+  }
+}
+
+template <class E>
+pa_status launch_dma(const PrefillArgs& a, hipStream_t st) {
+  const int blocks = ceil_div(a.max_query, kDmaRows / a.group);
+  if (blocks <= 0) return PA_OK;
+  const dim3 grid(a.num_kv_heads, ceil_div(blocks, kDmaWaves), a.num_seqs);
+  if (a.window > 0)
+    hipLaunchKernelGGL((prefill_dma<E, true>), grid, dim3(kDmaThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_dma<E, false>), grid, dim3(kDmaThreads), 0, st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 template <class E, KvType KV>
 pa_status launch_lds(const PrefillArgs& a, hipStream_t st) {
   const int blocks = ceil_div(a.max_query, kLdsRows / a.group);
@@ -531,12 +955,21 @@ int prefill_query_blocks(int max_query_len, int group) {
   return max_query_len > 0 ? ceil_div(max_query_len, kLdsRows / group) : 0;
 }
 
-pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, hipStream_t st) {
+pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, int path, hipStream_t st) {
   const bool fp8 = kv == KvType::kFp8;
-  if (dtype == PA_BF16)
+  // the direct-to-LDS kernel runs 16-bit pools when asked for; AUTO runs the
+  // register-staged kernel, which measured as fast or faster on the 8B
+  // chunked-prefill workload
+  const bool dma = !fp8 && path == PA_PREFILL_DMA;
+  if (fp8 && path == PA_PREFILL_DMA) return PA_ERR_SHAPE;
+  if (dtype == PA_BF16) {
+    if (dma) return launch_dma<BF16>(a, st);
     return fp8 ? launch_lds<BF16, KvType::kFp8>(a, st) : launch_lds<BF16, KvType::kSame>(a, st);
-  if (dtype == PA_F16)
+  }
+  if (dtype == PA_F16) {
+    if (dma) return launch_dma<F16>(a, st);
     return fp8 ? launch_lds<F16, KvType::kFp8>(a, st) : launch_lds<F16, KvType::kSame>(a, st);
+  }
   return PA_ERR_SHAPE;
 }
 

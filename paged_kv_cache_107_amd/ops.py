@@ -212,6 +212,13 @@ def pa_set_decode_path(path: int) -> int:
     return prev
 
 
+def pa_set_prefill_path(path: int) -> int:
+    prev = int(lib().pa_set_prefill_path(int(path)))
+    if prev < 0:
+        raise ValueError(f"bad prefill path {path}")
+    return prev
+
+
 def pa_reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None, kv_scales=(1.0, 1.0)):
     """Write new tokens' K/V ([T][Hkv][D]) into their slots (quantised for an
     8-bit pool with kv_scales).  See pa.h."""

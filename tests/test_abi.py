@@ -123,6 +123,17 @@ def test_fp8_pool_validation():
         lib.pa_set_decode_path(prev)
 
 
+def test_prefill_path_setting():
+    lib = pa.lib()
+    prev = lib.pa_set_prefill_path(pa.PA_PREFILL_DMA)
+    try:
+        assert lib.pa_set_prefill_path(pa.PA_PREFILL_LDS) == pa.PA_PREFILL_DMA
+        assert lib.pa_set_prefill_path(7) == -1                 # unknown: unchanged
+        assert lib.pa_set_prefill_path(pa.PA_PREFILL_AUTO) == pa.PA_PREFILL_LDS
+    finally:
+        lib.pa_set_prefill_path(prev)
+
+
 def test_forced_paths_validate_shapes():
     lib = pa.lib()
     prev = lib.pa_set_decode_path(pa.PA_PATH_MFMA)

@@ -21,6 +21,16 @@ import paged_kv_cache_107_amd as pa  # noqa: E402
 from oracle.attention import paged_prefill  # noqa: E402
 
 
+@pytest.fixture(autouse=True, params=["lds", "dma"])
+def prefill_kernel(request):
+    """Every test runs on both prefill kernels: K/V tiles staged through
+    registers into LDS, and loaded straight into LDS with transposed reads."""
+    path = {"lds": pa.PA_PREFILL_LDS, "dma": pa.PA_PREFILL_DMA}[request.param]
+    prev = pa.pa_set_prefill_path(path)
+    yield request.param
+    pa.pa_set_prefill_path(prev)
+
+
 def run_gpu_prefill(d, kv, nan_fill=False):
     """Every phase of the scenario (the chunk's appends included) through the
     native allocator and the cache kernels, then one pa_prefill call."""

@@ -112,9 +112,18 @@ def test_windowed_decode_shapes_with_trims_and_poison(shape):
     assert err <= TOL[dtype]
 
 
+@pytest.fixture(params=["lds", "dma"])
+def prefill_kernel(request):
+    """The 16-bit prefill tests run on both prefill kernels."""
+    path = {"lds": pa.PA_PREFILL_LDS, "dma": pa.PA_PREFILL_DMA}[request.param]
+    prev = pa.pa_set_prefill_path(path)
+    yield request.param
+    pa.pa_set_prefill_path(prev)
+
+
 @pytest.mark.parametrize("window", [1, 7, 16, 40, 200])
 @pytest.mark.parametrize("g", [1, 4, 16])
-def test_windowed_prefill(window, g):
+def test_windowed_prefill(window, g, prefill_kernel):
     chunks = [1, 17, 64, 65, 100, 33]
     prefixes = [0, 40, 16, 300, 3, 1000]
     lens = [c + p for c, p in zip(chunks, prefixes)]
@@ -136,7 +145,7 @@ def test_windowed_prefill(window, g):
 
 @pytest.mark.parametrize("window", [7, 40])
 @pytest.mark.parametrize("g", [1, 4])
-def test_windowed_prefill_after_trims(window, g):
+def test_windowed_prefill_after_trims(window, g, prefill_kernel):
     """Blocks no chunk row's window reaches are released (each sequence is
     trimmed to window + its chunk length, so the chunk's first row keeps its
     whole window), the released blocks are poisoned with NaN and the tables
