@@ -72,7 +72,7 @@ PREFILL_DESCRIPTION = ("8B GQA chunked prefill, 1 layer: 16 sequences x 512-toke
 # measured partition + reduce time on MI355X.
 DEFAULT_PARTITION = {"8b_gqa": 2048, "7b_mha": 512, "cow": 2048, "qwen32b_long": 512,
                      "qwen32b_long_bs32": 512, "tiny": 512}
-# every decode workload the task names, in its order
+# the decode workloads measured, in the order they are listed
 CONFIG_WORKLOADS = ["tiny", "7b_mha", "8b_gqa", "cow", "qwen32b_long", "qwen32b_long_bs32"]
 
 
@@ -275,7 +275,7 @@ def time_step(cache, plan, q, out, ws, k_new, v_new, wl, part_tokens: int, reps:
 
 
 def measure_configs(names, reps: int, log):
-    """Every other decode workload the task names, each on its own freshly
+    """Each listed decode workload, each on its own freshly
     populated cache (device-drawn contents): the decode step's passes timed
     with HIP events on the launch stream, sequences/s of the step, KV GB/s
     and the partition kernel's HBM roofline."""
@@ -291,14 +291,26 @@ def measure_configs(names, reps: int, log):
         t = time_step(*state, wl, pt, reps)
         ctx = d.context_lens.astype(np.int64)
         eb = wl.elem_bytes
-        kv = int(ctx.sum()) * 2 * wl.num_kv_heads * wl.head_dim * eb
-        alg = (kv + 2 * d.batch * wl.num_q_heads * wl.head_dim * eb +
+        row = 2 * wl.num_kv_heads * wl.head_dim * eb          # K + V bytes of one token
+        kv = int(ctx.sum()) * row
+        # K/V of the distinct blocks the batch attends: a block shared by
+        # several sequences is one block of memory, read for each of them;
+        # the roofline counts it once (its tokens: the most any sharer uses)
+        used = {}
+        tables = plan.tables.cpu().numpy()
+        for i, c in enumerate(ctx.tolist()):
+            for j in range(-(-c // wl.block_size)):
+                b = int(tables[i, j])
+                used[b] = max(used.get(b, 0), min(wl.block_size, c - j * wl.block_size))
+        kv_unique = sum(used.values()) * row
+        alg = (kv_unique + 2 * d.batch * wl.num_q_heads * wl.head_dim * eb +
                int(np.sum(-(-ctx // wl.block_size))) * 4 + 4 * d.batch)
         part = t["decode_partition"]
         gbps = alg / (part * 1e-6) / 1e9
         rec = {"workload": DESCRIPTIONS[name], "dtype": wl.dtype, "batch": d.batch,
                "attended_tokens": int(ctx.sum()), "partition_tokens": pt,
-               "cow_pairs": int(plan.pairs.shape[0]), "kv_bytes": kv, "algorithmic_bytes": alg,
+               "cow_pairs": int(plan.pairs.shape[0]), "kv_bytes": kv,
+               "kv_bytes_distinct_blocks": kv_unique, "algorithmic_bytes": alg,
                "step_us": round(t["step"], 2),
                "passes_us": {k: round(v, 2) for k, v in t.items() if k != "step"},
                "seq_per_s": round(d.batch / (t["step"] * 1e-6), 1),
@@ -307,8 +319,8 @@ def measure_configs(names, reps: int, log):
                             "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
         if name == "cow":
-            rec["note"] = ("branches share their 1000-token prefix blocks, so the attended "
-                           "bytes exceed what HBM supplies (shared blocks hit in cache)")
+            rec["note"] = ("branches share their prefix blocks: kv_bytes counts them per "
+                           "sequence, the roofline once (kv_bytes_distinct_blocks)")
         if name == "tiny":
             rec["note"] = "latency-bound (110 KiB of K/V): no bandwidth claim"
         res[name] = rec
@@ -431,10 +443,9 @@ def measure_prefill(reps: int, log):
     flops_w = 4 * wl.head_dim * wl.num_q_heads * attended(VARIANT_WINDOW)
     tflops_w = flops_w / (us_w * 1e-6) / 1e12
     log(f"prefill window_{VARIANT_WINDOW}: {us_w:.1f} us, {tflops_w:.1f} TFLOP/s")
-    # 8-bit E4M3 pools of the same shape (random finite codes: the time does
-    # not depend on the values), same attended keys
-    codes = tuple(torch.randint(0, 0x78, shape, generator=gen, device="cuda", dtype=torch.uint8)
-                  .view(torch.float8_e4m3fn) for _ in range(2))
+    # 8-bit E4M3 pools holding the quantised contents of the 16-bit pools
+    # (every slot through the quantising pa_reshape_and_cache), same attended keys
+    codes = quantised_pools(cache.k_pool, cache.v_pool)
     us_8 = timed(0, (q, *codes) + args[3:], kv_scales=FP8_SCALES)
     tflops_8 = flops / (us_8 * 1e-6) / 1e12
     log(f"prefill fp8_e4m3: {us_8:.1f} us, {tflops_8:.1f} TFLOP/s")
@@ -461,6 +472,21 @@ VARIANT_WINDOW = 1024
 FP8_SCALES = (0.05, 0.05)
 
 
+def quantised_pools(k_pool, v_pool):
+    """8-bit E4M3 copies of both pools: every slot written once by the
+    quantising pa_reshape_and_cache (scales FP8_SCALES)."""
+    import torch
+    import paged_kv_cache_107_amd as pa
+    n_blocks, hkv, bs, dh = k_pool.shape
+    flat = lambda p: p.permute(0, 2, 1, 3).reshape(n_blocks * bs, hkv, dh).contiguous()
+    k8 = torch.zeros_like(k_pool, dtype=torch.uint8).view(pa.FP8)
+    v8 = torch.zeros_like(k8)
+    slots = torch.arange(n_blocks * bs, dtype=torch.int64, device="cuda")
+    pa.pa_reshape_and_cache(flat(k_pool), flat(v_pool), slots, k8, v8, kv_scales=FP8_SCALES)
+    torch.cuda.synchronize()
+    return k8, v8
+
+
 def measure_variants(cache, plan, q, d, reps: int, log):
     """Decode of the same 8B batch (same block tables, same q) in the
     attention variants: a sliding window of 1024 positions on the 16-bit
@@ -475,15 +501,7 @@ def measure_variants(cache, plan, q, d, reps: int, log):
     wl = d.wl
     ctx = d.context_lens.astype(np.int64)
     n_blocks, hkv, bs, dh = cache.k_pool.shape
-    # the 8-bit copy of the pools: every slot written once by the quantising write
-    flat = lambda p: p.permute(0, 2, 1, 3).reshape(n_blocks * bs, hkv, dh).contiguous()
-    k8 = torch.zeros_like(cache.k_pool, dtype=torch.uint8).view(pa.FP8)
-    v8 = torch.zeros_like(k8)
-    slots = torch.arange(n_blocks * bs, dtype=torch.int64, device="cuda")
-    pa.pa_reshape_and_cache(flat(cache.k_pool), flat(cache.v_pool), slots, k8, v8,
-                            kv_scales=FP8_SCALES)
-    torch.cuda.synchronize()
-    del slots
+    k8, v8 = quantised_pools(cache.k_pool, cache.v_pool)
     out = torch.empty_like(q)
     ws = cache.workspace(d.batch, wl.num_q_heads, plan.max_context_len)
     stream = torch.cuda.current_stream()
@@ -783,8 +801,9 @@ def main(argv=None):
     ap.add_argument("--e2e-steps", type=int, default=50,
                     help="real decode steps (plan + run) at the end, timing the host "
                          "planner (0 = skip)")
-    ap.add_argument("--only-configs", action="store_true",
-                    help="time the other named workloads only (for a profiler run)")
+    ap.add_argument("--only-configs", nargs="*", metavar="NAME", default=None,
+                    help="time the other named workloads only, or just the NAMEs given (for a "
+                         "profiler run)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
@@ -799,8 +818,13 @@ def main(argv=None):
     torch.cuda.set_device(0)
     pa.lib()
     others = [n for n in CONFIG_WORKLOADS if n != args.workload]
-    if args.only_configs:
-        print(json.dumps({"configs": measure_configs(others, max(args.config_reps, 1), log)}),
+    if args.only_configs is not None:
+        names = args.only_configs or others
+        unknown = [n for n in names if n not in CONFIG_WORKLOADS]
+        if unknown:
+            print(f"unknown workloads {unknown}; named: {list(CONFIG_WORKLOADS)}", file=sys.stderr)
+            return 2
+        print(json.dumps({"configs": measure_configs(names, max(args.config_reps, 1), log)}),
               flush=True)
         return 0
     d = W.draw(args.workload)

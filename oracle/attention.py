@@ -207,3 +207,48 @@ def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_tables, query_start, c
             q = decode_bits(q_bits[a + j], dtype)
             out[a + j] = dense_attention(q, k[lo:pos + 1 - first], v[lo:pos + 1 - first], scale)
     return out
+
+
+def paged_prefill_rows_at_once(q_bits, k_pool_bits, v_pool_bits, block_tables, query_start,
+                               context_lens, scale: float, dtype: str, window: int = 0,
+                               kv_dtype=None, k_scale: float = 1.0, v_scale: float = 1.0,
+                               seqs=None) -> np.ndarray:
+    """The attention of ``paged_prefill`` with all of a chunk's rows at once,
+    for workloads too large for the row-by-row loop.
+
+    Same arguments, readings and result (float64 [T][Hq][D]; rows of
+    sequences not in ``seqs``, when given, stay zero).  Per sequence and q
+    head h (kv head g = h // (Hq / Hkv)) it is the dense form
+    softmax(scale Q K^T + M) V of the pages ("放下账簿，打开源码", section
+    "注意力计算的改写") with the mask M written out: M[j, t] = 0 where chunk
+    row j (position p = ctx - n + j) may attend key position t
+    (window_start(p, W) <= t <= p) and -inf elsewhere; rows with p < 0 are
+    zero.  Only the rounding order differs from the row-by-row loop.
+    """
+    out = np.zeros(q_bits.shape, dtype=np.float64)
+    kvt = kv_dtype or dtype
+    hq, hkv = q_bits.shape[1], k_pool_bits.shape[1]
+    group = hq // hkv
+    for i in (range(len(context_lens)) if seqs is None else seqs):
+        a, b = int(query_start[i]), int(query_start[i + 1])
+        n, ctx = b - a, int(context_lens[i])
+        if n <= 0 or ctx <= 0:
+            continue
+        first = window_start(max(ctx - n, 0), window)
+        k = decode_bits(gather_sequence(k_pool_bits, block_tables[i], ctx, first), kvt, k_scale)
+        v = decode_bits(gather_sequence(v_pool_bits, block_tables[i], ctx, first), kvt, v_scale)
+        pos = ctx - n + np.arange(n)                      # each row's position
+        keys = first + np.arange(ctx - first)             # each key's position
+        lo = np.array([window_start(int(p), window) for p in pos])
+        allowed = (keys[None, :] <= pos[:, None]) & (keys[None, :] >= lo[:, None])
+        live = pos >= 0
+        q = decode_bits(q_bits[a:b], dtype)               # [n][Hq][D]
+        for h in range(hq):
+            g = h // group
+            s = scale * (q[:, h, :] @ k[:, g, :].T)       # [n][keys]
+            s = np.where(allowed, s, -np.inf)
+            m = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
+            p = np.exp(s - m[:, None])
+            o = (p @ v[:, g, :]) / np.where(live, p.sum(axis=1), 1.0)[:, None]
+            out[a:b, h, :] = np.where(live[:, None], o, 0.0)
+    return out

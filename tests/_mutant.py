@@ -45,6 +45,15 @@ MUTANTS = {
                         "            pos = ctx - n + j - 1\n", PRE),
     "negative_guard": ("oracle.attention", "            if pos < 0:\n                continue\n            lo",
                        "            lo", PRE),
+    # prefill, matrix form
+    "rows_causal_limit": ("oracle.attention", "allowed = (keys[None, :] <= pos[:, None])",
+                          "allowed = (keys[None, :] < pos[:, None])", PRE),
+    "rows_window_limit": ("oracle.attention", "& (keys[None, :] >= lo[:, None])",
+                          "& (keys[None, :] > lo[:, None])", PRE + VAR),
+    "rows_gqa_index": ("oracle.attention", "            g = h // group\n            s = scale * (q[:, h, :]",
+                       "            g = h % hkv\n            s = scale * (q[:, h, :]", PRE),
+    "rows_norm": ("oracle.attention", "np.where(live, p.sum(axis=1), 1.0)",
+                  "np.where(live, p.sum(axis=1) + 1e-9, 1.0)", PRE),
     # allocator
     "cow_no_decrement": ("oracle.allocator",
                          "            self.refcount[src] -= 1\n            if self.refcount[src] == 0:",

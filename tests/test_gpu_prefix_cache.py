@@ -22,7 +22,7 @@ if not torch.cuda.is_available():  # the CPU suite deselects these; never a fall
     pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="needs a GPU")]
 
 import paged_kv_cache_107_amd as pa  # noqa: E402
-from oracle.attention import paged_prefill  # noqa: E402
+from oracle.attention import paged_prefill, paged_prefill_rows_at_once  # noqa: E402
 
 
 def run_prompts_gpu(ps, cached: bool):
@@ -91,26 +91,19 @@ def test_cached_prefill_matches_oracle(dtype, bs):
         assert max_abs_err(g["out"][a:b], full) <= TOL[dtype]
 
 
-def test_system_prompt_workload_full_size_sampled():
+def test_system_prompt_workload_full_size():
     """100 requests on one 1024-token system prompt: the 99 later requests
-    hit all 64 of its blocks; 4 rows of every request (its first and last
-    computed rows and two between) checked against the oracle computed for
-    that row alone."""
+    hit all 64 of its blocks; every computed row of every request against
+    the oracle (the matrix form of its chunked prefill)."""
     ps = W.prompt_set("prefix_1k")
     o = run_prompts_oracle(ps, cached=True)
     g = run_prompts_gpu(ps, cached=True)
     assert g["hits"].tolist() == [0] + [1024] * 99
     assert np.array_equal(g["tables"], o["tables"])
     assert np.array_equal(from_device_bits(g["cache"].k_pool, "bf16"), o["kp"])
-    rng = np.random.default_rng(11)
-    worst = 0.0
-    for r in range(ps.requests):
-        a, b = int(g["query_start"][r]), int(g["query_start"][r + 1])
-        n = b - a
-        for j in {0, n - 1, *rng.integers(0, n, 2).tolist()}:
-            pos = int(ps.prompt_lens[r]) - n + j
-            want = paged_prefill(o["q"][a + j:a + j + 1], o["kp"], o["vp"], o["tables"][r:r + 1],
-                                 np.array([0, 1]), np.array([pos + 1]), ps.wl.scale, "bf16")
-            worst = max(worst, max_abs_err(g["out"][a + j:a + j + 1], want))
-    print(f"prefix_1k sampled max_abs_err={worst:.3e}", flush=True)
-    assert worst <= TOL["bf16"]
+    assert np.array_equal(from_device_bits(g["cache"].v_pool, "bf16"), o["vp"])
+    want = paged_prefill_rows_at_once(o["q"], o["kp"], o["vp"], o["tables"], o["query_start"],
+                                      o["lens"], ps.wl.scale, "bf16")
+    err = max_abs_err(g["out"], want)
+    print(f"prefix_1k {want.shape[0]} rows max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]

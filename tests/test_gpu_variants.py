@@ -10,7 +10,7 @@ through the C ABI.
   E4M3 encoding (every bf16 value in range, saturation, signed zero); decode
   (grid and stream splits, G 1-16) and prefill on 8-bit pools against the
   oracle on the same codes; copies of 8-bit blocks bit-exact; windows and
-  8-bit pools together; the 8B decode batch at full size on sampled rows.
+  8-bit pools together (full-size workloads: test_gpu_full_size.py).
 Tolerance: max-abs error <= 2e-2 (16-bit activations, fp32 accumulation), as
 for 16-bit pools: the codes are exact inputs on both sides.
 """
@@ -327,36 +327,3 @@ def test_fp8_prefill(window, g, dtype):
     err = max_abs_err(out, want)
     print(f"fp8 prefill {dtype} G={g} window={window} max_abs_err={err:.3e}", flush=True)
     assert err <= TOL[dtype]
-
-
-def test_fp8_full_size_sampled():
-    """The 8B decode batch (256 sequences) on 8-bit pools: the codes of 8
-    sequences and 32 sampled output rows against the oracle; the stream split
-    (the default kernel)."""
-    d = W.draw("8b_gqa")
-    kv = KV(d)
-    from paged_kv_cache_107_amd.cache import PagedKVCache
-    wl = d.wl
-    cache = PagedKVCache(d.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.dtype,
-                         d.free_order, kv_dtype="fp8_e4m3", kv_scales=SCALES)
-    for i in range(d.batch):
-        assert cache.create() == i
-        k, v = kv(i)
-        s, _ = cache.reserve(i, k.shape[0])
-        cache.write_host(to_device(k, wl.dtype), to_device(v, wl.dtype), s, [])
-    q = to_device(W.query_bits(d), wl.dtype)
-    out, tables, lens = decode_gpu(cache, list(range(d.batch)), q, wl.scale, 0, SCALES)
-    rng = np.random.default_rng(3)
-    rows = np.concatenate([[0, d.batch - 1], rng.choice(np.arange(1, d.batch - 1), 30, False)])
-    kp, vp = fp8_bits(cache.k_pool), fp8_bits(cache.v_pool)
-    for i in rows[:8]:
-        k, v = kv(i)
-        t = tables[i][: -(-int(lens[i]) // 16)]
-        got_k = kp[t].transpose(0, 2, 1, 3).reshape(-1, wl.num_kv_heads, wl.head_dim)[:lens[i]]
-        want_k = fp8.quantize(decode_bits(k, wl.dtype).astype(np.float32), SCALES[0])
-        assert np.array_equal(got_k, want_k)
-    want = paged_decode(W.query_bits(d), kp, vp, tables, lens, wl.scale, wl.dtype, seqs=rows,
-                        kv_dtype="fp8_e4m3", k_scale=SCALES[0], v_scale=SCALES[1])
-    err = max_abs_err(out[torch.from_numpy(rows).cuda()], want)
-    print(f"fp8 8b_gqa sampled max_abs_err={err:.3e}", flush=True)
-    assert err <= TOL["bf16"]

@@ -7,7 +7,10 @@
 * the same positions give the same rows whatever the chunk boundary;
 * closed forms: a prompt's first token returns its own V row; equal keys give
   the running mean of the V rows;
-* a token whose position would be negative gets a zero row.
+* a token whose position would be negative gets a zero row;
+* ``paged_prefill_rows_at_once`` (the matrix form for full-size workloads)
+  passes the SDPA pin above and equals the row-by-row loop within rounding on
+  windows, 8-bit pools, negative positions and sequence subsets.
 """
 import math
 
@@ -16,7 +19,7 @@ import pytest
 import torch
 
 import workloads as W
-from oracle.attention import decode_bits, paged_decode, paged_prefill
+from oracle.attention import decode_bits, paged_decode, paged_prefill, paged_prefill_rows_at_once
 from test_oracle_attention import page_sequences
 
 
@@ -43,16 +46,17 @@ def sdpa_chunk(q64, k64, v64, scale):
     return out[0].numpy().transpose(1, 0, 2)
 
 
+@pytest.mark.parametrize("fn", [paged_prefill, paged_prefill_rows_at_once])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bs", [16, 4])
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4)])
-def test_prefill_equals_dense_sdpa_with_causal_mask(dtype, bs, hq, hkv):
+def test_prefill_equals_dense_sdpa_with_causal_mask(dtype, bs, hq, hkv, fn):
     rng = np.random.default_rng(21)
     ctxs, chunks = [40, 17, 64, 5, 33], [40, 9, 20, 1, 16]   # full prompt, tails, a 1-token step
     d = 32
     q, ks, vs, qs, kp, vp, tables, lens = chunk_case(rng, ctxs, chunks, hq, hkv, d, dtype, bs)
     scale = 1 / math.sqrt(d)
-    out = paged_prefill(q, kp, vp, tables, qs, lens, scale, dtype)
+    out = fn(q, kp, vp, tables, qs, lens, scale, dtype)
     for i in range(len(ctxs)):
         a, b = qs[i], qs[i + 1]
         ref = sdpa_chunk(decode_bits(q[a:b], dtype), decode_bits(ks[i], dtype),
@@ -116,3 +120,23 @@ def test_workload_scenario_builds_the_chunks():
     step = W.scenario(d)[-1]
     assert step == [("append", i, int(d.context_lens[i]) - 512, 512) for i in range(16)]
     assert d.query_start[-1] == 8192 and W.prefill_query_bits(d).shape == (8192, 32, 128)
+
+
+@pytest.mark.parametrize("window", [0, 1, 7, 40])
+@pytest.mark.parametrize("kv_dtype", [None, "fp8_e4m3"])
+def test_rows_at_once_equals_the_row_loop(window, kv_dtype):
+    rng = np.random.default_rng(27)
+    ctxs, chunks = [40, 17, 64, 5, 33, 3], [40, 9, 20, 1, 16, 5]   # the last: 2 negative rows
+    q, ks, vs, qs, kp, vp, tables, lens = chunk_case(rng, ctxs, chunks, 8, 2, 32, "bf16", 4)
+    if kv_dtype:   # arbitrary finite E4M3 codes in both pools
+        kp = rng.integers(0, 0x7F, kp.shape).astype(np.uint8) | (rng.integers(0, 2, kp.shape) << 7).astype(np.uint8)
+        vp = rng.integers(0, 0x7F, vp.shape).astype(np.uint8)
+    kw = dict(window=window, kv_dtype=kv_dtype, k_scale=0.3, v_scale=0.7)
+    want = paged_prefill(q, kp, vp, tables, qs, lens, 0.2, "bf16", **kw)
+    got = paged_prefill_rows_at_once(q, kp, vp, tables, qs, lens, 0.2, "bf16", **kw)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)   # 8-bit values reach ~300
+    assert not got[qs[5]:qs[5] + 2].any() and got[qs[5] + 2:].any()
+    sub = paged_prefill_rows_at_once(q, kp, vp, tables, qs, lens, 0.2, "bf16", seqs=[1, 4], **kw)
+    for i in range(len(ctxs)):
+        rows = slice(qs[i], qs[i + 1])
+        np.testing.assert_array_equal(sub[rows], got[rows] if i in (1, 4) else 0.0)
