@@ -127,8 +127,12 @@ const char* pa_status_string(int32_t status);
  *   scale         softmax scale (typically 1 / sqrt(head_dim))
  *   out           device, [num_seqs][num_q_heads][head_dim], dtype
  *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
- *                 aligned; may be NULL when that size is 0.  Scratch only:
- *                 its contents on entry do not matter.  Layout is private.
+ *                 aligned; may be NULL when that size is 0.  Split-K scratch,
+ *                 except that the stream split keeps its balance state (see
+ *                 pa_set_decode_balance) in the first 256 bytes between
+ *                 calls: any contents on entry are valid input (a header it
+ *                 does not recognise means the even cut).  Reusing one
+ *                 workspace across calls lets the balance adapt.
  *   partition_tokens  multiple of 16 and of block_size, in [16, 4096];
  *                 0 selects the default (512).  Sizes the grid split's
  *                 partitions; validated but unused by the stream split.
@@ -194,7 +198,8 @@ pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool
 /* pa_decode without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, results and kernels as
- * pa_decode (bit-identical output), minus workspace and workspace_bytes: the
+ * pa_decode (bit-identical output for the same cut of the stream split, e.g.
+ * with pa_set_decode_balance(0)), minus workspace and workspace_bytes: the
  * split-K workspace is a static device array of PA_NOALLOC_SCRATCH_BYTES that
  * the library holds on each device it runs on until the process ends.  The
  * call allocates nothing.  It runs on the current device (hip_stream must
@@ -205,7 +210,8 @@ pa_status pa_decode_reduce(const void* q, const void* k_pool, const void* v_pool
  * uses the same array: calls that can overlap on one device (different
  * streams without ordering between them) race and must not be made; calls
  * on one stream are ordered and safe.  Nothing in the array needs to start
- * at zero, so stale contents from an earlier call do not matter. */
+ * at zero: stale contents from an earlier call are at most the stream
+ * split's balance state, which every call on the device shares. */
 #define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
                             const pa_pool_desc* pool, const int32_t* block_tables,
@@ -229,6 +235,23 @@ typedef enum {
   PA_PATH_MFMA_GRID = 3
 } pa_decode_path;
 int32_t pa_set_decode_path(int32_t path);
+
+/* Run-time balance of the stream split (the block loop and cross-partition
+ * merge of page "放下账簿，打开源码", section "注意力计算的改写", cut over the
+ * GPU's dies).  The stream split cuts the batch's tiles into one chunk per
+ * XCD (each XCD with its own L2); the dies do not run equally fast, so with
+ * balancing on (1, the default) each partition pass of at least 16 tiles per
+ * wave records how long each chunk's slowest wave took, and the next reduce
+ * pass moves each chunk's share of the next call's tiles halfway towards its
+ * measured rate (shares kept within 1/16 .. 3/16).  The state lives in the
+ * first 256 bytes of the workspace (of the static array for
+ * pa_decode_noalloc), so it carries over only between calls that share one.
+ * The cut changes where the fp32 merges fall: outputs of two calls then
+ * agree up to the order of those merges, not bit for bit.  With balancing
+ * off (0) the cut is even and repeated calls are bit-identical.
+ * Process-wide setting; returns the previous value (-1 for a value other
+ * than 0 or 1, which leaves the setting unchanged). */
+int32_t pa_set_decode_balance(int32_t on);
 
 /* ------------------------------------------------------------------------
  * Chunked prefill attention: a step that runs a chunk of each sequence's

@@ -54,6 +54,7 @@ SIGNATURES = {
     "pa_status_string": (C.c_char_p, [_i32]),
     "pa_set_decode_path": (_i32, [_i32]),
     "pa_set_prefill_path": (_i32, [_i32]),
+    "pa_set_decode_balance": (_i32, [_i32]),
     "pa_decode_workspace_bytes": (_sz, [_desc, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, _DECODE_ARGS),
     "pa_decode_partition": (_i32, _DECODE_ARGS),

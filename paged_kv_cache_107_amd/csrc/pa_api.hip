@@ -19,12 +19,13 @@ static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES]
 
 namespace {
 
-constexpr int32_t kAbiVersion = 5;
+constexpr int32_t kAbiVersion = 6;
 constexpr int32_t kDefaultPartition = 512;
 constexpr int32_t kMaxPartition = 4096;
 constexpr int32_t kMaxGridYZ = 65535;
 
 std::atomic<int32_t> g_decode_path{PA_PATH_AUTO};
+std::atomic<int32_t> g_decode_balance{1};
 std::atomic<int32_t> g_prefill_path{PA_PREFILL_AUTO};
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -82,8 +83,10 @@ constexpr size_t kStreamOwnerBytes = pa::kStreamMaxWaves * 4 * sizeof(int32_t);
 size_t stream_ml_bytes(int32_t b, int32_t hkv, int32_t g) {
   return align256(stream_heads(b, hkv, g) * sizeof(float2));
 }
+// The balance header (kept between calls) comes first.
 size_t stream_ws_bytes(int32_t b, int32_t hkv, int32_t g, int32_t d) {
-  return kStreamOwnerBytes + stream_ml_bytes(b, hkv, g) + stream_heads(b, hkv, g) * d * sizeof(float);
+  return pa::kStreamBalanceBytes + kStreamOwnerBytes + stream_ml_bytes(b, hkv, g) +
+         stream_heads(b, hkv, g) * d * sizeof(float);
 }
 
 constexpr size_t kStaticScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
@@ -219,6 +222,9 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
   a.out = out;
   char* ws = static_cast<char*>(workspace);
   if (stream) {
+    a.ws_balance = reinterpret_cast<pa::StreamBalance*>(ws);
+    ws += pa::kStreamBalanceBytes;
+    a.balance = g_decode_balance.load();
     a.ws_owner = reinterpret_cast<int32_t*>(ws);
     a.ws_ml = reinterpret_cast<float2*>(ws + kStreamOwnerBytes);
     a.ws_o = reinterpret_cast<float*>(ws + kStreamOwnerBytes +
@@ -308,6 +314,11 @@ int32_t pa_set_decode_path(int32_t path) {
       path != PA_PATH_MFMA_GRID)
     return -1;
   return g_decode_path.exchange(path);
+}
+
+int32_t pa_set_decode_balance(int32_t on) {
+  if (on != 0 && on != 1) return -1;
+  return g_decode_balance.exchange(on);
 }
 
 int32_t pa_set_prefill_path(int32_t path) {

@@ -339,8 +339,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
 // of the batch is put in one flat order -- kv head, then sequence, then
 // token -- and the grid (kStreamWgPerCu workgroups per CU) is treated as a
 // set of independent waves, each taking one contiguous run of that order
-// (StreamSplit).  All waves get the same number of tiles to within one, none
-// waits on a sibling (there is no barrier after the prologue), and one
+// (StreamSplit).  The waves of one XCD's chunk get the same number of tiles
+// to within one (the chunks are equal, or sized by the XCDs' measured rates:
+// StreamBalance), none waits on a sibling (no barrier after the prologue), and one
 // register ring runs through the wave's whole run, across the (kv head,
 // sequence) pairs it touches, so the next pair's loads are in flight while
 // the current one is stored.  The run of a kv head stays on one or two XCDs,
@@ -393,21 +394,31 @@ __device__ void scan_tiles(const int* ctx, const int* first, int* tb, int n, int
   __syncthreads();
 }
 
-// Even split of T flat tiles over the kWaves * nwg waves of nwg workgroups.
-// The hardware deals workgroups to the XCDs round-robin, so workgroup b runs
-// on XCD b % X (X = min(8, nwg)).  The tiles are cut into X contiguous
-// chunks, chunk x going to the workgroups b = x, x + X, ...; each chunk is
-// split evenly over its waves.  Ranks number the waves in flat order: rank
-// r's run is [lo(r), lo(r + 1)).
+// Split of T flat tiles over the kWaves * nwg waves of nwg workgroups.  The
+// hardware deals workgroups to the XCDs round-robin, so workgroup b runs on
+// XCD b % X (X = min(8, nwg)).  The tiles are cut into X contiguous chunks,
+// chunk x going to the workgroups b = x, x + X, ...; each chunk is split
+// evenly over its waves.  The chunks are equal, or, with weights (X = 8),
+// chunk x covers [T cum[x] / 2^16, T cum[x + 1] / 2^16).  Ranks number the
+// waves in flat order: rank r's run is [lo(r), lo(r + 1)).  Any monotone cut
+// keeps the slot rule of the stream kernel.
+constexpr uint32_t kBalanceMagic = 0x6C614257u;
+constexpr uint32_t kBalanceOne = 1u << 16;
+// a chunk's share of the tiles under weights: 1/16 .. 3/16
+constexpr uint32_t kShareMin = kBalanceOne / 16, kShareMax = 3 * kBalanceOne / 16;
+// weights apply (and passes are timed) from this many tiles per wave on
+constexpr int kBalanceMinTilesPerWave = 16;
+
 struct StreamSplit {
   long long T;
   int nwg;
+  const int* cut = nullptr;  // weights: chunk x is [cut[x], cut[x + 1]) (in LDS)
   __device__ int chunks() const { return min(kXcds, nwg); }
   __device__ int wgs_of(int x) const { return nwg / chunks() + (x < nwg % chunks() ? 1 : 0); }
   __device__ int base(int x) const {  // first rank of chunk x
     return kWaves * (x * (nwg / chunks()) + min(x, nwg % chunks()));
   }
-  __device__ long long chunk_lo(int x) const { return T * x / chunks(); }
+  __device__ long long chunk_lo(int x) const { return cut ? cut[x] : T * x / chunks(); }
   __device__ long long lo(int r) const {
     if (r >= kWaves * nwg) return T;
     int x = 0;
@@ -421,17 +432,119 @@ struct StreamSplit {
   }
   // every run non-empty: at least as many tiles in each chunk as waves
   __device__ int dense() const {
-    return T / chunks() >= (long long)kWaves * ((nwg + chunks() - 1) / chunks()) ? 1 : 0;
+    if (!cut)
+      return T / chunks() >= (long long)kWaves * ((nwg + chunks() - 1) / chunks()) ? 1 : 0;
+    for (int x = 0; x < chunks(); ++x)
+      if (chunk_lo(x + 1) - chunk_lo(x) < (long long)kWaves * wgs_of(x)) return 0;
+    return 1;
   }
   // rank whose run holds tile t, 0 <= t < T
   __device__ int rank_of(long long t) const {
-    const int x = (int)(((t + 1) * chunks() - 1) / T);
+    int x;
+    if (cut) {  // the last chunk starting at or before t (empty ones skipped)
+      x = 0;
+      while (x + 1 < chunks() && chunk_lo(x + 1) <= t) ++x;
+    } else {
+      x = (int)(((t + 1) * chunks() - 1) / T);
+    }
     const long long c0 = chunk_lo(x), tx = chunk_lo(x + 1) - c0;
     return base(x) + (int)(((t - c0 + 1) * (kWaves * wgs_of(x)) - 1) / tx);
   }
+  // whether passes of this size are timed and may use weights
+  __device__ bool balanced_size() const {
+    return chunks() == kXcds && T >= (long long)kBalanceMinTilesPerWave * kWaves * nwg;
+  }
 };
 
-size_t stream_smem_bytes(int num_seqs) { return (3 * (size_t)num_seqs + 1 + kThreads) * 4; }
+// A balance header's cut, if the header is valid: magic, cum[0] = 0,
+// cum[8] = 2^16, every share within [kShareMin, kShareMax].
+__device__ bool read_cut(const StreamBalance* h, uint32_t (&cum)[kXcds + 1]) {
+  if (h == nullptr || h->magic != kBalanceMagic) return false;
+  for (int x = 0; x <= kXcds; ++x) cum[x] = h->cum[x];
+  if (cum[0] != 0 || cum[kXcds] != kBalanceOne) return false;
+  for (int x = 0; x < kXcds; ++x) {
+    if (cum[x + 1] < cum[x]) return false;
+    const uint32_t sh = cum[x + 1] - cum[x];
+    if (sh < kShareMin || sh > kShareMax) return false;
+  }
+  return true;
+}
+
+// The cut of a partition pass, by thread 0 into s_cut[0..8] (LDS; the caller
+// puts a barrier after it): weighted by the workspace's balance state when
+// balancing is on, the pass is large enough, the header is valid and every
+// run stays non-empty (so the reduce pass, which sees only dense records
+// under weights, never needs the cut); else s_cut[0] = -1 (the even cut).
+__device__ void partition_cut(const DecodeArgs& a, long long T, int nwg, int* s_cut) {
+  StreamSplit sp{T, nwg};
+  uint32_t cum[kXcds + 1];
+  s_cut[0] = -1;
+  if (!a.balance || !sp.balanced_size() || !read_cut(a.ws_balance, cum)) return;
+  for (int x = 0; x <= kXcds; ++x) s_cut[x] = (int)((T * (long long)cum[x]) >> 16);
+  sp.cut = s_cut;
+  if (!sp.dense()) s_cut[0] = -1;
+}
+
+// The reduce pass's first workgroup: turn the last partition pass's record
+// into the next cut, or initialise an invalid header with the even cut.
+// One thread; plain vector loads and stores (the partition pass's atomics
+// and stores are complete: it ran before on the same stream).
+__device__ void update_balance(StreamBalance* h) {
+  uint32_t cum[kXcds + 1];
+  if (!read_cut(h, cum)) {
+    h->magic = kBalanceMagic;
+    for (int x = 0; x <= kXcds; ++x) h->cum[x] = kBalanceOne / kXcds * x;
+    for (int x = 0; x < kXcds; ++x) h->tiles[x] = h->dur[x] = 0;
+    h->stamped = 0;
+    return;
+  }
+  if (!h->stamped) return;
+  float rate[kXcds], total = 0.f;
+  bool ok = true;
+  uint32_t dmin = 0xFFFFFFFFu, dmax = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    const uint32_t n = h->tiles[x], d = h->dur[x];
+    ok = ok && n > 0 && d > 0;
+    rate[x] = d > 0 ? (float)n / (float)d : 0.f;
+    total += rate[x];
+    dmin = min(dmin, d);
+    dmax = max(dmax, d);
+  }
+  // chunks ending within 1/64 of each other: balanced, the cut stays
+  if (ok && total > 0.f && dmax - dmin > dmax / 64) {
+    // halfway from the current share to the measured one, kept within
+    // [1/16, 3/16] (a little inside, so rounding stays in range)
+    float sh[kXcds];
+    for (int x = 0; x < kXcds; ++x)
+      sh[x] = 0.5f * (float)(cum[x + 1] - cum[x]) / (float)kBalanceOne + 0.5f * rate[x] / total;
+    for (int it = 0; it < 4; ++it) {
+      float s = 0.f;
+      for (int x = 0; x < kXcds; ++x) s += sh[x];
+      for (int x = 0; x < kXcds; ++x) sh[x] = fminf(fmaxf(sh[x] / s, 0.0675f), 0.1825f);
+    }
+    float s = 0.f;
+    for (int x = 0; x < kXcds; ++x) s += sh[x];
+    float run = 0.f;
+    uint32_t next[kXcds + 1];
+    next[0] = 0;
+    for (int x = 0; x < kXcds; ++x) {
+      run += sh[x];
+      next[x + 1] = x + 1 == kXcds ? kBalanceOne : (uint32_t)__float2uint_rn(run / s * kBalanceOne);
+    }
+    bool good = true;
+    for (int x = 0; x < kXcds; ++x)
+      good = good && next[x + 1] >= next[x] && next[x + 1] - next[x] >= kShareMin &&
+             next[x + 1] - next[x] <= kShareMax;
+    if (good)
+      for (int x = 0; x <= kXcds; ++x) h->cum[x] = next[x];
+  }
+  for (int x = 0; x < kXcds; ++x) h->dur[x] = 0;
+  h->stamped = 0;
+}
+
+size_t stream_smem_bytes(int num_seqs) {
+  return (3 * (size_t)num_seqs + 1 + kThreads + kXcds + 1) * 4;
+}
 
 template <class E, KvType KV>
 __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeArgs a) {
@@ -445,6 +558,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   int* s_first = s_ctx + B;   // [B] first attended position (sliding window)
   int* s_tb = s_first + B;    // [B + 1] tile offset of each sequence in a head's run
   int* s_tmp = s_tb + B + 1;  // [kThreads]
+  int* s_cut = s_tmp + kThreads;  // [kXcds + 1] the weighted cut, or s_cut[0] = -1
   for (int i = threadIdx.x; i < B; i += kThreads) {
     const int ctx = max(clamp_ctx(a, i), 0);
     s_ctx[i] = ctx;
@@ -456,8 +570,20 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   const int lane = threadIdx.x % kWave, w = wave_id();
   const int c16 = lane & 15, g4 = lane >> 4;
   const int Th = uni(s_tb[B]);  // tiles of one kv head's run
-  const StreamSplit split{(long long)Th * Hkv, (int)gridDim.x};
+  if (threadIdx.x == 0) partition_cut(a, (long long)Th * Hkv, (int)gridDim.x, s_cut);
+  __syncthreads();
+  StreamSplit split{(long long)Th * Hkv, (int)gridDim.x};
+  if (uni(s_cut[0]) >= 0) split.cut = s_cut;
   const int rank = split.rank(blockIdx.x, w);
+  // the pass's record for the balance state: each chunk's tiles, and (at
+  // the end) the longest time one of its waves took
+  const bool timed = a.ws_balance != nullptr && split.balanced_size();
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+  if (timed && blockIdx.x == 0 && threadIdx.x < kXcds) {
+    a.ws_balance->tiles[threadIdx.x] =
+        (uint32_t)(split.chunk_lo(threadIdx.x + 1) - split.chunk_lo(threadIdx.x));
+    if (threadIdx.x == 0) a.ws_balance->stamped = 1;
+  }
   const int lo = (int)split.lo(rank), hi = (int)split.lo(rank + 1);
   // rows of empty sequences are zero; spread over the workgroups
   for (int i = blockIdx.x; i < B; i += gridDim.x) {
@@ -725,6 +851,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
                  split.dense()};
     }
     reinterpret_cast<int4*>(a.ws_owner)[rank] = rec;
+    if (timed) {
+      const uint32_t took = (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
+      __hip_atomic_fetch_max(&a.ws_balance->dur[blockIdx.x % kXcds], took, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -984,11 +1115,13 @@ template <class E>
 __global__ __launch_bounds__(kThreads) void decode_reduce_stream(DecodeArgs a) {
   constexpr int D = 128;
   const int r = blockIdx.x;
+  if (r == 0 && threadIdx.x == 0 && a.ws_balance != nullptr) update_balance(a.ws_balance);
   const int4 rec = reinterpret_cast<const int4*>(a.ws_owner)[r];
   const int pq = rec.x;
   if (pq < 0) return;
   const int B = a.num_seqs, G = a.group;
   const int g = pq / B, i = pq - g * B;
+  // records of weighted passes are dense; others were cut evenly
   const StreamSplit split{(long long)rec.z * a.num_kv_heads, a.stream_waves / kWaves};
   const bool dense = rec.w != 0;
   const size_t base = (size_t)pq + r;

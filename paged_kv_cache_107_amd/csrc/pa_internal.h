@@ -39,7 +39,29 @@ struct DecodeArgs {
   int32_t window;        // sliding window in positions, 0 = none
   float v_scale;         // output factor: v_scale for 8-bit pools, else 1
   int32_t* status;       // caller's status word (kStatusBadBlock is ORed in), or null
+  struct StreamBalance* ws_balance;  // stream split: the balance state, else null
+  int32_t balance;       // stream split: cut the tile order by the measured rates
 };
+
+// Balance of the stream split, kept between calls in the first
+// kStreamBalanceBytes of a stream workspace.  The flat tile order is cut into
+// one chunk per XCD; with weights, chunk x covers tiles [T cum[x] / 2^16,
+// T cum[x + 1] / 2^16).  A partition pass records each chunk's tile count and
+// the longest time one of its waves took (100 MHz ticks, vector atomics); the
+// next reduce pass's first workgroup turns them into the cut of the next
+// call, with each chunk's share moved halfway towards its measured rate
+// (left alone when the chunks ended within 1/64 of each other).  A
+// workspace whose magic does not match starts from the even cut.
+struct StreamBalance {
+  uint32_t magic;    // kBalanceMagic when the fields below are valid
+  uint32_t stamped;  // tiles/dur hold a partition pass's record
+  uint32_t pad[2];
+  uint32_t cum[12];  // cum[0..8]: the cut, cum[0] = 0, cum[8] = 2^16
+  uint32_t tiles[8];
+  uint32_t dur[8];
+};
+constexpr size_t kStreamBalanceBytes = 256;
+static_assert(sizeof(StreamBalance) <= kStreamBalanceBytes, "balance header");
 
 // Bit of the caller's status word: a table entry inside an attended range
 // named a block outside [0, num_blocks).

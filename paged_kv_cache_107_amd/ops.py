@@ -212,6 +212,15 @@ def pa_set_decode_path(path: int) -> int:
     return prev
 
 
+def pa_set_decode_balance(on: bool) -> bool:
+    """Run-time balance of the stream split on (default) or off; returns the
+    previous setting.  See pa.h."""
+    prev = int(lib().pa_set_decode_balance(int(bool(on))))
+    if prev < 0:
+        raise ValueError(f"bad balance setting {on}")
+    return bool(prev)
+
+
 def pa_set_prefill_path(path: int) -> int:
     prev = int(lib().pa_set_prefill_path(int(path)))
     if prev < 0:

@@ -14,3 +14,13 @@ if TESTS not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+@pytest.fixture
+def even_cut():
+    """The decode stream split with its even cut (balance off), for tests
+    that compare outputs of separate calls bit for bit."""
+    import paged_kv_cache_107_amd as pa
+    prev = pa.pa_set_decode_balance(False)
+    yield
+    pa.pa_set_decode_balance(prev)

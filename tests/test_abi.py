@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = pa.lib()
-    assert lib.pa_abi_version() == 5
+    assert lib.pa_abi_version() == 6
     assert lib.pa_status_string(0) == b"PA_OK"
     assert lib.pa_status_string(-4) == b"PA_ERR_OOM"
     assert lib.pa_status_string(-99) == b"PA_ERR_UNKNOWN"
@@ -58,11 +58,12 @@ def test_workspace_bytes():
     assert f(f32, b, hq, 8192, 512) == grid
     assert f(f32, b, hq, 8192, 0) == f(f32, b, hq, 8192, 512)
 
-    # stream split: 16-byte merge records of the 1024 wave ranks, then
-    # (max, sum) and outputs for (B * Hkv + 1024) slots of G heads each
+    # stream split: the 256-byte balance header, 16-byte merge records of the
+    # 1024 wave ranks, then (max, sum) and outputs for (B * Hkv + 1024) slots
+    # of G heads each
     def stream(b, hkv, g):
         heads = (b * hkv + 1024) * g
-        return 16 * 1024 + (heads * 8 + 255) // 256 * 256 + heads * d * 4
+        return 256 + 16 * 1024 + (heads * 8 + 255) // 256 * 256 + heads * d * 4
     assert f(bf16, b, hq, 8192, 512) == max(grid, stream(b, 8, 4))
     assert f(bf16, b, hq, 100, 512) == stream(b, 8, 4)
     assert f(bf16, 4096, hq, 100, 512) == stream(4096, 8, 4)
@@ -121,6 +122,13 @@ def test_fp8_pool_validation():
         assert decode_status(good) == -3                  # 8-bit pools need the matrix cores
     finally:
         lib.pa_set_decode_path(prev)
+
+
+def test_decode_balance_setting():
+    assert pa.pa_set_decode_balance(False) is True           # on by default
+    assert pa.pa_set_decode_balance(True) is False
+    assert pa.lib().pa_set_decode_balance(2) == -1            # unchanged
+    assert pa.pa_set_decode_balance(True) is True
 
 
 def test_prefill_path_setting():

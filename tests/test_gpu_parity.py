@@ -54,6 +54,16 @@ def check_case(d, partition_tokens=0, nan_fill=False, state=True):
 PATHS = {"valu": pa.PA_PATH_VALU, "grid": pa.PA_PATH_MFMA_GRID, "stream": pa.PA_PATH_MFMA}
 
 
+@pytest.fixture(autouse=True)
+def _cut(request):
+    """Outputs of separate calls are compared bit for bit here, so the
+    stream split keeps its even cut; the full-size tests run balanced (the
+    benchmark's setting)."""
+    prev = pa.pa_set_decode_balance(request.node.name.startswith("test_full_size"))
+    yield
+    pa.pa_set_decode_balance(prev)
+
+
 @pytest.fixture
 def decode_path():
     prev = pa.pa_set_decode_path(pa.PA_PATH_AUTO)
