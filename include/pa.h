@@ -129,7 +129,7 @@ const char* pa_status_string(int32_t status);
  *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
  *                 aligned; may be NULL when that size is 0.  Split-K scratch,
  *                 except that the stream split keeps its balance state (see
- *                 pa_set_decode_balance) in the first 256 bytes between
+ *                 pa_set_decode_balance) in the first 4352 bytes between
  *                 calls: any contents on entry are valid input (a header it
  *                 does not recognise means the even cut).  Reusing one
  *                 workspace across calls lets the balance adapt.
@@ -244,7 +244,7 @@ int32_t pa_set_decode_path(int32_t path);
  * wave records how long each chunk's slowest wave took, and the next reduce
  * pass moves each chunk's share of the next call's tiles halfway towards its
  * measured rate (shares kept within 1/16 .. 3/16).  The state lives in the
- * first 256 bytes of the workspace (of the static array for
+ * first 4352 bytes of the workspace (of the static array for
  * pa_decode_noalloc), so it carries over only between calls that share one.
  * The cut changes where the fp32 merges fall: outputs of two calls then
  * agree up to the order of those merges, not bit for bit.  With balancing
@@ -294,8 +294,9 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
  * through registers into LDS (16-bit and 8-bit pools).  PA_PREFILL_DMA: the
  * tiles go from memory straight into LDS and the P.V operands are read from
  * it transposed (16-bit pools only; PA_ERR_SHAPE for 8-bit pools).
- * PA_PREFILL_AUTO: the faster of the two on the measured workloads (today
- * the LDS kernel).  Results agree up to the order of fp32 sums.
+ * PA_PREFILL_AUTO: the faster of the two on the measured workloads (the DMA
+ * kernel for 16-bit pools, the LDS kernel for 8-bit pools).  Results agree
+ * up to the order of fp32 sums.
  * Process-wide; returns the previous value (-1 for an unknown path, which
  * leaves the setting unchanged). */
 typedef enum { PA_PREFILL_AUTO = 0, PA_PREFILL_LDS = 1, PA_PREFILL_DMA = 2 } pa_prefill_path;

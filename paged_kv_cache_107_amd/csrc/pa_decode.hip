@@ -485,25 +485,44 @@ __device__ void partition_cut(const DecodeArgs& a, long long T, int nwg, int* s_
   if (!sp.dense()) s_cut[0] = -1;
 }
 
-// The reduce pass's first workgroup: turn the last partition pass's record
-// into the next cut, or initialise an invalid header with the even cut.
-// One thread; plain vector loads and stores (the partition pass's atomics
-// and stores are complete: it ran before on the same stream).
-__device__ void update_balance(StreamBalance* h) {
+// The reduce pass's first workgroup (every thread): turn the last partition
+// pass's record into the next cut, or initialise an invalid header with the
+// even cut.  Each chunk's time is the largest of its waves' slots (LDS
+// maximum), then one thread updates the cut.  Plain vector loads and stores:
+// the partition pass ran before on the same stream, so its stores are
+// complete.  nwg: the partition pass's workgroups.
+__device__ void update_balance(StreamBalance* h, int nwg) {
+  __shared__ uint32_t s_dmax[kXcds];
+  __shared__ int s_state;  // 0: nothing to do, 1: initialise, 2: update
+  if (threadIdx.x == 0) {
+    uint32_t cum[kXcds + 1];
+    s_state = !read_cut(h, cum) ? 1 : (h->stamped && nwg % kXcds == 0) ? 2 : 0;
+  }
+  if (threadIdx.x < kXcds) s_dmax[threadIdx.x] = 0;
+  __syncthreads();
+  const int state = s_state;
+  if (state == 2) {
+    // with nwg a multiple of 8, the ranks of chunk x are [x R, (x + 1) R)
+    const int R = kWaves * (nwg / kXcds);
+    for (int r = threadIdx.x; r < kWaves * nwg; r += kThreads)
+      atomicMax(&s_dmax[r / R], h->wave_dur[r]);
+  }
+  __syncthreads();
+  if (threadIdx.x != 0 || state == 0) return;
   uint32_t cum[kXcds + 1];
-  if (!read_cut(h, cum)) {
+  if (state == 1) {
     h->magic = kBalanceMagic;
     for (int x = 0; x <= kXcds; ++x) h->cum[x] = kBalanceOne / kXcds * x;
-    for (int x = 0; x < kXcds; ++x) h->tiles[x] = h->dur[x] = 0;
+    for (int x = 0; x < kXcds; ++x) h->tiles[x] = 0;
     h->stamped = 0;
     return;
   }
-  if (!h->stamped) return;
+  read_cut(h, cum);
   float rate[kXcds], total = 0.f;
   bool ok = true;
   uint32_t dmin = 0xFFFFFFFFu, dmax = 0;
   for (int x = 0; x < kXcds; ++x) {
-    const uint32_t n = h->tiles[x], d = h->dur[x];
+    const uint32_t n = h->tiles[x], d = s_dmax[x];
     ok = ok && n > 0 && d > 0;
     rate[x] = d > 0 ? (float)n / (float)d : 0.f;
     total += rate[x];
@@ -538,7 +557,6 @@ __device__ void update_balance(StreamBalance* h) {
     if (good)
       for (int x = 0; x <= kXcds; ++x) h->cum[x] = next[x];
   }
-  for (int x = 0; x < kXcds; ++x) h->dur[x] = 0;
   h->stamped = 0;
 }
 
@@ -851,11 +869,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
                  split.dense()};
     }
     reinterpret_cast<int4*>(a.ws_owner)[rank] = rec;
-    if (timed) {
-      const uint32_t took = (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
-      __hip_atomic_fetch_max(&a.ws_balance->dur[blockIdx.x % kXcds], took, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (timed) a.ws_balance->wave_dur[rank] = (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
   }
 }
 
@@ -1115,7 +1129,7 @@ template <class E>
 __global__ __launch_bounds__(kThreads) void decode_reduce_stream(DecodeArgs a) {
   constexpr int D = 128;
   const int r = blockIdx.x;
-  if (r == 0 && threadIdx.x == 0 && a.ws_balance != nullptr) update_balance(a.ws_balance);
+  if (r == 0 && a.ws_balance != nullptr) update_balance(a.ws_balance, a.stream_waves / kWaves);
   const int4 rec = reinterpret_cast<const int4*>(a.ws_owner)[r];
   const int pq = rec.x;
   if (pq < 0) return;

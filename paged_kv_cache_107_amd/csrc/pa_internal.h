@@ -10,6 +10,11 @@
 namespace pa {
 
 // Everything a decode kernel needs, passed by value.
+// Stream split limits: the sequence table lives in LDS, and the wave count
+// (one 4-wave workgroup per CU of a 256-CU part) bounds the workspace.
+constexpr int kStreamMaxSeqs = 4096;
+constexpr int kStreamMaxWaves = 1024;
+
 struct DecodeArgs {
   const void* q;
   const void* k_pool;
@@ -46,21 +51,24 @@ struct DecodeArgs {
 // Balance of the stream split, kept between calls in the first
 // kStreamBalanceBytes of a stream workspace.  The flat tile order is cut into
 // one chunk per XCD; with weights, chunk x covers tiles [T cum[x] / 2^16,
-// T cum[x + 1] / 2^16).  A partition pass records each chunk's tile count and
-// the longest time one of its waves took (100 MHz ticks, vector atomics); the
-// next reduce pass's first workgroup turns them into the cut of the next
-// call, with each chunk's share moved halfway towards its measured rate
-// (left alone when the chunks ended within 1/64 of each other).  A
-// workspace whose magic does not match starts from the even cut.
+// T cum[x + 1] / 2^16).  A partition pass records each chunk's tile count,
+// and each wave the time it took (100 MHz ticks) in its own slot of
+// wave_dur (plain stores: no atomics on shared words); the next reduce
+// pass's first workgroup takes each chunk's slowest wave and turns the
+// record into the cut of the next call, with each chunk's share moved
+// halfway towards its measured rate (left alone when the chunks ended within
+// 1/64 of each other).  A workspace whose magic does not match starts from
+// the even cut.
 struct StreamBalance {
   uint32_t magic;    // kBalanceMagic when the fields below are valid
-  uint32_t stamped;  // tiles/dur hold a partition pass's record
+  uint32_t stamped;  // tiles and wave_dur hold a partition pass's record
   uint32_t pad[2];
   uint32_t cum[12];  // cum[0..8]: the cut, cum[0] = 0, cum[8] = 2^16
   uint32_t tiles[8];
-  uint32_t dur[8];
+  uint32_t pad2[40];
+  uint32_t wave_dur[kStreamMaxWaves];  // by wave rank
 };
-constexpr size_t kStreamBalanceBytes = 256;
+constexpr size_t kStreamBalanceBytes = 256 + 4 * kStreamMaxWaves;
 static_assert(sizeof(StreamBalance) <= kStreamBalanceBytes, "balance header");
 
 // Bit of the caller's status word: a table entry inside an attended range
@@ -74,10 +82,6 @@ enum class DecodeKernel {
   kMfmaStream,  // matrix cores, flat tile order split evenly over the waves
 };
 
-// Stream split limits: the sequence table lives in LDS, and the wave count
-// (one 4-wave workgroup per CU of a 256-CU part) bounds the workspace.
-constexpr int kStreamMaxSeqs = 4096;
-constexpr int kStreamMaxWaves = 1024;
 
 // Pool element types the kernels are built for: the activation dtype itself,
 // or 8-bit E4M3 codes (matrix-core kernels only).

@@ -525,19 +525,22 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
 // state of its column (shared with its partner lane ^ 32) with the lazy
 // rescale of the decode kernel.
 //
-// LDS: three stages of [K 32 x 128 | V 32 x 128] 16-bit rows; a row's 16
-// chunks of 16 bytes are stored in the order chunk ^ swz(row), so the K
-// operand reads (16 rows, one chunk) and the transposed V reads (4 rows, two
-// chunks) spread over the banks.  A workgroup's four waves load one step
-// (16 KiB, four 1 KiB loads per wave) two steps ahead, with one barrier per
-// step.
-#ifndef PF_PRIO
-#define PF_PRIO 0    // raise wave priority around the products
-#endif
-#ifndef PF_WAVES
-#define PF_WAVES 4   // waves per workgroup (4 or 8)
-#endif
-constexpr int kDmaWaves = PF_WAVES;
+// LDS: a ring of four stages of [K 32 x 128 | V 32 x 128] 16-bit rows; a
+// row's 16 chunks of 16 bytes are stored in the order chunk ^ swz(row), so
+// the K operand reads (16 rows, one chunk) and the transposed V reads (4
+// rows, two chunks) spread over the banks.  A workgroup's four waves load
+// one step (16 KiB, four 1 KiB loads per wave) three steps ahead, with one
+// barrier per step.  The operand reads are plain LDS loads of distinct stage
+// arrays, so the compiler waits only for loads into the stage it reads.
+//
+// Each iteration forms the scores of the next step (K of st + 1) and
+// finishes step st (mask, weights, P.V with V of st): the score products do
+// not depend on the weights, so they run on the matrix cores while the wave
+// computes the weights.  The block ids of a step are loaded by scalar loads
+// one iteration before their first use.  Groups of four steps that need no
+// mask (every key inside the wave's rows' ranges, five or more steps before
+// the end of the walk) run a lean iteration without masks or bounds checks.
+constexpr int kDmaWaves = 4;
 constexpr int kDmaPieces = 8 / kDmaWaves;  // 1 KiB pieces of K (and of V) a wave loads per step
 constexpr int kDmaThreads = kDmaWaves * kWave;
 constexpr int kDmaRows = 32;                      // query rows per wave
@@ -560,50 +563,6 @@ __device__ __forceinline__ int dma_swz(int r) {
 }
 // byte offset of (row r, 16-byte chunk c) in a 32-row region
 __device__ __forceinline__ int dma_pos(int r, int c) { return (r * 16 + (c ^ dma_swz(r))) * 16; }
-
-// LDS operand reads for the DMA kernel, written as inline asm with their wait
-// inside the block.  The stages are filled by direct-to-LDS loads; the
-// compiler cannot tell which stage a pending load writes, and before a read
-// of a stage it would otherwise wait for every load in flight -- including
-// those of the steps ahead, just issued.  The kernel's own counter waits and
-// barriers order the loads and the reads.  Every output is used.
-__device__ __forceinline__ void lds_read8_b128(u32x4 (&r)[8], const uint32_t (&a)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %9\n\t"
-      "ds_read_b128 %2, %10\n\t"
-      "ds_read_b128 %3, %11\n\t"
-      "ds_read_b128 %4, %12\n\t"
-      "ds_read_b128 %5, %13\n\t"
-      "ds_read_b128 %6, %14\n\t"
-      "ds_read_b128 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-}
-// Eight transposed 64-bit reads (ds_read_b64_tr_b16), paired into four
-// 128-bit operands: r[j] = {read 2 j, read 2 j + 1}.
-__device__ __forceinline__ void lds_read8_tr16(u32x4 (&r)[4], const uint32_t (&a)[8]) {
-  u32x2 x[8];
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
-        "=&v"(x[6]), "=&v"(x[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = u32x4{x[2 * j][0], x[2 * j][1], x[2 * j + 1][0], x[2 * j + 1][1]};
-}
 
 template <class E>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
@@ -691,12 +650,26 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
       WIN ? max(max(ctx - n + max(top - (kDmaWaves - 1), 0) * QT, 0) - W + 1, 0) / kDmaKeys : 0;
   const int kbeg = WIN ? max(unmasked - W + 1, 0) : 0;
 
-  // tile t of the walk: its block id when inside the pool, else -1
-  auto block_of = [&](int t) __attribute__((always_inline)) -> int {
-    if (t >= ntiles) return -1;
-    const int b = scalar_load(table + ((t * kTile) >> a.log2_bs));
-    return (unsigned)b < (unsigned)a.num_blocks ? b : -1;
+  // Block ids of step st's two tiles (2 st, 2 st + 1): -1 past the walk or
+  // outside the pool.  Scalar loads, issued one step ahead of their use so
+  // that the wait at the top of the next step covers them.
+  struct Ids {
+    int b0, b1;
   };
+  // raw table entries (unchecked: the check is the first use, placed
+  // after the wait that covers the loads)
+  auto raw_ids = [&](int st) __attribute__((always_inline)) -> Ids {
+    const int t = 2 * st;
+    int b0 = -1, b1 = -1;
+    if (t < ntiles) b0 = scalar_load(table + ((t * kTile) >> a.log2_bs));
+    if (t + 1 < ntiles) b1 = scalar_load(table + (((t + 1) * kTile) >> a.log2_bs));
+    return Ids{b0, b1};
+  };
+  auto checked = [&](const Ids& r) __attribute__((always_inline)) -> Ids {
+    return Ids{(unsigned)r.b0 < (unsigned)a.num_blocks ? r.b0 : -1,
+               (unsigned)r.b1 < (unsigned)a.num_blocks ? r.b1 : -1};
+  };
+  auto ids_of = [&](int st) __attribute__((always_inline)) -> Ids { return checked(raw_ids(st)); };
 
   // DMA lane offsets: wave w loads 1 KiB pieces 2 w and 2 w + 1 of the K
   // and the V region, rows 8 w .. 8 w + 7 of the step, i.e. rows 8 (w % 2) ..
@@ -709,11 +682,6 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int r = 4 * (kDmaPieces * w + x) + (lane >> 4);
     dma_off[x] = (uint32_t)((r & 15) * kRowBytes128 + (((lane & 15) ^ dma_swz(r)) * 16));
   }
-  // LDS read offsets within a stage.  K operand of k-step s: row pi(c32),
-  // chunk 2 s + h.  V^T operand of d-tile dt, k-step ks, half hr: the
-  // transposed 64-bit read whose source lane (l % 16) addresses row 16 ks +
-  // 8 (l / 32) + 4 hr + (l % 16) / 4, elements 32 dt + 16 ((l / 16) % 2) +
-  // 4 (l % 4) .. +3.
   const int kr = 16 * (c32 >> 4) + 8 * ((c32 >> 2) & 1) + 4 * ((c32 >> 3) & 1) + (c32 & 3);
   uint32_t koff[8];
 #pragma unroll
@@ -731,9 +699,8 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
       }
     }
 
-  // Loads of step st into stage buffer `buf`: this wave's two K and two V
-  // pieces of tile 2 st + w / 2 (V rows past the sequence read as zeros).
-  auto issue = [&](int st, char* buf, int b) __attribute__((always_inline)) {
+  auto issue = [&](int st, char* buf, const Ids& id) __attribute__((always_inline)) {
+    const int b = tw ? id.b1 : id.b0;
     const int t = 2 * st + tw;
     const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
     const rsrc_t ks = make_rsrc(kbase0 + off, b >= 0 ? 16u * kRowBytes128 : 0u);
@@ -755,48 +722,39 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
 
-  // S^T of one step from stage buffer `buf`: the eight K operands, then the
-  // eight products (the matrix cores accumulate back to back).
-  auto lds_addr = [](const char* buf) __attribute__((always_inline)) -> uint32_t {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)buf;
-  };
+  typedef const __attribute__((address_space(3))) char lds_cchar;
   auto qk = [&](const char* buf) __attribute__((always_inline)) -> f32x16 {
-    const uint32_t b = lds_addr(buf);
-    uint32_t ka[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) ka[s] = b + koff[s];
-    u32x4 kop[8];
-    lds_read8_b128(kop, ka);
     f32x16 sacc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) sacc = mfma32<E>(kop[s], qv[s], sacc);
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 kop = *reinterpret_cast<const lds_u32x4*>((lds_cchar*)buf + koff[s]);
+      sacc = mfma32<E>(kop, qv[s], sacc);
+    }
     return sacc;
   };
-  // The rest of step st from its scores: masks, the lazy rescale, the
-  // weights, and O^T += V^T . P^T with the V^T operands read transposed from
-  // `buf`; oka / okb: the step's two tiles had blocks in the pool.
-  auto softmax_pv = [&](int st, const f32x16& sacc, const char* buf, bool oka, bool okb)
-      __attribute__((always_inline)) {
+  auto vtr = [&](const char* buf, uint32_t off) __attribute__((always_inline)) -> u32x2 {
+    const i16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + off));
+    return __builtin_bit_cast(u32x2, r);
+  };
+  auto softmax_pv = [&](int st, const f32x16& sacc, const char* buf, bool oka, bool okb,
+                        const char* nbuf, f32x16& snext, bool may_mask) __attribute__((always_inline)) {
     const int k0 = st * kDmaKeys;
-    const uint32_t b = lds_addr(buf);
     u32x4 vop[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint32_t va[8];
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        va[2 * dt] = b + voff[dt][2 * ks];
-        va[2 * dt + 1] = b + voff[dt][2 * ks + 1];
+        const u32x2 lo2 = vtr(buf, voff[dt][2 * ks]), hi2 = vtr(buf, voff[dt][2 * ks + 1]);
+        vop[ks][dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
       }
-      lds_read8_tr16(vop[ks], va);
-    }
     float sv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = sacc[v];
     const bool masked =
-        k0 + kDmaKeys - 1 > unmasked || (WIN && k0 < kend - W) || !oka || !okb;
+        may_mask && (k0 + kDmaKeys - 1 > unmasked || (WIN && k0 < kend - W) || !oka || !okb);
     if (masked) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -816,6 +774,9 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
       m = mn;
     }
+    // the next step's scores: products independent of the weights below,
+    // so the matrix cores run them while this wave computes the weights
+    snext = qk(nbuf);
     u32x4 pw[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -826,63 +787,90 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
                      Mfma<E>::round16x2(pf[4], pf[5]), Mfma<E>::round16x2(pf[6], pf[7])};
       lsum = sum2(E{}, pw[ks][3], sum2(E{}, pw[ks][2], sum2(E{}, pw[ks][1], sum2(E{}, pw[ks][0], lsum))));
     }
-    if (PF_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32<E>(vop[ks][dt], pw[ks], o[dt]);
-    if (PF_PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
-  // this wave computes step st: its rows reach keys [kbeg, kend)
   auto runs = [&](int st) __attribute__((always_inline)) {
     return mine && st * kDmaKeys < kend && (!WIN || (st + 1) * kDmaKeys > kbeg);
   };
-  auto tile_ok = [&](int st, int half) __attribute__((always_inline)) {
-    return block_of(2 * st + half) >= 0;
-  };
   // The ring: step st lives in stage (st - s0) % 4, loaded three steps
-  // ahead.  The step is software-pipelined across the iterations: iteration
-  // st forms the scores of st + 1 (its products run on the matrix cores
-  // while this wave computes the weights of st) and finishes st.  So before
-  // iteration st a wave waits for its own loads of st + 1 (those of st + 2
-  // may still be in flight); the barrier then makes every wave's loads of
-  // st + 1 visible and frees the stage of st - 1, which the loads of st + 3
-  // fill.
+  // ahead; iteration st forms the scores of st + 1 and finishes st.  Block
+  // ids run four steps ahead of the compute (ids of st .. st + 3 held, those
+  // of st + 4 loaded during iteration st).
   const int s0 = st_begin;
-  issue(s0, s_st0, block_of(2 * s0 + tw));
-  if (s0 + 1 < nsteps) issue(s0 + 1, s_st1, block_of(2 * s0 + 2 + tw));
-  if (s0 + 2 < nsteps) issue(s0 + 2, s_st2, block_of(2 * s0 + 4 + tw));
-  // wait for this wave's loads of s0 (those of s0 + 1 and s0 + 2 may be
-  // outstanding), a plain s_barrier: __syncthreads would wait for them all
+  Ids id0 = ids_of(s0), id1 = ids_of(s0 + 1), id2 = ids_of(s0 + 2), raw3 = raw_ids(s0 + 3);
+  issue(s0, s_st0, id0);
+  if (s0 + 1 < nsteps) issue(s0 + 1, s_st1, id1);
+  if (s0 + 2 < nsteps) issue(s0 + 2, s_st2, id2);
   if (s0 + 2 < nsteps)
-    __builtin_amdgcn_s_waitcnt(0x0070 | (4 * kDmaPieces));  // vmcnt(two steps' loads), lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0070 | (4 * kDmaPieces));
   else if (s0 + 1 < nsteps)
-    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));  // vmcnt(one step's loads), lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));
   else
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0070);
   __builtin_amdgcn_s_barrier();
   f32x16 scur = {};
-  if (runs(s0) && (tile_ok(s0, 0) || tile_ok(s0, 1))) scur = qk(s_st0);
+  if (runs(s0) && (id0.b0 >= 0 || id0.b1 >= 0)) scur = qk(s_st0);
   auto step = [&](int st, const char* cur, const char* next, char* fill)
       __attribute__((always_inline)) {
     if (st + 2 < nsteps)
       __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));  // own loads of st + 1 landed
     else
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(0x0070);
     __builtin_amdgcn_s_barrier();
-    if (st + 3 < nsteps) issue(st + 3, fill, block_of(2 * (st + 3) + tw));
-    f32x16 snext = {};
-    if (st + 1 < nsteps && runs(st + 1) && (tile_ok(st + 1, 0) || tile_ok(st + 1, 1))) {
-      if (PF_PRIO) __builtin_amdgcn_s_setprio(1);
+    const Ids id3 = checked(raw3);  // loaded during the previous step
+    if (st + 3 < nsteps) issue(st + 3, fill, id3);
+    raw3 = raw_ids(st + 4);
+    // The next step's scores are formed whether or not this wave needs them
+    // (past its rows' keys, or past the walk, they are dropped unread), so
+    // the products share one block with this step's weights.
+    f32x16 snext;
+    if (runs(st) && (id0.b0 >= 0 || id0.b1 >= 0))
+      softmax_pv(st, scur, cur, id0.b0 >= 0, id0.b1 >= 0, next, snext, true);
+    else
       snext = qk(next);
-      if (PF_PRIO) __builtin_amdgcn_s_setprio(0);
-    }
-    const bool oka = tile_ok(st, 0), okb = tile_ok(st, 1);
-    if (runs(st) && (oka || okb)) softmax_pv(st, scur, cur, oka, okb);
     scur = snext;
+    id0 = id1;
+    id1 = id2;
+    id2 = id3;
   };
-  for (int st = s0; st < nsteps; st += 4) {
+  // Steady state: groups of four steps whose keys all lie inside this
+  // wave's rows' ranges, at least five steps before the end of the walk: no
+  // masks and no bounds checks.  A table entry outside the pool there loads
+  // zeros (an empty descriptor) instead of being masked: the output of that
+  // sequence is then unspecified, as for any bad entry, and the status scan
+  // after the walk reports it.
+  const int fast_end = WIN ? s0 : min(nsteps - 5, mine ? (unmasked + 1) / kDmaKeys : s0);
+  const int groups = max(fast_end - s0, 0) >> 2;
+  auto fast_step = [&](int st, const char* cur, const char* next, char* fill)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));  // own loads of st + 1 landed
+    __builtin_amdgcn_s_barrier();
+    const Ids id3 = checked(raw3);
+    issue(st + 3, fill, id3);
+    {
+      const int t = 2 * (st + 4);
+      raw3 = Ids{scalar_load(table + ((t * kTile) >> a.log2_bs)),
+                 scalar_load(table + (((t + 1) * kTile) >> a.log2_bs))};
+    }
+    f32x16 snext;
+    softmax_pv(st, scur, cur, true, true, next, snext, false);
+    scur = snext;
+    id0 = id1;
+    id1 = id2;
+    id2 = id3;
+  };
+  int st = s0;
+  for (int gi = 0; gi < groups; ++gi, st += 4) {
+    fast_step(st, s_st0, s_st1, s_st3);
+    fast_step(st + 1, s_st1, s_st2, s_st0);
+    fast_step(st + 2, s_st2, s_st3, s_st1);
+    fast_step(st + 3, s_st3, s_st0, s_st2);
+  }
+  for (; st < nsteps; st += 4) {
     step(st, s_st0, s_st1, s_st3);
     if (st + 1 >= nsteps) break;
     step(st + 1, s_st1, s_st2, s_st0);
@@ -957,10 +945,11 @@ int prefill_query_blocks(int max_query_len, int group) {
 
 pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, int path, hipStream_t st) {
   const bool fp8 = kv == KvType::kFp8;
-  // the direct-to-LDS kernel runs 16-bit pools when asked for; AUTO runs the
-  // register-staged kernel, which measured as fast or faster on the 8B
-  // chunked-prefill workload
-  const bool dma = !fp8 && path == PA_PREFILL_DMA;
+  // 16-bit pools run the direct-to-LDS kernel unless the register-staged one
+  // is asked for (AUTO: the direct kernel, about 7% faster on the 8B chunked
+  // workload); 8-bit pools, whose codes are widened on the way into LDS, run
+  // the register-staged kernel
+  const bool dma = !fp8 && path != PA_PREFILL_LDS;
   if (fp8 && path == PA_PREFILL_DMA) return PA_ERR_SHAPE;
   if (dtype == PA_BF16) {
     if (dma) return launch_dma<BF16>(a, st);

@@ -58,12 +58,12 @@ def test_workspace_bytes():
     assert f(f32, b, hq, 8192, 512) == grid
     assert f(f32, b, hq, 8192, 0) == f(f32, b, hq, 8192, 512)
 
-    # stream split: the 256-byte balance header, 16-byte merge records of the
-    # 1024 wave ranks, then (max, sum) and outputs for (B * Hkv + 1024) slots
-    # of G heads each
+    # stream split: the balance header (256 bytes and a 4-byte time per wave
+    # rank), 16-byte merge records of the 1024 wave ranks, then (max, sum) and
+    # outputs for (B * Hkv + 1024) slots of G heads each
     def stream(b, hkv, g):
         heads = (b * hkv + 1024) * g
-        return 256 + 16 * 1024 + (heads * 8 + 255) // 256 * 256 + heads * d * 4
+        return 256 + 4 * 1024 + 16 * 1024 + (heads * 8 + 255) // 256 * 256 + heads * d * 4
     assert f(bf16, b, hq, 8192, 512) == max(grid, stream(b, 8, 4))
     assert f(bf16, b, hq, 100, 512) == stream(b, 8, 4)
     assert f(bf16, 4096, hq, 100, 512) == stream(4096, 8, 4)
