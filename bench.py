@@ -801,6 +801,9 @@ def main(argv=None):
     ap.add_argument("--e2e-steps", type=int, default=50,
                     help="real decode steps (plan + run) at the end, timing the host "
                          "planner (0 = skip)")
+    ap.add_argument("--decode-balance", type=int, choices=(0, 1), default=1,
+                    help="run-time balance of the decode stream split's XCD chunks (1, the "
+                         "library default) or the even cut (0)")
     ap.add_argument("--only-configs", nargs="*", metavar="NAME", default=None,
                     help="time the other named workloads only, or just the NAMEs given (for a "
                          "profiler run)")
@@ -817,6 +820,7 @@ def main(argv=None):
     import paged_kv_cache_107_amd as pa
     torch.cuda.set_device(0)
     pa.lib()
+    pa.pa_set_decode_balance(bool(args.decode_balance))
     others = [n for n in CONFIG_WORKLOADS if n != args.workload]
     if args.only_configs is not None:
         names = args.only_configs or others
@@ -941,6 +945,7 @@ def main(argv=None):
             "global_batch": d.batch,
             "attended_tokens": int(ctx.sum()),
             "partition_tokens": pt,
+            "decode_balance": "run-time XCD balance" if args.decode_balance else "even cut",
             "parallelism": "none (1 GPU)",
         },
         "kv_gbps": round(kv_gbps_step, 1),

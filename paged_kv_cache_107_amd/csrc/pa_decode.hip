@@ -457,10 +457,11 @@ struct StreamSplit {
 };
 
 // A balance header's cut, if the header is valid: magic, cum[0] = 0,
-// cum[8] = 2^16, every share within [kShareMin, kShareMax].
-__device__ bool read_cut(const StreamBalance* h, uint32_t (&cum)[kXcds + 1]) {
-  if (h == nullptr || h->magic != kBalanceMagic) return false;
-  for (int x = 0; x <= kXcds; ++x) cum[x] = h->cum[x];
+// cum[8] = 2^16, every share within [kShareMin, kShareMax].  `w`: the
+// header's words (magic at 0, cum at 4..12), in global memory or an LDS copy.
+__device__ bool read_cut(const uint32_t* w, uint32_t (&cum)[kXcds + 1]) {
+  if (w == nullptr || w[0] != kBalanceMagic) return false;
+  for (int x = 0; x <= kXcds; ++x) cum[x] = w[4 + x];
   if (cum[0] != 0 || cum[kXcds] != kBalanceOne) return false;
   for (int x = 0; x < kXcds; ++x) {
     if (cum[x + 1] < cum[x]) return false;
@@ -468,6 +469,9 @@ __device__ bool read_cut(const StreamBalance* h, uint32_t (&cum)[kXcds + 1]) {
     if (sh < kShareMin || sh > kShareMax) return false;
   }
   return true;
+}
+__device__ const uint32_t* header_words(const StreamBalance* h) {
+  return reinterpret_cast<const uint32_t*>(h);
 }
 
 // The cut of a partition pass, by thread 0 into s_cut[0..8] (LDS; the caller
@@ -479,7 +483,7 @@ __device__ void partition_cut(const DecodeArgs& a, long long T, int nwg, int* s_
   StreamSplit sp{T, nwg};
   uint32_t cum[kXcds + 1];
   s_cut[0] = -1;
-  if (!a.balance || !sp.balanced_size() || !read_cut(a.ws_balance, cum)) return;
+  if (!a.balance || !sp.balanced_size() || !read_cut(header_words(a.ws_balance), cum)) return;
   for (int x = 0; x <= kXcds; ++x) s_cut[x] = (int)((T * (long long)cum[x]) >> 16);
   sp.cut = s_cut;
   if (!sp.dense()) s_cut[0] = -1;
@@ -487,42 +491,51 @@ __device__ void partition_cut(const DecodeArgs& a, long long T, int nwg, int* s_
 
 // The reduce pass's first workgroup (every thread): turn the last partition
 // pass's record into the next cut, or initialise an invalid header with the
-// even cut.  Each chunk's time is the largest of its waves' slots (LDS
-// maximum), then one thread updates the cut.  Plain vector loads and stores:
-// the partition pass ran before on the same stream, so its stores are
-// complete.  nwg: the partition pass's workgroups.
+// even cut.  One round of loads: the header's first 24 words into LDS and
+// each thread's wave slots, in parallel; each chunk's time is the largest
+// of its waves' slots (LDS maximum); then one thread updates the cut.  Plain
+// vector loads and stores: the partition pass ran before on the same stream,
+// so its stores are complete.  nwg: the partition pass's workgroups.
 __device__ void update_balance(StreamBalance* h, int nwg) {
+  constexpr int kWords = 24;  // magic, stamped, pad[2], cum[12], tiles[8]
+  constexpr int kPer = kStreamMaxWaves / kThreads;
+  __shared__ uint32_t s_hdr[kWords];
   __shared__ uint32_t s_dmax[kXcds];
-  __shared__ int s_state;  // 0: nothing to do, 1: initialise, 2: update
-  if (threadIdx.x == 0) {
-    uint32_t cum[kXcds + 1];
-    s_state = !read_cut(h, cum) ? 1 : (h->stamped && nwg % kXcds == 0) ? 2 : 0;
-  }
+  const int n = kWaves * nwg;  // wave ranks of the partition pass (<= kStreamMaxWaves)
+  if (threadIdx.x < kWords) s_hdr[threadIdx.x] = header_words(h)[threadIdx.x];
   if (threadIdx.x < kXcds) s_dmax[threadIdx.x] = 0;
-  __syncthreads();
-  const int state = s_state;
-  if (state == 2) {
-    // with nwg a multiple of 8, the ranks of chunk x are [x R, (x + 1) R)
-    const int R = kWaves * (nwg / kXcds);
-    for (int r = threadIdx.x; r < kWaves * nwg; r += kThreads)
-      atomicMax(&s_dmax[r / R], h->wave_dur[r]);
+  uint32_t d[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int r = (int)threadIdx.x + k * kThreads;
+    d[k] = r < n ? h->wave_dur[r] : 0u;
   }
   __syncthreads();
-  if (threadIdx.x != 0 || state == 0) return;
+  if (nwg % kXcds == 0) {
+    // with nwg a multiple of 8, the ranks of chunk x are [x R, (x + 1) R)
+    const int R = n / kXcds;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int r = (int)threadIdx.x + k * kThreads;
+      if (r < n) atomicMax(&s_dmax[r / R], d[k]);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
   uint32_t cum[kXcds + 1];
-  if (state == 1) {
+  if (!read_cut(s_hdr, cum)) {
     h->magic = kBalanceMagic;
     for (int x = 0; x <= kXcds; ++x) h->cum[x] = kBalanceOne / kXcds * x;
     for (int x = 0; x < kXcds; ++x) h->tiles[x] = 0;
     h->stamped = 0;
     return;
   }
-  read_cut(h, cum);
+  if (!s_hdr[1] || nwg % kXcds != 0) return;  // no record to use
   float rate[kXcds], total = 0.f;
   bool ok = true;
   uint32_t dmin = 0xFFFFFFFFu, dmax = 0;
   for (int x = 0; x < kXcds; ++x) {
-    const uint32_t n = h->tiles[x], d = s_dmax[x];
+    const uint32_t n = s_hdr[16 + x], d = s_dmax[x];
     ok = ok && n > 0 && d > 0;
     rate[x] = d > 0 ? (float)n / (float)d : 0.f;
     total += rate[x];
