@@ -95,7 +95,8 @@ __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
 // kLptSeqs in batch order.
 // Every thread of the workgroup calls it (it has barriers).
 template <int THREADS>
-__device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
+__device__ void pick_item_in(const PrefillArgs& a, int k, int Z, int& i, int& zq,
+                             uint8_t* s_cls, int* s_cnt, int* s_pick) {
   const int B = a.num_seqs;
   if (B <= kLptSeqs) {
     // Classes are counted in LDS; class C holds ranks [start(C), start(C) +
@@ -103,8 +104,6 @@ __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
     // [start * Z, (start + cnt) * Z), sequence by sequence.  The item's class is found
     // from the counts, then its sequence -- the j-th of the class in batch
     // order -- by one wave with ballots over 64 sequences at a time.
-    __shared__ uint8_t s_cls[kLptSeqs];  // length class of each sequence (< kClasses)
-    __shared__ int s_cnt[kClasses], s_pick[3];
     const int t = threadIdx.x;
     for (int c = t; c < kClasses; c += THREADS) s_cnt[c] = 0;
     __syncthreads();
@@ -168,6 +167,13 @@ __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
     i = k / Z;
     zq = k - i * Z;
   }
+}
+
+template <int THREADS>
+__device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
+  __shared__ uint8_t s_cls[kLptSeqs];  // length class of each sequence (< kClasses)
+  __shared__ int s_cnt[kClasses], s_pick[3];
+  pick_item_in<THREADS>(a, k, Z, i, zq, s_cls, s_cnt, s_pick);
 }
 
 // Kernel: the K/V tiles of a step are shared through LDS.  Four
@@ -525,21 +531,25 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
 // state of its column (shared with its partner lane ^ 32) with the lazy
 // rescale of the decode kernel.
 //
-// LDS: a ring of four stages of [K 32 x 128 | V 32 x 128] 16-bit rows; a
+// LDS: a ring of three stages of [K 32 x 128 | V 32 x 128] 16-bit rows; a
 // row's 16 chunks of 16 bytes are stored in the order chunk ^ swz(row), so
 // the K operand reads (16 rows, one chunk) and the transposed V reads (4
 // rows, two chunks) spread over the banks.  A workgroup's four waves load
-// one step (16 KiB, four 1 KiB loads per wave) three steps ahead, with one
+// one step (16 KiB, four 1 KiB loads per wave) two steps ahead, with one
 // barrier per step.  The operand reads are plain LDS loads of distinct stage
 // arrays, so the compiler waits only for loads into the stage it reads.
 //
-// Each iteration forms the scores of the next step (K of st + 1) and
-// finishes step st (mask, weights, P.V with V of st): the score products do
-// not depend on the weights, so they run on the matrix cores while the wave
-// computes the weights.  The block ids of a step are loaded by scalar loads
-// one iteration before their first use.  Groups of four steps that need no
-// mask (every key inside the wave's rows' ranges, five or more steps before
-// the end of the walk) run a lean iteration without masks or bounds checks.
+// Three workgroups share a CU (three waves per SIMD: 48 KiB of LDS and at
+// most 170 VGPRs each; the item choice's LDS scratch borrows the third
+// stage): a wave's step is a chain of dependent phases (barrier, loads,
+// scores, maxima, exponentials, P.V), so a third wave per SIMD gives more
+// than overlapping the phases inside one wave, which needs the registers of
+// a second score tile.  The operand read offsets are derived per step from
+// five bases (XORs with immediates) rather than held in 24 registers.  The
+// block ids of a step are loaded by scalar loads one step before their
+// first use.  Groups of three steps that need no mask (every key inside the
+// wave's rows' ranges, three or more steps before the end of the walk) run a
+// lean step without masks or bounds checks.
 constexpr int kDmaWaves = 4;
 constexpr int kDmaPieces = 8 / kDmaWaves;  // 1 KiB pieces of K (and of V) a wave loads per step
 constexpr int kDmaThreads = kDmaWaves * kWave;
@@ -578,18 +588,21 @@ __device__ __forceinline__ f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 template <class E, bool WIN>
-__global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_dma(PrefillArgs a) {
+__global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))) void prefill_dma(PrefillArgs a) {
   constexpr int D = 128;
   using S = typename E::storage;
   __shared__ __attribute__((aligned(1024))) char s_st0[2 * kDmaRegion];
   __shared__ __attribute__((aligned(1024))) char s_st1[2 * kDmaRegion];
   __shared__ __attribute__((aligned(1024))) char s_st2[2 * kDmaRegion];
-  __shared__ __attribute__((aligned(1024))) char s_st3[2 * kDmaRegion];
   const int g = blockIdx.x;
   const int Z = gridDim.y;
   const int k = (int)blockIdx.y + Z * (int)blockIdx.z;
   int i, zq;
-  pick_item<kDmaThreads>(a, k, Z, i, zq);
+  // the item choice's scratch lives in stage 2, which no load fills before
+  // the prologue's barrier
+  pick_item_in<kDmaThreads>(a, k, Z, i, zq, reinterpret_cast<uint8_t*>(s_st2),
+                            reinterpret_cast<int*>(s_st2 + kLptSeqs),
+                            reinterpret_cast<int*>(s_st2 + kLptSeqs + 4 * kClasses));
   const int G = a.group, QT = kDmaRows / G;  // chunk tokens per wave
   const int qa = a.query_start[i], qb = a.query_start[i + 1];
   if (qa < 0 || qb > a.num_tokens || qb <= qa) return;  // the whole workgroup
@@ -608,21 +621,18 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
   const int kend = blk >= 0 ? pos0 + ntok : 0;
   S* out = reinterpret_cast<S*>(a.out);
 
-  // this lane's query column: token tl, head hh
   const int tl = c32 / G, hh = c32 - tl * G;
   const bool live = tl < ntok && pos0 + tl >= 0;
   const int lim = live ? pos0 + tl : kend - 1;
   const int row = tl < ntok ? (qa + tok0 + tl) * a.num_q_heads + g * G + hh : -1;
-  if (kend_wg <= 0) {  // every position of the item negative: zero rows
+  if (kend_wg <= 0) {
     if (row >= 0)
       for (int d = 4 * h; d < D; d += 8)
         *reinterpret_cast<uint2*>(out + (size_t)row * D + d) = uint2{0u, 0u};
-    return;  // the whole workgroup
+    return;
   }
   const bool mine = kend > 0;
 
-  // Q^T operand of k-step s (head_dim 16 s .. 16 s + 15): elements
-  // 16 s + 8 h .. +7 of the lane's query row.
   u32x4 qv[8];
   {
     const S* qrow = reinterpret_cast<const S*>(a.q) + (size_t)max(row, 0) * D + 8 * h;
@@ -650,14 +660,9 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
       WIN ? max(max(ctx - n + max(top - (kDmaWaves - 1), 0) * QT, 0) - W + 1, 0) / kDmaKeys : 0;
   const int kbeg = WIN ? max(unmasked - W + 1, 0) : 0;
 
-  // Block ids of step st's two tiles (2 st, 2 st + 1): -1 past the walk or
-  // outside the pool.  Scalar loads, issued one step ahead of their use so
-  // that the wait at the top of the next step covers them.
   struct Ids {
     int b0, b1;
   };
-  // raw table entries (unchecked: the check is the first use, placed
-  // after the wait that covers the loads)
   auto raw_ids = [&](int st) __attribute__((always_inline)) -> Ids {
     const int t = 2 * st;
     int b0 = -1, b1 = -1;
@@ -669,12 +674,7 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
     return Ids{(unsigned)r.b0 < (unsigned)a.num_blocks ? r.b0 : -1,
                (unsigned)r.b1 < (unsigned)a.num_blocks ? r.b1 : -1};
   };
-  auto ids_of = [&](int st) __attribute__((always_inline)) -> Ids { return checked(raw_ids(st)); };
 
-  // DMA lane offsets: wave w loads 1 KiB pieces 2 w and 2 w + 1 of the K
-  // and the V region, rows 8 w .. 8 w + 7 of the step, i.e. rows 8 (w % 2) ..
-  // of tile w / 2; lane l of piece j fills unit 64 j + l = (row r, slot
-  // l % 16) with chunk (l % 16) ^ swz(r) of that row.
   const int tw = (kDmaPieces * w) >> 2;
   uint32_t dma_off[kDmaPieces];
 #pragma unroll
@@ -683,20 +683,15 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
     dma_off[x] = (uint32_t)((r & 15) * kRowBytes128 + (((lane & 15) ^ dma_swz(r)) * 16));
   }
   const int kr = 16 * (c32 >> 4) + 8 * ((c32 >> 2) & 1) + 4 * ((c32 >> 3) & 1) + (c32 & 3);
-  uint32_t koff[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) koff[s] = (uint32_t)dma_pos(kr, 2 * s + h);
-  uint32_t voff[4][4];
+  const uint32_t koff0 = (uint32_t)dma_pos(kr, h);
+  uint32_t voff0[4];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int hr = 0; hr < 2; ++hr) {
       const int R = 16 * ks + 8 * h + 4 * hr + ((lane & 15) >> 2);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int el = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        voff[dt][2 * ks + hr] = (uint32_t)(kDmaRegion + dma_pos(R, el >> 3) + 2 * (el & 7));
-      }
+      const int el = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      voff0[2 * ks + hr] = (uint32_t)(kDmaRegion + dma_pos(R, el >> 3) + 2 * (el & 7));
     }
 
   auto issue = [&](int st, char* buf, const Ids& id) __attribute__((always_inline)) {
@@ -723,39 +718,26 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
 
   typedef const __attribute__((address_space(3))) char lds_cchar;
-  auto qk = [&](const char* buf) __attribute__((always_inline)) -> f32x16 {
+  // One step from stage `buf`: scores, mask, weights, P.V.  The read
+  // offsets are derived here (XORs with immediates) from bases made opaque,
+  // so they are not held across the loop.
+  auto compute = [&](int st, const char* buf, bool oka, bool okb, bool may_mask)
+      __attribute__((always_inline)) {
+    uint32_t kb0 = koff0, vb[4] = {voff0[0], voff0[1], voff0[2], voff0[3]};
+    asm volatile("" : "+v"(kb0), "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]));
     f32x16 sacc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const u32x4 kop = *reinterpret_cast<const lds_u32x4*>((lds_cchar*)buf + koff[s]);
+      const u32x4 kop = *reinterpret_cast<const lds_u32x4*>((lds_cchar*)buf + (kb0 ^ (32u * s)));
       sacc = mfma32<E>(kop, qv[s], sacc);
     }
-    return sacc;
-  };
-  auto vtr = [&](const char* buf, uint32_t off) __attribute__((always_inline)) -> u32x2 {
-    const i16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + off));
-    return __builtin_bit_cast(u32x2, r);
-  };
-  auto softmax_pv = [&](int st, const f32x16& sacc, const char* buf, bool oka, bool okb,
-                        const char* nbuf, f32x16& snext, bool may_mask) __attribute__((always_inline)) {
     const int k0 = st * kDmaKeys;
-    u32x4 vop[2][4];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const u32x2 lo2 = vtr(buf, voff[dt][2 * ks]), hi2 = vtr(buf, voff[dt][2 * ks + 1]);
-        vop[ks][dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-      }
     float sv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = sacc[v];
-    const bool masked =
-        may_mask && (k0 + kDmaKeys - 1 > unmasked || (WIN && k0 < kend - W) || !oka || !okb);
-    if (masked) {
+    if (may_mask && (k0 + kDmaKeys - 1 > unmasked || (WIN && k0 < kend - W) || !oka || !okb)) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = k0 + 16 * (v >> 3) + 8 * h + (v & 7);
@@ -774,114 +756,69 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2))
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
       m = mn;
     }
-    // the next step's scores: products independent of the weights below,
-    // so the matrix cores run them while this wave computes the weights
-    snext = qk(nbuf);
-    u32x4 pw[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float pf[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(__builtin_fmaf(sv[8 * ks + e], c, -m));
-      pw[ks] = u32x4{Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3]),
-                     Mfma<E>::round16x2(pf[4], pf[5]), Mfma<E>::round16x2(pf[6], pf[7])};
-      lsum = sum2(E{}, pw[ks][3], sum2(E{}, pw[ks][2], sum2(E{}, pw[ks][1], sum2(E{}, pw[ks][0], lsum))));
+      const u32x4 pw = {Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3]),
+                        Mfma<E>::round16x2(pf[4], pf[5]), Mfma<E>::round16x2(pf[6], pf[7])};
+      lsum = sum2(E{}, pw[3], sum2(E{}, pw[2], sum2(E{}, pw[1], sum2(E{}, pw[0], lsum))));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const i16x4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + (vb[2 * ks] ^ (64u * dt))));
+        const i16x4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + (vb[2 * ks + 1] ^ (64u * dt))));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
+        o[dt] = mfma32<E>(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pw, o[dt]);
+      }
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32<E>(vop[ks][dt], pw[ks], o[dt]);
   };
-
   auto runs = [&](int st) __attribute__((always_inline)) {
     return mine && st * kDmaKeys < kend && (!WIN || (st + 1) * kDmaKeys > kbeg);
   };
-  // The ring: step st lives in stage (st - s0) % 4, loaded three steps
-  // ahead; iteration st forms the scores of st + 1 and finishes st.  Block
-  // ids run four steps ahead of the compute (ids of st .. st + 3 held, those
-  // of st + 4 loaded during iteration st).
+
+  // Ring of three stages, loads two steps ahead, one barrier per step: at
+  // the top of step st a wave waits for its own loads of st (those of st + 1
+  // may be in flight); the barrier makes every wave's visible and frees the
+  // stage of st - 1, which the loads of st + 2 fill.
   const int s0 = st_begin;
-  Ids id0 = ids_of(s0), id1 = ids_of(s0 + 1), id2 = ids_of(s0 + 2), raw3 = raw_ids(s0 + 3);
+  Ids id0 = checked(raw_ids(s0)), id1 = checked(raw_ids(s0 + 1));
+  Ids raw2 = raw_ids(s0 + 2);
   issue(s0, s_st0, id0);
   if (s0 + 1 < nsteps) issue(s0 + 1, s_st1, id1);
-  if (s0 + 2 < nsteps) issue(s0 + 2, s_st2, id2);
-  if (s0 + 2 < nsteps)
-    __builtin_amdgcn_s_waitcnt(0x0070 | (4 * kDmaPieces));
-  else if (s0 + 1 < nsteps)
-    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));
-  else
-    __builtin_amdgcn_s_waitcnt(0x0070);
-  __builtin_amdgcn_s_barrier();
-  f32x16 scur = {};
-  if (runs(s0) && (id0.b0 >= 0 || id0.b1 >= 0)) scur = qk(s_st0);
-  auto step = [&](int st, const char* cur, const char* next, char* fill)
-      __attribute__((always_inline)) {
-    if (st + 2 < nsteps)
-      __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));  // own loads of st + 1 landed
+  const int fast_end = WIN ? s0 : min(nsteps - 3, mine ? (unmasked + 1) / kDmaKeys : s0);
+  auto step = [&](int st, const char* cur, char* fill, bool fast) __attribute__((always_inline)) {
+    if (fast || st + 1 < nsteps)
+      __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));  // own loads of st landed
     else
       __builtin_amdgcn_s_waitcnt(0x0070);
     __builtin_amdgcn_s_barrier();
-    const Ids id3 = checked(raw3);  // loaded during the previous step
-    if (st + 3 < nsteps) issue(st + 3, fill, id3);
-    raw3 = raw_ids(st + 4);
-    // The next step's scores are formed whether or not this wave needs them
-    // (past its rows' keys, or past the walk, they are dropped unread), so
-    // the products share one block with this step's weights.
-    f32x16 snext;
-    if (runs(st) && (id0.b0 >= 0 || id0.b1 >= 0))
-      softmax_pv(st, scur, cur, id0.b0 >= 0, id0.b1 >= 0, next, snext, true);
-    else
-      snext = qk(next);
-    scur = snext;
+    const Ids id2 = checked(raw2);
+    if (fast || st + 2 < nsteps) issue(st + 2, fill, id2);
+    raw2 = raw_ids(st + 3);
+    if (fast)
+      compute(st, cur, true, true, false);
+    else if (runs(st) && (id0.b0 >= 0 || id0.b1 >= 0))
+      compute(st, cur, id0.b0 >= 0, id0.b1 >= 0, true);
     id0 = id1;
     id1 = id2;
-    id2 = id3;
-  };
-  // Steady state: groups of four steps whose keys all lie inside this
-  // wave's rows' ranges, at least five steps before the end of the walk: no
-  // masks and no bounds checks.  A table entry outside the pool there loads
-  // zeros (an empty descriptor) instead of being masked: the output of that
-  // sequence is then unspecified, as for any bad entry, and the status scan
-  // after the walk reports it.
-  const int fast_end = WIN ? s0 : min(nsteps - 5, mine ? (unmasked + 1) / kDmaKeys : s0);
-  const int groups = max(fast_end - s0, 0) >> 2;
-  auto fast_step = [&](int st, const char* cur, const char* next, char* fill)
-      __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));  // own loads of st + 1 landed
-    __builtin_amdgcn_s_barrier();
-    const Ids id3 = checked(raw3);
-    issue(st + 3, fill, id3);
-    {
-      const int t = 2 * (st + 4);
-      raw3 = Ids{scalar_load(table + ((t * kTile) >> a.log2_bs)),
-                 scalar_load(table + (((t + 1) * kTile) >> a.log2_bs))};
-    }
-    f32x16 snext;
-    softmax_pv(st, scur, cur, true, true, next, snext, false);
-    scur = snext;
-    id0 = id1;
-    id1 = id2;
-    id2 = id3;
   };
   int st = s0;
-  for (int gi = 0; gi < groups; ++gi, st += 4) {
-    fast_step(st, s_st0, s_st1, s_st3);
-    fast_step(st + 1, s_st1, s_st2, s_st0);
-    fast_step(st + 2, s_st2, s_st3, s_st1);
-    fast_step(st + 3, s_st3, s_st0, s_st2);
+  for (; st + 3 <= fast_end; st += 3) {
+    step(st, s_st0, s_st2, true);
+    step(st + 1, s_st1, s_st0, true);
+    step(st + 2, s_st2, s_st1, true);
   }
-  for (; st < nsteps; st += 4) {
-    step(st, s_st0, s_st1, s_st3);
+  for (; st < nsteps; st += 3) {
+    step(st, s_st0, s_st2, false);
     if (st + 1 >= nsteps) break;
-    step(st + 1, s_st1, s_st2, s_st0);
+    step(st + 1, s_st1, s_st0, false);
     if (st + 2 >= nsteps) break;
-    step(st + 2, s_st2, s_st3, s_st1);
-    if (st + 3 >= nsteps) break;
-    step(st + 3, s_st3, s_st0, s_st2);
+    step(st + 2, s_st2, s_st1, false);
   }
 
-  // Normalise and store: lane (c32, h) holds O[column c32][32 dt + 8 j + 4 h + r]
-  // = o[dt][4 j + r].
   const float total = lsum + shfl_xor(lsum, 32);
   if (row >= 0) {
     const float inv = live && total > 0.f ? a.v_scale / total : 0.f;
