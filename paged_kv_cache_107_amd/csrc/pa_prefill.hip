@@ -53,6 +53,7 @@ constexpr float kMFloor = -1.0e30f;         // initial running maximum
 constexpr int kLptSeqs = 4096;              // batches up to this size run longest first
 constexpr int kLenClassShift = 9;           // length classes of 512 positions
 constexpr int kClasses = 4 * 64;            // classes counted (longer ones share the top class)
+constexpr int kPickRanges = 1024;           // batches up to this size keep query ranges and lengths in LDS
 
 // Score maxima: the IEEE maximum, which gfx950 does as v_maximum3_f32 on the
 // MFMA results directly (fmaxf first quiets each operand with an extra
@@ -92,11 +93,14 @@ __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int i) {
 // The item (sequence i, query-block group zq) of workgroup item index k (Z
 // groups per sequence): longest sequences first (length classes counted in
 // LDS), a sequence's groups back to back within a class; batches above
-// kLptSeqs in batch order.
+// kLptSeqs in batch order.  Given s_qs and s_ctx, batches of up to
+// kPickRanges sequences also leave every query range (s_qs[0 .. B]) and
+// clamped length (s_ctx) there, read in the same pass as the lengths.
 // Every thread of the workgroup calls it (it has barriers).
 template <int THREADS>
 __device__ void pick_item_in(const PrefillArgs& a, int k, int Z, int& i, int& zq,
-                             uint8_t* s_cls, int* s_cnt, int* s_pick) {
+                             uint8_t* s_cls, int* s_cnt, int* s_pick, int* s_qs = nullptr,
+                             int* s_ctx = nullptr) {
   const int B = a.num_seqs;
   if (B <= kLptSeqs) {
     // Classes are counted in LDS; class C holds ranks [start(C), start(C) +
@@ -107,10 +111,21 @@ __device__ void pick_item_in(const PrefillArgs& a, int k, int Z, int& i, int& zq
     const int t = threadIdx.x;
     for (int c = t; c < kClasses; c += THREADS) s_cnt[c] = 0;
     __syncthreads();
+    const bool keep = s_qs != nullptr && B <= kPickRanges;
     for (int u = t; u < B; u += THREADS) {
-      const int c = min(max(clamp_ctx(a, u), 0) >> kLenClassShift, kClasses - 1);
+      // all three loads in flight together
+      const int raw = a.context_lens[u];
+      const int qsu = keep ? a.query_start[u] : 0;
+      const int qsb = keep && u == B - 1 ? a.query_start[B] : 0;
+      const int cu = min(min(raw, a.max_ctx), a.max_blocks << a.log2_bs);
+      const int c = min(max(cu, 0) >> kLenClassShift, kClasses - 1);
       s_cls[u] = (uint8_t)c;
       atomicAdd(&s_cnt[c], 1);
+      if (keep) {
+        s_ctx[u] = cu;
+        s_qs[u] = qsu;
+        if (u == B - 1) s_qs[B] = qsb;
+      }
     }
     __syncthreads();
     // Wave 0: lane l holds the counts of classes 255 - 4l .. 252 - 4l (the
@@ -143,7 +158,7 @@ __device__ void pick_item_in(const PrefillArgs& a, int k, int Z, int& i, int& zq
       }
     }
     __syncthreads();
-    const int cls = s_pick[0], first = s_pick[1], cnt = s_cnt[cls];
+    const int cls = s_pick[0], first = s_pick[1];
     const int off = k - first * Z;
     int j = off / Z;  // the j-th sequence of the class, in batch order
     zq = off - j * Z;
@@ -531,25 +546,34 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
 // state of its column (shared with its partner lane ^ 32) with the lazy
 // rescale of the decode kernel.
 //
-// LDS: a ring of three stages of [K 32 x 128 | V 32 x 128] 16-bit rows; a
-// row's 16 chunks of 16 bytes are stored in the order chunk ^ swz(row), so
-// the K operand reads (16 rows, one chunk) and the transposed V reads (4
-// rows, two chunks) spread over the banks.  A workgroup's four waves load
-// one step (16 KiB, four 1 KiB loads per wave) two steps ahead, with one
-// barrier per step.  The operand reads are plain LDS loads of distinct stage
-// arrays, so the compiler waits only for loads into the stage it reads.
+// LDS: a ring of three stages of [K 32 x 128 | V 32 x 128] 16-bit rows.
+// Every operand read is one of two per-lane base addresses plus an
+// immediate, with no bank conflicts, and every 1 KiB load is four whole
+// rows of one tile (contiguous in the pool).  A load fills 64 slots of 16
+// bytes; inside such a 4-row piece a row's 16-byte chunk c sits at slot
+// 4 (4 (c / 4) + r) + ((c % 4) ^ tau(r)): each row's 64-byte chunk groups
+// stay contiguous (one per lane quad), and tau flips one chunk bit by row
+// bit 1.  V pieces are packed; the four K pieces of a tile start at slots 0,
+// 136, 66 and 202 (0, 8, 2 and 10 modulo 16), so the 16 rows of a K operand
+// read, which share a chunk, land on 16 distinct bank groups (8 for each
+// half of the lanes, should the LDS serve 128 bytes per cycle), as do the 4
+// rows x 4 chunks of a transposed V read.  A workgroup's four waves load one
+// step (four 1 KiB loads per wave) two steps ahead, with one barrier per
+// step.  The operand reads are plain LDS loads of distinct stage arrays, so
+// the compiler waits only for loads into the stage it reads.
 //
-// Three workgroups share a CU (three waves per SIMD: 48 KiB of LDS and at
+// Three workgroups share a CU (three waves per SIMD: 49.5 KiB of LDS and at
 // most 170 VGPRs each; the item choice's LDS scratch borrows the third
 // stage): a wave's step is a chain of dependent phases (barrier, loads,
 // scores, maxima, exponentials, P.V), so a third wave per SIMD gives more
 // than overlapping the phases inside one wave, which needs the registers of
-// a second score tile.  The operand read offsets are derived per step from
-// five bases (XORs with immediates) rather than held in 24 registers.  The
-// block ids of a step are loaded by scalar loads one step before their
-// first use.  Groups of three steps that need no mask (every key inside the
-// wave's rows' ranges, three or more steps before the end of the walk) run a
-// lean step without masks or bounds checks.
+// a second score tile.  The block ids of a step are loaded by scalar loads
+// one step before their first use, issued after the step's last LDS wait
+// (scalar and LDS loads share a counter, and an outstanding scalar load
+// makes every LDS wait a full one).  Groups of three steps that need no
+// mask (every key inside the wave's rows' ranges, three or more steps
+// before the end of the walk) run a lean step without masks or bounds
+// checks.
 constexpr int kDmaWaves = 4;
 constexpr int kDmaPieces = 8 / kDmaWaves;  // 1 KiB pieces of K (and of V) a wave loads per step
 constexpr int kDmaThreads = kDmaWaves * kWave;
@@ -557,22 +581,24 @@ constexpr int kDmaRows = 32;                      // query rows per wave
 constexpr int kDmaKeys = 32;                      // keys per step
 constexpr int kRowBytes128 = 128 * 2;             // one 16-bit K or V row
 constexpr int kDmaRegion = kDmaKeys * kRowBytes128;  // K or V of one step: 8 KiB
+// K region: two 16-row tiles of 272 16-byte slots (a tile's four pieces at
+// slots 0, 136, 66 and 202); V region: eight packed 1 KiB pieces
+constexpr int kKTileSlots = 272;
+constexpr int kKRegion = 2 * kKTileSlots * 16;      // 8704 bytes
+constexpr int kStage = kKRegion + kDmaRegion;       // 16896 bytes
+__device__ __forceinline__ int k_piece_slot(int q) { return (q & 1) * 136 + (q >> 1) * 66; }
+// slot of (row r, chunk c) inside a 4-row piece
+__device__ __forceinline__ int piece_slot(int r, int c, int tau) {
+  return 4 * (4 * (c >> 2) + r) + ((c & 3) ^ tau);
+}
+__device__ __forceinline__ int tau_k(int r) { return (r >> 1) & 1; }
+__device__ __forceinline__ int tau_v(int r) { return 2 * ((r >> 1) & 1); }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4v lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
-
-// A linear (XOR) map of the row's low four bits, chosen so that both read
-// patterns touch distinct banks whether the LDS serves 128 or 256 bytes per
-// cycle: the K operand reads (16 rows, one chunk) and the transposed V reads
-// (4 consecutive rows, 2 or 4 consecutive chunks).
-__device__ __forceinline__ int dma_swz(int r) {
-  return ((r & 1) * 10) ^ ((r & 2) << 1) ^ ((r & 4) >> 1) ^ ((r & 8) >> 3);
-}
-// byte offset of (row r, 16-byte chunk c) in a 32-row region
-__device__ __forceinline__ int dma_pos(int r, int c) { return (r * 16 + (c ^ dma_swz(r))) * 16; }
 
 template <class E>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
@@ -591,20 +617,38 @@ template <class E, bool WIN>
 __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))) void prefill_dma(PrefillArgs a) {
   constexpr int D = 128;
   using S = typename E::storage;
-  __shared__ __attribute__((aligned(1024))) char s_st0[2 * kDmaRegion];
-  __shared__ __attribute__((aligned(1024))) char s_st1[2 * kDmaRegion];
-  __shared__ __attribute__((aligned(1024))) char s_st2[2 * kDmaRegion];
+  __shared__ __attribute__((aligned(256))) char s_st0[kStage];
+  __shared__ __attribute__((aligned(256))) char s_st1[kStage];
+  __shared__ __attribute__((aligned(256))) char s_st2[kStage];
   const int g = blockIdx.x;
   const int Z = gridDim.y;
   const int k = (int)blockIdx.y + Z * (int)blockIdx.z;
   int i, zq;
   // the item choice's scratch lives in stage 2, which no load fills before
   // the prologue's barrier
+  int* const s_qs = reinterpret_cast<int*>(s_st2 + kLptSeqs + 4 * kClasses + 16);
+  int* const s_ctx = s_qs + kPickRanges + 1;
   pick_item_in<kDmaThreads>(a, k, Z, i, zq, reinterpret_cast<uint8_t*>(s_st2),
                             reinterpret_cast<int*>(s_st2 + kLptSeqs),
-                            reinterpret_cast<int*>(s_st2 + kLptSeqs + 4 * kClasses));
+                            reinterpret_cast<int*>(s_st2 + kLptSeqs + 4 * kClasses), s_qs, s_ctx);
   const int G = a.group, QT = kDmaRows / G;  // chunk tokens per wave
-  const int qa = a.query_start[i], qb = a.query_start[i + 1];
+  // the item's query range and length: from the item choice's LDS copy when
+  // it made one (small batches), else from memory
+  i = __builtin_amdgcn_readfirstlane(i);  // the same in every lane
+  zq = __builtin_amdgcn_readfirstlane(zq);
+  int qa, qb, ctx;
+  if (a.num_seqs <= kPickRanges) {
+    qa = s_qs[i];
+    qb = s_qs[i + 1];
+    ctx = s_ctx[i];
+  } else {
+    qa = a.query_start[i];
+    qb = a.query_start[i + 1];
+    ctx = clamp_ctx(a, i);
+  }
+  qa = __builtin_amdgcn_readfirstlane(qa);
+  qb = __builtin_amdgcn_readfirstlane(qb);
+  ctx = __builtin_amdgcn_readfirstlane(ctx);
   if (qa < 0 || qb > a.num_tokens || qb <= qa) return;  // the whole workgroup
   const int n = qb - qa, nq = min(n, a.max_query);
   const int nqb = ceil_div(nq, QT);
@@ -613,7 +657,6 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
   const int w = wave_id();
   const int lane = threadIdx.x % kWave;
   const int c32 = lane & 31, h = lane >> 5;
-  const int ctx = clamp_ctx(a, i);
   const int kend_wg = ctx - n + min(top * QT + QT, nq);  // the walk: keys [0, kend_wg)
   const int blk = top - w;                               // this wave's query block
   const int tok0 = blk * QT, ntok = blk >= 0 ? min(QT, nq - tok0) : 0;
@@ -663,11 +706,12 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
   struct Ids {
     int b0, b1;
   };
-  auto raw_ids = [&](int st) __attribute__((always_inline)) -> Ids {
+  // `inside`: both tiles lie inside the walk (every fast step)
+  auto raw_ids = [&](int st, bool inside) __attribute__((always_inline)) -> Ids {
     const int t = 2 * st;
     int b0 = -1, b1 = -1;
-    if (t < ntiles) b0 = scalar_load(table + ((t * kTile) >> a.log2_bs));
-    if (t + 1 < ntiles) b1 = scalar_load(table + (((t + 1) * kTile) >> a.log2_bs));
+    if (inside || t < ntiles) b0 = scalar_load(table + ((t * kTile) >> a.log2_bs));
+    if (inside || t + 1 < ntiles) b1 = scalar_load(table + (((t + 1) * kTile) >> a.log2_bs));
     return Ids{b0, b1};
   };
   auto checked = [&](const Ids& r) __attribute__((always_inline)) -> Ids {
@@ -676,41 +720,51 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
   };
 
   const int tw = (kDmaPieces * w) >> 2;
-  uint32_t dma_off[kDmaPieces];
+  // lane j of a piece load fills slot j: row (j / 4) % 4 of the piece, a
+  // chunk of the row's 64-byte group j / 16
+  uint32_t koff_g[kDmaPieces], voff_g[kDmaPieces];
+  {
+    const int pr = (lane >> 2) & 3, grp = lane >> 4, i4 = lane & 3;
 #pragma unroll
-  for (int x = 0; x < kDmaPieces; ++x) {
-    const int r = 4 * (kDmaPieces * w + x) + (lane >> 4);
-    dma_off[x] = (uint32_t)((r & 15) * kRowBytes128 + (((lane & 15) ^ dma_swz(r)) * 16));
+    for (int x = 0; x < kDmaPieces; ++x) {
+      const int q = (kDmaPieces * w + x) & 3;
+      const int row = 4 * q + pr;
+      koff_g[x] = (uint32_t)(row * kRowBytes128 + 16 * (4 * grp + (i4 ^ tau_k(pr))));
+      voff_g[x] = (uint32_t)(row * kRowBytes128 + 16 * (4 * grp + (i4 ^ tau_v(pr))));
+    }
   }
   const int kr = 16 * (c32 >> 4) + 8 * ((c32 >> 2) & 1) + 4 * ((c32 >> 3) & 1) + (c32 & 3);
-  const uint32_t koff0 = (uint32_t)dma_pos(kr, h);
-  uint32_t voff0[4];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int hr = 0; hr < 2; ++hr) {
-      const int R = 16 * ks + 8 * h + 4 * hr + ((lane & 15) >> 2);
-      const int el = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      voff0[2 * ks + hr] = (uint32_t)(kDmaRegion + dma_pos(R, el >> 3) + 2 * (el & 7));
-    }
+  // K operand of k-step s at kb + 256 (s / 2) + 32 (s % 2)
+  const uint32_t kb = (uint32_t)(16 * ((kr >> 4) * kKTileSlots + k_piece_slot((kr >> 2) & 3) +
+                                       piece_slot(kr & 3, h, tau_k(kr & 3))));
+  // V^T operand (k-step ks, row half hr, d-tile dt) at vb + 4096 ks + 1024 hr + 256 dt
+  const uint32_t vb = (uint32_t)(kKRegion + 2048 * h +
+                                 16 * piece_slot((lane & 15) >> 2, 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1),
+                                                 tau_v((lane & 15) >> 2)) +
+                                 8 * (lane & 1));
 
-  auto issue = [&](int st, char* buf, const Ids& id) __attribute__((always_inline)) {
+  // `full`: the tile lies wholly below the context length (every fast step)
+  auto issue = [&](int st, char* buf, const Ids& id, bool full) __attribute__((always_inline)) {
     const int b = tw ? id.b1 : id.b0;
     const int t = 2 * st + tw;
     const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
     const rsrc_t ks = make_rsrc(kbase0 + off, b >= 0 ? 16u * kRowBytes128 : 0u);
-    const uint32_t vbytes = b >= 0 ? (uint32_t)max(min(kTile, ctx - t * kTile), 0) * kRowBytes128 : 0u;
+    const uint32_t vbytes =
+        b < 0 ? 0u
+              : full ? 16u * kRowBytes128
+                     : (uint32_t)max(min(kTile, ctx - t * kTile), 0) * kRowBytes128;
     const rsrc_t vs = make_rsrc(vbase0 + off, vbytes);
 #pragma unroll
     for (int x = 0; x < kDmaPieces; ++x) {
+      const int pc = kDmaPieces * w + x;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ks, (lds_void*)(buf + (kDmaPieces * w + x) * 1024), 16, dma_off[x], 0, 0, 0);
+          ks, (lds_void*)(buf + 16 * (tw * kKTileSlots + k_piece_slot(pc & 3))), 16, koff_g[x], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vs, (lds_void*)(buf + kDmaRegion + (kDmaPieces * w + x) * 1024), 16, dma_off[x], 0, 0, 0);
+          vs, (lds_void*)(buf + kKRegion + pc * 1024), 16, voff_g[x], 0, 0, 0);
     }
   };
 
-  float m = kMFloor, lsum = 0.f;
+  float m = kMFloor, lsum = 0.f, thr = (kMFloor + kRescaleSlack) * inv_c;
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -718,19 +772,17 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
 
   typedef const __attribute__((address_space(3))) char lds_cchar;
-  // One step from stage `buf`: scores, mask, weights, P.V.  The read
-  // offsets are derived here (XORs with immediates) from bases made opaque,
-  // so they are not held across the loop.
+  // One step from stage `buf`: scores, mask, weights, P.V.  Every operand
+  // read is one of two per-lane bases plus an immediate.
   auto compute = [&](int st, const char* buf, bool oka, bool okb, bool may_mask)
       __attribute__((always_inline)) {
-    uint32_t kb0 = koff0, vb[4] = {voff0[0], voff0[1], voff0[2], voff0[3]};
-    asm volatile("" : "+v"(kb0), "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]));
     f32x16 sacc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const u32x4 kop = *reinterpret_cast<const lds_u32x4*>((lds_cchar*)buf + (kb0 ^ (32u * s)));
+      const u32x4 kop =
+          *reinterpret_cast<const lds_u32x4*>((lds_cchar*)buf + kb + (256u * (s >> 1) + 32u * (s & 1)));
       sacc = mfma32<E>(kop, qv[s], sacc);
     }
     const int k0 = st * kDmaKeys;
@@ -744,10 +796,12 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
         if (key > lim || (WIN && key <= lim - W) || !((v >> 3) ? okb : oka)) sv[v] = neg_inf();
       }
     }
-    float mt = smax(smax(smax(sv[0], sv[1]), smax(sv[2], sv[3])), smax(smax(sv[4], sv[5]), smax(sv[6], sv[7])));
-    mt = smax(mt, smax(smax(smax(sv[8], sv[9]), smax(sv[10], sv[11])),
-                       smax(smax(sv[12], sv[13]), smax(sv[14], sv[15]))));
-    if (__builtin_amdgcn_ballot_w64(mt > (m + kRescaleSlack) * inv_c)) {
+    // maxima as a tree of three-input maxima (eight instructions)
+    const float t0 = smax(smax(sv[0], sv[1]), sv[2]), t1 = smax(smax(sv[3], sv[4]), sv[5]);
+    const float t2 = smax(smax(sv[6], sv[7]), sv[8]), t3 = smax(smax(sv[9], sv[10]), sv[11]);
+    const float t4 = smax(smax(sv[12], sv[13]), sv[14]);
+    const float mt = smax(smax(smax(t0, t1), sv[15]), smax(smax(t2, t3), t4));
+    if (__builtin_amdgcn_ballot_w64(mt > thr)) {
       const float x = smax(mt, shfl_xor(mt, 32));
       const float mn = smax(m, x * c);
       const float alpha = fast_exp2(m - mn);
@@ -755,6 +809,7 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
       m = mn;
+      thr = (m + kRescaleSlack) * inv_c;
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -767,9 +822,9 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const i16x4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + (vb[2 * ks] ^ (64u * dt))));
+            (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + vb + (4096u * ks + 256u * dt)));
         const i16x4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + (vb[2 * ks + 1] ^ (64u * dt))));
+            (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + vb + (4096u * ks + 1024u + 256u * dt)));
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
         o[dt] = mfma32<E>(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pw, o[dt]);
       }
@@ -784,10 +839,10 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
   // may be in flight); the barrier makes every wave's visible and frees the
   // stage of st - 1, which the loads of st + 2 fill.
   const int s0 = st_begin;
-  Ids id0 = checked(raw_ids(s0)), id1 = checked(raw_ids(s0 + 1));
-  Ids raw2 = raw_ids(s0 + 2);
-  issue(s0, s_st0, id0);
-  if (s0 + 1 < nsteps) issue(s0 + 1, s_st1, id1);
+  Ids id0 = checked(raw_ids(s0, false)), id1 = checked(raw_ids(s0 + 1, false));
+  Ids raw2 = raw_ids(s0 + 2, false);
+  issue(s0, s_st0, id0, false);
+  if (s0 + 1 < nsteps) issue(s0 + 1, s_st1, id1, false);
   const int fast_end = WIN ? s0 : min(nsteps - 3, mine ? (unmasked + 1) / kDmaKeys : s0);
   auto step = [&](int st, const char* cur, char* fill, bool fast) __attribute__((always_inline)) {
     if (fast || st + 1 < nsteps)
@@ -796,12 +851,19 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
       __builtin_amdgcn_s_waitcnt(0x0070);
     __builtin_amdgcn_s_barrier();
     const Ids id2 = checked(raw2);
-    if (fast || st + 2 < nsteps) issue(st + 2, fill, id2);
-    raw2 = raw_ids(st + 3);
+    if (fast)
+      issue(st + 2, fill, id2, true);
+    else if (st + 2 < nsteps)
+      issue(st + 2, fill, id2, false);
     if (fast)
       compute(st, cur, true, true, false);
     else if (runs(st) && (id0.b0 >= 0 || id0.b1 >= 0))
       compute(st, cur, id0.b0 >= 0, id0.b1 >= 0, true);
+    // the next ids' scalar loads go out after the step's last LDS wait: the
+    // two kinds share a counter, and an outstanding scalar load would make
+    // every LDS wait a full one
+    __builtin_amdgcn_sched_barrier(0);
+    raw2 = raw_ids(st + 3, fast);
     id0 = id1;
     id1 = id2;
   };
@@ -826,13 +888,10 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t b0 = float_to_bits(E{}, o[dt][4 * j] * inv);
-        const uint32_t b1 = float_to_bits(E{}, o[dt][4 * j + 1] * inv);
-        const uint32_t b2 = float_to_bits(E{}, o[dt][4 * j + 2] * inv);
-        const uint32_t b3 = float_to_bits(E{}, o[dt][4 * j + 3] * inv);
-        *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * j) = uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
-      }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * j) =
+            uint2{Mfma<E>::round16x2(o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv),
+                  Mfma<E>::round16x2(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv)};
   }
   if (a.status != nullptr) {
     const int kfirst =
@@ -883,7 +942,7 @@ int prefill_query_blocks(int max_query_len, int group) {
 pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, int path, hipStream_t st) {
   const bool fp8 = kv == KvType::kFp8;
   // 16-bit pools run the direct-to-LDS kernel unless the register-staged one
-  // is asked for (AUTO: the direct kernel, about 7% faster on the 8B chunked
+  // is asked for (AUTO: the direct kernel, 15-20% faster on the 8B chunked
   // workload); 8-bit pools, whose codes are widened on the way into LDS, run
   // the register-staged kernel
   const bool dma = !fp8 && path != PA_PREFILL_LDS;
