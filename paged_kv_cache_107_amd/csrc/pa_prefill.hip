@@ -706,12 +706,15 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
   struct Ids {
     int b0, b1;
   };
-  // `inside`: both tiles lie inside the walk (every fast step)
+  // `inside`: the step lies inside the walk (every fast step), so its first
+  // tile does; its second may be one past the walk's end (odd tile counts),
+  // whose entry is then the last tile's (the tile is masked or not computed)
   auto raw_ids = [&](int st, bool inside) __attribute__((always_inline)) -> Ids {
     const int t = 2 * st;
     int b0 = -1, b1 = -1;
     if (inside || t < ntiles) b0 = scalar_load(table + ((t * kTile) >> a.log2_bs));
-    if (inside || t + 1 < ntiles) b1 = scalar_load(table + (((t + 1) * kTile) >> a.log2_bs));
+    if (inside || t + 1 < ntiles)
+      b1 = scalar_load(table + ((min(t + 1, ntiles - 1) * kTile) >> a.log2_bs));
     return Ids{b0, b1};
   };
   auto checked = [&](const Ids& r) __attribute__((always_inline)) -> Ids {
