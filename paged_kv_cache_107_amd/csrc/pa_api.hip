@@ -230,6 +230,7 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
     a.ws_o = reinterpret_cast<float*>(ws + kStreamOwnerBytes +
                                       stream_ml_bytes(num_seqs, pool->num_kv_heads, group));
     a.stream_waves = pa::stream_waves();
+    a.xcds = pa::device_xcds();
     if (a.stream_waves <= 0 || a.stream_waves > pa::kStreamMaxWaves) return PA_ERR_HIP;
   } else if (need > 0) {
     a.ws_ml = reinterpret_cast<float2*>(ws);

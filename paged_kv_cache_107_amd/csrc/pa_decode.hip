@@ -395,10 +395,12 @@ __device__ void scan_tiles(const int* ctx, const int* first, int* tb, int n, int
 }
 
 // Split of T flat tiles over the kWaves * nwg waves of nwg workgroups.  The
-// hardware deals workgroups to the XCDs round-robin, so workgroup b runs on
-// XCD b % X (X = min(8, nwg)).  The tiles are cut into X contiguous chunks,
-// chunk x going to the workgroups b = x, x + X, ...; each chunk is split
-// evenly over its waves.  The chunks are equal, or, with weights (X = 8),
+// hardware deals workgroups to the device's XCDs round-robin, so workgroup b
+// runs on XCD b % X (X = min(xcds, nwg); xcds is queried from the device: 8
+// on a whole MI355X, fewer in a partition mode).  The tiles are cut into X
+// contiguous chunks, chunk x going to the workgroups b = x, x + X, ...; each
+// chunk is split evenly over its waves.  The chunks are equal, or, with
+// weights (X = 8),
 // chunk x covers [T cum[x] / 2^16, T cum[x + 1] / 2^16).  Ranks number the
 // waves in flat order: rank r's run is [lo(r), lo(r + 1)).  Any monotone cut
 // keeps the slot rule of the stream kernel.
@@ -413,7 +415,8 @@ struct StreamSplit {
   long long T;
   int nwg;
   const int* cut = nullptr;  // weights: chunk x is [cut[x], cut[x + 1]) (in LDS)
-  __device__ int chunks() const { return min(kXcds, nwg); }
+  int xcds = kXcds;
+  __device__ int chunks() const { return min(min(max(xcds, 1), kXcds), nwg); }
   __device__ int wgs_of(int x) const { return nwg / chunks() + (x < nwg % chunks() ? 1 : 0); }
   __device__ int base(int x) const {  // first rank of chunk x
     return kWaves * (x * (nwg / chunks()) + min(x, nwg % chunks()));
@@ -452,7 +455,8 @@ struct StreamSplit {
   }
   // whether passes of this size are timed and may use weights
   __device__ bool balanced_size() const {
-    return chunks() == kXcds && T >= (long long)kBalanceMinTilesPerWave * kWaves * nwg;
+    return xcds == kXcds && chunks() == kXcds &&
+           T >= (long long)kBalanceMinTilesPerWave * kWaves * nwg;
   }
 };
 
@@ -480,7 +484,7 @@ __device__ const uint32_t* header_words(const StreamBalance* h) {
 // run stays non-empty (so the reduce pass, which sees only dense records
 // under weights, never needs the cut); else s_cut[0] = -1 (the even cut).
 __device__ void partition_cut(const DecodeArgs& a, long long T, int nwg, int* s_cut) {
-  StreamSplit sp{T, nwg};
+  StreamSplit sp{T, nwg, nullptr, a.xcds};
   uint32_t cum[kXcds + 1];
   s_cut[0] = -1;
   if (!a.balance || !sp.balanced_size() || !read_cut(header_words(a.ws_balance), cum)) return;
@@ -603,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   const int Th = uni(s_tb[B]);  // tiles of one kv head's run
   if (threadIdx.x == 0) partition_cut(a, (long long)Th * Hkv, (int)gridDim.x, s_cut);
   __syncthreads();
-  StreamSplit split{(long long)Th * Hkv, (int)gridDim.x};
+  StreamSplit split{(long long)Th * Hkv, (int)gridDim.x, nullptr, a.xcds};
   if (uni(s_cut[0]) >= 0) split.cut = s_cut;
   const int rank = split.rank(blockIdx.x, w);
   // the pass's record for the balance state: each chunk's tiles, and (at
@@ -1149,7 +1153,7 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_stream(DecodeArgs a) {
   const int B = a.num_seqs, G = a.group;
   const int g = pq / B, i = pq - g * B;
   // records of weighted passes are dense; others were cut evenly
-  const StreamSplit split{(long long)rec.z * a.num_kv_heads, a.stream_waves / kWaves};
+  const StreamSplit split{(long long)rec.z * a.num_kv_heads, a.stream_waves / kWaves, nullptr, a.xcds};
   const bool dense = rec.w != 0;
   const size_t base = (size_t)pq + r;
   for (int hh = wave_id(); hh < G; hh += kWaves) {
@@ -1233,6 +1237,19 @@ pa_status launch_reduce(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int device_xcds() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kXcds;
+  int n = cache[dev].load();
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n <= 0) n = kXcds;
+    n = std::min(n, kXcds);
+    cache[dev].store(n);
+  }
+  return n;
+}
 
 int stream_waves() {
   const int cus = device_cus();

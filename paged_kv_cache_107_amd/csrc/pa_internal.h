@@ -46,6 +46,7 @@ struct DecodeArgs {
   int32_t* status;       // caller's status word (kStatusBadBlock is ORed in), or null
   struct StreamBalance* ws_balance;  // stream split: the balance state, else null
   int32_t balance;       // stream split: cut the tile order by the measured rates
+  int32_t xcds;          // stream split: dies (XCCs) the workgroups are dealt over, 1..8
 };
 
 // Balance of the stream split, kept between calls in the first
@@ -91,6 +92,7 @@ bool mfma_supports(int dtype, int head_dim, int group);
 bool valu_supports(int dtype, int head_dim, int group);
 bool stream_supports(int num_seqs, int num_kv_heads, int max_ctx);
 int stream_waves();  // on the current device; 0 if it cannot be queried
+int device_xcds();   // XCCs of the current device, 1..8 (8 if it cannot be queried)
 pa_status launch_decode_partition(const DecodeArgs& a, int dtype, KvType kv, int head_dim,
                                   DecodeKernel k, hipStream_t st);
 pa_status launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, DecodeKernel k,

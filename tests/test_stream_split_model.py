@@ -1,7 +1,8 @@
 """Model check of the stream split's arithmetic (CPU only).
 
 The decode kernel's stream split cuts a flat order of T tiles into one
-chunk per XCD (equal chunks, or chunks sized by the balance state's cut) and
+chunk per XCD (the device's count, at most 8: equal chunks, or, with 8,
+chunks sized by the balance state's cut) and
 each chunk evenly over its waves; a (kv head, sequence) pair cut between
 waves leaves one partial per wave in workspace slot (pair index + wave
 rank), merged by the pair's first wave's rank.  This file restates that
@@ -26,11 +27,11 @@ SHARE_MIN, SHARE_MAX = ONE // 16, 3 * ONE // 16
 
 
 class Split:
-    def __init__(self, T, nwg, cut=None):
-        self.T, self.nwg, self.cut = T, nwg, cut
+    def __init__(self, T, nwg, cut=None, xcds=K_XCDS):
+        self.T, self.nwg, self.cut, self.xcds = T, nwg, cut, xcds
 
     def chunks(self):
-        return min(K_XCDS, self.nwg)
+        return min(self.xcds, K_XCDS, self.nwg)
 
     def wgs_of(self, x):
         c = self.chunks()
@@ -112,15 +113,16 @@ def check_split(sp, pair_tiles):
 
 @settings(max_examples=150, deadline=None)
 @given(nwg=st.integers(1, 64), seed=st.integers(0, 2**31), weighted=st.booleans(),
-       pairs=st.integers(1, 300))
-def test_runs_ranks_and_slots(nwg, seed, weighted, pairs):
+       pairs=st.integers(1, 300), xcds=st.integers(1, K_XCDS))
+def test_runs_ranks_and_slots(nwg, seed, weighted, pairs, xcds):
     rng = np.random.default_rng(seed)
     pair_tiles = rng.integers(0, 40, pairs)
     T = int(pair_tiles.sum())
     if T == 0:
         return
-    cut = cut_of(T, random_shares(rng)) if weighted and nwg >= K_XCDS else None
-    check_split(Split(T, nwg, cut), pair_tiles)
+    # weights only with all eight dies
+    cut = cut_of(T, random_shares(rng)) if weighted and nwg >= K_XCDS and xcds == K_XCDS else None
+    check_split(Split(T, nwg, cut, xcds), pair_tiles)
 
 
 @settings(max_examples=100, deadline=None)
