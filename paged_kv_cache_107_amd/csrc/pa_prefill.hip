@@ -509,11 +509,11 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
     S* dst = out + (size_t)row[q] * D + 32 * g4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      uint32_t b[8];
+      uint32_t b[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = float_to_bits(E{}, o[q][e][r] * inv);
-      *reinterpret_cast<u32x4*>(dst + 8 * r) =
-          u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+      for (int e = 0; e < 4; ++e)
+        b[e] = Mfma<E>::round16x2(o[q][2 * e][r] * inv, o[q][2 * e + 1][r] * inv);
+      *reinterpret_cast<u32x4*>(dst + 8 * r) = u32x4{b[0], b[1], b[2], b[3]};
     }
   }
   // Table entries outside the pool among the blocks some row of the item

@@ -191,6 +191,18 @@ def test_bad_block_ids_inside_a_sequence():
     assert torch.equal(out, g["out"]) and int(status.item()) == 0
 
 
+@pytest.mark.parametrize("n", [1500])
+def test_longest_first_batches_without_the_range_copy(n):
+    """Longest-first order for a batch too large for the item choice's LDS
+    copy of query ranges and lengths (more than 1024 sequences): the item's
+    range and length come from memory."""
+    rng = np.random.default_rng(11)
+    chunks = [int(x) for x in rng.integers(1, 41, n)]
+    prefixes = [int(x) for x in rng.integers(0, 600, n)]
+    lens = [c + p for c, p in zip(chunks, prefixes)]
+    check(W.custom(341, 8, 2, 128, "bf16", 16, lens, chunk_lens=chunks))
+
+
 def test_batches_above_the_longest_first_limit():
     """More sequences than the longest-first order counts (4096): the items
     run in batch order, each sequence's query-block groups back to back."""
