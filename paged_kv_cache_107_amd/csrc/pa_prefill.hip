@@ -10,17 +10,17 @@
 // sequence and to itself (the autoregressive rule of the same §2.1).  K/V
 // rows are found through the block table as in decode.
 //
-// The step: the G query heads of a kv head and 32 / G consecutive chunk
-// tokens make a wave's 32 query rows, taken as two groups of 16; each group
-// is the 16 columns of the decode kernel's tile products (S^T = K . Q^T with
-// v_mfma_f32_16x16x32), so one K/V tile feeds both groups' products.  Keys
-// are walked 32 at a time (two 16-key tiles); with 32 keys per step the P.V
-// product also runs on the double-rate v_mfma_f32_16x16x32 (O^T += V^T .
-// P^T).  Steps at and past the rows' first position are masked per element.
-// Each lane keeps the softmax state of its column in each group, with the
-// decode kernel's lazy rescale; the running maximum starts at a finite
-// floor, so a step has no branch between the rescale test and the P.V
-// product.
+// Two kernels share the grid, the item order and the walk below:
+// prefill_dma (16-bit pools, the default: tiles loaded straight into LDS,
+// 32x32x16 products) and prefill_mfma_lds (8-bit pools, and 16-bit ones on
+// request: tiles staged through registers, 16x16x32 products); each is
+// described above its code.  In both, the G query heads of a kv head and
+// 32 / G consecutive chunk tokens make a wave's 32 query rows, keys are
+// walked 32 at a time (two 16-key tiles), steps at and past the rows' first
+// position are masked per element, and each lane keeps the softmax state of
+// its query column with the decode kernel's lazy rescale (the running
+// maximum starts at a finite floor, so a step has no branch between the
+// rescale test and the P.V product).
 //
 // With a sliding window of W positions a row at position p attends only
 // positions p - W + 1 .. p.  8-bit pools are widened to the 16-bit operand
@@ -191,7 +191,12 @@ __device__ void pick_item(const PrefillArgs& a, int k, int Z, int& i, int& zq) {
   pick_item_in<THREADS>(a, k, Z, i, zq, s_cls, s_cnt, s_pick);
 }
 
-// Kernel: the K/V tiles of a step are shared through LDS.  Four
+// Register-staged kernel (prefill_mfma_lds).  A wave's 32 query rows are
+// taken as two groups of 16; each group is the 16 columns of the decode
+// kernel's tile products (S^T = K . Q^T with v_mfma_f32_16x16x32), so one K/V
+// tile feeds both groups' products, and with 32 keys per step the P.V
+// product also runs on the double-rate v_mfma_f32_16x16x32 (O^T += V^T .
+// P^T).  The K/V tiles of a step are shared through LDS.  Four
 // waves of 32 query rows each (two 16-column groups) take the 128 / G chunk
 // tokens of one item, and each 32-key step's two K/V tiles are read from
 // memory once per workgroup into a ring of three LDS buffers, one barrier per
