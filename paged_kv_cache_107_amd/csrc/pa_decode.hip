@@ -493,7 +493,7 @@ __device__ void partition_cut(const DecodeArgs& a, long long T, int nwg, int* s_
   if (!sp.dense()) s_cut[0] = -1;
 }
 
-// The reduce pass's first workgroup (every thread): turn the last partition
+// The reduce pass's last workgroup (every thread): turn the last partition
 // pass's record into the next cut, or initialise an invalid header with the
 // even cut.  One round of loads: the header's first 24 words into LDS and
 // each thread's wave slots, in parallel; each chunk's time is the largest
@@ -1146,7 +1146,12 @@ template <class E>
 __global__ __launch_bounds__(kThreads) void decode_reduce_stream(DecodeArgs a) {
   constexpr int D = 128;
   const int r = blockIdx.x;
-  if (r == 0 && a.ws_balance != nullptr) update_balance(a.ws_balance, a.stream_waves / kWaves);
+  // one workgroup past the records updates the balance state, beside the
+  // merges rather than ahead of one of them
+  if (r == a.stream_waves) {
+    if (a.ws_balance != nullptr) update_balance(a.ws_balance, a.stream_waves / kWaves);
+    return;
+  }
   const int4 rec = reinterpret_cast<const int4*>(a.ws_owner)[r];
   const int pq = rec.x;
   if (pq < 0) return;
@@ -1225,7 +1230,9 @@ pa_status launch_mfma_stream(const DecodeArgs& a, hipStream_t st) {
 
 template <class E>
 pa_status launch_reduce_stream(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_reduce_stream<E>), dim3(a.stream_waves), dim3(kThreads), 0, st, a);
+  // one workgroup per merge record, plus one for the balance update
+  hipLaunchKernelGGL((decode_reduce_stream<E>), dim3(a.stream_waves + (a.ws_balance != nullptr ? 1 : 0)),
+                     dim3(kThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -55,7 +55,7 @@ struct DecodeArgs {
 // T cum[x + 1] / 2^16).  A partition pass records each chunk's tile count,
 // and each wave the time it took (100 MHz ticks) in its own slot of
 // wave_dur (plain stores: no atomics on shared words); the next reduce
-// pass's first workgroup takes each chunk's slowest wave and turns the
+// pass's extra workgroup takes each chunk's slowest wave and turns the
 // record into the cut of the next call, with each chunk's share moved
 // halfway towards its measured rate (left alone when the chunks ended within
 // 1/64 of each other).  A workspace whose magic does not match starts from
