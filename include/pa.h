@@ -241,7 +241,7 @@ int32_t pa_set_decode_path(int32_t path);
  * GPU's dies).  The stream split cuts the batch's tiles into one chunk per
  * XCD (each XCD with its own L2; the count is queried from the device, 8 on
  * a whole MI355X); the dies do not run equally fast, so with balancing on
- * (1, the default; used with 8 XCDs) each partition pass of at least 16 tiles per
+ * (1, the default; used with 8 XCDs) each partition pass of at least 80 tiles per
  * wave records how long each chunk's slowest wave took, and the next reduce
  * pass moves each chunk's share of the next call's tiles halfway towards its
  * measured rate (shares kept within 1/16 .. 3/16).  The state lives in the

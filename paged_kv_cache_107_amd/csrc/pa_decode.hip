@@ -409,7 +409,10 @@ constexpr uint32_t kBalanceOne = 1u << 16;
 // a chunk's share of the tiles under weights: 1/16 .. 3/16
 constexpr uint32_t kShareMin = kBalanceOne / 16, kShareMax = 3 * kBalanceOne / 16;
 // weights apply (and passes are timed) from this many tiles per wave on
-constexpr int kBalanceMinTilesPerWave = 16;
+// (passes of about 80 us): below it the cut's prologue load and the timing
+// record cost more than the balance returns (a 71-tile pass measured 57.5
+// against 55.8 us even; a 96-tile one 146 against 149-151 us)
+constexpr int kBalanceMinTilesPerWave = 80;
 
 struct StreamSplit {
   long long T;

@@ -55,7 +55,7 @@ def check_header(h):
 
 @pytest.fixture(scope="module")
 def case():
-    d = W.draw("8b_gqa", batch=48)      # > 16 tiles per wave: the balanced size
+    d = W.draw("8b_gqa", batch=128)     # > 80 tiles per wave: the balanced size
     kv = KV(d)
     o = run_oracle(d, kv)
     g = run_gpu(d, kv)

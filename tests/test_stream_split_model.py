@@ -13,7 +13,7 @@ properties the kernels rely on:
 * rank_of(t) is the rank whose run holds t;
 * dense() holds exactly when every run is non-empty;
 * slots never collide: the slots of different pairs are disjoint;
-* a weighted cut at the sizes where weights apply (16 tiles per wave) is
+* a weighted cut at the sizes where weights apply (80 tiles per wave) is
   always dense, so the reduce pass never needs the cut;
 * the balance update keeps every share within [1/16, 3/16] and the cut
   summing to 2^16, moves shares towards the measured rates, and leaves the
@@ -129,7 +129,7 @@ def test_runs_ranks_and_slots(nwg, seed, weighted, pairs, xcds):
 @given(nwg=st.integers(8, 256), extra=st.integers(0, 10**6), seed=st.integers(0, 2**31))
 def test_weighted_cut_is_dense_where_weights_apply(nwg, extra, seed):
     rng = np.random.default_rng(seed)
-    T = 16 * K_WAVES * nwg + extra                      # balanced_size()
+    T = 80 * K_WAVES * nwg + extra                      # balanced_size()
     for shares in (random_shares(rng), np.array([SHARE_MIN] * 4 + [SHARE_MAX] * 4)):
         assert Split(T, nwg, cut_of(T, shares)).dense()
 
