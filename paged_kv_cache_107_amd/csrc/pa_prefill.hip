@@ -585,12 +585,12 @@ constexpr int kDmaThreads = kDmaWaves * kWave;
 constexpr int kDmaRows = 32;                      // query rows per wave
 constexpr int kDmaKeys = 32;                      // keys per step
 constexpr int kRowBytes128 = 128 * 2;             // one 16-bit K or V row
-constexpr int kDmaRegion = kDmaKeys * kRowBytes128;  // K or V of one step: 8 KiB
+constexpr int kVRegion = kDmaKeys * kRowBytes128;    // V of one step: 8 KiB
 // K region: two 16-row tiles of 272 16-byte slots (a tile's four pieces at
 // slots 0, 136, 66 and 202); V region: eight packed 1 KiB pieces
 constexpr int kKTileSlots = 272;
 constexpr int kKRegion = 2 * kKTileSlots * 16;      // 8704 bytes
-constexpr int kStage = kKRegion + kDmaRegion;       // 16896 bytes
+constexpr int kStage = kKRegion + kVRegion;         // 16896 bytes
 __device__ __forceinline__ int k_piece_slot(int q) { return (q & 1) * 136 + (q >> 1) * 66; }
 // slot of (row r, chunk c) inside a 4-row piece
 __device__ __forceinline__ int piece_slot(int r, int c, int tau) {
