@@ -576,9 +576,10 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(2))
 // one step before their first use, issued after the step's last LDS wait
 // (scalar and LDS loads share a counter, and an outstanding scalar load
 // makes every LDS wait a full one).  Groups of three steps that need no
-// mask (every key inside the wave's rows' ranges, three or more steps
-// before the end of the walk) run a lean step without masks or bounds
-// checks.
+// mask (every key inside the wave's rows' ranges -- below the first row
+// and, with a window, at or above the last row's window start -- and three
+// or more steps before the end of the walk) run a lean step without masks
+// or bounds checks.
 constexpr int kDmaWaves = 4;
 constexpr int kDmaPieces = 8 / kDmaWaves;  // 1 KiB pieces of K (and of V) a wave loads per step
 constexpr int kDmaThreads = kDmaWaves * kWave;
@@ -851,7 +852,16 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
   Ids raw2 = raw_ids(s0 + 2, false);
   issue(s0, s_st0, id0, false);
   if (s0 + 1 < nsteps) issue(s0 + 1, s_st1, id1, false);
-  const int fast_end = WIN ? s0 : min(nsteps - 3, mine ? (unmasked + 1) / kDmaKeys : s0);
+  // lean steps: every key below the wave's first row (no causal mask) and,
+  // with a window, at or above its last row's window start (no window mask)
+  int fast_end = min(nsteps - 3, mine ? (unmasked + 1) / kDmaKeys : s0);
+  int fast_begin = s0;
+  if (WIN) {
+    // the lean segment starts in step with the stage order (groups of three)
+    const int first = max(ceil_div(max(kend - W, 0), kDmaKeys), s0);
+    fast_begin = s0 + 3 * ceil_div(first - s0, 3);
+    if (fast_begin + 3 > fast_end) fast_begin = fast_end = s0;  // no lean group
+  }
   auto step = [&](int st, const char* cur, char* fill, bool fast) __attribute__((always_inline)) {
     if (fast || st + 1 < nsteps)
       __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kDmaPieces));  // own loads of st landed
@@ -876,6 +886,11 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
     id1 = id2;
   };
   int st = s0;
+  for (; st < fast_begin; st += 3) {  // window: the steps below the lean ones
+    step(st, s_st0, s_st2, false);
+    step(st + 1, s_st1, s_st0, false);
+    step(st + 2, s_st2, s_st1, false);
+  }
   for (; st + 3 <= fast_end; st += 3) {
     step(st, s_st0, s_st2, true);
     step(st + 1, s_st1, s_st0, true);
