@@ -356,6 +356,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma(DecodeArgs a) 
 // ws_owner[rank] = (pair, number of segments, tiles per kv head, whether
 // every run is non-empty), or pair -1.  Rows of empty sequences are zeroed
 // here.
+//
+// A wave's segment outputs (a whole pair's rows, or a split pair's (m, l, o))
+// are staged in its own LDS area and written to memory after its walk (or
+// when the area is full): stores count in the same counter as the ring's
+// loads, so a store issued inside the walk made the following tiles' waits
+// deeper than their own loads needed (measured on the 8B batch: about 1.5 us
+// per pair in a wave's run with the stores in the walk, 0.5 us without).
 constexpr int kStreamWgPerCu = 1;  // resident workgroups per CU: one wave per SIMD
 constexpr int kXcds = 8;           // accelerator dies, each with its own L2
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
@@ -580,8 +587,24 @@ __device__ void update_balance(StreamBalance* h, int nwg) {
   h->stamped = 0;
 }
 
+// LDS of the stream kernel: the sequence table and scan scratch, then each
+// wave's staging area for segment outputs (kStashBytes of entries, then
+// kStashEntries descriptors).  An entry holds, for lanes (c16 < G, g4), 128
+// bytes each at (4 c16 + g4) * 128 (a split pair's o; a whole pair's rows use
+// the first 64 of (4 c16 + g4) * 64), then G (m, l) pairs.
+constexpr int kStashBytes = 16384;
+constexpr int kStashEntries = 16;
+constexpr int kStashWave = kStashBytes + 16 * kStashEntries;
+__host__ __device__ constexpr int stash_offset(int num_seqs) {
+  return ((3 * num_seqs + 1 + kThreads + kXcds + 1) * 4 + 15) & ~15;
+}
+__host__ __device__ constexpr int stash_entry_bytes(int group) {
+  return (group * 520 + 15) & ~15;
+}
+static_assert(stash_entry_bytes(16) <= kStashBytes, "one entry of the largest group fits");
+
 size_t stream_smem_bytes(int num_seqs) {
-  return (3 * (size_t)num_seqs + 1 + kThreads + kXcds + 1) * 4;
+  return (size_t)stash_offset(num_seqs) + (size_t)kWaves * kStashWave;
 }
 
 template <class E, KvType KV>
@@ -590,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   using S = typename E::storage;
   using Tile = KvTile<E, KV>;
   using P = typename Tile::P;
-  extern __shared__ int s_int[];
+  extern __shared__ __attribute__((aligned(16))) int s_int[];
   const int B = a.num_seqs, Hkv = a.num_kv_heads, G = a.group;
   int* s_ctx = s_int;         // [B] clamped lengths, >= 0
   int* s_first = s_ctx + B;   // [B] first attended position (sliding window)
@@ -816,35 +839,72 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
     }
   };
 
-  // Store the segment: the normalised rows when it is the whole pair, else
-  // its (m, l, o) in slot (pair + rank).  Lane (c16, g4) holds
+  // Segment outputs go through the wave's LDS staging area: `nst` entries
+  // held, each described by (whole, sequence, kv head).
+  char* const sd = reinterpret_cast<char*>(s_int) + stash_offset(B) + w * kStashWave;
+  int4* const sdesc = reinterpret_cast<int4*>(sd + kStashBytes);
+  const int es = stash_entry_bytes(G);
+  const int cap = min(kStashEntries, kStashBytes / es);
+  const int lo128 = (4 * c16 + g4) * 128, lo64 = (4 * c16 + g4) * 64;
+  int nst = 0;
+  // Write the held entries: a whole pair's rows to `out`, a split pair's
+  // (m, l, o) to slot (pair + rank).
+  auto flush = [&]() {
+    for (int e = 0; e < nst; ++e) {
+      const int4 dsc = sdesc[e];
+      const int whole = uni(dsc.x), i = uni(dsc.y), g = uni(dsc.z);
+      const char* src = sd + e * es;
+      if (c16 < G) {
+        if (whole) {
+          S* dst = reinterpret_cast<S*>(a.out) +
+                   ((size_t)i * a.num_q_heads + (size_t)g * G + c16) * D + 32 * g4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<u32x4*>(dst + 8 * r) =
+                *reinterpret_cast<const u32x4*>(src + lo64 + 16 * r);
+        } else {
+          const size_t slot = (size_t)g * B + i + rank;
+          float* dst = a.ws_o + (slot * G + c16) * D + 32 * g4;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<f32x4*>(dst + 4 * k) =
+                *reinterpret_cast<const f32x4*>(src + lo128 + 16 * k);
+          if (g4 == 0)
+            a.ws_ml[slot * G + c16] = *reinterpret_cast<const float2*>(src + G * 512 + 8 * c16);
+        }
+      }
+    }
+    nst = 0;
+  };
+  // End of a segment: the normalised rows when it is the whole pair, else its
+  // (m, l, o), into the next entry.  Lane (c16, g4) holds
   // O[head c16][32 g4 + 8 r + e] = o[e][r].
   auto end_segment = [&]() {
     const float lsum = across_groups_sum<16>(l);
     const bool whole = seg_t0 == 0 && cc.t + 1 == cc.n;
-    if (c16 >= G) return;
-    if (whole) {
-      const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
-      S* dst = reinterpret_cast<S*>(a.out) +
-               ((size_t)cc.i * a.num_q_heads + (size_t)cc.g * G + c16) * D + 32 * g4;
+    if (nst == cap) flush();
+    char* dst = sd + nst * es;
+    if (c16 < G) {
+      if (whole) {
+        const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t b[8];
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<u32x4*>(dst + lo64 + 16 * r) =
+              u32x4{Mfma<E>::round16x2(o[0][r] * inv, o[1][r] * inv),
+                    Mfma<E>::round16x2(o[2][r] * inv, o[3][r] * inv),
+                    Mfma<E>::round16x2(o[4][r] * inv, o[5][r] * inv),
+                    Mfma<E>::round16x2(o[6][r] * inv, o[7][r] * inv)};
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b[e] = float_to_bits(E{}, o[e][r] * inv);
-        *reinterpret_cast<u32x4*>(dst + 8 * r) =
-            u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+        for (int r = 0; r < 4; ++r) {
+          *reinterpret_cast<f32x4*>(dst + lo128 + 32 * r) = f32x4{o[0][r], o[1][r], o[2][r], o[3][r]};
+          *reinterpret_cast<f32x4*>(dst + lo128 + 32 * r + 16) = f32x4{o[4][r], o[5][r], o[6][r], o[7][r]};
+        }
+        if (g4 == 0) *reinterpret_cast<float2*>(dst + G * 512 + 8 * c16) = make_float2(m, lsum);
       }
-    } else {
-      const size_t slot = (size_t)cc.g * B + cc.i + rank;
-      float* dst = a.ws_o + (slot * G + c16) * D + 32 * g4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<f32x4*>(dst + 8 * r) = f32x4{o[0][r], o[1][r], o[2][r], o[3][r]};
-        *reinterpret_cast<f32x4*>(dst + 8 * r + 4) = f32x4{o[4][r], o[5][r], o[6][r], o[7][r]};
-      }
-      if (g4 == 0) a.ws_ml[slot * G + c16] = make_float2(m, lsum);
     }
+    if (lane == 0) sdesc[nst] = int4{whole ? 1 : 0, cc.i, cc.g, 0};
+    ++nst;
   };
 
   begin_segment();
@@ -877,6 +937,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
       }
     }
   } while (crem > 0);
+  flush();
 
   report_bad_block(a.status, bad);
   // The run's last segment (still in cc): if it starts its pair and the pair
