@@ -26,21 +26,40 @@
 
 namespace pa {
 
+// Token and chunk of flat chunk index idx (32-bit division when the indices
+// fit, which is every write but the very largest).
+__device__ __forceinline__ void token_chunk(int64_t idx, int64_t total, int32_t per_token,
+                                            int64_t& t, int32_t& c) {
+  if (total <= 0x7FFFFFFF) {
+    const uint32_t t32 = (uint32_t)idx / (uint32_t)per_token;
+    t = t32;
+    c = (int32_t)((uint32_t)idx - t32 * (uint32_t)per_token);
+  } else {
+    t = idx / per_token;
+    c = (int32_t)(idx - t * per_token);
+  }
+}
+
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const u32x4* __restrict__ k, const u32x4* __restrict__ v, const int64_t* __restrict__ slots,
     int64_t total_chunks, int32_t chunks_per_token, int32_t chunks_per_row, int32_t num_kv_heads,
     int32_t block_size, int64_t num_slots, u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total_chunks) return;
-  const int64_t t = idx / chunks_per_token;
-  const int32_t c = (int32_t)(idx - t * chunks_per_token);
+  // the chunk's loads go out with its slot's, so a write waits for one
+  // round trip to memory instead of two
+  const u32x4 kc = k[idx], vc = v[idx];
+  int64_t t;
+  int32_t c;
+  token_chunk(idx, total_chunks, chunks_per_token, t, c);
   const int64_t slot = slots[t];
   if (slot < 0 || slot >= num_slots) return;
   const int32_t h = c / chunks_per_row, cc = c - h * chunks_per_row;
-  const int64_t blk = slot / block_size, off = slot - blk * block_size;
+  // block sizes are powers of two (the pool check admits 16 and 32)
+  const int64_t blk = slot >> __builtin_ctz(block_size), off = slot & (block_size - 1);
   const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * chunks_per_row + cc;
-  k_pool[dst] = k[idx];
-  v_pool[dst] = v[idx];
+  k_pool[dst] = kc;
+  v_pool[dst] = vc;
 }
 
 // 8 values of type E (one 16-byte chunk) -> 8 E4M3 codes of x * inv.
@@ -63,15 +82,18 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     float k_inv, float v_inv) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total_chunks) return;
-  const int64_t t = idx / chunks_per_token;
-  const int32_t c = (int32_t)(idx - t * chunks_per_token);
+  const u32x4 kc = k[idx], vc = v[idx];
+  int64_t t;
+  int32_t c;
+  token_chunk(idx, total_chunks, chunks_per_token, t, c);
   const int64_t slot = slots[t];
   if (slot < 0 || slot >= num_slots) return;
   const int32_t h = c / chunks_per_row, cc = c - h * chunks_per_row;
-  const int64_t blk = slot / block_size, off = slot - blk * block_size;
+  // block sizes are powers of two (the pool check admits 16 and 32)
+  const int64_t blk = slot >> __builtin_ctz(block_size), off = slot & (block_size - 1);
   const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * chunks_per_row + cc;
-  k_pool[dst] = quantize8<E>(k[idx], k_inv);
-  v_pool[dst] = quantize8<E>(v[idx], v_inv);
+  k_pool[dst] = quantize8<E>(kc, k_inv);
+  v_pool[dst] = quantize8<E>(vc, v_inv);
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_pool,
