@@ -377,27 +377,30 @@ __device__ __forceinline__ int seq_tiles(int ctx, int first) {
 
 // tb[i] = sum over j < i of seq_tiles(ctx[j], first[j]) (tile offset of
 // sequence i within a kv head's run), tb[n] = total.  Block-wide; ends with a
-// barrier.
+// barrier.  Each thread sums a contiguous range of sequences; the ranges are
+// scanned within each wave by lane shuffles and across the waves through
+// tmp[0..kWaves), with two barriers.
 __device__ void scan_tiles(const int* ctx, const int* first, int* tb, int n, int* tmp) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t % kWave, w = t / kWave;
   const int per = (n + kThreads - 1) / kThreads;
   const int lo = min(n, t * per), hi = min(n, lo + per);
   int sum = 0;
   for (int k = lo; k < hi; ++k) sum += seq_tiles(ctx[k], first[k]);
-  tmp[t] = sum;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int x = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += x;
-    __syncthreads();
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int x = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += x;
   }
-  int run = t > 0 ? tmp[t - 1] : 0;
+  if (lane == kWave - 1) tmp[w] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int v = 0; v < w; ++v) run += tmp[v];
   for (int k = lo; k < hi; ++k) {
     tb[k] = run;
     run += seq_tiles(ctx[k], first[k]);
   }
-  if (t == kThreads - 1) tb[n] = tmp[t];
+  if (t == kThreads - 1) tb[n] = run;
   __syncthreads();
 }
 
@@ -488,16 +491,32 @@ __device__ const uint32_t* header_words(const StreamBalance* h) {
   return reinterpret_cast<const uint32_t*>(h);
 }
 
+// The header words the cut is read from (magic at 0, cum at 4..12), loaded
+// by thread 0 at the start of a partition pass so that their latency
+// overlaps the sequence table's.
+constexpr int kHeaderCutWords = 4 + kXcds + 1;
+__device__ void load_cut_words(const DecodeArgs& a, uint32_t (&hw)[kHeaderCutWords]) {
+#pragma unroll
+  for (int x = 0; x < kHeaderCutWords; ++x) hw[x] = 0;
+  if (!a.balance || a.ws_balance == nullptr) return;
+  const uint32_t* src = header_words(a.ws_balance);
+  hw[0] = src[0];
+#pragma unroll
+  for (int x = 4; x < kHeaderCutWords; ++x) hw[x] = src[x];
+}
+
 // The cut of a partition pass, by thread 0 into s_cut[0..8] (LDS; the caller
 // puts a barrier after it): weighted by the workspace's balance state when
 // balancing is on, the pass is large enough, the header is valid and every
 // run stays non-empty (so the reduce pass, which sees only dense records
 // under weights, never needs the cut); else s_cut[0] = -1 (the even cut).
-__device__ void partition_cut(const DecodeArgs& a, long long T, int nwg, int* s_cut) {
+// hw: the header's words from load_cut_words.
+__device__ void partition_cut(const DecodeArgs& a, long long T, int nwg, int* s_cut,
+                              const uint32_t (&hw)[kHeaderCutWords]) {
   StreamSplit sp{T, nwg, nullptr, a.xcds};
   uint32_t cum[kXcds + 1];
   s_cut[0] = -1;
-  if (!a.balance || !sp.balanced_size() || !read_cut(header_words(a.ws_balance), cum)) return;
+  if (!a.balance || a.ws_balance == nullptr || !sp.balanced_size() || !read_cut(hw, cum)) return;
   for (int x = 0; x <= kXcds; ++x) s_cut[x] = (int)((T * (long long)cum[x]) >> 16);
   sp.cut = s_cut;
   if (!sp.dense()) s_cut[0] = -1;
@@ -620,6 +639,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   int* s_tb = s_first + B;    // [B + 1] tile offset of each sequence in a head's run
   int* s_tmp = s_tb + B + 1;  // [kThreads]
   int* s_cut = s_tmp + kThreads;  // [kXcds + 1] the weighted cut, or s_cut[0] = -1
+  uint32_t hw[kHeaderCutWords];
+  if (threadIdx.x == 0) load_cut_words(a, hw);
   for (int i = threadIdx.x; i < B; i += kThreads) {
     const int ctx = max(clamp_ctx(a, i), 0);
     s_ctx[i] = ctx;
@@ -631,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   const int lane = threadIdx.x % kWave, w = wave_id();
   const int c16 = lane & 15, g4 = lane >> 4;
   const int Th = uni(s_tb[B]);  // tiles of one kv head's run
-  if (threadIdx.x == 0) partition_cut(a, (long long)Th * Hkv, (int)gridDim.x, s_cut);
+  if (threadIdx.x == 0) partition_cut(a, (long long)Th * Hkv, (int)gridDim.x, s_cut, hw);
   __syncthreads();
   StreamSplit split{(long long)Th * Hkv, (int)gridDim.x, nullptr, a.xcds};
   if (uni(s_cut[0]) >= 0) split.cut = s_cut;

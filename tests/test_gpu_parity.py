@@ -321,6 +321,18 @@ def test_empty_sequences_between_others(path, decode_path):
     assert max_abs_err(out[kept], want) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("g", [4, 8, 16])
+def test_stream_runs_of_many_short_pairs(g, decode_path):
+    """4000 sequences of 1-48 tokens on the stream split: every wave's run
+    crosses many (kv head, sequence) pairs, more than its LDS staging area
+    holds (7, 3 and 1 entries at G = 4, 8, 16), so the area is written out
+    inside the walk as well as after it."""
+    decode_path("stream")
+    lens = [1 + (i * 13) % 48 for i in range(4000)]
+    d = W.custom(23 + g, 2 * g, 2, 128, "bf16", 16, lens)
+    check_case(d, state=False)
+
+
 def test_batch_beyond_stream_split_limit():
     """4100 sequences: the matrix-core kernel falls back to the grid split."""
     lens = [1 + (i * 7) % 40 for i in range(4100)]
