@@ -526,15 +526,18 @@ __device__ void partition_cut(const DecodeArgs& a, long long T, int nwg, int* s_
 // pass's record into the next cut, or initialise an invalid header with the
 // even cut.  One round of loads: the header's first 24 words into LDS and
 // each thread's wave slots, in parallel; each chunk's time is the largest
-// of its waves' slots (LDS maximum); then one thread updates the cut.  Plain
-// vector loads and stores: the partition pass ran before on the same stream,
-// so its stores are complete.  nwg: the partition pass's workgroups.
+// of its waves' slots (a wave maximum per chunk when a wave's 64 ranks lie
+// in one chunk, else per lane; then an LDS maximum); then eight lanes of
+// wave 0, one per chunk, update the cut (sums and scans by lane shuffles).
+// Plain vector loads and stores: the partition pass ran before on the same
+// stream, so its stores are complete.  nwg: the partition pass's workgroups.
 __device__ void update_balance(StreamBalance* h, int nwg) {
   constexpr int kWords = 24;  // magic, stamped, pad[2], cum[12], tiles[8]
   constexpr int kPer = kStreamMaxWaves / kThreads;
   __shared__ uint32_t s_hdr[kWords];
   __shared__ uint32_t s_dmax[kXcds];
   const int n = kWaves * nwg;  // wave ranks of the partition pass (<= kStreamMaxWaves)
+  const int lane = threadIdx.x % kWave;
   if (threadIdx.x < kWords) s_hdr[threadIdx.x] = header_words(h)[threadIdx.x];
   if (threadIdx.x < kXcds) s_dmax[threadIdx.x] = 0;
   uint32_t d[kPer];
@@ -550,60 +553,79 @@ __device__ void update_balance(StreamBalance* h, int nwg) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int r = (int)threadIdx.x + k * kThreads;
-      if (r < n) atomicMax(&s_dmax[r / R], d[k]);
+      if (R % kWave == 0) {  // the wave's 64 ranks share a chunk
+        uint32_t v = d[k];
+#pragma unroll
+        for (int m = 1; m < kWave; m <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
+        if (lane == 0 && r < n) atomicMax(&s_dmax[r / R], v);
+      } else if (r < n) {
+        atomicMax(&s_dmax[r / R], d[k]);
+      }
     }
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
+  if (threadIdx.x >= kWave) return;
+  // wave 0; lane x < 8 stands for chunk x
+  const int x = lane;
+  const bool lx = x < kXcds;
   uint32_t cum[kXcds + 1];
   if (!read_cut(s_hdr, cum)) {
-    h->magic = kBalanceMagic;
-    for (int x = 0; x <= kXcds; ++x) h->cum[x] = kBalanceOne / kXcds * x;
-    for (int x = 0; x < kXcds; ++x) h->tiles[x] = 0;
-    h->stamped = 0;
+    if (x <= kXcds) h->cum[x] = kBalanceOne / kXcds * x;
+    if (lx) h->tiles[x] = 0;
+    if (x == 0) {
+      h->magic = kBalanceMagic;
+      h->stamped = 0;
+    }
     return;
   }
   if (!s_hdr[1] || nwg % kXcds != 0) return;  // no record to use
-  float rate[kXcds], total = 0.f;
-  bool ok = true;
-  uint32_t dmin = 0xFFFFFFFFu, dmax = 0;
-  for (int x = 0; x < kXcds; ++x) {
-    const uint32_t n = s_hdr[16 + x], d = s_dmax[x];
-    ok = ok && n > 0 && d > 0;
-    rate[x] = d > 0 ? (float)n / (float)d : 0.f;
-    total += rate[x];
-    dmin = min(dmin, d);
-    dmax = max(dmax, d);
+  const uint32_t nt = lx ? s_hdr[16 + x] : 0u, dd = lx ? s_dmax[x] : 0u;
+  const bool ok = __builtin_amdgcn_ballot_w64(lx && (nt == 0 || dd == 0)) == 0;
+  const float rate = dd > 0 ? (float)nt / (float)dd : 0.f;
+  // sums, minima and maxima over the eight chunk lanes (lanes 0..7 hold
+  // them; the xor shuffles below 8 stay inside that group)
+  auto sum8 = [](float v) {
+    v += __shfl_xor(v, 1, kWave);
+    v += __shfl_xor(v, 2, kWave);
+    v += __shfl_xor(v, 4, kWave);
+    return v;
+  };
+  const float total = sum8(rate);
+  uint32_t dmin = lx ? dd : 0xFFFFFFFFu, dmax = dd;
+#pragma unroll
+  for (int m = 1; m < kXcds; m <<= 1) {
+    dmin = min(dmin, (uint32_t)__shfl_xor((int)dmin, m, kWave));
+    dmax = max(dmax, (uint32_t)__shfl_xor((int)dmax, m, kWave));
   }
   // chunks ending within 1/64 of each other: balanced, the cut stays
   if (ok && total > 0.f && dmax - dmin > dmax / 64) {
     // halfway from the current share to the measured one, kept within
     // [1/16, 3/16] (a little inside, so rounding stays in range)
-    float sh[kXcds];
-    for (int x = 0; x < kXcds; ++x)
-      sh[x] = 0.5f * (float)(cum[x + 1] - cum[x]) / (float)kBalanceOne + 0.5f * rate[x] / total;
+    const uint32_t c0 = lx ? s_hdr[4 + x] : 0u, c1 = lx ? s_hdr[5 + x] : 0u;
+    float sh = lx ? 0.5f * (float)(c1 - c0) / (float)kBalanceOne + 0.5f * rate / total : 0.f;
     for (int it = 0; it < 4; ++it) {
-      float s = 0.f;
-      for (int x = 0; x < kXcds; ++x) s += sh[x];
-      for (int x = 0; x < kXcds; ++x) sh[x] = fminf(fmaxf(sh[x] / s, 0.0675f), 0.1825f);
+      const float s = sum8(sh);
+      sh = lx ? fminf(fmaxf(sh / s, 0.0675f), 0.1825f) : 0.f;
     }
-    float s = 0.f;
-    for (int x = 0; x < kXcds; ++x) s += sh[x];
-    float run = 0.f;
-    uint32_t next[kXcds + 1];
-    next[0] = 0;
-    for (int x = 0; x < kXcds; ++x) {
-      run += sh[x];
-      next[x + 1] = x + 1 == kXcds ? kBalanceOne : (uint32_t)__float2uint_rn(run / s * kBalanceOne);
+    const float s = sum8(sh);
+    float run = sh;  // inclusive scan over the chunk lanes
+#pragma unroll
+    for (int m = 1; m < kXcds; m <<= 1) {
+      const float y = __shfl_up(run, m, kWave);
+      if (x >= m) run += y;
     }
-    bool good = true;
-    for (int x = 0; x < kXcds; ++x)
-      good = good && next[x + 1] >= next[x] && next[x + 1] - next[x] >= kShareMin &&
-             next[x + 1] - next[x] <= kShareMax;
-    if (good)
-      for (int x = 0; x <= kXcds; ++x) h->cum[x] = next[x];
+    const uint32_t next =
+        x + 1 == kXcds ? kBalanceOne : (uint32_t)__float2uint_rn(run / s * kBalanceOne);
+    // every lane takes part in the shuffle (a lane left out supplies no value)
+    const uint32_t below = (uint32_t)__shfl_up((int)next, 1, kWave);
+    const uint32_t prev = x == 0 ? 0u : below;
+    const bool bad_x = lx && (next < prev || next - prev < kShareMin || next - prev > kShareMax);
+    if (__builtin_amdgcn_ballot_w64(bad_x) == 0) {
+      if (lx) h->cum[x + 1] = next;
+      if (x == 0) h->cum[0] = 0;
+    }
   }
-  h->stamped = 0;
+  if (x == 0) h->stamped = 0;
 }
 
 // LDS of the stream kernel: the sequence table and scan scratch, then each
