@@ -630,9 +630,10 @@ __device__ void update_balance(StreamBalance* h, int nwg) {
 
 // LDS of the stream kernel: the sequence table and scan scratch, then each
 // wave's staging area for segment outputs (kStashBytes of entries, then
-// kStashEntries descriptors).  An entry holds, for lanes (c16 < G, g4), 128
-// bytes each at (4 c16 + g4) * 128 (a split pair's o; a whole pair's rows use
-// the first 64 of (4 c16 + g4) * 64), then G (m, l) pairs.
+// kStashEntries descriptors).  An entry holds the 16-byte pieces of lanes
+// (c16 < G, g4): piece k of lane j = 4 c16 + g4 at 16 (4 G k + j), so the
+// lanes of one store or load cover contiguous bytes (eight pieces of a split
+// pair's o, or four of a whole pair's rows), then G (m, l) pairs.
 constexpr int kStashBytes = 16384;
 constexpr int kStashEntries = 16;
 constexpr int kStashWave = kStashBytes + 16 * kStashEntries;
@@ -888,7 +889,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
   int4* const sdesc = reinterpret_cast<int4*>(sd + kStashBytes);
   const int es = stash_entry_bytes(G);
   const int cap = min(kStashEntries, kStashBytes / es);
-  const int lo128 = (4 * c16 + g4) * 128, lo64 = (4 * c16 + g4) * 64;
+  const int lj = 16 * (4 * c16 + g4), lk = 64 * G;  // lane's piece 0, piece stride
   int nst = 0;
   // Write the held entries: a whole pair's rows to `out`, a split pair's
   // (m, l, o) to slot (pair + rank).
@@ -904,14 +905,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             *reinterpret_cast<u32x4*>(dst + 8 * r) =
-                *reinterpret_cast<const u32x4*>(src + lo64 + 16 * r);
+                *reinterpret_cast<const u32x4*>(src + lj + lk * r);
         } else {
           const size_t slot = (size_t)g * B + i + rank;
           float* dst = a.ws_o + (slot * G + c16) * D + 32 * g4;
 #pragma unroll
           for (int k = 0; k < 8; ++k)
             *reinterpret_cast<f32x4*>(dst + 4 * k) =
-                *reinterpret_cast<const f32x4*>(src + lo128 + 16 * k);
+                *reinterpret_cast<const f32x4*>(src + lj + lk * k);
           if (g4 == 0)
             a.ws_ml[slot * G + c16] = *reinterpret_cast<const float2*>(src + G * 512 + 8 * c16);
         }
@@ -932,7 +933,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
         const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          *reinterpret_cast<u32x4*>(dst + lo64 + 16 * r) =
+          *reinterpret_cast<u32x4*>(dst + lj + lk * r) =
               u32x4{Mfma<E>::round16x2(o[0][r] * inv, o[1][r] * inv),
                     Mfma<E>::round16x2(o[2][r] * inv, o[3][r] * inv),
                     Mfma<E>::round16x2(o[4][r] * inv, o[5][r] * inv),
@@ -940,8 +941,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_stream(DecodeA
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          *reinterpret_cast<f32x4*>(dst + lo128 + 32 * r) = f32x4{o[0][r], o[1][r], o[2][r], o[3][r]};
-          *reinterpret_cast<f32x4*>(dst + lo128 + 32 * r + 16) = f32x4{o[4][r], o[5][r], o[6][r], o[7][r]};
+          *reinterpret_cast<f32x4*>(dst + lj + lk * (2 * r)) = f32x4{o[0][r], o[1][r], o[2][r], o[3][r]};
+          *reinterpret_cast<f32x4*>(dst + lj + lk * (2 * r + 1)) = f32x4{o[4][r], o[5][r], o[6][r], o[7][r]};
         }
         if (g4 == 0) *reinterpret_cast<float2*>(dst + G * 512 + 8 * c16) = make_float2(m, lsum);
       }
