@@ -472,6 +472,61 @@ VARIANT_WINDOW = 1024
 FP8_SCALES = (0.05, 0.05)
 
 
+def decode_tile_offsets(plan, d):
+    """Byte offsets, in the pool, of every 16-token tile the decode step
+    reads, in the stream split's flat order (kv head, sequence, tile)."""
+    wl = d.wl
+    tables = plan.tables.cpu().numpy().astype(np.int64)
+    lens = plan.lens.cpu().numpy().astype(np.int64)
+    row = wl.head_dim * wl.elem_bytes
+    blk = wl.num_kv_heads * wl.block_size * row
+    offs = []
+    for g in range(wl.num_kv_heads):
+        for i in range(d.batch):
+            pos = np.arange(-(-int(lens[i]) // 16), dtype=np.int64) * 16
+            offs.append(tables[i, pos // wl.block_size] * blk + g * wl.block_size * row +
+                        (pos % wl.block_size) * row)
+    return np.concatenate(offs)
+
+
+def measure_read_probe(cache, plan, d, part_us: float, reps: int, log):
+    """The read ceiling of the decode access pattern: pa_probe_tile_reads over
+    the step's K tiles and then its V tiles, `reps` back-to-back pairs
+    between two HIP events, (a) with the decode stream kernel's work split
+    (one run per wave, 4 waves per CU), set beside the partition kernel,
+    which reads the same tiles that way, and (b) with one tile per wave."""
+    import torch
+    import paged_kv_cache_107_amd as pa
+    offs = decode_tile_offsets(plan, d)
+    offs_d = torch.from_numpy(offs.astype(np.uint32).view(np.int32)).cuda()
+    tile_bytes = 16 * d.wl.head_dim * d.wl.elem_bytes
+    per_tile = 4 * (-(-len(offs) // 4))
+    out = torch.empty(per_tile, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    nbytes = 2 * len(offs) * tile_bytes
+    rec = {"tiles_per_pool": int(len(offs)), "tile_bytes": tile_bytes, "bytes": nbytes}
+    for name, waves in (("decode_split", 0), ("one_tile_per_wave", per_tile)):
+        for _ in range(3):
+            pa.pa_probe_tile_reads(cache.k_pool, offs_d, tile_bytes, waves, out)
+            pa.pa_probe_tile_reads(cache.v_pool, offs_d, tile_bytes, waves, out)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            pa.pa_probe_tile_reads(cache.k_pool, offs_d, tile_bytes, waves, out)
+            pa.pa_probe_tile_reads(cache.v_pool, offs_d, tile_bytes, waves, out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / reps
+        rate = nbytes / (us * 1e-6) / 1e9
+        rec[name] = {"us_k_and_v": round(us, 2), "gbps": round(rate, 1),
+                     "frac_of_hbm_peak": round(rate / HBM_PEAK_GBPS, 4),
+                     "partition_frac_of_probe_rate": round(us / part_us, 4)}
+        log(f"read probe ({name}): {len(offs)} tiles x 2 pools ({nbytes / 1e9:.3f} GB) in "
+            f"{us:.1f} us = {rate:.0f} GB/s ({rate / HBM_PEAK_GBPS:.1%} of peak); the partition "
+            f"kernel reads the same tiles at {us / part_us:.1%} of that rate")
+    return rec
+
+
 def quantised_pools(k_pool, v_pool):
     """8-bit E4M3 copies of both pools: every slot written once by the
     quantising pa_reshape_and_cache (scales FP8_SCALES)."""
@@ -796,6 +851,8 @@ def main(argv=None):
     ap.add_argument("--prefix-reps", type=int, default=10,
                     help="timed prefill passes per variant on the shared-system-prompt "
                          "workload, with and without the prefix cache (0 = skip)")
+    ap.add_argument("--probe-reps", type=int, default=20,
+                    help="read-ceiling probe passes over the step's K and V tiles (0 = skip)")
     ap.add_argument("--config-reps", type=int, default=30,
                     help="timed decode steps on each other named workload (0 = skip)")
     ap.add_argument("--e2e-steps", type=int, default=50,
@@ -903,6 +960,9 @@ def main(argv=None):
     seq_per_s = d.batch / (ms_per_step * 1e-3)
     kv_gbps_step = kv_bytes / (ms_per_step * 1e-3) / 1e9
 
+    probe = None
+    if args.probe_reps > 0:
+        probe = measure_read_probe(cache, plan, d, part_us, args.probe_reps, log)
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(d, out, args.cpu_budget, log)
@@ -962,6 +1022,7 @@ def main(argv=None):
             "kernel_us": round(part_us, 2),
         },
         "passes_us": passes_us,
+        "read_probe": probe,
         "host_step_ms": None if e2e is None else e2e["host_plan_ms_median"],
         "e2e": e2e,
         "cpu_baseline": cpu,

@@ -586,6 +586,35 @@ pa_status pa_swap_blocks(void* k_pool, void* v_pool, void* k_host, void* v_host,
                          int32_t num_host_blocks, const pa_pool_desc* pool, const int32_t* pairs,
                          int32_t num_pairs, int32_t direction, void* hip_stream);
 
+/* ------------------------------------------------------------------------
+ * Read ceiling of the decode access pattern (a measurement aid).  Decode
+ * reads every attended K/V row once per step and is bound by memory (page
+ * "vLLM：把 KV 缓存当成虚拟内存", section "KV 的体积从哪来，页表如何把它切开"),
+ * in tiles scattered over the pool.  This call reads a list of such tiles
+ * and does nothing else with them: 4-wave workgroups, each wave a contiguous
+ * run of the list (wave rank r of W: tiles [n r / W, n (r + 1) / W)), 32
+ * 16-byte loads in flight per wave, each tile's offset read one tile ahead.
+ * With W = 4 per compute unit it is the decode stream kernel's work split,
+ * and its rate over a step's tiles is what that split allows; with W = n
+ * (one tile per wave) it is the rate of the tiles alone.
+ *   pool          device bytes [pool_bytes], 16-byte aligned; pool_bytes
+ *                 below 2^32
+ *   tile_offsets  device uint32 [num_tiles]: tile t is the tile_bytes bytes
+ *                 at byte offset tile_offsets[t] of pool, a multiple of 16
+ *                 (bytes past pool_bytes read as zeros)
+ *   tile_bytes    1024, 2048 or 4096
+ *   num_waves     W, a positive multiple of 4 up to 2^24, or 0 for 4 per
+ *                 compute unit (the decode stream split's grid)
+ *   out           device uint32 [out_len]: out[r] = the XOR of every 32-bit
+ *                 word wave r read; out_len >= W
+ *   waves         host int32, or NULL: receives W
+ * PA_ERR_ARG for a null or misaligned pointer, a size out of range or an
+ * out_len below W; PA_ERR_HIP when the device cannot be queried.  Runs
+ * asynchronously on the stream; allocates nothing. */
+pa_status pa_probe_tile_reads(const void* pool, uint64_t pool_bytes, const uint32_t* tile_offsets,
+                              int64_t num_tiles, int32_t tile_bytes, int32_t num_waves,
+                              uint32_t* out, int32_t out_len, int32_t* waves, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

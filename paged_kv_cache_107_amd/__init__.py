@@ -15,5 +15,5 @@ from ._lib import (LIB_PATH, PA_BF16, PA_F16, PA_F32, PA_KV_FP8_E4M3, PA_KV_SAME
 from .allocator import PaAllocator  # noqa: F401
 from .ops import (FP8, alloc_workspace, pa_copy_blocks, pa_decode, pa_decode_noalloc,  # noqa: F401
                   pa_decode_partition, pa_decode_reduce, pa_decode_workspace_bytes, pa_prefill, pa_reshape_and_cache,
-                  pa_set_decode_balance, pa_set_decode_path, pa_set_prefill_path,
-                  pa_swap_blocks, pool_desc)
+                  pa_probe_tile_reads, pa_set_decode_balance, pa_set_decode_path,
+                  pa_set_prefill_path, pa_swap_blocks, pool_desc)

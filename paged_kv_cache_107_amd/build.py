@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
 ARCH = "gfx950"
-SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cache.hip", "pa_alloc.cpp"]
+SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cache.hip", "pa_probe.hip",
+           "pa_alloc.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.  The host pass
 # does not know the feature and says so; that warning is harmless.
