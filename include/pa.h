@@ -220,14 +220,19 @@ pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_poo
                             float scale, int32_t sliding_window, void* out,
                             int32_t partition_tokens, int32_t* status, void* hip_stream);
 
-/* Decode kernel family.  PA_PATH_AUTO: the matrix-core kernel for 16-bit
- * pools with head_dim 128 and G = num_q_heads / num_kv_heads in [2, 16], the
- * vector kernel otherwise.  PA_PATH_MFMA / PA_PATH_VALU force one family
- * (PA_ERR_SHAPE if it does not support the shape).  The matrix-core kernel
- * uses the stream split when the batch has at most 4096 sequences, else the
- * grid split; PA_PATH_MFMA_GRID forces the grid split.  Results agree up to
- * the order of the fp32 merges.  Process-wide setting; returns the previous
- * value (-1 for an unknown path, which leaves the setting unchanged). */
+/* Decode kernel family.  PA_PATH_AUTO: the matrix-core kernels for 16-bit
+ * and 8-bit pools with head_dim 128 and G = num_q_heads / num_kv_heads in
+ * [1, 16], the vector kernel otherwise; among the matrix-core kernels, the
+ * grid split for a small single-partition pass (max_context_len <=
+ * partition_tokens and num_seqs * num_kv_heads * ceil(max_context_len / 16)
+ * at most 80 tiles per stream wave: no reduce pass is needed and the
+ * hardware's workgroup dispatch balances it), else the stream split when the
+ * batch has at most 4096 sequences, else the grid split.  PA_PATH_MFMA /
+ * PA_PATH_VALU force one family (PA_ERR_SHAPE if it does not support the
+ * shape), PA_PATH_MFMA taking the stream split up to 4096 sequences;
+ * PA_PATH_MFMA_GRID forces the grid split.  Results agree up to the order of
+ * the fp32 merges.  Process-wide setting; returns the previous value (-1 for
+ * an unknown path, which leaves the setting unchanged). */
 typedef enum {
   PA_PATH_AUTO = 0,
   PA_PATH_VALU = 1,

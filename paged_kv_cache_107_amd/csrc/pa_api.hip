@@ -128,17 +128,39 @@ inline pa::KvType kv_type(const pa_pool_desc* pool) {
   return pool->kv_dtype == PA_KV_FP8_E4M3 ? pa::KvType::kFp8 : pa::KvType::kSame;
 }
 
+// Small single-partition passes: every sequence fits one partition and the
+// batch has at most kSmallPassTilesPerWave tiles per stream wave even if
+// every sequence had the longest length.  The grid split then needs no
+// reduce pass, and the hardware's workgroup dispatch balances it; the stream
+// split's fixed costs (its prologue, the reduce pass) are a large part of
+// such a pass.  Measured (bf16/f16, one call = partition + reduce): 128 CoW
+// branches 50 against 55 us; 32 sequences up to 2048 tokens 31 against
+// 40 us; 64 sequences of G = 1 up to 512 tokens 22 against 30 us; at 256
+// tiles per wave the stream split wins (256 sequences up to 2048 tokens: 180
+// against 188 us).
+constexpr int64_t kSmallPassTilesPerWave = 80;
+bool small_single_partition_pass(const pa_pool_desc* pool, int32_t num_seqs,
+                                 int32_t max_context_len, int32_t partition_tokens) {
+  if (max_context_len > partition_tokens) return false;
+  const int64_t waves = pa::stream_waves();
+  const int64_t tiles = (int64_t)num_seqs * pool->num_kv_heads * ((max_context_len + 15) / 16);
+  return waves > 0 && tiles <= kSmallPassTilesPerWave * waves;
+}
+
 // The kernel pa_decode runs for this shape under the current path setting.
 // 8-bit pools run on the matrix-core kernels only (any G up to 16).
 pa_status choose_kernel(const pa_pool_desc* pool, int32_t group, int32_t num_seqs,
-                        int32_t max_context_len, pa::DecodeKernel* k) {
+                        int32_t max_context_len, int32_t partition_tokens,
+                        pa::DecodeKernel* k) {
   const bool mfma = pa::mfma_supports(pool->dtype, pool->head_dim, group);
   const bool stream = mfma && pa::stream_supports(num_seqs, pool->num_kv_heads, max_context_len);
   const int32_t path = g_decode_path.load();
   if (kv_type(pool) == pa::KvType::kFp8) {
     if (!mfma || path == PA_PATH_VALU) return PA_ERR_SHAPE;
-    *k = stream && path != PA_PATH_MFMA_GRID ? pa::DecodeKernel::kMfmaStream
-                                             : pa::DecodeKernel::kMfmaGrid;
+    const bool small = path == PA_PATH_AUTO &&
+                       small_single_partition_pass(pool, num_seqs, max_context_len, partition_tokens);
+    *k = stream && path != PA_PATH_MFMA_GRID && !small ? pa::DecodeKernel::kMfmaStream
+                                                       : pa::DecodeKernel::kMfmaGrid;
     return PA_OK;
   }
   if (path == PA_PATH_VALU) {
@@ -147,9 +169,13 @@ pa_status choose_kernel(const pa_pool_desc* pool, int32_t group, int32_t num_seq
   } else if (path == PA_PATH_MFMA_GRID) {
     if (!mfma) return PA_ERR_SHAPE;
     *k = pa::DecodeKernel::kMfmaGrid;
-  } else if (path == PA_PATH_MFMA || (mfma && group >= 2)) {
+  } else if (path == PA_PATH_MFMA) {
     if (!mfma) return PA_ERR_SHAPE;
     *k = stream ? pa::DecodeKernel::kMfmaStream : pa::DecodeKernel::kMfmaGrid;
+  } else if (mfma) {  // PA_PATH_AUTO on a matrix-core shape, any G
+    *k = stream && !small_single_partition_pass(pool, num_seqs, max_context_len, partition_tokens)
+             ? pa::DecodeKernel::kMfmaStream
+             : pa::DecodeKernel::kMfmaGrid;
   } else {
     if (!pa::valu_supports(pool->dtype, pool->head_dim, group)) return PA_ERR_SHAPE;
     *k = pa::DecodeKernel::kValu;
@@ -181,7 +207,7 @@ pa_status prepare_decode(const void* q, const void* k_pool, const void* v_pool,
       partition_tokens % pool->block_size != 0)
     return PA_ERR_ARG;
   pa::DecodeKernel kernel;
-  st = choose_kernel(pool, group, num_seqs, max_context_len, &kernel);
+  st = choose_kernel(pool, group, num_seqs, max_context_len, partition_tokens, &kernel);
   if (st != PA_OK) return st;
   if (num_seqs == 0) {
     *pr = Prepared{};

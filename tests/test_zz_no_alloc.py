@@ -98,15 +98,21 @@ def test_noalloc_equals_workspace_decode(path, seed, hq, hkv, d, dtype, bs, lens
 
 def test_noalloc_refuses_oversize_without_launch():
     """A shape whose workspace exceeds the static scratch: PA_ERR_SCRATCH,
-    and the output is untouched."""
+    and the output is untouched.  The matrix-core path is forced: this pass
+    is small and fits one partition, so PA_PATH_AUTO would take the grid
+    split, which needs no scratch for it."""
     hkv, g, b = 8, 16, 4096
     pool = torch.zeros((64, hkv, 16, 128), dtype=torch.bfloat16, device="cuda")
     q = torch.zeros((b, hkv * g, 128), dtype=torch.bfloat16, device="cuda")
     out = torch.full_like(q, 7.0)
     tables = torch.zeros((b, 1), dtype=torch.int32, device="cuda")
     lens = torch.ones(b, dtype=torch.int32, device="cuda")
-    with pytest.raises(pa.PaError) as e:
-        pa.pa_decode_noalloc(q, pool, pool, tables, lens, 0.1, out, 16)
-    assert e.value.status == -9
+    prev = pa.pa_set_decode_path(pa.PA_PATH_MFMA)
+    try:
+        with pytest.raises(pa.PaError) as e:
+            pa.pa_decode_noalloc(q, pool, pool, tables, lens, 0.1, out, 16)
+        assert e.value.status == -9
+    finally:
+        pa.pa_set_decode_path(prev)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
