@@ -491,10 +491,11 @@ def decode_tile_offsets(plan, d):
 
 def measure_read_probe(cache, plan, d, part_us: float, reps: int, log):
     """The read ceiling of the decode access pattern: pa_probe_tile_reads over
-    the step's K tiles and then its V tiles, `reps` back-to-back pairs
-    between two HIP events, (a) with the decode stream kernel's work split
-    (one run per wave, 4 waves per CU), set beside the partition kernel,
-    which reads the same tiles that way, and (b) with one tile per wave."""
+    the step's tiles, each (block, kv head)'s K and V tile read together as
+    the partition kernel reads them, `reps` back-to-back calls between two
+    HIP events, (a) with the decode stream kernel's work split (one run per
+    wave, 4 waves per CU), set beside the partition kernel, and (b) with one
+    tile per wave."""
     import torch
     import paged_kv_cache_107_amd as pa
     offs = decode_tile_offsets(plan, d)
@@ -507,13 +508,11 @@ def measure_read_probe(cache, plan, d, part_us: float, reps: int, log):
     rec = {"tiles_per_pool": int(len(offs)), "tile_bytes": tile_bytes, "bytes": nbytes}
     for name, waves in (("decode_split", 0), ("one_tile_per_wave", per_tile)):
         for _ in range(3):
-            pa.pa_probe_tile_reads(cache.k_pool, offs_d, tile_bytes, waves, out)
-            pa.pa_probe_tile_reads(cache.v_pool, offs_d, tile_bytes, waves, out)
+            pa.pa_probe_tile_reads(cache.k_pool, offs_d, tile_bytes, waves, out, cache.v_pool)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(reps):
-            pa.pa_probe_tile_reads(cache.k_pool, offs_d, tile_bytes, waves, out)
-            pa.pa_probe_tile_reads(cache.v_pool, offs_d, tile_bytes, waves, out)
+            pa.pa_probe_tile_reads(cache.k_pool, offs_d, tile_bytes, waves, out, cache.v_pool)
         b.record(stream)
         torch.cuda.synchronize()
         us = 1e3 * a.elapsed_time(b) / reps
@@ -521,7 +520,7 @@ def measure_read_probe(cache, plan, d, part_us: float, reps: int, log):
         rec[name] = {"us_k_and_v": round(us, 2), "gbps": round(rate, 1),
                      "frac_of_hbm_peak": round(rate / HBM_PEAK_GBPS, 4),
                      "partition_frac_of_probe_rate": round(us / part_us, 4)}
-        log(f"read probe ({name}): {len(offs)} tiles x 2 pools ({nbytes / 1e9:.3f} GB) in "
+        log(f"read probe ({name}): {len(offs)} K and V tiles ({nbytes / 1e9:.3f} GB) in "
             f"{us:.1f} us = {rate:.0f} GB/s ({rate / HBM_PEAK_GBPS:.1%} of peak); the partition "
             f"kernel reads the same tiles at {us / part_us:.1%} of that rate")
     return rec

@@ -135,7 +135,9 @@ const char* pa_status_string(int32_t status);
  *                 workspace across calls lets the balance adapt.
  *   partition_tokens  multiple of 16 and of block_size, in [16, 4096];
  *                 0 selects the default (512).  Sizes the grid split's
- *                 partitions; validated but unused by the stream split.
+ *                 partitions, and under PA_PATH_AUTO decides whether a small
+ *                 pass fits one partition (see pa_set_decode_path); unused
+ *                 by the stream split.
  *   sliding_window  0: none.  W > 0: the query (position ctx - 1) attends only
  *                 positions max(0, ctx - W) .. ctx - 1 (its own and the W - 1
  *                 before it); table entries of blocks wholly below that are
@@ -598,27 +600,32 @@ pa_status pa_swap_blocks(void* k_pool, void* v_pool, void* k_host, void* v_host,
  * in tiles scattered over the pool.  This call reads a list of such tiles
  * and does nothing else with them: 4-wave workgroups, each wave a contiguous
  * run of the list (wave rank r of W: tiles [n r / W, n (r + 1) / W)), 32
- * 16-byte loads in flight per wave, each tile's offset read one tile ahead.
+ * 16-byte loads in flight per wave, each tile's offset read one tile ahead
+ * (one offset for both pools' tiles when two are given).
  * With W = 4 per compute unit it is the decode stream kernel's work split,
  * and its rate over a step's tiles is what that split allows; with W = n
  * (one tile per wave) it is the rate of the tiles alone.
  *   pool          device bytes [pool_bytes], 16-byte aligned; pool_bytes
  *                 below 2^32
+ *   pool2         a second pool of pool_bytes, or NULL: each tile is then
+ *                 read from both pools at the same offset (as the decode
+ *                 kernel reads the K and V tiles of one (block, kv head))
  *   tile_offsets  device uint32 [num_tiles]: tile t is the tile_bytes bytes
- *                 at byte offset tile_offsets[t] of pool, a multiple of 16
- *                 (bytes past pool_bytes read as zeros)
+ *                 at byte offset tile_offsets[t] of pool (and of pool2), a
+ *                 multiple of 16 (bytes past pool_bytes read as zeros)
  *   tile_bytes    1024, 2048 or 4096
  *   num_waves     W, a positive multiple of 4 up to 2^24, or 0 for 4 per
  *                 compute unit (the decode stream split's grid)
  *   out           device uint32 [out_len]: out[r] = the XOR of every 32-bit
- *                 word wave r read; out_len >= W
+ *                 word wave r read (of both pools); out_len >= W
  *   waves         host int32, or NULL: receives W
  * PA_ERR_ARG for a null or misaligned pointer, a size out of range or an
  * out_len below W; PA_ERR_HIP when the device cannot be queried.  Runs
  * asynchronously on the stream; allocates nothing. */
-pa_status pa_probe_tile_reads(const void* pool, uint64_t pool_bytes, const uint32_t* tile_offsets,
-                              int64_t num_tiles, int32_t tile_bytes, int32_t num_waves,
-                              uint32_t* out, int32_t out_len, int32_t* waves, void* hip_stream);
+pa_status pa_probe_tile_reads(const void* pool, const void* pool2, uint64_t pool_bytes,
+                              const uint32_t* tile_offsets, int64_t num_tiles, int32_t tile_bytes,
+                              int32_t num_waves, uint32_t* out, int32_t out_len, int32_t* waves,
+                              void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -90,7 +90,8 @@ SIGNATURES = {
     "pa_seq_swap_in": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
     "pa_swap_query": (_i32, [_vp, C.POINTER(pa_swap_stats), _pi32]),
     "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _desc, _vp, _i32, _i32, _vp]),
-    "pa_probe_tile_reads": (_i32, [_vp, C.c_uint64, _vp, _i64, _i32, _i32, _vp, _i32, _pi32, _vp]),
+    "pa_probe_tile_reads": (_i32, [_vp, _vp, C.c_uint64, _vp, _i64, _i32, _i32, _vp, _i32, _pi32,
+                                   _vp]),
 }
 
 # Host allocator entry points (plain C++, no device code).  With the

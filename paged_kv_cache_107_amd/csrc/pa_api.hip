@@ -543,9 +543,10 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const pa_pool_desc* pool,
                                 static_cast<hipStream_t>(hip_stream));
 }
 
-pa_status pa_probe_tile_reads(const void* pool, uint64_t pool_bytes, const uint32_t* tile_offsets,
-                              int64_t num_tiles, int32_t tile_bytes, int32_t num_waves,
-                              uint32_t* out, int32_t out_len, int32_t* waves, void* hip_stream) {
+pa_status pa_probe_tile_reads(const void* pool, const void* pool2, uint64_t pool_bytes,
+                              const uint32_t* tile_offsets, int64_t num_tiles, int32_t tile_bytes,
+                              int32_t num_waves, uint32_t* out, int32_t out_len, int32_t* waves,
+                              void* hip_stream) {
   if (num_waves < 0 || num_waves > (1 << 24) || num_waves % 4 != 0) return PA_ERR_ARG;
   const int w = num_waves > 0 ? num_waves : pa::stream_waves();
   if (w <= 0) return PA_ERR_HIP;
@@ -554,11 +555,11 @@ pa_status pa_probe_tile_reads(const void* pool, uint64_t pool_bytes, const uint3
       (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096) || out_len < w)
     return PA_ERR_ARG;
   if (!pool || !out || (num_tiles > 0 && !tile_offsets)) return PA_ERR_ARG;
-  if (!aligned16(pool) || (reinterpret_cast<uintptr_t>(out) & 3u) ||
+  if (!aligned16(pool) || !aligned16(pool2) || (reinterpret_cast<uintptr_t>(out) & 3u) ||
       (reinterpret_cast<uintptr_t>(tile_offsets) & 3u))
     return PA_ERR_ARG;
-  return pa::launch_probe_reads(pool, (uint32_t)pool_bytes, tile_offsets, num_tiles, tile_bytes, out,
-                                w, static_cast<hipStream_t>(hip_stream));
+  return pa::launch_probe_reads(pool, pool2, (uint32_t)pool_bytes, tile_offsets, num_tiles,
+                                tile_bytes, out, w, static_cast<hipStream_t>(hip_stream));
 }
 
 pa_status pa_swap_blocks(void* k_pool, void* v_pool, void* k_host, void* v_host,

@@ -93,9 +93,11 @@ bool valu_supports(int dtype, int head_dim, int group);
 bool stream_supports(int num_seqs, int num_kv_heads, int max_ctx);
 int stream_waves();  // on the current device; 0 if it cannot be queried
 // The tile read probe (pa_probe.hip): `waves` waves (a multiple of 4) read
-// tiles [n r / waves, n (r + 1) / waves) each.
-pa_status launch_probe_reads(const void* pool, uint32_t pool_bytes, const uint32_t* offs,
-                             int64_t n, int tile_bytes, uint32_t* out, int waves, hipStream_t st);
+// tiles [n r / waves, n (r + 1) / waves) each, from pool and (if not null)
+// pool2 at the same offsets.
+pa_status launch_probe_reads(const void* pool, const void* pool2, uint32_t pool_bytes,
+                             const uint32_t* offs, int64_t n, int tile_bytes, uint32_t* out,
+                             int waves, hipStream_t st);
 int device_xcds();   // XCCs of the current device, 1..8 (8 if it cannot be queried)
 pa_status launch_decode_partition(const DecodeArgs& a, int dtype, KvType kv, int head_dim,
                                   DecodeKernel k, hipStream_t st);

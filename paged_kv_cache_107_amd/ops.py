@@ -257,21 +257,26 @@ def pa_copy_blocks(k_pool, v_pool, pairs, stream=None):
 
 
 def pa_probe_tile_reads(pool, tile_offsets, tile_bytes: int, num_waves: int = 0, out=None,
-                        stream=None):
+                        pool2=None, stream=None):
     """Read the listed tiles of a pool (tile t: tile_bytes bytes at byte offset
-    tile_offsets[t], uint32 values in an int32 device tensor) with num_waves
-    waves (0: the decode stream split's grid) and nothing else.  Returns the
-    per-wave XOR of the words read (uint32 values, int32 storage).  See pa.h."""
+    tile_offsets[t], uint32 values in an int32 device tensor), and of pool2 at
+    the same offsets when given, with num_waves waves (0: the decode stream
+    split's grid) and nothing else.  Returns the per-wave XOR of the words
+    read (uint32 values, int32 storage).  See pa.h."""
     _need_cuda("pool", pool)
+    nbytes = pool.numel() * pool.element_size()
+    if pool2 is not None:
+        _need_cuda("pool2", pool2)
+        if pool2.numel() * pool2.element_size() != nbytes:
+            raise ValueError("pool2 must have the size of pool")
     _need_cuda("tile_offsets", tile_offsets, torch.int32)
     if out is None:
         out = torch.empty(max(int(num_waves), 1024), dtype=torch.int32, device=pool.device)
     _need_cuda("out", out, torch.int32)
     waves = C.c_int32(0)
-    st = lib().pa_probe_tile_reads(_ptr(pool), pool.numel() * pool.element_size(),
-                                   _ptr(tile_offsets), int(tile_offsets.numel()), int(tile_bytes),
-                                   int(num_waves), _ptr(out), int(out.numel()), C.byref(waves),
-                                   _stream(stream))
+    st = lib().pa_probe_tile_reads(_ptr(pool), _ptr(pool2), nbytes, _ptr(tile_offsets),
+                                   int(tile_offsets.numel()), int(tile_bytes), int(num_waves),
+                                   _ptr(out), int(out.numel()), C.byref(waves), _stream(stream))
     check("pa_probe_tile_reads", st)
     return out[:waves.value]
 

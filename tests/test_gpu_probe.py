@@ -37,11 +37,14 @@ def host_xor(pool_words: np.ndarray, offs: np.ndarray, tile_bytes: int, waves: i
 @pytest.mark.parametrize("tile_bytes", [1024, 2048, 4096])
 @pytest.mark.parametrize("n", [0, 5, 3000, 20011])
 @pytest.mark.parametrize("waves", ["decode", "8", "per_tile"])
-def test_probe_xor_matches_host(tile_bytes, n, waves):
+@pytest.mark.parametrize("pools", [1, 2])
+def test_probe_xor_matches_host(tile_bytes, n, waves, pools):
     g = torch.Generator(device="cuda").manual_seed(tile_bytes + n)
     blocks = 257
     pool = torch.randint(-2**31, 2**31 - 1, (blocks * tile_bytes // 4,), generator=g,
                          device="cuda", dtype=torch.int32)
+    pool2 = (torch.randint(-2**31, 2**31 - 1, (blocks * tile_bytes // 4,), generator=g,
+                           device="cuda", dtype=torch.int32) if pools == 2 else None)
     rng = np.random.default_rng(n)
     offs = rng.integers(0, blocks, n).astype(np.int64) * tile_bytes
     if n:
@@ -49,11 +52,13 @@ def test_probe_xor_matches_host(tile_bytes, n, waves):
         offs[-1] = blocks * tile_bytes + 4096        # wholly past the end: zeros
     offs_d = torch.from_numpy(offs.astype(np.uint32).view(np.int32)).cuda()
     num_waves = {"decode": 0, "8": 8, "per_tile": 4 * max(-(-n // 4), 1)}[waves]
-    out = pa.pa_probe_tile_reads(pool, offs_d, tile_bytes, num_waves)
+    out = pa.pa_probe_tile_reads(pool, offs_d, tile_bytes, num_waves, pool2=pool2)
     torch.cuda.synchronize()
     got = out.cpu().numpy().view(np.uint32)
     want = host_xor(pool.cpu().numpy().view(np.uint32), offs, tile_bytes, len(got))
-    print(f"tile_bytes={tile_bytes} n={n} waves={len(got)}", flush=True)
+    if pool2 is not None:
+        want ^= host_xor(pool2.cpu().numpy().view(np.uint32), offs, tile_bytes, len(got))
+    print(f"tile_bytes={tile_bytes} n={n} waves={len(got)} pools={pools}", flush=True)
     assert np.array_equal(got, want)
 
 
