@@ -594,6 +594,26 @@ def measure_variants(cache, plan, q, d, reps: int, log):
                                   "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
         log(f"{name}: partition {part:.1f} us ({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS:.1%}), "
             f"decode {whole:.1f} us, {d.batch / (whole * 1e-6):.0f} seq/s")
+        if name == "fp8_e4m3":
+            # the read ceiling of the 8-bit step's tiles (2 KiB each, K with
+            # its V), as for the 16-bit pools in the main record
+            offs = decode_tile_offsets(plan, d) // wl.elem_bytes
+            offs_d = torch.from_numpy(offs.astype(np.uint32).view(np.int32)).cuda()
+            pout = torch.empty(1024, dtype=torch.int32, device="cuda")
+            for _ in range(3):
+                pa.pa_probe_tile_reads(k8, offs_d, 2048, 0, pout, v8)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                pa.pa_probe_tile_reads(k8, offs_d, 2048, 0, pout, v8)
+            b.record(stream)
+            torch.cuda.synchronize()
+            pus = 1e3 * a.elapsed_time(b) / reps
+            res[name]["read_probe"] = {"us_k_and_v": round(pus, 2),
+                                       "gbps": round(2 * len(offs) * 2048 / (pus * 1e-6) / 1e9, 1),
+                                       "partition_frac_of_probe_rate": round(pus / part, 4)}
+            log(f"{name}: read probe over the same 2 KiB K and V tiles {pus:.1f} us; the "
+                f"partition kernel at {pus / part:.1%} of that rate")
     del k8, v8
     torch.cuda.empty_cache()
     return res
