@@ -299,12 +299,13 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                      void* hip_stream);
 
 /* Prefill kernel.  PA_PREFILL_LDS: the K/V tiles of a 32-key step are loaded
- * through registers into LDS (16-bit and 8-bit pools).  PA_PREFILL_DMA: the
- * tiles go from memory straight into LDS and the P.V operands are read from
- * it transposed (16-bit pools only; PA_ERR_SHAPE for 8-bit pools).
- * PA_PREFILL_AUTO: the faster of the two on the measured workloads (the DMA
- * kernel for 16-bit pools, the LDS kernel for 8-bit pools).  Results agree
- * up to the order of fp32 sums.
+ * through registers into LDS (8-bit codes widened on the way).
+ * PA_PREFILL_DMA: the tiles go from memory straight into LDS (8-bit codes
+ * into a code stage, then widened into a 16-bit stage by the waves that
+ * loaded them) and the P.V operands are read from it transposed.
+ * PA_PREFILL_AUTO: the faster of the two on the measured workloads, the DMA
+ * kernel for 16-bit and 8-bit pools.  Both paths take every pool type and
+ * shape pa_prefill accepts; results agree up to the order of fp32 sums.
  * Process-wide; returns the previous value (-1 for an unknown path, which
  * leaves the setting unchanged). */
 typedef enum { PA_PREFILL_AUTO = 0, PA_PREFILL_LDS = 1, PA_PREFILL_DMA = 2 } pa_prefill_path;

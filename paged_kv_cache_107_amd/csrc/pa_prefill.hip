@@ -10,11 +10,11 @@
 // sequence and to itself (the autoregressive rule of the same §2.1).  K/V
 // rows are found through the block table as in decode.
 //
-// Two kernels share the grid, the item order and the walk below:
-// prefill_dma (16-bit pools, the default: tiles loaded straight into LDS,
-// 32x32x16 products) and prefill_mfma_lds (8-bit pools, and 16-bit ones on
-// request: tiles staged through registers, 16x16x32 products); each is
-// described above its code.  In both, the G query heads of a kv head and
+// Two kernel designs share the grid, the item order and the walk below:
+// the direct-to-LDS kernels, the default (prefill_dma on 16-bit pools,
+// prefill_dma8 on 8-bit ones: tiles loaded straight into LDS, 32x32x16
+// products), and prefill_mfma_lds on request (tiles staged through
+// registers, 16x16x32 products); each is described above its code.  In both, the G query heads of a kv head and
 // 32 / G consecutive chunk tokens make a wave's 32 query rows, keys are
 // walked 32 at a time (two 16-key tiles), steps at and past the rows' first
 // position are masked per element, and each lane keeps the softmax state of
@@ -23,9 +23,10 @@
 // rescale test and the P.V product).
 //
 // With a sliding window of W positions a row at position p attends only
-// positions p - W + 1 .. p.  8-bit pools are widened to the 16-bit operand
-// type as their tiles are stored into LDS (the codes as KvTile<E, kFp8>
-// orders them).
+// positions p - W + 1 .. p.  8-bit pools are widened exactly to the 16-bit
+// operand type in LDS (prefill_dma8) or on the way into it
+// (prefill_mfma_lds); the scales fold into the score factor and the
+// output factor.
 //
 // Grid: kv head x, then a flat item index k over (sequence, query-block
 // group z); group z takes query blocks nqb-1-4z .. nqb-4-4z of its sequence
@@ -927,6 +928,376 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
   }
 }
 
+// prefill_dma8 (8-bit pools): the same products and stage layout as
+// prefill_dma, with the codes staged twice.  Each wave loads its own eight K
+// and eight V rows of a step (1 KiB each, 16 bytes a lane) straight into a
+// code stage, two steps ahead; one step ahead it widens them exactly to the
+// operand type and writes them into a 16-bit stage in the piece layout
+// above.  A wave widens only the codes it loaded, so its own load wait
+// covers them, and the one barrier per step makes every wave's widened rows
+// visible.  LDS: two 16-bit stages and two 8 KiB code stages (49 KiB, three
+// workgroups per CU as before).
+constexpr int kCodeStage = 2 * kDmaKeys * 128;  // K and V codes of one step
+
+template <class E, bool WIN>
+__global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))) void prefill_dma8(PrefillArgs a) {
+  constexpr int D = 128;
+  using S = typename E::storage;
+  __shared__ __attribute__((aligned(256))) char s_st0[kStage];
+  __shared__ __attribute__((aligned(256))) char s_st1[kStage];
+  __shared__ __attribute__((aligned(256))) char s_cd0[kCodeStage];
+  __shared__ __attribute__((aligned(256))) char s_cd1[kCodeStage];
+  const int g = blockIdx.x;
+  const int Z = gridDim.y;
+  const int k = (int)blockIdx.y + Z * (int)blockIdx.z;
+  int i, zq;
+  // the item choice's scratch lives in the second 16-bit stage, which no
+  // wave writes before the first step's barrier
+  int* const s_qs = reinterpret_cast<int*>(s_st1 + kLptSeqs + 4 * kClasses + 16);
+  int* const s_ctx = s_qs + kPickRanges + 1;
+  pick_item_in<kDmaThreads>(a, k, Z, i, zq, reinterpret_cast<uint8_t*>(s_st1),
+                            reinterpret_cast<int*>(s_st1 + kLptSeqs),
+                            reinterpret_cast<int*>(s_st1 + kLptSeqs + 4 * kClasses), s_qs, s_ctx);
+  const int G = a.group, QT = kDmaRows / G;  // chunk tokens per wave
+  // the item's query range and length: from the item choice's LDS copy when
+  // it made one (small batches), else from memory
+  i = __builtin_amdgcn_readfirstlane(i);  // the same in every lane
+  zq = __builtin_amdgcn_readfirstlane(zq);
+  int qa, qb, ctx;
+  if (a.num_seqs <= kPickRanges) {
+    qa = s_qs[i];
+    qb = s_qs[i + 1];
+    ctx = s_ctx[i];
+  } else {
+    qa = a.query_start[i];
+    qb = a.query_start[i + 1];
+    ctx = clamp_ctx(a, i);
+  }
+  qa = __builtin_amdgcn_readfirstlane(qa);
+  qb = __builtin_amdgcn_readfirstlane(qb);
+  ctx = __builtin_amdgcn_readfirstlane(ctx);
+  if (qa < 0 || qb > a.num_tokens || qb <= qa) return;  // the whole workgroup
+  const int n = qb - qa, nq = min(n, a.max_query);
+  const int nqb = ceil_div(nq, QT);
+  const int top = nqb - 1 - kDmaWaves * zq;  // the item's latest query block
+  if (top < 0) return;                       // the whole workgroup
+  const int w = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int c32 = lane & 31, h = lane >> 5;
+  const int kend_wg = ctx - n + min(top * QT + QT, nq);  // the walk: keys [0, kend_wg)
+  const int blk = top - w;                               // this wave's query block
+  const int tok0 = blk * QT, ntok = blk >= 0 ? min(QT, nq - tok0) : 0;
+  const int pos0 = ctx - n + tok0;
+  const int kend = blk >= 0 ? pos0 + ntok : 0;
+  S* out = reinterpret_cast<S*>(a.out);
+
+  const int tl = c32 / G, hh = c32 - tl * G;
+  const bool live = tl < ntok && pos0 + tl >= 0;
+  const int lim = live ? pos0 + tl : kend - 1;
+  const int row = tl < ntok ? (qa + tok0 + tl) * a.num_q_heads + g * G + hh : -1;
+  if (kend_wg <= 0) {
+    if (row >= 0)
+      for (int d = 4 * h; d < D; d += 8)
+        *reinterpret_cast<uint2*>(out + (size_t)row * D + d) = uint2{0u, 0u};
+    return;
+  }
+  const bool mine = kend > 0;
+
+  u32x4 qv[8];
+  {
+    const S* qrow = reinterpret_cast<const S*>(a.q) + (size_t)max(row, 0) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qv[s] = row >= 0 ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
+  }
+  const float c = fabsf(a.scale_log2), inv_c = 1.f / c;
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+
+  const int bs_mask = (1 << a.log2_bs) - 1;
+  const size_t head_stride = (size_t)D << a.log2_bs;
+  const size_t block_stride = head_stride * a.num_kv_heads;
+  const int32_t* table = a.block_tables + (size_t)i * a.max_blocks;
+  const uint8_t* kbase0 = reinterpret_cast<const uint8_t*>(a.k_pool) + (size_t)g * head_stride;
+  const uint8_t* vbase0 = reinterpret_cast<const uint8_t*>(a.v_pool) + (size_t)g * head_stride;
+  const int ntiles = ceil_div(kend_wg, kTile);
+  const int nsteps = ceil_div(ntiles, 2);
+  const int unmasked = max(pos0, 0);
+  const int W = WIN ? a.window : 0;
+  const int st_begin =
+      WIN ? max(max(ctx - n + max(top - (kDmaWaves - 1), 0) * QT, 0) - W + 1, 0) / kDmaKeys : 0;
+  const int kbeg = WIN ? max(unmasked - W + 1, 0) : 0;
+
+  struct Ids {
+    int b0, b1;
+  };
+  // `inside`: the step lies inside the walk (every fast step), so its first
+  // tile does; its second may be one past the walk's end (odd tile counts),
+  // whose entry is then the last tile's (the tile is masked or not computed)
+  auto raw_ids = [&](int st, bool inside) __attribute__((always_inline)) -> Ids {
+    const int t = 2 * st;
+    int b0 = -1, b1 = -1;
+    if (inside || t < ntiles) b0 = scalar_load(table + ((t * kTile) >> a.log2_bs));
+    if (inside || t + 1 < ntiles)
+      b1 = scalar_load(table + ((min(t + 1, ntiles - 1) * kTile) >> a.log2_bs));
+    return Ids{b0, b1};
+  };
+  auto checked = [&](const Ids& r) __attribute__((always_inline)) -> Ids {
+    return Ids{(unsigned)r.b0 < (unsigned)a.num_blocks ? r.b0 : -1,
+               (unsigned)r.b1 < (unsigned)a.num_blocks ? r.b1 : -1};
+  };
+
+  const int tw = w >> 1;  // the tile of the step this wave loads rows of
+  // lane's 16 bytes of the wave's eight code rows (rows 8 (w % 2) .. of its
+  // tile, rows 8 w .. 8 w + 7 of the step)
+  const uint32_t coff = (uint32_t)(1024 * (w & 1) + 16 * lane);
+  // where the lane's two 16-byte chunks of 16-bit values (chunks 2 j and
+  // 2 j + 1 of step row R) go in a 16-bit stage: the direct-to-LDS kernel's
+  // piece layout
+  uint32_t kdst[2], vdst[2];
+  {
+    const int R = 8 * w + (lane >> 3), j = lane & 7;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int c = 2 * j + x;
+      kdst[x] = (uint32_t)(16 * ((R >> 4) * kKTileSlots + k_piece_slot((R & 15) >> 2) +
+                                 piece_slot(R & 3, c, tau_k(R & 3))));
+      vdst[x] = (uint32_t)(kKRegion + 1024 * (R >> 2) + 16 * piece_slot(R & 3, c, tau_v(R & 3)));
+    }
+  }
+  const int kr = 16 * (c32 >> 4) + 8 * ((c32 >> 2) & 1) + 4 * ((c32 >> 3) & 1) + (c32 & 3);
+  // K operand of k-step s at kb + 256 (s / 2) + 32 (s % 2)
+  const uint32_t kb = (uint32_t)(16 * ((kr >> 4) * kKTileSlots + k_piece_slot((kr >> 2) & 3) +
+                                       piece_slot(kr & 3, h, tau_k(kr & 3))));
+  // V^T operand (k-step ks, row half hr, d-tile dt) at vb + 4096 ks + 1024 hr + 256 dt
+  const uint32_t vb = (uint32_t)(kKRegion + 2048 * h +
+                                 16 * piece_slot((lane & 15) >> 2, 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1),
+                                                 tau_v((lane & 15) >> 2)) +
+                                 8 * (lane & 1));
+
+  // The codes of step st: this wave's eight K rows and eight V rows (1 KiB
+  // each, contiguous in the pool) straight into the code stage.  `full`: the
+  // tile lies wholly below the context length (every fast step).
+  auto issue = [&](int st, char* buf, const Ids& id, bool full) __attribute__((always_inline)) {
+    const int b = tw ? id.b1 : id.b0;
+    const int t = 2 * st + tw;
+    const size_t off = b >= 0 ? (size_t)b * block_stride + (size_t)((t * kTile) & bs_mask) * D : 0;
+    const rsrc_t ks = make_rsrc(kbase0 + off, b >= 0 ? 16u * 128u : 0u);
+    const uint32_t vbytes =
+        b < 0 ? 0u
+              : full ? 16u * 128u : (uint32_t)max(min(kTile, ctx - t * kTile), 0) * 128u;
+    const rsrc_t vs = make_rsrc(vbase0 + off, vbytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ks, (lds_void*)(buf + 1024 * w), 16, coff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vs, (lds_void*)(buf + 4096 + 1024 * w), 16, coff, 0,
+                                             0, 0);
+  };
+  // This wave's codes of a step, widened exactly to the operand type into a
+  // 16-bit stage (the rows it loaded itself, so its own wait covers them)
+  typedef const __attribute__((address_space(3))) char lds_cchar8;
+  typedef __attribute__((address_space(3))) char lds_char8;
+  struct Codes {
+    u32x4 k, v;
+  };
+  auto read_codes = [&](const char* cbuf) __attribute__((always_inline)) -> Codes {
+    return Codes{
+        *reinterpret_cast<const lds_u32x4*>((lds_cchar8*)cbuf + 1024 * w + 16 * lane),
+        *reinterpret_cast<const lds_u32x4*>((lds_cchar8*)cbuf + 4096 + 1024 * w + 16 * lane)};
+  };
+  auto widen_into = [&](const Codes& cd, char* bf) __attribute__((always_inline)) {
+    const u32x4 kc = cd.k, vc = cd.v;
+    *reinterpret_cast<lds_u32x4*>((lds_char8*)bf + kdst[0]) = widen8<E>(kc[0], kc[1]);
+    *reinterpret_cast<lds_u32x4*>((lds_char8*)bf + kdst[1]) = widen8<E>(kc[2], kc[3]);
+    *reinterpret_cast<lds_u32x4*>((lds_char8*)bf + vdst[0]) = widen8<E>(vc[0], vc[1]);
+    *reinterpret_cast<lds_u32x4*>((lds_char8*)bf + vdst[1]) = widen8<E>(vc[2], vc[3]);
+  };
+
+  float m = kMFloor, lsum = 0.f, thr = (kMFloor + kRescaleSlack) * inv_c;
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
+
+  typedef const __attribute__((address_space(3))) char lds_cchar;
+  // One step from stage `buf`: scores, mask, weights, P.V.  Every operand
+  // read is one of two per-lane bases plus an immediate.
+  auto compute = [&](int st, const char* buf, bool oka, bool okb, bool may_mask)
+      __attribute__((always_inline)) {
+    f32x16 sacc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 kop =
+          *reinterpret_cast<const lds_u32x4*>((lds_cchar*)buf + kb + (256u * (s >> 1) + 32u * (s & 1)));
+      sacc = mfma32<E>(kop, qv[s], sacc);
+    }
+    const int k0 = st * kDmaKeys;
+    float sv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sv[v] = sacc[v];
+    if (may_mask && (k0 + kDmaKeys - 1 > unmasked || (WIN && k0 < kend - W) || !oka || !okb)) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + 16 * (v >> 3) + 8 * h + (v & 7);
+        if (key > lim || (WIN && key <= lim - W) || !((v >> 3) ? okb : oka)) sv[v] = neg_inf();
+      }
+    }
+    // maxima as a tree of three-input maxima (eight instructions)
+    const float t0 = smax(smax(sv[0], sv[1]), sv[2]), t1 = smax(smax(sv[3], sv[4]), sv[5]);
+    const float t2 = smax(smax(sv[6], sv[7]), sv[8]), t3 = smax(smax(sv[9], sv[10]), sv[11]);
+    const float t4 = smax(smax(sv[12], sv[13]), sv[14]);
+    const float mt = smax(smax(smax(t0, t1), sv[15]), smax(smax(t2, t3), t4));
+    if (__builtin_amdgcn_ballot_w64(mt > thr)) {
+      const float x = smax(mt, shfl_xor(mt, 32));
+      const float mn = smax(m, x * c);
+      const float alpha = fast_exp2(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      m = mn;
+      thr = (m + kRescaleSlack) * inv_c;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float pf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(__builtin_fmaf(sv[8 * ks + e], c, -m));
+      const u32x4 pw = {Mfma<E>::round16x2(pf[0], pf[1]), Mfma<E>::round16x2(pf[2], pf[3]),
+                        Mfma<E>::round16x2(pf[4], pf[5]), Mfma<E>::round16x2(pf[6], pf[7])};
+      lsum = sum2(E{}, pw[3], sum2(E{}, pw[2], sum2(E{}, pw[1], sum2(E{}, pw[0], lsum))));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const i16x4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + vb + (4096u * ks + 256u * dt)));
+        const i16x4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_cchar*)buf + vb + (4096u * ks + 1024u + 256u * dt)));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
+        o[dt] = mfma32<E>(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pw, o[dt]);
+      }
+    }
+  };
+  auto runs = [&](int st) __attribute__((always_inline)) {
+    return mine && st * kDmaKeys < kend && (!WIN || (st + 1) * kDmaKeys > kbeg);
+  };
+
+  // Two 16-bit stages (the step computed, the next step's being widened) and
+  // two code stages (the next step's codes, and those of the step after,
+  // in flight); one barrier per step.  Step st: barrier (every wave's
+  // widened rows of st visible; the 16-bit stage of st - 1 free), the codes
+  // of st + 2 into the code stage of st, the products of st, then this
+  // wave's codes of st + 1 (loaded a step earlier) widened into the other
+  // 16-bit stage.
+  const int s0 = st_begin;
+  Ids id0 = checked(raw_ids(s0, false)), id1 = checked(raw_ids(s0 + 1, false));
+  Ids raw2 = raw_ids(s0 + 2, false);
+  issue(s0, s_cd0, id0, false);
+  if (s0 + 1 < nsteps) {
+    issue(s0 + 1, s_cd1, id1, false);
+    __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x000F | 2);  // own codes of s0 landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+  widen_into(read_codes(s_cd0), s_st0);
+  // lean steps: every key below the wave's first row (no causal mask) and,
+  // with a window, at or above its last row's window start (no window mask)
+  int fast_end = min(nsteps - 3, mine ? (unmasked + 1) / kDmaKeys : s0);
+  int fast_begin = s0;
+  if (WIN) {
+    // the lean segment starts in step with the stage order (groups of two)
+    const int first = max(ceil_div(max(kend - W, 0), kDmaKeys), s0);
+    fast_begin = s0 + 2 * ceil_div(first - s0, 2);
+    if (fast_begin + 2 > fast_end) fast_begin = fast_end = s0;  // no lean group
+  }
+  // cur / next: the 16-bit stages of st and st + 1; codes: the code stage of
+  // st + 1; fill: the code stage of st (free again), for st + 2
+  auto step = [&](int st, const char* cur, char* next, const char* codes, char* fill, bool fast)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0070 | 2);  // this wave's widened rows written
+    __builtin_amdgcn_s_barrier();
+    const Ids id2 = checked(raw2);
+    if (fast)
+      issue(st + 2, fill, id2, true);
+    else if (st + 2 < nsteps)
+      issue(st + 2, fill, id2, false);
+    if (fast)
+      compute(st, cur, true, true, false);
+    else if (runs(st) && (id0.b0 >= 0 || id0.b1 >= 0))
+      compute(st, cur, id0.b0 >= 0, id0.b1 >= 0, true);
+    // The next ids' scalar loads go out after the step's products and with
+    // the reads of the codes to widen: the two kinds share a counter (an
+    // outstanding scalar load makes every LDS wait a full one), so the
+    // latencies overlap in the one wait before the widening.
+    if (fast || st + 1 < nsteps) {
+      if (fast || st + 2 < nsteps)
+        __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x000F | 2);  // own codes of st + 1 landed
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      const Codes cd = read_codes(codes);
+      __builtin_amdgcn_sched_barrier(0);
+      raw2 = raw_ids(st + 3, fast);
+      __builtin_amdgcn_sched_barrier(0);
+      widen_into(cd, next);
+    } else {
+      __builtin_amdgcn_sched_barrier(0);
+      raw2 = raw_ids(st + 3, fast);
+    }
+    id0 = id1;
+    id1 = id2;
+  };
+  int st = s0;
+  for (; st < fast_begin; st += 2) {  // window: the steps below the lean ones
+    step(st, s_st0, s_st1, s_cd1, s_cd0, false);
+    step(st + 1, s_st1, s_st0, s_cd0, s_cd1, false);
+  }
+  for (; st + 2 <= fast_end; st += 2) {
+    step(st, s_st0, s_st1, s_cd1, s_cd0, true);
+    step(st + 1, s_st1, s_st0, s_cd0, s_cd1, true);
+  }
+  for (; st < nsteps; st += 2) {
+    step(st, s_st0, s_st1, s_cd1, s_cd0, false);
+    if (st + 1 >= nsteps) break;
+    step(st + 1, s_st1, s_st0, s_cd0, s_cd1, false);
+  }
+
+  const float total = lsum + shfl_xor(lsum, 32);
+  if (row >= 0) {
+    const float inv = live && total > 0.f ? a.v_scale / total : 0.f;
+    S* dst = out + (size_t)row * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * j) =
+            uint2{Mfma<E>::round16x2(o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv),
+                  Mfma<E>::round16x2(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv)};
+  }
+  if (a.status != nullptr) {
+    const int kfirst =
+        WIN ? max(max(ctx - n + max(top - (kDmaWaves - 1), 0) * QT, 0) - W + 1, 0) : 0;
+    bool bad = false;
+    for (int j = (kfirst >> a.log2_bs) + (int)threadIdx.x; j <= ((kend_wg - 1) >> a.log2_bs);
+         j += kDmaThreads)
+      bad |= (unsigned)table[j] >= (unsigned)a.num_blocks;
+    report_bad_block(a.status, __builtin_amdgcn_ballot_w64(bad) != 0);
+  }
+}
+
+
+template <class E>
+pa_status launch_dma8(const PrefillArgs& a, hipStream_t st) {
+  const int blocks = ceil_div(a.max_query, kDmaRows / a.group);
+  if (blocks <= 0) return PA_OK;
+  const dim3 grid(a.num_kv_heads, ceil_div(blocks, kDmaWaves), a.num_seqs);
+  if (a.window > 0)
+    hipLaunchKernelGGL((prefill_dma8<E, true>), grid, dim3(kDmaThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_dma8<E, false>), grid, dim3(kDmaThreads), 0, st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 template <class E>
 pa_status launch_dma(const PrefillArgs& a, hipStream_t st) {
   const int blocks = ceil_div(a.max_query, kDmaRows / a.group);
@@ -964,18 +1335,16 @@ int prefill_query_blocks(int max_query_len, int group) {
 
 pa_status launch_prefill(const PrefillArgs& a, int dtype, KvType kv, int path, hipStream_t st) {
   const bool fp8 = kv == KvType::kFp8;
-  // 16-bit pools run the direct-to-LDS kernel unless the register-staged one
-  // is asked for (AUTO: the direct kernel, 15-20% faster on the 8B chunked
-  // workload); 8-bit pools, whose codes are widened on the way into LDS, run
-  // the register-staged kernel
-  const bool dma = !fp8 && path != PA_PREFILL_LDS;
-  if (fp8 && path == PA_PREFILL_DMA) return PA_ERR_SHAPE;
+  // The direct-to-LDS kernels unless the register-staged one is asked for
+  // (AUTO: on the 8B chunked workload the direct kernel is 15-20% faster on
+  // 16-bit pools and a few percent faster on 8-bit pools)
+  const bool dma = path != PA_PREFILL_LDS;
   if (dtype == PA_BF16) {
-    if (dma) return launch_dma<BF16>(a, st);
+    if (dma) return fp8 ? launch_dma8<BF16>(a, st) : launch_dma<BF16>(a, st);
     return fp8 ? launch_lds<BF16, KvType::kFp8>(a, st) : launch_lds<BF16, KvType::kSame>(a, st);
   }
   if (dtype == PA_F16) {
-    if (dma) return launch_dma<F16>(a, st);
+    if (dma) return fp8 ? launch_dma8<F16>(a, st) : launch_dma<F16>(a, st);
     return fp8 ? launch_lds<F16, KvType::kFp8>(a, st) : launch_lds<F16, KvType::kSame>(a, st);
   }
   return PA_ERR_SHAPE;

@@ -4,8 +4,9 @@ benchmark times.
 
 * Chunked prefill, 16 sequences x 512-token chunks on cached prefixes (8192
   rows, 32 q / 8 kv heads, head_dim 128, bf16): without a window and with a
-  1024-position window, on both prefill kernels; and on 8-bit E4M3 pools
-  holding the quantised contents of the 16-bit pools (codes written by the
+  1024-position window, on both prefill kernels; and, on both kernels, on
+  8-bit E4M3 pools holding the quantised contents of the 16-bit pools (codes
+  written by the
   quantising cache write and checked bit for bit against the oracle's
   encoding of the oracle's own pools).
 * Decode of the 8B batch (256 sequences): a 1024-position window on the
@@ -124,8 +125,8 @@ def test_prefill_every_row(window, prefill_kernel):
     assert err <= TOL["bf16"]
 
 
-def test_prefill_every_row_on_quantised_pools():
-    print("prefill_8b full size on 8-bit pools", flush=True)
+def test_prefill_every_row_on_quantised_pools(prefill_kernel):
+    print(f"prefill_8b full size on 8-bit pools: kernel={prefill_kernel}", flush=True)
     k8, v8, ck, cv = prefill_codes()
     assert np.array_equal(fp8_bits(k8), ck) and np.array_equal(fp8_bits(v8), cv)
     out = run_prefill(k8, v8, 0, SCALES)

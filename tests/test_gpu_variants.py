@@ -306,7 +306,18 @@ def test_fp8_cow_workload_and_copies(dtype):
 @pytest.mark.parametrize("window,g,dtype", [(0, 1, "bf16"), (0, 4, "bf16"), (0, 8, "bf16"),
                                             (50, 1, "bf16"), (50, 4, "bf16"), (50, 8, "bf16"),
                                             (0, 4, "f16"), (50, 16, "f16")])
-def test_fp8_prefill(window, g, dtype):
+@pytest.mark.parametrize("kernel", ["lds", "dma"])
+def test_fp8_prefill(window, g, dtype, kernel):
+    """8-bit pools on both prefill kernels: codes widened in registers on the
+    way into LDS (lds), or loaded straight into LDS and widened there (dma)."""
+    prev = pa.pa_set_prefill_path({"lds": pa.PA_PREFILL_LDS, "dma": pa.PA_PREFILL_DMA}[kernel])
+    try:
+        fp8_prefill_case(window, g, dtype, kernel)
+    finally:
+        pa.pa_set_prefill_path(prev)
+
+
+def fp8_prefill_case(window, g, dtype, kernel):
     chunks = [1, 17, 64, 65, 100]
     prefixes = [0, 40, 16, 300, 3]
     lens = [c + p for c, p in zip(chunks, prefixes)]
@@ -325,5 +336,6 @@ def test_fp8_prefill(window, g, dtype):
                          o["lens"], d.wl.scale, dtype, window=window, kv_dtype="fp8_e4m3",
                          k_scale=SCALES[0], v_scale=SCALES[1])
     err = max_abs_err(out, want)
-    print(f"fp8 prefill {dtype} G={g} window={window} max_abs_err={err:.3e}", flush=True)
+    print(f"fp8 prefill {kernel} {dtype} G={g} window={window} max_abs_err={err:.3e}",
+          flush=True)
     assert err <= TOL[dtype]
