@@ -1050,15 +1050,19 @@ __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(3))
   };
 
   const int tw = w >> 1;  // the tile of the step this wave loads rows of
-  // lane's 16 bytes of the wave's eight code rows (rows 8 (w % 2) .. of its
-  // tile, rows 8 w .. 8 w + 7 of the step)
-  const uint32_t coff = (uint32_t)(1024 * (w & 1) + 16 * lane);
-  // where the lane's two 16-byte chunks of 16-bit values (chunks 2 j and
-  // 2 j + 1 of step row R) go in a 16-bit stage: the direct-to-LDS kernel's
+  // The lane's 16 codes: chunk jj of row rr of the wave's eight code rows
+  // (rows 8 (w % 2) .. of its tile, rows 8 w .. 8 w + 7 of the step).  The
+  // eight lanes of each group of the widened stores take the four rows of a
+  // piece and two chunks with different bit 0 of jj, so their stores land on
+  // eight distinct 16-byte bank groups.
+  const int rr = 4 * ((lane >> 3) & 1) + (lane & 3), jj = 2 * (lane >> 4) + ((lane >> 2) & 1);
+  const uint32_t coff = (uint32_t)(1024 * (w & 1) + 128 * rr + 16 * jj);
+  // where the lane's two 16-byte chunks of 16-bit values (chunks 2 jj and
+  // 2 jj + 1 of step row R) go in a 16-bit stage: the direct-to-LDS kernel's
   // piece layout
   uint32_t kdst[2], vdst[2];
   {
-    const int R = 8 * w + (lane >> 3), j = lane & 7;
+    const int R = 8 * w + rr, j = jj;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int c = 2 * j + x;
